@@ -1,0 +1,357 @@
+"""Plain CPU oracle of the HLQ/HOT linear-layer backward pass.
+
+TEST INFRASTRUCTURE.  This module is the slow, obviously-correct statement of
+what the GPU library computes.  Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark may import it; the GPU library shares no code
+with it and never calls it.
+
+Sources (the pages this follows; cited by title and section):
+
+* [HLQ] "HLQ: Fast and Efficient Backpropagation via Hadamard Low-rank
+  Quantization" (Kim, Park; arXiv 2406.15102, sciencestack.ai page).
+  TL;DR: the two backward products g_x = g_y . w and g_w = (1/B) gy_bar^T . x_bar,
+  4-bit Hadamard quantization (HQ) on g_x, low-rank int8 processing on g_w,
+  int4 activation compression (ACBP).  Table of contents, section
+  "Hadamard Transform" (body not on the page).  Figure 2 caption ("frequency
+  domain with Hadamard transform").
+* [HOT-abs] "HOT: Hadamard-based Optimized Training" (Hugging Face paper page),
+  abstract: Hadamard quantization and Hadamard low-rank approximation applied
+  per backward path, plus activation buffer compression and layer-wise
+  quantizer selection.
+* [HOT-sum] "HOT: Hadamard-based Optimized Training" (scime.ai summary),
+  section "Approach": INT4 Hadamard quantization for gx, Hadamard low-rank
+  approximation plus INT8 quantization for gw, stored activations compressed at
+  forward time, per-token vs per-tensor quantization chosen per layer.
+
+The pages print no formulas beyond the two TL;DR identities and no worked
+example, so every step below states the reading it takes where they are
+silent.  The readings (R1..R9) are:
+
+R1  Hadamard matrix: Sylvester order, entries H[i][j] = (-1)^popcount(i & j),
+    unnormalised; the single normalising factor 1/n is applied once, in the
+    fp64 epilogue.  ([HLQ] section "Hadamard Transform": title only.)
+R2  The transform's fp32 operation order is the radix-2 butterfly with
+    ascending stage distance h = 1, 2, 4, ..., n/2; pair (k, k+h) with
+    (k & h) == 0 becomes (a + b, a - b).  Arithmetic is IEEE fp32 with
+    round-to-nearest-even.  (Order is not on the pages; fixing it makes the
+    quantized codes unique.)
+R3  Blocks are aligned and non-overlapping from index 0; the transformed
+    dimension must be a multiple of the block size n.
+R4  "Low-rank" keeps, in each block of n tokens, the r rows of H_n with the
+    lowest sequency (number of sign changes).  For power-of-two r these are
+    the natural-order rows j*(n/r), j = 0..r-1; outputs are stored block by
+    block, j ascending.  ([HLQ] TL;DR "low-rank"; Figure 2 "frequency domain".)
+R5  Quantizer: symmetric absmax, no zero point.  For a scale group G with
+    qmax = 7 (INT4) or 127 (INT8): a = max|v|; a == 0 gives codes 0 and scale
+    0; otherwise inv = fl32(qmax / a), s = fl32(a / qmax),
+    q = clamp(rne(fl32(v * inv)), -qmax, qmax).
+R6  Scale groups (layer-wise quantizer selection, [HOT-sum] "Approach"):
+    PER_TOKEN gives one scale per GEMM output index of each operand (g_x path:
+    one per token t of the transformed g_y and one per input channel i of the
+    transformed w; g_w path: one per output channel o of the low-rank g_y and
+    one per input channel i of the low-rank x).  PER_TENSOR gives one scale
+    per operand.  Each path has its own mode.  ACBP is always per token.
+R7  The activation x reaches the backward as ACBP codes; it is dequantized as
+    fl32(s_x[t] * q[t, i]) before its low-rank transform.
+R8  The "1/B" of the g_w identity ([HLQ] TL;DR) is read as two factors: the
+    Hadamard normalisation 1/n (always) and an optional mean-reduction 1/T on
+    g_w only (argument ``reduction``).
+R9  Outputs g_x [T x I] and g_w [O x I] are fp32; the epilogue is evaluated in
+    fp64 and rounded once to fp32.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PER_TOKEN = 0
+PER_TENSOR = 1
+SUM = 0
+MEAN = 1
+
+QMAX_INT4 = 7
+QMAX_INT8 = 127
+
+
+def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to fp32; exact (the low 16 bits are 0)."""
+    u = np.asarray(u, dtype=np.uint16)
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Hadamard transform ([HLQ] section "Hadamard Transform"; readings R1-R4)
+# --------------------------------------------------------------------------
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """Explicit H_n with H[i][j] = (-1)^popcount(i & j) (reading R1), int64."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    bits = np.bitwise_and(i, j)
+    pop = np.zeros_like(bits)
+    while bits.any():
+        pop += bits & 1
+        bits = bits >> 1
+    return np.where(pop % 2 == 0, 1, -1).astype(np.int64)
+
+
+def fwht_blocks(v: np.ndarray, n: int, axis: int) -> np.ndarray:
+    """Block Walsh-Hadamard transform of ``v`` along ``axis`` (readings R1-R3).
+
+    Every aligned block of ``n`` entries along ``axis`` is replaced by H_n times
+    that block, computed with radix-2 butterflies in ascending stage order
+    (h = 1, 2, ..., n/2).  The arithmetic is done in ``v``'s own dtype: fp32
+    for the quantized path (each add/sub rounds once, RNE), fp64 for the
+    quantization-off self-checks.
+    """
+    if n < 1 or n & (n - 1):
+        raise ValueError("block size must be a power of two")
+    x = np.moveaxis(np.array(v, copy=True), axis, 0)
+    L = x.shape[0]
+    if L % n:
+        raise ValueError("transformed dimension must be a multiple of the block")
+    rest = x.shape[1:]
+    x = x.reshape((L // n, n) + rest)          # [block, position, ...]
+    h = 1
+    while h < n:
+        # positions k with (k & h) == 0 pair with k + h
+        lo = np.array([k for k in range(n) if k & h == 0])
+        a = x[:, lo].copy()
+        b = x[:, lo + h].copy()
+        x[:, lo] = a + b
+        x[:, lo + h] = a - b
+        h *= 2
+    x = x.reshape((L,) + rest)
+    return np.moveaxis(x, 0, axis)
+
+
+def lowrank_rows(n: int, r: int) -> np.ndarray:
+    """Rows of H_n kept by the low-rank step (reading R4): j*(n/r), j < r."""
+    if r < 1 or r > n or r & (r - 1):
+        raise ValueError("rank must be a power of two in [1, n]")
+    return np.arange(r) * (n // r)
+
+
+def sequency(h: np.ndarray) -> np.ndarray:
+    """Number of sign changes along each row of a +-1 matrix."""
+    return (h[:, 1:] != h[:, :-1]).sum(axis=1)
+
+
+def lowrank_transform(v: np.ndarray, n: int, r: int, axis: int = 0) -> np.ndarray:
+    """Hadamard low-rank approximation along ``axis`` (HLA; reading R4).
+
+    Full block transform along ``axis`` followed by keeping, in every block,
+    the rows j*(n/r) in ascending j.  The result has length L*r/n along
+    ``axis``.
+    """
+    full = fwht_blocks(v, n, axis)
+    x = np.moveaxis(full, axis, 0)
+    L = x.shape[0]
+    keep = (np.arange(L // n)[:, None] * n + lowrank_rows(n, r)[None, :]).reshape(-1)
+    return np.moveaxis(x[keep], 0, axis)
+
+
+# --------------------------------------------------------------------------
+# Quantizer (readings R5, R6)
+# --------------------------------------------------------------------------
+
+def quantize(v: np.ndarray, qmax: int, reduce_axis):
+    """Symmetric absmax quantization of fp32 ``v`` (reading R5).
+
+    ``reduce_axis`` is the axis a scale group runs along (``None``: the whole
+    tensor is one group).  Returns (codes int8, scales fp32); scales keep the
+    non-reduced axis (or are a 1-element array for the whole tensor).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    if reduce_axis is None:
+        a = np.abs(v).max(keepdims=True).reshape(1)
+        a_b = a.reshape((1,) * v.ndim)
+    else:
+        a_b = np.abs(v).max(axis=reduce_axis, keepdims=True)
+        a = np.squeeze(a_b, axis=reduce_axis)
+    qm = np.float32(qmax)
+    zero = a_b == 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        inv = np.where(zero, np.float32(0), qm / np.where(zero, np.float32(1), a_b)).astype(np.float32)
+        s = np.where(a == 0, np.float32(0), a / qm).astype(np.float32)
+    prod = (v * inv).astype(np.float32)            # one fp32 rounding
+    q = np.clip(np.rint(prod), -qmax, qmax)        # rint: round half to even
+    return q.astype(np.int8), s.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Activation buffer compression (ACBP): [HLQ] TL;DR, [HOT-abs], [HOT-sum]
+# --------------------------------------------------------------------------
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles, element 2k in bits 3:0, 2k+1 in bits 7:4."""
+    q = np.asarray(q, dtype=np.int16)
+    if q.shape[-1] % 2:
+        raise ValueError("last dimension must be even")
+    u = (q & 0xF).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint8)
+    lo = (b & 0xF).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def acbp_pack(x: np.ndarray):
+    """Store the layer input as INT4 codes with one fp32 scale per token.
+
+    x [T x I] (fp32 values) -> (codes uint8 [T][I/2], scales fp32 [T]).
+    """
+    q, s = quantize(np.asarray(x, dtype=np.float32), QMAX_INT4, reduce_axis=1)
+    return pack_int4(q), s
+
+
+def acbp_unpack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Dequantize ACBP codes: x[t, i] = fl32(s[t] * q[t, i]) (reading R7)."""
+    q = unpack_int4(codes).astype(np.float32)
+    return (np.asarray(scales, dtype=np.float32)[:, None] * q).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Integer GEMM and epilogue ([HLQ] TL;DR "int8-accelerated"; reading R9)
+# --------------------------------------------------------------------------
+
+def int_matmul(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Exact integer product a [M x K] . b [K x N] -> int64.
+
+    Evaluated with an fp64 matrix product: every partial sum is an integer of
+    magnitude below 2^53, so fp64 represents each one exactly.
+    """
+    a = np.asarray(a)
+    b = np.asarray(b)
+    K = a.shape[1]
+    bound = K * int(np.abs(a).max(initial=0)) * int(np.abs(b).max(initial=0))
+    assert bound < 2 ** 53, "integer GEMM would leave the exact fp64 range"
+    return np.rint(a.astype(np.float64) @ b.astype(np.float64)).astype(np.int64)
+
+
+def _group_axis(mode: int, axis: int):
+    if mode == PER_TOKEN:
+        return axis
+    if mode == PER_TENSOR:
+        return None
+    raise ValueError("mode must be PER_TOKEN or PER_TENSOR")
+
+
+def _bcast(s: np.ndarray, axis: int) -> np.ndarray:
+    """Scale vector -> broadcastable along the non-reduced axis."""
+    s = np.asarray(s, dtype=np.float64)
+    if s.size == 1:
+        return s.reshape(1, 1)
+    return s[:, None] if axis == 0 else s[None, :]
+
+
+# --------------------------------------------------------------------------
+# The backward pass
+# --------------------------------------------------------------------------
+
+def linear_backward(gy, x_codes, x_scales, w, block: int, rank: int,
+                    gx_mode: int = PER_TOKEN, gw_mode: int = PER_TOKEN,
+                    reduction: int = SUM) -> dict:
+    """HLQ/HOT backward of y = x . w^T for one linear layer.
+
+    gy [T x O] and w [O x I] hold fp32 values (bf16 inputs widened exactly);
+    x arrives as ACBP codes [T][I/2] with per-token scales [T].
+
+    g_x path ([HLQ] TL;DR "4-bit HQ for g_x"; [HOT-sum] "Approach"):
+      gy_h = H along O of gy (blocks of n), w_h = H along O of w; both
+      quantized to INT4; acc_x = q_gy . q_w (int); g_x = acc_x*s_gy*s_w/n.
+    g_w path ([HLQ] TL;DR "low-rank, int8-accelerated processing for g_w";
+    [HOT-sum] "Approach"):
+      gy_l, x_l = low-rank H along T of gy and of dequantized x; both
+      quantized to INT8; acc_w = q_gyl^T . q_xl; g_w = acc_w*s*s/n (/T if MEAN).
+
+    Returns every intermediate in its logical layout (codes as int8 values):
+      q_gy [T x O], s_gy [T] or [1], q_w [O x I], s_w [I] or [1],
+      acc_x [T x I], g_x [T x I],
+      q_gyl [T' x O], s_gyl [O] or [1], q_xl [T' x I], s_xl [I] or [1],
+      acc_w [O x I], g_w [O x I],  with T' = T*rank/block.
+    """
+    gy = np.asarray(gy, dtype=np.float32)
+    w = np.asarray(w, dtype=np.float32)
+    T, O = gy.shape
+    O2, I = w.shape
+    assert O2 == O
+    n, r = block, rank
+
+    # g_x path: Hadamard along O (the contracted dimension), INT4.
+    gy_h = fwht_blocks(gy, n, axis=1)
+    w_h = fwht_blocks(w, n, axis=0)
+    q_gy, s_gy = quantize(gy_h, QMAX_INT4, _group_axis(gx_mode, 1))
+    q_w, s_w = quantize(w_h, QMAX_INT4, _group_axis(gx_mode, 0))
+    acc_x = int_matmul(q_gy, q_w)
+    g_x = (acc_x.astype(np.float64) * _bcast(s_gy, 0) * _bcast(s_w, 1)
+           / n).astype(np.float32)
+
+    # g_w path: low-rank Hadamard along T (the contracted dimension), INT8.
+    x = acbp_unpack(x_codes, x_scales)
+    assert x.shape == (T, I)
+    gy_l = lowrank_transform(gy, n, r, axis=0)
+    x_l = lowrank_transform(x, n, r, axis=0)
+    q_gyl, s_gyl = quantize(gy_l, QMAX_INT8, _group_axis(gw_mode, 0))
+    q_xl, s_xl = quantize(x_l, QMAX_INT8, _group_axis(gw_mode, 0))
+    acc_w = int_matmul(q_gyl.T, q_xl)
+    gw64 = acc_w.astype(np.float64) * _bcast(s_gyl, 0) * _bcast(s_xl, 1) / n
+    if reduction == MEAN:
+        gw64 = gw64 / T
+    elif reduction != SUM:
+        raise ValueError("reduction must be SUM or MEAN")
+    g_w = gw64.astype(np.float32)
+
+    return dict(q_gy=q_gy, s_gy=s_gy, q_w=q_w, s_w=s_w, acc_x=acc_x, g_x=g_x,
+                x_deq=x, q_gyl=q_gyl, s_gyl=s_gyl, q_xl=q_xl, s_xl=s_xl,
+                acc_w=acc_w, g_w=g_w)
+
+
+def linear_backward_unquantized(gy, x, w, block: int, rank: int,
+                                reduction: int = SUM) -> dict:
+    """Quantization-off form of :func:`linear_backward` (self-checks only).
+
+    Same transforms, no ACBP, no quantizer, fp64 throughout.  With
+    rank == block this must give back g_x = gy . w and g_w = gy^T . x, since
+    H_n^T H_n = n I.
+    """
+    gy = np.asarray(gy, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    T = gy.shape[0]
+    n = block
+    g_x = fwht_blocks(gy, n, axis=1) @ fwht_blocks(w, n, axis=0) / n
+    g_w = lowrank_transform(gy, n, rank, axis=0).T @ lowrank_transform(x, n, rank, axis=0) / n
+    if reduction == MEAN:
+        g_w = g_w / T
+    return dict(g_x=g_x, g_w=g_w)
+
+
+def rel_fro(a, b) -> float:
+    """||a - b||_F / ||b||_F in fp64 (0 when both are zero)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    num = np.linalg.norm(a - b)
+    if den == 0:
+        return 0.0 if num == 0 else float("inf")
+    return float(num / den)
+
+
+__all__ = [
+    "PER_TOKEN", "PER_TENSOR", "SUM", "MEAN", "QMAX_INT4", "QMAX_INT8",
+    "bf16_bits_to_f32",
+    "sylvester_hadamard", "fwht_blocks", "lowrank_rows", "sequency",
+    "lowrank_transform", "quantize", "pack_int4", "unpack_int4", "acbp_pack",
+    "acbp_unpack", "int_matmul", "linear_backward",
+    "linear_backward_unquantized", "rel_fro",
+]
