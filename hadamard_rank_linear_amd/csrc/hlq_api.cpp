@@ -1,0 +1,278 @@
+// C ABI of the HLQ/HOT linear-layer backward: argument validation, workspace
+// carving and the launch sequence.  Everything here runs on the host; all
+// arithmetic of the method happens in the kernels of hlq_kernels.hip.
+//
+// Launch sequence of hlq_linear_backward (one stream, no host sync; each line
+// is one HLQ_STEP_* of hlq.h):
+//   1. clear the max accumulators, zero the K padding of the stored operands
+//   2. g_x operand A: H along O of g_y rows -> INT4 (per-token, or tensor max
+//      pass then quantize pass)
+//   3. g_x operand B: H along O of w columns -> INT4 transposed (max pass,
+//      quantize pass)
+//   4. g_w operand A: low-rank H along T of g_y -> INT8 transposed (max pass,
+//      quantize pass)
+//   5. g_w operand B: the same for the ACBP-decoded x
+//   6. INT4 GEMM with fused dequantizing epilogue -> g_x
+//   7. INT8 GEMM (split-K partials + finalize when the tile grid is small) -> g_w
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/hlq.h"
+#include "hlq_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxO = 171196;       // 256 * 49 * O < 2^31 (INT4 lanes hold 16*code)
+constexpr int64_t kMaxTLow = 133143;    // 127^2 * T' < 2^31
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  hlq_workspace_layout pub;
+  size_t maxes;        // uint32: colmax_w[I], colmax_gyl[O], colmax_xl[I], gmax[4]
+  size_t partial;      // int32 split-K partials of the g_w GEMM
+  hlq::GemmPlan plan_gx, plan_gw;
+};
+
+hlq_status check_shape(int64_t T, int64_t I, int64_t O, int block, int rank) {
+  if (T <= 0 || I <= 0 || O <= 0) return HLQ_ERR_SHAPE;
+  if (block != 16 && block != 32 && block != 64 && block != 128) return HLQ_ERR_BLOCK;
+  if (!pow2(rank) || rank > block) return HLQ_ERR_RANK;
+  if (T % block || O % block || I % 8) return HLQ_ERR_SHAPE;
+  if (O > kMaxO || T / block * rank > kMaxTLow) return HLQ_ERR_OVERFLOW;
+  return HLQ_OK;
+}
+
+Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
+  Layout L;
+  memset(&L, 0, sizeof(L));
+  const int64_t t_low = T / block * rank;
+  const int64_t kx = (O + 127) / 128 * 128;  // INT4 codes per row, 64-byte stages
+  const int64_t kxb = kx / 2;
+  const int64_t kwb = (t_low + 63) / 64 * 64;
+  L.pub.kx_pitch = kxb;
+  L.pub.kw_pitch = kwb;
+  L.pub.t_low = t_low;
+  L.plan_gx = hlq::plan_gemm(T, I, kxb);
+  L.plan_gw = hlq::plan_gemm(O, I, kwb);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L.pub.q_gy = take((size_t)T * kxb);
+  L.pub.s_gy = take((size_t)T * 4);
+  L.pub.q_w = take((size_t)I * kxb);
+  L.pub.s_w = take((size_t)I * 4);
+  L.pub.q_gyl = take((size_t)O * kwb);
+  L.pub.s_gyl = take((size_t)O * 4);
+  L.pub.q_xl = take((size_t)I * kwb);
+  L.pub.s_xl = take((size_t)I * 4);
+  L.maxes = take((size_t)(I + O + I + 4) * 4);
+  // split-K partials: the two GEMMs run one after the other on one stream and
+  // share this buffer
+  size_t part = 0;
+  if (L.plan_gx.splits > 1) part = (size_t)L.plan_gx.splits * T * I * 4;
+  if (L.plan_gw.splits > 1 && (size_t)L.plan_gw.splits * O * I * 4 > part)
+    part = (size_t)L.plan_gw.splits * O * I * 4;
+  L.pub.partial_bytes = part;
+  L.pub.gx_splits = L.plan_gx.splits;
+  L.pub.gw_splits = L.plan_gw.splits;
+  L.partial = take(part);
+  L.pub.partial = L.partial;
+  L.pub.total = off;
+  return L;
+}
+
+#define HLQ_TRY(expr)                       \
+  do {                                      \
+    if ((expr) != hipSuccess) return HLQ_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int hlq_version(void) { return 100; }
+
+const char* hlq_status_string(int status) {
+  switch (status) {
+    case HLQ_OK: return "ok";
+    case HLQ_ERR_NULL: return "a required pointer is NULL";
+    case HLQ_ERR_SHAPE: return "invalid shape (T, I, O > 0; T, O multiples of block; I multiple of 8)";
+    case HLQ_ERR_BLOCK: return "block must be 16, 32, 64 or 128";
+    case HLQ_ERR_RANK: return "rank must be a power of two in [1, block]";
+    case HLQ_ERR_MODE: return "quantizer mode or reduction out of range";
+    case HLQ_ERR_DTYPE: return "dtype must be HLQ_F32 or HLQ_BF16";
+    case HLQ_ERR_ALIGN: return "data pointers must be 16-byte aligned";
+    case HLQ_ERR_OVERFLOW: return "an INT32 accumulator could overflow (O or T*rank/block too large)";
+    case HLQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case HLQ_ERR_HIP: return "HIP runtime error while enqueueing";
+    default: return "unknown status";
+  }
+}
+
+hlq_status hlq_compress_act(const void* x, int x_dtype, int64_t T, int64_t I,
+                            uint8_t* x_codes, float* x_scales, void* stream) {
+  if (!x || !x_codes || !x_scales) return HLQ_ERR_NULL;
+  if (x_dtype != HLQ_F32 && x_dtype != HLQ_BF16) return HLQ_ERR_DTYPE;
+  if (T <= 0 || I < 8 || I % 8) return HLQ_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(x_codes) || !aligned16(x_scales)) return HLQ_ERR_ALIGN;
+  HLQ_TRY(hlq::launch_acbp(x, x_dtype, T, I, x_codes, x_scales,
+                           static_cast<hipStream_t>(stream)));
+  return HLQ_OK;
+}
+
+size_t hlq_linear_backward_workspace_size(int64_t T, int64_t I, int64_t O, int block,
+                                          int rank) {
+  if (check_shape(T, I, O, block, rank) != HLQ_OK) return 0;
+  return make_layout(T, I, O, block, rank).pub.total;
+}
+
+hlq_status hlq_workspace_layout_query(int64_t T, int64_t I, int64_t O, int block,
+                                      int rank, hlq_workspace_layout* out) {
+  if (!out) return HLQ_ERR_NULL;
+  hlq_status st = check_shape(T, I, O, block, rank);
+  if (st != HLQ_OK) return st;
+  *out = make_layout(T, I, O, block, rank).pub;
+  return HLQ_OK;
+}
+
+hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
+                                     const uint8_t* x_codes, const float* x_scales,
+                                     const void* w, int w_dtype, int64_t T, int64_t I,
+                                     int64_t O, int block, int rank, int gx_mode,
+                                     int gw_mode, int reduction, float* g_x, float* g_w,
+                                     void* workspace, size_t workspace_bytes,
+                                     uint32_t step_mask, void* stream) {
+  if (!g_y || !x_codes || !x_scales || !w || !g_x || !g_w) return HLQ_ERR_NULL;
+  if ((gy_dtype != HLQ_F32 && gy_dtype != HLQ_BF16) ||
+      (w_dtype != HLQ_F32 && w_dtype != HLQ_BF16))
+    return HLQ_ERR_DTYPE;
+  hlq_status st = check_shape(T, I, O, block, rank);
+  if (st != HLQ_OK) return st;
+  if ((gx_mode != HLQ_PER_TOKEN && gx_mode != HLQ_PER_TENSOR) ||
+      (gw_mode != HLQ_PER_TOKEN && gw_mode != HLQ_PER_TENSOR) ||
+      (reduction != HLQ_SUM && reduction != HLQ_MEAN))
+    return HLQ_ERR_MODE;
+  const Layout L = make_layout(T, I, O, block, rank);
+  if (!workspace || workspace_bytes < L.pub.total) return HLQ_ERR_WORKSPACE;
+  if (!aligned16(g_y) || !aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w) ||
+      !aligned16(g_x) || !aligned16(g_w) || !aligned16(workspace))
+    return HLQ_ERR_ALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* q_gy = ws + L.pub.q_gy;
+  float* s_gy = reinterpret_cast<float*>(ws + L.pub.s_gy);
+  uint8_t* q_w = ws + L.pub.q_w;
+  float* s_w = reinterpret_cast<float*>(ws + L.pub.s_w);
+  uint8_t* q_gyl = ws + L.pub.q_gyl;
+  float* s_gyl = reinterpret_cast<float*>(ws + L.pub.s_gyl);
+  uint8_t* q_xl = ws + L.pub.q_xl;
+  float* s_xl = reinterpret_cast<float*>(ws + L.pub.s_xl);
+  uint32_t* colmax_w = reinterpret_cast<uint32_t*>(ws + L.maxes);
+  uint32_t* colmax_gyl = colmax_w + I;
+  uint32_t* colmax_xl = colmax_gyl + O;
+  uint32_t* gmax = colmax_xl + I;  // [0] H.g_y  [1] H.w  [2] low-rank g_y  [3] low-rank x
+  int32_t* partial = reinterpret_cast<int32_t*>(ws + L.partial);
+  const int64_t kxb = L.pub.kx_pitch, kwb = L.pub.kw_pitch, tl = L.pub.t_low;
+  const bool gx_tok = gx_mode == HLQ_PER_TOKEN;
+  const bool gw_tok = gw_mode == HLQ_PER_TOKEN;
+  const hlq::HlaSource gy_src = gy_dtype == HLQ_F32 ? hlq::SRC_F32 : hlq::SRC_BF16;
+  auto on = [&](int step) { return (step_mask >> step) & 1u; };
+
+  if (on(HLQ_STEP_CLEAR)) {
+    HLQ_TRY(hlq::launch_fill_u32(colmax_w, I + O + I + 4, 0u, s));
+    HLQ_TRY(hlq::launch_zero_pad(q_w, I, kxb, O / 2, s));
+    HLQ_TRY(hlq::launch_zero_pad(q_gyl, O, kwb, tl, s));
+    HLQ_TRY(hlq::launch_zero_pad(q_xl, I, kwb, tl, s));
+  }
+  if (on(HLQ_STEP_GX_A_MAX) && !gx_tok)
+    HLQ_TRY(hlq::launch_rows(g_y, gy_dtype, T, O, block, kxb, q_gy, s_gy, gmax + 0,
+                             hlq::ABS_ONLY, s));
+  if (on(HLQ_STEP_GX_A_QUANT))
+    HLQ_TRY(hlq::launch_rows(g_y, gy_dtype, T, O, block, kxb, q_gy, s_gy, gmax + 0,
+                             gx_tok ? hlq::QUANT_OWN : hlq::QUANT_GLOBAL, s));
+  if (on(HLQ_STEP_GX_B_MAX))
+    HLQ_TRY(hlq::launch_cols(w, w_dtype, O, I, block, kxb, q_w, s_w, colmax_w, gmax + 1,
+                             hlq::ABS_ONLY, s));
+  if (on(HLQ_STEP_GX_B_QUANT))
+    HLQ_TRY(hlq::launch_cols(w, w_dtype, O, I, block, kxb, q_w, s_w, colmax_w, gmax + 1,
+                             gx_tok ? hlq::QUANT_OWN : hlq::QUANT_GLOBAL, s));
+  if (on(HLQ_STEP_GW_A_MAX))
+    HLQ_TRY(hlq::launch_hla(g_y, nullptr, gy_src, T, O, block, rank, kwb, q_gyl, s_gyl,
+                            colmax_gyl, gmax + 2, hlq::ABS_ONLY, s));
+  if (on(HLQ_STEP_GW_A_QUANT))
+    HLQ_TRY(hlq::launch_hla(g_y, nullptr, gy_src, T, O, block, rank, kwb, q_gyl, s_gyl,
+                            colmax_gyl, gmax + 2,
+                            gw_tok ? hlq::QUANT_OWN : hlq::QUANT_GLOBAL, s));
+  if (on(HLQ_STEP_GW_B_MAX))
+    HLQ_TRY(hlq::launch_hla(x_codes, x_scales, hlq::SRC_INT4, T, I, block, rank, kwb, q_xl,
+                            s_xl, colmax_xl, gmax + 3, hlq::ABS_ONLY, s));
+  if (on(HLQ_STEP_GW_B_QUANT))
+    HLQ_TRY(hlq::launch_hla(x_codes, x_scales, hlq::SRC_INT4, T, I, block, rank, kwb, q_xl,
+                            s_xl, colmax_xl, gmax + 3,
+                            gw_tok ? hlq::QUANT_OWN : hlq::QUANT_GLOBAL, s));
+  const float inv_n = 1.0f / (float)block;
+  if (on(HLQ_STEP_GEMM_GX))  // g_x = acc * s_gy[t] * s_w[i] / n
+    HLQ_TRY(hlq::launch_gemm(true, q_gy, q_w, T, I, kxb, L.plan_gx, s_gy, gx_tok ? 1 : 0,
+                             s_w, gx_tok ? 1 : 0, inv_n, hlq::EPI_F32, g_x, nullptr,
+                             partial, s));
+  if (on(HLQ_STEP_GEMM_GW)) {  // g_w = acc * s_gyl[o] * s_xl[i] / n  (/ T)
+    const float alpha =
+        reduction == HLQ_MEAN ? (float)(1.0 / ((double)block * (double)T)) : inv_n;
+    HLQ_TRY(hlq::launch_gemm(false, q_gyl, q_xl, O, I, kwb, L.plan_gw, s_gyl,
+                             gw_tok ? 1 : 0, s_xl, gw_tok ? 1 : 0, alpha, hlq::EPI_F32,
+                             g_w, nullptr, partial, s));
+  }
+  return HLQ_OK;
+}
+
+hlq_status hlq_linear_backward(const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                               const float* x_scales, const void* w, int w_dtype,
+                               int64_t T, int64_t I, int64_t O, int block, int rank,
+                               int gx_mode, int gw_mode, int reduction, float* g_x,
+                               float* g_w, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return hlq_linear_backward_steps(g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O,
+                                   block, rank, gx_mode, gw_mode, reduction, g_x, g_w,
+                                   workspace, workspace_bytes, HLQ_STEPS_ALL, stream);
+}
+
+hlq_status hlq_gemm_gx_acc(const void* workspace, int64_t T, int64_t I, int64_t O,
+                           int block, int rank, int32_t* acc_x, void* stream) {
+  if (!workspace || !acc_x) return HLQ_ERR_NULL;
+  hlq_status st = check_shape(T, I, O, block, rank);
+  if (st != HLQ_OK) return st;
+  if (!aligned16(workspace) || !aligned16(acc_x)) return HLQ_ERR_ALIGN;
+  const Layout L = make_layout(T, I, O, block, rank);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  HLQ_TRY(hlq::launch_gemm(true, ws + L.pub.q_gy, ws + L.pub.q_w, T, I, L.pub.kx_pitch,
+                           L.plan_gx, nullptr, 0, nullptr, 0, 1.f, hlq::EPI_I32, nullptr,
+                           acc_x, nullptr, static_cast<hipStream_t>(stream)));
+  return HLQ_OK;
+}
+
+hlq_status hlq_gemm_gw_acc(const void* workspace, int64_t T, int64_t I, int64_t O,
+                           int block, int rank, int32_t* acc_w, void* stream) {
+  if (!workspace || !acc_w) return HLQ_ERR_NULL;
+  hlq_status st = check_shape(T, I, O, block, rank);
+  if (st != HLQ_OK) return st;
+  if (!aligned16(workspace) || !aligned16(acc_w)) return HLQ_ERR_ALIGN;
+  const Layout L = make_layout(T, I, O, block, rank);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  HLQ_TRY(hlq::launch_gemm(false, ws + L.pub.q_gyl, ws + L.pub.q_xl, O, I, L.pub.kw_pitch,
+                           L.plan_gw, nullptr, 0, nullptr, 0, 1.f, hlq::EPI_I32, nullptr,
+                           acc_w, nullptr, static_cast<hipStream_t>(stream)));
+  return HLQ_OK;
+}
+
+}  // extern "C"

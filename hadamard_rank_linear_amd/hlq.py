@@ -1,0 +1,210 @@
+"""Python binding of libhlq.so, the gfx950 HLQ/HOT linear-layer backward.
+
+Argument marshalling only: every step of the backward runs in the HIP kernels
+behind the C ABI declared in ``include/hlq.h``.  torch supplies device memory
+and the current stream.  Importing fails loudly when the library has not been
+built (``python -m hadamard_rank_linear_amd.build``); there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhlq.so")
+
+HLQ_F32, HLQ_BF16 = 0, 1
+HLQ_PER_TOKEN, HLQ_PER_TENSOR = 0, 1
+HLQ_SUM, HLQ_MEAN = 0, 1
+STEP_NAMES = ("clear", "gx_a_max", "gx_a_quant", "gx_b_max", "gx_b_quant", "gw_a_max",
+              "gw_a_quant", "gw_b_max", "gw_b_quant", "gemm_gx", "gemm_gw")
+HLQ_STEPS_ALL = (1 << len(STEP_NAMES)) - 1
+
+EXPORTED = (
+    "hlq_compress_act",
+    "hlq_linear_backward_workspace_size",
+    "hlq_linear_backward",
+    "hlq_linear_backward_steps",
+    "hlq_workspace_layout_query",
+    "hlq_gemm_gx_acc",
+    "hlq_gemm_gw_acc",
+    "hlq_status_string",
+    "hlq_version",
+)
+
+
+class HLQError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: status {status}: {text}")
+        self.status = status
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("q_gy", "s_gy", "q_w", "s_w", "q_gyl", "s_gyl", "q_xl", "s_xl")] + [
+        ("kx_pitch", ctypes.c_int64), ("kw_pitch", ctypes.c_int64),
+        ("t_low", ctypes.c_int64), ("total", ctypes.c_size_t),
+        ("partial", ctypes.c_size_t), ("partial_bytes", ctypes.c_size_t),
+        ("gx_splits", ctypes.c_int32), ("gw_splits", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m hadamard_rank_linear_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.hlq_compress_act.argtypes = [P, I32, I64, I64, P, P, P]
+    lib.hlq_compress_act.restype = I32
+    lib.hlq_linear_backward_workspace_size.argtypes = [I64, I64, I64, I32, I32]
+    lib.hlq_linear_backward_workspace_size.restype = SZ
+    lib.hlq_linear_backward.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I32, I32,
+                                        I32, I32, I32, P, P, P, SZ, P]
+    lib.hlq_linear_backward.restype = I32
+    lib.hlq_linear_backward_steps.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I32, I32,
+                                              I32, I32, I32, P, P, P, SZ, ctypes.c_uint32, P]
+    lib.hlq_linear_backward_steps.restype = I32
+    lib.hlq_workspace_layout_query.argtypes = [I64, I64, I64, I32, I32,
+                                               ctypes.POINTER(WorkspaceLayout)]
+    lib.hlq_workspace_layout_query.restype = I32
+    lib.hlq_gemm_gx_acc.argtypes = [P, I64, I64, I64, I32, I32, P, P]
+    lib.hlq_gemm_gx_acc.restype = I32
+    lib.hlq_gemm_gw_acc.argtypes = [P, I64, I64, I64, I32, I32, P, P]
+    lib.hlq_gemm_gw_acc.restype = I32
+    lib.hlq_status_string.argtypes = [I32]
+    lib.hlq_status_string.restype = ctypes.c_char_p
+    lib.hlq_version.argtypes = []
+    lib.hlq_version.restype = I32
+    return lib
+
+
+_lib = _load()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise HLQError(fn, status, _lib.hlq_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return HLQ_F32
+    if t.dtype == torch.bfloat16:
+        return HLQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def version() -> int:
+    return _lib.hlq_version()
+
+
+def status_string(status: int) -> str:
+    return _lib.hlq_status_string(status).decode()
+
+
+def hlq_compress_act(x, x_codes=None, x_scales=None, stream=None):
+    """ACBP: x [T, I] (fp32/bf16, GPU) -> (codes uint8 [T, I/2], scales fp32 [T])."""
+    import torch
+    T, I = x.shape
+    if x_codes is None:
+        x_codes = torch.empty((T, I // 2), dtype=torch.uint8, device=x.device)
+    if x_scales is None:
+        x_scales = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _require_cuda(x, x_codes, x_scales)
+    _check("hlq_compress_act", _lib.hlq_compress_act(
+        _ptr(x), _dtype_code(x), T, I, _ptr(x_codes), _ptr(x_scales), _stream(stream)))
+    return x_codes, x_scales
+
+
+def hlq_linear_backward_workspace_size(T, I, O, block, rank) -> int:
+    return int(_lib.hlq_linear_backward_workspace_size(T, I, O, block, rank))
+
+
+def hlq_workspace_layout_query(T, I, O, block, rank) -> dict:
+    out = WorkspaceLayout()
+    _check("hlq_workspace_layout_query",
+           _lib.hlq_workspace_layout_query(T, I, O, block, rank, ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in WorkspaceLayout._fields_}
+
+
+def hlq_linear_backward(g_y, x_codes, x_scales, w, block, rank,
+                        gx_mode=HLQ_PER_TOKEN, gw_mode=HLQ_PER_TOKEN, reduction=HLQ_SUM,
+                        g_x=None, g_w=None, workspace=None, stream=None, steps=None):
+    """HLQ/HOT backward: returns (g_x [T, I], g_w [O, I]) fp32.
+
+    g_y [T, O] and w [O, I] are fp32 or bf16; (x_codes, x_scales) come from
+    :func:`hlq_compress_act`.  ``workspace`` is a uint8 GPU tensor of at least
+    :func:`hlq_linear_backward_workspace_size` bytes; it is allocated here when
+    omitted.  ``steps`` (a bit mask over :data:`STEP_NAMES`) restricts the call
+    to those launches (``hlq_linear_backward_steps``).
+    """
+    import torch
+    T, O = g_y.shape
+    O2, I = w.shape
+    if O2 != O:
+        raise ValueError("w must be [O, I] with O = g_y.shape[1]")
+    dev = g_y.device
+    if g_x is None:
+        g_x = torch.empty((T, I), dtype=torch.float32, device=dev)
+    if g_w is None:
+        g_w = torch.empty((O, I), dtype=torch.float32, device=dev)
+    need = hlq_linear_backward_workspace_size(T, I, O, block, rank)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _require_cuda(g_y, x_codes, x_scales, w, g_x, g_w, workspace)
+    args = (_ptr(g_y), _dtype_code(g_y), _ptr(x_codes), _ptr(x_scales), _ptr(w),
+            _dtype_code(w), T, I, O, block, rank, gx_mode, gw_mode, reduction, _ptr(g_x),
+            _ptr(g_w), _ptr(workspace), workspace.numel() * workspace.element_size())
+    if steps is None:
+        _check("hlq_linear_backward", _lib.hlq_linear_backward(*args, _stream(stream)))
+    else:
+        _check("hlq_linear_backward_steps",
+               _lib.hlq_linear_backward_steps(*args, steps, _stream(stream)))
+    return g_x, g_w
+
+
+def hlq_gemm_gx_acc(workspace, T, I, O, block, rank, acc_x=None, stream=None):
+    import torch
+    if acc_x is None:
+        acc_x = torch.empty((T, I), dtype=torch.int32, device=workspace.device)
+    _require_cuda(workspace, acc_x)
+    _check("hlq_gemm_gx_acc", _lib.hlq_gemm_gx_acc(
+        _ptr(workspace), T, I, O, block, rank, _ptr(acc_x), _stream(stream)))
+    return acc_x
+
+
+def hlq_gemm_gw_acc(workspace, T, I, O, block, rank, acc_w=None, stream=None):
+    import torch
+    if acc_w is None:
+        acc_w = torch.empty((O, I), dtype=torch.int32, device=workspace.device)
+    _require_cuda(workspace, acc_w)
+    _check("hlq_gemm_gw_acc", _lib.hlq_gemm_gw_acc(
+        _ptr(workspace), T, I, O, block, rank, _ptr(acc_w), _stream(stream)))
+    return acc_w
+
+
+def lib_handle():
+    """The loaded ctypes library (for tests of the raw C ABI)."""
+    return _lib

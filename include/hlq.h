@@ -1,0 +1,209 @@
+/*
+ * hlq.h - C ABI of the HLQ/HOT linear-layer backward on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method: "HLQ: Fast and Efficient Backpropagation via Hadamard Low-rank
+ * Quantization" (Kim, Park; arXiv 2406.15102), TL;DR, and "HOT:
+ * Hadamard-based Optimized Training" (HF paper page abstract; scime.ai summary,
+ * section "Approach").  For y = x . w^T the backward needs
+ *     g_x = g_y . w            (T x I)
+ *     g_w = g_y^T . x          (O x I)
+ * g_x runs through 4-bit Hadamard quantization along O; g_w through a
+ * Hadamard low-rank approximation along the token dimension T followed by
+ * INT8 quantization; x is kept as INT4 from the forward pass (activation
+ * buffer compression, ACBP); per-token or per-tensor scales are chosen per
+ * path (layer-wise quantizer selection).
+ *
+ * Conventions for every entry point
+ *  - Data pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or keeps them.  Matrices are row-major and densely
+ *    packed.  Every data pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it and return; nothing is synchronised.  A kernel fault
+ *    surfaces at the caller's next synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error no work is enqueued and outputs are untouched.
+ *  - Thread-safe for distinct (stream, workspace) pairs.  Outputs must not
+ *    alias inputs or the workspace.
+ *  - Hadamard blocks are aligned and non-overlapping; the transform is the
+ *    unnormalised Sylvester matrix H[i][j] = (-1)^popcount(i&j), applied with
+ *    fp32 radix-2 butterflies in ascending stage order; the normalising 1/n is
+ *    applied once in the GEMM epilogue.
+ *  - Quantizer: symmetric absmax; for a scale group with maximum magnitude a,
+ *    scale s = fl(a/qmax), code q = clamp(rne(fl(v * fl(qmax/a))), +-qmax);
+ *    a == 0 gives s = 0 and all codes 0.  qmax = 7 (INT4) or 127 (INT8).
+ */
+#ifndef HLQ_H
+#define HLQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hlq_status {
+  HLQ_OK = 0,
+  HLQ_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  HLQ_ERR_SHAPE = 2,     /* T, I or O non-positive or not a required multiple */
+  HLQ_ERR_BLOCK = 3,     /* block not in {16, 32, 64, 128}                    */
+  HLQ_ERR_RANK = 4,      /* rank not a power of two in [1, block]             */
+  HLQ_ERR_MODE = 5,      /* quantizer mode or reduction out of range          */
+  HLQ_ERR_DTYPE = 6,     /* dtype code out of range                           */
+  HLQ_ERR_ALIGN = 7,     /* a data pointer is not 16-byte aligned             */
+  HLQ_ERR_OVERFLOW = 8,  /* an INT32 accumulator could overflow              */
+  HLQ_ERR_WORKSPACE = 9, /* workspace NULL or smaller than required           */
+  HLQ_ERR_HIP = 10       /* the HIP runtime refused a launch                  */
+} hlq_status;
+
+/* Element type of g_y, w and of the forward activation x. */
+enum { HLQ_F32 = 0, HLQ_BF16 = 1 };
+/* Scale granularity per path (layer-wise quantizer selection, HOT). */
+enum { HLQ_PER_TOKEN = 0, HLQ_PER_TENSOR = 1 };
+/* Reduction of g_w: MEAN multiplies g_w by 1/T (the "1/B" of the HLQ TL;DR
+   identity for g_w, read as a mean over tokens). */
+enum { HLQ_SUM = 0, HLQ_MEAN = 1 };
+
+/*
+ * ACBP - activation buffer compression (HLQ TL;DR: int4 activation
+ * compression; HOT summary, "Approach": stored activations compressed at
+ * forward time).
+ *   x        [T][I] f32 or bf16 (x_dtype), the layer input.
+ *   x_codes  [T][I/2] bytes out: two's-complement INT4 codes, element 2k in
+ *            bits 3:0 and element 2k+1 in bits 7:4 of byte k.
+ *   x_scales [T] f32 out: one scale per token (qmax 7).
+ * Requires T >= 1, I >= 8, I % 8 == 0.
+ */
+hlq_status hlq_compress_act(const void* x, int x_dtype, int64_t T, int64_t I,
+                            uint8_t* x_codes, float* x_scales, void* stream);
+
+/*
+ * Bytes of device workspace hlq_linear_backward needs for this shape
+ * (0 if the shape or block/rank is invalid).  Independent of modes/dtypes.
+ */
+size_t hlq_linear_backward_workspace_size(int64_t T, int64_t I, int64_t O,
+                                          int block, int rank);
+
+/*
+ * The HLQ/HOT backward of one linear layer (HLQ TL;DR; HOT summary,
+ * "Approach").
+ *   g_y      [T][O] f32 or bf16 (gy_dtype), upstream gradient.
+ *   x_codes  [T][I/2], x_scales [T]: the ACBP buffer of hlq_compress_act.
+ *   w        [O][I] f32 or bf16 (w_dtype).
+ *   block    Hadamard block n in {16, 32, 64, 128}; T % n == 0, O % n == 0.
+ *   rank     r, power of two, 1 <= r <= n: rows kept per block of n tokens
+ *            on the g_w path (the r lowest-sequency rows, j*n/r).
+ *   gx_mode  HLQ_PER_TOKEN: one scale per token of H.g_y and per input channel
+ *            of H.w; HLQ_PER_TENSOR: one scale per operand.
+ *   gw_mode  HLQ_PER_TOKEN: one scale per output channel of the low-rank g_y
+ *            and per input channel of the low-rank x; HLQ_PER_TENSOR: one each.
+ *   reduction HLQ_SUM or HLQ_MEAN (g_w only).
+ *   g_x      [T][I] f32 out = acc_x * s_gy * s_w / n.
+ *   g_w      [O][I] f32 out = acc_w * s_gyl * s_xl / n  (/ T for MEAN).
+ *   workspace device buffer of at least hlq_linear_backward_workspace_size()
+ *            bytes; holds the quantized operands and scales afterwards (layout
+ *            from hlq_workspace_layout).
+ * Also requires I % 8 == 0 and that no INT32 accumulator can overflow:
+ * O <= 171196 and T*rank/block <= 133143.
+ */
+hlq_status hlq_linear_backward(const void* g_y, int gy_dtype,
+                               const uint8_t* x_codes, const float* x_scales,
+                               const void* w, int w_dtype,
+                               int64_t T, int64_t I, int64_t O,
+                               int block, int rank,
+                               int gx_mode, int gw_mode, int reduction,
+                               float* g_x, float* g_w,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The launches hlq_linear_backward enqueues, in order.  Bit k of a step mask
+ * selects HLQ_STEP k.  HLQ_STEP_GX_A_MAX runs only with gx_mode PER_TENSOR.
+ */
+enum {
+  HLQ_STEP_CLEAR = 0,       /* clear max accumulators, zero operand K padding  */
+  HLQ_STEP_GX_A_MAX = 1,    /* tensor max of H.g_y (along O)                   */
+  HLQ_STEP_GX_A_QUANT = 2,  /* H.g_y -> INT4 codes + scales                    */
+  HLQ_STEP_GX_B_MAX = 3,    /* per-column and tensor max of H.w (along O)      */
+  HLQ_STEP_GX_B_QUANT = 4,  /* H.w -> INT4 codes (transposed) + scales         */
+  HLQ_STEP_GW_A_MAX = 5,    /* maxima of the low-rank g_y (along T)            */
+  HLQ_STEP_GW_A_QUANT = 6,  /* low-rank g_y -> INT8 codes (transposed) + scales */
+  HLQ_STEP_GW_B_MAX = 7,    /* maxima of the low-rank ACBP-decoded x           */
+  HLQ_STEP_GW_B_QUANT = 8,  /* low-rank x -> INT8 codes (transposed) + scales  */
+  HLQ_STEP_GEMM_GX = 9,     /* INT4 GEMM + dequantizing epilogue -> g_x        */
+  HLQ_STEP_GEMM_GW = 10,    /* INT8 GEMM + dequantizing epilogue -> g_w        */
+  HLQ_STEP_COUNT = 11
+};
+#define HLQ_STEPS_ALL 0x7FFu
+
+/*
+ * hlq_linear_backward restricted to the steps whose bit is set in step_mask
+ * (same arguments, same validation).  All steps in one call equal
+ * hlq_linear_backward.  A subset re-runs those launches on a workspace that
+ * the earlier steps have filled (every step is idempotent given its inputs),
+ * which lets a caller time or inspect one kernel of the sequence in place.
+ */
+hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
+                                     const uint8_t* x_codes, const float* x_scales,
+                                     const void* w, int w_dtype,
+                                     int64_t T, int64_t I, int64_t O,
+                                     int block, int rank,
+                                     int gx_mode, int gw_mode, int reduction,
+                                     float* g_x, float* g_w,
+                                     void* workspace, size_t workspace_bytes,
+                                     uint32_t step_mask, void* stream);
+
+/*
+ * Where hlq_linear_backward leaves its intermediates inside the workspace
+ * (byte offsets), for tests and diagnostics.
+ *   q_gy   [T][kx_pitch]  INT4 codes of H.g_y (along O), packed as in ACBP;
+ *          bytes past O/2 in each row are zero.
+ *   s_gy   [T] (PER_TOKEN) or [1] f32.
+ *   q_w    [I][kx_pitch]  INT4 codes of H.w, stored transposed (K = O
+ *          contiguous), packed as above, zero-padded.
+ *   s_w    [I] or [1] f32.
+ *   q_gyl  [O][kw_pitch]  INT8 codes of the low-rank g_y, transposed (K = T'
+ *          contiguous), zero past T' = T*rank/block.
+ *   s_gyl  [O] or [1] f32.
+ *   q_xl   [I][kw_pitch]  INT8 codes of the low-rank x, transposed.
+ *   s_xl   [I] or [1] f32.
+ *   partial  scratch of the split-K GEMMs (contents unspecified).
+ */
+typedef struct hlq_workspace_layout {
+  size_t q_gy, s_gy, q_w, s_w, q_gyl, s_gyl, q_xl, s_xl;
+  int64_t kx_pitch;  /* bytes per row of q_gy and q_w  */
+  int64_t kw_pitch;  /* bytes per row of q_gyl and q_xl */
+  int64_t t_low;     /* T' = T * rank / block           */
+  size_t total;      /* == hlq_linear_backward_workspace_size() */
+  size_t partial;    /* INT32 split-K partial sums shared by both GEMMs */
+  size_t partial_bytes;
+  int32_t gx_splits; /* split-K factor of the g_x GEMM (1 = none) */
+  int32_t gw_splits; /* split-K factor of the g_w GEMM            */
+} hlq_workspace_layout;
+
+hlq_status hlq_workspace_layout_query(int64_t T, int64_t I, int64_t O, int block,
+                                      int rank, hlq_workspace_layout* out);
+
+/*
+ * INT32 accumulators of the two integer GEMMs, recomputed by the same GEMM
+ * kernels from a workspace that hlq_linear_backward has filled (tests and
+ * diagnostics).  acc_x [T][I] = sum_o q_gy[t,o] q_w[o,i];
+ * acc_w [O][I] = sum_t' q_gyl[t',o] q_xl[t',i].
+ */
+hlq_status hlq_gemm_gx_acc(const void* workspace, int64_t T, int64_t I, int64_t O,
+                           int block, int rank, int32_t* acc_x, void* stream);
+hlq_status hlq_gemm_gw_acc(const void* workspace, int64_t T, int64_t I, int64_t O,
+                           int block, int rank, int32_t* acc_w, void* stream);
+
+/* Static text for a status code. */
+const char* hlq_status_string(int status);
+
+/* Library ABI version (major*100 + minor). */
+int hlq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLQ_H */

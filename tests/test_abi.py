@@ -1,0 +1,136 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library loads, exports every function include/hlq.h declares, validates
+arguments before enqueueing anything, and plans a consistent workspace.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hadamard_rank_linear_amd as h
+from hadamard_rank_linear_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hlq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hlq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert set(declared_functions()) == set(h.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(h.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(11):
+        assert h.status_string(s) and h.status_string(s) != "unknown status"
+    assert h.status_string(99) == "unknown status"
+    assert h.version() >= 100
+
+
+def _raw_backward(**kw):
+    args = dict(gy=1 << 20, gy_dt=0, codes=1 << 20, scales=1 << 20, w=1 << 20, w_dt=0,
+                T=64, I=40, O=48, block=16, rank=8, gx=0, gw=0, red=0,
+                g_x=1 << 20, g_w=1 << 20, ws=1 << 20, ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    lib = h.lib_handle()
+    return lib.hlq_linear_backward(*(args[k] for k in (
+        "gy", "gy_dt", "codes", "scales", "w", "w_dt", "T", "I", "O", "block", "rank",
+        "gx", "gw", "red", "g_x", "g_w", "ws", "ws_bytes", "stream")))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gy=None), 1),
+    (dict(g_w=None), 1),
+    (dict(T=0), 2),
+    (dict(T=72), 2),                 # T not a multiple of the block
+    (dict(O=40), 2),                 # O not a multiple of the block
+    (dict(I=36), 2),                 # I not a multiple of 8
+    (dict(block=24), 3),
+    (dict(block=256), 3),
+    (dict(rank=3), 4),
+    (dict(rank=32), 4),              # rank above block
+    (dict(rank=0), 4),
+    (dict(gx=2), 5),
+    (dict(red=7), 5),
+    (dict(gy_dt=3), 6),
+    (dict(w=(1 << 20) + 4), 7),      # misaligned
+    (dict(O=171200, block=16), 8),   # INT4 accumulator could overflow
+    (dict(T=16 * 133144, rank=16), 8),
+    (dict(ws=None), 9),
+    (dict(ws_bytes=100), 9),
+])
+def test_validation_rejects_before_launch(kw, status):
+    # pointers are fake host addresses: validation must refuse before any launch
+    assert _raw_backward(**kw) == status
+
+
+def test_compress_act_validation():
+    lib = h.lib_handle()
+    P = 1 << 20
+    assert lib.hlq_compress_act(None, 0, 4, 8, P, P, None) == 1
+    assert lib.hlq_compress_act(P, 5, 4, 8, P, P, None) == 6
+    assert lib.hlq_compress_act(P, 0, 4, 12, P, P, None) == 2
+    assert lib.hlq_compress_act(P, 0, 0, 8, P, P, None) == 2
+    assert lib.hlq_compress_act(P + 2, 0, 4, 8, P, P, None) == 7
+
+
+@pytest.mark.parametrize("cfg", wl.CONFIGS, ids=[c.name for c in wl.CONFIGS])
+def test_workspace_layout_consistent(cfg):
+    T, I, O, n, r = cfg.T, cfg.I, cfg.O, cfg.block, cfg.rank
+    lay = h.hlq_workspace_layout_query(T, I, O, n, r)
+    size = h.hlq_linear_backward_workspace_size(T, I, O, n, r)
+    assert lay["total"] == size > 0
+    assert lay["t_low"] == T * r // n
+    assert lay["kx_pitch"] % 64 == 0 and lay["kx_pitch"] * 2 >= O
+    assert lay["kw_pitch"] % 64 == 0 and lay["kw_pitch"] >= lay["t_low"]
+    regions = sorted([
+        (lay["q_gy"], T * lay["kx_pitch"]), (lay["s_gy"], 4 * T),
+        (lay["q_w"], I * lay["kx_pitch"]), (lay["s_w"], 4 * I),
+        (lay["q_gyl"], O * lay["kw_pitch"]), (lay["s_gyl"], 4 * O),
+        (lay["q_xl"], I * lay["kw_pitch"]), (lay["s_xl"], 4 * I)])
+    for (a, la), (b, _) in zip(regions, regions[1:]):
+        assert a % 256 == 0 and a + la <= b
+    assert regions[-1][0] + regions[-1][1] <= size
+
+
+SPLIT_SHAPES = [(c.T, c.I, c.O, c.block, c.rank) for c in wl.CONFIGS] + [
+    (64, 40, 48, 16, 16), (96, 72, 96, 32, 1), (256, 136, 192, 64, 8),
+    (256, 64, 128, 128, 128), (384, 96, 256, 128, 32), (208, 264, 160, 16, 2),
+    (64, 64, 4608, 16, 4), (1040, 520, 336, 16, 8), (16, 8, 16384, 16, 16),
+    (65536, 8, 16, 16, 16), (1040, 768, 2304, 16, 8), (1056, 3072, 768, 32, 8),
+    (1024, 14336, 4096, 64, 16), (2064, 2304, 256, 16, 4), (528, 768, 2304, 16, 8)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+def test_split_k_partials_fit(shape):
+    # regression: a split-K GEMM must always have its partial-sum buffer
+    T, I, O, n, r = shape
+    lay = h.hlq_workspace_layout_query(T, I, O, n, r)
+    need = 0
+    if lay["gx_splits"] > 1:
+        need = max(need, lay["gx_splits"] * T * I * 4)
+    if lay["gw_splits"] > 1:
+        need = max(need, lay["gw_splits"] * O * I * 4)
+    assert lay["partial_bytes"] >= need
+    assert lay["partial"] % 256 == 0
+    assert lay["partial"] + lay["partial_bytes"] <= lay["total"]
+    for other in ("q_gy", "q_w", "q_gyl", "q_xl"):
+        assert lay[other] < lay["partial"] or lay["partial_bytes"] == 0
+
+
+def test_workspace_size_zero_for_invalid_shape():
+    assert h.hlq_linear_backward_workspace_size(64, 40, 48, 24, 8) == 0
+    with pytest.raises(h.HLQError):
+        h.hlq_workspace_layout_query(64, 40, 40, 16, 8)

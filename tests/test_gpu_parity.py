@@ -1,0 +1,143 @@
+"""GPU parity: libhlq.so (gfx950) against the CPU oracle on the same seeded inputs.
+
+Every case prints its name before it touches the GPU.  Shapes span several
+GEMM tiles with ragged M/N/K tails; the layer configs run at reduced token
+counts element by element and at their full sizes (the sizes the benchmark
+times).  The bar: codes, scales and INT32 accumulators bit-exact, fp32 g_x and
+g_w within relative Frobenius error 1e-5.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle as o
+from hadamard_rank_linear_amd import workloads as wl
+from parity_util import compare, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+
+
+def _case(cfg, plant=False, reduction=None, seed=0):
+    _say(f"{cfg.name} T={cfg.T} I={cfg.I} O={cfg.O} n={cfg.block} r={cfg.rank} "
+         f"modes=({cfg.gx_mode},{cfg.gw_mode}) dtype={cfg.dtype} red={reduction} "
+         f"plant={plant} seed={seed}")
+    inp = wl.make_inputs(cfg, seed=seed, plant_zero_rows=plant)
+    ocodes, oscales, ref = run_oracle(cfg, inp, reduction=reduction)
+    gpu = run_gpu(cfg, inp, x_codes=ocodes, x_scales=oscales, reduction=reduction)
+    ex, ew = compare(cfg, gpu, ocodes, oscales, ref)
+    _say(f"ok rel_fro g_x={ex:.2e} g_w={ew:.2e}")
+
+
+# ----------------------------------------------------------------- tiny layer
+
+def test_tiny_config_exact():
+    _case(wl.CONFIGS[0])
+
+
+def test_tiny_mean_reduction():
+    _case(wl.CONFIGS[0], reduction=wl.MEAN)
+
+
+@pytest.mark.parametrize("gx_mode,gw_mode", [(0, 1), (1, 0), (1, 1)])
+def test_tiny_mode_combinations(gx_mode, gw_mode):
+    _case(dataclasses.replace(wl.CONFIGS[0], gx_mode=gx_mode, gw_mode=gw_mode))
+
+
+def test_tiny_zero_groups():
+    # planted all-zero token / weight row: scale 0 and codes 0 on every path
+    _case(wl.CONFIGS[0], plant=True)
+    _case(dataclasses.replace(wl.CONFIGS[0], gx_mode=1, gw_mode=1), plant=True)
+
+
+# ----------------------------------------------- block sizes, ranks, tails
+
+SHAPES = [
+    # (T, I, O, n, r, dtype)
+    (64, 40, 48, 16, 16, wl.F32),       # N tail (I=40), K=48 padded to 128
+    (96, 72, 96, 32, 1, wl.BF16),       # rank 1
+    (256, 136, 192, 64, 8, wl.BF16),
+    (256, 64, 128, 128, 128, wl.F32),   # full rank at the largest block
+    (384, 96, 256, 128, 32, wl.BF16),
+    (208, 264, 160, 16, 2, wl.F32),     # M tail (T=208), N tail (264)
+    (64, 64, 4608, 16, 4, wl.BF16),     # rows longer than the register buffer
+    (1040, 520, 336, 16, 8, wl.BF16),   # several tiles, ragged everywhere
+]
+
+
+@pytest.mark.parametrize("T,I,O,n,r,dt", SHAPES)
+@pytest.mark.parametrize("gx_mode,gw_mode", [(0, 0), (1, 1)])
+def test_shapes(T, I, O, n, r, dt, gx_mode, gw_mode):
+    base = wl.CONFIGS[1] if dt == wl.BF16 else wl.CONFIGS[0]
+    cfg = dataclasses.replace(base, T=T, I=I, O=O, block=n, rank=r, dtype=dt,
+                              gx_mode=gx_mode, gw_mode=gw_mode, index=100 + T % 97)
+    _case(cfg)
+
+
+# ----------------------------------------------- layer configs, reduced tokens
+
+REDUCED_T = {1: 1040, 2: 1056, 3: 1024, 4: 2064}
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_layer_config_reduced_tokens(idx):
+    cfg = wl.CONFIGS[idx].with_tokens(REDUCED_T[idx])
+    _case(cfg)
+
+
+# ----------------------------------------------- layer configs, full size
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_layer_config_full_size(idx):
+    _case(wl.CONFIGS[idx])
+
+
+# ----------------------------------------------- behaviour
+
+def test_gpu_acbp_matches_oracle_bf16_and_f32():
+    for cfg in (wl.CONFIGS[0], wl.CONFIGS[1].with_tokens(64)):
+        _say(f"acbp {cfg.name}")
+        inp = wl.make_inputs(cfg, plant_zero_rows=True)
+        import hadamard_rank_linear_amd as h
+        from parity_util import host_f32, to_device
+        codes, scales = h.hlq_compress_act(to_device(inp["x"], cfg.dtype))
+        oc, os_ = o.acbp_pack(host_f32(inp["x"], cfg.dtype))
+        assert np.array_equal(codes.cpu().numpy(), oc)
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
+def test_deterministic_reruns():
+    cfg = wl.CONFIGS[1].with_tokens(528)
+    _say("determinism")
+    inp = wl.make_inputs(cfg)
+    a = run_gpu(cfg, inp, want_acc=False)
+    b = run_gpu(cfg, inp, want_acc=False)
+    assert np.array_equal(a.g_x.view(np.uint32), b.g_x.view(np.uint32))
+    assert np.array_equal(a.g_w.view(np.uint32), b.g_w.view(np.uint32))
+
+
+def test_invalid_arguments_enqueue_nothing():
+    import torch
+    import hadamard_rank_linear_amd as h
+    _say("validation")
+    gy = torch.zeros((64, 48), dtype=torch.float32, device="cuda")
+    w = torch.zeros((48, 40), dtype=torch.float32, device="cuda")
+    codes = torch.zeros((64, 20), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((64,), dtype=torch.float32, device="cuda")
+    gx = torch.full((64, 40), 7.0, device="cuda")
+    gw = torch.full((48, 40), 7.0, device="cuda")
+    with pytest.raises(h.HLQError):
+        h.hlq_linear_backward(gy, codes, sc, w, 24, 8, g_x=gx, g_w=gw)      # bad block
+    with pytest.raises(h.HLQError):
+        h.hlq_linear_backward(gy, codes, sc, w, 16, 3, g_x=gx, g_w=gw)      # bad rank
+    with pytest.raises(h.HLQError):
+        h.hlq_linear_backward(gy, codes, sc, w, 16, 8, gx_mode=2, g_x=gx, g_w=gw)
+    small = torch.zeros((16,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(h.HLQError):
+        h.hlq_linear_backward(gy, codes, sc, w, 16, 8, g_x=gx, g_w=gw, workspace=small)
+    torch.cuda.synchronize()
+    assert (gx == 7.0).all() and (gw == 7.0).all()
