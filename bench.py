@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Per-layer HLQ/HOT backward latency on one MI355X.
+
+One step = one full backward of the layer (hlq_linear_backward: every launch
+of the hot path) on inputs already resident in HBM.  The ACBP compression of x
+happens at forward time; it is timed separately and reported as acbp_us.
+
+Timing: W untimed warm-up steps, then K steps bracketed by
+torch.cuda.synchronize(); the steps rotate over several copies of the
+inputs/outputs/workspace whose total exceeds the 256 MB last-level cache, so
+every step reads its operands from HBM.  A second, instrumented pass records
+HIP events around each launch step (same stream, same rotation) to get
+per-kernel durations; the longest one is reported against its roofline.
+
+The CPU baseline is the oracle (numpy) running the same layer once on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
+LLC_BYTES = 256 << 20
+METRIC = "per-layer BP latency (us) + effective TOPS & % roofline, ViT-B qkv/fc2 shape"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_costs(cfg, dt_bytes):
+    """Algorithmic (ops, bytes) per launch step: each input read once, each
+    output written once."""
+    T, I, O, Tl = cfg.T, cfg.I, cfg.O, cfg.Tl
+    gy = T * O * dt_bytes
+    w = O * I * dt_bytes
+    xc = T * I // 2 + 4 * T
+    return {
+        "gx_a_max": (0, gy),
+        "gx_a_quant": (0, gy + T * O // 2 + 4 * T),
+        "gx_b_max": (0, w),
+        "gx_b_quant": (0, w + I * O // 2 + 4 * I),
+        "gw_a_max": (0, gy),
+        "gw_a_quant": (0, gy + O * Tl + 4 * O),
+        "gw_b_max": (0, xc),
+        "gw_b_quant": (0, xc + I * Tl + 4 * I),
+        "gemm_gx": (2 * T * I * O, T * O // 2 + I * O // 2 + 4 * T + 4 * I + 4 * T * I),
+        "gemm_gw": (2 * O * I * Tl, O * Tl + I * Tl + 4 * O + 4 * I + 4 * O * I),
+    }
+
+
+def ideal_us(ops, nbytes):
+    t_mfma = ops / (INT8_PEAK_TOPS * 1e12) * 1e6
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    return max(t_mfma, t_hbm), ("mfma" if t_mfma > t_hbm else "hbm")
+
+
+class LayerSets:
+    """Rotating device copies of one layer's inputs, outputs and workspace."""
+
+    def __init__(self, cfg, inp, nsets):
+        import torch
+        import hadamard_rank_linear_amd as h
+        self.cfg = cfg
+        dev = torch.device("cuda:0")
+        bf = cfg.dtype == 1
+        import numpy as np
+
+        def dev_t(a):
+            if bf:
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        gy0, x0, w0 = dev_t(inp["gy"]), dev_t(inp["x"]), dev_t(inp["w"])
+        codes0, scales0 = h.hlq_compress_act(x0)
+        self.x0 = x0
+        ws_bytes = h.hlq_linear_backward_workspace_size(cfg.T, cfg.I, cfg.O, cfg.block, cfg.rank)
+        self.sets = []
+        for _ in range(nsets):
+            self.sets.append(dict(
+                gy=gy0.clone(), codes=codes0.clone(), scales=scales0.clone(), w=w0.clone(),
+                g_x=torch.empty((cfg.T, cfg.I), dtype=torch.float32, device=dev),
+                g_w=torch.empty((cfg.O, cfg.I), dtype=torch.float32, device=dev),
+                ws=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)))
+        self.bytes_per_set = sum(t.numel() * t.element_size() for t in self.sets[0].values())
+        del gy0, w0
+        torch.cuda.synchronize()
+
+    def run(self, i, steps=None):
+        import hadamard_rank_linear_amd as h
+        s = self.sets[i % len(self.sets)]
+        c = self.cfg
+        h.hlq_linear_backward(s["gy"], s["codes"], s["scales"], s["w"], c.block, c.rank,
+                              c.gx_mode, c.gw_mode, c.reduction, g_x=s["g_x"], g_w=s["g_w"],
+                              workspace=s["ws"], steps=steps)
+
+
+def time_layer(cfg, inp, steps, warmup, per_kernel=True):
+    import torch
+    import hadamard_rank_linear_amd as h
+    probe = LayerSets(cfg, inp, 1)
+    nsets = max(2, -(-2 * LLC_BYTES // probe.bytes_per_set))
+    del probe
+    torch.cuda.empty_cache()
+    sets = LayerSets(cfg, inp, nsets)
+    log(f"{cfg.name}: {nsets} rotating sets of {sets.bytes_per_set / 1e6:.1f} MB")
+    for i in range(warmup):
+        sets.run(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        sets.run(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    gpu_ms = ev0.elapsed_time(ev1)
+    res = dict(wall_ms_per_step=wall_ms / steps, gpu_ms_per_step=gpu_ms / steps, nsets=nsets)
+
+    # ACBP (forward time) on the same rotation scheme
+    xs = [sets.x0.clone() for _ in range(nsets)]
+    codes = [s["codes"] for s in sets.sets]
+    scales = [s["scales"] for s in sets.sets]
+    for i in range(warmup):
+        h.hlq_compress_act(xs[i % nsets], codes[i % nsets], scales[i % nsets])
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(steps):
+        h.hlq_compress_act(xs[i % nsets], codes[i % nsets], scales[i % nsets])
+    ev1.record()
+    torch.cuda.synchronize()
+    res["acbp_us"] = ev0.elapsed_time(ev1) / steps * 1e3
+    del xs
+
+    if per_kernel:
+        # In-pipeline per-kernel durations: an event before every launch step
+        # of every step, enqueued while a spin kernel holds the GPU so that the
+        # queue is full and no launch gap lands inside a measured interval.
+        active = [k for k in range(len(h.STEP_NAMES)) if not (k == 1 and cfg.gx_mode == 0)]
+        n_inst = min(steps, 20)
+        cal0 = torch.cuda.Event(enable_timing=True)
+        cal1 = torch.cuda.Event(enable_timing=True)
+        cal0.record()
+        torch.cuda._sleep(1 << 20)
+        cal1.record()
+        torch.cuda.synchronize()
+        cycles_per_us = (1 << 20) / max(cal0.elapsed_time(cal1) * 1e3, 1e-3)
+        hold_us = 2000 + n_inst * len(active) * 60
+        torch.cuda._sleep(int(hold_us * cycles_per_us))
+        marks = []
+        for i in range(n_inst):
+            for k in active:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                marks.append((k, e))
+                sets.run(i, steps=1 << k)
+        end = torch.cuda.Event(enable_timing=True)
+        end.record()
+        torch.cuda.synchronize()
+        marks.append((None, end))
+        acc = {k: 0.0 for k in active}
+        for (k, a), (_, b) in zip(marks, marks[1:]):
+            acc[k] += a.elapsed_time(b)
+        res["kernels_us"] = {h.STEP_NAMES[k]: acc[k] / n_inst * 1e3 for k in active}
+        res["instrumented_steps"] = n_inst
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, inp):
+    import numpy as np
+    import oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    f = (lambda a: a) if cfg.dtype == 0 else o.bf16_bits_to_f32
+    gy, x, w = f(inp["gy"]), f(inp["x"]), f(inp["w"])
+    codes, scales = o.acbp_pack(x)
+    t0 = time.perf_counter()
+    o.linear_backward(gy, codes, scales, w, cfg.block, cfg.rank, cfg.gx_mode, cfg.gw_mode,
+                      cfg.reduction)
+    sec = time.perf_counter() - t0
+    return {"value": round(sec * 1e6, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": (f"one full {cfg.name} layer backward (T={cfg.T}, I={cfg.I}, O={cfg.O}) by "
+                       f"the numpy oracle: fp32 transforms/quantizers single-threaded, exact "
+                       f"integer GEMMs as fp64 BLAS on {threads} threads; ACBP excluded"),
+            "seconds": round(sec, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="vitb_qkv")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the fc2 side measurement")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the HLQ/HOT layer backward here runs on a "
+              "single MI355X (no sharding, no collectives); run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hadamard_rank_linear_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    cfg = wl.BY_NAME[args.workload]
+    log(f"generating {cfg.name} inputs")
+    inp = wl.make_inputs(cfg)
+    res = time_layer(cfg, inp, args.steps, args.warmup)
+    lat_us = res["wall_ms_per_step"] * 1e3
+    dt_bytes = 4 if cfg.dtype == 0 else 2
+    costs = step_costs(cfg, dt_bytes)
+    ops_total = 2 * cfg.T * cfg.I * cfg.O + 2 * cfg.Tl * cfg.O * cfg.I
+    ideal_total = sum(ideal_us(*costs[k])[0] for k in res["kernels_us"] if k in costs)
+
+    # dominant kernel against its roofline
+    kname = max((k for k in res["kernels_us"] if k in costs), key=lambda k: res["kernels_us"][k])
+    kus = res["kernels_us"][kname]
+    ops, nbytes = costs[kname]
+    _, bound = ideal_us(ops, nbytes)
+    if bound == "mfma":
+        achieved = ops / (kus * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+    else:
+        achieved = nbytes / (kus * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update(kernel=kname, kernel_us=round(kus, 2), algorithmic_bytes=nbytes,
+                algorithmic_ops=ops, traffic=None)
+
+    extra = {}
+    if not args.no_extra and cfg.name != "vitb_fc2":
+        c2 = wl.BY_NAME["vitb_fc2"]
+        log("side measurement: vitb_fc2")
+        r2 = time_layer(c2, wl.make_inputs(c2), max(10, args.steps // 2), args.warmup,
+                        per_kernel=False)
+        extra["vitb_fc2_us"] = round(r2["wall_ms_per_step"] * 1e3, 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(cfg, inp)
+
+    line = {
+        "metric": METRIC,
+        "value": round(lat_us, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["wall_ms_per_step"], 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "I": cfg.I, "O": cfg.O,
+                   "block": cfg.block, "rank": cfg.rank, "gx_mode": cfg.gx_mode,
+                   "gw_mode": cfg.gw_mode, "input_dtype": "bf16" if cfg.dtype else "f32",
+                   "global_batch": cfg.T, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "gpu_event_us": round(res["gpu_ms_per_step"] * 1e3, 2),
+        "effective_tops": round(ops_total / (lat_us * 1e-6) / 1e12, 1),
+        "layer_roofline_frac": round(ideal_total / lat_us, 4),
+        "acbp_us": round(res["acbp_us"], 2),
+        "kernels_us": {k: round(v, 2) for k, v in res["kernels_us"].items()},
+        "rotating_sets": res["nsets"],
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
