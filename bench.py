@@ -37,20 +37,17 @@ def log(msg):
 
 def step_costs(cfg, dt_bytes):
     """Algorithmic (ops, bytes) per launch step: each input read once, each
-    output written once."""
+    output written once (partial maxima and scale vectors included)."""
     T, I, O, Tl = cfg.T, cfg.I, cfg.O, cfg.Tl
     gy = T * O * dt_bytes
     w = O * I * dt_bytes
     xc = T * I // 2 + 4 * T
+    parts = 4 * (T * -(-O // 128) + O * -(-T // 128) + I * -(-T // 128) + I * -(-O // 128))
     return {
-        "gx_a_max": (0, gy),
-        "gx_a_quant": (0, gy + T * O // 2 + 4 * T),
-        "gx_b_max": (0, w),
-        "gx_b_quant": (0, w + I * O // 2 + 4 * I),
-        "gw_a_max": (0, gy),
-        "gw_a_quant": (0, gy + O * Tl + 4 * O),
-        "gw_b_max": (0, xc),
-        "gw_b_quant": (0, xc + I * Tl + 4 * I),
+        "tr_max": (0, gy + xc + w + parts),
+        "tr_reduce": (0, parts + 4 * (T + O + 2 * I)),
+        "tr_quant": (0, gy + xc + w + T * O // 2 + I * O // 2 + O * Tl + I * Tl
+                     + 4 * (T + O + 2 * I)),
         "gemm_gx": (2 * T * I * O, T * O // 2 + I * O // 2 + 4 * T + 4 * I + 4 * T * I),
         "gemm_gw": (2 * O * I * Tl, O * Tl + I * Tl + 4 * O + 4 * I + 4 * O * I),
     }
@@ -145,7 +142,7 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
         # In-pipeline per-kernel durations: an event before every launch step
         # of every step, enqueued while a spin kernel holds the GPU so that the
         # queue is full and no launch gap lands inside a measured interval.
-        active = [k for k in range(len(h.STEP_NAMES)) if not (k == 1 and cfg.gx_mode == 0)]
+        active = list(range(len(h.STEP_NAMES)))
         n_inst = min(steps, 20)
         cal0 = torch.cuda.Event(enable_timing=True)
         cal1 = torch.cuda.Event(enable_timing=True)

@@ -2,18 +2,16 @@
 // carving and the launch sequence.  Everything here runs on the host; all
 // arithmetic of the method happens in the kernels of hlq_kernels.hip.
 //
-// Launch sequence of hlq_linear_backward (one stream, no host sync; each line
-// is one HLQ_STEP_* of hlq.h):
-//   1. clear the max accumulators, zero the K padding of the stored operands
-//   2. g_x operand A: H along O of g_y rows -> INT4 (per-token, or tensor max
-//      pass then quantize pass)
-//   3. g_x operand B: H along O of w columns -> INT4 transposed (max pass,
-//      quantize pass)
-//   4. g_w operand A: low-rank H along T of g_y -> INT8 transposed (max pass,
-//      quantize pass)
-//   5. g_w operand B: the same for the ACBP-decoded x
-//   6. INT4 GEMM with fused dequantizing epilogue -> g_x
-//   7. INT8 GEMM (split-K partials + finalize when the tile grid is small) -> g_w
+// Launch sequence of hlq_linear_backward (one stream, no host sync; each
+// line is one HLQ_STEP_* of hlq.h):
+//   1. MAX pass of the transform engine over g_y, the ACBP codes of x and w:
+//      partial maxima of H.g_y rows, low-rank g_y / x columns, H.w columns
+//   2. fold the partials: per-token maxima and scales, tensor maxima
+//   3. QUANT pass: the same transforms again, quantized and written as the
+//      GEMM operands (INT4 H.g_y rows, INT4 H.w transposed, INT8 low-rank g_y
+//      and x transposed), K padding zeroed
+//   4. INT4 GEMM with fused dequantizing epilogue -> g_x
+//   5. INT8 GEMM (split-K partials + finalize when the tile grid is small) -> g_w
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -35,8 +33,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Layout {
   hlq_workspace_layout pub;
-  size_t maxes;        // uint32: colmax_w[I], colmax_gyl[O], colmax_xl[I], gmax[4]
-  size_t partial;      // int32 split-K partials of the g_w GEMM
+  size_t part_gy, part_gyl, part_xl, part_w;  // partial maxima of the MAX pass
+  size_t max_gy, max_gyl, max_xl, max_w;      // folded per-token maxima
+  size_t bmax;                                // per-block maxima [4][nred]
+  int64_t nred;
+  size_t partial;                             // int32 split-K partials
+  int64_t nch_o, nch_i, ntr_t, ntr_o;         // transform tile grid
   hlq::GemmPlan plan_gx, plan_gw;
 };
 
@@ -59,8 +61,8 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   L.pub.kx_pitch = kxb;
   L.pub.kw_pitch = kwb;
   L.pub.t_low = t_low;
-  L.plan_gx = hlq::plan_gemm(T, I, kxb);
-  L.plan_gw = hlq::plan_gemm(O, I, kwb);
+  L.plan_gx = hlq::plan_gemm(true, T, I, kxb);
+  L.plan_gw = hlq::plan_gemm(false, O, I, kwb);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -75,7 +77,20 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   L.pub.s_gyl = take((size_t)O * 4);
   L.pub.q_xl = take((size_t)I * kwb);
   L.pub.s_xl = take((size_t)I * 4);
-  L.maxes = take((size_t)(I + O + I + 4) * 4);
+  L.nch_o = (O + hlq::TR_COLS - 1) / hlq::TR_COLS;
+  L.nch_i = (I + hlq::TR_COLS - 1) / hlq::TR_COLS;
+  L.ntr_t = (T + hlq::TR_ROWS - 1) / hlq::TR_ROWS;
+  L.ntr_o = (O + hlq::TR_ROWS - 1) / hlq::TR_ROWS;
+  L.part_gy = take((size_t)L.nch_o * T * 4);
+  L.part_gyl = take((size_t)L.ntr_t * O * 4);
+  L.part_xl = take((size_t)L.ntr_t * I * 4);
+  L.part_w = take((size_t)L.ntr_o * I * 4);
+  L.max_gy = take((size_t)T * 4);
+  L.max_gyl = take((size_t)O * 4);
+  L.max_xl = take((size_t)I * 4);
+  L.max_w = take((size_t)I * 4);
+  L.nred = (T + O + 2 * I + hlq::TR_RED_ENTRIES - 1) / hlq::TR_RED_ENTRIES;
+  L.bmax = take((size_t)4 * L.nred * 4);
   // split-K partials: the two GEMMs run one after the other on one stream and
   // share this buffer
   size_t part = 0;
@@ -170,67 +185,47 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* q_gy = ws + L.pub.q_gy;
-  float* s_gy = reinterpret_cast<float*>(ws + L.pub.s_gy);
-  uint8_t* q_w = ws + L.pub.q_w;
-  float* s_w = reinterpret_cast<float*>(ws + L.pub.s_w);
-  uint8_t* q_gyl = ws + L.pub.q_gyl;
-  float* s_gyl = reinterpret_cast<float*>(ws + L.pub.s_gyl);
-  uint8_t* q_xl = ws + L.pub.q_xl;
-  float* s_xl = reinterpret_cast<float*>(ws + L.pub.s_xl);
-  uint32_t* colmax_w = reinterpret_cast<uint32_t*>(ws + L.maxes);
-  uint32_t* colmax_gyl = colmax_w + I;
-  uint32_t* colmax_xl = colmax_gyl + O;
-  uint32_t* gmax = colmax_xl + I;  // [0] H.g_y  [1] H.w  [2] low-rank g_y  [3] low-rank x
-  int32_t* partial = reinterpret_cast<int32_t*>(ws + L.partial);
-  const int64_t kxb = L.pub.kx_pitch, kwb = L.pub.kw_pitch, tl = L.pub.t_low;
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const bool gx_tok = gx_mode == HLQ_PER_TOKEN;
   const bool gw_tok = gw_mode == HLQ_PER_TOKEN;
-  const hlq::HlaSource gy_src = gy_dtype == HLQ_F32 ? hlq::SRC_F32 : hlq::SRC_BF16;
+
+  hlq::TrArgs a;
+  a.gy = g_y; a.gy_dt = gy_dtype;
+  a.xc = x_codes; a.xs = x_scales;
+  a.w = w; a.w_dt = w_dtype;
+  a.T = T; a.I = I; a.O = O;
+  a.kxb = L.pub.kx_pitch; a.kwb = L.pub.kw_pitch; a.tl = L.pub.t_low;
+  a.gx_tok = gx_tok; a.gw_tok = gw_tok;
+  a.q_gy = ws + L.pub.q_gy; a.q_w = ws + L.pub.q_w;
+  a.q_gyl = ws + L.pub.q_gyl; a.q_xl = ws + L.pub.q_xl;
+  a.s_gy = f32(L.pub.s_gy); a.s_w = f32(L.pub.s_w);
+  a.s_gyl = f32(L.pub.s_gyl); a.s_xl = f32(L.pub.s_xl);
+  a.part_gy = f32(L.part_gy); a.part_gyl = f32(L.part_gyl);
+  a.part_xl = f32(L.part_xl); a.part_w = f32(L.part_w);
+  a.max_gy = f32(L.max_gy); a.max_gyl = f32(L.max_gyl);
+  a.max_xl = f32(L.max_xl); a.max_w = f32(L.max_w);
+  a.bmax = f32(L.bmax);
+  a.nred = L.nred;
+  a.nch_o = L.nch_o; a.nch_i = L.nch_i; a.ntr_t = L.ntr_t; a.ntr_o = L.ntr_o;
+  a.wg_gy = L.ntr_t * L.nch_o;
+  a.wg_x = L.ntr_t * L.nch_i;
+  a.wg_w = L.ntr_o * L.nch_i;
+  int32_t* partial = reinterpret_cast<int32_t*>(ws + L.partial);
   auto on = [&](int step) { return (step_mask >> step) & 1u; };
 
-  if (on(HLQ_STEP_CLEAR)) {
-    HLQ_TRY(hlq::launch_fill_u32(colmax_w, I + O + I + 4, 0u, s));
-    HLQ_TRY(hlq::launch_zero_pad(q_w, I, kxb, O / 2, s));
-    HLQ_TRY(hlq::launch_zero_pad(q_gyl, O, kwb, tl, s));
-    HLQ_TRY(hlq::launch_zero_pad(q_xl, I, kwb, tl, s));
-  }
-  if (on(HLQ_STEP_GX_A_MAX) && !gx_tok)
-    HLQ_TRY(hlq::launch_rows(g_y, gy_dtype, T, O, block, kxb, q_gy, s_gy, gmax + 0,
-                             hlq::ABS_ONLY, s));
-  if (on(HLQ_STEP_GX_A_QUANT))
-    HLQ_TRY(hlq::launch_rows(g_y, gy_dtype, T, O, block, kxb, q_gy, s_gy, gmax + 0,
-                             gx_tok ? hlq::QUANT_OWN : hlq::QUANT_GLOBAL, s));
-  if (on(HLQ_STEP_GX_B_MAX))
-    HLQ_TRY(hlq::launch_cols(w, w_dtype, O, I, block, kxb, q_w, s_w, colmax_w, gmax + 1,
-                             hlq::ABS_ONLY, s));
-  if (on(HLQ_STEP_GX_B_QUANT))
-    HLQ_TRY(hlq::launch_cols(w, w_dtype, O, I, block, kxb, q_w, s_w, colmax_w, gmax + 1,
-                             gx_tok ? hlq::QUANT_OWN : hlq::QUANT_GLOBAL, s));
-  if (on(HLQ_STEP_GW_A_MAX))
-    HLQ_TRY(hlq::launch_hla(g_y, nullptr, gy_src, T, O, block, rank, kwb, q_gyl, s_gyl,
-                            colmax_gyl, gmax + 2, hlq::ABS_ONLY, s));
-  if (on(HLQ_STEP_GW_A_QUANT))
-    HLQ_TRY(hlq::launch_hla(g_y, nullptr, gy_src, T, O, block, rank, kwb, q_gyl, s_gyl,
-                            colmax_gyl, gmax + 2,
-                            gw_tok ? hlq::QUANT_OWN : hlq::QUANT_GLOBAL, s));
-  if (on(HLQ_STEP_GW_B_MAX))
-    HLQ_TRY(hlq::launch_hla(x_codes, x_scales, hlq::SRC_INT4, T, I, block, rank, kwb, q_xl,
-                            s_xl, colmax_xl, gmax + 3, hlq::ABS_ONLY, s));
-  if (on(HLQ_STEP_GW_B_QUANT))
-    HLQ_TRY(hlq::launch_hla(x_codes, x_scales, hlq::SRC_INT4, T, I, block, rank, kwb, q_xl,
-                            s_xl, colmax_xl, gmax + 3,
-                            gw_tok ? hlq::QUANT_OWN : hlq::QUANT_GLOBAL, s));
+  if (on(HLQ_STEP_TR_MAX)) HLQ_TRY(hlq::launch_tr(a, hlq::PASS_MAX, block, rank, s));
+  if (on(HLQ_STEP_TR_REDUCE)) HLQ_TRY(hlq::launch_tr_reduce(a, s));
+  if (on(HLQ_STEP_TR_QUANT)) HLQ_TRY(hlq::launch_tr(a, hlq::PASS_QUANT, block, rank, s));
   const float inv_n = 1.0f / (float)block;
   if (on(HLQ_STEP_GEMM_GX))  // g_x = acc * s_gy[t] * s_w[i] / n
-    HLQ_TRY(hlq::launch_gemm(true, q_gy, q_w, T, I, kxb, L.plan_gx, s_gy, gx_tok ? 1 : 0,
-                             s_w, gx_tok ? 1 : 0, inv_n, hlq::EPI_F32, g_x, nullptr,
-                             partial, s));
+    HLQ_TRY(hlq::launch_gemm(true, a.q_gy, a.q_w, T, I, a.kxb, L.plan_gx, a.s_gy,
+                             gx_tok ? 1 : 0, a.s_w, gx_tok ? 1 : 0, inv_n, hlq::EPI_F32,
+                             g_x, nullptr, partial, s));
   if (on(HLQ_STEP_GEMM_GW)) {  // g_w = acc * s_gyl[o] * s_xl[i] / n  (/ T)
     const float alpha =
         reduction == HLQ_MEAN ? (float)(1.0 / ((double)block * (double)T)) : inv_n;
-    HLQ_TRY(hlq::launch_gemm(false, q_gyl, q_xl, O, I, kwb, L.plan_gw, s_gyl,
-                             gw_tok ? 1 : 0, s_xl, gw_tok ? 1 : 0, alpha, hlq::EPI_F32,
+    HLQ_TRY(hlq::launch_gemm(false, a.q_gyl, a.q_xl, O, I, a.kwb, L.plan_gw, a.s_gyl,
+                             gw_tok ? 1 : 0, a.s_xl, gw_tok ? 1 : 0, alpha, hlq::EPI_F32,
                              g_w, nullptr, partial, s));
   }
   return HLQ_OK;

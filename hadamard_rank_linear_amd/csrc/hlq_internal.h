@@ -8,42 +8,55 @@
 
 namespace hlq {
 
-enum AbsMode { ABS_ONLY = 0, QUANT_OWN = 1, QUANT_GLOBAL = 2 };
-enum HlaSource { SRC_F32 = 0, SRC_BF16 = 1, SRC_INT4 = 2 };
 enum GemmEpi { EPI_F32 = 0, EPI_I32 = 1, EPI_PARTIAL = 2 };
+enum TrPass { PASS_MAX = 0, PASS_QUANT = 1 };
+
+// Rows and columns of one transform tile (see the tile engine in
+// hlq_kernels.hip); the host sizes the partial-maximum arrays with them.
+constexpr int TR_ROWS = 128;
+constexpr int TR_COLS = 128;
+constexpr int TR_RED_ENTRIES = 64;  // entries folded per reduce block
+
+// Everything the three transform launches (MAX, reduce, QUANT) read and write.
+struct TrArgs {
+  const void* gy;  int gy_dt;
+  const uint8_t* xc; const float* xs;
+  const void* w;   int w_dt;
+  int64_t T, I, O, kxb, kwb, tl;
+  int gx_tok, gw_tok;
+  uint8_t *q_gy, *q_w, *q_gyl, *q_xl;
+  float *s_gy, *s_w, *s_gyl, *s_xl;
+  // partial maxima: rows of H.g_y per column chunk [nch_o][T]; low-rank g_y
+  // columns per token range [ntr_t][O]; low-rank x [ntr_t][I]; H.w [ntr_o][I]
+  float *part_gy, *part_gyl, *part_xl, *part_w;
+  // folded maxima (per-token modes)
+  float *max_gy, *max_gyl, *max_xl, *max_w;
+  // per-block maxima of the reduce launch, [4][nred]: list 0 H.g_y, 1 H.w,
+  // 2 low-rank g_y, 3 low-rank x (tensor maxima are folded from these)
+  float* bmax;
+  int64_t nred;  // reduce blocks = ceil((T + O + 2 I) / TR_RED_ENTRIES)
+  int64_t nch_o, nch_i, ntr_t, ntr_o;
+  int64_t wg_gy, wg_x, wg_w;
+};
 
 // Launch configuration of one integer GEMM C[m][n] = sum_k A[m][k] B[n][k],
 // both operands K-contiguous ("NT").
 struct GemmPlan {
+  int cfg;         // tile configuration index (see plan_gemm)
   int bm, bn;      // block tile
   int splits;      // split-K factor (partials summed by gemm_finalize)
-  int64_t stages;  // 64-byte K stages in total
+  int64_t stages;  // K stages in total
 };
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t kbytes);
-
-hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
-hipError_t launch_zero_pad(uint8_t* p, int64_t rows, int64_t pitch, int64_t from,
-                           hipStream_t s);
+GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes);
 
 hipError_t launch_acbp(const void* x, int dtype, int64_t T, int64_t I, uint8_t* codes,
                        float* scales, hipStream_t s);
 
-// H along O of each row of g_y [T][O] -> INT4 rows [T][kxb] (+ scales).
-hipError_t launch_rows(const void* gy, int dtype, int64_t T, int64_t O, int n,
-                       int64_t kxb, uint8_t* q, float* scale, uint32_t* gmax,
-                       AbsMode mode, hipStream_t s);
-
-// H along O of each column of w [O][I] -> INT4 stored [I][kxb] (+ scales).
-hipError_t launch_cols(const void* w, int dtype, int64_t O, int64_t I, int n,
-                       int64_t kxb, uint8_t* q, float* scale, uint32_t* colmax,
-                       uint32_t* gmax, AbsMode mode, hipStream_t s);
-
-// Low-rank H along T of [T][C] -> INT8 stored [C][kwb] (+ scales).
-hipError_t launch_hla(const void* src, const float* src_scale, HlaSource kind,
-                      int64_t T, int64_t C, int n, int r, int64_t kwb, uint8_t* q,
-                      float* scale, uint32_t* colmax, uint32_t* gmax, AbsMode mode,
-                      hipStream_t s);
+// Transform pass over g_y, the ACBP codes of x and w (one grid for all three).
+hipError_t launch_tr(const TrArgs& a, int pass, int n, int r, hipStream_t s);
+// Fold the partial maxima of the MAX pass (per-token maxima, scales, tensor maxima).
+hipError_t launch_tr_reduce(const TrArgs& a, hipStream_t s);
 
 hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
                        int64_t N, int64_t pitch, const GemmPlan& plan,

@@ -105,22 +105,6 @@ __device__ __forceinline__ uint32_t pack8_int4(const int (&q)[8]) {
 __device__ __forceinline__ float inv_of(float a, float qmax) { return a == 0.f ? 0.f : qmax / a; }
 __device__ __forceinline__ float scale_of(float a, float qmax) { return a == 0.f ? 0.f : a / qmax; }
 
-// ------------------------------------------------------------ small utility kernels
-
-__global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
-// Zero bytes [from, pitch) of each of `rows` rows (K padding of GEMM operands).
-__global__ void k_zero_pad(uint8_t* p, int64_t rows, int64_t pitch, int64_t from) {
-  const int64_t w = pitch - from;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows * w) return;
-  int64_t r = i / w, c = i % w;
-  p[r * pitch + from + c] = 0;
-}
-
 // ------------------------------------------------------------ ACBP pack
 // One wave per token row: absmax over the row, then INT4 codes (qmax 7).
 
@@ -153,381 +137,579 @@ __global__ __launch_bounds__(256) void k_acbp(const void* __restrict__ x, int64_
   if (lane == 0) scales[row] = scale_of(a, 7.f);
 }
 
-// ------------------------------------------------------------ g_x operand A
-// Rows of g_y [T][O]: block FWHT along O (n/8 lanes per block, 8 elements per
-// lane), absmax per row, INT4 codes into [T][kxb] with zero K padding.
-// NCH > 0: the transformed row (<= NCH*512 elements) stays in registers;
-// NCH == 0: the second pass reloads and transforms again.
-
-template <int DT, int MODE, int NCH>
-__global__ __launch_bounds__(256) void k_rows(const void* __restrict__ gy, int64_t T,
-                                              int64_t O, int n, int64_t kxb,
-                                              uint8_t* __restrict__ q,
-                                              float* __restrict__ scale,
-                                              uint32_t* __restrict__ gmax) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= T) return;
-  const int lpb = n / 8;
-  const int64_t base = row * O;
-  const int64_t kx = kxb * 2;
-  const int nch = (int)((kx + 511) / 512);
-
-  float buf[NCH > 0 ? NCH : 1][8];
-  float a = 0.f;
-  if constexpr (MODE != QUANT_GLOBAL) {
-    for (int ch = 0; ch < nch; ++ch) {
-      const int64_t c = (int64_t)ch * 512 + lane * 8;
-      float v[8];
-      if (c < O) load8<DT>(gy, base + c, v);
-      else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = 0.f;
-      }
-      fwht8(v);
-      fwht_lanes(v, lane, lpb);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(v[k]));
-      if constexpr (NCH > 0) {
-#pragma unroll
-        for (int cc = 0; cc < NCH; ++cc)
-          if (cc == ch) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) buf[cc][k] = v[k];
-          }
-      }
-    }
-    a = wave_max(a);
-  }
-  if constexpr (MODE == ABS_ONLY) {
-    if (lane == 0) atomicMax(gmax, __float_as_uint(a));
-    return;
-  } else {
-    if constexpr (MODE == QUANT_GLOBAL) a = __uint_as_float(*gmax);
-    const float inv = inv_of(a, 7.f);
-    uint8_t* out = q + row * kxb;
-    for (int ch = 0; ch < nch; ++ch) {
-      const int64_t c = (int64_t)ch * 512 + lane * 8;
-      float v[8];
-      if constexpr (NCH > 0 && MODE == QUANT_OWN) {
-#pragma unroll
-        for (int cc = 0; cc < NCH; ++cc)
-          if (cc == ch) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = buf[cc][k];
-          }
-      } else {
-        if (c < O) load8<DT>(gy, base + c, v);
-        else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = 0.f;
-        }
-        fwht8(v);
-        fwht_lanes(v, lane, lpb);
-      }
-      if (c < kx) {
-        int qq[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) qq[k] = quant1<7>(v[k], inv);
-        *reinterpret_cast<uint32_t*>(out + c / 2) = (c < O) ? pack8_int4(qq) : 0u;
-      }
-    }
-    if (lane == 0) {
-      if constexpr (MODE == QUANT_OWN) scale[row] = scale_of(a, 7.f);
-      else if (row == 0) scale[0] = scale_of(a, 7.f);
-    }
-  }
-}
-
-// ------------------------------------------------------------ g_x operand B
-// Columns of w [O][I]: one thread per column i, a run of SEG = max(n, 64) rows
-// per block row of the grid.  FWHT of n rows in registers; absmax per column
-// (pass ABS_ONLY, into colmax and gmax) or INT4 codes stored transposed into
-// [I][kxb] (pass QUANT_OWN: per-column scale, QUANT_GLOBAL: tensor scale).
-
-template <int DT, int MODE, int N>
-__global__ __launch_bounds__(64) void k_cols(const void* __restrict__ w, int64_t O,
-                                             int64_t I, int64_t kxb, int seg,
-                                             uint8_t* __restrict__ q,
-                                             float* __restrict__ scale,
-                                             uint32_t* __restrict__ colmax,
-                                             uint32_t* __restrict__ gmax) {
-  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  const bool active = i < I;
-  const int64_t ic = active ? i : I - 1;
-  const int64_t o_begin = (int64_t)blockIdx.y * seg;
-  float a = 0.f;
-  float inv = 0.f;
-  if constexpr (MODE == QUANT_OWN) {
-    a = __uint_as_float(colmax[ic]);
-    inv = inv_of(a, 7.f);
-  } else if constexpr (MODE == QUANT_GLOBAL) {
-    a = __uint_as_float(*gmax);
-    inv = inv_of(a, 7.f);
-  }
-  for (int64_t o0 = o_begin; o0 < o_begin + seg && o0 < O; o0 += N) {
-    float v[N];
-#pragma unroll
-    for (int k = 0; k < N; ++k) v[k] = load1<DT>(w, (o0 + k) * I + ic);
-#pragma unroll
-    for (int h = 1; h < N; h <<= 1) {
-#pragma unroll
-      for (int k = 0; k < N; ++k) {
-        if ((k & h) == 0) {
-          float x0 = v[k], x1 = v[k + h];
-          v[k] = x0 + x1;
-          v[k + h] = x0 - x1;
-        }
-      }
-    }
-    if constexpr (MODE == ABS_ONLY) {
-#pragma unroll
-      for (int k = 0; k < N; ++k) a = fmaxf(a, fabsf(v[k]));
-    } else {
-      uint32_t packed[N / 8];
-#pragma unroll
-      for (int g = 0; g < N / 8; ++g) {
-        int qq[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) qq[k] = quant1<7>(v[g * 8 + k], inv);
-        packed[g] = pack8_int4(qq);
-      }
-      if (active) {
-        uint8_t* dst = q + i * kxb + o0 / 2;
-        if constexpr (N == 16) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
-        } else {
-#pragma unroll
-          for (int g = 0; g < N / 8; g += 4)
-            *reinterpret_cast<uint4*>(dst + g * 4) =
-                make_uint4(packed[g], packed[g + 1], packed[g + 2], packed[g + 3]);
-        }
-      }
-    }
-  }
-  if constexpr (MODE == ABS_ONLY) {
-    if (active) atomicMax(colmax + i, __float_as_uint(a));
-    float wm = wave_max(active ? a : 0.f);
-    if (threadIdx.x == 0) atomicMax(gmax, __float_as_uint(wm));
-  } else {
-    if (active && blockIdx.y == 0) {
-      if constexpr (MODE == QUANT_OWN) scale[i] = scale_of(a, 7.f);
-      else if (i == 0) scale[0] = scale_of(a, 7.f);
-    }
-  }
-}
-
-// ------------------------------------------------------------ g_w operands
-// Low-rank Hadamard along T.  In block b of n tokens the kept rows j*(n/r) of
-// H_n equal H_r applied to the r sums of n/r consecutive tokens (the low
-// bits of the row index are zero), so each thread forms those group sums in
-// adjacent-pair tree order (identical fp32 result to the first log2(n/r)
-// butterfly stages) and then applies H_r in registers.
+// ------------------------------------------------------------ operand transforms
+// All four GEMM operands come from one tile engine.  A tile is TT rows x CW
+// columns of a row-major source: g_y [T][O] (rows = tokens), the ACBP codes of
+// x [T][I], or w [O][I] (rows = output features).  Each tile is loaded once
+// with coalesced 16-byte loads (all of a thread's loads issued before any
+// arithmetic) and parked in LDS in its source form - bf16 or fp32 values, or
+// the packed INT4 codes plus one scale per row - with 16-byte LDS writes.
+// Every column is then transformed along the rows by one thread per (column,
+// block) task reading LDS column-wise (consecutive threads take consecutive
+// columns: no bank conflicts):
+//   * g_y and x: the low-rank rows of H_n along tokens (g_w path);
+//   * w: the full H_n along O (g_x path, operand B).
+// g_y rows are also transformed along O in registers while loading (g_x path,
+// operand A): each lane owns 8 consecutive columns, n/8 lanes form a block,
+// butterflies cross lanes with xor shuffles.
 //
-// Block = 32 column chunks (x) * 8 token segments (y); a chunk is CPT
-// consecutive columns, a segment SEGB consecutive blocks of n tokens.
-// ABS_ONLY: per-column maxima -> colmax (atomicMax) and the tensor max ->
-// gmax.  QUANT_*: INT8 codes stored transposed into [C][kwb].
+// Two launches of the same kernel:
+//   MAX:   every tile writes its partial maxima (per row chunk, per column
+//          range) to plain arrays - no atomics;
+//   QUANT: after k_tr_reduce has folded the partials, every tile recomputes
+//          its transforms and writes codes; the transposed operands are
+//          staged in LDS so each column's run of codes leaves in wide stores.
+// Workgroups of the three sources share one grid (g_y first: largest tiles).
+// Keeping the tile in its source form (35 KB for bf16) lets four workgroups
+// share a CU, which the load/transform/store phases need to overlap.
 
-template <int KIND, int CPT>
-__device__ __forceinline__ void hla_load(const void* src, const float* sx, int64_t t,
-                                         int64_t C, int64_t c0, float (&v)[CPT]) {
-  if constexpr (KIND == SRC_INT4) {
-    const uint8_t* p = static_cast<const uint8_t*>(src) + t * (C / 2) + c0 / 2;
-    uint32_t u;
-    if constexpr (CPT == 8) u = *reinterpret_cast<const uint32_t*>(p);
-    else if constexpr (CPT == 4) u = *reinterpret_cast<const uint16_t*>(p);
-    else u = *p;
-    const float s = sx[t];
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      int nib = (int)((u >> (4 * k)) & 0xFu);
-      nib = (nib ^ 8) - 8;
-      v[k] = s * (float)nib;
-    }
-  } else if constexpr (KIND == SRC_BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(src) + t * C + c0;
-    if constexpr (CPT == 8) {
-      uint4 u = *reinterpret_cast<const uint4*>(p);
-      uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[2 * k] = bf16_to_f32(w4[k] & 0xFFFFu);
-        v[2 * k + 1] = bf16_to_f32(w4[k] >> 16);
-      }
-    } else if constexpr (CPT == 4) {
-      uint2 u = *reinterpret_cast<const uint2*>(p);
-      v[0] = bf16_to_f32(u.x & 0xFFFFu); v[1] = bf16_to_f32(u.x >> 16);
-      v[2] = bf16_to_f32(u.y & 0xFFFFu); v[3] = bf16_to_f32(u.y >> 16);
-    } else {
-      uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-      v[0] = bf16_to_f32(u & 0xFFFFu); v[1] = bf16_to_f32(u >> 16);
-    }
-  } else {
-    const float* p = static_cast<const float*>(src) + t * C + c0;
-#pragma unroll
-    for (int k = 0; k < CPT; k += 2) {
-      float2 f = *reinterpret_cast<const float2*>(p + k);
-      v[k] = f.x;
-      v[k + 1] = f.y;
-    }
-  }
-}
+constexpr int TT = TR_ROWS;     // rows per tile
+constexpr int CW = TR_COLS;     // columns per tile
+constexpr int P_F32 = CW + 4;   // LDS pitches (elements); rows stay 16-byte aligned
+constexpr int P_B16 = CW + 8;
+constexpr int P_I4 = CW / 2 + 16;  // bytes: two codes per byte
+constexpr int OUT_BYTES = 128;  // staging bytes per column (>= TT*r/n and TT/2)
 
-template <int R>
-struct HlaLevels {  // stack depth for group sums of up to 128/R tokens
-  static constexpr int value = (R >= 128) ? 1 : (R >= 64) ? 2 : (R >= 32) ? 3 : (R >= 16) ? 4
-                             : (R >= 8) ? 5 : (R >= 4) ? 6 : (R >= 2) ? 7 : 8;
+template <bool F32>
+struct TileSmem {
+  static constexpr int bytes = F32 ? TT * P_F32 * 4 : TT * P_B16 * 2;
 };
 
-template <int KIND, int MODE, int R, int CPT>
-__global__ __launch_bounds__(256) void k_hla(const void* __restrict__ src,
-                                             const float* __restrict__ sx, int64_t T,
-                                             int64_t C, int n, int segb, int64_t kwb,
-                                             uint8_t* __restrict__ q,
-                                             float* __restrict__ scale,
-                                             uint32_t* __restrict__ colmax,
-                                             uint32_t* __restrict__ gmax) {
-  constexpr int LV = HlaLevels<R>::value;
-  __shared__ float red[8][32][CPT];
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int64_t ncc = C / CPT;
-  const int64_t cc = (int64_t)blockIdx.x * 32 + tx;
-  const bool col_ok = cc < ncc;
-  const int64_t c0 = (col_ok ? cc : ncc - 1) * CPT;
-  const int64_t nblk = T / n;
-  const int64_t b_begin = ((int64_t)blockIdx.y * 8 + ty) * segb;
-  const int g = n / R;
-  int logg = 0;
-  while ((1 << logg) < g) ++logg;
-
-  float amax[CPT];
-  float inv[CPT];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    amax[c] = 0.f;
-    inv[c] = 0.f;
+// Column readers: value of (row, c) of the tile as fp32, exactly as the
+// source holds it (bf16 widened; INT4 code times its row scale, one rounding).
+struct RdF32 {
+  const float* t;
+  __device__ __forceinline__ float operator()(int r, int c) const { return t[r * P_F32 + c]; }
+};
+struct RdB16 {
+  const uint16_t* t;
+  __device__ __forceinline__ float operator()(int r, int c) const {
+    return __uint_as_float((uint32_t)t[r * P_B16 + c] << 16);
   }
-  if constexpr (MODE == QUANT_OWN) {
+};
+struct RdI4 {
+  const uint8_t* q;
+  const float* s;
+  __device__ __forceinline__ float operator()(int r, int c) const {
+    const int byte = q[r * P_I4 + (c >> 1)];
+    const int code = __builtin_amdgcn_sbfe(byte, (c & 1) * 4, 4);
+    return s[r] * (float)code;
+  }
+};
+
+// Tensor maximum of list l (0 H.g_y, 1 H.w, 2 low-rank g_y, 3 low-rank x):
+// the max over the per-block maxima k_tr_reduce left (a few hundred floats,
+// L2-resident); every QUANT workgroup folds it itself, so no atomics.  All
+// threads of the workgroup must call it.
+__device__ __forceinline__ float tensor_max(const TrArgs& a, int l) {
+  __shared__ float part[4];
+  float m = 0.f;
+  for (int64_t i = threadIdx.x; i < a.nred; i += 256) m = fmaxf(m, a.bmax[l * a.nred + i]);
+  m = wave_max(m);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
+__device__ __forceinline__ float max_over_16_lanes(float a) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      amax[c] = __uint_as_float(colmax[c0 + c]);
-      inv[c] = inv_of(amax[c], 127.f);
-    }
-  } else if constexpr (MODE == QUANT_GLOBAL) {
-    const float a = __uint_as_float(*gmax);
+  for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
+  return a;
+}
+
+// Butterflies across the lanes of one 16-lane row group (element distance
+// 8*m lives in lane ^ m; m < 16 keeps the exchange inside the group).  The
+// lower lane keeps p + v, the upper lane p - v = p + (-v) (a is the lower
+// lane's value): both exact IEEE adds.
+template <int N>
+__device__ __forceinline__ void fwht_lanes_n(float (&v)[8], int lc) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      amax[c] = a;
-      inv[c] = inv_of(a, 127.f);
+  for (int m = 1; m < N / 8; m <<= 1) {
+    const bool upper = (lc & m) != 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float p = __shfl_xor(v[k], m);
+      v[k] = p + (upper ? -v[k] : v[k]);
     }
   }
+}
 
-  for (int64_t b = b_begin; b < b_begin + segb && b < nblk; ++b) {
-    float gs[R][CPT];
+// Low-rank rows of H_N for one column block: group sums of N/R consecutive
+// rows in adjacent-pair tree order (the first log2(N/R) butterfly stages on
+// the kept rows), then H_R in registers.
+template <int N, int R, class RD>
+__device__ __forceinline__ void lowrank_col(const RD& rd, int r0, int c, float (&g)[R]) {
+  constexpr int G = N / R;
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      float stk[LV][CPT];
-      const int64_t t0 = b * n + (int64_t)j * g;
-      for (int k = 0; k < g; ++k) {
-        float v[CPT];
-        hla_load<KIND, CPT>(src, sx, t0 + k, C, c0, v);
-        const int tz = __builtin_ctz(~(unsigned)k);  // trailing ones of k
+  for (int j = 0; j < R; ++j) {
+    float s[G];
 #pragma unroll
-        for (int l = 0; l < LV - 1; ++l) {
-          if (l < tz) {
+    for (int k = 0; k < G; ++k) s[k] = rd(r0 + j * G + k, c);
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) v[c] = stk[l][c] + v[c];
-          }
-        }
+    for (int h = 1; h < G; h <<= 1)
 #pragma unroll
-        for (int l = 0; l < LV; ++l) {
-          if (l == tz) {
+      for (int k = 0; k < G; k += 2 * h) s[k] = s[k] + s[k + h];
+    g[j] = s[0];
+  }
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) stk[l][c] = v[c];
-          }
-        }
+  for (int h = 1; h < R; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if ((j & h) == 0) {
+        float x0 = g[j], x1 = g[j + h];
+        g[j] = x0 + x1;
+        g[j + h] = x0 - x1;
       }
+}
+
+// Full H_N of one column block.
+template <int N, class RD>
+__device__ __forceinline__ void full_col(const RD& rd, int r0, int c, float (&v)[N]) {
 #pragma unroll
-      for (int l = 0; l < LV; ++l) {
-        if (l == logg) {
+  for (int k = 0; k < N; ++k) v[k] = rd(r0 + k, c);
 #pragma unroll
-          for (int c = 0; c < CPT; ++c) gs[j][c] = stk[l][c];
-        }
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if ((k & h) == 0) {
+        float x0 = v[k], x1 = v[k + h];
+        v[k] = x0 + x1;
+        v[k + h] = x0 - x1;
       }
-    }
+}
+
+// 8 consecutive source elements as raw 16 bytes (bf16) or 32 bytes (fp32).
+struct Raw8 {
+  uint4 a, b;
+};
+__device__ __forceinline__ void load_raw8(const void* base, int dt, int64_t e, Raw8& r) {
+  if (dt == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + e);
+    r.a = p[0];
+    r.b = p[1];
+  } else {
+    r.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+  }
+}
+__device__ __forceinline__ void raw8_to_f32(const Raw8& r, int dt, float (&v)[8]) {
+  if (dt == 0) {
+    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+    v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+    v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+  } else {
+    v[0] = bf16_to_f32(r.a.x & 0xFFFFu); v[1] = bf16_to_f32(r.a.x >> 16);
+    v[2] = bf16_to_f32(r.a.y & 0xFFFFu); v[3] = bf16_to_f32(r.a.y >> 16);
+    v[4] = bf16_to_f32(r.a.z & 0xFFFFu); v[5] = bf16_to_f32(r.a.z >> 16);
+    v[6] = bf16_to_f32(r.a.w & 0xFFFFu); v[7] = bf16_to_f32(r.a.w >> 16);
+  }
+}
+// Park 8 source elements of (row, col..col+7) in the tile (16-byte writes).
+// A fp32 tile widens bf16 exactly; a bf16 tile only ever holds bf16 sources.
+template <bool F32>
+__device__ __forceinline__ void park8(uint8_t* smem, int row, int col, const Raw8& r, int dt) {
+  if constexpr (F32) {
+    float v[8];
+    raw8_to_f32(r, dt, v);
+    float* t = reinterpret_cast<float*>(smem) + row * P_F32 + col;
+    *reinterpret_cast<float4*>(t) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(t + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(smem) + row * P_B16 + col) = r.a;
+  }
+}
+
+// Column maxima of a tile: thread tid covers column tid % CW; the two threads
+// of a column meet in LDS.
+__device__ __forceinline__ void tile_colmax_store(float m, float* red, int tid, int cols,
+                                                  float* dst) {
+  red[tid] = m;
+  __syncthreads();
+  if (tid < CW && tid < cols) dst[tid] = fmaxf(red[tid], red[tid + CW]);
+}
+
+// Store the staged transposed codes: column c of the tile owns `len` bytes at
+// dst + c * pitch (dst already offset to the tile's first K byte).  Byte runs
+// go out in the widest unit that divides both the run and its offset.
+__device__ __forceinline__ void store_staged(const uint8_t (*outs)[OUT_BYTES], int cols,
+                                             int len, uint8_t* dst, int64_t pitch,
+                                             int64_t koff, int tid) {
+  int wdt = 16;
+  while (wdt > 1 && ((len % wdt) || (koff % wdt))) wdt >>= 1;
+  const int per_col = len / wdt;
+  const int total = cols * per_col;
+  for (int i = tid; i < total; i += 256) {
+    const int c = i / per_col, k = (i % per_col) * wdt;
+    uint8_t* d = dst + (int64_t)c * pitch + k;
+    const uint8_t* s = &outs[c][k];
+    if (wdt == 16) *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+    else if (wdt == 8) *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(s);
+    else if (wdt == 4) *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
+    else if (wdt == 2) *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
+    else *d = *s;
+  }
+}
+
+// Zero bytes [from, to) of `cols` rows of a K-major operand (K padding).
+__device__ __forceinline__ void zero_tail(uint8_t* dst, int64_t pitch, int cols, int64_t from,
+                                          int64_t to, int tid) {
+  const int64_t w = to - from;
+  if (w <= 0) return;
+  for (int64_t i = tid; i < (int64_t)cols * w; i += 256) dst[(i / w) * pitch + from + i % w] = 0;
+}
+
+// Column pass, low-rank rows of H_N (g_w operands).  Thread tid owns column
+// c = tid % CW and blocks b = tid / CW + 2t.  MAX: the tile's column maxima ->
+// part[0..cols).  QUANT: INT8 codes (scale from colmax[c], or from tensor
+// list `list` when colmax is null) staged in LDS over the tile (after a
+// barrier) and stored K-contiguous at q[(c0 + c) * pitch + t0 / N * R ...].
+template <int PASS, int N, int R, class RD>
+__device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, uint8_t* smem,
+                                                float* red, int rows, int cols, int64_t c0,
+                                                const float* colmax, int list, float* part,
+                                                uint8_t* q, int64_t pitch, int64_t tl,
+                                                int64_t t0, bool last) {
+  constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;  // tasks per thread
+  constexpr int WPR = (R + 3) / 4;                           // code words per task
+  const int tid = threadIdx.x;
+  const int c = tid % CW;
+  const int nb = rows / N;
+  float inv_c = 0.f;
+  if constexpr (PASS == PASS_QUANT) {
+    const float tmax = colmax ? 0.f : tensor_max(a, list);
+    const float amax = colmax ? (c < cols ? colmax[c0 + c] : 0.f) : tmax;
+    inv_c = inv_of(amax, 127.f);
+  }
+  float cm = 0.f;
+  uint32_t words[TPT][WPR];
 #pragma unroll
-    for (int h = 1; h < R; h <<= 1) {
+  for (int t = 0; t < TPT; ++t) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
-        if ((j & h) == 0) {
+    for (int w = 0; w < WPR; ++w) words[t][w] = 0;
+    const int b = tid / CW + 2 * t;
+    if (b < nb && c < cols) {
+      float g[R];
+      lowrank_col<N, R>(rd, b * N, c, g);
+      if constexpr (PASS == PASS_MAX) {
 #pragma unroll
-          for (int c = 0; c < CPT; ++c) {
-            float x0 = gs[j][c], x1 = gs[j + h][c];
-            gs[j][c] = x0 + x1;
-            gs[j + h][c] = x0 - x1;
-          }
-        }
-      }
-    }
-    if constexpr (MODE == ABS_ONLY) {
-#pragma unroll
-      for (int j = 0; j < R; ++j)
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) amax[c] = fmaxf(amax[c], fabsf(gs[j][c]));
-    } else if (col_ok) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        uint8_t* dst = q + (c0 + c) * kwb + b * R;
-        uint32_t words[(R + 3) / 4];
-#pragma unroll
-        for (int wi = 0; wi < (R + 3) / 4; ++wi) words[wi] = 0;
+        for (int j = 0; j < R; ++j) cm = fmaxf(cm, fabsf(g[j]));
+      } else {
 #pragma unroll
         for (int j = 0; j < R; ++j)
-          words[j / 4] |= (uint32_t)(quant1<127>(gs[j][c], inv[c]) & 0xFF) << (8 * (j % 4));
-        if constexpr (R == 1) *dst = (uint8_t)words[0];
-        else if constexpr (R == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)words[0];
-        else if constexpr (R == 4) *reinterpret_cast<uint32_t*>(dst) = words[0];
-        else if constexpr (R == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
-        else {
+          words[t][j / 4] |= (uint32_t)(quant1<127>(g[j], inv_c) & 0xFF) << (8 * (j % 4));
+      }
+    }
+  }
+  if constexpr (PASS == PASS_MAX) {
+    tile_colmax_store(cm, red, tid, cols, part);
+  } else {
+    uint8_t (*outs)[OUT_BYTES] = reinterpret_cast<uint8_t (*)[OUT_BYTES]>(smem);
+    __syncthreads();  // every thread is done reading the tile
 #pragma unroll
-          for (int wi = 0; wi < R / 4; wi += 4)
-            *reinterpret_cast<uint4*>(dst + wi * 4) =
-                make_uint4(words[wi], words[wi + 1], words[wi + 2], words[wi + 3]);
+    for (int t = 0; t < TPT; ++t) {
+      const int b = tid / CW + 2 * t;
+      if (b < nb && c < cols) {
+        if constexpr (R >= 4) {
+#pragma unroll
+          for (int w = 0; w < WPR; ++w)
+            *reinterpret_cast<uint32_t*>(&outs[c][b * R + 4 * w]) = words[t][w];
+        } else {
+#pragma unroll
+          for (int j = 0; j < R; ++j) outs[c][b * R + j] = (uint8_t)(words[t][0] >> (8 * j));
+        }
+      }
+    }
+    __syncthreads();
+    const int64_t koff = t0 / N * R;
+    store_staged(outs, cols, nb * R, q + c0 * pitch + koff, pitch, koff, tid);
+    if (last) zero_tail(q + c0 * pitch, pitch, cols, tl, pitch, tid);
+  }
+}
+
+// Column pass with the full H_N along the rows (w -> INT4 codes for g_x).
+template <int PASS, int N, class RD>
+__device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint8_t* smem,
+                                             float* red, int rows, int cols, int64_t c0,
+                                             const float* colmax, int list, float* part,
+                                             uint8_t* q, int64_t pitch, int64_t o0, int64_t O,
+                                             bool last) {
+  constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;
+  constexpr int WPT = N / 8;  // code words (8 nibbles) per task
+  const int tid = threadIdx.x;
+  const int c = tid % CW;
+  const int nb = rows / N;
+  float inv_c = 0.f;
+  if constexpr (PASS == PASS_QUANT) {
+    const float tmax = colmax ? 0.f : tensor_max(a, list);
+    const float amax = colmax ? (c < cols ? colmax[c0 + c] : 0.f) : tmax;
+    inv_c = inv_of(amax, 7.f);
+  }
+  float cm = 0.f;
+  uint32_t words[TPT][WPT];
+#pragma unroll
+  for (int t = 0; t < TPT; ++t) {
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) words[t][w] = 0;
+    const int b = tid / CW + 2 * t;
+    if (b < nb && c < cols) {
+      float v[N];
+      full_col<N>(rd, b * N, c, v);
+      if constexpr (PASS == PASS_MAX) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) cm = fmaxf(cm, fabsf(v[k]));
+      } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+          words[t][k / 8] |= (uint32_t)(quant1<7>(v[k], inv_c) & 0xF) << (4 * (k % 8));
+      }
+    }
+  }
+  if constexpr (PASS == PASS_MAX) {
+    tile_colmax_store(cm, red, tid, cols, part);
+  } else {
+    uint8_t (*outs)[OUT_BYTES] = reinterpret_cast<uint8_t (*)[OUT_BYTES]>(smem);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const int b = tid / CW + 2 * t;
+      if (b < nb && c < cols) {
+#pragma unroll
+        for (int w = 0; w < WPT; ++w)
+          *reinterpret_cast<uint32_t*>(&outs[c][b * (N / 2) + 4 * w]) = words[t][w];
+      }
+    }
+    __syncthreads();
+    const int64_t koff = o0 / 2;
+    store_staged(outs, cols, rows / 2, q + c0 * pitch + koff, pitch, koff, tid);
+    if (last) zero_tail(q + c0 * pitch, pitch, cols, O / 2, pitch, tid);
+  }
+}
+
+// ---- job: g_y tile (rows along O for g_x, low-rank columns along T for g_w)
+template <int PASS, int N, int R, bool F32>
+__device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
+  const int tid = threadIdx.x;
+  const int64_t tr = bid / a.nch_o, ch = bid % a.nch_o;
+  const int64_t t0 = tr * TT, c0 = ch * CW;
+  const int rows = (int)(a.T - t0 < TT ? a.T - t0 : TT);
+  const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
+  // 16 rows per sweep, 16 lanes x 8 columns per row
+  constexpr int SW = TT / 16;
+  const int lr = tid >> 4, lc = tid & 15;
+  const int col = lc * 8;
+  Raw8 raw[SW];
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 16 + lr;
+    raw[sw].a = make_uint4(0, 0, 0, 0);
+    raw[sw].b = make_uint4(0, 0, 0, 0);
+    if (row < rows && col < cols) load_raw8(a.gy, a.gy_dt, (t0 + row) * a.O + c0 + col, raw[sw]);
+  }
+  float inv_tensor = 0.f;
+  if constexpr (PASS == PASS_QUANT) {
+    if (!a.gx_tok) inv_tensor = inv_of(tensor_max(a, 0), 7.f);
+  }
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 16 + lr;
+    park8<F32>(smem, row, col, raw[sw], a.gy_dt);
+    float v[8];
+    raw8_to_f32(raw[sw], a.gy_dt, v);
+    fwht8(v);
+    fwht_lanes_n<N>(v, lc);
+    if constexpr (PASS == PASS_MAX) {
+      float m = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+      m = max_over_16_lanes(m);
+      if (lc == 0 && row < rows) a.part_gy[ch * a.T + t0 + row] = m;
+    } else if (row < rows) {
+      const float inv = a.gx_tok ? inv_of(a.max_gy[t0 + row], 7.f) : inv_tensor;
+      int qv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[k] = quant1<7>(v[k], inv);
+      // columns past O inside the chunk are zero -> zero codes (K padding)
+      *reinterpret_cast<uint32_t*>(a.q_gy + (t0 + row) * a.kxb + (c0 + col) / 2) =
+          col < cols ? pack8_int4(qv) : 0u;
+    }
+  }
+  __syncthreads();
+  const bool last = t0 + rows == a.T;
+  if constexpr (F32) {
+    RdF32 rd{reinterpret_cast<const float*>(smem)};
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.max_gyl : nullptr,
+                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.kwb, a.tl, t0, last);
+  } else {
+    RdB16 rd{reinterpret_cast<const uint16_t*>(smem)};
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.max_gyl : nullptr,
+                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.kwb, a.tl, t0, last);
+  }
+}
+
+// ---- job: x tile (ACBP codes, low-rank columns along T for g_w)
+template <int PASS, int N, int R>
+__device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
+  const int tid = threadIdx.x;
+  const int64_t tr = bid / a.nch_i, ch = bid % a.nch_i;
+  const int64_t t0 = tr * TT, c0 = ch * CW;
+  const int rows = (int)(a.T - t0 < TT ? a.T - t0 : TT);
+  const int cols = (int)(a.I - c0 < CW ? a.I - c0 : CW);
+  uint8_t* codes = smem;                                          // [TT][P_I4] bytes
+  float* scales = reinterpret_cast<float*>(smem + TT * P_I4);     // [TT]
+  // 64 code bytes per tile row: 4 lanes x 16 bytes, 64 rows per sweep.  Rows
+  // are I/2 bytes (a multiple of 4, not of 16), so the loads are dwords.
+  constexpr int SW = TT / 64;
+  const int lr = tid >> 2, lq = tid & 3;
+  const int col = lq * 32;
+  uint32_t w4[SW][4];
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 64 + lr;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w4[sw][d] = 0u;
+    if (row < rows && col < cols) {
+      const uint32_t* src =
+          reinterpret_cast<const uint32_t*>(a.xc + (t0 + row) * (a.I / 2) + (c0 + col) / 2);
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        if (col + 8 * d < cols) w4[sw][d] = src[d];
+    }
+  }
+  if (tid < TT) scales[tid] = tid < rows ? a.xs[t0 + tid] : 0.f;
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw)
+    *reinterpret_cast<uint4*>(codes + (sw * 64 + lr) * P_I4 + col / 2) =
+        make_uint4(w4[sw][0], w4[sw][1], w4[sw][2], w4[sw][3]);
+  __syncthreads();
+  RdI4 rd{codes, scales};
+  colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.max_xl : nullptr, 3,
+                              a.part_xl + tr * a.I + c0, a.q_xl, a.kwb, a.tl, t0,
+                              t0 + rows == a.T);
+}
+
+// ---- job: w tile (full H_N along O, INT4 stored transposed for g_x)
+template <int PASS, int N, bool F32>
+__device__ void tr_job_w(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
+  const int tid = threadIdx.x;
+  const int64_t tr = bid / a.nch_i, ch = bid % a.nch_i;
+  const int64_t o0 = tr * TT, c0 = ch * CW;
+  const int rows = (int)(a.O - o0 < TT ? a.O - o0 : TT);
+  const int cols = (int)(a.I - c0 < CW ? a.I - c0 : CW);
+  constexpr int SW = TT / 16;
+  const int lr = tid >> 4, lc = tid & 15;
+  const int col = lc * 8;
+  Raw8 raw[SW];
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 16 + lr;
+    raw[sw].a = make_uint4(0, 0, 0, 0);
+    raw[sw].b = make_uint4(0, 0, 0, 0);
+    if (row < rows && col < cols) load_raw8(a.w, a.w_dt, (o0 + row) * a.I + c0 + col, raw[sw]);
+  }
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) park8<F32>(smem, sw * 16 + lr, col, raw[sw], a.w_dt);
+  __syncthreads();
+  const bool last = o0 + rows == a.O;
+  if constexpr (F32) {
+    RdF32 rd{reinterpret_cast<const float*>(smem)};
+    colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.max_w : nullptr, 1,
+                          a.part_w + tr * a.I + c0, a.q_w, a.kxb, o0, a.O, last);
+  } else {
+    RdB16 rd{reinterpret_cast<const uint16_t*>(smem)};
+    colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.max_w : nullptr, 1,
+                          a.part_w + tr * a.I + c0, a.q_w, a.kxb, o0, a.O, last);
+  }
+}
+
+// F32: the g_y / w tiles hold fp32 (any fp32 source); otherwise bf16.
+template <int PASS, int N, int R, bool F32>
+__global__ __launch_bounds__(256) void k_tr(TrArgs a) {
+  static_assert(TT * P_I4 + TT * 4 <= TileSmem<F32>::bytes, "x tile fits the smem buffer");
+  static_assert(CW * OUT_BYTES <= TileSmem<F32>::bytes, "staging fits the smem buffer");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TileSmem<F32>::bytes];
+  __shared__ float red[256];
+  int64_t bid = blockIdx.x;
+  if constexpr (PASS == PASS_QUANT) {
+    if (bid == 0) {
+      // tensor scales of per-tensor modes (the maxima are final now)
+      const float m0 = a.gx_tok ? 0.f : tensor_max(a, 0);
+      const float m1 = a.gx_tok ? 0.f : tensor_max(a, 1);
+      const float m2 = a.gw_tok ? 0.f : tensor_max(a, 2);
+      const float m3 = a.gw_tok ? 0.f : tensor_max(a, 3);
+      if (threadIdx.x == 0) {
+        if (!a.gx_tok) {
+          a.s_gy[0] = scale_of(m0, 7.f);
+          a.s_w[0] = scale_of(m1, 7.f);
+        }
+        if (!a.gw_tok) {
+          a.s_gyl[0] = scale_of(m2, 127.f);
+          a.s_xl[0] = scale_of(m3, 127.f);
         }
       }
     }
   }
+  if (bid < a.wg_gy) {
+    tr_job_gy<PASS, N, R, F32>(a, bid, smem, red);
+    return;
+  }
+  bid -= a.wg_gy;
+  if (bid < a.wg_x) {
+    tr_job_x<PASS, N, R>(a, bid, smem, red);
+    return;
+  }
+  bid -= a.wg_x;
+  if (bid < a.wg_w) tr_job_w<PASS, N, F32>(a, bid, smem, red);
+}
 
-  if constexpr (MODE == ABS_ONLY) {
+// Fold the partial maxima.  Entry e of each list takes the max over its
+// partials and stores it (per-token modes also store the scale); every block
+// leaves its per-list maximum in bmax[l][block], which QUANT workgroups fold
+// into tensor maxima (tensor_max), so no atomics are needed and the result is
+// schedule-independent.  Lists: T rows of H.g_y, O low-rank g_y columns, I
+// low-rank x columns, I columns of H.w.  A block covers 64 consecutive
+// entries; its 4 waves split each entry's partials (stride 4) so every wave
+// keeps several loads in flight.
+constexpr int RED_ENTRIES = TR_RED_ENTRIES;
+
+__global__ __launch_bounds__(256) void k_tr_reduce(TrArgs a) {
+  __shared__ float wpart[4][RED_ENTRIES];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t e = (int64_t)blockIdx.x * RED_ENTRIES + lane;
+  const int64_t n0 = a.T, n1 = n0 + a.O, n2 = n1 + a.I, n3 = n2 + a.I;
+  const float* p = nullptr;
+  int64_t np = 0, stride = 0;
+  int list = -1;
+  if (e < n0) { list = 0; p = a.part_gy + e; np = a.nch_o; stride = a.T; }
+  else if (e < n1) { list = 2; p = a.part_gyl + (e - n0); np = a.ntr_t; stride = a.O; }
+  else if (e < n2) { list = 3; p = a.part_xl + (e - n1); np = a.ntr_t; stride = a.I; }
+  else if (e < n3) { list = 1; p = a.part_w + (e - n2); np = a.ntr_o; stride = a.I; }
+  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+  int64_t k = wv;
+  for (; k + 12 < np; k += 16) {
+    m0 = fmaxf(m0, p[k * stride]);
+    m1 = fmaxf(m1, p[(k + 4) * stride]);
+    m2 = fmaxf(m2, p[(k + 8) * stride]);
+    m3 = fmaxf(m3, p[(k + 12) * stride]);
+  }
+  for (; k < np; k += 4) m0 = fmaxf(m0, p[k * stride]);
+  wpart[wv][lane] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  __syncthreads();
+  if (wv != 0) return;
+  const float m = fmaxf(fmaxf(wpart[0][lane], wpart[1][lane]), fmaxf(wpart[2][lane], wpart[3][lane]));
+  if (list == 0) {
+    if (a.gx_tok) { a.max_gy[e] = m; a.s_gy[e] = scale_of(m, 7.f); }
+  } else if (list == 2) {
+    if (a.gw_tok) { a.max_gyl[e - n0] = m; a.s_gyl[e - n0] = scale_of(m, 127.f); }
+  } else if (list == 3) {
+    if (a.gw_tok) { a.max_xl[e - n1] = m; a.s_xl[e - n1] = scale_of(m, 127.f); }
+  } else if (list == 1) {
+    if (a.gx_tok) { a.max_w[e - n2] = m; a.s_w[e - n2] = scale_of(m, 7.f); }
+  }
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) red[ty][tx][c] = amax[c];
-    __syncthreads();
-    if (ty == 0) {
-      float bm = 0.f;
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        float m = red[0][tx][c];
-#pragma unroll
-        for (int y = 1; y < 8; ++y) m = fmaxf(m, red[y][tx][c]);
-        if (col_ok) {
-          atomicMax(colmax + c0 + c, __float_as_uint(m));
-          bm = fmaxf(bm, m);
-        }
-      }
-      // ty == 0 is the low half of wave 0: reduce over its 32 lanes
-#pragma unroll
-      for (int m = 16; m >= 1; m >>= 1) bm = fmaxf(bm, __shfl_xor(bm, m));
-      if (tx == 0) atomicMax(gmax, __float_as_uint(bm));
-    }
-  } else {
-    if (col_ok && blockIdx.y == 0 && ty == 0) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        if constexpr (MODE == QUANT_OWN) scale[c0 + c] = scale_of(amax[c], 127.f);
-        else if (c0 + c == 0) scale[0] = scale_of(amax[c], 127.f);
-      }
-    }
+  for (int l = 0; l < 4; ++l) {
+    const float v = wave_max(list == l ? m : 0.f);
+    if (lane == 0) a.bmax[l * a.nred + blockIdx.x] = v;
   }
 }
 
@@ -538,142 +720,214 @@ __global__ __launch_bounds__(256) void k_hla(const void* __restrict__ src,
 // lanes holding 16*code (low nibble shifted up, high nibble masked in place),
 // so the INT32 sum is 256 times the code product sum and is shifted back
 // exactly.  The nibble order inside a lane is permuted the same way for both
-// operands, which leaves the dot product unchanged.
+// operands, which leaves the dot product unchanged.  Operands stay packed in
+// HBM, L2 and LDS: the GEMMs here are limited by operand fetch, so halving
+// the bytes matters more than the widening instructions.
 //
 // v_mfma_i32_16x16x64_i8: operand X (16 rows of D) comes from B's rows (n),
 // operand Y (16 columns of D) from A's rows (m); lane l then holds
 // D[4*(l/16)+e][l%16] = C[m0 + l%16][n0 + 4*(l/16) + e], four consecutive n,
 // which the epilogue stores as one 16-byte vector.
 //
-// 256 threads = 4 waves in a 2x2 grid, wave tile (BM/2) x (BN/2), 64-byte K
-// stages double-buffered in LDS (one barrier per stage).
+// Pipeline: 64*WM*WN threads, wave tile (BM/WM) x (BN/WN), KB-byte K stages
+// double-buffered in LDS (one barrier per stage).  Global loads run P stages
+// ahead in a ring of registers: stage st+1 is written to LDS from register
+// slot (st mod P) at the start of stage st, and that slot is refilled with
+// stage st+1+P.  The stage loop is unrolled by P (static slots, so the ring
+// lives in VGPRs); the last S mod P stages run in a static tail.
+// Workgroups are mapped to tiles XCD-aware: hardware hands consecutive
+// workgroup ids to the 8 XCDs in turn, so each XCD gets a contiguous run of
+// tiles (n fastest) and its L2 serves the A rows those tiles share.
 
-constexpr int KST = 64;        // bytes of K per stage
-constexpr int LROW = KST + 16; // LDS row pitch (padding spreads banks)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ v4i widen_int4(uint2 p) {
-  v4i r;
-  r[0] = (int)((p.x << 4) & 0xF0F0F0F0u);
-  r[1] = (int)(p.x & 0xF0F0F0F0u);
-  r[2] = (int)((p.y << 4) & 0xF0F0F0F0u);
-  r[3] = (int)(p.y & 0xF0F0F0F0u);
-  return r;
+__device__ __forceinline__ void widen_int4x2(u32x4 p, v4i& a, v4i& b) {
+  a[0] = (int)((p[0] << 4) & 0xF0F0F0F0u); a[1] = (int)(p[0] & 0xF0F0F0F0u);
+  a[2] = (int)((p[1] << 4) & 0xF0F0F0F0u); a[3] = (int)(p[1] & 0xF0F0F0F0u);
+  b[0] = (int)((p[2] << 4) & 0xF0F0F0F0u); b[1] = (int)(p[2] & 0xF0F0F0F0u);
+  b[2] = (int)((p[3] << 4) & 0xF0F0F0F0u); b[3] = (int)(p[3] & 0xF0F0F0F0u);
 }
 
-template <int L, int ROWS>
-__device__ __forceinline__ void gemm_gload(uint4 (&r)[L], const uint8_t* __restrict__ P,
-                                           int64_t row0, int64_t rows, int64_t pitch,
-                                           int64_t kb, int tid) {
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const int c = tid + 256 * i;
-    int64_t rr = row0 + (c >> 2);
-    rr = rr < rows ? rr : rows - 1;
-    r[i] = *reinterpret_cast<const uint4*>(P + rr * pitch + kb + (c & 3) * 16);
-  }
+__device__ __forceinline__ bool xcd_tile(int64_t w, int64_t nt_m, int64_t nt_n, int64_t& tm,
+                                         int64_t& tn) {
+  const int64_t total = nt_m * nt_n;
+  const int64_t per = (total + 7) / 8;
+  const int64_t t = (w % 8) * per + w / 8;
+  if (t >= total) return false;
+  tm = t / nt_n;
+  tn = t % nt_n;
+  return true;
 }
 
-template <int L>
-__device__ __forceinline__ void gemm_sstore(const uint4 (&r)[L], uint8_t* lds, int tid) {
+template <bool INT4, int BM, int BN, int WM, int WN, int KB>
+struct GemmShape {
+  static constexpr int NT = 64 * WM * WN, TM = BM / WM / 16, TN = BN / WN / 16;
+  static constexpr int PITCH = KB + 16, CPR = KB / 16;
+  static constexpr int LA = BM * CPR / NT, LB = BN * CPR / NT;
+  static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "tile load split");
+  static_assert(TM >= 1 && TN >= 1, "wave tile smaller than one MFMA tile");
+};
+
+template <bool INT4, int BM, int BN, int WM, int WN, int KB>
+__device__ __forceinline__ void gemm_stage(
+    const uint8_t* as, const uint8_t* bs, int wm, int wn, int fr, int fg,
+    v4i (&acc)[GemmShape<INT4, BM, BN, WM, WN, KB>::TM][GemmShape<INT4, BM, BN, WM, WN, KB>::TN]) {
+  using G = GemmShape<INT4, BM, BN, WM, WN, KB>;
+  constexpr int TM = G::TM, TN = G::TN, PITCH = G::PITCH;
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const int c = tid + 256 * i;
-    *reinterpret_cast<uint4*>(lds + (c >> 2) * LROW + (c & 3) * 16) = r[i];
-  }
-}
-
-template <bool INT4, int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A,
-                                              const uint8_t* __restrict__ B, int64_t M,
-                                              int64_t N, int64_t pitch,
-                                              int64_t stages_per_split,
-                                              const float* __restrict__ sa, int sa_step,
-                                              const float* __restrict__ sb, int sb_step,
-                                              float alpha, float* __restrict__ C,
-                                              int32_t* __restrict__ Ci) {
-  constexpr int TM = BM / 32, TN = BN / 32;   // 16x16 tiles per wave
-  constexpr int LA = BM * KST / 16 / 256;     // 16-byte loads per thread
-  constexpr int LB = BN * KST / 16 / 256;
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * LROW];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * LROW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.x * BM;
-  const int64_t n0 = (int64_t)blockIdx.y * BN;
-  const int64_t kb0 = (int64_t)blockIdx.z * stages_per_split * KST;
-  const int64_t kb1 = kb0 + stages_per_split * KST;
-
-  uint4 ra[LA], rb[LB];
-  v4i acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-  const int fr = lane & 15, fg = lane >> 4;
-  gemm_gload<LA, BM>(ra, A, m0, M, pitch, kb0, tid);
-  gemm_gload<LB, BN>(rb, B, n0, N, pitch, kb0, tid);
-  gemm_sstore<LA>(ra, As[0], tid);
-  gemm_sstore<LB>(rb, Bs[0], tid);
-  __syncthreads();
-  int cur = 0;
-  for (int64_t kb = kb0; kb < kb1; kb += KST) {
-    // prefetch the next stage (the last iteration reloads its own stage, in
-    // bounds, and parks it in the idle buffer)
-    const int64_t kn = kb + KST < kb1 ? kb + KST : kb;
-    gemm_gload<LA, BM>(ra, A, m0, M, pitch, kn, tid);
-    gemm_gload<LB, BN>(rb, B, n0, N, pitch, kn, tid);
-    const uint8_t* as = As[cur];
-    const uint8_t* bs = Bs[cur];
+  for (int kc = 0; kc < KB; kc += 64) {
     if constexpr (INT4) {
+      // 16 packed bytes per lane = 32 codes = two MFMA K-steps
+      v4i ya0[TM], ya1[TM], xb0[TN], xb1[TN];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        v4i ya[TM], xb[TN];
+      for (int i = 0; i < TM; ++i)
+        widen_int4x2(*reinterpret_cast<const u32x4*>(as + (wm * (BM / WM) + i * 16 + fr) * PITCH + kc + fg * 16), ya0[i], ya1[i]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          ya[i] = widen_int4(*reinterpret_cast<const uint2*>(
-              as + (wm * (BM / 2) + i * 16 + fr) * LROW + ks * 32 + fg * 8));
+      for (int j = 0; j < TN; ++j)
+        widen_int4x2(*reinterpret_cast<const u32x4*>(bs + (wn * (BN / WN) + j * 16 + fr) * PITCH + kc + fg * 16), xb0[j], xb1[j]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          xb[j] = widen_int4(*reinterpret_cast<const uint2*>(
-              bs + (wn * (BN / 2) + j * 16 + fr) * LROW + ks * 32 + fg * 8));
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb0[j], ya0[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], ya[i], acc[i][j], 0, 0, 0);
-      }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb1[j], ya1[i], acc[i][j], 0, 0, 0);
     } else {
       v4i ya[TM], xb[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        ya[i] = *reinterpret_cast<const v4i*>(as + (wm * (BM / 2) + i * 16 + fr) * LROW + fg * 16);
+        ya[i] = *reinterpret_cast<const v4i*>(as + (wm * (BM / WM) + i * 16 + fr) * PITCH + kc + fg * 16);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        xb[j] = *reinterpret_cast<const v4i*>(bs + (wn * (BN / 2) + j * 16 + fr) * LROW + fg * 16);
+        xb[j] = *reinterpret_cast<const v4i*>(bs + (wn * (BN / WN) + j * 16 + fr) * PITCH + kc + fg * 16);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], ya[i], acc[i][j], 0, 0, 0);
     }
-    gemm_sstore<LA>(ra, As[cur ^ 1], tid);
-    gemm_sstore<LB>(rb, Bs[cur ^ 1], tid);
-    __syncthreads();
-    cur ^= 1;
   }
+}
+
+template <bool INT4, int BM, int BN, int WM, int WN, int P, int KB, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm(const uint8_t* __restrict__ A,
+                                                       const uint8_t* __restrict__ B, int64_t M,
+                                                       int64_t N, int64_t pitch,
+                                                       int64_t stages_per_split,
+                                                       const float* __restrict__ sa, int sa_step,
+                                                       const float* __restrict__ sb, int sb_step,
+                                                       float alpha, float* __restrict__ C,
+                                                       int32_t* __restrict__ Ci) {
+  using G = GemmShape<INT4, BM, BN, WM, WN, KB>;
+  constexpr int NT = G::NT, TM = G::TM, TN = G::TN, PITCH = G::PITCH, CPR = G::CPR;
+  constexpr int LA = G::LA, LB = G::LB;
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  int64_t tm, tn;
+  if (!xcd_tile(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn)) return;
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int64_t S = stages_per_split;
+  const int64_t kbase = (int64_t)blockIdx.y * stages_per_split * KB;
+
+  const uint8_t* pa[LA];
+  const uint8_t* pb[LB];
+  int la_off[LA], lb_off[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int c = tid + NT * i;
+    int64_t r = m0 + c / CPR;
+    r = r < M ? r : M - 1;
+    pa[i] = A + r * pitch + kbase + (c % CPR) * 16;
+    la_off[i] = (c / CPR) * PITCH + (c % CPR) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int c = tid + NT * i;
+    int64_t r = n0 + c / CPR;
+    r = r < N ? r : N - 1;
+    pb[i] = B + r * pitch + kbase + (c % CPR) * 16;
+    lb_off[i] = (c / CPR) * PITCH + (c % CPR) * 16;
+  }
+  u32x4 ra[P][LA], rb[P][LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i)
+    *reinterpret_cast<u32x4*>(As[0] + la_off[i]) = *reinterpret_cast<const u32x4*>(pa[i]);
+#pragma unroll
+  for (int i = 0; i < LB; ++i)
+    *reinterpret_cast<u32x4*>(Bs[0] + lb_off[i]) = *reinterpret_cast<const u32x4*>(pb[i]);
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int64_t kb = (1 + p < S ? 1 + p : S - 1) * KB;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ra[p][i] = *reinterpret_cast<const u32x4*>(pa[i] + kb);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rb[p][i] = *reinterpret_cast<const u32x4*>(pb[i] + kb);
+  }
+  __syncthreads();
+
+  v4i acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+  const int fr = lane & 15, fg = lane >> 4;
+
+  const int64_t S_main = S - S % P;
+  for (int64_t s0 = 0; s0 < S_main; s0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int64_t st = s0 + p;
+      const int nb = (int)((st + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(As[nb] + la_off[i]) = ra[p][i];
+#pragma unroll
+      for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(Bs[nb] + lb_off[i]) = rb[p][i];
+      const int64_t kl = (st + 1 + P < S ? st + 1 + P : S - 1) * KB;
+#pragma unroll
+      for (int i = 0; i < LA; ++i) ra[p][i] = *reinterpret_cast<const u32x4*>(pa[i] + kl);
+#pragma unroll
+      for (int i = 0; i < LB; ++i) rb[p][i] = *reinterpret_cast<const u32x4*>(pb[i] + kl);
+      gemm_stage<INT4, BM, BN, WM, WN, KB>(As[nb ^ 1], Bs[nb ^ 1], wm, wn, fr, fg, acc);
+      __syncthreads();
+    }
+  }
+  // last S mod P stages: their data already sits in slots 0..R-1
+#define HLQ_GEMM_TAIL(R)                                                                   \
+  case R: {                                                                                \
+    _Pragma("unroll") for (int p = 0; p < R; ++p) {                                       \
+      const int nb = (int)((S_main + p + 1) & 1);                                          \
+      if (p + 1 < R) {                                                                     \
+        _Pragma("unroll") for (int i = 0; i < LA; ++i)                                     \
+            *reinterpret_cast<u32x4*>(As[nb] + la_off[i]) = ra[p][i];                      \
+        _Pragma("unroll") for (int i = 0; i < LB; ++i)                                     \
+            *reinterpret_cast<u32x4*>(Bs[nb] + lb_off[i]) = rb[p][i];                      \
+      }                                                                                    \
+      gemm_stage<INT4, BM, BN, WM, WN, KB>(As[nb ^ 1], Bs[nb ^ 1], wm, wn, fr, fg, acc);   \
+      __syncthreads();                                                                     \
+    }                                                                                      \
+  } break;
+  switch ((int)(S - S_main)) {
+    HLQ_GEMM_TAIL(1)
+    HLQ_GEMM_TAIL(2)
+    HLQ_GEMM_TAIL(3)
+    default: break;
+  }
+#undef HLQ_GEMM_TAIL
 
   constexpr int SH = INT4 ? 8 : 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + wm * (BM / 2) + i * 16 + fr;
+    const int64_t m = m0 + wm * (BM / WM) + i * 16 + fr;
     if (m >= M) continue;
     const float s_m = (EPI == EPI_F32) ? sa[m * sa_step] * alpha : 0.f;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int64_t nn = n0 + wn * (BN / 2) + j * 16 + fg * 4;
+      const int64_t nn = n0 + wn * (BN / WN) + j * 16 + fg * 4;
       if (nn >= N) continue;
       v4i r = acc[i][j];
       if constexpr (EPI == EPI_F32) {
@@ -684,7 +938,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A,
         o.w = (float)(r[3] >> SH) * s_m * sb[(nn + 3) * sb_step];
         *reinterpret_cast<float4*>(C + m * N + nn) = o;
       } else {
-        int32_t* dst = Ci + (EPI == EPI_PARTIAL ? (int64_t)blockIdx.z * M * N : 0) + m * N + nn;
+        int32_t* dst = Ci + (EPI == EPI_PARTIAL ? (int64_t)blockIdx.y * M * N : 0) + m * N + nn;
         *reinterpret_cast<int4*>(dst) = make_int4(r[0] >> SH, r[1] >> SH, r[2] >> SH, r[3] >> SH);
       }
     }
@@ -721,21 +975,6 @@ __global__ __launch_bounds__(256) void k_gemm_finalize(const int32_t* __restrict
 
 static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
-hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_u32, dim3(cdiv(n, 256)), dim3(256), 0, s, p, n, v);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_pad(uint8_t* p, int64_t rows, int64_t pitch, int64_t from,
-                           hipStream_t s) {
-  const int64_t total = rows * (pitch - from);
-  if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_pad, dim3(cdiv(total, 256)), dim3(256), 0, s, p, rows, pitch,
-                     from);
-  return hipGetLastError();
-}
-
 hipError_t launch_acbp(const void* x, int dtype, int64_t T, int64_t I, uint8_t* codes,
                        float* scales, hipStream_t s) {
   dim3 grid(cdiv(T, 4)), block(256);
@@ -744,147 +983,86 @@ hipError_t launch_acbp(const void* x, int dtype, int64_t T, int64_t I, uint8_t* 
   return hipGetLastError();
 }
 
-template <int DT, int MODE>
-static void rows_dispatch(int nch, dim3 g, dim3 b, hipStream_t s, const void* gy,
-                          int64_t T, int64_t O, int n, int64_t kxb, uint8_t* q,
-                          float* scale, uint32_t* gmax) {
-#define HLQ_ROWS(NC) hipLaunchKernelGGL((k_rows<DT, MODE, NC>), g, b, 0, s, gy, T, O, n, kxb, q, scale, gmax)
-  switch (nch) {
-    case 1: HLQ_ROWS(1); break;
-    case 2: HLQ_ROWS(2); break;
-    case 3: HLQ_ROWS(3); break;
-    case 4: HLQ_ROWS(4); break;
-    case 5: case 6: HLQ_ROWS(6); break;
-    case 7: case 8: HLQ_ROWS(8); break;
-    default: HLQ_ROWS(0); break;
+template <int PASS, bool F32>
+static hipError_t tr_dispatch(int n, int r, dim3 g, hipStream_t s, const TrArgs& a) {
+#define HLQ_TR(NN, RR) hipLaunchKernelGGL((k_tr<PASS, NN, RR, F32>), g, dim3(256), 0, s, a)
+#define HLQ_TR_N(NN)                                                      \
+  switch (r) {                                                            \
+    case 1: HLQ_TR(NN, 1); break;                                         \
+    case 2: HLQ_TR(NN, 2); break;                                         \
+    case 4: HLQ_TR(NN, 4); break;                                         \
+    case 8: HLQ_TR(NN, 8); break;                                         \
+    case 16: HLQ_TR(NN, 16); break;                                       \
+    case 32: if (NN >= 32) HLQ_TR(NN, (NN >= 32 ? 32 : 1)); break;        \
+    case 64: if (NN >= 64) HLQ_TR(NN, (NN >= 64 ? 64 : 1)); break;        \
+    case 128: if (NN >= 128) HLQ_TR(NN, (NN >= 128 ? 128 : 1)); break;    \
+    default: return hipErrorInvalidValue;                                 \
   }
-#undef HLQ_ROWS
-}
-
-hipError_t launch_rows(const void* gy, int dtype, int64_t T, int64_t O, int n,
-                       int64_t kxb, uint8_t* q, float* scale, uint32_t* gmax,
-                       AbsMode mode, hipStream_t s) {
-  dim3 grid(cdiv(T, 4)), block(256);
-  const int nch = (int)cdiv(kxb * 2, 512);
-  if (dtype == 0) {
-    if (mode == ABS_ONLY) rows_dispatch<0, ABS_ONLY>(nch, grid, block, s, gy, T, O, n, kxb, q, scale, gmax);
-    else if (mode == QUANT_OWN) rows_dispatch<0, QUANT_OWN>(nch, grid, block, s, gy, T, O, n, kxb, q, scale, gmax);
-    else rows_dispatch<0, QUANT_GLOBAL>(0, grid, block, s, gy, T, O, n, kxb, q, scale, gmax);
-  } else {
-    if (mode == ABS_ONLY) rows_dispatch<1, ABS_ONLY>(nch, grid, block, s, gy, T, O, n, kxb, q, scale, gmax);
-    else if (mode == QUANT_OWN) rows_dispatch<1, QUANT_OWN>(nch, grid, block, s, gy, T, O, n, kxb, q, scale, gmax);
-    else rows_dispatch<1, QUANT_GLOBAL>(0, grid, block, s, gy, T, O, n, kxb, q, scale, gmax);
-  }
-  return hipGetLastError();
-}
-
-template <int DT, int MODE>
-static void cols_dispatch(int n, dim3 g, dim3 b, hipStream_t s, const void* w,
-                          int64_t O, int64_t I, int64_t kxb, int seg, uint8_t* q,
-                          float* scale, uint32_t* colmax, uint32_t* gmax) {
-#define HLQ_COLS(NN) hipLaunchKernelGGL((k_cols<DT, MODE, NN>), g, b, 0, s, w, O, I, kxb, seg, q, scale, colmax, gmax)
   switch (n) {
-    case 16: HLQ_COLS(16); break;
-    case 32: HLQ_COLS(32); break;
-    case 64: HLQ_COLS(64); break;
-    default: HLQ_COLS(128); break;
+    case 16: HLQ_TR_N(16); break;
+    case 32: HLQ_TR_N(32); break;
+    case 64: HLQ_TR_N(64); break;
+    case 128: HLQ_TR_N(128); break;
+    default: return hipErrorInvalidValue;
   }
-#undef HLQ_COLS
-}
-
-hipError_t launch_cols(const void* w, int dtype, int64_t O, int64_t I, int n,
-                       int64_t kxb, uint8_t* q, float* scale, uint32_t* colmax,
-                       uint32_t* gmax, AbsMode mode, hipStream_t s) {
-  const int seg = n > 64 ? n : 64;
-  dim3 grid(cdiv(I, 64), cdiv(O, seg)), block(64);
-  if (dtype == 0) {
-    if (mode == ABS_ONLY) cols_dispatch<0, ABS_ONLY>(n, grid, block, s, w, O, I, kxb, seg, q, scale, colmax, gmax);
-    else if (mode == QUANT_OWN) cols_dispatch<0, QUANT_OWN>(n, grid, block, s, w, O, I, kxb, seg, q, scale, colmax, gmax);
-    else cols_dispatch<0, QUANT_GLOBAL>(n, grid, block, s, w, O, I, kxb, seg, q, scale, colmax, gmax);
-  } else {
-    if (mode == ABS_ONLY) cols_dispatch<1, ABS_ONLY>(n, grid, block, s, w, O, I, kxb, seg, q, scale, colmax, gmax);
-    else if (mode == QUANT_OWN) cols_dispatch<1, QUANT_OWN>(n, grid, block, s, w, O, I, kxb, seg, q, scale, colmax, gmax);
-    else cols_dispatch<1, QUANT_GLOBAL>(n, grid, block, s, w, O, I, kxb, seg, q, scale, colmax, gmax);
-  }
+#undef HLQ_TR_N
+#undef HLQ_TR
   return hipGetLastError();
 }
 
-template <int KIND, int MODE>
-static void hla_dispatch(int r, dim3 g, dim3 b, hipStream_t s, const void* src,
-                         const float* sx, int64_t T, int64_t C, int n, int segb,
-                         int64_t kwb, uint8_t* q, float* scale, uint32_t* colmax,
-                         uint32_t* gmax) {
-#define HLQ_HLA(RR, CP) hipLaunchKernelGGL((k_hla<KIND, MODE, RR, CP>), g, b, 0, s, src, sx, T, C, n, segb, kwb, q, scale, colmax, gmax)
-  switch (r) {
-    case 1: HLQ_HLA(1, 8); break;
-    case 2: HLQ_HLA(2, 8); break;
-    case 4: HLQ_HLA(4, 8); break;
-    case 8: HLQ_HLA(8, 8); break;
-    case 16: HLQ_HLA(16, 8); break;
-    case 32: HLQ_HLA(32, 4); break;
-    case 64: HLQ_HLA(64, 2); break;
-    default: HLQ_HLA(128, 2); break;
-  }
-#undef HLQ_HLA
+hipError_t launch_tr(const TrArgs& a, int pass, int n, int r, hipStream_t s) {
+  if (r > n) return hipErrorInvalidValue;
+  const int64_t wgs = a.wg_gy + a.wg_x + a.wg_w;
+  if (wgs <= 0) return hipSuccess;
+  dim3 g((unsigned)wgs);
+  const bool f32 = a.gy_dt == 0 || a.w_dt == 0;
+  if (pass == PASS_MAX)
+    return f32 ? tr_dispatch<PASS_MAX, true>(n, r, g, s, a) : tr_dispatch<PASS_MAX, false>(n, r, g, s, a);
+  return f32 ? tr_dispatch<PASS_QUANT, true>(n, r, g, s, a)
+             : tr_dispatch<PASS_QUANT, false>(n, r, g, s, a);
 }
 
-static int hla_cpt(int r) { return r <= 16 ? 8 : (r == 32 ? 4 : 2); }
-
-hipError_t launch_hla(const void* src, const float* src_scale, HlaSource kind,
-                      int64_t T, int64_t C, int n, int r, int64_t kwb, uint8_t* q,
-                      float* scale, uint32_t* colmax, uint32_t* gmax, AbsMode mode,
-                      hipStream_t s) {
-  const int cpt = hla_cpt(r);
-  const int64_t ncc = C / cpt;
-  const int64_t nblk = T / n;
-  // enough token segments to give ~96k threads, at most 16 blocks each
-  int64_t want_segs = (98304 + ncc - 1) / ncc;
-  int64_t segb = (nblk + want_segs - 1) / want_segs;
-  if (segb < 1) segb = 1;
-  if (segb > 16) segb = 16;
-  const int64_t nseg = (nblk + segb - 1) / segb;
-  dim3 grid(cdiv(ncc, 32), cdiv(nseg, 8)), block(256);
-#define HLQ_HLA_K(KD)                                                                        \
-  do {                                                                                       \
-    if (mode == ABS_ONLY) hla_dispatch<KD, ABS_ONLY>(r, grid, block, s, src, src_scale, T, C, n, (int)segb, kwb, q, scale, colmax, gmax); \
-    else if (mode == QUANT_OWN) hla_dispatch<KD, QUANT_OWN>(r, grid, block, s, src, src_scale, T, C, n, (int)segb, kwb, q, scale, colmax, gmax); \
-    else hla_dispatch<KD, QUANT_GLOBAL>(r, grid, block, s, src, src_scale, T, C, n, (int)segb, kwb, q, scale, colmax, gmax); \
-  } while (0)
-  if (kind == SRC_F32) HLQ_HLA_K(SRC_F32);
-  else if (kind == SRC_BF16) HLQ_HLA_K(SRC_BF16);
-  else HLQ_HLA_K(SRC_INT4);
-#undef HLQ_HLA_K
+hipError_t launch_tr_reduce(const TrArgs& a, hipStream_t s) {
+  if (a.nred != (int64_t)cdiv(a.T + a.O + 2 * a.I, RED_ENTRIES)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tr_reduce, dim3((unsigned)a.nred), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t kbytes) {
+GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes) {
+  static const int cfg_bm[4] = {256, 128, 64, 64}, cfg_bn[4] = {128, 128, 128, 64};
   GemmPlan p;
-  p.stages = kbytes / KST;
-  const int64_t target = 512;  // two blocks per CU
-  auto tiles = [&](int bm, int bn) { return (int64_t)cdiv(M, bm) * cdiv(N, bn); };
-  if (tiles(128, 128) >= target) { p.bm = 128; p.bn = 128; }
-  else if (tiles(64, 128) >= target) { p.bm = 64; p.bn = 128; }
-  else if (tiles(128, 64) >= target) { p.bm = 128; p.bn = 64; }
-  else { p.bm = 64; p.bn = 64; }
-  const int64_t t = tiles(p.bm, p.bn);
+  auto tiles = [&](int c) { return (int64_t)cdiv(M, cfg_bm[c]) * cdiv(N, cfg_bn[c]); };
+  const int64_t want = int4 ? 1024 : 512;
+  if (tiles(0) >= want) p.cfg = 0;
+  else if (int4 && tiles(1) >= want) p.cfg = 1;
+  else if (int4 || tiles(2) >= 200) p.cfg = 2;
+  else p.cfg = 3;
+  p.bm = cfg_bm[p.cfg];
+  p.bn = cfg_bn[p.cfg];
+  p.stages = kbytes / 64;
+  // split K when the tile grid cannot fill the 256 CUs
+  const int64_t t = tiles(p.cfg);
   int64_t sp = 1;
-  while (t * sp * 2 <= target && p.stages / (sp * 2) >= 8 && sp < 8) sp *= 2;
-  // splits must divide the stage count
-  while (sp > 1 && p.stages % sp) sp /= 2;
+  while (t * sp < 256 && p.stages / (sp * 2) >= 16 && sp < 8) sp *= 2;
+  while (sp > 1 && p.stages % sp) sp /= 2;  // splits divide the stage count
   p.splits = (int)sp;
   return p;
 }
 
 template <bool I4, int EPI>
-static void gemm_dispatch(int bm, int bn, dim3 g, hipStream_t s, const uint8_t* A,
-                          const uint8_t* B, int64_t M, int64_t N, int64_t pitch,
-                          int64_t sps, const float* sa, int sa_step, const float* sb,
-                          int sb_step, float alpha, float* C, int32_t* Ci) {
-#define HLQ_GEMM(BM_, BN_) hipLaunchKernelGGL((k_gemm<I4, BM_, BN_, EPI>), g, dim3(256), 0, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, Ci)
-  if (bm == 128 && bn == 128) HLQ_GEMM(128, 128);
-  else if (bm == 64 && bn == 128) HLQ_GEMM(64, 128);
-  else if (bm == 128 && bn == 64) HLQ_GEMM(128, 64);
-  else HLQ_GEMM(64, 64);
+static void gemm_dispatch(int cfg, dim3 g, hipStream_t s, const uint8_t* A, const uint8_t* B,
+                          int64_t M, int64_t N, int64_t pitch, int64_t sps, const float* sa,
+                          int sa_step, const float* sb, int sb_step, float alpha, float* C,
+                          int32_t* Ci) {
+#define HLQ_GEMM(BM_, BN_, WM_, WN_, P_, KB_)                                                  \
+  hipLaunchKernelGGL((k_gemm<I4, BM_, BN_, WM_, WN_, P_, KB_, EPI>), g, dim3(64 * WM_ * WN_), \
+                     0, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, Ci)
+  switch (cfg) {
+    case 0: HLQ_GEMM(256, 128, 4, 2, 3, 64); break;
+    case 1: HLQ_GEMM(128, 128, 2, 2, 2, 64); break;
+    case 2: HLQ_GEMM(64, 128, 2, 2, 4, 64); break;
+    default: HLQ_GEMM(64, 64, 2, 2, 4, 64); break;
+  }
 #undef HLQ_GEMM
 }
 
@@ -895,7 +1073,8 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
                        int32_t* partial, hipStream_t s) {
   const int splits = epi == EPI_I32 ? 1 : plan.splits;
   const int64_t sps = plan.stages / splits;
-  dim3 grid(cdiv(M, plan.bm), cdiv(N, plan.bn), splits);
+  const int64_t tiles = (int64_t)cdiv(M, plan.bm) * cdiv(N, plan.bn);
+  dim3 grid((unsigned)((tiles + 7) / 8 * 8), splits);
   const bool use_partial = (epi == EPI_F32 && splits > 1);
   if (use_partial && partial == nullptr) return hipErrorInvalidValue;
   if (epi == EPI_F32 && (C == nullptr || sa == nullptr || sb == nullptr))
@@ -904,13 +1083,13 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
   const int e = use_partial ? EPI_PARTIAL : epi;
   int32_t* dst = use_partial ? partial : Ci;
   if (int4) {
-    if (e == EPI_F32) gemm_dispatch<true, EPI_F32>(plan.bm, plan.bn, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else if (e == EPI_I32) gemm_dispatch<true, EPI_I32>(plan.bm, plan.bn, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else gemm_dispatch<true, EPI_PARTIAL>(plan.bm, plan.bn, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    if (e == EPI_F32) gemm_dispatch<true, EPI_F32>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    else if (e == EPI_I32) gemm_dispatch<true, EPI_I32>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    else gemm_dispatch<true, EPI_PARTIAL>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
   } else {
-    if (e == EPI_F32) gemm_dispatch<false, EPI_F32>(plan.bm, plan.bn, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else if (e == EPI_I32) gemm_dispatch<false, EPI_I32>(plan.bm, plan.bn, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else gemm_dispatch<false, EPI_PARTIAL>(plan.bm, plan.bn, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    if (e == EPI_F32) gemm_dispatch<false, EPI_F32>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    else if (e == EPI_I32) gemm_dispatch<false, EPI_I32>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    else gemm_dispatch<false, EPI_PARTIAL>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !use_partial) return err;

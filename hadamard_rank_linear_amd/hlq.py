@@ -16,8 +16,7 @@ LIB_PATH = os.path.join(HERE, "libhlq.so")
 HLQ_F32, HLQ_BF16 = 0, 1
 HLQ_PER_TOKEN, HLQ_PER_TENSOR = 0, 1
 HLQ_SUM, HLQ_MEAN = 0, 1
-STEP_NAMES = ("clear", "gx_a_max", "gx_a_quant", "gx_b_max", "gx_b_quant", "gw_a_max",
-              "gw_a_quant", "gw_b_max", "gw_b_quant", "gemm_gx", "gemm_gw")
+STEP_NAMES = ("tr_max", "tr_reduce", "tr_quant", "gemm_gx", "gemm_gw")
 HLQ_STEPS_ALL = (1 << len(STEP_NAMES)) - 1
 
 EXPORTED = (

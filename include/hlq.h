@@ -119,23 +119,19 @@ hlq_status hlq_linear_backward(const void* g_y, int gy_dtype,
 
 /*
  * The launches hlq_linear_backward enqueues, in order.  Bit k of a step mask
- * selects HLQ_STEP k.  HLQ_STEP_GX_A_MAX runs only with gx_mode PER_TENSOR.
+ * selects HLQ_STEP k.
  */
 enum {
-  HLQ_STEP_CLEAR = 0,       /* clear max accumulators, zero operand K padding  */
-  HLQ_STEP_GX_A_MAX = 1,    /* tensor max of H.g_y (along O)                   */
-  HLQ_STEP_GX_A_QUANT = 2,  /* H.g_y -> INT4 codes + scales                    */
-  HLQ_STEP_GX_B_MAX = 3,    /* per-column and tensor max of H.w (along O)      */
-  HLQ_STEP_GX_B_QUANT = 4,  /* H.w -> INT4 codes (transposed) + scales         */
-  HLQ_STEP_GW_A_MAX = 5,    /* maxima of the low-rank g_y (along T)            */
-  HLQ_STEP_GW_A_QUANT = 6,  /* low-rank g_y -> INT8 codes (transposed) + scales */
-  HLQ_STEP_GW_B_MAX = 7,    /* maxima of the low-rank ACBP-decoded x           */
-  HLQ_STEP_GW_B_QUANT = 8,  /* low-rank x -> INT8 codes (transposed) + scales  */
-  HLQ_STEP_GEMM_GX = 9,     /* INT4 GEMM + dequantizing epilogue -> g_x        */
-  HLQ_STEP_GEMM_GW = 10,    /* INT8 GEMM + dequantizing epilogue -> g_w        */
-  HLQ_STEP_COUNT = 11
+  HLQ_STEP_TR_MAX = 0,     /* partial maxima of H.g_y (along O), the low-rank
+                              g_y and x (along T) and H.w (along O)          */
+  HLQ_STEP_TR_REDUCE = 1,  /* fold partials: per-token maxima, scales,
+                              tensor maxima                                  */
+  HLQ_STEP_TR_QUANT = 2,   /* transforms again -> INT4 / INT8 GEMM operands  */
+  HLQ_STEP_GEMM_GX = 3,    /* INT4 GEMM + dequantizing epilogue -> g_x       */
+  HLQ_STEP_GEMM_GW = 4,    /* INT8 GEMM + dequantizing epilogue -> g_w       */
+  HLQ_STEP_COUNT = 5
 };
-#define HLQ_STEPS_ALL 0x7FFu
+#define HLQ_STEPS_ALL 0x1Fu
 
 /*
  * hlq_linear_backward restricted to the steps whose bit is set in step_mask
