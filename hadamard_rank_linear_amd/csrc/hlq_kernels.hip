@@ -88,21 +88,33 @@ __device__ __forceinline__ void fwht_lanes(float (&v)[8], int lane, int lanes_pe
   }
 }
 
+// Quantizer code of v: rne(fl(v * inv)) as the low bits of a two's-complement
+// integer.  Adding 1.5 * 2^23 to fl(v * inv) (|.| < 2^22) lands in [2^23, 2^24),
+// where the fp32 spacing is 1, so that one IEEE add performs the
+// round-half-to-even and leaves the integer in the low mantissa bits (the
+// build forbids contracting the multiply into the add).  No clamp is needed:
+// |v| <= a gives |fl(v * fl(QMAX / a))| <= QMAX * (1 + 2^-24), which rounds to
+// at most QMAX.  Mask the result to 4 (INT4) or 8 (INT8) bits.
 template <int QMAX>
-__device__ __forceinline__ int quant1(float v, float inv) {
-  float q = __builtin_rintf(v * inv);
-  q = fminf(fmaxf(q, -(float)QMAX), (float)QMAX);
-  return (int)q;
+__device__ __forceinline__ uint32_t quant_bits(float v, float inv) {
+  const float p = v * inv;
+  return __float_as_uint(p + 12582912.0f);
 }
 
-__device__ __forceinline__ uint32_t pack8_int4(const int (&q)[8]) {
+// 8 INT4 codes of v[0..8) packed two per byte, element 2k in the low nibble.
+__device__ __forceinline__ uint32_t quant_pack8_int4(const float (&v)[8], float inv) {
   uint32_t u = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) u |= (uint32_t)(q[k] & 0xF) << (4 * k);
+  for (int k = 0; k < 8; ++k) u |= (quant_bits<7>(v[k], inv) & 0xFu) << (4 * k);
   return u;
 }
 
-__device__ __forceinline__ float inv_of(float a, float qmax) { return a == 0.f ? 0.f : qmax / a; }
+// Reciprocal scale of a group with absmax a.  A zero group, and a group so
+// small that qmax / a overflows fp32, get 0: all their codes are zero.
+__device__ __forceinline__ float inv_of(float a, float qmax) {
+  const float r = qmax / a;
+  return (a == 0.f || r == __builtin_huge_valf()) ? 0.f : r;
+}
 __device__ __forceinline__ float scale_of(float a, float qmax) { return a == 0.f ? 0.f : a / qmax; }
 
 // ------------------------------------------------------------ ACBP pack
@@ -129,10 +141,7 @@ __global__ __launch_bounds__(256) void k_acbp(const void* __restrict__ x, int64_
   for (int64_t c = lane * 8; c < I; c += 512) {
     float v[8];
     load8<DT>(x, base + c, v);
-    int q[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) q[k] = quant1<7>(v[k], inv);
-    *reinterpret_cast<uint32_t*>(out + c / 2) = pack8_int4(q);
+    *reinterpret_cast<uint32_t*>(out + c / 2) = quant_pack8_int4(v, inv);
   }
   if (lane == 0) scales[row] = scale_of(a, 7.f);
 }
@@ -397,7 +406,7 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
       } else {
 #pragma unroll
         for (int j = 0; j < R; ++j)
-          words[t][j / 4] |= (uint32_t)(quant1<127>(g[j], inv_c) & 0xFF) << (8 * (j % 4));
+          words[t][j / 4] |= (quant_bits<127>(g[j], inv_c) & 0xFFu) << (8 * (j % 4));
       }
     }
   }
@@ -461,7 +470,7 @@ __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint
       } else {
 #pragma unroll
         for (int k = 0; k < N; ++k)
-          words[t][k / 8] |= (uint32_t)(quant1<7>(v[k], inv_c) & 0xF) << (4 * (k % 8));
+          words[t][k / 8] |= (quant_bits<7>(v[k], inv_c) & 0xFu) << (4 * (k % 8));
       }
     }
   }
@@ -526,12 +535,9 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
       if (lc == 0 && row < rows) a.part_gy[ch * a.T + t0 + row] = m;
     } else if (row < rows) {
       const float inv = a.gx_tok ? inv_of(a.max_gy[t0 + row], 7.f) : inv_tensor;
-      int qv[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) qv[k] = quant1<7>(v[k], inv);
       // columns past O inside the chunk are zero -> zero codes (K padding)
       *reinterpret_cast<uint32_t*>(a.q_gy + (t0 + row) * a.kxb + (c0 + col) / 2) =
-          col < cols ? pack8_int4(qv) : 0u;
+          col < cols ? quant_pack8_int4(v, inv) : 0u;
     }
   }
   __syncthreads();
@@ -671,9 +677,10 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
 // entries; its 4 waves split each entry's partials (stride 4) so every wave
 // keeps several loads in flight.
 constexpr int RED_ENTRIES = TR_RED_ENTRIES;
+constexpr int RED_WAVES = 16;
 
-__global__ __launch_bounds__(256) void k_tr_reduce(TrArgs a) {
-  __shared__ float wpart[4][RED_ENTRIES];
+__global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
+  __shared__ float wpart[RED_WAVES][RED_ENTRIES];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t e = (int64_t)blockIdx.x * RED_ENTRIES + lane;
   const int64_t n0 = a.T, n1 = n0 + a.O, n2 = n1 + a.I, n3 = n2 + a.I;
@@ -684,19 +691,23 @@ __global__ __launch_bounds__(256) void k_tr_reduce(TrArgs a) {
   else if (e < n1) { list = 2; p = a.part_gyl + (e - n0); np = a.ntr_t; stride = a.O; }
   else if (e < n2) { list = 3; p = a.part_xl + (e - n1); np = a.ntr_t; stride = a.I; }
   else if (e < n3) { list = 1; p = a.part_w + (e - n2); np = a.ntr_o; stride = a.I; }
+  // wave wv folds partials wv, wv + 16, ...; four loads in flight per step
   float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
   int64_t k = wv;
-  for (; k + 12 < np; k += 16) {
+  constexpr int W = RED_WAVES;
+  for (; k + 3 * W < np; k += 4 * W) {
     m0 = fmaxf(m0, p[k * stride]);
-    m1 = fmaxf(m1, p[(k + 4) * stride]);
-    m2 = fmaxf(m2, p[(k + 8) * stride]);
-    m3 = fmaxf(m3, p[(k + 12) * stride]);
+    m1 = fmaxf(m1, p[(k + W) * stride]);
+    m2 = fmaxf(m2, p[(k + 2 * W) * stride]);
+    m3 = fmaxf(m3, p[(k + 3 * W) * stride]);
   }
-  for (; k < np; k += 4) m0 = fmaxf(m0, p[k * stride]);
+  for (; k < np; k += W) m0 = fmaxf(m0, p[k * stride]);
   wpart[wv][lane] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
   __syncthreads();
   if (wv != 0) return;
-  const float m = fmaxf(fmaxf(wpart[0][lane], wpart[1][lane]), fmaxf(wpart[2][lane], wpart[3][lane]));
+  float m = wpart[0][lane];
+#pragma unroll
+  for (int q = 1; q < RED_WAVES; ++q) m = fmaxf(m, wpart[q][lane]);
   if (list == 0) {
     if (a.gx_tok) { a.max_gy[e] = m; a.s_gy[e] = scale_of(m, 7.f); }
   } else if (list == 2) {
@@ -1024,7 +1035,7 @@ hipError_t launch_tr(const TrArgs& a, int pass, int n, int r, hipStream_t s) {
 
 hipError_t launch_tr_reduce(const TrArgs& a, hipStream_t s) {
   if (a.nred != (int64_t)cdiv(a.T + a.O + 2 * a.I, RED_ENTRIES)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_tr_reduce, dim3((unsigned)a.nred), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_tr_reduce, dim3((unsigned)a.nred), dim3(64 * RED_WAVES), 0, s, a);
   return hipGetLastError();
 }
 

@@ -44,7 +44,10 @@ R4  "Low-rank" keeps, in each block of n tokens, the r rows of H_n with the
 R5  Quantizer: symmetric absmax, no zero point.  For a scale group G with
     qmax = 7 (INT4) or 127 (INT8): a = max|v|; a == 0 gives codes 0 and scale
     0; otherwise inv = fl32(qmax / a), s = fl32(a / qmax),
-    q = clamp(rne(fl32(v * inv)), -qmax, qmax).
+    q = clamp(rne(fl32(v * inv)), -qmax, qmax).  A group so small that
+    qmax / a overflows fp32 (a below about qmax / 3.4e38) is treated like a
+    zero group for its codes (inv = 0, codes 0) and keeps s = fl32(a / qmax).
+    (The pages do not reach this corner; the reading keeps every code finite.)
 R6  Scale groups (layer-wise quantizer selection, [HOT-sum] "Approach"):
     PER_TOKEN gives one scale per GEMM output index of each operand (g_x path:
     one per token t of the transformed g_y and one per input channel i of the
@@ -172,8 +175,9 @@ def quantize(v: np.ndarray, qmax: int, reduce_axis):
         a = np.squeeze(a_b, axis=reduce_axis)
     qm = np.float32(qmax)
     zero = a_b == 0
-    with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         inv = np.where(zero, np.float32(0), qm / np.where(zero, np.float32(1), a_b)).astype(np.float32)
+        inv = np.where(np.isinf(inv), np.float32(0), inv).astype(np.float32)  # R5 overflow corner
         s = np.where(a == 0, np.float32(0), a / qm).astype(np.float32)
     prod = (v * inv).astype(np.float32)            # one fp32 rounding
     q = np.clip(np.rint(prod), -qmax, qmax)        # rint: round half to even

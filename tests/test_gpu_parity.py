@@ -54,6 +54,21 @@ def test_tiny_zero_groups():
     _case(dataclasses.replace(wl.CONFIGS[0], gx_mode=1, gw_mode=1), plant=True)
 
 
+def test_tiny_denormal_group():
+    # token 1 of g_y holds denormals only: qmax / a overflows fp32, so that
+    # token's g_x-path codes are all zero while its scale stays a / 7
+    cfg = dataclasses.replace(wl.CONFIGS[0], dtype=wl.F32)
+    _say(f"denormal token row: {cfg.name} T={cfg.T} I={cfg.I} O={cfg.O}")
+    inp = wl.make_inputs(cfg, seed=3)
+    gy = inp["gy"].copy()
+    gy[1, :] = (np.arange(cfg.O) % 5 - 2).astype(np.float32) * np.float32(1.4e-45)
+    inp = dict(inp, gy=gy)
+    ocodes, oscales, ref = run_oracle(cfg, inp)
+    assert (ref["q_gy"][1] == 0).all() and ref["s_gy"][1] > 0
+    gpu = run_gpu(cfg, inp, x_codes=ocodes, x_scales=oscales)
+    compare(cfg, gpu, ocodes, oscales, ref)
+
+
 # ----------------------------------------------- block sizes, ranks, tails
 
 SHAPES = [

@@ -190,6 +190,33 @@ def test_quant_invariants(qmax):
     assert (err <= s[:, None] * (0.5 + 1e-5)).all()
 
 
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_quant_reciprocal_overflow_group(qmax):
+    # reading R5's corner: qmax / a overflows fp32 for a deep in the denormal
+    # range; codes are 0 and the scale is still a / qmax
+    v = np.zeros((2, 8), np.float32)
+    v[0, :3] = [1e-44, -3e-45, 7e-45]
+    v[1, :2] = [1.0, -0.5]
+    q, s = o.quantize(v, qmax, 1)
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(qmax) / np.float32(1e-44))
+    assert (q[0] == 0).all() and float(s[0]) == float(np.float32(1e-44) / np.float32(qmax))
+    assert q[1, 0] == qmax and q[1, 1] == -int(np.rint(qmax / 2))
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_quant_product_never_exceeds_qmax(qmax):
+    # |fl(v * fl(qmax / a))| <= qmax(1 + 2^-24) rounds to at most qmax, so the
+    # clamp of R5 never changes a code; probe groups whose absmax sweeps many
+    # binades and mantissas
+    rng = np.random.default_rng(77 + qmax)
+    a = (rng.uniform(1, 2, 4096) * 2.0 ** rng.integers(-120, 120, 4096)).astype(np.float32)
+    inv = (np.float32(qmax) / a).astype(np.float32)
+    assert np.isfinite(inv).all()
+    prod = (a * inv).astype(np.float32)
+    assert (np.rint(prod) <= qmax).all() and (np.rint(-prod) >= -qmax).all()
+
+
 def test_quant_group_axis():
     # catches a swapped scale-group axis: per-column groups along axis 0
     rng = np.random.default_rng(5)
