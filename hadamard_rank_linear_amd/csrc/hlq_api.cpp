@@ -57,7 +57,7 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   const int64_t t_low = T / block * rank;
   const int64_t kx = (O + 127) / 128 * 128;  // INT4 codes per row, 64-byte stages
   const int64_t kxb = kx / 2;
-  const int64_t kwb = (t_low + 63) / 64 * 64;
+  const int64_t kwb = (t_low + 127) / 128 * 128;  // INT8 codes, 128-byte stages
   L.pub.kx_pitch = kxb;
   L.pub.kw_pitch = kwb;
   L.pub.t_low = t_low;

@@ -44,8 +44,10 @@ struct TrArgs {
 struct GemmPlan {
   int cfg;         // tile configuration index (see plan_gemm)
   int bm, bn;      // block tile
+  int kb;          // K bytes per pipeline stage (the operand pitch is a multiple)
   int splits;      // split-K factor (partials summed by gemm_finalize)
   int64_t stages;  // K stages in total
+  int64_t sps;     // stages per split (the last split takes the remainder)
 };
 
 GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes);

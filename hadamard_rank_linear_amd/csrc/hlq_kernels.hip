@@ -726,31 +726,41 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
 
 // ------------------------------------------------------------ integer GEMM
 // C[m][n] = sum_k A[m][k] * B[n][k]; A [M][pitch], B [N][pitch] bytes, K
-// contiguous and zero-padded to a multiple of 64 bytes.  INT4 operands hold
-// two codes per byte; they are widened on the LDS->register path into int8
-// lanes holding 16*code (low nibble shifted up, high nibble masked in place),
-// so the INT32 sum is 256 times the code product sum and is shifted back
-// exactly.  The nibble order inside a lane is permuted the same way for both
-// operands, which leaves the dot product unchanged.  Operands stay packed in
-// HBM, L2 and LDS: the GEMMs here are limited by operand fetch, so halving
-// the bytes matters more than the widening instructions.
+// contiguous and zero-padded to a multiple of the stage depth KB.  INT4
+// operands hold two codes per byte and stay packed in HBM, L2 and LDS; each
+// 16-byte fragment is widened on the LDS->register path into two int8
+// fragments holding 16*code (low nibble shifted up, high nibble masked in
+// place), so the INT32 sum is 256 times the code product sum and is shifted
+// back exactly.  Both operands are widened the same way, so the nibble order
+// inside a lane leaves the dot product unchanged.
 //
-// v_mfma_i32_16x16x64_i8: operand X (16 rows of D) comes from B's rows (n),
-// operand Y (16 columns of D) from A's rows (m); lane l then holds
-// D[4*(l/16)+e][l%16] = C[m0 + l%16][n0 + 4*(l/16) + e], four consecutive n,
-// which the epilogue stores as one 16-byte vector.
+// Matrix core: v_mfma_i32_32x32x32_i8 (32 cycles of the matrix pipe for a
+// 32x32x32 product; the 16x16x64 form needs more independent accumulators
+// than a wave has to stay busy).  Operand X holds 32 rows of A, operand Y 32
+// rows of B; lane l feeds row l%32 with 16 consecutive K bytes of half l/32.
+// Lane l then holds D[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator r: one
+// column n of C per lane, so a store of register r writes 128 contiguous
+// bytes of a C row per half-wave.
 //
-// Pipeline: 64*WM*WN threads, wave tile (BM/WM) x (BN/WN), KB-byte K stages
-// double-buffered in LDS (one barrier per stage).  Global loads run P stages
-// ahead in a ring of registers: stage st+1 is written to LDS from register
-// slot (st mod P) at the start of stage st, and that slot is refilled with
-// stage st+1+P.  The stage loop is unrolled by P (static slots, so the ring
-// lives in VGPRs); the last S mod P stages run in a static tail.
-// Workgroups are mapped to tiles XCD-aware: hardware hands consecutive
-// workgroup ids to the 8 XCDs in turn, so each XCD gets a contiguous run of
-// tiles (n fastest) and its L2 serves the A rows those tiles share.
+// Pipeline (256 threads, 2x2 waves, wave tile (BM/2) x (BN/2)):
+//   * K advances in stages of KB bytes held in an NS-deep LDS ring.  Stages
+//     are fetched with LDS DMA (global_load_lds_dwordx4: lane i of a wave
+//     instruction fills bytes 16i..16i+15 of a 1 KB LDS run), NS stages
+//     ahead; no VGPR staging.  Each row's 16-byte chunks are XOR-swizzled
+//     (chunk c of row r sits at c ^ swz(r)) so the fragment reads of 32 rows
+//     at one chunk hit distinct banks.
+//   * Fragments are double-buffered in registers: the reads of k-step kk+1
+//     are issued between the MFMAs of step kk.
+//   * One barrier per stage, after the stage's last MFMAs are issued: it
+//     publishes the next stage (every wave has waited for its own DMA with
+//     vmcnt) and frees the stage just read, which is refilled at once.
+// Workgroups map to tiles XCD-aware: consecutive workgroup ids go to the 8
+// XCDs in turn, so each XCD takes a contiguous run of tiles (n fastest) and
+// its L2 serves the A rows those tiles share.  blockIdx.y selects a split of
+// the K stages (partials summed by k_gemm_finalize).
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ void widen_int4x2(u32x4 p, v4i& a, v4i& b) {
   a[0] = (int)((p[0] << 4) & 0xF0F0F0F0u); a[1] = (int)(p[0] & 0xF0F0F0F0u);
@@ -770,189 +780,224 @@ __device__ __forceinline__ bool xcd_tile(int64_t w, int64_t nt_m, int64_t nt_n, 
   return true;
 }
 
-template <bool INT4, int BM, int BN, int WM, int WN, int KB>
-struct GemmShape {
-  static constexpr int NT = 64 * WM * WN, TM = BM / WM / 16, TN = BN / WN / 16;
-  static constexpr int PITCH = KB + 16, CPR = KB / 16;
-  static constexpr int LA = BM * CPR / NT, LB = BN * CPR / NT;
-  static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "tile load split");
-  static_assert(TM >= 1 && TN >= 1, "wave tile smaller than one MFMA tile");
-};
-
-template <bool INT4, int BM, int BN, int WM, int WN, int KB>
-__device__ __forceinline__ void gemm_stage(
-    const uint8_t* as, const uint8_t* bs, int wm, int wn, int fr, int fg,
-    v4i (&acc)[GemmShape<INT4, BM, BN, WM, WN, KB>::TM][GemmShape<INT4, BM, BN, WM, WN, KB>::TN]) {
-  using G = GemmShape<INT4, BM, BN, WM, WN, KB>;
-  constexpr int TM = G::TM, TN = G::TN, PITCH = G::PITCH;
-#pragma unroll
-  for (int kc = 0; kc < KB; kc += 64) {
-    if constexpr (INT4) {
-      // 16 packed bytes per lane = 32 codes = two MFMA K-steps
-      v4i ya0[TM], ya1[TM], xb0[TN], xb1[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        widen_int4x2(*reinterpret_cast<const u32x4*>(as + (wm * (BM / WM) + i * 16 + fr) * PITCH + kc + fg * 16), ya0[i], ya1[i]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        widen_int4x2(*reinterpret_cast<const u32x4*>(bs + (wn * (BN / WN) + j * 16 + fr) * PITCH + kc + fg * 16), xb0[j], xb1[j]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb0[j], ya0[i], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb1[j], ya1[i], acc[i][j], 0, 0, 0);
-    } else {
-      v4i ya[TM], xb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        ya[i] = *reinterpret_cast<const v4i*>(as + (wm * (BM / WM) + i * 16 + fr) * PITCH + kc + fg * 16);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        xb[j] = *reinterpret_cast<const v4i*>(bs + (wn * (BN / WN) + j * 16 + fr) * PITCH + kc + fg * 16);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], ya[i], acc[i][j], 0, 0, 0);
-    }
-  }
+// s_waitcnt with vmcnt = N and the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <bool INT4, int BM, int BN, int WM, int WN, int P, int KB, int EPI>
-__global__ __launch_bounds__(64 * WM * WN) void k_gemm(const uint8_t* __restrict__ A,
-                                                       const uint8_t* __restrict__ B, int64_t M,
-                                                       int64_t N, int64_t pitch,
-                                                       int64_t stages_per_split,
-                                                       const float* __restrict__ sa, int sa_step,
-                                                       const float* __restrict__ sb, int sb_step,
-                                                       float alpha, float* __restrict__ C,
-                                                       int32_t* __restrict__ Ci) {
-  using G = GemmShape<INT4, BM, BN, WM, WN, KB>;
-  constexpr int NT = G::NT, TM = G::TM, TN = G::TN, PITCH = G::PITCH, CPR = G::CPR;
-  constexpr int LA = G::LA, LB = G::LB;
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * PITCH];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * PITCH];
+// 16 bytes per lane from global memory into LDS run l (lane i -> l + 16 i).
+__device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+// Physical 16-byte chunk slot of logical chunk 0 in row r (XOR with it).
+// Depends on r & 15 only, so fragment bases (multiples of 32 rows) keep it.
+template <int KB>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (KB == 128) return (r & 7) ^ ((r >> 3) & 1);
+  else return (r >> 2) & 3;
+}
+
+template <bool INT4, int BM, int BN, int KB, int NS>
+struct GemmShape {
+  static constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
+  static constexpr int CPR = KB / 16;                              // chunks per row
+  static constexpr int IA = BM * CPR / 256, IB = BN * CPR / 256;   // DMA ops per wave
+  static constexpr int IPW = IA + IB;
+  static constexpr int STAGE = (BM + BN) * KB;
+  static constexpr int KK = KB / 32;                               // k-steps per stage
+  static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA tile");
+  static_assert(IA * 256 == BM * CPR && IB * 256 == BN * CPR, "stage load split");
+  static_assert(KK % 2 == 0, "fragment slots alternate per k-step");
+  static_assert(KB == 64 || KB == 128, "swizzle covers 4 or 8 chunks per row");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  static_assert(NS * STAGE <= 160 * 1024, "LDS ring fits the CU");
+};
+
+#define HLQ_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
+template <bool INT4, int BM, int BN, int KB, int NS, int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ A,
+                                                 const uint8_t* __restrict__ B, int64_t M,
+                                                 int64_t N, int64_t pitch, int64_t S_total,
+                                                 int64_t sps, const float* __restrict__ sa,
+                                                 int sa_step, const float* __restrict__ sb,
+                                                 int sb_step, float alpha,
+                                                 float* __restrict__ C,
+                                                 int32_t* __restrict__ Ci) {
+  using G = GemmShape<INT4, BM, BN, KB, NS>;
+  constexpr int FM = G::FM, FN = G::FN, IA = G::IA, IB = G::IB, IPW = G::IPW;
+  constexpr int CPR = G::CPR, KK = G::KK;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * G::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave >> 1, wn = wave & 1;
   int64_t tm, tn;
   if (!xcd_tile(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn)) return;
   const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int64_t S = stages_per_split;
-  const int64_t kbase = (int64_t)blockIdx.y * stages_per_split * KB;
+  const int64_t s_first = (int64_t)blockIdx.y * sps;
+  const int64_t S = (S_total - s_first < sps ? S_total - s_first : sps);  // >= 1 by plan
+  const int64_t kbase = s_first * KB;
 
-  const uint8_t* pa[LA];
-  const uint8_t* pb[LB];
-  int la_off[LA], lb_off[LB];
+  // DMA sources of this lane for stage 0 (rows past M / N re-read the last row)
+  const uint8_t* src[IPW];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int c = tid + NT * i;
-    int64_t r = m0 + c / CPR;
-    r = r < M ? r : M - 1;
-    pa[i] = A + r * pitch + kbase + (c % CPR) * 16;
-    la_off[i] = (c / CPR) * PITCH + (c % CPR) * 16;
+  for (int j = 0; j < IA; ++j) {
+    const int slot = (wave * IA + j) * 64 + lane;
+    const int row = slot / CPR, c = (slot % CPR) ^ chunk_swz<KB>(row);
+    const int64_t r = m0 + row < M ? m0 + row : M - 1;
+    src[j] = A + r * pitch + kbase + c * 16;
   }
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int c = tid + NT * i;
-    int64_t r = n0 + c / CPR;
-    r = r < N ? r : N - 1;
-    pb[i] = B + r * pitch + kbase + (c % CPR) * 16;
-    lb_off[i] = (c / CPR) * PITCH + (c % CPR) * 16;
+  for (int j = 0; j < IB; ++j) {
+    const int slot = (wave * IB + j) * 64 + lane;
+    const int row = slot / CPR, c = (slot % CPR) ^ chunk_swz<KB>(row);
+    const int64_t r = n0 + row < N ? n0 + row : N - 1;
+    src[IA + j] = B + r * pitch + kbase + c * 16;
   }
-  u32x4 ra[P][LA], rb[P][LB];
-#pragma unroll
-  for (int i = 0; i < LA; ++i)
-    *reinterpret_cast<u32x4*>(As[0] + la_off[i]) = *reinterpret_cast<const u32x4*>(pa[i]);
-#pragma unroll
-  for (int i = 0; i < LB; ++i)
-    *reinterpret_cast<u32x4*>(Bs[0] + lb_off[i]) = *reinterpret_cast<const u32x4*>(pb[i]);
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int64_t kb = (1 + p < S ? 1 + p : S - 1) * KB;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) ra[p][i] = *reinterpret_cast<const u32x4*>(pa[i] + kb);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) rb[p][i] = *reinterpret_cast<const u32x4*>(pb[i] + kb);
-  }
-  __syncthreads();
+#define HLQ_GEMM_ISSUE(st, bf)                                                           \
+  do {                                                                                   \
+    uint8_t* base_ = lds + (bf) * G::STAGE;                                              \
+    for (int j = 0; j < IA; ++j) lds_dma16(src[j] + (st) * KB, base_ + (wave * IA + j) * 1024); \
+    for (int j = 0; j < IB; ++j)                                                         \
+      lds_dma16(src[IA + j] + (st) * KB, base_ + BM * KB + (wave * IB + j) * 1024);      \
+  } while (0)
+  // wait until at most k stages of this wave's DMA are still in flight
+#define HLQ_GEMM_WAIT(k)                                        \
+  do {                                                          \
+    const int64_t k_ = (k);                                     \
+    if (k_ <= 0) wait_vmcnt<0>();                               \
+    else if (k_ == 1) wait_vmcnt<IPW>();                        \
+    else if (k_ == 2) wait_vmcnt<(2 * IPW < 63 ? 2 * IPW : 63)>(); \
+    else wait_vmcnt<(3 * IPW < 63 ? 3 * IPW : 63)>();           \
+  } while (0)
 
-  v4i acc[TM][TN];
+  const int fr = lane & 31, fh = lane >> 5;
+  const int a_off = (wm * G::WTM + fr) * KB;
+  const int b_off = BM * KB + (wn * G::WTN + fr) * KB;
+  const int sw = chunk_swz<KB>(fr);
+  int coff[KK];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-  const int fr = lane & 15, fg = lane >> 4;
+  for (int kk = 0; kk < KK; ++kk) coff[kk] = ((kk * 2 + fh) ^ sw) * 16;
 
-  const int64_t S_main = S - S % P;
-  for (int64_t s0 = 0; s0 < S_main; s0 += P) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int64_t st = s0 + p;
-      const int nb = (int)((st + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(As[nb] + la_off[i]) = ra[p][i];
-#pragma unroll
-      for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(Bs[nb] + lb_off[i]) = rb[p][i];
-      const int64_t kl = (st + 1 + P < S ? st + 1 + P : S - 1) * KB;
-#pragma unroll
-      for (int i = 0; i < LA; ++i) ra[p][i] = *reinterpret_cast<const u32x4*>(pa[i] + kl);
-#pragma unroll
-      for (int i = 0; i < LB; ++i) rb[p][i] = *reinterpret_cast<const u32x4*>(pb[i] + kl);
-      gemm_stage<INT4, BM, BN, WM, WN, KB>(As[nb ^ 1], Bs[nb ^ 1], wm, wn, fr, fg, acc);
-      __syncthreads();
-    }
-  }
-  // last S mod P stages: their data already sits in slots 0..R-1
-#define HLQ_GEMM_TAIL(R)                                                                   \
-  case R: {                                                                                \
-    _Pragma("unroll") for (int p = 0; p < R; ++p) {                                       \
-      const int nb = (int)((S_main + p + 1) & 1);                                          \
-      if (p + 1 < R) {                                                                     \
-        _Pragma("unroll") for (int i = 0; i < LA; ++i)                                     \
-            *reinterpret_cast<u32x4*>(As[nb] + la_off[i]) = ra[p][i];                      \
-        _Pragma("unroll") for (int i = 0; i < LB; ++i)                                     \
-            *reinterpret_cast<u32x4*>(Bs[nb] + lb_off[i]) = rb[p][i];                      \
-      }                                                                                    \
-      gemm_stage<INT4, BM, BN, WM, WN, KB>(As[nb ^ 1], Bs[nb ^ 1], wm, wn, fr, fg, acc);   \
-      __syncthreads();                                                                     \
-    }                                                                                      \
-  } break;
-  switch ((int)(S - S_main)) {
-    HLQ_GEMM_TAIL(1)
-    HLQ_GEMM_TAIL(2)
-    HLQ_GEMM_TAIL(3)
-    default: break;
-  }
-#undef HLQ_GEMM_TAIL
+  for (int p = 0; p < NS; ++p)
+    if (p < S) HLQ_GEMM_ISSUE(p, p);
 
-  constexpr int SH = INT4 ? 8 : 0;
+  v16i acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + wm * (BM / WM) + i * 16 + fr;
-    if (m >= M) continue;
-    const float s_m = (EPI == EPI_F32) ? sa[m * sa_step] * alpha : 0.f;
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t nn = n0 + wn * (BN / WN) + j * 16 + fg * 4;
-      if (nn >= N) continue;
-      v4i r = acc[i][j];
-      if constexpr (EPI == EPI_F32) {
-        float4 o;
-        o.x = (float)(r[0] >> SH) * s_m * sb[(nn + 0) * sb_step];
-        o.y = (float)(r[1] >> SH) * s_m * sb[(nn + 1) * sb_step];
-        o.z = (float)(r[2] >> SH) * s_m * sb[(nn + 2) * sb_step];
-        o.w = (float)(r[3] >> SH) * s_m * sb[(nn + 3) * sb_step];
-        *reinterpret_cast<float4*>(C + m * N + nn) = o;
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  u32x4 fa[2][FM], fb[2][FN];
+  HLQ_GEMM_WAIT((S - 1 < NS - 1 ? S - 1 : NS - 1));
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    fa[0][i] = *reinterpret_cast<const u32x4*>(lds + a_off + i * 32 * KB + coff[0]);
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    fb[0][j] = *reinterpret_cast<const u32x4*>(lds + b_off + j * 32 * KB + coff[0]);
+
+  int buf = 0;
+  for (int64_t st = 0; st < S; ++st) {
+    const uint8_t* base = lds + buf * G::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk + 1 < KK) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fa[nxt][i] = *reinterpret_cast<const u32x4*>(base + a_off + i * 32 * KB + coff[kk + 1]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[nxt][j] = *reinterpret_cast<const u32x4*>(base + b_off + j * 32 * KB + coff[kk + 1]);
+      }
+      if constexpr (INT4) {
+        v4i xa0[FM], xa1[FM], yb0[FN], yb1[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) widen_int4x2(fa[cur][i], xa0[i], xa1[i]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) widen_int4x2(fb[cur][j], yb0[j], yb1[j]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa0[i], yb0[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa1[i], yb1[j], acc[i][j], 0, 0, 0);
+        if (kk + 1 < KK) {
+          // next fragments' reads between MFMAs, widening spread behind them
+#pragma unroll
+          for (int q = 0; q < FM + FN; ++q) { HLQ_SGB(0x100, 1); HLQ_SGB(0x008, 1); HLQ_SGB(0x002, 12); }
+          HLQ_SGB(0x008, 2 * FM * FN - (FM + FN));
+        }
       } else {
-        int32_t* dst = Ci + (EPI == EPI_PARTIAL ? (int64_t)blockIdx.y * M * N : 0) + m * N + nn;
-        *reinterpret_cast<int4*>(dst) = make_int4(r[0] >> SH, r[1] >> SH, r[2] >> SH, r[3] >> SH);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const u32x4 xa = fa[cur][i], yb = fb[cur][j];
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                v4i{(int)xa[0], (int)xa[1], (int)xa[2], (int)xa[3]},
+                v4i{(int)yb[0], (int)yb[1], (int)yb[2], (int)yb[3]}, acc[i][j], 0, 0, 0);
+          }
+        if (kk + 1 < KK) {
+#pragma unroll
+          for (int q = 0; q < FM + FN; ++q) { HLQ_SGB(0x100, 1); HLQ_SGB(0x008, 1); }
+          if (FM * FN > FM + FN) HLQ_SGB(0x008, FM * FN - (FM + FN));
+        }
+      }
+      if (kk + 1 == KK && st + 1 < S) {
+        // stage st+1 landed in every wave (st+2 .. st+NS-1 may still fly) ...
+        HLQ_GEMM_WAIT((S - st - 2 < NS - 2 ? S - st - 2 : NS - 2));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // ... and no wave reads stage st any more: refill its buffer
+        if (st + NS < S) HLQ_GEMM_ISSUE(st + NS, buf);
+        buf = buf + 1 == NS ? 0 : buf + 1;
+        const uint8_t* nb = lds + buf * G::STAGE;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fa[0][i] = *reinterpret_cast<const u32x4*>(nb + a_off + i * 32 * KB + coff[0]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[0][j] = *reinterpret_cast<const u32x4*>(nb + b_off + j * 32 * KB + coff[0]);
       }
     }
+  }
+#undef HLQ_GEMM_ISSUE
+#undef HLQ_GEMM_WAIT
+
+  constexpr int SH = INT4 ? 8 : 0;
+  int32_t* Cp = Ci + (EPI == EPI_PARTIAL ? (int64_t)blockIdx.y * M * N : 0);
+  float s_n[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
+    s_n[j] = (EPI == EPI_F32 && n < N) ? sb[n * sb_step] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t m = m0 + wm * G::WTM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
+      if (m >= M) continue;
+      const float s_m = (EPI == EPI_F32) ? sa[m * sa_step] * alpha : 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
+        if (n >= N) continue;
+        const int32_t v = acc[i][j][r] >> SH;
+        if constexpr (EPI == EPI_F32) C[m * N + n] = (float)v * s_m * s_n[j];
+        else Cp[m * N + n] = v;
+      }
   }
 }
 
@@ -1039,40 +1084,44 @@ hipError_t launch_tr_reduce(const TrArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Tile configurations (rows of A x rows of B, stage depth, ring depth):
+//   0: 128 x 128, KB  64, 3 stages  (48 KB LDS, two workgroups per CU)
+//   1: 256 x 128, KB  64, 3 stages  (72 KB LDS, two workgroups per CU)
+//   2: 128 x 128, KB 128, 2 stages  (64 KB LDS, two workgroups per CU)
+// Large grids take the 256 x 128 tile; INT8 operands with K a multiple of 128
+// bytes take the deeper stage; grids below the CU count split K.
 GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes) {
-  static const int cfg_bm[4] = {256, 128, 64, 64}, cfg_bn[4] = {128, 128, 128, 64};
+  static const int cfg_bm[3] = {128, 256, 128}, cfg_bn[3] = {128, 128, 128};
+  static const int cfg_kb[3] = {64, 64, 128};
   GemmPlan p;
   auto tiles = [&](int c) { return (int64_t)cdiv(M, cfg_bm[c]) * cdiv(N, cfg_bn[c]); };
-  const int64_t want = int4 ? 1024 : 512;
-  if (tiles(0) >= want) p.cfg = 0;
-  else if (int4 && tiles(1) >= want) p.cfg = 1;
-  else if (int4 || tiles(2) >= 200) p.cfg = 2;
-  else p.cfg = 3;
+  if (tiles(1) >= 1024) p.cfg = 1;
+  else if (!int4 && kbytes % 128 == 0) p.cfg = 2;
+  else p.cfg = 0;
   p.bm = cfg_bm[p.cfg];
   p.bn = cfg_bn[p.cfg];
-  p.stages = kbytes / 64;
-  // split K when the tile grid cannot fill the 256 CUs
+  p.kb = cfg_kb[p.cfg];
+  p.stages = kbytes / p.kb;
   const int64_t t = tiles(p.cfg);
   int64_t sp = 1;
-  while (t * sp < 256 && p.stages / (sp * 2) >= 16 && sp < 8) sp *= 2;
-  while (sp > 1 && p.stages % sp) sp /= 2;  // splits divide the stage count
-  p.splits = (int)sp;
+  while (t * sp < 256 && sp < 8 && p.stages / (sp * 2) >= 8) sp *= 2;
+  p.sps = (p.stages + sp - 1) / sp;
+  p.splits = (int)((p.stages + p.sps - 1) / p.sps);  // every split non-empty
   return p;
 }
 
 template <bool I4, int EPI>
 static void gemm_dispatch(int cfg, dim3 g, hipStream_t s, const uint8_t* A, const uint8_t* B,
-                          int64_t M, int64_t N, int64_t pitch, int64_t sps, const float* sa,
-                          int sa_step, const float* sb, int sb_step, float alpha, float* C,
-                          int32_t* Ci) {
-#define HLQ_GEMM(BM_, BN_, WM_, WN_, P_, KB_)                                                  \
-  hipLaunchKernelGGL((k_gemm<I4, BM_, BN_, WM_, WN_, P_, KB_, EPI>), g, dim3(64 * WM_ * WN_), \
-                     0, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, Ci)
+                          int64_t M, int64_t N, int64_t pitch, int64_t stages, int64_t sps,
+                          const float* sa, int sa_step, const float* sb, int sb_step,
+                          float alpha, float* C, int32_t* Ci) {
+#define HLQ_GEMM(BM_, BN_, KB_, NS_)                                                     \
+  hipLaunchKernelGGL((k_gemm<I4, BM_, BN_, KB_, NS_, EPI>), g, dim3(256), 0, s, A, B, M, N, \
+                     pitch, stages, sps, sa, sa_step, sb, sb_step, alpha, C, Ci)
   switch (cfg) {
-    case 0: HLQ_GEMM(256, 128, 4, 2, 3, 64); break;
-    case 1: HLQ_GEMM(128, 128, 2, 2, 2, 64); break;
-    case 2: HLQ_GEMM(64, 128, 2, 2, 4, 64); break;
-    default: HLQ_GEMM(64, 64, 2, 2, 4, 64); break;
+    case 1: HLQ_GEMM(256, 128, 64, 3); break;
+    case 2: HLQ_GEMM(128, 128, 128, 2); break;
+    default: HLQ_GEMM(128, 128, 64, 3); break;
   }
 #undef HLQ_GEMM
 }
@@ -1082,8 +1131,9 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
                        const float* sa, int sa_step, const float* sb, int sb_step,
                        float alpha, GemmEpi epi, float* C, int32_t* Ci,
                        int32_t* partial, hipStream_t s) {
+  if (pitch % plan.kb != 0 || plan.stages * plan.kb != pitch) return hipErrorInvalidValue;
   const int splits = epi == EPI_I32 ? 1 : plan.splits;
-  const int64_t sps = plan.stages / splits;
+  const int64_t sps = splits == 1 ? plan.stages : plan.sps;
   const int64_t tiles = (int64_t)cdiv(M, plan.bm) * cdiv(N, plan.bn);
   dim3 grid((unsigned)((tiles + 7) / 8 * 8), splits);
   const bool use_partial = (epi == EPI_F32 && splits > 1);
@@ -1094,13 +1144,13 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
   const int e = use_partial ? EPI_PARTIAL : epi;
   int32_t* dst = use_partial ? partial : Ci;
   if (int4) {
-    if (e == EPI_F32) gemm_dispatch<true, EPI_F32>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else if (e == EPI_I32) gemm_dispatch<true, EPI_I32>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else gemm_dispatch<true, EPI_PARTIAL>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    if (e == EPI_F32) gemm_dispatch<true, EPI_F32>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    else if (e == EPI_I32) gemm_dispatch<true, EPI_I32>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    else gemm_dispatch<true, EPI_PARTIAL>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
   } else {
-    if (e == EPI_F32) gemm_dispatch<false, EPI_F32>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else if (e == EPI_I32) gemm_dispatch<false, EPI_I32>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else gemm_dispatch<false, EPI_PARTIAL>(plan.cfg, grid, s, A, B, M, N, pitch, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    if (e == EPI_F32) gemm_dispatch<false, EPI_F32>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    else if (e == EPI_I32) gemm_dispatch<false, EPI_I32>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    else gemm_dispatch<false, EPI_PARTIAL>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !use_partial) return err;
