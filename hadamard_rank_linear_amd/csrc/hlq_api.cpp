@@ -34,8 +34,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct Layout {
   hlq_workspace_layout pub;
   size_t part_gy, part_gyl, part_xl, part_w;  // partial maxima of the MAX pass
-  size_t max_gy, max_gyl, max_xl, max_w;      // folded per-token maxima
-  size_t bmax;                                // per-block maxima [4][nred]
+  size_t inv_gy, inv_gyl, inv_xl, inv_w;      // reciprocal scales of per-token maxima
+  size_t tmax;                                // tensor maxima (float bits) [4]
   int64_t nred;
   size_t partial;                             // int32 split-K partials
   int64_t nch_o, nch_i, ntr_t, ntr_o;         // transform tile grid
@@ -82,15 +82,15 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   L.ntr_t = (T + hlq::TR_ROWS - 1) / hlq::TR_ROWS;
   L.ntr_o = (O + hlq::TR_ROWS - 1) / hlq::TR_ROWS;
   L.part_gy = take((size_t)L.nch_o * T * 4);
-  L.part_gyl = take((size_t)L.ntr_t * O * 4);
+  L.part_gyl = take((size_t)((T + hlq::TR_GY_REG_ROWS - 1) / hlq::TR_GY_REG_ROWS) * O * 4);
   L.part_xl = take((size_t)L.ntr_t * I * 4);
   L.part_w = take((size_t)L.ntr_o * I * 4);
-  L.max_gy = take((size_t)T * 4);
-  L.max_gyl = take((size_t)O * 4);
-  L.max_xl = take((size_t)I * 4);
-  L.max_w = take((size_t)I * 4);
+  L.inv_gy = take((size_t)T * 4);
+  L.inv_gyl = take((size_t)O * 4);
+  L.inv_xl = take((size_t)I * 4);
+  L.inv_w = take((size_t)I * 4);
   L.nred = (T + O + 2 * I + hlq::TR_RED_ENTRIES - 1) / hlq::TR_RED_ENTRIES;
-  L.bmax = take((size_t)4 * L.nred * 4);
+  L.tmax = take(4 * 4);
   // split-K partials: the two GEMMs run one after the other on one stream and
   // share this buffer
   size_t part = 0;
@@ -202,12 +202,17 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
   a.s_gyl = f32(L.pub.s_gyl); a.s_xl = f32(L.pub.s_xl);
   a.part_gy = f32(L.part_gy); a.part_gyl = f32(L.part_gyl);
   a.part_xl = f32(L.part_xl); a.part_w = f32(L.part_w);
-  a.max_gy = f32(L.max_gy); a.max_gyl = f32(L.max_gyl);
-  a.max_xl = f32(L.max_xl); a.max_w = f32(L.max_w);
-  a.bmax = f32(L.bmax);
+  a.inv_gy = f32(L.inv_gy); a.inv_gyl = f32(L.inv_gyl);
+  a.inv_xl = f32(L.inv_xl); a.inv_w = f32(L.inv_w);
+  a.tmax = reinterpret_cast<unsigned*>(ws + L.tmax);
   a.nred = L.nred;
   a.nch_o = L.nch_o; a.nch_i = L.nch_i; a.ntr_t = L.ntr_t; a.ntr_o = L.ntr_o;
-  a.wg_gy = L.ntr_t * L.nch_o;
+  // bf16 g_y with n <= 64 runs the register-resident kernel (64-token tiles;
+  // part_gyl is sized for them)
+  a.gy_reg = (gy_dtype == HLQ_BF16 && block <= 64) ? 1 : 0;
+  a.ntr_gy = a.gy_reg ? (T + hlq::TR_GY_REG_ROWS - 1) / hlq::TR_GY_REG_ROWS : L.ntr_t;
+  a.wg_gy = a.ntr_gy * L.nch_o;
+  a.gy_workers = 0;  // chosen per pass by launch_tr
   a.wg_x = L.ntr_t * L.nch_i;
   a.wg_w = L.ntr_o * L.nch_i;
   int32_t* partial = reinterpret_cast<int32_t*>(ws + L.partial);

@@ -16,6 +16,7 @@ enum TrPass { PASS_MAX = 0, PASS_QUANT = 1 };
 constexpr int TR_ROWS = 128;
 constexpr int TR_COLS = 128;
 constexpr int TR_RED_ENTRIES = 64;  // entries folded per reduce block
+constexpr int TR_GY_REG_ROWS = 64;   // token rows of a register-resident g_y tile (one wave)
 
 // Everything the three transform launches (MAX, reduce, QUANT) read and write.
 struct TrArgs {
@@ -27,16 +28,23 @@ struct TrArgs {
   uint8_t *q_gy, *q_w, *q_gyl, *q_xl;
   float *s_gy, *s_w, *s_gyl, *s_xl;
   // partial maxima: rows of H.g_y per column chunk [nch_o][T]; low-rank g_y
-  // columns per token range [ntr_t][O]; low-rank x [ntr_t][I]; H.w [ntr_o][I]
+  // columns per token range [ntr_gy][O] (ntr_gy <= ceil(T / TR_GY_REG_ROWS));
+  // low-rank x [ntr_t][I]; H.w [ntr_o][I]
   float *part_gy, *part_gyl, *part_xl, *part_w;
-  // folded maxima (per-token modes)
-  float *max_gy, *max_gyl, *max_xl, *max_w;
-  // per-block maxima of the reduce launch, [4][nred]: list 0 H.g_y, 1 H.w,
-  // 2 low-rank g_y, 3 low-rank x (tensor maxima are folded from these)
-  float* bmax;
+  // reciprocal scales qmax / max of the folded maxima (per-token modes)
+  float *inv_gy, *inv_gyl, *inv_xl, *inv_w;
+  // tensor maxima as float bit patterns, [4]: list 0 H.g_y, 1 H.w,
+  // 2 low-rank g_y, 3 low-rank x (zeroed by the MAX pass, folded by reduce)
+  unsigned* tmax;
   int64_t nred;  // reduce blocks = ceil((T + O + 2 I) / TR_RED_ENTRIES)
   int64_t nch_o, nch_i, ntr_t, ntr_o;
-  int64_t wg_gy, wg_x, wg_w;
+  // gy_reg: the MAX pass runs g_y on the register-resident kernel (bf16 g_y,
+  // n <= 64, TR_GY_REG_ROWS-token tiles, wg_gy of them); ntr_gy = its token
+  // tiles (rows of part_gyl).  The LDS engine uses TR_ROWS-token tiles.
+  int gy_reg;
+  int64_t ntr_gy;
+  int64_t wg_gy, wg_x, wg_w;  // tiles of each job
+  int64_t gy_workers;         // g_y tiles of the shared kernel (set per launch)
 };
 
 // Launch configuration of one integer GEMM C[m][n] = sum_k A[m][k] B[n][k],

@@ -101,12 +101,27 @@ __device__ __forceinline__ uint32_t quant_bits(float v, float inv) {
   return __float_as_uint(p + 12582912.0f);
 }
 
-// 8 INT4 codes of v[0..8) packed two per byte, element 2k in the low nibble.
+// Low bytes of four words gathered into one word (byte i <- w_i), 3 v_perm.
+__device__ __forceinline__ uint32_t pack_lo_bytes(uint32_t w0, uint32_t w1, uint32_t w2,
+                                                  uint32_t w3) {
+  const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u);  // w0.b0 w1.b0 0 0
+  const uint32_t hi = __builtin_amdgcn_perm(w3, w2, 0x0c0c0400u);  // w2.b0 w3.b0 0 0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// 8 INT4 codes packed two per byte, element 2k in the low nibble: the low
+// bytes of the even and odd elements are gathered, then nibble-merged.
+__device__ __forceinline__ uint32_t pack8_nibbles(const uint32_t (&q)[8]) {
+  const uint32_t ev = pack_lo_bytes(q[0], q[2], q[4], q[6]);
+  const uint32_t od = pack_lo_bytes(q[1], q[3], q[5], q[7]);
+  return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+}
+
 __device__ __forceinline__ uint32_t quant_pack8_int4(const float (&v)[8], float inv) {
-  uint32_t u = 0;
+  uint32_t q[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) u |= (quant_bits<7>(v[k], inv) & 0xFu) << (4 * k);
-  return u;
+  for (int k = 0; k < 8; ++k) q[k] = quant_bits<7>(v[k], inv);
+  return pack8_nibbles(q);
 }
 
 // Reciprocal scale of a group with absmax a.  A zero group, and a group so
@@ -144,6 +159,17 @@ __global__ __launch_bounds__(256) void k_acbp(const void* __restrict__ x, int64_
     *reinterpret_cast<uint32_t*>(out + c / 2) = quant_pack8_int4(v, inv);
   }
   if (lane == 0) scales[row] = scale_of(a, 7.f);
+}
+
+// Workgroup id -> tile id such that each of the 8 XCDs (which take workgroup
+// ids round-robin) runs one contiguous range of tiles.  Neighbouring tiles
+// write neighbouring pieces of the same output lines, which then meet in one
+// L2 instead of leaving it as partial lines from several.  The grid is
+// rounded up to a multiple of 8; ids past the last tile return -1.
+__device__ __forceinline__ int64_t xcd_range_tile(int64_t w, int64_t total) {
+  const int64_t per = (total + 7) / 8;
+  const int64_t t = (w % 8) * per + w / 8;
+  return t < total ? t : -1;
 }
 
 // ------------------------------------------------------------ operand transforms
@@ -205,21 +231,6 @@ struct RdI4 {
     return s[r] * (float)code;
   }
 };
-
-// Tensor maximum of list l (0 H.g_y, 1 H.w, 2 low-rank g_y, 3 low-rank x):
-// the max over the per-block maxima k_tr_reduce left (a few hundred floats,
-// L2-resident); every QUANT workgroup folds it itself, so no atomics.  All
-// threads of the workgroup must call it.
-__device__ __forceinline__ float tensor_max(const TrArgs& a, int l) {
-  __shared__ float part[4];
-  float m = 0.f;
-  for (int64_t i = threadIdx.x; i < a.nred; i += 256) m = fmaxf(m, a.bmax[l * a.nred + i]);
-  m = wave_max(m);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
-  __syncthreads();
-  return fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-}
 
 __device__ __forceinline__ float max_over_16_lanes(float a) {
 #pragma unroll
@@ -360,23 +371,24 @@ __device__ __forceinline__ void store_staged(const uint8_t (*outs)[OUT_BYTES], i
   }
 }
 
-// Zero bytes [from, to) of `cols` rows of a K-major operand (K padding).
+// Zero bytes [from, to) of `cols` rows of a K-major operand (K padding);
+// nthr threads share the work.
 __device__ __forceinline__ void zero_tail(uint8_t* dst, int64_t pitch, int cols, int64_t from,
-                                          int64_t to, int tid) {
+                                          int64_t to, int tid, int nthr = 256) {
   const int64_t w = to - from;
   if (w <= 0) return;
-  for (int64_t i = tid; i < (int64_t)cols * w; i += 256) dst[(i / w) * pitch + from + i % w] = 0;
+  for (int64_t i = tid; i < (int64_t)cols * w; i += nthr) dst[(i / w) * pitch + from + i % w] = 0;
 }
 
 // Column pass, low-rank rows of H_N (g_w operands).  Thread tid owns column
 // c = tid % CW and blocks b = tid / CW + 2t.  MAX: the tile's column maxima ->
-// part[0..cols).  QUANT: INT8 codes (scale from colmax[c], or from tensor
-// list `list` when colmax is null) staged in LDS over the tile (after a
+// part[0..cols).  QUANT: INT8 codes (reciprocal scale colinv[c], or that of tensor
+// list `list` when colinv is null) staged in LDS over the tile (after a
 // barrier) and stored K-contiguous at q[(c0 + c) * pitch + t0 / N * R ...].
 template <int PASS, int N, int R, class RD>
 __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, uint8_t* smem,
                                                 float* red, int rows, int cols, int64_t c0,
-                                                const float* colmax, int list, float* part,
+                                                const float* colinv, int list, float* part,
                                                 uint8_t* q, int64_t pitch, int64_t tl,
                                                 int64_t t0, bool last) {
   constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;  // tasks per thread
@@ -386,9 +398,8 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
   const int nb = rows / N;
   float inv_c = 0.f;
   if constexpr (PASS == PASS_QUANT) {
-    const float tmax = colmax ? 0.f : tensor_max(a, list);
-    const float amax = colmax ? (c < cols ? colmax[c0 + c] : 0.f) : tmax;
-    inv_c = inv_of(amax, 127.f);
+    const float tinv = colinv ? 0.f : inv_of(__uint_as_float(a.tmax[list]), list == 1 ? 7.f : 127.f);
+    inv_c = colinv ? (c < cols ? colinv[c0 + c] : 0.f) : tinv;
   }
   float cm = 0.f;
   uint32_t words[TPT][WPR];
@@ -440,7 +451,7 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
 template <int PASS, int N, class RD>
 __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint8_t* smem,
                                              float* red, int rows, int cols, int64_t c0,
-                                             const float* colmax, int list, float* part,
+                                             const float* colinv, int list, float* part,
                                              uint8_t* q, int64_t pitch, int64_t o0, int64_t O,
                                              bool last) {
   constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;
@@ -450,9 +461,8 @@ __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint
   const int nb = rows / N;
   float inv_c = 0.f;
   if constexpr (PASS == PASS_QUANT) {
-    const float tmax = colmax ? 0.f : tensor_max(a, list);
-    const float amax = colmax ? (c < cols ? colmax[c0 + c] : 0.f) : tmax;
-    inv_c = inv_of(amax, 7.f);
+    const float tinv = colinv ? 0.f : inv_of(__uint_as_float(a.tmax[list]), list == 1 ? 7.f : 127.f);
+    inv_c = colinv ? (c < cols ? colinv[c0 + c] : 0.f) : tinv;
   }
   float cm = 0.f;
   uint32_t words[TPT][WPT];
@@ -517,7 +527,7 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
   }
   float inv_tensor = 0.f;
   if constexpr (PASS == PASS_QUANT) {
-    if (!a.gx_tok) inv_tensor = inv_of(tensor_max(a, 0), 7.f);
+    if (!a.gx_tok) inv_tensor = inv_of(__uint_as_float(a.tmax[0]), 7.f);
   }
 #pragma unroll
   for (int sw = 0; sw < SW; ++sw) {
@@ -534,7 +544,7 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
       m = max_over_16_lanes(m);
       if (lc == 0 && row < rows) a.part_gy[ch * a.T + t0 + row] = m;
     } else if (row < rows) {
-      const float inv = a.gx_tok ? inv_of(a.max_gy[t0 + row], 7.f) : inv_tensor;
+      const float inv = a.gx_tok ? a.inv_gy[t0 + row] : inv_tensor;
       // columns past O inside the chunk are zero -> zero codes (K padding)
       *reinterpret_cast<uint32_t*>(a.q_gy + (t0 + row) * a.kxb + (c0 + col) / 2) =
           col < cols ? quant_pack8_int4(v, inv) : 0u;
@@ -544,13 +554,225 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
   const bool last = t0 + rows == a.T;
   if constexpr (F32) {
     RdF32 rd{reinterpret_cast<const float*>(smem)};
-    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.max_gyl : nullptr,
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_gyl : nullptr,
                                 2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.kwb, a.tl, t0, last);
   } else {
     RdB16 rd{reinterpret_cast<const uint16_t*>(smem)};
-    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.max_gyl : nullptr,
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_gyl : nullptr,
                                 2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.kwb, a.tl, t0, last);
   }
+}
+
+// ---- MAX pass over g_y tiles held in registers (bf16 g_y, n <= 64)
+// One wave per tile of GYR_ROWS = 64 tokens x CW = 128 channels; the waves of
+// a workgroup never wait for each other and finish independently.
+// Lane c16 = lane & 7 owns channels c0 + 16 c16 .. +15 and row group
+// rg = lane >> 3 owns tokens t0 + 8 rg .. +7, loaded once into registers
+// (8 tokens x 32 bytes).  A Hadamard block of n
+// channels spans n/16 adjacent lanes; a block of n tokens spans n/8 row
+// groups of one wave, i.e. lanes 8 apart.  Nothing goes through LDS:
+//   * along O (g_x operand A): per token, stages h = 1..8 in-lane, stages
+//     h >= 16 across lanes c16 ^ h/16 (DPP quad permutes);
+//   * along T (g_w operand): per channel, stages h = 1, 2, 4 over the lane's
+//     8 tokens, stages h = 8, 16, 32 across lanes 8, 16, 32 apart.
+// The low-rank rows are the butterfly network pruned to its surviving
+// entries: stages with h < n/r keep only a + b (the pairwise-tree group sums),
+// the later stages are full butterflies over the group sums (H_r), all in
+// ascending h as the full transform runs them.
+constexpr int GYR_ROWS = TR_GY_REG_ROWS;
+
+// Value of lane ^ M of the wave (M = 1, 2: DPP quad permute; 8: DPP row
+// rotate by 8; 4, 16: swizzle inside 32 lanes; 32: bpermute).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int b = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));
+  else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));
+  else if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));
+  else if constexpr (M == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x101F));
+  else if constexpr (M == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x401F));
+  else return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) & 63) * 4, b));
+}
+
+// Max over the 8 lanes c16 = 0..7 of a row group (quad swaps, then the
+// half-row mirror pairs each lane with one of the other quad).
+__device__ __forceinline__ float group8_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, true)));
+  return m;
+}
+
+// Butterfly stage with the partner lane ^ M: the lower lane keeps
+// own + partner, the upper partner - own; fma(+-1, own, partner) is that one
+// IEEE add, so the result equals the in-register butterfly bit for bit.
+template <int M>
+__device__ __forceinline__ float xbfly(float v, float sgn) {
+  return __builtin_fmaf(sgn, v, lane_xor<M>(v));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// max |v[i]| over 16 values with three-input maxima
+__device__ __forceinline__ float absmax16(const float (&v)[16]) {
+  float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) m = fmaxf(fmaxf(m, fabsf(v[i])), fabsf(v[i + 1]));
+  return fmaxf(m, fabsf(v[15]));
+}
+
+// Registers of one tile (zero outside T and O).
+__device__ __forceinline__ void gyr_load(const TrArgs& a, int64_t bid, uint4 (&raw)[8][2]) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tr = bid / a.nch_o, ch = bid % a.nch_o;
+  const int64_t t0 = tr * GYR_ROWS, c0 = ch * CW;
+  const int rows = (int)(a.T - t0 < GYR_ROWS ? a.T - t0 : GYR_ROWS);
+  const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
+  const int col = (lane & 7) * 16, r0 = (lane >> 3) * 8;
+  const bool ok = r0 < rows && col < cols;
+  const uint16_t* gy = static_cast<const uint16_t*>(a.gy);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    raw[k][0] = make_uint4(0, 0, 0, 0);
+    raw[k][1] = make_uint4(0, 0, 0, 0);
+    if (ok) {
+      const uint4* src = reinterpret_cast<const uint4*>(gy + (t0 + r0 + k) * a.O + c0 + col);
+      raw[k][0] = src[0];
+      raw[k][1] = src[1];
+    }
+  }
+}
+
+// Maxima of one tile: row maxima of H.g_y along O -> part_gy[ch][t], column
+// maxima of the low-rank g_y along T -> part_gyl[tr][o].
+template <int N, int R>
+__device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
+                                             const uint4 (&raw)[8][2]) {
+  static_assert(N >= 16 && N <= 64, "a token block spans 2..8 row groups of one wave");
+  constexpr int G = N / R;             // tokens per low-rank group
+  constexpr int GL = G < 8 ? G : 8;    // in-lane span of a group
+  constexpr int RGB = N / 8;           // row groups per token block
+  const int lane = threadIdx.x & 63;
+  const int c16 = lane & 7, rg = lane >> 3;
+  const int64_t tr = bid / a.nch_o, ch = bid % a.nch_o;
+  const int64_t t0 = tr * GYR_ROWS, c0 = ch * CW;
+  const int rows = (int)(a.T - t0 < GYR_ROWS ? a.T - t0 : GYR_ROWS);
+  const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
+  const int col = c16 * 16;
+  const int r0 = rg * 8;               // first token of this lane in the tile
+  const bool act = r0 < rows;          // rows is a multiple of n >= 16
+  const bool cact = col < cols;        // cols is a multiple of n >= 16
+
+  // ---- along O: one token per iteration
+  const float sgn1 = (c16 & 1) ? -1.f : 1.f, sgn2 = (c16 & 2) ? -1.f : 1.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      v[8 * q + 0] = bf16_lo(raw[k][q].x); v[8 * q + 1] = bf16_hi(raw[k][q].x);
+      v[8 * q + 2] = bf16_lo(raw[k][q].y); v[8 * q + 3] = bf16_hi(raw[k][q].y);
+      v[8 * q + 4] = bf16_lo(raw[k][q].z); v[8 * q + 5] = bf16_hi(raw[k][q].z);
+      v[8 * q + 6] = bf16_lo(raw[k][q].w); v[8 * q + 7] = bf16_hi(raw[k][q].w);
+    }
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((e & h) == 0) {
+          const float p = v[e], q = v[e + h];
+          v[e] = p + q;
+          v[e + h] = p - q;
+        }
+    if constexpr (N >= 32) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = xbfly<1>(v[e], sgn1);
+    }
+    if constexpr (N >= 64) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = xbfly<2>(v[e], sgn2);
+    }
+    const float m = group8_max(absmax16(v));
+    if (c16 == 0 && act) a.part_gy[ch * a.T + t0 + r0 + k] = m;
+  }
+
+  // ---- along T: one channel per iteration
+  const int rib = rg % RGB;                                  // row group inside its block
+  const bool owner = (G <= 8) || (rib % (G / 8) == 0);       // holds surviving entries
+  const float sg8 = (rib & 1) ? -1.f : 1.f, sg16 = (rib & 2) ? -1.f : 1.f;
+  const float sg32 = (rib & 4) ? -1.f : 1.f;
+  float cmax[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint4& w4 = raw[k][j / 8];
+      const int jj = j % 8;
+      const uint32_t w = jj < 2 ? w4.x : jj < 4 ? w4.y : jj < 6 ? w4.z : w4.w;
+      x[k] = (jj & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+      if (h < G) {  // group sums: pairwise tree
+#pragma unroll
+        for (int k = 0; k < 8; k += 2 * h) x[k] = x[k] + x[k + h];
+      } else {      // full butterflies over the surviving group sums
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if ((k & h) == 0 && k % G == 0) {
+            const float p = x[k], q = x[k + h];
+            x[k] = p + q;
+            x[k + h] = p - q;
+          }
+      }
+    }
+    if constexpr (N >= 16) {
+#pragma unroll
+      for (int k = 0; k < 8; k += GL) x[k] = (8 < G) ? x[k] + lane_xor<8>(x[k]) : xbfly<8>(x[k], sg8);
+    }
+    if constexpr (N >= 32) {
+#pragma unroll
+      for (int k = 0; k < 8; k += GL) x[k] = (16 < G) ? x[k] + lane_xor<16>(x[k]) : xbfly<16>(x[k], sg16);
+    }
+    if constexpr (N >= 64) {
+#pragma unroll
+      for (int k = 0; k < 8; k += GL) x[k] = (32 < G) ? x[k] + lane_xor<32>(x[k]) : xbfly<32>(x[k], sg32);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k += GL) m = fmaxf(m, fabsf(x[k]));
+    cmax[j] = owner && act && cact ? m : 0.f;
+  }
+  // fold the eight row groups (lanes 8, 16, 32 apart)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float m = cmax[j];
+    m = fmaxf(m, lane_xor<8>(m));
+    m = fmaxf(m, lane_xor<16>(m));
+    m = fmaxf(m, lane_xor<32>(m));
+    cmax[j] = m;
+  }
+  if (lane < 8 && cact) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a.part_gyl[tr * a.O + c0 + col + j] = cmax[j];
+  }
+}
+
+// Four independent waves per workgroup (tiles 4 w .. 4 w + 3 of the
+// XCD-ordered workgroup w): no barriers, and dispatch works in 4-wave units.
+// MAX pass only: the QUANT pass runs the g_y tiles on the LDS engine, whose
+// staged, wide code stores suit the transposed INT8 output better.
+template <int N, int R>
+__global__ __launch_bounds__(256) void k_tr_gy_max(TrArgs a) {
+  const int64_t wg = xcd_range_tile(blockIdx.x, (a.wg_gy + 3) / 4);
+  if (wg < 0) return;
+  const int64_t bid = wg * 4 + (threadIdx.x >> 6);
+  if (bid >= a.wg_gy) return;
+  uint4 raw[8][2];
+  gyr_load(a, bid, raw);
+  gyr_tile_max<N, R>(a, bid, raw);
 }
 
 // ---- job: x tile (ACBP codes, low-rank columns along T for g_w)
@@ -589,7 +811,7 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
         make_uint4(w4[sw][0], w4[sw][1], w4[sw][2], w4[sw][3]);
   __syncthreads();
   RdI4 rd{codes, scales};
-  colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.max_xl : nullptr, 3,
+  colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_xl : nullptr, 3,
                               a.part_xl + tr * a.I + c0, a.q_xl, a.kwb, a.tl, t0,
                               t0 + rows == a.T);
 }
@@ -619,11 +841,11 @@ __device__ void tr_job_w(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
   const bool last = o0 + rows == a.O;
   if constexpr (F32) {
     RdF32 rd{reinterpret_cast<const float*>(smem)};
-    colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.max_w : nullptr, 1,
+    colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.inv_w : nullptr, 1,
                           a.part_w + tr * a.I + c0, a.q_w, a.kxb, o0, a.O, last);
   } else {
     RdB16 rd{reinterpret_cast<const uint16_t*>(smem)};
-    colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.max_w : nullptr, 1,
+    colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.inv_w : nullptr, 1,
                           a.part_w + tr * a.I + c0, a.q_w, a.kxb, o0, a.O, last);
   }
 }
@@ -634,32 +856,26 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
   static_assert(TT * P_I4 + TT * 4 <= TileSmem<F32>::bytes, "x tile fits the smem buffer");
   static_assert(CW * OUT_BYTES <= TileSmem<F32>::bytes, "staging fits the smem buffer");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TileSmem<F32>::bytes];
-  __shared__ float red[256];
-  int64_t bid = blockIdx.x;
-  if constexpr (PASS == PASS_QUANT) {
-    if (bid == 0) {
-      // tensor scales of per-tensor modes (the maxima are final now)
-      const float m0 = a.gx_tok ? 0.f : tensor_max(a, 0);
-      const float m1 = a.gx_tok ? 0.f : tensor_max(a, 1);
-      const float m2 = a.gw_tok ? 0.f : tensor_max(a, 2);
-      const float m3 = a.gw_tok ? 0.f : tensor_max(a, 3);
-      if (threadIdx.x == 0) {
-        if (!a.gx_tok) {
-          a.s_gy[0] = scale_of(m0, 7.f);
-          a.s_w[0] = scale_of(m1, 7.f);
-        }
-        if (!a.gw_tok) {
-          a.s_gyl[0] = scale_of(m2, 127.f);
-          a.s_xl[0] = scale_of(m3, 127.f);
-        }
+  __shared__ float red[4 * CW];
+  int64_t bid = xcd_range_tile(blockIdx.x, a.gy_workers + a.wg_x + a.wg_w);
+  if (bid < 0) return;
+  if constexpr (PASS == PASS_MAX) {
+    if (bid == 0 && threadIdx.x < 4) a.tmax[threadIdx.x] = 0u;  // k_tr_reduce folds into it
+  } else {
+    if (bid == 0 && threadIdx.x < 4) {  // tensor scales of the per-tensor modes
+      const int l = threadIdx.x;
+      const float qmax = l < 2 ? 7.f : 127.f;
+      if (l < 2 ? !a.gx_tok : !a.gw_tok) {
+        float* sc = l == 0 ? a.s_gy : l == 1 ? a.s_w : l == 2 ? a.s_gyl : a.s_xl;
+        sc[0] = scale_of(__uint_as_float(a.tmax[l]), qmax);
       }
     }
   }
-  if (bid < a.wg_gy) {
+  if (bid < a.gy_workers) {  // g_y tiles on the LDS engine
     tr_job_gy<PASS, N, R, F32>(a, bid, smem, red);
     return;
   }
-  bid -= a.wg_gy;
+  bid -= a.gy_workers;
   if (bid < a.wg_x) {
     tr_job_x<PASS, N, R>(a, bid, smem, red);
     return;
@@ -669,13 +885,13 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
 }
 
 // Fold the partial maxima.  Entry e of each list takes the max over its
-// partials and stores it (per-token modes also store the scale); every block
-// leaves its per-list maximum in bmax[l][block], which QUANT workgroups fold
-// into tensor maxima (tensor_max), so no atomics are needed and the result is
-// schedule-independent.  Lists: T rows of H.g_y, O low-rank g_y columns, I
-// low-rank x columns, I columns of H.w.  A block covers 64 consecutive
-// entries; its 4 waves split each entry's partials (stride 4) so every wave
-// keeps several loads in flight.
+// partials; per-token modes store its scale and reciprocal scale (the QUANT
+// pass multiplies by the latter).  Every block folds its per-list maxima into
+// the four tensor maxima with one atomicMax each (lists: 0 H.g_y rows, 1 H.w
+// columns, 2 low-rank g_y columns, 3 low-rank x columns).  Max is exact and
+// commutes, so the result does not depend on the schedule.  A block covers 64 consecutive entries; its 16
+// waves split each entry's partials (stride 16) so every wave keeps several
+// loads in flight.
 constexpr int RED_ENTRIES = TR_RED_ENTRIES;
 constexpr int RED_WAVES = 16;
 
@@ -688,7 +904,7 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
   int64_t np = 0, stride = 0;
   int list = -1;
   if (e < n0) { list = 0; p = a.part_gy + e; np = a.nch_o; stride = a.T; }
-  else if (e < n1) { list = 2; p = a.part_gyl + (e - n0); np = a.ntr_t; stride = a.O; }
+  else if (e < n1) { list = 2; p = a.part_gyl + (e - n0); np = a.ntr_gy; stride = a.O; }
   else if (e < n2) { list = 3; p = a.part_xl + (e - n1); np = a.ntr_t; stride = a.I; }
   else if (e < n3) { list = 1; p = a.part_w + (e - n2); np = a.ntr_o; stride = a.I; }
   // wave wv folds partials wv, wv + 16, ...; four loads in flight per step
@@ -704,23 +920,27 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
   for (; k < np; k += W) m0 = fmaxf(m0, p[k * stride]);
   wpart[wv][lane] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
   __syncthreads();
-  if (wv != 0) return;
+  if (wv == 0) {
   float m = wpart[0][lane];
 #pragma unroll
   for (int q = 1; q < RED_WAVES; ++q) m = fmaxf(m, wpart[q][lane]);
   if (list == 0) {
-    if (a.gx_tok) { a.max_gy[e] = m; a.s_gy[e] = scale_of(m, 7.f); }
+    if (a.gx_tok) { a.inv_gy[e] = inv_of(m, 7.f); a.s_gy[e] = scale_of(m, 7.f); }
   } else if (list == 2) {
-    if (a.gw_tok) { a.max_gyl[e - n0] = m; a.s_gyl[e - n0] = scale_of(m, 127.f); }
+    if (a.gw_tok) { a.inv_gyl[e - n0] = inv_of(m, 127.f); a.s_gyl[e - n0] = scale_of(m, 127.f); }
   } else if (list == 3) {
-    if (a.gw_tok) { a.max_xl[e - n1] = m; a.s_xl[e - n1] = scale_of(m, 127.f); }
+    if (a.gw_tok) { a.inv_xl[e - n1] = inv_of(m, 127.f); a.s_xl[e - n1] = scale_of(m, 127.f); }
   } else if (list == 1) {
-    if (a.gx_tok) { a.max_w[e - n2] = m; a.s_w[e - n2] = scale_of(m, 7.f); }
+    if (a.gx_tok) { a.inv_w[e - n2] = inv_of(m, 7.f); a.s_w[e - n2] = scale_of(m, 7.f); }
   }
 #pragma unroll
   for (int l = 0; l < 4; ++l) {
+    // tensor maxima: max over blocks by atomicMax on the bit patterns of
+    // non-negative floats (they order like the values), exact and
+    // schedule-independent; zeroed by the MAX pass
     const float v = wave_max(list == l ? m : 0.f);
-    if (lane == 0) a.bmax[l * a.nred + blockIdx.x] = v;
+    if (lane == 0 && v > 0.f) atomicMax(a.tmax + l, __float_as_uint(v));
+  }
   }
 }
 
@@ -1066,11 +1286,48 @@ static hipError_t tr_dispatch(int n, int r, dim3 g, hipStream_t s, const TrArgs&
   return hipGetLastError();
 }
 
-hipError_t launch_tr(const TrArgs& a, int pass, int n, int r, hipStream_t s) {
+static hipError_t tr_gy_max_dispatch(int n, int r, dim3 g, hipStream_t s, const TrArgs& a) {
+#define HLQ_TRG(NN, RR) hipLaunchKernelGGL((k_tr_gy_max<NN, RR>), g, dim3(256), 0, s, a)
+#define HLQ_TRG_N(NN)                                                   \
+  switch (r) {                                                          \
+    case 1: HLQ_TRG(NN, 1); break;                                      \
+    case 2: HLQ_TRG(NN, 2); break;                                      \
+    case 4: HLQ_TRG(NN, 4); break;                                      \
+    case 8: HLQ_TRG(NN, 8); break;                                      \
+    case 16: HLQ_TRG(NN, 16); break;                                    \
+    case 32: if (NN >= 32) HLQ_TRG(NN, (NN >= 32 ? 32 : 1)); break;     \
+    case 64: if (NN >= 64) HLQ_TRG(NN, (NN >= 64 ? 64 : 1)); break;     \
+    default: return hipErrorInvalidValue;                               \
+  }
+  switch (n) {
+    case 16: HLQ_TRG_N(16); break;
+    case 32: HLQ_TRG_N(32); break;
+    case 64: HLQ_TRG_N(64); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef HLQ_TRG_N
+#undef HLQ_TRG
+  return hipGetLastError();
+}
+
+hipError_t launch_tr(const TrArgs& args, int pass, int n, int r, hipStream_t s) {
   if (r > n) return hipErrorInvalidValue;
-  const int64_t wgs = a.wg_gy + a.wg_x + a.wg_w;
+  TrArgs a = args;
+  // g_y tiles of the shared kernel: all LDS-engine tiles, except in the MAX
+  // pass of the register path, which k_tr_gy_max runs instead
+  a.gy_workers = a.ntr_t * a.nch_o;
+  if (pass == PASS_MAX && a.gy_reg) {
+    if (a.gy_dt != 1 || n > 64) return hipErrorInvalidValue;
+    a.gy_workers = 0;
+    if (a.wg_gy > 0) {
+      const dim3 gg((unsigned)(((a.wg_gy + 3) / 4 + 7) / 8 * 8));
+      const hipError_t e = tr_gy_max_dispatch(n, r, gg, s, a);
+      if (e != hipSuccess) return e;
+    }
+  }
+  const int64_t wgs = a.gy_workers + a.wg_x + a.wg_w;
   if (wgs <= 0) return hipSuccess;
-  dim3 g((unsigned)wgs);
+  dim3 g((unsigned)((wgs + 7) / 8 * 8));
   const bool f32 = a.gy_dt == 0 || a.w_dt == 0;
   if (pass == PASS_MAX)
     return f32 ? tr_dispatch<PASS_MAX, true>(n, r, g, s, a) : tr_dispatch<PASS_MAX, false>(n, r, g, s, a);
