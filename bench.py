@@ -42,7 +42,11 @@ def step_costs(cfg, dt_bytes):
     gy = T * O * dt_bytes
     w = O * I * dt_bytes
     xc = T * I // 2 + 4 * T
-    parts = 4 * (T * -(-O // 128) + O * -(-T // 128) + I * -(-T // 128) + I * -(-O // 128))
+    # partial maxima: H.g_y rows per 128-channel chunk, low-rank g_y columns per
+    # token tile (64 tokens on the register path: bf16 g_y with n <= 64, else
+    # 128), low-rank x columns per 128 tokens, H.w columns per 128 channels
+    gy_rows = 64 if (dt_bytes == 2 and cfg.block <= 64) else 128
+    parts = 4 * (T * -(-O // 128) + O * -(-T // gy_rows) + I * -(-T // 128) + I * -(-O // 128))
     return {
         "tr_max": (0, gy + xc + w + parts),
         "tr_reduce": (0, parts + 4 * (T + O + 2 * I)),
@@ -51,6 +55,41 @@ def step_costs(cfg, dt_bytes):
         "gemm_gx": (2 * T * I * O, T * O // 2 + I * O // 2 + 4 * T + 4 * I + 4 * T * I),
         "gemm_gw": (2 * O * I * Tl, O * Tl + I * Tl + 4 * O + 4 * I + 4 * O * I),
     }
+
+
+def kernel_source_sha():
+    import hashlib
+    path = os.path.join(ROOT, "hadamard_rank_linear_amd", "csrc", "hlq_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-kernel calibrated), or None when
+    there is none or the kernel source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernels_source_sha256") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes=256 << 20, reps=5):
+    """Plain device-to-device copies of known size: their FETCH_SIZE and
+    WRITE_SIZE in a counter run give the scale of those counters."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
 
 
 def ideal_us(ops, nbytes):
@@ -204,6 +243,8 @@ def main():
     ap.add_argument("--workload", default="vitb_qkv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the fc2 side measurement")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run 256 MiB device copies (scale of the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -241,8 +282,9 @@ def main():
         achieved = nbytes / (kus * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    traffic = measured_traffic(cfg.name, kname)
     roof.update(kernel=kname, kernel_us=round(kus, 2), algorithmic_bytes=nbytes,
-                algorithmic_ops=ops, traffic=None)
+                algorithmic_ops=ops, traffic=traffic)
 
     extra = {}
     if not args.no_extra and cfg.name != "vitb_fc2":
@@ -251,6 +293,9 @@ def main():
         r2 = time_layer(c2, wl.make_inputs(c2), max(10, args.steps // 2), args.warmup,
                         per_kernel=False)
         extra["vitb_fc2_us"] = round(r2["wall_ms_per_step"] * 1e3, 2)
+
+    if args.copy_calib:
+        copy_calibration()
 
     cpu = None
     if not args.no_cpu_baseline:
