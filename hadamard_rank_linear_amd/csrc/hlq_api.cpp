@@ -11,7 +11,10 @@
 //      GEMM operands (INT4 H.g_y rows, INT4 H.w transposed, INT8 low-rank g_y
 //      and x transposed), K padding zeroed
 //   4. INT4 GEMM with fused dequantizing epilogue -> g_x
-//   5. INT8 GEMM (split-K partials + finalize when the tile grid is small) -> g_w
+//   5. INT8 GEMM with fused dequantizing epilogue -> g_w
+// Steps 4 and 5 requested together run as one launch holding both tile grids
+// (no split-K); either alone uses split-K partials + a finalize pass when its
+// tile grid is smaller than the CU count.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -222,17 +225,23 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
   if (on(HLQ_STEP_TR_REDUCE)) HLQ_TRY(hlq::launch_tr_reduce(a, s));
   if (on(HLQ_STEP_TR_QUANT)) HLQ_TRY(hlq::launch_tr(a, hlq::PASS_QUANT, block, rank, s));
   const float inv_n = 1.0f / (float)block;
+  const float gw_alpha =
+      reduction == HLQ_MEAN ? (float)(1.0 / ((double)block * (double)T)) : inv_n;
+  if (on(HLQ_STEP_GEMM_GX) && on(HLQ_STEP_GEMM_GW)) {  // both GEMMs, one launch
+    HLQ_TRY(hlq::launch_gemm_pair(a.q_gy, a.q_w, T, I, a.kxb, L.plan_gx, a.s_gy, a.s_w,
+                                  gx_tok ? 1 : 0, inv_n, g_x, a.q_gyl, a.q_xl, O, a.kwb,
+                                  L.plan_gw, a.s_gyl, a.s_xl, gw_tok ? 1 : 0, gw_alpha, g_w,
+                                  s));
+    return HLQ_OK;
+  }
   if (on(HLQ_STEP_GEMM_GX))  // g_x = acc * s_gy[t] * s_w[i] / n
     HLQ_TRY(hlq::launch_gemm(true, a.q_gy, a.q_w, T, I, a.kxb, L.plan_gx, a.s_gy,
                              gx_tok ? 1 : 0, a.s_w, gx_tok ? 1 : 0, inv_n, hlq::EPI_F32,
                              g_x, nullptr, partial, s));
-  if (on(HLQ_STEP_GEMM_GW)) {  // g_w = acc * s_gyl[o] * s_xl[i] / n  (/ T)
-    const float alpha =
-        reduction == HLQ_MEAN ? (float)(1.0 / ((double)block * (double)T)) : inv_n;
+  if (on(HLQ_STEP_GEMM_GW))  // g_w = acc * s_gyl[o] * s_xl[i] / n  (/ T)
     HLQ_TRY(hlq::launch_gemm(false, a.q_gyl, a.q_xl, O, I, a.kwb, L.plan_gw, a.s_gyl,
-                             gw_tok ? 1 : 0, a.s_xl, gw_tok ? 1 : 0, alpha, hlq::EPI_F32,
+                             gw_tok ? 1 : 0, a.s_xl, gw_tok ? 1 : 0, gw_alpha, hlq::EPI_F32,
                              g_w, nullptr, partial, s));
-  }
   return HLQ_OK;
 }
 

@@ -74,6 +74,17 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
                        float alpha, GemmEpi epi, float* C, int32_t* Ci,
                        int32_t* partial, hipStream_t s);
 
+// Both GEMMs of the backward in one launch, fp32 epilogues, no split-K:
+// g_x = acc(q_gy, q_w) * s_gy * s_w * gx_alpha, g_w = acc(q_gyl, q_xl) *
+// s_gyl * s_xl * gw_alpha (scale steps 1 per-token, 0 per-tensor).  The
+// plans fix the tile configurations; their splits are ignored.
+hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, int64_t I,
+                            int64_t kx_pitch, const GemmPlan& px, const float* s_gy,
+                            const float* s_w, int gx_step, float gx_alpha, float* g_x,
+                            const uint8_t* gwA, const uint8_t* gwB, int64_t O, int64_t kw_pitch,
+                            const GemmPlan& pw, const float* s_gyl, const float* s_xl,
+                            int gw_step, float gw_alpha, float* g_w, hipStream_t s);
+
 hipError_t launch_gemm_finalize(const int32_t* partial, int splits, int64_t M,
                                 int64_t N, const float* sa, int sa_step,
                                 const float* sb, int sb_step, float alpha, float* C,

@@ -1038,25 +1038,44 @@ struct GemmShape {
 
 #define HLQ_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 
+// One GEMM of a launch: operands, shape, K stages (split into sps-stage
+// pieces) and the dequantizing epilogue's scales.
+struct GemmArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  int64_t M, N, pitch, S_total, sps;
+  const float* sa;
+  int sa_step;
+  const float* sb;
+  int sb_step;
+  float alpha;
+  float* C;
+  int32_t* Ci;
+};
+
+// One output tile (workgroup w of the tile grid, K split `split`) of one GEMM.
+// Every thread of the workgroup calls it; `lds` holds NS * STAGE bytes.
 template <bool INT4, int BM, int BN, int KB, int NS, int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ A,
-                                                 const uint8_t* __restrict__ B, int64_t M,
-                                                 int64_t N, int64_t pitch, int64_t S_total,
-                                                 int64_t sps, const float* __restrict__ sa,
-                                                 int sa_step, const float* __restrict__ sb,
-                                                 int sb_step, float alpha,
-                                                 float* __restrict__ C,
-                                                 int32_t* __restrict__ Ci) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t split,
+                                          uint8_t* lds) {
   using G = GemmShape<INT4, BM, BN, KB, NS>;
   constexpr int FM = G::FM, FN = G::FN, IA = G::IA, IB = G::IB, IPW = G::IPW;
   constexpr int CPR = G::CPR, KK = G::KK;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * G::STAGE];
+  const uint8_t* __restrict__ A = g.A;
+  const uint8_t* __restrict__ B = g.B;
+  const int64_t M = g.M, N = g.N, pitch = g.pitch, S_total = g.S_total, sps = g.sps;
+  const float* __restrict__ sa = g.sa;
+  const float* __restrict__ sb = g.sb;
+  const int sa_step = g.sa_step, sb_step = g.sb_step;
+  const float alpha = g.alpha;
+  float* __restrict__ C = g.C;
+  int32_t* __restrict__ Ci = g.Ci;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int64_t tm, tn;
-  if (!xcd_tile(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn)) return;
+  if (!xcd_tile(w, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn)) return;
   const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int64_t s_first = (int64_t)blockIdx.y * sps;
+  const int64_t s_first = split * sps;
   const int64_t S = (S_total - s_first < sps ? S_total - s_first : sps);  // >= 1 by plan
   const int64_t kbase = s_first * KB;
 
@@ -1196,7 +1215,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ A,
 #undef HLQ_GEMM_WAIT
 
   constexpr int SH = INT4 ? 8 : 0;
-  int32_t* Cp = Ci + (EPI == EPI_PARTIAL ? (int64_t)blockIdx.y * M * N : 0);
+  int32_t* Cp = Ci + (EPI == EPI_PARTIAL ? split * M * N : 0);
   float s_n[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
@@ -1219,6 +1238,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ A,
         else Cp[m * N + n] = v;
       }
   }
+}
+
+template <bool INT4, int BM, int BN, int KB, int NS, int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * GemmShape<INT4, BM, BN, KB, NS>::STAGE];
+  gemm_tile<INT4, BM, BN, KB, NS, EPI>(g, blockIdx.x, blockIdx.y, lds);
+}
+
+// Both GEMMs of the backward in one launch (fp32 epilogues, no split-K): the
+// first n1 workgroups take the g_w tiles (longer K, so they start first), the
+// rest the g_x tiles, which fill the CUs around them.  One launch instead of
+// two plus a split-K pass, and neither GEMM's tail leaves the GPU idle.
+template <int BM1, int BN1, int KB1, int NS1, int BM0, int BN0, int KB0, int NS0>
+__global__ __launch_bounds__(256, 2) void k_gemm_pair(GemmArgs gw, int64_t n1, GemmArgs gx) {
+  constexpr int L1 = NS1 * GemmShape<false, BM1, BN1, KB1, NS1>::STAGE;
+  constexpr int L0 = NS0 * GemmShape<true, BM0, BN0, KB0, NS0>::STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L1 > L0 ? L1 : L0];
+  const int64_t b = blockIdx.x;
+  if (b < n1) gemm_tile<false, BM1, BN1, KB1, NS1, EPI_F32>(gw, b, 0, lds);
+  else gemm_tile<true, BM0, BN0, KB0, NS0, EPI_F32>(gx, b - n1, 0, lds);
 }
 
 // Sum of split-K INT32 partials (exact) followed by the dequantizing epilogue.
@@ -1368,13 +1407,9 @@ GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes) {
 }
 
 template <bool I4, int EPI>
-static void gemm_dispatch(int cfg, dim3 g, hipStream_t s, const uint8_t* A, const uint8_t* B,
-                          int64_t M, int64_t N, int64_t pitch, int64_t stages, int64_t sps,
-                          const float* sa, int sa_step, const float* sb, int sb_step,
-                          float alpha, float* C, int32_t* Ci) {
-#define HLQ_GEMM(BM_, BN_, KB_, NS_)                                                     \
-  hipLaunchKernelGGL((k_gemm<I4, BM_, BN_, KB_, NS_, EPI>), g, dim3(256), 0, s, A, B, M, N, \
-                     pitch, stages, sps, sa, sa_step, sb, sb_step, alpha, C, Ci)
+static void gemm_dispatch(int cfg, dim3 g, hipStream_t s, const GemmArgs& a) {
+#define HLQ_GEMM(BM_, BN_, KB_, NS_) \
+  hipLaunchKernelGGL((k_gemm<I4, BM_, BN_, KB_, NS_, EPI>), g, dim3(256), 0, s, a)
   switch (cfg) {
     case 1: HLQ_GEMM(256, 128, 64, 3); break;
     case 2: HLQ_GEMM(128, 128, 128, 2); break;
@@ -1399,19 +1434,58 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
     return hipErrorInvalidValue;
   if (epi == EPI_I32 && Ci == nullptr) return hipErrorInvalidValue;
   const int e = use_partial ? EPI_PARTIAL : epi;
-  int32_t* dst = use_partial ? partial : Ci;
+  GemmArgs a{A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C,
+             use_partial ? partial : Ci};
   if (int4) {
-    if (e == EPI_F32) gemm_dispatch<true, EPI_F32>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else if (e == EPI_I32) gemm_dispatch<true, EPI_I32>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else gemm_dispatch<true, EPI_PARTIAL>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    if (e == EPI_F32) gemm_dispatch<true, EPI_F32>(plan.cfg, grid, s, a);
+    else if (e == EPI_I32) gemm_dispatch<true, EPI_I32>(plan.cfg, grid, s, a);
+    else gemm_dispatch<true, EPI_PARTIAL>(plan.cfg, grid, s, a);
   } else {
-    if (e == EPI_F32) gemm_dispatch<false, EPI_F32>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else if (e == EPI_I32) gemm_dispatch<false, EPI_I32>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
-    else gemm_dispatch<false, EPI_PARTIAL>(plan.cfg, grid, s, A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C, dst);
+    if (e == EPI_F32) gemm_dispatch<false, EPI_F32>(plan.cfg, grid, s, a);
+    else if (e == EPI_I32) gemm_dispatch<false, EPI_I32>(plan.cfg, grid, s, a);
+    else gemm_dispatch<false, EPI_PARTIAL>(plan.cfg, grid, s, a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !use_partial) return err;
   return launch_gemm_finalize(partial, splits, M, N, sa, sa_step, sb, sb_step, alpha, C, s);
+}
+
+hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, int64_t I,
+                            int64_t kx_pitch, const GemmPlan& px, const float* s_gy,
+                            const float* s_w, int gx_step, float gx_alpha, float* g_x,
+                            const uint8_t* gwA, const uint8_t* gwB, int64_t O, int64_t kw_pitch,
+                            const GemmPlan& pw, const float* s_gyl, const float* s_xl,
+                            int gw_step, float gw_alpha, float* g_w, hipStream_t s) {
+  if (kx_pitch % px.kb || px.stages * px.kb != kx_pitch) return hipErrorInvalidValue;
+  if (kw_pitch % pw.kb || pw.stages * pw.kb != kw_pitch) return hipErrorInvalidValue;
+  if (!g_x || !g_w || !s_gy || !s_w || !s_gyl || !s_xl) return hipErrorInvalidValue;
+  const GemmArgs ax{gxA, gxB, T, I, kx_pitch, px.stages, px.stages, s_gy, gx_step, s_w, gx_step,
+                    gx_alpha, g_x, nullptr};
+  const GemmArgs aw{gwA, gwB, O, I, kw_pitch, pw.stages, pw.stages, s_gyl, gw_step, s_xl, gw_step,
+                    gw_alpha, g_w, nullptr};
+  const int64_t tx = (int64_t)cdiv(T, px.bm) * cdiv(I, px.bn);
+  const int64_t tw = (int64_t)cdiv(O, pw.bm) * cdiv(I, pw.bn);
+  const int64_t n1 = (tw + 7) / 8 * 8, n0 = (tx + 7) / 8 * 8;
+  const dim3 g((unsigned)(n1 + n0));
+#define HLQ_PAIR(W_, X_) hipLaunchKernelGGL((k_gemm_pair<W_, X_>), g, dim3(256), 0, s, aw, n1, ax)
+#define HLQ_W0 128, 128, 64, 3
+#define HLQ_W1 256, 128, 64, 3
+#define HLQ_W2 128, 128, 128, 2
+#define HLQ_X0 128, 128, 64, 3
+#define HLQ_X1 256, 128, 64, 3
+  const bool x1 = px.cfg == 1;
+  switch (pw.cfg) {
+    case 1: if (x1) HLQ_PAIR(HLQ_W1, HLQ_X1); else HLQ_PAIR(HLQ_W1, HLQ_X0); break;
+    case 2: if (x1) HLQ_PAIR(HLQ_W2, HLQ_X1); else HLQ_PAIR(HLQ_W2, HLQ_X0); break;
+    default: if (x1) HLQ_PAIR(HLQ_W0, HLQ_X1); else HLQ_PAIR(HLQ_W0, HLQ_X0); break;
+  }
+#undef HLQ_PAIR
+#undef HLQ_W0
+#undef HLQ_W1
+#undef HLQ_W2
+#undef HLQ_X0
+#undef HLQ_X1
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_finalize(const int32_t* partial, int splits, int64_t M,
