@@ -215,7 +215,8 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
   a.gy_reg = (gy_dtype == HLQ_BF16 && block <= 64) ? 1 : 0;
   a.ntr_gy = a.gy_reg ? (T + hlq::TR_GY_REG_ROWS - 1) / hlq::TR_GY_REG_ROWS : L.ntr_t;
   a.wg_gy = a.ntr_gy * L.nch_o;
-  a.gy_workers = 0;  // chosen per pass by launch_tr
+  a.gy_workers = 0;  // both chosen per pass by launch_tr
+  a.gyreg_wgs = 0;
   a.wg_x = L.ntr_t * L.nch_i;
   a.wg_w = L.ntr_o * L.nch_i;
   int32_t* partial = reinterpret_cast<int32_t*>(ws + L.partial);

@@ -44,7 +44,8 @@ struct TrArgs {
   int gy_reg;
   int64_t ntr_gy;
   int64_t wg_gy, wg_x, wg_w;  // tiles of each job
-  int64_t gy_workers;         // g_y tiles of the shared kernel (set per launch)
+  int64_t gy_workers;         // LDS-engine g_y tiles of the transform launch (set per launch)
+  int64_t gyreg_wgs;          // register-path g_y workgroups of that launch (4 tiles each)
 };
 
 // Launch configuration of one integer GEMM C[m][n] = sum_k A[m][k] B[n][k],

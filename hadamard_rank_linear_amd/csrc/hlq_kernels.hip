@@ -564,8 +564,10 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
 }
 
 // ---- MAX pass over g_y tiles held in registers (bf16 g_y, n <= 64)
-// One wave per tile of GYR_ROWS = 64 tokens x CW = 128 channels; the waves of
-// a workgroup never wait for each other and finish independently.
+// One wave per tile of GYR_ROWS = 64 tokens x CW = 128 channels; the four
+// waves of a workgroup take four tiles, never wait for each other and finish
+// independently.  These workgroups run in the same MAX launch as the x and w
+// tiles of the LDS engine.
 // Lane c16 = lane & 7 owns channels c0 + 16 c16 .. +15 and row group
 // rg = lane >> 3 owns tokens t0 + 8 rg .. +7, loaded once into registers
 // (8 tokens x 32 bytes).  A Hadamard block of n
@@ -760,21 +762,6 @@ __device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
   }
 }
 
-// Four independent waves per workgroup (tiles 4 w .. 4 w + 3 of the
-// XCD-ordered workgroup w): no barriers, and dispatch works in 4-wave units.
-// MAX pass only: the QUANT pass runs the g_y tiles on the LDS engine, whose
-// staged, wide code stores suit the transposed INT8 output better.
-template <int N, int R>
-__global__ __launch_bounds__(256) void k_tr_gy_max(TrArgs a) {
-  const int64_t wg = xcd_range_tile(blockIdx.x, (a.wg_gy + 3) / 4);
-  if (wg < 0) return;
-  const int64_t bid = wg * 4 + (threadIdx.x >> 6);
-  if (bid >= a.wg_gy) return;
-  uint4 raw[8][2];
-  gyr_load(a, bid, raw);
-  gyr_tile_max<N, R>(a, bid, raw);
-}
-
 // ---- job: x tile (ACBP codes, low-rank columns along T for g_w)
 template <int PASS, int N, int R>
 __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
@@ -857,8 +844,21 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
   static_assert(CW * OUT_BYTES <= TileSmem<F32>::bytes, "staging fits the smem buffer");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TileSmem<F32>::bytes];
   __shared__ float red[4 * CW];
-  int64_t bid = xcd_range_tile(blockIdx.x, a.gy_workers + a.wg_x + a.wg_w);
+  int64_t bid = xcd_range_tile(blockIdx.x, a.gyreg_wgs + a.gy_workers + a.wg_x + a.wg_w);
   if (bid < 0) return;
+  if constexpr (PASS == PASS_MAX && N <= 64) {
+    // register-resident g_y tiles: four independent waves, one tile each
+    if (bid < a.gyreg_wgs) {
+      const int64_t tile = bid * 4 + (threadIdx.x >> 6);
+      if (tile < a.wg_gy) {
+        uint4 raw[8][2];
+        gyr_load(a, tile, raw);
+        gyr_tile_max<N, R>(a, tile, raw);
+      }
+      return;
+    }
+  }
+  bid -= a.gyreg_wgs;
   if constexpr (PASS == PASS_MAX) {
     if (bid == 0 && threadIdx.x < 4) a.tmax[threadIdx.x] = 0u;  // k_tr_reduce folds into it
   } else {
@@ -1325,46 +1325,19 @@ static hipError_t tr_dispatch(int n, int r, dim3 g, hipStream_t s, const TrArgs&
   return hipGetLastError();
 }
 
-static hipError_t tr_gy_max_dispatch(int n, int r, dim3 g, hipStream_t s, const TrArgs& a) {
-#define HLQ_TRG(NN, RR) hipLaunchKernelGGL((k_tr_gy_max<NN, RR>), g, dim3(256), 0, s, a)
-#define HLQ_TRG_N(NN)                                                   \
-  switch (r) {                                                          \
-    case 1: HLQ_TRG(NN, 1); break;                                      \
-    case 2: HLQ_TRG(NN, 2); break;                                      \
-    case 4: HLQ_TRG(NN, 4); break;                                      \
-    case 8: HLQ_TRG(NN, 8); break;                                      \
-    case 16: HLQ_TRG(NN, 16); break;                                    \
-    case 32: if (NN >= 32) HLQ_TRG(NN, (NN >= 32 ? 32 : 1)); break;     \
-    case 64: if (NN >= 64) HLQ_TRG(NN, (NN >= 64 ? 64 : 1)); break;     \
-    default: return hipErrorInvalidValue;                               \
-  }
-  switch (n) {
-    case 16: HLQ_TRG_N(16); break;
-    case 32: HLQ_TRG_N(32); break;
-    case 64: HLQ_TRG_N(64); break;
-    default: return hipErrorInvalidValue;
-  }
-#undef HLQ_TRG_N
-#undef HLQ_TRG
-  return hipGetLastError();
-}
-
 hipError_t launch_tr(const TrArgs& args, int pass, int n, int r, hipStream_t s) {
   if (r > n) return hipErrorInvalidValue;
   TrArgs a = args;
-  // g_y tiles of the shared kernel: all LDS-engine tiles, except in the MAX
-  // pass of the register path, which k_tr_gy_max runs instead
+  // g_y tiles: the LDS engine's, except in the MAX pass of the register path,
+  // where workgroups of four register-resident waves take them
   a.gy_workers = a.ntr_t * a.nch_o;
+  a.gyreg_wgs = 0;
   if (pass == PASS_MAX && a.gy_reg) {
     if (a.gy_dt != 1 || n > 64) return hipErrorInvalidValue;
     a.gy_workers = 0;
-    if (a.wg_gy > 0) {
-      const dim3 gg((unsigned)(((a.wg_gy + 3) / 4 + 7) / 8 * 8));
-      const hipError_t e = tr_gy_max_dispatch(n, r, gg, s, a);
-      if (e != hipSuccess) return e;
-    }
+    a.gyreg_wgs = (a.wg_gy + 3) / 4;
   }
-  const int64_t wgs = a.gy_workers + a.wg_x + a.wg_w;
+  const int64_t wgs = a.gyreg_wgs + a.gy_workers + a.wg_x + a.wg_w;
   if (wgs <= 0) return hipSuccess;
   dim3 g((unsigned)((wgs + 7) / 8 * 8));
   const bool f32 = a.gy_dt == 0 || a.w_dt == 0;
