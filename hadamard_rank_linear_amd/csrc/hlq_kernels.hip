@@ -1216,11 +1216,42 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 
   constexpr int SH = INT4 ? 8 : 0;
   int32_t* Cp = Ci + (EPI == EPI_PARTIAL ? split * M * N : 0);
-  float s_n[FN];
+  // Every scale load is issued before the first store: the memory counter
+  // also counts stores, so a load waited for between stores would wait for
+  // them too.  Rows and columns past M / N read the last one (not stored).
+  float s_n[FN], s_m[FM][16];
+  if constexpr (EPI == EPI_F32) {
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
-    s_n[j] = (EPI == EPI_F32 && n < N) ? sb[n * sb_step] : 0.f;
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
+      s_n[j] = sb[(n < N ? n : N - 1) * sb_step];
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * G::WTM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
+        s_m[i][r] = sa[(m < M ? m : M - 1) * sa_step] * alpha;
+      }
+  }
+  // Interior tiles store without per-lane guards: branch-free code lets the
+  // counter waits before the stores be exact instead of full drains.
+  const bool full = m0 + BM <= M && n0 + BN <= N;
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * G::WTM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
+          const int32_t v = acc[i][j][r] >> SH;
+          if constexpr (EPI == EPI_F32) C[m * N + n] = (float)v * s_m[i][r] * s_n[j];
+          else Cp[m * N + n] = v;
+        }
+      }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -1228,13 +1259,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
     for (int r = 0; r < 16; ++r) {
       const int64_t m = m0 + wm * G::WTM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
       if (m >= M) continue;
-      const float s_m = (EPI == EPI_F32) ? sa[m * sa_step] * alpha : 0.f;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
         if (n >= N) continue;
         const int32_t v = acc[i][j][r] >> SH;
-        if constexpr (EPI == EPI_F32) C[m * N + n] = (float)v * s_m * s_n[j];
+        if constexpr (EPI == EPI_F32) C[m * N + n] = (float)v * s_m[i][r] * s_n[j];
         else Cp[m * N + n] = v;
       }
   }
