@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "hlq_internal.h"
 
 namespace hlq {
@@ -172,6 +174,39 @@ __device__ __forceinline__ int64_t xcd_range_tile(int64_t w, int64_t total) {
   return t < total ? t : -1;
 }
 
+// Value of lane ^ M of the wave (M = 1, 2: DPP quad permute; 8: DPP row
+// rotate by 8; 4, 16: swizzle inside 32 lanes; 32: bpermute).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int b = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));
+  else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));
+  else if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));
+  else if constexpr (M == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x101F));
+  else if constexpr (M == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x401F));
+  else return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) & 63) * 4, b));
+}
+
+// Max over the 8 lanes c16 = 0..7 of a row group (quad swaps, then the
+// half-row mirror pairs each lane with one of the other quad).
+__device__ __forceinline__ float group8_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, true)));
+  return m;
+}
+
+// Butterfly stage with the partner lane ^ M: the lower lane keeps
+// own + partner, the upper partner - own; fma(+-1, own, partner) is that one
+// IEEE add, so the result equals the in-register butterfly bit for bit.
+template <int M>
+__device__ __forceinline__ float xbfly(float v, float sgn) {
+  return __builtin_fmaf(sgn, v, lane_xor<M>(v));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
 // ------------------------------------------------------------ operand transforms
 // All four GEMM operands come from one tile engine.  A tile is TT rows x CW
 // columns of a row-major source: g_y [T][O] (rows = tokens), the ACBP codes of
@@ -204,6 +239,9 @@ constexpr int P_F32 = CW + 4;   // LDS pitches (elements); rows stay 16-byte ali
 constexpr int P_B16 = CW + 8;
 constexpr int P_I4 = CW / 2 + 16;  // bytes: two codes per byte
 constexpr int OUT_BYTES = 128;  // staging bytes per column (>= TT*r/n and TT/2)
+// Pitch of a staged column: 36 banks apart, so the 4-byte writes of 64
+// consecutive columns spread over 16 banks instead of 2.
+constexpr int OUT_PITCH = 144;
 
 template <bool F32>
 struct TileSmem {
@@ -352,7 +390,7 @@ __device__ __forceinline__ void tile_colmax_store(float m, float* red, int tid, 
 // Store the staged transposed codes: column c of the tile owns `len` bytes at
 // dst + c * pitch (dst already offset to the tile's first K byte).  Byte runs
 // go out in the widest unit that divides both the run and its offset.
-__device__ __forceinline__ void store_staged(const uint8_t (*outs)[OUT_BYTES], int cols,
+__device__ __forceinline__ void store_staged(const uint8_t (*outs)[OUT_PITCH], int cols,
                                              int len, uint8_t* dst, int64_t pitch,
                                              int64_t koff, int tid) {
   int wdt = 16;
@@ -368,6 +406,21 @@ __device__ __forceinline__ void store_staged(const uint8_t (*outs)[OUT_BYTES], i
     else if (wdt == 4) *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
     else if (wdt == 2) *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
     else *d = *s;
+  }
+}
+
+// store_staged for a full tile whose runs are LEN bytes (a multiple of 16)
+// at a 16-byte aligned offset: every column, 16-byte stores.
+template <int LEN>
+__device__ __forceinline__ void store_staged_full(const uint8_t (*outs)[OUT_PITCH], uint8_t* dst,
+                                                  int64_t pitch, int tid) {
+  static_assert(LEN % 16 == 0 && LEN <= OUT_BYTES, "16-byte runs");
+  constexpr int PER = LEN / 16;
+#pragma unroll
+  for (int i = tid; i < CW * PER; i += 256) {
+    const int c = i / PER, k = (i % PER) * 16;
+    *reinterpret_cast<uint4*>(dst + (int64_t)c * pitch + k) =
+        *reinterpret_cast<const uint4*>(&outs[c][k]);
   }
 }
 
@@ -424,7 +477,7 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
   if constexpr (PASS == PASS_MAX) {
     tile_colmax_store(cm, red, tid, cols, part);
   } else {
-    uint8_t (*outs)[OUT_BYTES] = reinterpret_cast<uint8_t (*)[OUT_BYTES]>(smem);
+    uint8_t (*outs)[OUT_PITCH] = reinterpret_cast<uint8_t (*)[OUT_PITCH]>(smem);
     __syncthreads();  // every thread is done reading the tile
 #pragma unroll
     for (int t = 0; t < TPT; ++t) {
@@ -442,7 +495,11 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
     }
     __syncthreads();
     const int64_t koff = t0 / N * R;
-    store_staged(outs, cols, nb * R, q + c0 * pitch + koff, pitch, koff, tid);
+    constexpr int LEN = (TT / N) * R;
+    if (LEN % 16 == 0 && rows == TT && cols == CW)
+      store_staged_full<(LEN % 16 == 0 ? LEN : 16)>(outs, q + c0 * pitch + koff, pitch, tid);
+    else
+      store_staged(outs, cols, nb * R, q + c0 * pitch + koff, pitch, koff, tid);
     if (last) zero_tail(q + c0 * pitch, pitch, cols, tl, pitch, tid);
   }
 }
@@ -487,7 +544,7 @@ __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint
   if constexpr (PASS == PASS_MAX) {
     tile_colmax_store(cm, red, tid, cols, part);
   } else {
-    uint8_t (*outs)[OUT_BYTES] = reinterpret_cast<uint8_t (*)[OUT_BYTES]>(smem);
+    uint8_t (*outs)[OUT_PITCH] = reinterpret_cast<uint8_t (*)[OUT_PITCH]>(smem);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < TPT; ++t) {
@@ -500,8 +557,86 @@ __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint
     }
     __syncthreads();
     const int64_t koff = o0 / 2;
-    store_staged(outs, cols, rows / 2, q + c0 * pitch + koff, pitch, koff, tid);
+    if (rows == TT && cols == CW)
+      store_staged_full<TT / 2>(outs, q + c0 * pitch + koff, pitch, tid);
+    else
+      store_staged(outs, cols, rows / 2, q + c0 * pitch + koff, pitch, koff, tid);
     if (last) zero_tail(q + c0 * pitch, pitch, cols, O / 2, pitch, tid);
+  }
+}
+
+// Cross-lane butterfly stages h = 8, 16, .. N/2 of the row transform (lane
+// lc of a 16-lane row holds elements 8 lc .. 8 lc + 7): DPP / swizzle
+// exchanges, one fma(+-1, own, partner) per element (the exact IEEE add).
+template <int N>
+__device__ __forceinline__ void fwht_lanes_dpp(float (&v)[8], int lc) {
+  if constexpr (N >= 16) {
+    const float sg = (lc & 1) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xbfly<1>(v[k], sg);
+  }
+  if constexpr (N >= 32) {
+    const float sg = (lc & 2) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xbfly<2>(v[k], sg);
+  }
+  if constexpr (N >= 64) {
+    const float sg = (lc & 4) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xbfly<4>(v[k], sg);
+  }
+  if constexpr (N >= 128) {
+    const float sg = (lc & 8) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xbfly<8>(v[k], sg);
+  }
+}
+
+// Row phase of a full bf16 g_y tile (TT rows x CW columns inside T and O):
+// the same per-row work as the general loop of tr_job_gy, with tile-uniform
+// base pointers and 32-bit lane offsets, no bounds guards, and DPP exchanges.
+template <int PASS, int N>
+__device__ __forceinline__ void gy_rows_bf16_full(const TrArgs& a, int64_t t0, int64_t c0,
+                                                  int64_t ch, uint8_t* smem, float inv_tensor) {
+  constexpr int SW = TT / 16;
+  const int tid = threadIdx.x, lr = tid >> 4, lc = tid & 15, col = lc * 8;
+  const uint32_t O32 = (uint32_t)a.O;
+  const uint8_t* gbase = static_cast<const uint8_t*>(a.gy) + (t0 * a.O + c0) * 2;
+  const uint32_t goff = ((uint32_t)lr * O32 + (uint32_t)col) * 2u;
+  uint4 raw[SW];
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw)
+    raw[sw] = *reinterpret_cast<const uint4*>(gbase + goff + (uint32_t)sw * 32u * O32);
+  float inv[SW];
+  if constexpr (PASS == PASS_QUANT) {
+    const float* ib = a.inv_gy + t0;
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) inv[sw] = a.gx_tok ? ib[sw * 16 + lr] : inv_tensor;
+  }
+  const uint32_t K32 = (uint32_t)a.kxb;
+  uint8_t* qbase = a.q_gy + t0 * a.kxb + c0 / 2;
+  const uint32_t qoff = (uint32_t)lr * K32 + (uint32_t)(col / 2);
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 16 + lr;
+    *reinterpret_cast<uint4*>(smem + (row * P_B16 + col) * 2) = raw[sw];
+    float v[8] = {bf16_lo(raw[sw].x), bf16_hi(raw[sw].x), bf16_lo(raw[sw].y), bf16_hi(raw[sw].y),
+                  bf16_lo(raw[sw].z), bf16_hi(raw[sw].z), bf16_lo(raw[sw].w), bf16_hi(raw[sw].w)};
+    fwht8(v);
+    fwht_lanes_dpp<N>(v, lc);
+    if constexpr (PASS == PASS_MAX) {
+      float m = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+      m = fmaxf(m, lane_xor<1>(m));
+      m = fmaxf(m, lane_xor<2>(m));
+      m = fmaxf(m, lane_xor<4>(m));
+      m = fmaxf(m, lane_xor<8>(m));
+      if (lc == 0) a.part_gy[ch * a.T + t0 + row] = m;
+    } else {
+      *reinterpret_cast<uint32_t*>(qbase + qoff + (uint32_t)sw * 16u * K32) =
+          quant_pack8_int4(v, inv[sw]);
+    }
   }
 }
 
@@ -509,10 +644,19 @@ __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint
 template <int PASS, int N, int R, bool F32>
 __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
   const int tid = threadIdx.x;
-  const int64_t tr = bid / a.nch_o, ch = bid % a.nch_o;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
   const int64_t t0 = tr * TT, c0 = ch * CW;
   const int rows = (int)(a.T - t0 < TT ? a.T - t0 : TT);
   const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
+  float inv_tensor = 0.f;
+  if constexpr (PASS == PASS_QUANT) {
+    if (!a.gx_tok) inv_tensor = inv_of(__uint_as_float(a.tmax[0]), 7.f);
+  }
+  if (!F32 && rows == TT && cols == CW) {
+    gy_rows_bf16_full<PASS, N>(a, t0, c0, ch, smem, inv_tensor);
+  } else {
   // 16 rows per sweep, 16 lanes x 8 columns per row
   constexpr int SW = TT / 16;
   const int lr = tid >> 4, lc = tid & 15;
@@ -524,10 +668,6 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
     raw[sw].a = make_uint4(0, 0, 0, 0);
     raw[sw].b = make_uint4(0, 0, 0, 0);
     if (row < rows && col < cols) load_raw8(a.gy, a.gy_dt, (t0 + row) * a.O + c0 + col, raw[sw]);
-  }
-  float inv_tensor = 0.f;
-  if constexpr (PASS == PASS_QUANT) {
-    if (!a.gx_tok) inv_tensor = inv_of(__uint_as_float(a.tmax[0]), 7.f);
   }
 #pragma unroll
   for (int sw = 0; sw < SW; ++sw) {
@@ -549,6 +689,7 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
       *reinterpret_cast<uint32_t*>(a.q_gy + (t0 + row) * a.kxb + (c0 + col) / 2) =
           col < cols ? quant_pack8_int4(v, inv) : 0u;
     }
+  }
   }
   __syncthreads();
   const bool last = t0 + rows == a.T;
@@ -583,39 +724,6 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
 // ascending h as the full transform runs them.
 constexpr int GYR_ROWS = TR_GY_REG_ROWS;
 
-// Value of lane ^ M of the wave (M = 1, 2: DPP quad permute; 8: DPP row
-// rotate by 8; 4, 16: swizzle inside 32 lanes; 32: bpermute).
-template <int M>
-__device__ __forceinline__ float lane_xor(float v) {
-  const int b = __float_as_int(v);
-  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));
-  else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));
-  else if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));
-  else if constexpr (M == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x101F));
-  else if constexpr (M == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x401F));
-  else return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) & 63) * 4, b));
-}
-
-// Max over the 8 lanes c16 = 0..7 of a row group (quad swaps, then the
-// half-row mirror pairs each lane with one of the other quad).
-__device__ __forceinline__ float group8_max(float m) {
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, true)));
-  return m;
-}
-
-// Butterfly stage with the partner lane ^ M: the lower lane keeps
-// own + partner, the upper partner - own; fma(+-1, own, partner) is that one
-// IEEE add, so the result equals the in-register butterfly bit for bit.
-template <int M>
-__device__ __forceinline__ float xbfly(float v, float sgn) {
-  return __builtin_fmaf(sgn, v, lane_xor<M>(v));
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
 // max |v[i]| over 16 values with three-input maxima
 __device__ __forceinline__ float absmax16(const float (&v)[16]) {
   float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
@@ -627,7 +735,9 @@ __device__ __forceinline__ float absmax16(const float (&v)[16]) {
 // Registers of one tile (zero outside T and O).
 __device__ __forceinline__ void gyr_load(const TrArgs& a, int64_t bid, uint4 (&raw)[8][2]) {
   const int lane = threadIdx.x & 63;
-  const int64_t tr = bid / a.nch_o, ch = bid % a.nch_o;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
   const int64_t t0 = tr * GYR_ROWS, c0 = ch * CW;
   const int rows = (int)(a.T - t0 < GYR_ROWS ? a.T - t0 : GYR_ROWS);
   const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
@@ -657,7 +767,9 @@ __device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
   constexpr int RGB = N / 8;           // row groups per token block
   const int lane = threadIdx.x & 63;
   const int c16 = lane & 7, rg = lane >> 3;
-  const int64_t tr = bid / a.nch_o, ch = bid % a.nch_o;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
   const int64_t t0 = tr * GYR_ROWS, c0 = ch * CW;
   const int rows = (int)(a.T - t0 < GYR_ROWS ? a.T - t0 : GYR_ROWS);
   const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
@@ -766,7 +878,9 @@ __device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
 template <int PASS, int N, int R>
 __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
   const int tid = threadIdx.x;
-  const int64_t tr = bid / a.nch_i, ch = bid % a.nch_i;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_i;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
   const int64_t t0 = tr * TT, c0 = ch * CW;
   const int rows = (int)(a.T - t0 < TT ? a.T - t0 : TT);
   const int cols = (int)(a.I - c0 < CW ? a.I - c0 : CW);
@@ -807,7 +921,9 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
 template <int PASS, int N, bool F32>
 __device__ void tr_job_w(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
   const int tid = threadIdx.x;
-  const int64_t tr = bid / a.nch_i, ch = bid % a.nch_i;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_i;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
   const int64_t o0 = tr * TT, c0 = ch * CW;
   const int rows = (int)(a.O - o0 < TT ? a.O - o0 : TT);
   const int cols = (int)(a.I - c0 < CW ? a.I - c0 : CW);
@@ -841,7 +957,7 @@ __device__ void tr_job_w(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
 template <int PASS, int N, int R, bool F32>
 __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
   static_assert(TT * P_I4 + TT * 4 <= TileSmem<F32>::bytes, "x tile fits the smem buffer");
-  static_assert(CW * OUT_BYTES <= TileSmem<F32>::bytes, "staging fits the smem buffer");
+  static_assert(CW * OUT_PITCH <= TileSmem<F32>::bytes, "staging fits the smem buffer");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TileSmem<F32>::bytes];
   __shared__ float red[4 * CW];
   int64_t bid = xcd_range_tile(blockIdx.x, a.gyreg_wgs + a.gy_workers + a.wg_x + a.wg_w);
@@ -1057,7 +1173,7 @@ struct GemmArgs {
 // Every thread of the workgroup calls it; `lds` holds NS * STAGE bytes.
 template <bool INT4, int BM, int BN, int KB, int NS, int EPI>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t split,
-                                          uint8_t* lds) {
+                                          uint8_t* lds, float* sc) {
   using G = GemmShape<INT4, BM, BN, KB, NS>;
   constexpr int FM = G::FM, FN = G::FN, IA = G::IA, IB = G::IB, IPW = G::IPW;
   constexpr int CPR = G::CPR, KK = G::KK;
@@ -1120,9 +1236,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) coff[kk] = ((kk * 2 + fh) ^ sw) * 16;
 
+  // Dequantization scales of the tile's rows (times alpha) and columns, read
+  // before the K loop and parked in LDS (sc, an array of its own, so the
+  // ring's DMA does not order its accesses): the epilogue then waits on no
+  // global load while its stores are in flight.
+  constexpr int NSC = (BM + BN + 255) / 256;
+  float scv[NSC];
+  if constexpr (EPI == EPI_F32) {
+#pragma unroll
+    for (int q = 0; q < NSC; ++q) {
+      // one unconditional load per slot (a select of the address, so the
+      // loaded value is not merged across branches, which would wait on it)
+      const int i = tid + 256 * q;
+      const int64_t m = m0 + i, n = n0 + (i - BM);
+      const float* src = i < BM ? sa + (m < M ? m : M - 1) * sa_step
+                                : sb + (n < N ? (n >= 0 ? n : 0) : N - 1) * sb_step;
+      scv[q] = *src;
+    }
+  }
+
 #pragma unroll
   for (int p = 0; p < NS; ++p)
     if (p < S) HLQ_GEMM_ISSUE(p, p);
+  // keep the scales' LDS writes below the ring's first wait (no stall on
+  // the scale loads before the stage loads are in flight)
+  asm volatile("" ::: "memory");
 
   v16i acc[FM][FN];
 #pragma unroll
@@ -1134,6 +1272,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 
   u32x4 fa[2][FM], fb[2][FN];
   HLQ_GEMM_WAIT((S - 1 < NS - 1 ? S - 1 : NS - 1));
+  if constexpr (EPI == EPI_F32) {
+#pragma unroll
+    for (int q = 0; q < NSC; ++q)
+      if (tid + 256 * q < BM + BN) sc[tid + 256 * q] = tid + 256 * q < BM ? scv[q] * alpha : scv[q];
+  }
   asm volatile("s_barrier" ::: "memory");
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -1142,12 +1285,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   for (int j = 0; j < FN; ++j)
     fb[0][j] = *reinterpret_cast<const u32x4*>(lds + b_off + j * 32 * KB + coff[0]);
 
+  // One K stage.  MODE 0: steady state (refill a buffer, prefetch the next
+  // stage's first fragments); 1: the last NS-1 stages but one (prefetch, no
+  // refill); 2: the last stage.  Separate bodies keep each stage one block
+  // of straight-line code for the scheduler.
   int buf = 0;
-  for (int64_t st = 0; st < S; ++st) {
+  auto stage = [&](int64_t st, auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
     const uint8_t* base = lds + buf * G::STAGE;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1, nxt = cur ^ 1;
+      const bool reads = kk + 1 < KK || MODE != 2;
       if (kk + 1 < KK) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -1155,6 +1304,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           fb[nxt][j] = *reinterpret_cast<const u32x4*>(base + b_off + j * 32 * KB + coff[kk + 1]);
+      } else if constexpr (MODE != 2) {
+        // Before the stage's last k-step (its fragments are already in
+        // registers): stage st+1 landed in every wave (st+2 .. st+NS-1 may
+        // still fly) and no wave reads stage st any more ...
+        if constexpr (MODE == 0) wait_vmcnt<(NS - 2) * IPW>();
+        else HLQ_GEMM_WAIT((S - st - 2 < NS - 2 ? S - st - 2 : NS - 2));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // ... so the first fragments of stage st+1 load under this step's
+        // MFMAs, and stage st's buffer is refilled (after those reads are
+        // issued: an LDS read behind a DMA into LDS would wait for the DMA).
+        const int ob = buf;
+        buf = buf + 1 == NS ? 0 : buf + 1;
+        const uint8_t* nb = lds + buf * G::STAGE;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fa[nxt][i] = *reinterpret_cast<const u32x4*>(nb + a_off + i * 32 * KB + coff[0]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[nxt][j] = *reinterpret_cast<const u32x4*>(nb + b_off + j * 32 * KB + coff[0]);
+        if constexpr (MODE == 0) HLQ_GEMM_ISSUE(st + NS, ob);
       }
       if constexpr (INT4) {
         v4i xa0[FM], xa1[FM], yb0[FN], yb1[FN];
@@ -1172,7 +1341,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa1[i], yb1[j], acc[i][j], 0, 0, 0);
-        if (kk + 1 < KK) {
+        if (reads) {
           // next fragments' reads between MFMAs, widening spread behind them
 #pragma unroll
           for (int q = 0; q < FM + FN; ++q) { HLQ_SGB(0x100, 1); HLQ_SGB(0x008, 1); HLQ_SGB(0x002, 12); }
@@ -1188,51 +1357,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
                 v4i{(int)xa[0], (int)xa[1], (int)xa[2], (int)xa[3]},
                 v4i{(int)yb[0], (int)yb[1], (int)yb[2], (int)yb[3]}, acc[i][j], 0, 0, 0);
           }
-        if (kk + 1 < KK) {
+        if (reads) {
 #pragma unroll
           for (int q = 0; q < FM + FN; ++q) { HLQ_SGB(0x100, 1); HLQ_SGB(0x008, 1); }
           if (FM * FN > FM + FN) HLQ_SGB(0x008, FM * FN - (FM + FN));
         }
       }
-      if (kk + 1 == KK && st + 1 < S) {
-        // stage st+1 landed in every wave (st+2 .. st+NS-1 may still fly) ...
-        HLQ_GEMM_WAIT((S - st - 2 < NS - 2 ? S - st - 2 : NS - 2));
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // ... and no wave reads stage st any more: refill its buffer
-        if (st + NS < S) HLQ_GEMM_ISSUE(st + NS, buf);
-        buf = buf + 1 == NS ? 0 : buf + 1;
-        const uint8_t* nb = lds + buf * G::STAGE;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          fa[0][i] = *reinterpret_cast<const u32x4*>(nb + a_off + i * 32 * KB + coff[0]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          fb[0][j] = *reinterpret_cast<const u32x4*>(nb + b_off + j * 32 * KB + coff[0]);
-      }
     }
-  }
+  };
+  int64_t st = 0;
+  for (; st + NS < S; ++st) stage(st, std::integral_constant<int, 0>());
+  for (; st + 1 < S; ++st) stage(st, std::integral_constant<int, 1>());
+  stage(st, std::integral_constant<int, 2>());  // S >= 1
 #undef HLQ_GEMM_ISSUE
 #undef HLQ_GEMM_WAIT
 
   constexpr int SH = INT4 ? 8 : 0;
   int32_t* Cp = Ci + (EPI == EPI_PARTIAL ? split * M * N : 0);
-  // Every scale load is issued before the first store: the memory counter
-  // also counts stores, so a load waited for between stores would wait for
-  // them too.  Rows and columns past M / N read the last one (not stored).
+  // Scales from LDS (written before the K loop; its barriers published them).
   float s_n[FN], s_m[FM][16];
   if constexpr (EPI == EPI_F32) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
-      s_n[j] = sb[(n < N ? n : N - 1) * sb_step];
-    }
+    for (int j = 0; j < FN; ++j) s_n[j] = sc[BM + wn * G::WTN + j * 32 + fr];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * G::WTM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
-        s_m[i][r] = sa[(m < M ? m : M - 1) * sa_step] * alpha;
-      }
+      for (int r = 0; r < 16; ++r) s_m[i][r] = sc[wm * G::WTM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4)];
   }
   // Interior tiles store without per-lane guards: branch-free code lets the
   // counter waits before the stores be exact instead of full drains.
@@ -1273,7 +1423,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 template <bool INT4, int BM, int BN, int KB, int NS, int EPI>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * GemmShape<INT4, BM, BN, KB, NS>::STAGE];
-  gemm_tile<INT4, BM, BN, KB, NS, EPI>(g, blockIdx.x, blockIdx.y, lds);
+  __shared__ float sc[BM + BN];
+  gemm_tile<INT4, BM, BN, KB, NS, EPI>(g, blockIdx.x, blockIdx.y, lds, sc);
 }
 
 // Both GEMMs of the backward in one launch (fp32 epilogues, no split-K): the
@@ -1284,10 +1435,12 @@ template <int BM1, int BN1, int KB1, int NS1, int BM0, int BN0, int KB0, int NS0
 __global__ __launch_bounds__(256, 2) void k_gemm_pair(GemmArgs gw, int64_t n1, GemmArgs gx) {
   constexpr int L1 = NS1 * GemmShape<false, BM1, BN1, KB1, NS1>::STAGE;
   constexpr int L0 = NS0 * GemmShape<true, BM0, BN0, KB0, NS0>::STAGE;
+  constexpr int SC = BM1 + BN1 > BM0 + BN0 ? BM1 + BN1 : BM0 + BN0;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L1 > L0 ? L1 : L0];
+  __shared__ float sc[SC];
   const int64_t b = blockIdx.x;
-  if (b < n1) gemm_tile<false, BM1, BN1, KB1, NS1, EPI_F32>(gw, b, 0, lds);
-  else gemm_tile<true, BM0, BN0, KB0, NS0, EPI_F32>(gx, b - n1, 0, lds);
+  if (b < n1) gemm_tile<false, BM1, BN1, KB1, NS1, EPI_F32>(gw, b, 0, lds, sc);
+  else gemm_tile<true, BM0, BN0, KB0, NS0, EPI_F32>(gx, b - n1, 0, lds, sc);
 }
 
 // Sum of split-K INT32 partials (exact) followed by the dequantizing epilogue.
@@ -1466,26 +1619,34 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
                     gx_alpha, g_x, nullptr};
   const GemmArgs aw{gwA, gwB, O, I, kw_pitch, pw.stages, pw.stages, s_gyl, gw_step, s_xl, gw_step,
                     gw_alpha, g_w, nullptr};
+  // g_w tile: the plan's, except that a long-K g_w grid smaller than the CU
+  // count (its tiles would be the launch's critical path) takes 64-row tiles
+  // (cfg 3: 64 x 128, KB 128, 3 stages): twice the tiles, half the K work each.
+  int wcfg = pw.cfg, wbm = pw.bm;
+  if (pw.cfg == 2 && (int64_t)cdiv(O, 128) * cdiv(I, 128) < 256) { wcfg = 3; wbm = 64; }
   const int64_t tx = (int64_t)cdiv(T, px.bm) * cdiv(I, px.bn);
-  const int64_t tw = (int64_t)cdiv(O, pw.bm) * cdiv(I, pw.bn);
+  const int64_t tw = (int64_t)cdiv(O, wbm) * cdiv(I, pw.bn);
   const int64_t n1 = (tw + 7) / 8 * 8, n0 = (tx + 7) / 8 * 8;
   const dim3 g((unsigned)(n1 + n0));
 #define HLQ_PAIR(W_, X_) hipLaunchKernelGGL((k_gemm_pair<W_, X_>), g, dim3(256), 0, s, aw, n1, ax)
 #define HLQ_W0 128, 128, 64, 3
 #define HLQ_W1 256, 128, 64, 3
 #define HLQ_W2 128, 128, 128, 2
+#define HLQ_W3 64, 128, 128, 3
 #define HLQ_X0 128, 128, 64, 3
 #define HLQ_X1 256, 128, 64, 3
   const bool x1 = px.cfg == 1;
-  switch (pw.cfg) {
+  switch (wcfg) {
     case 1: if (x1) HLQ_PAIR(HLQ_W1, HLQ_X1); else HLQ_PAIR(HLQ_W1, HLQ_X0); break;
     case 2: if (x1) HLQ_PAIR(HLQ_W2, HLQ_X1); else HLQ_PAIR(HLQ_W2, HLQ_X0); break;
+    case 3: if (x1) HLQ_PAIR(HLQ_W3, HLQ_X1); else HLQ_PAIR(HLQ_W3, HLQ_X0); break;
     default: if (x1) HLQ_PAIR(HLQ_W0, HLQ_X1); else HLQ_PAIR(HLQ_W0, HLQ_X0); break;
   }
 #undef HLQ_PAIR
 #undef HLQ_W0
 #undef HLQ_W1
 #undef HLQ_W2
+#undef HLQ_W3
 #undef HLQ_X0
 #undef HLQ_X1
   return hipGetLastError();
