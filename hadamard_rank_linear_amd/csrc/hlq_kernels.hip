@@ -163,16 +163,6 @@ __global__ __launch_bounds__(256) void k_acbp(const void* __restrict__ x, int64_
   if (lane == 0) scales[row] = scale_of(a, 7.f);
 }
 
-// Workgroup id -> tile id such that each of the 8 XCDs (which take workgroup
-// ids round-robin) runs one contiguous range of tiles.  Neighbouring tiles
-// write neighbouring pieces of the same output lines, which then meet in one
-// L2 instead of leaving it as partial lines from several.  The grid is
-// rounded up to a multiple of 8; ids past the last tile return -1.
-__device__ __forceinline__ int64_t xcd_range_tile(int64_t w, int64_t total) {
-  const int64_t per = (total + 7) / 8;
-  const int64_t t = (w % 8) * per + w / 8;
-  return t < total ? t : -1;
-}
 
 // Value of lane ^ M of the wave (M = 1, 2: DPP quad permute; 8: DPP row
 // rotate by 8; 4, 16: swizzle inside 32 lanes; 32: bpermute).
@@ -960,25 +950,10 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
   static_assert(CW * OUT_PITCH <= TileSmem<F32>::bytes, "staging fits the smem buffer");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TileSmem<F32>::bytes];
   __shared__ float red[4 * CW];
-  int64_t bid = xcd_range_tile(blockIdx.x, a.gyreg_wgs + a.gy_workers + a.wg_x + a.wg_w);
-  if (bid < 0) return;
-  if constexpr (PASS == PASS_MAX && N <= 64) {
-    // register-resident g_y tiles: four independent waves, one tile each
-    if (bid < a.gyreg_wgs) {
-      const int64_t tile = bid * 4 + (threadIdx.x >> 6);
-      if (tile < a.wg_gy) {
-        uint4 raw[8][2];
-        gyr_load(a, tile, raw);
-        gyr_tile_max<N, R>(a, tile, raw);
-      }
-      return;
-    }
-  }
-  bid -= a.gyreg_wgs;
-  if constexpr (PASS == PASS_MAX) {
-    if (bid == 0 && threadIdx.x < 4) a.tmax[threadIdx.x] = 0u;  // k_tr_reduce folds into it
-  } else {
-    if (bid == 0 && threadIdx.x < 4) {  // tensor scales of the per-tensor modes
+  if (blockIdx.x == 0 && threadIdx.x < 4) {
+    if constexpr (PASS == PASS_MAX) {
+      a.tmax[threadIdx.x] = 0u;  // k_tr_reduce folds into it
+    } else {  // tensor scales of the per-tensor modes
       const int l = threadIdx.x;
       const float qmax = l < 2 ? 7.f : 127.f;
       if (l < 2 ? !a.gx_tok : !a.gw_tok) {
@@ -987,17 +962,44 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
       }
     }
   }
-  if (bid < a.gy_workers) {  // g_y tiles on the LDS engine
-    tr_job_gy<PASS, N, R, F32>(a, bid, smem, red);
+  // Workgroup -> job: consecutive ids go to the 8 XCDs in turn; slot s of an
+  // XCD walks that XCD's eighth of each job list in the order register g_y,
+  // LDS g_y, x, w (longest tiles first).  Every XCD gets the same mix of
+  // jobs, and within a job list a contiguous range of tiles.
+  const int64_t xcd = blockIdx.x % 8;
+  int64_t slot = blockIdx.x / 8;
+  const int64_t per_r = (a.gyreg_wgs + 7) / 8, per_g = (a.gy_workers + 7) / 8;
+  const int64_t per_x = (a.wg_x + 7) / 8, per_w = (a.wg_w + 7) / 8;
+  if constexpr (PASS == PASS_MAX && N <= 64) {
+    // register-resident g_y tiles: four independent waves, one tile each
+    if (slot < per_r) {
+      const int64_t bid = xcd * per_r + slot;
+      const int64_t tile = bid * 4 + (threadIdx.x >> 6);
+      if (bid < a.gyreg_wgs && tile < a.wg_gy) {
+        uint4 raw[8][2];
+        gyr_load(a, tile, raw);
+        gyr_tile_max<N, R>(a, tile, raw);
+      }
+      return;
+    }
+  }
+  slot -= per_r;
+  if (slot < per_g) {  // g_y tiles on the LDS engine
+    const int64_t bid = xcd * per_g + slot;
+    if (bid < a.gy_workers) tr_job_gy<PASS, N, R, F32>(a, bid, smem, red);
     return;
   }
-  bid -= a.gy_workers;
-  if (bid < a.wg_x) {
-    tr_job_x<PASS, N, R>(a, bid, smem, red);
+  slot -= per_g;
+  if (slot < per_x) {
+    const int64_t bid = xcd * per_x + slot;
+    if (bid < a.wg_x) tr_job_x<PASS, N, R>(a, bid, smem, red);
     return;
   }
-  bid -= a.wg_x;
-  if (bid < a.wg_w) tr_job_w<PASS, N, F32>(a, bid, smem, red);
+  slot -= per_x;
+  if (slot < per_w) {
+    const int64_t bid = xcd * per_w + slot;
+    if (bid < a.wg_w) tr_job_w<PASS, N, F32>(a, bid, smem, red);
+  }
 }
 
 // Fold the partial maxima.  Entry e of each list takes the max over its
@@ -1520,9 +1522,11 @@ hipError_t launch_tr(const TrArgs& args, int pass, int n, int r, hipStream_t s) 
     a.gy_workers = 0;
     a.gyreg_wgs = (a.wg_gy + 3) / 4;
   }
-  const int64_t wgs = a.gyreg_wgs + a.gy_workers + a.wg_x + a.wg_w;
-  if (wgs <= 0) return hipSuccess;
-  dim3 g((unsigned)((wgs + 7) / 8 * 8));
+  // eight slots per XCD row: each XCD takes an eighth of every job list
+  const int64_t slots = (a.gyreg_wgs + 7) / 8 + (a.gy_workers + 7) / 8 + (a.wg_x + 7) / 8 +
+                        (a.wg_w + 7) / 8;
+  if (slots <= 0) return hipSuccess;
+  dim3 g((unsigned)(slots * 8));
   const bool f32 = a.gy_dt == 0 || a.w_dt == 0;
   if (pass == PASS_MAX)
     return f32 ? tr_dispatch<PASS_MAX, true>(n, r, g, s, a) : tr_dispatch<PASS_MAX, false>(n, r, g, s, a);
