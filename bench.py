@@ -10,7 +10,8 @@ torch.cuda.synchronize(); the steps rotate over several copies of the
 inputs/outputs/workspace whose total exceeds the 256 MB last-level cache, so
 every step reads its operands from HBM.  A second, instrumented pass records
 HIP events around each launch step (same stream, same rotation) to get
-per-kernel durations; the longest one is reported against its roofline.
+per-kernel durations (less the interval of an empty step, the cost of the
+event itself); the longest one is reported against its roofline.
 
 The CPU baseline is the oracle (numpy) running the same layer once on the host.
 """
@@ -185,8 +186,10 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
         # queue is full and no launch gap lands inside a measured interval.
         # launch units as the full backward runs them: the two GEMM steps
         # together are one launch
+        # The "empty" unit launches nothing: its interval is the cost of one
+        # event record in the queue, subtracted from the others.
         units = [("tr_max", 1 << 0), ("tr_reduce", 1 << 1), ("tr_quant", 1 << 2),
-                 ("gemm", (1 << 3) | (1 << 4))]
+                 ("gemm", (1 << 3) | (1 << 4)), ("empty", 0)]
         active = list(range(len(units)))
         n_inst = min(steps, 20)
         cal0 = torch.cuda.Event(enable_timing=True)
@@ -212,7 +215,11 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
         acc = {k: 0.0 for k in active}
         for (k, a), (_, b) in zip(marks, marks[1:]):
             acc[k] += a.elapsed_time(b)
-        res["kernels_us"] = {units[k][0]: acc[k] / n_inst * 1e3 for k in active}
+        raw = {units[k][0]: acc[k] / n_inst * 1e3 for k in active}
+        empty = raw.pop("empty")
+        res["kernels_event_us"] = raw
+        res["event_overhead_us"] = empty
+        res["kernels_us"] = {k: max(v - empty, 0.0) for k, v in raw.items()}
         res["instrumented_steps"] = n_inst
     del sets
     torch.cuda.empty_cache()
@@ -332,6 +339,8 @@ def main():
         "layer_roofline_frac": round(ideal_total / lat_us, 4),
         "acbp_us": round(res["acbp_us"], 2),
         "kernels_us": {k: round(v, 2) for k, v in res["kernels_us"].items()},
+        "kernels_event_us": {k: round(v, 2) for k, v in res["kernels_event_us"].items()},
+        "event_overhead_us": round(res["event_overhead_us"], 2),
         "rotating_sets": res["nsets"],
     }
     line.update(extra)
