@@ -1623,11 +1623,13 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
                     gx_alpha, g_x, nullptr};
   const GemmArgs aw{gwA, gwB, O, I, kw_pitch, pw.stages, pw.stages, s_gyl, gw_step, s_xl, gw_step,
                     gw_alpha, g_w, nullptr};
-  // g_w tile: the plan's, except that a long-K g_w grid smaller than the CU
-  // count (its tiles would be the launch's critical path) takes 64-row tiles
-  // (cfg 3: 64 x 128, KB 128, 3 stages): twice the tiles, half the K work each.
+  // g_w tile: the plan's, except that a long-K g_w grid of fewer than 64
+  // tiles (a quarter of the CU count; its tiles are the launch's critical
+  // path) takes 64-row tiles (cfg 3: 64 x 128, KB 128, 3 stages): twice the
+  // tiles, half the K work each.  Larger grids keep 128 x 128, which reads
+  // fewer LDS bytes per MFMA (ViT-B qkv, 108 tiles: 46 -> 43 us).
   int wcfg = pw.cfg, wbm = pw.bm;
-  if (pw.cfg == 2 && (int64_t)cdiv(O, 128) * cdiv(I, 128) < 256) { wcfg = 3; wbm = 64; }
+  if (pw.cfg == 2 && (int64_t)cdiv(O, 128) * cdiv(I, 128) < 64) { wcfg = 3; wbm = 64; }
   const int64_t tx = (int64_t)cdiv(T, px.bm) * cdiv(I, px.bn);
   const int64_t tw = (int64_t)cdiv(O, wbm) * cdiv(I, pw.bn);
   const int64_t n1 = (tw + 7) / 8 * 8, n0 = (tx + 7) / 8 * 8;
