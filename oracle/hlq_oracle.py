@@ -61,6 +61,18 @@ R8  The "1/B" of the g_w identity ([HLQ] TL;DR) is read as two factors: the
     g_w only (argument ``reduction``).
 R9  Outputs g_x [T x I] and g_w [O x I] are fp32; the epilogue is evaluated in
     fp64 and rounded once to fp32.
+R10 Layer-wise quantizer selection (LQS; [HOT-abs] abstract, [HOT-sum]
+    "Approach" and "Limitations": chosen per layer from a calibration set with
+    a 50% MSE-difference threshold).  For each of the four GEMM operands (the
+    transformed g_y and w of the g_x path, the low-rank g_y and x of the g_w
+    path) and each mode, the squared reconstruction error of every element is
+    e^2 with e = fl32(v - fl32(s * q)) (codes and scale of reading R5), summed
+    in fp64 over the calibration batches together with sum(v^2).  A path's
+    error in a mode is the sum over its two operands of SSE / sum(v^2).  The
+    path takes PER_TOKEN when its PER_TENSOR error exceeds its PER_TOKEN error
+    by more than the threshold (0.5: more than 50% larger), else PER_TENSOR,
+    the single-scale quantizer.  (The pages name the threshold, not the error
+    measure; this is the plainest reading of "MSE difference".)
 """
 from __future__ import annotations
 
@@ -340,6 +352,83 @@ def linear_backward_unquantized(gy, x, w, block: int, rank: int,
     return dict(g_x=g_x, g_w=g_w)
 
 
+# --------------------------------------------------------------------------
+# Layer-wise quantizer selection ([HOT-abs] abstract; [HOT-sum] "Approach",
+# "Limitations"; reading R10)
+# --------------------------------------------------------------------------
+
+LQS_THRESHOLD = 0.5
+LQS_OPERANDS = ("H.g_y", "H.w", "lowrank g_y", "lowrank x")
+
+
+def lqs_operands(gy, x_codes, x_scales, w, block: int, rank: int):
+    """The four transformed GEMM operands as (values fp32, qmax, group axis).
+
+    The group axis is the axis one PER_TOKEN scale runs along (reading R6):
+    along O for each token of H.g_y, along O for each input channel of H.w,
+    along T' for each channel of the low-rank g_y and x.
+    """
+    gy = np.asarray(gy, dtype=np.float32)
+    w = np.asarray(w, dtype=np.float32)
+    n, r = block, rank
+    x = acbp_unpack(x_codes, x_scales)
+    return [(fwht_blocks(gy, n, axis=1), QMAX_INT4, 1),
+            (fwht_blocks(w, n, axis=0), QMAX_INT4, 0),
+            (lowrank_transform(gy, n, r, axis=0), QMAX_INT8, 0),
+            (lowrank_transform(x, n, r, axis=0), QMAX_INT8, 0)]
+
+
+def quant_sq_error(v: np.ndarray, qmax: int, reduce_axis) -> float:
+    """Sum over v of e^2 (fp64), e = fl32(v - fl32(s * q)) with the codes and
+    scales of :func:`quantize` for that grouping (reading R10)."""
+    v = np.asarray(v, dtype=np.float32)
+    q, s = quantize(v, qmax, reduce_axis)
+    if reduce_axis is None:
+        sb = s.reshape((1,) * v.ndim)
+    else:
+        sb = np.expand_dims(s, reduce_axis)
+    deq = (sb * q.astype(np.float32)).astype(np.float32)
+    e = (v - deq).astype(np.float32)
+    return float(np.sum(e.astype(np.float64) ** 2))
+
+
+def lqs_stats(gy, x_codes, x_scales, w, block: int, rank: int) -> np.ndarray:
+    """LQS statistics of one calibration batch: 16 fp64 values, four per
+    operand k (order of LQS_OPERANDS): [4k] sum(v^2), [4k+1] SSE PER_TOKEN,
+    [4k+2] SSE PER_TENSOR, [4k+3] element count.  Batches add up."""
+    out = np.zeros(16, dtype=np.float64)
+    for k, (v, qmax, axis) in enumerate(lqs_operands(gy, x_codes, x_scales, w, block, rank)):
+        out[4 * k] = float(np.sum(v.astype(np.float64) ** 2))
+        out[4 * k + 1] = quant_sq_error(v, qmax, axis)
+        out[4 * k + 2] = quant_sq_error(v, qmax, None)
+        out[4 * k + 3] = float(v.size)
+    return out
+
+
+def lqs_path_errors(stats) -> tuple:
+    """((E_tok, E_ten) of the g_x path, (E_tok, E_ten) of the g_w path):
+    per mode, the sum over the path's two operands of SSE / sum(v^2), each
+    term 0 for an all-zero operand."""
+    st = np.asarray(stats, dtype=np.float64)
+
+    def rel(k, col):
+        ss = st[4 * k]
+        return 0.0 if ss == 0.0 else float(st[4 * k + col] / ss)
+
+    gx = (rel(0, 1) + rel(1, 1), rel(0, 2) + rel(1, 2))
+    gw = (rel(2, 1) + rel(3, 1), rel(2, 2) + rel(3, 2))
+    return gx, gw
+
+
+def lqs_select(stats, threshold: float = LQS_THRESHOLD) -> tuple:
+    """(gx_mode, gw_mode): PER_TOKEN for a path whose PER_TENSOR error is more
+    than (1 + threshold) times its PER_TOKEN error, else PER_TENSOR."""
+    modes = []
+    for e_tok, e_ten in lqs_path_errors(stats):
+        modes.append(PER_TOKEN if e_ten > (1.0 + threshold) * e_tok else PER_TENSOR)
+    return tuple(modes)
+
+
 def rel_fro(a, b) -> float:
     """||a - b||_F / ||b||_F in fp64 (0 when both are zero)."""
     a = np.asarray(a, dtype=np.float64)
@@ -357,5 +446,6 @@ __all__ = [
     "sylvester_hadamard", "fwht_blocks", "lowrank_rows", "sequency",
     "lowrank_transform", "quantize", "pack_int4", "unpack_int4", "acbp_pack",
     "acbp_unpack", "int_matmul", "linear_backward",
-    "linear_backward_unquantized", "rel_fro",
+    "linear_backward_unquantized", "rel_fro", "LQS_THRESHOLD", "LQS_OPERANDS",
+    "lqs_operands", "quant_sq_error", "lqs_stats", "lqs_path_errors", "lqs_select",
 ]
