@@ -226,6 +226,46 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
     return res
 
 
+def time_lqs(cfg, inp, reps=10):
+    """Layer-wise quantizer selection statistics of one calibration batch
+    (hlq_lqs_accumulate: five launches) on the layer's inputs, and the modes
+    the 50% rule picks from them.  Algorithmic bytes: both passes read g_y
+    twice (rows along O, columns along T), w once and the ACBP codes once."""
+    import numpy as np
+    import torch
+    import hadamard_rank_linear_amd as h
+    dev = torch.device("cuda:0")
+    bf = cfg.dtype == 1
+
+    def dev_t(a):
+        if bf:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    gy, x, w = dev_t(inp["gy"]), dev_t(inp["x"]), dev_t(inp["w"])
+    codes, scales = h.hlq_compress_act(x)
+    ws = torch.empty((h.hlq_lqs_workspace_size(cfg.T, cfg.I, cfg.O, cfg.block, cfg.rank),),
+                     dtype=torch.uint8, device=dev)
+    stats = torch.zeros((16,), dtype=torch.float64, device=dev)
+    h.hlq_lqs_accumulate(gy, codes, scales, w, cfg.block, cfg.rank, stats=stats, workspace=ws)
+    torch.cuda.synchronize()
+    modes = h.hlq_lqs_select(stats)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        h.hlq_lqs_accumulate(gy, codes, scales, w, cfg.block, cfg.rank, stats=stats, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    e = 2 if bf else 4
+    nbytes = 2 * (2 * cfg.T * cfg.O * e + cfg.O * cfg.I * e + cfg.T * cfg.I // 2 + 4 * cfg.T)
+    return {"us": round(us, 2), "algorithmic_bytes": nbytes,
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "selected_modes": {"gx": "per_token" if modes[0] == 0 else "per_tensor",
+                               "gw": "per_token" if modes[1] == 0 else "per_tensor"}}
+
+
 def cpu_baseline(cfg, inp):
     import numpy as np
     import oracle as o
@@ -255,7 +295,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vitb_qkv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the fc2 side measurement")
+    ap.add_argument("--no-extra", action="store_true", help="skip the side measurements (fc2 layer, LQS statistics)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run 256 MiB device copies (scale of the HBM byte counters)")
     args = ap.parse_args()
@@ -300,6 +340,9 @@ def main():
                 algorithmic_ops=ops, traffic=traffic)
 
     extra = {}
+    if not args.no_extra:
+        log("layer-wise quantizer selection statistics")
+        extra["lqs"] = time_lqs(cfg, inp)
     if not args.no_extra and cfg.name != "vitb_fc2":
         c2 = wl.BY_NAME["vitb_fc2"]
         log("side measurement: vitb_fc2")

@@ -109,6 +109,41 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   return L;
 }
 
+// Workspace of hlq_lqs_accumulate: group maxima, tensor maxima, per-workgroup
+// partial sums.
+struct LqsLayout {
+  size_t gmax, tmax, part, total;
+  int64_t items[4], wg0[5];
+  double count[4];
+};
+
+LqsLayout make_lqs_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
+  LqsLayout L;
+  memset(&L, 0, sizeof(L));
+  const int64_t n = block, S = hlq::LQS_STRIP;
+  L.items[0] = T * (O / n);
+  L.items[1] = (O / n + S - 1) / S * I;
+  L.items[2] = (T / n + S - 1) / S * O;
+  L.items[3] = (T / n + S - 1) / S * I;
+  L.count[0] = (double)(T * O);
+  L.count[1] = (double)(O * I);
+  L.count[2] = (double)(T / n * rank * O);
+  L.count[3] = (double)(T / n * rank * I);
+  L.wg0[0] = 0;
+  for (int k = 0; k < 4; ++k) L.wg0[k + 1] = L.wg0[k] + (L.items[k] + 255) / 256;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L.gmax = take((size_t)(T + 2 * I + O) * 4);
+  L.tmax = take(4 * 4);
+  L.part = take((size_t)L.wg0[4] * 3 * 8);
+  L.total = off;
+  return L;
+}
+
 #define HLQ_TRY(expr)                       \
   do {                                      \
     if ((expr) != hipSuccess) return HLQ_ERR_HIP; \
@@ -282,6 +317,62 @@ hlq_status hlq_gemm_gw_acc(const void* workspace, int64_t T, int64_t I, int64_t 
   HLQ_TRY(hlq::launch_gemm(false, ws + L.pub.q_gyl, ws + L.pub.q_xl, O, I, L.pub.kw_pitch,
                            L.plan_gw, nullptr, 0, nullptr, 0, 1.f, hlq::EPI_I32, nullptr,
                            acc_w, nullptr, static_cast<hipStream_t>(stream)));
+  return HLQ_OK;
+}
+
+size_t hlq_lqs_workspace_size(int64_t T, int64_t I, int64_t O, int block, int rank) {
+  if (check_shape(T, I, O, block, rank) != HLQ_OK) return 0;
+  return make_lqs_layout(T, I, O, block, rank).total;
+}
+
+hlq_status hlq_lqs_accumulate(const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                              const float* x_scales, const void* w, int w_dtype, int64_t T,
+                              int64_t I, int64_t O, int block, int rank, double* stats,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!g_y || !x_codes || !x_scales || !w || !stats) return HLQ_ERR_NULL;
+  if ((gy_dtype != HLQ_F32 && gy_dtype != HLQ_BF16) ||
+      (w_dtype != HLQ_F32 && w_dtype != HLQ_BF16))
+    return HLQ_ERR_DTYPE;
+  hlq_status st = check_shape(T, I, O, block, rank);
+  if (st != HLQ_OK) return st;
+  const LqsLayout L = make_lqs_layout(T, I, O, block, rank);
+  if (!workspace || workspace_bytes < L.total) return HLQ_ERR_WORKSPACE;
+  if (!aligned16(g_y) || !aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w) ||
+      !aligned16(stats) || !aligned16(workspace))
+    return HLQ_ERR_ALIGN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hlq::LqsArgs a;
+  memset(&a, 0, sizeof(a));
+  a.gy = g_y; a.gy_dt = gy_dtype;
+  a.xc = x_codes; a.xs = x_scales;
+  a.w = w; a.w_dt = w_dtype;
+  a.T = T; a.I = I; a.O = O; a.r = rank;
+  a.gmax = reinterpret_cast<unsigned*>(ws + L.gmax);
+  a.tmax = reinterpret_cast<unsigned*>(ws + L.tmax);
+  a.part = reinterpret_cast<double*>(ws + L.part);
+  a.stats = stats;
+  for (int k = 0; k < 4; ++k) {
+    a.items[k] = L.items[k];
+    a.count[k] = L.count[k];
+  }
+  for (int k = 0; k < 5; ++k) a.wg0[k] = L.wg0[k];
+  HLQ_TRY(hlq::launch_lqs(a, block, static_cast<hipStream_t>(stream)));
+  return HLQ_OK;
+}
+
+hlq_status hlq_lqs_select(const double* stats, double threshold, int* gx_mode,
+                          int* gw_mode) {
+  if (!stats || !gx_mode || !gw_mode) return HLQ_ERR_NULL;
+  if (!(threshold >= 0.0)) return HLQ_ERR_MODE;
+  // relative error of operand k in mode column c (1 per-token, 2 per-tensor)
+  auto rel = [&](int k, int c) {
+    const double ss = stats[4 * k];
+    return ss == 0.0 ? 0.0 : stats[4 * k + c] / ss;
+  };
+  const double gx_tok = rel(0, 1) + rel(1, 1), gx_ten = rel(0, 2) + rel(1, 2);
+  const double gw_tok = rel(2, 1) + rel(3, 1), gw_ten = rel(2, 2) + rel(3, 2);
+  *gx_mode = gx_ten > (1.0 + threshold) * gx_tok ? HLQ_PER_TOKEN : HLQ_PER_TENSOR;
+  *gw_mode = gw_ten > (1.0 + threshold) * gw_tok ? HLQ_PER_TOKEN : HLQ_PER_TENSOR;
   return HLQ_OK;
 }
 

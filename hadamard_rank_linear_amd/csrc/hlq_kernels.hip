@@ -1471,6 +1471,221 @@ __global__ __launch_bounds__(256) void k_gemm_finalize(const int32_t* __restrict
   *reinterpret_cast<float4*>(C + e) = o;
 }
 
+// ------------------------------------------------------------ LQS statistics
+// Layer-wise quantizer selection ("HOT: Hadamard-based Optimized Training",
+// abstract; scime.ai summary, "Approach" and "Limitations": per-token or
+// per-tensor chosen per layer from calibration data with a 50% MSE-difference
+// threshold).  For each of the four operands the backward quantizes, the
+// squared reconstruction error under per-token and under per-tensor scales,
+// with sum(v^2) and the element count.  Two passes over the inputs: group
+// maxima (MAX), then errors (ERR) once every scale is known.  One thread
+// transforms one block of n values of one operand:
+//   op 0  H.g_y          row t, block beta along O      group: token t
+//   op 1  H.w            column i, block beta along O   group: input channel i
+//   op 2  low-rank g_y   column o, token block b        group: channel o
+//   op 3  low-rank x     column i, token block b        group: channel i
+// with the fp32 butterfly network of the backward (ascending stages); the
+// low-rank operands keep outputs j * (n / r).  A thread of a column operand
+// walks LQS_STRIP consecutive blocks of its column (one group maximum per
+// strip).  Calibration work, not the backward's hot path: no tiling.
+
+__device__ __forceinline__ float ld_dt(const void* base, int dt, int64_t e) {
+  return dt == 0 ? static_cast<const float*>(base)[e]
+                 : bf16_to_f32(static_cast<const uint16_t*>(base)[e]);
+}
+
+template <int N>
+__device__ __forceinline__ void fwht_reg(float (&v)[N]) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if ((k & h) == 0) {
+        const float p = v[k], q = v[k + h];
+        v[k] = p + q;
+        v[k + h] = p - q;
+      }
+}
+
+// Quantizer of a group whose largest magnitude is a: s = fl(a / qmax),
+// inv = fl(qmax / a); codes are 0 when a is 0 or qmax / a overflows.
+struct LqsQuant {
+  float inv, s, qmax;
+  bool on;
+};
+
+__device__ __forceinline__ LqsQuant lqs_quant(float a, float qmax) {
+  LqsQuant z{0.f, 0.f, qmax, false};
+  if (a != 0.f) {
+    z.inv = qmax / a;
+    z.s = a / qmax;
+    z.on = !__builtin_isinf(z.inv);
+  }
+  return z;
+}
+
+// fl(v - fl(s * q)): reconstruction error of v under quantizer z.
+__device__ __forceinline__ float lqs_err(float v, const LqsQuant& z) {
+  const float q = z.on ? fminf(fmaxf(rintf(v * z.inv), -z.qmax), z.qmax) : 0.f;
+  const float d = z.s * q;
+  return v - d;
+}
+
+__global__ __launch_bounds__(256) void k_lqs_zero(unsigned* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+template <int N, int PASS>
+__global__ __launch_bounds__(256) void k_lqs(LqsArgs a) {
+  __shared__ double red[3][256];
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const int op = (b >= a.wg0[1]) + (b >= a.wg0[2]) + (b >= a.wg0[3]);
+  const int64_t item = (b - a.wg0[op]) * 256 + tid;
+  const bool valid = item < a.items[op];
+  const int64_t T = a.T, I = a.I, O = a.O;
+  const int step = op >= 2 ? N / a.r : 1;  // outputs k with k % step == 0 are kept
+  const float qmax = op >= 2 ? 127.f : 7.f;
+  // a column operand's thread walks LQS_STRIP consecutive blocks of its column
+  const int64_t ncol = op == 1 ? I : (op == 2 ? O : I);
+  const int64_t nblk = op == 1 ? O / N : T / N;
+  int group = 0;
+  int64_t col = 0, blk0 = 0, blk1 = 0;
+  if (op == 0) {
+    group = (int)(item / (O / N));
+  } else {
+    col = item % ncol;
+    blk0 = item / ncol * LQS_STRIP;
+    blk1 = blk0 + LQS_STRIP < nblk ? blk0 + LQS_STRIP : nblk;
+    group = (int)((op == 1 ? T : (op == 2 ? T + I : T + I + O)) + col);
+  }
+  // the thread's group is fixed: both quantizers are computed once
+  LqsQuant zt{0.f, 0.f, qmax, false}, zT{0.f, 0.f, qmax, false};
+  if constexpr (PASS == 1) {
+    if (valid) {
+      zt = lqs_quant(__uint_as_float(a.gmax[group]), qmax);
+      zT = lqs_quant(__uint_as_float(a.tmax[op]), qmax);
+    }
+  }
+  float m = 0.f;
+  double ss = 0.0, e_tok = 0.0, e_ten = 0.0;
+  float v[N];
+  auto consume = [&]() {
+    fwht_reg<N>(v);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if ((k & (step - 1)) == 0) {
+        const float x = v[k];
+        if constexpr (PASS == 0) {
+          m = fmaxf(m, fabsf(x));
+        } else {
+          const float d1 = lqs_err(x, zt), d2 = lqs_err(x, zT);
+          ss += (double)x * (double)x;
+          e_tok += (double)d1 * (double)d1;
+          e_ten += (double)d2 * (double)d2;
+        }
+      }
+  };
+  if (valid) {
+    if (op == 0) {
+      const int64_t e0 = (int64_t)group * O + item % (O / N) * N;
+#pragma unroll
+      for (int k = 0; k < N; k += 8) {
+        float u[8];
+        if (a.gy_dt == 0) load8<0>(a.gy, e0 + k, u); else load8<1>(a.gy, e0 + k, u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[k + j] = u[j];
+      }
+      consume();
+    } else {
+      for (int64_t bb = blk0; bb < blk1; ++bb) {
+        if (op == 1) {
+#pragma unroll
+          for (int k = 0; k < N; ++k) v[k] = ld_dt(a.w, a.w_dt, (bb * N + k) * I + col);
+        } else if (op == 2) {
+#pragma unroll
+          for (int k = 0; k < N; ++k) v[k] = ld_dt(a.gy, a.gy_dt, (bb * N + k) * O + col);
+        } else {
+          const int64_t half = I / 2;
+#pragma unroll
+          for (int k = 0; k < N; ++k) {
+            const int64_t t = bb * N + k;
+            const unsigned byte = a.xc[t * half + col / 2];
+            const int code = (int)(((col & 1) ? byte >> 4 : byte) & 15u);
+            v[k] = a.xs[t] * (float)((code ^ 8) - 8);  // x = fl(s_x[t] * q)
+          }
+        }
+        consume();
+      }
+    }
+  }
+  if constexpr (PASS == 0) {
+    // consecutive blocks of one row share a group: one atomic per wave then
+    const int g0 = __shfl(group, 0);
+    if (__all(valid && group == g0)) {
+      m = wave_max(m);
+      if ((tid & 63) == 0) atomicMax(&a.gmax[g0], __float_as_uint(m));
+    } else if (valid) {
+      atomicMax(&a.gmax[group], __float_as_uint(m));
+    }
+  } else {
+    red[0][tid] = ss;
+    red[1][tid] = e_tok;
+    red[2][tid] = e_ten;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {  // fixed order: the sums are reproducible
+      if (tid < h) {
+        red[0][tid] += red[0][tid + h];
+        red[1][tid] += red[1][tid + h];
+        red[2][tid] += red[2][tid + h];
+      }
+      __syncthreads();
+    }
+    if (tid < 3) a.part[b * 3 + tid] = red[tid][0];
+  }
+}
+
+// Tensor maxima: the largest group maximum of each operand.
+__global__ __launch_bounds__(256) void k_lqs_fold(LqsArgs a) {
+  __shared__ unsigned red[256];
+  const int tid = threadIdx.x;
+  const int64_t base[5] = {0, a.T, a.T + a.I, a.T + a.I + a.O, a.T + 2 * a.I + a.O};
+  for (int op = 0; op < 4; ++op) {
+    unsigned m = 0u;
+    for (int64_t g = base[op] + tid; g < base[op + 1]; g += 256) m = max(m, a.gmax[g]);
+    red[tid] = m;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+      if (tid < h) red[tid] = max(red[tid], red[tid + h]);
+      __syncthreads();
+    }
+    if (tid == 0) a.tmax[op] = red[0];
+    __syncthreads();
+  }
+}
+
+// Sum the per-workgroup partials in a fixed order and add them (and the
+// element counts) to the caller's statistics.
+__global__ __launch_bounds__(256) void k_lqs_final(LqsArgs a) {
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  for (int op = 0; op < 4; ++op)
+    for (int c = 0; c < 3; ++c) {
+      double acc = 0.0;
+      for (int64_t g = a.wg0[op] + tid; g < a.wg0[op + 1]; g += 256) acc += a.part[g * 3 + c];
+      red[tid] = acc;
+      __syncthreads();
+      for (int h = 128; h > 0; h >>= 1) {
+        if (tid < h) red[tid] += red[tid + h];
+        __syncthreads();
+      }
+      if (tid == 0) a.stats[4 * op + c] += red[0];
+      __syncthreads();
+    }
+  if (tid < 4) a.stats[4 * tid + 3] += a.count[tid];
+}
+
 // ------------------------------------------------------------ launchers
 
 static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
@@ -1665,6 +1880,30 @@ hipError_t launch_gemm_finalize(const int32_t* partial, int splits, int64_t M,
   const int64_t q4 = M * N / 4;
   hipLaunchKernelGGL(k_gemm_finalize, dim3(cdiv(q4, 256)), dim3(256), 0, s, partial, splits,
                      M, N, sa, sa_step, sb, sb_step, alpha, C);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_lqs(const LqsArgs& a, int n, hipStream_t s) {
+  const int64_t groups = a.T + 2 * a.I + a.O;
+  const unsigned zb = (unsigned)(cdiv(groups, 256) < 1024 ? cdiv(groups, 256) : 1024);
+  hipLaunchKernelGGL(k_lqs_zero, dim3(zb), dim3(256), 0, s, a.gmax, groups);
+  const dim3 g((unsigned)a.wg0[4]);
+  switch (n) {
+    case 16: hipLaunchKernelGGL((k_lqs<16, 0>), g, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_lqs<32, 0>), g, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_lqs<64, 0>), g, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((k_lqs<128, 0>), g, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL(k_lqs_fold, dim3(1), dim3(256), 0, s, a);
+  switch (n) {
+    case 16: hipLaunchKernelGGL((k_lqs<16, 1>), g, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_lqs<32, 1>), g, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_lqs<64, 1>), g, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_lqs<128, 1>), g, dim3(256), 0, s, a); break;
+  }
+  hipLaunchKernelGGL(k_lqs_final, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

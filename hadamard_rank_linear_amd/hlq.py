@@ -27,6 +27,9 @@ EXPORTED = (
     "hlq_workspace_layout_query",
     "hlq_gemm_gx_acc",
     "hlq_gemm_gw_acc",
+    "hlq_lqs_workspace_size",
+    "hlq_lqs_accumulate",
+    "hlq_lqs_select",
     "hlq_status_string",
     "hlq_version",
 )
@@ -71,6 +74,14 @@ def _load():
     lib.hlq_gemm_gx_acc.restype = I32
     lib.hlq_gemm_gw_acc.argtypes = [P, I64, I64, I64, I32, I32, P, P]
     lib.hlq_gemm_gw_acc.restype = I32
+    lib.hlq_lqs_workspace_size.argtypes = [I64, I64, I64, I32, I32]
+    lib.hlq_lqs_workspace_size.restype = SZ
+    lib.hlq_lqs_accumulate.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I32, I32, P, P,
+                                       SZ, P]
+    lib.hlq_lqs_accumulate.restype = I32
+    lib.hlq_lqs_select.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_double,
+                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    lib.hlq_lqs_select.restype = I32
     lib.hlq_status_string.argtypes = [I32]
     lib.hlq_status_string.restype = ctypes.c_char_p
     lib.hlq_version.argtypes = []
@@ -202,6 +213,54 @@ def hlq_gemm_gw_acc(workspace, T, I, O, block, rank, acc_w=None, stream=None):
     _check("hlq_gemm_gw_acc", _lib.hlq_gemm_gw_acc(
         _ptr(workspace), T, I, O, block, rank, _ptr(acc_w), _stream(stream)))
     return acc_w
+
+
+HLQ_LQS_STATS = 16
+HLQ_LQS_THRESHOLD = 0.5
+
+
+def hlq_lqs_workspace_size(T, I, O, block, rank) -> int:
+    return int(_lib.hlq_lqs_workspace_size(T, I, O, block, rank))
+
+
+def hlq_lqs_accumulate(g_y, x_codes, x_scales, w, block, rank, stats=None, workspace=None,
+                       stream=None):
+    """Add one calibration batch to the layer-wise quantizer selection
+    statistics: ``stats`` is a float64 GPU tensor of 16 values (zeros when
+    omitted), returned.  Same inputs as :func:`hlq_linear_backward`."""
+    import torch
+    T, O = g_y.shape
+    O2, I = w.shape
+    if O2 != O:
+        raise ValueError("w must be [O, I] with O = g_y.shape[1]")
+    dev = g_y.device
+    if stats is None:
+        stats = torch.zeros((HLQ_LQS_STATS,), dtype=torch.float64, device=dev)
+    if stats.dtype != torch.float64 or stats.numel() != HLQ_LQS_STATS:
+        raise ValueError("stats must be a float64 tensor of 16 values")
+    need = hlq_lqs_workspace_size(T, I, O, block, rank)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _require_cuda(g_y, x_codes, x_scales, w, stats, workspace)
+    _check("hlq_lqs_accumulate", _lib.hlq_lqs_accumulate(
+        _ptr(g_y), _dtype_code(g_y), _ptr(x_codes), _ptr(x_scales), _ptr(w), _dtype_code(w),
+        T, I, O, block, rank, _ptr(stats), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return stats
+
+
+def hlq_lqs_select(stats, threshold=HLQ_LQS_THRESHOLD):
+    """(gx_mode, gw_mode) from 16 statistics (any host sequence or tensor)."""
+    if hasattr(stats, "detach"):
+        stats = stats.detach().cpu().tolist()
+    vals = [float(v) for v in stats]
+    if len(vals) != HLQ_LQS_STATS:
+        raise ValueError("expected 16 statistics")
+    arr = (ctypes.c_double * HLQ_LQS_STATS)(*vals)
+    gx, gw = ctypes.c_int(-1), ctypes.c_int(-1)
+    _check("hlq_lqs_select", _lib.hlq_lqs_select(arr, float(threshold), ctypes.byref(gx),
+                                                 ctypes.byref(gw)))
+    return gx.value, gw.value
 
 
 def lib_handle():

@@ -193,6 +193,48 @@ hlq_status hlq_gemm_gw_acc(const void* workspace, int64_t T, int64_t I, int64_t 
                            int block, int rank, int32_t* acc_w, void* stream);
 
 /* Static text for a status code. */
+/*
+ * Layer-wise quantizer selection (LQS).  "HOT: Hadamard-based Optimized
+ * Training": HF page abstract (layer-wise quantizer selection), scime.ai
+ * summary "Approach" (per-token vs per-tensor chosen per layer) and
+ * "Limitations" (chosen from a calibration set with a 50% MSE-difference
+ * threshold).  The pages name the threshold, not the error measure; the
+ * reading taken here: the squared reconstruction error of each quantized
+ * GEMM operand under each mode.
+ *
+ * hlq_lqs_accumulate adds one calibration batch (the same inputs as
+ * hlq_linear_backward) to `stats`, a DEVICE array of 16 doubles the caller
+ * zeroes once and keeps across batches.  For operand k = 0 (H.g_y along O,
+ * INT4), 1 (H.w along O, INT4), 2 (low-rank g_y along T, INT8), 3 (low-rank
+ * x along T, INT8), with v the fp32 transformed values of the backward:
+ *   stats[4k]   += sum v^2
+ *   stats[4k+1] += sum e^2 with PER_TOKEN scales (one per group of reading R6)
+ *   stats[4k+2] += sum e^2 with a PER_TENSOR scale
+ *   stats[4k+3] += number of elements
+ * where e = fl32(v - fl32(s * q)) with the code q and scale s the backward's
+ * quantizer gives v; e^2 and the sums are fp64 (fixed summation order, so a
+ * call is reproducible).  Five launches on `stream`; the workspace (at least
+ * hlq_lqs_workspace_size bytes) holds group maxima and partial sums.  Shape
+ * rules and errors as for hlq_linear_backward; `stats` must be 16-byte
+ * aligned.
+ *
+ * hlq_lqs_select is a host function on a HOST copy of the 16 statistics.
+ * A path's error in a mode is the sum over its two operands of
+ * SSE / sum v^2 (0 for an all-zero operand).  The path takes HLQ_PER_TOKEN
+ * when its per-tensor error exceeds (1 + threshold) times its per-token
+ * error, else HLQ_PER_TENSOR (the single-scale quantizer).  The pages'
+ * threshold is 0.5.  Errors: HLQ_ERR_NULL, HLQ_ERR_MODE (threshold negative
+ * or NaN).
+ */
+size_t hlq_lqs_workspace_size(int64_t T, int64_t I, int64_t O, int block, int rank);
+hlq_status hlq_lqs_accumulate(const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                              const float* x_scales, const void* w, int w_dtype,
+                              int64_t T, int64_t I, int64_t O, int block, int rank,
+                              double* stats, void* workspace, size_t workspace_bytes,
+                              void* stream);
+hlq_status hlq_lqs_select(const double* stats, double threshold, int* gx_mode,
+                          int* gw_mode);
+
 const char* hlq_status_string(int status);
 
 /* Library ABI version (major*100 + minor). */

@@ -134,3 +134,47 @@ def test_workspace_size_zero_for_invalid_shape():
     assert h.hlq_linear_backward_workspace_size(64, 40, 48, 24, 8) == 0
     with pytest.raises(h.HLQError):
         h.hlq_workspace_layout_query(64, 40, 40, 16, 8)
+
+
+# ---------------------------------------------- layer-wise quantizer selection
+
+def test_lqs_select_matches_oracle_rule():
+    import numpy as np
+    import oracle as o
+    rng = np.random.default_rng(3)
+    cases = [np.zeros(16)]
+    for _ in range(300):
+        st = rng.uniform(0, 1, 16) * (rng.uniform(0, 1, 16) < 0.9)
+        st[[2, 6, 10, 14]] = st[[1, 5, 9, 13]] * rng.choice([0.5, 1.0, 1.4, 1.5, 1.6, 3.0])
+        cases.append(st)
+    for st in cases:
+        for thr in (0.0, 0.5, 2.0):
+            assert h.hlq_lqs_select(st.tolist(), thr) == o.lqs_select(st, thr)
+
+
+def test_lqs_select_rejects_bad_threshold():
+    with pytest.raises(h.HLQError):
+        h.hlq_lqs_select([0.0] * 16, -0.1)
+    with pytest.raises(h.HLQError):
+        h.hlq_lqs_select([0.0] * 16, float("nan"))
+
+
+def test_lqs_workspace_size():
+    assert h.hlq_lqs_workspace_size(64, 40, 48, 16, 8) > 0
+    assert h.hlq_lqs_workspace_size(72, 40, 48, 16, 8) == 0    # T not a multiple of 16
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gy=None), 1), (dict(stats=None), 1), (dict(T=72), 2), (dict(block=24), 3),
+    (dict(rank=3), 4), (dict(gy_dt=2), 6), (dict(ws_bytes=16), 9), (dict(stats=(1 << 20) + 8), 7),
+])
+def test_lqs_accumulate_validates_before_launch(kw, status):
+    args = dict(gy=1 << 20, gy_dt=0, codes=1 << 20, scales=1 << 20, w=1 << 20, w_dt=0,
+                T=64, I=40, O=48, block=16, rank=8, stats=1 << 20, ws=1 << 20,
+                ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    lib = h.lib_handle()
+    got = lib.hlq_lqs_accumulate(*(args[k] for k in (
+        "gy", "gy_dt", "codes", "scales", "w", "w_dt", "T", "I", "O", "block", "rank",
+        "stats", "ws", "ws_bytes", "stream")))
+    assert got == status
