@@ -335,6 +335,11 @@ hlq_status hlq_lqs_accumulate(const void* g_y, int gy_dtype, const uint8_t* x_co
     return HLQ_ERR_DTYPE;
   hlq_status st = check_shape(T, I, O, block, rank);
   if (st != HLQ_OK) return st;
+  // the statistics kernels address every input with 32-bit byte offsets
+  const int64_t lim = (int64_t)1 << 32;
+  const int64_t gy_b = T * O * (gy_dtype == HLQ_F32 ? 4 : 2);
+  const int64_t w_b = O * I * (w_dtype == HLQ_F32 ? 4 : 2);
+  if (gy_b >= lim || w_b >= lim || T * I / 2 >= lim || T * 4 >= lim) return HLQ_ERR_OVERFLOW;
   const LqsLayout L = make_lqs_layout(T, I, O, block, rank);
   if (!workspace || workspace_bytes < L.total) return HLQ_ERR_WORKSPACE;
   if (!aligned16(g_y) || !aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w) ||

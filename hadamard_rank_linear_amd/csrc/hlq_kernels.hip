@@ -1489,11 +1489,6 @@ __global__ __launch_bounds__(256) void k_gemm_finalize(const int32_t* __restrict
 // walks LQS_STRIP consecutive blocks of its column (one group maximum per
 // strip).  Calibration work, not the backward's hot path: no tiling.
 
-__device__ __forceinline__ float ld_dt(const void* base, int dt, int64_t e) {
-  return dt == 0 ? static_cast<const float*>(base)[e]
-                 : bf16_to_f32(static_cast<const uint16_t*>(base)[e]);
-}
-
 template <int N>
 __device__ __forceinline__ void fwht_reg(float (&v)[N]) {
 #pragma unroll
@@ -1536,22 +1531,30 @@ __global__ __launch_bounds__(256) void k_lqs_zero(unsigned* __restrict__ p, int6
     p[i] = 0u;
 }
 
+// Element e of a uniform base pointer through a 32-bit byte offset (the host
+// keeps every input below 4 GiB): one VGPR per address, no 64-bit adds.
+__device__ __forceinline__ float ld_off(const void* base, int dt, uint32_t e) {
+  const char* b = static_cast<const char*>(base);
+  if (dt == 0) return *reinterpret_cast<const float*>(b + (e << 2));
+  return bf16_to_f32(*reinterpret_cast<const uint16_t*>(b + (e << 1)));
+}
+
 template <int N, int PASS>
 __global__ __launch_bounds__(256) void k_lqs(LqsArgs a) {
   __shared__ double red[3][256];
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
   const int op = (b >= a.wg0[1]) + (b >= a.wg0[2]) + (b >= a.wg0[3]);
-  const int64_t item = (b - a.wg0[op]) * 256 + tid;
-  const bool valid = item < a.items[op];
-  const int64_t T = a.T, I = a.I, O = a.O;
+  const uint32_t item = (uint32_t)((b - a.wg0[op]) * 256 + tid);
+  const bool valid = item < (uint32_t)a.items[op];
+  const uint32_t T = (uint32_t)a.T, I = (uint32_t)a.I, O = (uint32_t)a.O;
   const int step = op >= 2 ? N / a.r : 1;  // outputs k with k % step == 0 are kept
   const float qmax = op >= 2 ? 127.f : 7.f;
   // a column operand's thread walks LQS_STRIP consecutive blocks of its column
-  const int64_t ncol = op == 1 ? I : (op == 2 ? O : I);
-  const int64_t nblk = op == 1 ? O / N : T / N;
+  const uint32_t ncol = op == 2 ? O : I;
+  const uint32_t nblk = op == 1 ? O / N : T / N;
   int group = 0;
-  int64_t col = 0, blk0 = 0, blk1 = 0;
+  uint32_t col = 0, blk0 = 0, blk1 = 0;
   if (op == 0) {
     group = (int)(item / (O / N));
   } else {
@@ -1589,31 +1592,46 @@ __global__ __launch_bounds__(256) void k_lqs(LqsArgs a) {
   };
   if (valid) {
     if (op == 0) {
-      const int64_t e0 = (int64_t)group * O + item % (O / N) * N;
+      const uint32_t e0 = (uint32_t)group * O + item % (O / N) * N;
+      const char* base = static_cast<const char*>(a.gy);
 #pragma unroll
       for (int k = 0; k < N; k += 8) {
-        float u[8];
-        if (a.gy_dt == 0) load8<0>(a.gy, e0 + k, u); else load8<1>(a.gy, e0 + k, u);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[k + j] = u[j];
+        if (a.gy_dt == 0) {
+          const float4* p = reinterpret_cast<const float4*>(base + ((e0 + k) << 2));
+          const float4 x0 = p[0], x1 = p[1];
+          v[k] = x0.x; v[k + 1] = x0.y; v[k + 2] = x0.z; v[k + 3] = x0.w;
+          v[k + 4] = x1.x; v[k + 5] = x1.y; v[k + 6] = x1.z; v[k + 7] = x1.w;
+        } else {
+          const uint4 u = *reinterpret_cast<const uint4*>(base + ((e0 + k) << 1));
+          v[k] = bf16_to_f32(u.x & 0xFFFFu); v[k + 1] = bf16_to_f32(u.x >> 16);
+          v[k + 2] = bf16_to_f32(u.y & 0xFFFFu); v[k + 3] = bf16_to_f32(u.y >> 16);
+          v[k + 4] = bf16_to_f32(u.z & 0xFFFFu); v[k + 5] = bf16_to_f32(u.z >> 16);
+          v[k + 6] = bf16_to_f32(u.w & 0xFFFFu); v[k + 7] = bf16_to_f32(u.w >> 16);
+        }
       }
       consume();
     } else {
-      for (int64_t bb = blk0; bb < blk1; ++bb) {
+      // one block of loads in flight per thread (unrolling the strip would hold
+      // every block's addresses and values at once: fewer resident waves)
+#pragma unroll 1
+      for (uint32_t bb = blk0; bb < blk1; ++bb) {
         if (op == 1) {
 #pragma unroll
-          for (int k = 0; k < N; ++k) v[k] = ld_dt(a.w, a.w_dt, (bb * N + k) * I + col);
+          for (int k = 0; k < N; ++k) v[k] = ld_off(a.w, a.w_dt, (bb * N + k) * I + col);
         } else if (op == 2) {
 #pragma unroll
-          for (int k = 0; k < N; ++k) v[k] = ld_dt(a.gy, a.gy_dt, (bb * N + k) * O + col);
+          for (int k = 0; k < N; ++k) v[k] = ld_off(a.gy, a.gy_dt, (bb * N + k) * O + col);
         } else {
-          const int64_t half = I / 2;
+          const uint32_t half = I / 2;
+          const char* xc = reinterpret_cast<const char*>(a.xc);
+          const char* xs = reinterpret_cast<const char*>(a.xs);
 #pragma unroll
           for (int k = 0; k < N; ++k) {
-            const int64_t t = bb * N + k;
-            const unsigned byte = a.xc[t * half + col / 2];
+            const uint32_t t = bb * N + k;
+            const unsigned byte = *reinterpret_cast<const uint8_t*>(xc + (t * half + col / 2));
             const int code = (int)(((col & 1) ? byte >> 4 : byte) & 15u);
-            v[k] = a.xs[t] * (float)((code ^ 8) - 8);  // x = fl(s_x[t] * q)
+            const float sx = *reinterpret_cast<const float*>(xs + (t << 2));
+            v[k] = sx * (float)((code ^ 8) - 8);  // x = fl(s_x[t] * q)
           }
         }
         consume();
@@ -1646,43 +1664,49 @@ __global__ __launch_bounds__(256) void k_lqs(LqsArgs a) {
   }
 }
 
-// Tensor maxima: the largest group maximum of each operand.
-__global__ __launch_bounds__(256) void k_lqs_fold(LqsArgs a) {
-  __shared__ unsigned red[256];
+// Tensor maxima: the largest group maximum of each operand (one workgroup).
+__global__ __launch_bounds__(1024) void k_lqs_fold(LqsArgs a) {
+  __shared__ unsigned red[4][1024];
   const int tid = threadIdx.x;
   const int64_t base[5] = {0, a.T, a.T + a.I, a.T + a.I + a.O, a.T + 2 * a.I + a.O};
+#pragma unroll
   for (int op = 0; op < 4; ++op) {
     unsigned m = 0u;
-    for (int64_t g = base[op] + tid; g < base[op + 1]; g += 256) m = max(m, a.gmax[g]);
-    red[tid] = m;
-    __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
-      if (tid < h) red[tid] = max(red[tid], red[tid + h]);
-      __syncthreads();
-    }
-    if (tid == 0) a.tmax[op] = red[0];
+    for (int64_t g = base[op] + tid; g < base[op + 1]; g += 1024) m = max(m, a.gmax[g]);
+    red[op][tid] = m;
+  }
+  __syncthreads();
+  for (int h = 512; h > 0; h >>= 1) {
+    if (tid < h)
+#pragma unroll
+      for (int op = 0; op < 4; ++op) red[op][tid] = max(red[op][tid], red[op][tid + h]);
     __syncthreads();
   }
+  if (tid < 4) a.tmax[tid] = red[tid][0];
 }
 
 // Sum the per-workgroup partials in a fixed order and add them (and the
-// element counts) to the caller's statistics.
-__global__ __launch_bounds__(256) void k_lqs_final(LqsArgs a) {
-  __shared__ double red[256];
+// element counts) to the caller's statistics (one workgroup).
+__global__ __launch_bounds__(1024) void k_lqs_final(LqsArgs a) {
+  __shared__ double red[3][1024];
   const int tid = threadIdx.x;
-  for (int op = 0; op < 4; ++op)
-    for (int c = 0; c < 3; ++c) {
-      double acc = 0.0;
-      for (int64_t g = a.wg0[op] + tid; g < a.wg0[op + 1]; g += 256) acc += a.part[g * 3 + c];
-      red[tid] = acc;
-      __syncthreads();
-      for (int h = 128; h > 0; h >>= 1) {
-        if (tid < h) red[tid] += red[tid + h];
-        __syncthreads();
-      }
-      if (tid == 0) a.stats[4 * op + c] += red[0];
+  for (int op = 0; op < 4; ++op) {
+    double acc[3] = {0.0, 0.0, 0.0};
+    for (int64_t g = a.wg0[op] + tid; g < a.wg0[op + 1]; g += 1024)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) acc[c] += a.part[g * 3 + c];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) red[c][tid] = acc[c];
+    __syncthreads();
+    for (int h = 512; h > 0; h >>= 1) {
+      if (tid < h)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) red[c][tid] += red[c][tid + h];
       __syncthreads();
     }
+    if (tid < 3) a.stats[4 * op + tid] += red[tid][0];
+    __syncthreads();
+  }
   if (tid < 4) a.stats[4 * tid + 3] += a.count[tid];
 }
 
@@ -1896,14 +1920,14 @@ hipError_t launch_lqs(const LqsArgs& a, int n, hipStream_t s) {
     case 128: hipLaunchKernelGGL((k_lqs<128, 0>), g, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(k_lqs_fold, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_lqs_fold, dim3(1), dim3(1024), 0, s, a);
   switch (n) {
     case 16: hipLaunchKernelGGL((k_lqs<16, 1>), g, dim3(256), 0, s, a); break;
     case 32: hipLaunchKernelGGL((k_lqs<32, 1>), g, dim3(256), 0, s, a); break;
     case 64: hipLaunchKernelGGL((k_lqs<64, 1>), g, dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL((k_lqs<128, 1>), g, dim3(256), 0, s, a); break;
   }
-  hipLaunchKernelGGL(k_lqs_final, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_lqs_final, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -216,7 +216,8 @@ hlq_status hlq_gemm_gw_acc(const void* workspace, int64_t T, int64_t I, int64_t 
  * call is reproducible).  Five launches on `stream`; the workspace (at least
  * hlq_lqs_workspace_size bytes) holds group maxima and partial sums.  Shape
  * rules and errors as for hlq_linear_backward; `stats` must be 16-byte
- * aligned.
+ * aligned; HLQ_ERR_OVERFLOW also when g_y, w or the ACBP codes hold 4 GiB or
+ * more (the statistics kernels use 32-bit byte offsets).
  *
  * hlq_lqs_select is a host function on a HOST copy of the 16 statistics.
  * A path's error in a mode is the sum over its two operands of
