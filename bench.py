@@ -266,6 +266,60 @@ def time_lqs(cfg, inp, reps=10):
                                "gw": "per_token" if modes[1] == 0 else "per_tensor"}}
 
 
+def time_torch_bf16_backward(cfg, inp, steps=20, warmup=5):
+    """Context, not this library: the plain bf16 backward of the same layer in
+    torch (g_x = g_y . w and g_w = g_y^T . x, two 2-D matmuls on hipBLASLt),
+    µs per layer on rotating operand copies.  The transposed operand is the
+    left one of a 2-D product."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+
+    def dev_t(a):
+        if cfg.dtype == 1:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev).to(torch.bfloat16)
+
+    gy0, x0, w0 = dev_t(inp["gy"]), dev_t(inp["x"]), dev_t(inp["w"])
+    per_set = (gy0.numel() + x0.numel() + w0.numel() + cfg.T * cfg.I + cfg.O * cfg.I) * 2
+    n = max(2, -(-2 * LLC_BYTES // per_set))
+    sets = [(gy0.clone(), x0.clone(), w0.clone(),
+             torch.empty((cfg.T, cfg.I), dtype=torch.bfloat16, device=dev),
+             torch.empty((cfg.O, cfg.I), dtype=torch.bfloat16, device=dev)) for _ in range(n)]
+
+    def step(i):
+        gy, x, w, gx, gw = sets[i % n]
+        torch.mm(gy, w, out=gx)
+        torch.mm(gy.t(), x, out=gw)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    return round((time.perf_counter() - t0) / steps * 1e6, 2)
+
+
+def per_config_side(steps, warmup):
+    """Every other layer config at full size: µs per backward, effective TOPS
+    and the per-launch event times (no roofline object: the bench line's
+    roofline is the headline layer's)."""
+    from hadamard_rank_linear_amd import workloads as wl
+    out = {}
+    for cfg in wl.CONFIGS:
+        if cfg.name in ("vitb_qkv", "vitb_fc2"):
+            continue
+        log(f"side measurement: {cfg.name}")
+        r = time_layer(cfg, wl.make_inputs(cfg), steps, warmup)
+        us = r["wall_ms_per_step"] * 1e3
+        ops = 2 * cfg.T * cfg.I * cfg.O + 2 * cfg.Tl * cfg.O * cfg.I
+        out[cfg.name] = {"us": round(us, 2), "effective_tops": round(ops / (us * 1e-6) / 1e12, 1),
+                         "kernels_us": {k: round(v, 2) for k, v in r["kernels_us"].items()}}
+    return out
+
+
 def cpu_baseline(cfg, inp):
     import numpy as np
     import oracle as o
@@ -349,6 +403,10 @@ def main():
         r2 = time_layer(c2, wl.make_inputs(c2), max(10, args.steps // 2), args.warmup,
                         per_kernel=False)
         extra["vitb_fc2_us"] = round(r2["wall_ms_per_step"] * 1e3, 2)
+    if not args.no_extra:
+        extra["per_config"] = per_config_side(max(10, args.steps // 2), args.warmup)
+        log("context: torch bf16 backward of the same layer")
+        extra["context_torch_bf16_backward_us"] = time_torch_bf16_backward(cfg, inp)
 
     if args.copy_calib:
         copy_calibration()
