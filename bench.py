@@ -228,9 +228,11 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
 
 def time_lqs(cfg, inp, reps=10):
     """Layer-wise quantizer selection statistics of one calibration batch
-    (hlq_lqs_accumulate: five launches) on the layer's inputs, and the modes
-    the 50% rule picks from them.  Algorithmic bytes: both passes read g_y
-    twice (rows along O, columns along T), w once and the ACBP codes once."""
+    (hlq_lqs_accumulate: the backward's MAX and reduce launches, an error
+    pass, a fold) on the layer's inputs, and the modes the 50% rule picks from
+    them.  Algorithmic bytes: the MAX launch reads g_y, w and the ACBP codes
+    once; the error pass reads g_y twice (rows along O, columns along T), w
+    and the codes once."""
     import numpy as np
     import torch
     import hadamard_rank_linear_amd as h
@@ -259,7 +261,8 @@ def time_lqs(cfg, inp, reps=10):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / reps * 1e3
     e = 2 if bf else 4
-    nbytes = 2 * (2 * cfg.T * cfg.O * e + cfg.O * cfg.I * e + cfg.T * cfg.I // 2 + 4 * cfg.T)
+    once = cfg.O * cfg.I * e + cfg.T * cfg.I // 2 + 4 * cfg.T
+    nbytes = (cfg.T * cfg.O * e + once) + (2 * cfg.T * cfg.O * e + once)
     return {"us": round(us, 2), "algorithmic_bytes": nbytes,
             "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "selected_modes": {"gx": "per_token" if modes[0] == 0 else "per_tensor",

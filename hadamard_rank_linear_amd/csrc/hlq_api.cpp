@@ -109,10 +109,10 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   return L;
 }
 
-// Workspace of hlq_lqs_accumulate: group maxima, tensor maxima, per-workgroup
-// partial sums.
+// Workspace of hlq_lqs_accumulate: the backward's (its MAX and reduce
+// launches run on it) followed by the per-workgroup partial sums.
 struct LqsLayout {
-  size_t gmax, tmax, part, total;
+  size_t part, total;
   int64_t items[4], wg0[5];
   double count[4];
 };
@@ -131,17 +131,46 @@ LqsLayout make_lqs_layout(int64_t T, int64_t I, int64_t O, int block, int rank) 
   L.count[3] = (double)(T / n * rank * I);
   L.wg0[0] = 0;
   for (int k = 0; k < 4; ++k) L.wg0[k + 1] = L.wg0[k] + (L.items[k] + 255) / 256;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t at = off;
-    off = align256(off + bytes);
-    return at;
-  };
-  L.gmax = take((size_t)(T + 2 * I + O) * 4);
-  L.tmax = take(4 * 4);
-  L.part = take((size_t)L.wg0[4] * 3 * 8);
-  L.total = off;
+  L.part = align256(make_layout(T, I, O, block, rank).pub.total);
+  L.total = align256(L.part + (size_t)L.wg0[4] * 3 * 8);
   return L;
+}
+
+// Arguments of the transform launches (MAX, reduce, QUANT) over the
+// backward's workspace layout.
+hlq::TrArgs make_tr_args(const Layout& L, const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                         const float* x_scales, const void* w, int w_dtype, int64_t T,
+                         int64_t I, int64_t O, int block, bool gx_tok, bool gw_tok,
+                         uint8_t* ws) {
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  hlq::TrArgs a;
+  a.gy = g_y; a.gy_dt = gy_dtype;
+  a.xc = x_codes; a.xs = x_scales;
+  a.w = w; a.w_dt = w_dtype;
+  a.T = T; a.I = I; a.O = O;
+  a.kxb = L.pub.kx_pitch; a.kwb = L.pub.kw_pitch; a.tl = L.pub.t_low;
+  a.gx_tok = gx_tok; a.gw_tok = gw_tok;
+  a.q_gy = ws + L.pub.q_gy; a.q_w = ws + L.pub.q_w;
+  a.q_gyl = ws + L.pub.q_gyl; a.q_xl = ws + L.pub.q_xl;
+  a.s_gy = f32(L.pub.s_gy); a.s_w = f32(L.pub.s_w);
+  a.s_gyl = f32(L.pub.s_gyl); a.s_xl = f32(L.pub.s_xl);
+  a.part_gy = f32(L.part_gy); a.part_gyl = f32(L.part_gyl);
+  a.part_xl = f32(L.part_xl); a.part_w = f32(L.part_w);
+  a.inv_gy = f32(L.inv_gy); a.inv_gyl = f32(L.inv_gyl);
+  a.inv_xl = f32(L.inv_xl); a.inv_w = f32(L.inv_w);
+  a.tmax = reinterpret_cast<unsigned*>(ws + L.tmax);
+  a.nred = L.nred;
+  a.nch_o = L.nch_o; a.nch_i = L.nch_i; a.ntr_t = L.ntr_t; a.ntr_o = L.ntr_o;
+  // bf16 g_y with n <= 64 runs the register-resident kernel (64-token tiles;
+  // part_gyl is sized for them)
+  a.gy_reg = (gy_dtype == HLQ_BF16 && block <= 64) ? 1 : 0;
+  a.ntr_gy = a.gy_reg ? (T + hlq::TR_GY_REG_ROWS - 1) / hlq::TR_GY_REG_ROWS : L.ntr_t;
+  a.wg_gy = a.ntr_gy * L.nch_o;
+  a.gy_workers = 0;  // both chosen per pass by launch_tr
+  a.gyreg_wgs = 0;
+  a.wg_x = L.ntr_t * L.nch_i;
+  a.wg_w = L.ntr_o * L.nch_i;
+  return a;
 }
 
 #define HLQ_TRY(expr)                       \
@@ -223,37 +252,10 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const bool gx_tok = gx_mode == HLQ_PER_TOKEN;
   const bool gw_tok = gw_mode == HLQ_PER_TOKEN;
-
-  hlq::TrArgs a;
-  a.gy = g_y; a.gy_dt = gy_dtype;
-  a.xc = x_codes; a.xs = x_scales;
-  a.w = w; a.w_dt = w_dtype;
-  a.T = T; a.I = I; a.O = O;
-  a.kxb = L.pub.kx_pitch; a.kwb = L.pub.kw_pitch; a.tl = L.pub.t_low;
-  a.gx_tok = gx_tok; a.gw_tok = gw_tok;
-  a.q_gy = ws + L.pub.q_gy; a.q_w = ws + L.pub.q_w;
-  a.q_gyl = ws + L.pub.q_gyl; a.q_xl = ws + L.pub.q_xl;
-  a.s_gy = f32(L.pub.s_gy); a.s_w = f32(L.pub.s_w);
-  a.s_gyl = f32(L.pub.s_gyl); a.s_xl = f32(L.pub.s_xl);
-  a.part_gy = f32(L.part_gy); a.part_gyl = f32(L.part_gyl);
-  a.part_xl = f32(L.part_xl); a.part_w = f32(L.part_w);
-  a.inv_gy = f32(L.inv_gy); a.inv_gyl = f32(L.inv_gyl);
-  a.inv_xl = f32(L.inv_xl); a.inv_w = f32(L.inv_w);
-  a.tmax = reinterpret_cast<unsigned*>(ws + L.tmax);
-  a.nred = L.nred;
-  a.nch_o = L.nch_o; a.nch_i = L.nch_i; a.ntr_t = L.ntr_t; a.ntr_o = L.ntr_o;
-  // bf16 g_y with n <= 64 runs the register-resident kernel (64-token tiles;
-  // part_gyl is sized for them)
-  a.gy_reg = (gy_dtype == HLQ_BF16 && block <= 64) ? 1 : 0;
-  a.ntr_gy = a.gy_reg ? (T + hlq::TR_GY_REG_ROWS - 1) / hlq::TR_GY_REG_ROWS : L.ntr_t;
-  a.wg_gy = a.ntr_gy * L.nch_o;
-  a.gy_workers = 0;  // both chosen per pass by launch_tr
-  a.gyreg_wgs = 0;
-  a.wg_x = L.ntr_t * L.nch_i;
-  a.wg_w = L.ntr_o * L.nch_i;
+  const hlq::TrArgs a = make_tr_args(L, g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O,
+                                     block, gx_tok, gw_tok, ws);
   int32_t* partial = reinterpret_cast<int32_t*>(ws + L.partial);
   auto on = [&](int step) { return (step_mask >> step) & 1u; };
 
@@ -345,15 +347,26 @@ hlq_status hlq_lqs_accumulate(const void* g_y, int gy_dtype, const uint8_t* x_co
   if (!aligned16(g_y) || !aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w) ||
       !aligned16(stats) || !aligned16(workspace))
     return HLQ_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  // group maxima, per-token scales and tensor maxima: the backward's MAX and
+  // reduce launches with both paths per token
+  const Layout B = make_layout(T, I, O, block, rank);
+  const hlq::TrArgs t = make_tr_args(B, g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O,
+                                     block, true, true, ws);
+  HLQ_TRY(hlq::launch_tr(t, hlq::PASS_MAX, block, rank, s));
+  HLQ_TRY(hlq::launch_tr_reduce(t, s));
   hlq::LqsArgs a;
   memset(&a, 0, sizeof(a));
   a.gy = g_y; a.gy_dt = gy_dtype;
   a.xc = x_codes; a.xs = x_scales;
   a.w = w; a.w_dt = w_dtype;
   a.T = T; a.I = I; a.O = O; a.r = rank;
-  a.gmax = reinterpret_cast<unsigned*>(ws + L.gmax);
-  a.tmax = reinterpret_cast<unsigned*>(ws + L.tmax);
+  a.tok_inv[0] = t.inv_gy; a.tok_s[0] = t.s_gy;
+  a.tok_inv[1] = t.inv_w; a.tok_s[1] = t.s_w;
+  a.tok_inv[2] = t.inv_gyl; a.tok_s[2] = t.s_gyl;
+  a.tok_inv[3] = t.inv_xl; a.tok_s[3] = t.s_xl;
+  a.tmax = t.tmax;
   a.part = reinterpret_cast<double*>(ws + L.part);
   a.stats = stats;
   for (int k = 0; k < 4; ++k) {
@@ -361,7 +374,7 @@ hlq_status hlq_lqs_accumulate(const void* g_y, int gy_dtype, const uint8_t* x_co
     a.count[k] = L.count[k];
   }
   for (int k = 0; k < 5; ++k) a.wg0[k] = L.wg0[k];
-  HLQ_TRY(hlq::launch_lqs(a, block, static_cast<hipStream_t>(stream)));
+  HLQ_TRY(hlq::launch_lqs(a, block, s));
   return HLQ_OK;
 }
 

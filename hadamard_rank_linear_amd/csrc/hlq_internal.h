@@ -61,7 +61,9 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes);
 
-// Layer-wise quantizer selection statistics (one calibration batch).
+// Layer-wise quantizer selection statistics (one calibration batch).  The
+// per-token scales and the tensor maxima come from the backward's MAX and
+// reduce launches run with both paths per token.
 constexpr int LQS_STRIP = 4;  // blocks per thread along a column operand
 struct LqsArgs {
   const void* gy; int gy_dt;
@@ -69,18 +71,20 @@ struct LqsArgs {
   const void* w; int w_dt;
   int64_t T, I, O;
   int r;
-  unsigned* gmax;     // group maxima as float bits: [T] H.g_y, [I] H.w,
-                      // [O] low-rank g_y, [I] low-rank x
-  unsigned* tmax;     // [4] tensor maxima (float bits)
-  double* part;       // [wg0[4]][3] per-workgroup sums of v^2, e_tok^2, e_ten^2
-  double* stats;      // [16] the caller's accumulated statistics
-  int64_t items[4];   // threads per operand: a row block (op 0) or a strip of
-                      // LQS_STRIP column blocks (ops 1-3)
-  int64_t wg0[5];     // first workgroup of each operand; wg0[4] = total
-  double count[4];    // elements per operand (items x n, or x r when low-rank)
+  // per operand (0 H.g_y, 1 H.w, 2 low-rank g_y, 3 low-rank x): per-token
+  // reciprocal scales and scales, [T], [I], [O], [I]
+  const float* tok_inv[4];
+  const float* tok_s[4];
+  const unsigned* tmax;  // [4] tensor maxima (float bits)
+  double* part;          // [wg0[4]][3] per-workgroup sums of v^2, e_tok^2, e_ten^2
+  double* stats;         // [16] the caller's accumulated statistics
+  int64_t items[4];      // threads per operand: a row block (op 0) or a strip of
+                         // LQS_STRIP column blocks (ops 1-3)
+  int64_t wg0[5];        // first workgroup of each operand; wg0[4] = total
+  double count[4];       // elements per operand
 };
 
-// Zero the group maxima, MAX pass, tensor maxima, ERR pass, final fold.
+// ERR pass and the final fold (after launch_tr MAX and launch_tr_reduce).
 hipError_t launch_lqs(const LqsArgs& a, int n, hipStream_t s);
 
 hipError_t launch_acbp(const void* x, int dtype, int64_t T, int64_t I, uint8_t* codes,

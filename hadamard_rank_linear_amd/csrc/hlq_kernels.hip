@@ -1496,17 +1496,18 @@ __global__ __launch_bounds__(256) void k_gemm_finalize(const int32_t* __restrict
 // per-tensor chosen per layer from calibration data with a 50% MSE-difference
 // threshold).  For each of the four operands the backward quantizes, the
 // squared reconstruction error under per-token and under per-tensor scales,
-// with sum(v^2) and the element count.  Two passes over the inputs: group
-// maxima (MAX), then errors (ERR) once every scale is known.  One thread
-// transforms one block of n values of one operand:
+// with sum(v^2) and the element count.  The group maxima, per-token scales,
+// reciprocal scales and tensor maxima come from the backward's own MAX and
+// reduce launches (both paths per token); this ERR pass then recomputes the
+// transformed values.  One thread transforms one block of n values:
 //   op 0  H.g_y          row t, block beta along O      group: token t
 //   op 1  H.w            column i, block beta along O   group: input channel i
 //   op 2  low-rank g_y   column o, token block b        group: channel o
 //   op 3  low-rank x     column i, token block b        group: channel i
 // with the fp32 butterfly network of the backward (ascending stages); the
 // low-rank operands keep outputs j * (n / r).  A thread of a column operand
-// walks LQS_STRIP consecutive blocks of its column (one group maximum per
-// strip).  Calibration work, not the backward's hot path: no tiling.
+// walks LQS_STRIP consecutive blocks of its column.  Calibration work, not the
+// backward's hot path: no tiling.
 
 template <int N>
 __device__ __forceinline__ void fwht_reg(float (&v)[N]) {
@@ -1521,33 +1522,17 @@ __device__ __forceinline__ void fwht_reg(float (&v)[N]) {
       }
 }
 
-// Quantizer of a group whose largest magnitude is a: s = fl(a / qmax),
-// inv = fl(qmax / a); codes are 0 when a is 0 or qmax / a overflows.
+// Quantizer of a group: scale s and reciprocal scale inv (0 for a group whose
+// codes are all 0: a zero group, or qmax / a overflowing).
 struct LqsQuant {
   float inv, s, qmax;
-  bool on;
 };
 
-__device__ __forceinline__ LqsQuant lqs_quant(float a, float qmax) {
-  LqsQuant z{0.f, 0.f, qmax, false};
-  if (a != 0.f) {
-    z.inv = qmax / a;
-    z.s = a / qmax;
-    z.on = !__builtin_isinf(z.inv);
-  }
-  return z;
-}
-
-// fl(v - fl(s * q)): reconstruction error of v under quantizer z.
+// fl(v - fl(s * q)) with q = clamp(rne(fl(v * inv)), +-qmax).
 __device__ __forceinline__ float lqs_err(float v, const LqsQuant& z) {
-  const float q = z.on ? fminf(fmaxf(rintf(v * z.inv), -z.qmax), z.qmax) : 0.f;
+  const float q = fminf(fmaxf(rintf(v * z.inv), -z.qmax), z.qmax);
   const float d = z.s * q;
   return v - d;
-}
-
-__global__ __launch_bounds__(256) void k_lqs_zero(unsigned* __restrict__ p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    p[i] = 0u;
 }
 
 // Element e of a uniform base pointer through a 32-bit byte offset (the host
@@ -1558,7 +1543,7 @@ __device__ __forceinline__ float ld_off(const void* base, int dt, uint32_t e) {
   return bf16_to_f32(*reinterpret_cast<const uint16_t*>(b + (e << 1)));
 }
 
-template <int N, int PASS>
+template <int N>
 __global__ __launch_bounds__(256) void k_lqs(LqsArgs a) {
   __shared__ double red[3][256];
   const int tid = threadIdx.x;
@@ -1572,25 +1557,24 @@ __global__ __launch_bounds__(256) void k_lqs(LqsArgs a) {
   // a column operand's thread walks LQS_STRIP consecutive blocks of its column
   const uint32_t ncol = op == 2 ? O : I;
   const uint32_t nblk = op == 1 ? O / N : T / N;
-  int group = 0;
-  uint32_t col = 0, blk0 = 0, blk1 = 0;
+  uint32_t group = 0, col = 0, blk0 = 0, blk1 = 0;
   if (op == 0) {
-    group = (int)(item / (O / N));
+    group = item / (O / N);
   } else {
     col = item % ncol;
     blk0 = item / ncol * LQS_STRIP;
     blk1 = blk0 + LQS_STRIP < nblk ? blk0 + LQS_STRIP : nblk;
-    group = (int)((op == 1 ? T : (op == 2 ? T + I : T + I + O)) + col);
+    group = col;
   }
-  // the thread's group is fixed: both quantizers are computed once
-  LqsQuant zt{0.f, 0.f, qmax, false}, zT{0.f, 0.f, qmax, false};
-  if constexpr (PASS == 1) {
-    if (valid) {
-      zt = lqs_quant(__uint_as_float(a.gmax[group]), qmax);
-      zT = lqs_quant(__uint_as_float(a.tmax[op]), qmax);
-    }
+  // the thread's group is fixed: both quantizers are read / computed once
+  LqsQuant zt{0.f, 0.f, qmax}, zT{0.f, 0.f, qmax};
+  if (valid) {
+    zt.inv = a.tok_inv[op][group];
+    zt.s = a.tok_s[op][group];
+    const float at = __uint_as_float(a.tmax[op]);
+    zT.inv = inv_of(at, qmax);
+    zT.s = scale_of(at, qmax);
   }
-  float m = 0.f;
   double ss = 0.0, e_tok = 0.0, e_ten = 0.0;
   float v[N];
   auto consume = [&]() {
@@ -1599,19 +1583,15 @@ __global__ __launch_bounds__(256) void k_lqs(LqsArgs a) {
     for (int k = 0; k < N; ++k)
       if ((k & (step - 1)) == 0) {
         const float x = v[k];
-        if constexpr (PASS == 0) {
-          m = fmaxf(m, fabsf(x));
-        } else {
-          const float d1 = lqs_err(x, zt), d2 = lqs_err(x, zT);
-          ss += (double)x * (double)x;
-          e_tok += (double)d1 * (double)d1;
-          e_ten += (double)d2 * (double)d2;
-        }
+        const float d1 = lqs_err(x, zt), d2 = lqs_err(x, zT);
+        ss += (double)x * (double)x;
+        e_tok += (double)d1 * (double)d1;
+        e_ten += (double)d2 * (double)d2;
       }
   };
   if (valid) {
     if (op == 0) {
-      const uint32_t e0 = (uint32_t)group * O + item % (O / N) * N;
+      const uint32_t e0 = group * O + item % (O / N) * N;
       const char* base = static_cast<const char*>(a.gy);
 #pragma unroll
       for (int k = 0; k < N; k += 8) {
@@ -1657,16 +1637,7 @@ __global__ __launch_bounds__(256) void k_lqs(LqsArgs a) {
       }
     }
   }
-  if constexpr (PASS == 0) {
-    // consecutive blocks of one row share a group: one atomic per wave then
-    const int g0 = __shfl(group, 0);
-    if (__all(valid && group == g0)) {
-      m = wave_max(m);
-      if ((tid & 63) == 0) atomicMax(&a.gmax[g0], __float_as_uint(m));
-    } else if (valid) {
-      atomicMax(&a.gmax[group], __float_as_uint(m));
-    }
-  } else {
+  {
     red[0][tid] = ss;
     red[1][tid] = e_tok;
     red[2][tid] = e_ten;
@@ -1681,27 +1652,6 @@ __global__ __launch_bounds__(256) void k_lqs(LqsArgs a) {
     }
     if (tid < 3) a.part[b * 3 + tid] = red[tid][0];
   }
-}
-
-// Tensor maxima: the largest group maximum of each operand (one workgroup).
-__global__ __launch_bounds__(1024) void k_lqs_fold(LqsArgs a) {
-  __shared__ unsigned red[4][1024];
-  const int tid = threadIdx.x;
-  const int64_t base[5] = {0, a.T, a.T + a.I, a.T + a.I + a.O, a.T + 2 * a.I + a.O};
-#pragma unroll
-  for (int op = 0; op < 4; ++op) {
-    unsigned m = 0u;
-    for (int64_t g = base[op] + tid; g < base[op + 1]; g += 1024) m = max(m, a.gmax[g]);
-    red[op][tid] = m;
-  }
-  __syncthreads();
-  for (int h = 512; h > 0; h >>= 1) {
-    if (tid < h)
-#pragma unroll
-      for (int op = 0; op < 4; ++op) red[op][tid] = max(red[op][tid], red[op][tid + h]);
-    __syncthreads();
-  }
-  if (tid < 4) a.tmax[tid] = red[tid][0];
 }
 
 // Sum the per-workgroup partials in a fixed order and add them (and the
@@ -1928,23 +1878,13 @@ hipError_t launch_gemm_finalize(const int32_t* partial, int splits, int64_t M,
 
 
 hipError_t launch_lqs(const LqsArgs& a, int n, hipStream_t s) {
-  const int64_t groups = a.T + 2 * a.I + a.O;
-  const unsigned zb = (unsigned)(cdiv(groups, 256) < 1024 ? cdiv(groups, 256) : 1024);
-  hipLaunchKernelGGL(k_lqs_zero, dim3(zb), dim3(256), 0, s, a.gmax, groups);
   const dim3 g((unsigned)a.wg0[4]);
   switch (n) {
-    case 16: hipLaunchKernelGGL((k_lqs<16, 0>), g, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_lqs<32, 0>), g, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_lqs<64, 0>), g, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_lqs<128, 0>), g, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_lqs<16>), g, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_lqs<32>), g, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_lqs<64>), g, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((k_lqs<128>), g, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
-  }
-  hipLaunchKernelGGL(k_lqs_fold, dim3(1), dim3(1024), 0, s, a);
-  switch (n) {
-    case 16: hipLaunchKernelGGL((k_lqs<16, 1>), g, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_lqs<32, 1>), g, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_lqs<64, 1>), g, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_lqs<128, 1>), g, dim3(256), 0, s, a); break;
   }
   hipLaunchKernelGGL(k_lqs_final, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
