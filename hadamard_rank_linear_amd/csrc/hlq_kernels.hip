@@ -137,7 +137,11 @@ __device__ __forceinline__ float scale_of(float a, float qmax) { return a == 0.f
 // ------------------------------------------------------------ ACBP pack
 // One wave per token row: absmax over the row, then INT4 codes (qmax 7).
 
-template <int DT>
+// One wave per token row.  RC > 0: the row (at most RC * 512 elements) stays
+// in registers between the maximum and the codes, all of its loads issued
+// before the reduction (qkv rows: 8.9 -> 8.0 us; two rows per wave measured no
+// better); RC == 0: longer rows are read twice (the second time from cache).
+template <int DT, int RC>
 __global__ __launch_bounds__(256) void k_acbp(const void* __restrict__ x, int64_t T,
                                               int64_t I, uint8_t* __restrict__ codes,
                                               float* __restrict__ scales) {
@@ -145,20 +149,43 @@ __global__ __launch_bounds__(256) void k_acbp(const void* __restrict__ x, int64_
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
   const int64_t base = row * I;
-  float a = 0.f;
-  for (int64_t c = lane * 8; c < I; c += 512) {
-    float v[8];
-    load8<DT>(x, base + c, v);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(v[k]));
-  }
-  a = wave_max(a);
-  const float inv = inv_of(a, 7.f);
   uint8_t* out = codes + row * (I / 2);
-  for (int64_t c = lane * 8; c < I; c += 512) {
-    float v[8];
-    load8<DT>(x, base + c, v);
-    *reinterpret_cast<uint32_t*>(out + c / 2) = quant_pack8_int4(v, inv);
+  float a = 0.f;
+  if constexpr (RC > 0) {
+    float v[RC][8];
+#pragma unroll
+    for (int j = 0; j < RC; ++j) {
+      const int64_t c = lane * 8 + j * 512;
+      if (c < I) load8<DT>(x, base + c, v[j]);
+      else
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[j][k] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < RC; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(v[j][k]));
+    a = wave_max(a);
+    const float inv = inv_of(a, 7.f);
+#pragma unroll
+    for (int j = 0; j < RC; ++j) {
+      const int64_t c = lane * 8 + j * 512;
+      if (c < I) *reinterpret_cast<uint32_t*>(out + c / 2) = quant_pack8_int4(v[j], inv);
+    }
+  } else {
+    for (int64_t c = lane * 8; c < I; c += 512) {
+      float v[8];
+      load8<DT>(x, base + c, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(v[k]));
+    }
+    a = wave_max(a);
+    const float inv = inv_of(a, 7.f);
+    for (int64_t c = lane * 8; c < I; c += 512) {
+      float v[8];
+      load8<DT>(x, base + c, v);
+      *reinterpret_cast<uint32_t*>(out + c / 2) = quant_pack8_int4(v, inv);
+    }
   }
   if (lane == 0) scales[row] = scale_of(a, 7.f);
 }
@@ -1686,8 +1713,14 @@ static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1
 hipError_t launch_acbp(const void* x, int dtype, int64_t T, int64_t I, uint8_t* codes,
                        float* scales, hipStream_t s) {
   dim3 grid(cdiv(T, 4)), block(256);
-  if (dtype == 0) hipLaunchKernelGGL(k_acbp<0>, grid, block, 0, s, x, T, I, codes, scales);
-  else hipLaunchKernelGGL(k_acbp<1>, grid, block, 0, s, x, T, I, codes, scales);
+#define HLQ_ACBP(RC)                                                                    \
+  if (dtype == 0) hipLaunchKernelGGL((k_acbp<0, RC>), grid, block, 0, s, x, T, I, codes, scales); \
+  else hipLaunchKernelGGL((k_acbp<1, RC>), grid, block, 0, s, x, T, I, codes, scales)
+  if (I <= 512) { HLQ_ACBP(1); }
+  else if (I <= 1024) { HLQ_ACBP(2); }
+  else if (I <= 2048) { HLQ_ACBP(4); }
+  else { HLQ_ACBP(0); }
+#undef HLQ_ACBP
   return hipGetLastError();
 }
 

@@ -156,3 +156,20 @@ def test_invalid_arguments_enqueue_nothing():
         h.hlq_linear_backward(gy, codes, sc, w, 16, 8, g_x=gx, g_w=gw, workspace=small)
     torch.cuda.synchronize()
     assert (gx == 7.0).all() and (gw == 7.0).all()
+
+
+@pytest.mark.parametrize("I", [8, 520, 1032, 2048, 2056, 3080])
+@pytest.mark.parametrize("dt", [wl.F32, wl.BF16])
+def test_gpu_acbp_row_widths(I, dt):
+    # every row length class of the ACBP kernel (rows kept in registers in
+    # one, two or four 512-element chunks, ragged last chunk, rows read twice)
+    import dataclasses
+    import hadamard_rank_linear_amd as h
+    from parity_util import host_f32, to_device
+    cfg = dataclasses.replace(wl.CONFIGS[1], T=48, I=I, dtype=dt, index=90 + I % 7)
+    _say(f"acbp I={I} dtype={dt}")
+    inp = wl.make_inputs(cfg, plant_zero_rows=True)
+    codes, scales = h.hlq_compress_act(to_device(inp["x"], dt))
+    oc, os_ = o.acbp_pack(host_f32(inp["x"], dt))
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), os_.view(np.uint32))
