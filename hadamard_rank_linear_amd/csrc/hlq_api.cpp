@@ -121,16 +121,19 @@ LqsLayout make_lqs_layout(int64_t T, int64_t I, int64_t O, int block, int rank) 
   LqsLayout L;
   memset(&L, 0, sizeof(L));
   const int64_t n = block, S = hlq::LQS_STRIP;
+  // op 0: one thread per row block, 256-thread workgroups; ops 1-3: one
+  // 64-column x LQS_STRIP-block tile per single-wave workgroup
   L.items[0] = T * (O / n);
-  L.items[1] = (O / n + S - 1) / S * I;
-  L.items[2] = (T / n + S - 1) / S * O;
-  L.items[3] = (T / n + S - 1) / S * I;
+  L.items[1] = (I + 63) / 64 * ((O / n + S - 1) / S);
+  L.items[2] = (O + 63) / 64 * ((T / n + S - 1) / S);
+  L.items[3] = (I + 63) / 64 * ((T / n + S - 1) / S);
   L.count[0] = (double)(T * O);
   L.count[1] = (double)(O * I);
   L.count[2] = (double)(T / n * rank * O);
   L.count[3] = (double)(T / n * rank * I);
   L.wg0[0] = 0;
-  for (int k = 0; k < 4; ++k) L.wg0[k + 1] = L.wg0[k] + (L.items[k] + 255) / 256;
+  L.wg0[1] = (L.items[0] + 255) / 256;
+  for (int k = 1; k < 4; ++k) L.wg0[k + 1] = L.wg0[k] + L.items[k];
   L.part = align256(make_layout(T, I, O, block, rank).pub.total);
   L.total = align256(L.part + (size_t)L.wg0[4] * 3 * 8);
   return L;

@@ -78,9 +78,10 @@ struct LqsArgs {
   const unsigned* tmax;  // [4] tensor maxima (float bits)
   double* part;          // [wg0[4]][3] per-workgroup sums of v^2, e_tok^2, e_ten^2
   double* stats;         // [16] the caller's accumulated statistics
-  int64_t items[4];      // threads per operand: a row block (op 0) or a strip of
-                         // LQS_STRIP column blocks (ops 1-3)
-  int64_t wg0[5];        // first workgroup of each operand; wg0[4] = total
+  int64_t items[4];      // op 0: threads (one row block each); ops 1-3: tiles of
+                         // 64 columns x LQS_STRIP blocks (one wave each)
+  int64_t wg0[5];        // first partial-sum slot of each operand (op 0: one per
+                         // 256-thread workgroup, ops 1-3: one per tile); wg0[4] = total
   double count[4];       // elements per operand
 };
 

@@ -213,9 +213,10 @@ hlq_status hlq_gemm_gw_acc(const void* workspace, int64_t T, int64_t I, int64_t 
  *   stats[4k+3] += number of elements
  * where e = fl32(v - fl32(s * q)) with the code q and scale s the backward's
  * quantizer gives v; e^2 and the sums are fp64 (fixed summation order, so a
- * call is reproducible).  Four launches on `stream`: the backward's MAX and
+ * call is reproducible).  Five launches on `stream`: the backward's MAX and
  * reduce launches with both paths per token (group and tensor maxima,
- * scales), an error pass and a fixed-order fold.  The workspace (at least
+ * scales), two error passes (row and column operands) and a fixed-order
+ * fold.  The workspace (at least
  * hlq_lqs_workspace_size bytes) holds the backward's workspace regions
  * followed by per-workgroup partial sums.  Shape
  * rules and errors as for hlq_linear_backward; `stats` must be 16-byte
