@@ -173,3 +173,34 @@ def test_gpu_acbp_row_widths(I, dt):
     oc, os_ = o.acbp_pack(host_f32(inp["x"], dt))
     assert np.array_equal(codes.cpu().numpy(), oc)
     assert np.array_equal(scales.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
+@pytest.mark.parametrize("gy_dt,w_dt", [(wl.BF16, wl.F32), (wl.F32, wl.BF16)])
+def test_mixed_input_dtypes(gy_dt, w_dt):
+    # g_y and w in different element types: each input is read in its own
+    # type (backward and LQS statistics)
+    import dataclasses
+    import torch
+    import hadamard_rank_linear_amd as h
+    from parity_util import host_f32, to_device
+    cfg = dataclasses.replace(wl.CONFIGS[1], T=320, I=200, O=192, block=32, rank=8, index=91)
+    _say(f"mixed dtypes gy={gy_dt} w={w_dt}")
+    inp_b = wl.make_inputs(dataclasses.replace(cfg, dtype=wl.BF16))
+    inp_f = wl.make_inputs(dataclasses.replace(cfg, dtype=wl.F32))
+    gy_h = inp_b["gy"] if gy_dt == wl.BF16 else inp_f["gy"]
+    w_h = inp_b["w"] if w_dt == wl.BF16 else inp_f["w"]
+    gy32, w32 = host_f32(gy_h, gy_dt), host_f32(w_h, w_dt)
+    codes, scales = o.acbp_pack(inp_f["x"])
+    ref = o.linear_backward(gy32, codes, scales, w32, cfg.block, cfg.rank,
+                            cfg.gx_mode, cfg.gw_mode, cfg.reduction)
+    gy, w = to_device(gy_h, gy_dt), to_device(w_h, w_dt)
+    c = torch.from_numpy(codes).cuda()
+    s = torch.from_numpy(scales).cuda()
+    g_x, g_w = h.hlq_linear_backward(gy, c, s, w, cfg.block, cfg.rank, cfg.gx_mode,
+                                     cfg.gw_mode, cfg.reduction)
+    stats = h.hlq_lqs_accumulate(gy, c, s, w, cfg.block, cfg.rank)
+    torch.cuda.synchronize()
+    assert o.rel_fro(g_x.cpu().numpy(), ref["g_x"]) <= 1e-5
+    assert o.rel_fro(g_w.cpu().numpy(), ref["g_w"]) <= 1e-5
+    ost = o.lqs_stats(gy32, codes, scales, w32, cfg.block, cfg.rank)
+    np.testing.assert_allclose(stats.cpu().numpy(), ost, rtol=1e-9, atol=0)
