@@ -338,7 +338,15 @@ def cpu_baseline(cfg, inp):
     o.linear_backward(gy, codes, scales, w, cfg.block, cfg.rank, cfg.gx_mode, cfg.gw_mode,
                       cfg.reduction)
     sec = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                       cpu)
+    except OSError:
+        pass
     return {"value": round(sec * 1e6, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
+            "cpu": cpu, "host_cpus": os.cpu_count(),
             "sample": (f"one full {cfg.name} layer backward (T={cfg.T}, I={cfg.I}, O={cfg.O}) by "
                        f"the numpy oracle: fp32 transforms/quantizers single-threaded, exact "
                        f"integer GEMMs as fp64 BLAS on {threads} threads; ACBP excluded"),
