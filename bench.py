@@ -181,6 +181,30 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
     del xs
 
     if per_kernel:
+        # Distribution of single-step latencies: an event before every step of
+        # a run queued behind a spin kernel (no host gap inside an interval);
+        # the empty-interval cost measured below is subtracted.
+        n_dist = min(max(steps, 20), 100)
+        cal0 = torch.cuda.Event(enable_timing=True)
+        cal1 = torch.cuda.Event(enable_timing=True)
+        cal0.record()
+        torch.cuda._sleep(1 << 20)
+        cal1.record()
+        torch.cuda.synchronize()
+        cyc_per_us = (1 << 20) / max(cal0.elapsed_time(cal1) * 1e3, 1e-3)
+        torch.cuda._sleep(int((2000 + n_dist * 150) * cyc_per_us))
+        evs = []
+        for i in range(n_dist):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            evs.append(e)
+            sets.run(i)
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        evs.append(e)
+        torch.cuda.synchronize()
+        res["step_event_us"] = [a.elapsed_time(b) * 1e3 for a, b in zip(evs, evs[1:])]
+
         # In-pipeline per-kernel durations: an event before every launch step
         # of every step, enqueued while a spin kernel holds the GPU so that the
         # queue is full and no launch gap lands inside a measured interval.
@@ -220,6 +244,11 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
         res["kernels_event_us"] = raw
         res["event_overhead_us"] = empty
         res["kernels_us"] = {k: max(v - empty, 0.0) for k, v in raw.items()}
+        import numpy as np
+        lat = np.array(res.pop("step_event_us")) - empty
+        res["latency_us"] = {"p10": round(float(np.percentile(lat, 10)), 2),
+                             "p50": round(float(np.percentile(lat, 50)), 2),
+                             "p90": round(float(np.percentile(lat, 90)), 2), "steps": int(lat.size)}
         res["instrumented_steps"] = n_inst
     del sets
     torch.cuda.empty_cache()
@@ -450,6 +479,7 @@ def main():
         "effective_tops": round(ops_total / (lat_us * 1e-6) / 1e12, 1),
         "layer_roofline_frac": round(ideal_total / lat_us, 4),
         "acbp_us": round(res["acbp_us"], 2),
+        "latency_us": res["latency_us"],
         "kernels_us": {k: round(v, 2) for k, v in res["kernels_us"].items()},
         "kernels_event_us": {k: round(v, 2) for k, v in res["kernels_event_us"].items()},
         "event_overhead_us": round(res["event_overhead_us"], 2),
