@@ -340,7 +340,7 @@ def per_config_side(steps, warmup):
     roofline is the headline layer's)."""
     from hadamard_rank_linear_amd import workloads as wl
     out = {}
-    for cfg in wl.CONFIGS:
+    for cfg in wl.LAYERS:
         if cfg.name in ("vitb_qkv", "vitb_fc2"):
             continue
         log(f"side measurement: {cfg.name}")

@@ -56,7 +56,7 @@ class LayerConfig:
         return self.T * self.rank // self.block
 
 
-CONFIGS = [
+LAYERS = [
     LayerConfig(0, "tiny", 256, 64, 64, F32, 16, 8, PER_TOKEN, PER_TOKEN, SUM,
                 "normal(1)+1%x20", "normal(1)", "normal(0.02)"),
     LayerConfig(1, "vitb_qkv", 12608, 768, 2304, BF16, 16, 8, PER_TOKEN, PER_TENSOR, SUM,
@@ -68,7 +68,7 @@ CONFIGS = [
     LayerConfig(4, "resnet50_s3_conv", 50176, 2304, 256, BF16, 16, 4, PER_TENSOR, PER_TENSOR, SUM,
                 "normal(1e-3)", "relu(normal(1))", "he_normal(2304)"),
 ]
-BY_NAME = {c.name: c for c in CONFIGS}
+BY_NAME = {c.name: c for c in LAYERS}
 
 
 def _rng(seed: int, cfg: int, tensor: int) -> np.random.Generator:

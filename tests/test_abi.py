@@ -86,7 +86,7 @@ def test_compress_act_validation():
     assert lib.hlq_compress_act(P + 2, 0, 4, 8, P, P, None) == 7
 
 
-@pytest.mark.parametrize("cfg", wl.CONFIGS, ids=[c.name for c in wl.CONFIGS])
+@pytest.mark.parametrize("cfg", wl.LAYERS, ids=[c.name for c in wl.LAYERS])
 def test_workspace_layout_consistent(cfg):
     T, I, O, n, r = cfg.T, cfg.I, cfg.O, cfg.block, cfg.rank
     lay = h.hlq_workspace_layout_query(T, I, O, n, r)
@@ -105,7 +105,7 @@ def test_workspace_layout_consistent(cfg):
     assert regions[-1][0] + regions[-1][1] <= size
 
 
-SPLIT_SHAPES = [(c.T, c.I, c.O, c.block, c.rank) for c in wl.CONFIGS] + [
+SPLIT_SHAPES = [(c.T, c.I, c.O, c.block, c.rank) for c in wl.LAYERS] + [
     (64, 40, 48, 16, 16), (96, 72, 96, 32, 1), (256, 136, 192, 64, 8),
     (256, 64, 128, 128, 128), (384, 96, 256, 128, 32), (208, 264, 160, 16, 2),
     (64, 64, 4608, 16, 4), (1040, 520, 336, 16, 8), (16, 8, 16384, 16, 16),

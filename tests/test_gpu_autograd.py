@@ -16,12 +16,12 @@ def _say(msg):
     print(f"\n[gpu-case] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("idx,T", [(0, 256), (1, 1056)])
-def test_wrapper_gradients_match_library_and_oracle(idx, T):
+@pytest.mark.parametrize("name,T", [("tiny", 256), ("vitb_qkv", 1056)])
+def test_wrapper_gradients_match_library_and_oracle(name, T):
     import torch
     import hadamard_rank_linear_amd as h
     from hadamard_rank_linear_amd.autograd import hlq_linear
-    cfg = wl.CONFIGS[idx].with_tokens(T)
+    cfg = wl.BY_NAME[name].with_tokens(T)
     _say(f"autograd {cfg.name} T={T}")
     inp = wl.make_inputs(cfg)
     x = to_device(inp["x"], cfg.dtype).requires_grad_(True)

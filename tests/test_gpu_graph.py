@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 def test_backward_graph_replays_match_eager():
     import torch
     import hadamard_rank_linear_amd as h
-    cfg = wl.CONFIGS[1].with_tokens(1056)
+    cfg = wl.BY_NAME["vitb_qkv"].with_tokens(1056)
     print(f"\n[gpu-case] graph capture {cfg.name} T={cfg.T}", flush=True)
     inp = wl.make_inputs(cfg)
     gy, x, w = (to_device(inp[k], cfg.dtype) for k in ("gy", "x", "w"))

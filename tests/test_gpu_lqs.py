@@ -61,25 +61,26 @@ def _case(cfg, inp=None):
 
 
 def test_lqs_tiny():
-    _case(wl.CONFIGS[0])
+    _case(wl.BY_NAME["tiny"])
 
 
-@pytest.mark.parametrize("idx,T", [(1, 1056), (2, 1024), (3, 1024), (4, 1040)])
-def test_lqs_layer_configs_reduced(idx, T):
-    _case(wl.CONFIGS[idx].with_tokens(T))
+@pytest.mark.parametrize("name,T", [("vitb_qkv", 1056), ("vitb_fc2", 1024),
+                                    ("llama3_8b_down", 1024), ("resnet50_s3_conv", 1040)])
+def test_lqs_layer_configs_reduced(name, T):
+    _case(wl.BY_NAME[name].with_tokens(T))
 
 
 def test_lqs_block128_fp32():
-    _case(dataclasses.replace(wl.CONFIGS[0], T=256, I=72, O=256, block=128, rank=32,
+    _case(dataclasses.replace(wl.BY_NAME["tiny"], T=256, I=72, O=256, block=128, rank=32,
                               index=77))
 
 
 def test_lqs_full_qkv_layer():
-    _case(wl.CONFIGS[1])
+    _case(wl.BY_NAME["vitb_qkv"])
 
 
 def test_lqs_planted_outlier_token():
-    cfg = dataclasses.replace(wl.CONFIGS[0], T=256, I=64, O=128, index=78)
+    cfg = dataclasses.replace(wl.BY_NAME["tiny"], T=256, I=64, O=128, index=78)
     inp = wl.make_inputs(cfg)
     gy = inp["gy"].copy()
     gy[17] *= np.float32(20.0)
@@ -88,7 +89,7 @@ def test_lqs_planted_outlier_token():
 
 
 def test_lqs_accumulates_and_is_reproducible():
-    cfg = wl.CONFIGS[1].with_tokens(528)
+    cfg = wl.BY_NAME["vitb_qkv"].with_tokens(528)
     _say("lqs accumulate x2")
     inp = wl.make_inputs(cfg)
     codes, scales = o.acbp_pack(host_f32(inp["x"], cfg.dtype))

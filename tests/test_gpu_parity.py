@@ -36,28 +36,28 @@ def _case(cfg, plant=False, reduction=None, seed=0):
 # ----------------------------------------------------------------- tiny layer
 
 def test_tiny_config_exact():
-    _case(wl.CONFIGS[0])
+    _case(wl.BY_NAME["tiny"])
 
 
 def test_tiny_mean_reduction():
-    _case(wl.CONFIGS[0], reduction=wl.MEAN)
+    _case(wl.BY_NAME["tiny"], reduction=wl.MEAN)
 
 
 @pytest.mark.parametrize("gx_mode,gw_mode", [(0, 1), (1, 0), (1, 1)])
 def test_tiny_mode_combinations(gx_mode, gw_mode):
-    _case(dataclasses.replace(wl.CONFIGS[0], gx_mode=gx_mode, gw_mode=gw_mode))
+    _case(dataclasses.replace(wl.BY_NAME["tiny"], gx_mode=gx_mode, gw_mode=gw_mode))
 
 
 def test_tiny_zero_groups():
     # planted all-zero token / weight row: scale 0 and codes 0 on every path
-    _case(wl.CONFIGS[0], plant=True)
-    _case(dataclasses.replace(wl.CONFIGS[0], gx_mode=1, gw_mode=1), plant=True)
+    _case(wl.BY_NAME["tiny"], plant=True)
+    _case(dataclasses.replace(wl.BY_NAME["tiny"], gx_mode=1, gw_mode=1), plant=True)
 
 
 def test_tiny_denormal_group():
     # token 1 of g_y holds denormals only: qmax / a overflows fp32, so that
     # token's g_x-path codes are all zero while its scale stays a / 7
-    cfg = dataclasses.replace(wl.CONFIGS[0], dtype=wl.F32)
+    cfg = dataclasses.replace(wl.BY_NAME["tiny"], dtype=wl.F32)
     _say(f"denormal token row: {cfg.name} T={cfg.T} I={cfg.I} O={cfg.O}")
     inp = wl.make_inputs(cfg, seed=3)
     gy = inp["gy"].copy()
@@ -87,7 +87,7 @@ SHAPES = [
 @pytest.mark.parametrize("T,I,O,n,r,dt", SHAPES)
 @pytest.mark.parametrize("gx_mode,gw_mode", [(0, 0), (1, 1)])
 def test_shapes(T, I, O, n, r, dt, gx_mode, gw_mode):
-    base = wl.CONFIGS[1] if dt == wl.BF16 else wl.CONFIGS[0]
+    base = wl.BY_NAME["vitb_qkv"] if dt == wl.BF16 else wl.BY_NAME["tiny"]
     cfg = dataclasses.replace(base, T=T, I=I, O=O, block=n, rank=r, dtype=dt,
                               gx_mode=gx_mode, gw_mode=gw_mode, index=100 + T % 97)
     _case(cfg)
@@ -95,26 +95,28 @@ def test_shapes(T, I, O, n, r, dt, gx_mode, gw_mode):
 
 # ----------------------------------------------- layer configs, reduced tokens
 
-REDUCED_T = {1: 1040, 2: 1056, 3: 1024, 4: 2064}
+REDUCED_T = {"vitb_qkv": 1040, "vitb_fc2": 1056, "llama3_8b_down": 1024,
+             "resnet50_s3_conv": 2064}
+FULL_LAYERS = list(REDUCED_T)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4])
-def test_layer_config_reduced_tokens(idx):
-    cfg = wl.CONFIGS[idx].with_tokens(REDUCED_T[idx])
+@pytest.mark.parametrize("name", FULL_LAYERS)
+def test_layer_config_reduced_tokens(name):
+    cfg = wl.BY_NAME[name].with_tokens(REDUCED_T[name])
     _case(cfg)
 
 
 # ----------------------------------------------- layer configs, full size
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4])
-def test_layer_config_full_size(idx):
-    _case(wl.CONFIGS[idx])
+@pytest.mark.parametrize("name", FULL_LAYERS)
+def test_layer_config_full_size(name):
+    _case(wl.BY_NAME[name])
 
 
 # ----------------------------------------------- behaviour
 
 def test_gpu_acbp_matches_oracle_bf16_and_f32():
-    for cfg in (wl.CONFIGS[0], wl.CONFIGS[1].with_tokens(64)):
+    for cfg in (wl.BY_NAME["tiny"], wl.BY_NAME["vitb_qkv"].with_tokens(64)):
         _say(f"acbp {cfg.name}")
         inp = wl.make_inputs(cfg, plant_zero_rows=True)
         import hadamard_rank_linear_amd as h
@@ -126,7 +128,7 @@ def test_gpu_acbp_matches_oracle_bf16_and_f32():
 
 
 def test_deterministic_reruns():
-    cfg = wl.CONFIGS[1].with_tokens(528)
+    cfg = wl.BY_NAME["vitb_qkv"].with_tokens(528)
     _say("determinism")
     inp = wl.make_inputs(cfg)
     a = run_gpu(cfg, inp, want_acc=False)
@@ -166,7 +168,7 @@ def test_gpu_acbp_row_widths(I, dt):
     import dataclasses
     import hadamard_rank_linear_amd as h
     from parity_util import host_f32, to_device
-    cfg = dataclasses.replace(wl.CONFIGS[1], T=48, I=I, dtype=dt, index=90 + I % 7)
+    cfg = dataclasses.replace(wl.BY_NAME["vitb_qkv"], T=48, I=I, dtype=dt, index=90 + I % 7)
     _say(f"acbp I={I} dtype={dt}")
     inp = wl.make_inputs(cfg, plant_zero_rows=True)
     codes, scales = h.hlq_compress_act(to_device(inp["x"], dt))
@@ -183,7 +185,7 @@ def test_mixed_input_dtypes(gy_dt, w_dt):
     import torch
     import hadamard_rank_linear_amd as h
     from parity_util import host_f32, to_device
-    cfg = dataclasses.replace(wl.CONFIGS[1], T=320, I=200, O=192, block=32, rank=8, index=91)
+    cfg = dataclasses.replace(wl.BY_NAME["vitb_qkv"], T=320, I=200, O=192, block=32, rank=8, index=91)
     _say(f"mixed dtypes gy={gy_dt} w={w_dt}")
     inp_b = wl.make_inputs(dataclasses.replace(cfg, dtype=wl.BF16))
     inp_f = wl.make_inputs(dataclasses.replace(cfg, dtype=wl.F32))

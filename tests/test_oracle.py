@@ -407,7 +407,7 @@ def test_mean_reduction_divides_gw_by_T():
 
 
 def test_zero_groups_on_planted_rows():
-    cfg = wl.CONFIGS[0]
+    cfg = wl.BY_NAME["tiny"]
     inp = wl.make_inputs(cfg, plant_zero_rows=True)
     codes, s = o.acbp_pack(inp["x"])
     assert s[0] == 0 and (codes[0] == 0).all()
