@@ -167,6 +167,7 @@ def test_lqs_workspace_size():
 @pytest.mark.parametrize("kw,status", [
     (dict(gy=None), 1), (dict(stats=None), 1), (dict(T=72), 2), (dict(block=24), 3),
     (dict(rank=3), 4), (dict(gy_dt=2), 6), (dict(ws_bytes=16), 9), (dict(stats=(1 << 20) + 8), 7),
+    (dict(T=1 << 20, O=4096, rank=1), 8),   # g_y of 8 GiB: beyond 32-bit offsets
 ])
 def test_lqs_accumulate_validates_before_launch(kw, status):
     args = dict(gy=1 << 20, gy_dt=0, codes=1 << 20, scales=1 << 20, w=1 << 20, w_dt=0,
