@@ -132,7 +132,8 @@ LqsLayout make_lqs_layout(int64_t T, int64_t I, int64_t O, int block, int rank) 
   L.count[2] = (double)(T / n * rank * O);
   L.count[3] = (double)(T / n * rank * I);
   L.wg0[0] = 0;
-  L.wg0[1] = (L.items[0] + 255) / 256;
+  const int64_t rows_per_wg = 256 * hlq::lqs_row_blocks(block);
+  L.wg0[1] = (L.items[0] + rows_per_wg - 1) / rows_per_wg;
   for (int k = 1; k < 4; ++k) L.wg0[k + 1] = L.wg0[k] + L.items[k];
   L.part = align256(make_layout(T, I, O, block, rank).pub.total);
   L.total = align256(L.part + (size_t)L.wg0[4] * 3 * 8);

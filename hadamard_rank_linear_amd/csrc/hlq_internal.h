@@ -65,6 +65,8 @@ GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes);
 // per-token scales and the tensor maxima come from the backward's MAX and
 // reduce launches run with both paths per token.
 constexpr int LQS_STRIP = 4;  // blocks per thread along a column operand
+// row blocks per thread of the LQS row pass (two while they fit registers)
+constexpr int lqs_row_blocks(int n) { return n <= 32 ? 2 : 1; }
 struct LqsArgs {
   const void* gy; int gy_dt;
   const uint8_t* xc; const float* xs;

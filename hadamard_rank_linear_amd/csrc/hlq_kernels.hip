@@ -1569,47 +1569,55 @@ __device__ __forceinline__ float ld_off(const void* base, int dt, uint32_t e) {
   return bf16_to_f32(*reinterpret_cast<const uint16_t*>(b + (e << 1)));
 }
 
-// Row operand (op 0, H.g_y): one thread per block of n values of a token row,
-// two 16-byte loads per 8 elements.
+// Row operand (op 0, H.g_y): a thread takes LQS_ROW_BLOCKS(N) blocks of n
+// values of token rows (blocks tid and tid + 256 of its workgroup's range, so
+// each load instruction of a wave reads contiguous bytes), every load issued
+// before the arithmetic; 16-byte loads.
 template <int N>
 __global__ __launch_bounds__(256) void k_lqs_rows(LqsArgs a) {
+  constexpr int RPT = lqs_row_blocks(N);
   __shared__ double red[3][256];
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
-  const uint32_t item = (uint32_t)(b * 256 + tid);
-  const bool valid = item < (uint32_t)a.items[0];
   const uint32_t O = (uint32_t)a.O;
-  const uint32_t t = item / (O / N);
-  LqsQuant zt{0.f, 0.f, 7.f}, zT{0.f, 0.f, 7.f};
+  const char* base = static_cast<const char*>(a.gy);
   double ss = 0.0, e_tok = 0.0, e_ten = 0.0;
-  if (valid) {
-    zt.inv = a.tok_inv[0][t];
-    zt.s = a.tok_s[0][t];
-    const float at = __uint_as_float(a.tmax[0]);
-    zT.inv = inv_of(at, 7.f);
-    zT.s = scale_of(at, 7.f);
-    float v[N];
-    const uint32_t e0 = t * O + item % (O / N) * N;
-    const char* base = static_cast<const char*>(a.gy);
+  float v[RPT][N];
+  uint32_t tq[RPT];
+  bool ok[RPT];
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    const uint32_t item = (uint32_t)((b * RPT + q) * 256 + tid);
+    ok[q] = item < (uint32_t)a.items[0];
+    tq[q] = item / (O / N);
+    if (!ok[q]) continue;
+    const uint32_t e0 = tq[q] * O + item % (O / N) * N;
 #pragma unroll
     for (int k = 0; k < N; k += 8) {
       if (a.gy_dt == 0) {
         const float4* p = reinterpret_cast<const float4*>(base + ((e0 + k) << 2));
         const float4 x0 = p[0], x1 = p[1];
-        v[k] = x0.x; v[k + 1] = x0.y; v[k + 2] = x0.z; v[k + 3] = x0.w;
-        v[k + 4] = x1.x; v[k + 5] = x1.y; v[k + 6] = x1.z; v[k + 7] = x1.w;
+        v[q][k] = x0.x; v[q][k + 1] = x0.y; v[q][k + 2] = x0.z; v[q][k + 3] = x0.w;
+        v[q][k + 4] = x1.x; v[q][k + 5] = x1.y; v[q][k + 6] = x1.z; v[q][k + 7] = x1.w;
       } else {
         const uint4 u = *reinterpret_cast<const uint4*>(base + ((e0 + k) << 1));
-        v[k] = bf16_to_f32(u.x & 0xFFFFu); v[k + 1] = bf16_to_f32(u.x >> 16);
-        v[k + 2] = bf16_to_f32(u.y & 0xFFFFu); v[k + 3] = bf16_to_f32(u.y >> 16);
-        v[k + 4] = bf16_to_f32(u.z & 0xFFFFu); v[k + 5] = bf16_to_f32(u.z >> 16);
-        v[k + 6] = bf16_to_f32(u.w & 0xFFFFu); v[k + 7] = bf16_to_f32(u.w >> 16);
+        v[q][k] = bf16_to_f32(u.x & 0xFFFFu); v[q][k + 1] = bf16_to_f32(u.x >> 16);
+        v[q][k + 2] = bf16_to_f32(u.y & 0xFFFFu); v[q][k + 3] = bf16_to_f32(u.y >> 16);
+        v[q][k + 4] = bf16_to_f32(u.z & 0xFFFFu); v[q][k + 5] = bf16_to_f32(u.z >> 16);
+        v[q][k + 6] = bf16_to_f32(u.w & 0xFFFFu); v[q][k + 7] = bf16_to_f32(u.w >> 16);
       }
     }
-    fwht_reg<N>(v);
+  }
+  const float at = __uint_as_float(a.tmax[0]);
+  const LqsQuant zT{inv_of(at, 7.f), scale_of(at, 7.f), 7.f};
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    if (!ok[q]) continue;
+    const LqsQuant zt{a.tok_inv[0][tq[q]], a.tok_s[0][tq[q]], 7.f};
+    fwht_reg<N>(v[q]);
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-      const float x = v[k];
+      const float x = v[q][k];
       const float d1 = lqs_err(x, zt), d2 = lqs_err(x, zT);
       ss += (double)x * (double)x;
       e_tok += (double)d1 * (double)d1;
