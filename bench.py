@@ -298,26 +298,30 @@ def time_lqs(cfg, inp, reps=10):
                                "gw": "per_token" if modes[1] == 0 else "per_tensor"}}
 
 
-def time_torch_bf16_backward(cfg, inp, steps=20, warmup=5):
-    """Context, not this library: the plain bf16 backward of the same layer in
-    torch (g_x = g_y . w and g_w = g_y^T . x, two 2-D matmuls on hipBLASLt),
-    µs per layer on rotating operand copies.  The transposed operand is the
-    left one of a 2-D product."""
+def time_torch_backward(cfg, inp, dtype_name="bf16", steps=20, warmup=5):
+    """Context, not this library: the plain backward of the same layer in
+    torch at bf16 or fp32 (g_x = g_y . w and g_w = g_y^T . x, two 2-D matmuls
+    on hipBLASLt), µs per layer on rotating operand copies.  The transposed
+    operand is the left one of a 2-D product."""
     import numpy as np
     import torch
     dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
 
     def dev_t(a):
         if cfg.dtype == 1:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev).to(torch.bfloat16)
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(a)
+        return t.to(dev).to(tdt)
 
     gy0, x0, w0 = dev_t(inp["gy"]), dev_t(inp["x"]), dev_t(inp["w"])
-    per_set = (gy0.numel() + x0.numel() + w0.numel() + cfg.T * cfg.I + cfg.O * cfg.I) * 2
+    esz = 2 if tdt == torch.bfloat16 else 4
+    per_set = (gy0.numel() + x0.numel() + w0.numel() + cfg.T * cfg.I + cfg.O * cfg.I) * esz
     n = max(2, -(-2 * LLC_BYTES // per_set))
     sets = [(gy0.clone(), x0.clone(), w0.clone(),
-             torch.empty((cfg.T, cfg.I), dtype=torch.bfloat16, device=dev),
-             torch.empty((cfg.O, cfg.I), dtype=torch.bfloat16, device=dev)) for _ in range(n)]
+             torch.empty((cfg.T, cfg.I), dtype=tdt, device=dev),
+             torch.empty((cfg.O, cfg.I), dtype=tdt, device=dev)) for _ in range(n)]
 
     def step(i):
         gy, x, w, gx, gw = sets[i % n]
@@ -445,8 +449,10 @@ def main():
         extra["vitb_fc2_us"] = round(r2["wall_ms_per_step"] * 1e3, 2)
     if not args.no_extra:
         extra["per_config"] = per_config_side(max(10, args.steps // 2), args.warmup)
-        log("context: torch bf16 backward of the same layer")
-        extra["context_torch_bf16_backward_us"] = time_torch_bf16_backward(cfg, inp)
+        log("context: torch bf16 and fp32 backward of the same layer")
+        extra["context_torch_bf16_backward_us"] = time_torch_backward(cfg, inp, "bf16")
+        extra["context_torch_fp32_backward_us"] = time_torch_backward(cfg, inp, "fp32", steps=10,
+                                                                      warmup=3)
 
     if args.copy_calib:
         copy_calibration()
