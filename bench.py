@@ -60,11 +60,18 @@ def step_costs(cfg, dt_bytes):
     }
 
 
+KERNEL_SOURCES = ("hlq_device.h", "hlq_internal.h", "hlq_tr.hip", "hlq_gemm.hip", "hlq_acbp.hip")
+
+
 def kernel_source_sha():
+    """SHA-256 over the kernel sources (in a fixed order): a counter record
+    taken for other sources is not reported."""
     import hashlib
-    path = os.path.join(ROOT, "hadamard_rank_linear_amd", "csrc", "hlq_kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "hadamard_rank_linear_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload, kernel):

@@ -1,6 +1,6 @@
 // C ABI of the HLQ/HOT linear-layer backward: argument validation, workspace
 // carving and the launch sequence.  Everything here runs on the host; all
-// arithmetic of the method happens in the kernels of hlq_kernels.hip.
+// arithmetic of the method happens in the kernels of hlq_*.hip.
 //
 // Launch sequence of hlq_linear_backward (one stream, no host sync; each
 // line is one HLQ_STEP_* of hlq.h):
@@ -186,7 +186,7 @@ hlq::TrArgs make_tr_args(const Layout& L, const void* g_y, int gy_dtype, const u
 
 extern "C" {
 
-int hlq_version(void) { return 100; }
+int hlq_version(void) { return 200; }
 
 const char* hlq_status_string(int status) {
   switch (status) {
@@ -298,13 +298,27 @@ hlq_status hlq_linear_backward(const void* g_y, int gy_dtype, const uint8_t* x_c
                                    workspace, workspace_bytes, HLQ_STEPS_ALL, stream);
 }
 
-hlq_status hlq_gemm_gx_acc(const void* workspace, int64_t T, int64_t I, int64_t O,
-                           int block, int rank, int32_t* acc_x, void* stream) {
-  if (!workspace || !acc_x) return HLQ_ERR_NULL;
+// Shared checks of the accumulator exports: the workspace holds the layout of
+// hlq_linear_backward for this shape.
+static hlq_status acc_checks(const void* workspace, size_t workspace_bytes, int64_t T,
+                             int64_t I, int64_t O, int block, int rank, Layout* L) {
+  if (!workspace) return HLQ_ERR_NULL;
   hlq_status st = check_shape(T, I, O, block, rank);
   if (st != HLQ_OK) return st;
-  if (!aligned16(workspace) || !aligned16(acc_x)) return HLQ_ERR_ALIGN;
-  const Layout L = make_layout(T, I, O, block, rank);
+  *L = make_layout(T, I, O, block, rank);
+  if (workspace_bytes < L->pub.total) return HLQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return HLQ_ERR_ALIGN;
+  return HLQ_OK;
+}
+
+hlq_status hlq_gemm_gx_acc(const void* workspace, size_t workspace_bytes, int64_t T,
+                           int64_t I, int64_t O, int block, int rank, int32_t* acc_x,
+                           void* stream) {
+  if (!acc_x) return HLQ_ERR_NULL;
+  Layout L;
+  hlq_status st = acc_checks(workspace, workspace_bytes, T, I, O, block, rank, &L);
+  if (st != HLQ_OK) return st;
+  if (!aligned16(acc_x)) return HLQ_ERR_ALIGN;
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
   HLQ_TRY(hlq::launch_gemm(true, ws + L.pub.q_gy, ws + L.pub.q_w, T, I, L.pub.kx_pitch,
                            L.plan_gx, nullptr, 0, nullptr, 0, 1.f, hlq::EPI_I32, nullptr,
@@ -312,17 +326,35 @@ hlq_status hlq_gemm_gx_acc(const void* workspace, int64_t T, int64_t I, int64_t 
   return HLQ_OK;
 }
 
-hlq_status hlq_gemm_gw_acc(const void* workspace, int64_t T, int64_t I, int64_t O,
-                           int block, int rank, int32_t* acc_w, void* stream) {
-  if (!workspace || !acc_w) return HLQ_ERR_NULL;
-  hlq_status st = check_shape(T, I, O, block, rank);
+hlq_status hlq_gemm_gw_acc(const void* workspace, size_t workspace_bytes, int64_t T,
+                           int64_t I, int64_t O, int block, int rank, int32_t* acc_w,
+                           void* stream) {
+  if (!acc_w) return HLQ_ERR_NULL;
+  Layout L;
+  hlq_status st = acc_checks(workspace, workspace_bytes, T, I, O, block, rank, &L);
   if (st != HLQ_OK) return st;
-  if (!aligned16(workspace) || !aligned16(acc_w)) return HLQ_ERR_ALIGN;
-  const Layout L = make_layout(T, I, O, block, rank);
+  if (!aligned16(acc_w)) return HLQ_ERR_ALIGN;
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
   HLQ_TRY(hlq::launch_gemm(false, ws + L.pub.q_gyl, ws + L.pub.q_xl, O, I, L.pub.kw_pitch,
                            L.plan_gw, nullptr, 0, nullptr, 0, 1.f, hlq::EPI_I32, nullptr,
                            acc_w, nullptr, static_cast<hipStream_t>(stream)));
+  return HLQ_OK;
+}
+
+hlq_status hlq_gemm_pair_acc(const void* workspace, size_t workspace_bytes, int64_t T,
+                             int64_t I, int64_t O, int block, int rank, int32_t* acc_x,
+                             int32_t* acc_w, void* stream) {
+  if (!acc_x || !acc_w) return HLQ_ERR_NULL;
+  Layout L;
+  hlq_status st = acc_checks(workspace, workspace_bytes, T, I, O, block, rank, &L);
+  if (st != HLQ_OK) return st;
+  if (!aligned16(acc_x) || !aligned16(acc_w)) return HLQ_ERR_ALIGN;
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  HLQ_TRY(hlq::launch_gemm_pair(ws + L.pub.q_gy, ws + L.pub.q_w, T, I, L.pub.kx_pitch,
+                                L.plan_gx, nullptr, nullptr, 0, 1.f, nullptr, ws + L.pub.q_gyl,
+                                ws + L.pub.q_xl, O, L.pub.kw_pitch, L.plan_gw, nullptr, nullptr,
+                                0, 1.f, nullptr, static_cast<hipStream_t>(stream),
+                                hlq::EPI_I32, acc_x, acc_w));
   return HLQ_OK;
 }
 

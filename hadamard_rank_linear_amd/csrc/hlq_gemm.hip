@@ -1,0 +1,580 @@
+// gfx950 (CDNA4) kernels of the HLQ/HOT linear-layer backward: integer GEMMs.
+//
+// Method: "HLQ: Fast and Efficient Backpropagation via Hadamard Low-rank
+// Quantization" (TL;DR: g_x = g_y.w with 4-bit Hadamard quantization, g_w with
+// low-rank int8 processing, int4 activation compression) and "HOT:
+// Hadamard-based Optimized Training" (scime.ai summary, "Approach": INT4
+// Hadamard quantization for gx, Hadamard low-rank approximation plus INT8 for
+// gw, per-token or per-tensor scales chosen per layer).
+//
+// Numerics every kernel keeps (so codes are unique and reproducible):
+//  * Walsh-Hadamard butterflies in fp32, ascending stage distance
+//    h = 1, 2, 4, ...; pair (k, k+h) -> (a + b, a - b).  Built with
+//    -ffp-contract=off so nothing is fused into an FMA.
+//  * Quantizer: a = max|v| (exact), inv = qmax / a (IEEE division),
+//    q = clamp(rne(v * inv), -qmax, qmax), s = a / qmax; a == 0 -> q = 0, s = 0.
+//  * Cross-block maxima use atomicMax on the fp32 bit pattern of non-negative
+//    values, which orders like the values and commutes, so results do not
+//    depend on scheduling.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "hlq_device.h"
+#include "hlq_internal.h"
+
+namespace hlq {
+
+// ------------------------------------------------------------ integer GEMM
+// C[m][n] = sum_k A[m][k] * B[n][k]; A [M][pitch], B [N][pitch] bytes, K
+// contiguous and zero-padded to a multiple of the stage depth KB.  INT4
+// operands hold two codes per byte and stay packed in HBM, L2 and LDS; each
+// 16-byte fragment is widened on the LDS->register path into two int8
+// fragments holding 16*code (low nibble shifted up, high nibble masked in
+// place), so the INT32 sum is 256 times the code product sum and is shifted
+// back exactly.  Both operands are widened the same way, so the nibble order
+// inside a lane leaves the dot product unchanged.
+//
+// Matrix core: v_mfma_i32_32x32x32_i8 (32 cycles of the matrix pipe for a
+// 32x32x32 product; the 16x16x64 form needs more independent accumulators
+// than a wave has to stay busy).  Operand X holds 32 rows of A, operand Y 32
+// rows of B; lane l feeds row l%32 with 16 consecutive K bytes of half l/32.
+// Lane l then holds D[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator r: one
+// column n of C per lane, so a store of register r writes 128 contiguous
+// bytes of a C row per half-wave.
+//
+// Pipeline (256 threads, 2x2 waves, wave tile (BM/2) x (BN/2)):
+//   * K advances in stages of KB bytes held in an NS-deep LDS ring.  Stages
+//     are fetched with LDS DMA (global_load_lds_dwordx4: lane i of a wave
+//     instruction fills bytes 16i..16i+15 of a 1 KB LDS run), NS stages
+//     ahead; no VGPR staging.  Each row's 16-byte chunks are XOR-swizzled
+//     (chunk c of row r sits at c ^ swz(r)) so the fragment reads of 32 rows
+//     at one chunk hit distinct banks.
+//   * Fragments are double-buffered in registers: the reads of k-step kk+1
+//     are issued between the MFMAs of step kk.
+//   * One barrier per stage, after the stage's last MFMAs are issued: it
+//     publishes the next stage (every wave has waited for its own DMA with
+//     vmcnt) and frees the stage just read, which is refilled at once.
+// Workgroups map to tiles XCD-aware: consecutive workgroup ids go to the 8
+// XCDs in turn, so each XCD takes a contiguous run of tiles (n fastest) and
+// its L2 serves the A rows those tiles share.  blockIdx.y selects a split of
+// the K stages (partials summed by k_gemm_finalize).
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void widen_int4x2(u32x4 p, v4i& a, v4i& b) {
+  a[0] = (int)((p[0] << 4) & 0xF0F0F0F0u); a[1] = (int)(p[0] & 0xF0F0F0F0u);
+  a[2] = (int)((p[1] << 4) & 0xF0F0F0F0u); a[3] = (int)(p[1] & 0xF0F0F0F0u);
+  b[0] = (int)((p[2] << 4) & 0xF0F0F0F0u); b[1] = (int)(p[2] & 0xF0F0F0F0u);
+  b[2] = (int)((p[3] << 4) & 0xF0F0F0F0u); b[3] = (int)(p[3] & 0xF0F0F0F0u);
+}
+
+__device__ __forceinline__ bool xcd_tile(int64_t w, int64_t nt_m, int64_t nt_n, int64_t& tm,
+                                         int64_t& tn) {
+  const int64_t total = nt_m * nt_n;
+  const int64_t per = (total + 7) / 8;
+  const int64_t t = (w % 8) * per + w / 8;
+  if (t >= total) return false;
+  tm = t / nt_n;
+  tn = t % nt_n;
+  return true;
+}
+
+// s_waitcnt with vmcnt = N and the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory into LDS run l (lane i -> l + 16 i).
+__device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+// Physical 16-byte chunk slot of logical chunk 0 in row r (XOR with it).
+// Depends on r & 15 only, so fragment bases (multiples of 32 rows) keep it.
+template <int KB>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (KB == 128) return (r & 7) ^ ((r >> 3) & 1);
+  else return (r >> 2) & 3;
+}
+
+template <bool INT4, int BM, int BN, int KB, int NS>
+struct GemmShape {
+  static constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
+  static constexpr int CPR = KB / 16;                              // chunks per row
+  static constexpr int IA = BM * CPR / 256, IB = BN * CPR / 256;   // DMA ops per wave
+  static constexpr int IPW = IA + IB;
+  static constexpr int STAGE = (BM + BN) * KB;
+  static constexpr int KK = KB / 32;                               // k-steps per stage
+  static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA tile");
+  static_assert(IA * 256 == BM * CPR && IB * 256 == BN * CPR, "stage load split");
+  static_assert(KK % 2 == 0, "fragment slots alternate per k-step");
+  static_assert(KB == 64 || KB == 128, "swizzle covers 4 or 8 chunks per row");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  static_assert(NS * STAGE <= 160 * 1024, "LDS ring fits the CU");
+};
+
+#define HLQ_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
+// One GEMM of a launch: operands, shape, K stages (split into sps-stage
+// pieces) and the dequantizing epilogue's scales.
+struct GemmArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  int64_t M, N, pitch, S_total, sps;
+  const float* sa;
+  int sa_step;
+  const float* sb;
+  int sb_step;
+  float alpha;
+  float* C;
+  int32_t* Ci;
+};
+
+// One output tile (workgroup w of the tile grid, K split `split`) of one GEMM.
+// Every thread of the workgroup calls it; `lds` holds NS * STAGE bytes.
+template <bool INT4, int BM, int BN, int KB, int NS, int EPI>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t split,
+                                          uint8_t* lds, float* sc) {
+  using G = GemmShape<INT4, BM, BN, KB, NS>;
+  constexpr int FM = G::FM, FN = G::FN, IA = G::IA, IB = G::IB, IPW = G::IPW;
+  constexpr int CPR = G::CPR, KK = G::KK;
+  const uint8_t* __restrict__ A = g.A;
+  const uint8_t* __restrict__ B = g.B;
+  const int64_t M = g.M, N = g.N, pitch = g.pitch, S_total = g.S_total, sps = g.sps;
+  const float* __restrict__ sa = g.sa;
+  const float* __restrict__ sb = g.sb;
+  const int sa_step = g.sa_step, sb_step = g.sb_step;
+  const float alpha = g.alpha;
+  float* __restrict__ C = g.C;
+  int32_t* __restrict__ Ci = g.Ci;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int64_t tm, tn;
+  if (!xcd_tile(w, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn)) return;
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int64_t s_first = split * sps;
+  const int64_t S = (S_total - s_first < sps ? S_total - s_first : sps);  // >= 1 by plan
+  const int64_t kbase = s_first * KB;
+
+  // DMA sources of this lane for stage 0 (rows past M / N re-read the last row)
+  const uint8_t* src[IPW];
+#pragma unroll
+  for (int j = 0; j < IA; ++j) {
+    const int slot = (wave * IA + j) * 64 + lane;
+    const int row = slot / CPR, c = (slot % CPR) ^ chunk_swz<KB>(row);
+    const int64_t r = m0 + row < M ? m0 + row : M - 1;
+    src[j] = A + r * pitch + kbase + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < IB; ++j) {
+    const int slot = (wave * IB + j) * 64 + lane;
+    const int row = slot / CPR, c = (slot % CPR) ^ chunk_swz<KB>(row);
+    const int64_t r = n0 + row < N ? n0 + row : N - 1;
+    src[IA + j] = B + r * pitch + kbase + c * 16;
+  }
+#define HLQ_GEMM_ISSUE(st, bf)                                                           \
+  do {                                                                                   \
+    uint8_t* base_ = lds + (bf) * G::STAGE;                                              \
+    for (int j = 0; j < IA; ++j) lds_dma16(src[j] + (st) * KB, base_ + (wave * IA + j) * 1024); \
+    for (int j = 0; j < IB; ++j)                                                         \
+      lds_dma16(src[IA + j] + (st) * KB, base_ + BM * KB + (wave * IB + j) * 1024);      \
+  } while (0)
+  // wait until at most k stages of this wave's DMA are still in flight
+#define HLQ_GEMM_WAIT(k)                                        \
+  do {                                                          \
+    const int64_t k_ = (k);                                     \
+    if (k_ <= 0) wait_vmcnt<0>();                               \
+    else if (k_ == 1) wait_vmcnt<IPW>();                        \
+    else if (k_ == 2) wait_vmcnt<(2 * IPW < 63 ? 2 * IPW : 63)>(); \
+    else wait_vmcnt<(3 * IPW < 63 ? 3 * IPW : 63)>();           \
+  } while (0)
+
+  const int fr = lane & 31, fh = lane >> 5;
+  const int a_off = (wm * G::WTM + fr) * KB;
+  const int b_off = BM * KB + (wn * G::WTN + fr) * KB;
+  const int sw = chunk_swz<KB>(fr);
+  int coff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) coff[kk] = ((kk * 2 + fh) ^ sw) * 16;
+
+  // Dequantization scales of the tile's rows (times alpha) and columns, read
+  // before the K loop and parked in LDS (sc, an array of its own, so the
+  // ring's DMA does not order its accesses): the epilogue then waits on no
+  // global load while its stores are in flight.
+  constexpr int NSC = (BM + BN + 255) / 256;
+  float scv[NSC];
+  if constexpr (EPI == EPI_F32) {
+#pragma unroll
+    for (int q = 0; q < NSC; ++q) {
+      // one unconditional load per slot (a select of the address, so the
+      // loaded value is not merged across branches, which would wait on it)
+      const int i = tid + 256 * q;
+      const int64_t m = m0 + i, n = n0 + (i - BM);
+      const float* src = i < BM ? sa + (m < M ? m : M - 1) * sa_step
+                                : sb + (n < N ? (n >= 0 ? n : 0) : N - 1) * sb_step;
+      scv[q] = *src;
+    }
+  }
+
+#pragma unroll
+  for (int p = 0; p < NS; ++p)
+    if (p < S) HLQ_GEMM_ISSUE(p, p);
+  // keep the scales' LDS writes below the ring's first wait (no stall on
+  // the scale loads before the stage loads are in flight)
+  asm volatile("" ::: "memory");
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  u32x4 fa[2][FM], fb[2][FN];
+  HLQ_GEMM_WAIT((S - 1 < NS - 1 ? S - 1 : NS - 1));
+  if constexpr (EPI == EPI_F32) {
+#pragma unroll
+    for (int q = 0; q < NSC; ++q)
+      if (tid + 256 * q < BM + BN) sc[tid + 256 * q] = tid + 256 * q < BM ? scv[q] * alpha : scv[q];
+  }
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    fa[0][i] = *reinterpret_cast<const u32x4*>(lds + a_off + i * 32 * KB + coff[0]);
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    fb[0][j] = *reinterpret_cast<const u32x4*>(lds + b_off + j * 32 * KB + coff[0]);
+
+  // One K stage.  MODE 0: steady state (refill a buffer, prefetch the next
+  // stage's first fragments); 1: the last NS-1 stages but one (prefetch, no
+  // refill); 2: the last stage.  Separate bodies keep each stage one block
+  // of straight-line code for the scheduler.
+  int buf = 0;
+  auto stage = [&](int64_t st, auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    const uint8_t* base = lds + buf * G::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      const bool reads = kk + 1 < KK || MODE != 2;
+      if (kk + 1 < KK) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fa[nxt][i] = *reinterpret_cast<const u32x4*>(base + a_off + i * 32 * KB + coff[kk + 1]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[nxt][j] = *reinterpret_cast<const u32x4*>(base + b_off + j * 32 * KB + coff[kk + 1]);
+      } else if constexpr (MODE != 2) {
+        // Before the stage's last k-step (its fragments are already in
+        // registers): stage st+1 landed in every wave (st+2 .. st+NS-1 may
+        // still fly) and no wave reads stage st any more ...
+        if constexpr (MODE == 0) wait_vmcnt<(NS - 2) * IPW>();
+        else HLQ_GEMM_WAIT((S - st - 2 < NS - 2 ? S - st - 2 : NS - 2));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // ... so the first fragments of stage st+1 load under this step's
+        // MFMAs, and stage st's buffer is refilled (after those reads are
+        // issued: an LDS read behind a DMA into LDS would wait for the DMA).
+        const int ob = buf;
+        buf = buf + 1 == NS ? 0 : buf + 1;
+        const uint8_t* nb = lds + buf * G::STAGE;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fa[nxt][i] = *reinterpret_cast<const u32x4*>(nb + a_off + i * 32 * KB + coff[0]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[nxt][j] = *reinterpret_cast<const u32x4*>(nb + b_off + j * 32 * KB + coff[0]);
+        if constexpr (MODE == 0) HLQ_GEMM_ISSUE(st + NS, ob);
+      }
+      if constexpr (INT4) {
+        v4i xa0[FM], xa1[FM], yb0[FN], yb1[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) widen_int4x2(fa[cur][i], xa0[i], xa1[i]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) widen_int4x2(fb[cur][j], yb0[j], yb1[j]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa0[i], yb0[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa1[i], yb1[j], acc[i][j], 0, 0, 0);
+        // INT4: the compiler's own interleaving of reads, widening and MFMAs
+        // (explicit groups measured no better: fc2 pair 52.5 vs 51 us)
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const u32x4 xa = fa[cur][i], yb = fb[cur][j];
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                v4i{(int)xa[0], (int)xa[1], (int)xa[2], (int)xa[3]},
+                v4i{(int)yb[0], (int)yb[1], (int)yb[2], (int)yb[3]}, acc[i][j], 0, 0, 0);
+          }
+        if (reads) {
+          // every fragment read of the next k-step ahead of this step's
+          // MFMAs: the reads get a whole step to land (interleaved one per
+          // MFMA, the last one landed just before the next step needed it;
+          // qkv pair 42.4 -> 40.3 us)
+          HLQ_SGB(0x100, FM + FN);
+          HLQ_SGB(0x008, FM * FN);
+        }
+      }
+    }
+  };
+  int64_t st = 0;
+  for (; st + NS < S; ++st) stage(st, std::integral_constant<int, 0>());
+  for (; st + 1 < S; ++st) stage(st, std::integral_constant<int, 1>());
+  stage(st, std::integral_constant<int, 2>());  // S >= 1
+#undef HLQ_GEMM_ISSUE
+#undef HLQ_GEMM_WAIT
+
+  constexpr int SH = INT4 ? 8 : 0;
+  int32_t* Cp = Ci + (EPI == EPI_PARTIAL ? split * M * N : 0);
+  // Scales from LDS (written before the K loop; its barriers published them).
+  float s_n[FN], s_m[FM][16];
+  if constexpr (EPI == EPI_F32) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) s_n[j] = sc[BM + wn * G::WTN + j * 32 + fr];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_m[i][r] = sc[wm * G::WTM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4)];
+  }
+  // Interior tiles store without per-lane guards: branch-free code lets the
+  // counter waits before the stores be exact instead of full drains.  The fp32
+  // outputs are written once and not read again here: non-temporal stores
+  // stream them to HBM instead of leaving them dirty in L2 / the last-level
+  // cache, where the next layer's transform passes would have to evict them
+  // (ViT-B qkv: the following MAX pass 20 -> 17.6 us).
+  const bool full = m0 + BM <= M && n0 + BN <= N;
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * G::WTM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
+          const int32_t v = acc[i][j][r] >> SH;
+          if constexpr (EPI == EPI_F32) __builtin_nontemporal_store((float)v * s_m[i][r] * s_n[j], &C[m * N + n]);
+          else Cp[m * N + n] = v;
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t m = m0 + wm * G::WTM + i * 32 + 8 * (r / 4) + 4 * fh + (r % 4);
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
+        if (n >= N) continue;
+        const int32_t v = acc[i][j][r] >> SH;
+        if constexpr (EPI == EPI_F32) __builtin_nontemporal_store((float)v * s_m[i][r] * s_n[j], &C[m * N + n]);
+        else Cp[m * N + n] = v;
+      }
+  }
+}
+
+template <bool INT4, int BM, int BN, int KB, int NS, int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * GemmShape<INT4, BM, BN, KB, NS>::STAGE];
+  __shared__ float sc[BM + BN];
+  gemm_tile<INT4, BM, BN, KB, NS, EPI>(g, blockIdx.x, blockIdx.y, lds, sc);
+}
+
+// Both GEMMs of the backward in one launch (fp32 epilogues, no split-K): the
+// first n1 workgroups take the g_w tiles (longer K, so they start first), the
+// rest the g_x tiles, which fill the CUs around them.  One launch instead of
+// two plus a split-K pass, and neither GEMM's tail leaves the GPU idle.
+// EPI_I32 stores the INT32 accumulators instead of the fp32 gradients (tests
+// compare them bit for bit); everything else is the same launch.
+template <int BM1, int BN1, int KB1, int NS1, int BM0, int BN0, int KB0, int NS0, int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm_pair(GemmArgs gw, int64_t n1, GemmArgs gx) {
+  constexpr int L1 = NS1 * GemmShape<false, BM1, BN1, KB1, NS1>::STAGE;
+  constexpr int L0 = NS0 * GemmShape<true, BM0, BN0, KB0, NS0>::STAGE;
+  constexpr int SC = BM1 + BN1 > BM0 + BN0 ? BM1 + BN1 : BM0 + BN0;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L1 > L0 ? L1 : L0];
+  __shared__ float sc[SC];
+  const int64_t b = blockIdx.x;
+  if (b < n1) gemm_tile<false, BM1, BN1, KB1, NS1, EPI>(gw, b, 0, lds, sc);
+  else gemm_tile<true, BM0, BN0, KB0, NS0, EPI>(gx, b - n1, 0, lds, sc);
+}
+
+// Sum of split-K INT32 partials (exact) followed by the dequantizing epilogue.
+__global__ __launch_bounds__(256) void k_gemm_finalize(const int32_t* __restrict__ P,
+                                                       int splits, int64_t M, int64_t N,
+                                                       const float* __restrict__ sa,
+                                                       int sa_step,
+                                                       const float* __restrict__ sb,
+                                                       int sb_step, float alpha,
+                                                       float* __restrict__ C) {
+  const int64_t q4 = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index of 4 outputs
+  if (q4 * 4 >= M * N) return;
+  const int64_t e = q4 * 4;
+  const int64_t m = e / N, nn = e % N;
+  int4 s = *reinterpret_cast<const int4*>(P + e);
+  for (int z = 1; z < splits; ++z) {
+    int4 p = *reinterpret_cast<const int4*>(P + (int64_t)z * M * N + e);
+    s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+  }
+  const float s_m = sa[m * sa_step] * alpha;
+  float4 o;
+  o.x = (float)s.x * s_m * sb[(nn + 0) * sb_step];
+  o.y = (float)s.y * s_m * sb[(nn + 1) * sb_step];
+  o.z = (float)s.z * s_m * sb[(nn + 2) * sb_step];
+  o.w = (float)s.w * s_m * sb[(nn + 3) * sb_step];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<f32x4*>(C + e));
+}
+
+// Tile configurations (rows of A x rows of B, stage depth, ring depth):
+//   0: 128 x 128, KB  64, 3 stages  (48 KB LDS, two workgroups per CU)
+//   1: 256 x 128, KB  64, 3 stages  (72 KB LDS, two workgroups per CU)
+//   2: 128 x 128, KB 128, 2 stages  (64 KB LDS, two workgroups per CU)
+// Large grids take the 256 x 128 tile; INT8 operands with K a multiple of 128
+// bytes take the deeper stage; grids below the CU count split K.
+GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes) {
+  static const int cfg_bm[3] = {128, 256, 128}, cfg_bn[3] = {128, 128, 128};
+  static const int cfg_kb[3] = {64, 64, 128};
+  GemmPlan p;
+  auto tiles = [&](int c) { return (int64_t)cdiv(M, cfg_bm[c]) * cdiv(N, cfg_bn[c]); };
+  if (tiles(1) >= 1024) p.cfg = 1;
+  else if (!int4 && kbytes % 128 == 0) p.cfg = 2;
+  else p.cfg = 0;
+  p.bm = cfg_bm[p.cfg];
+  p.bn = cfg_bn[p.cfg];
+  p.kb = cfg_kb[p.cfg];
+  p.stages = kbytes / p.kb;
+  const int64_t t = tiles(p.cfg);
+  int64_t sp = 1;
+  while (t * sp < 256 && sp < 8 && p.stages / (sp * 2) >= 8) sp *= 2;
+  p.sps = (p.stages + sp - 1) / sp;
+  p.splits = (int)((p.stages + p.sps - 1) / p.sps);  // every split non-empty
+  return p;
+}
+
+template <bool I4, int EPI>
+static void gemm_dispatch(int cfg, dim3 g, hipStream_t s, const GemmArgs& a) {
+#define HLQ_GEMM(BM_, BN_, KB_, NS_) \
+  hipLaunchKernelGGL((k_gemm<I4, BM_, BN_, KB_, NS_, EPI>), g, dim3(256), 0, s, a)
+  switch (cfg) {
+    case 1: HLQ_GEMM(256, 128, 64, 3); break;
+    case 2: HLQ_GEMM(128, 128, 128, 2); break;
+    default: HLQ_GEMM(128, 128, 64, 3); break;
+  }
+#undef HLQ_GEMM
+}
+
+hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
+                       int64_t N, int64_t pitch, const GemmPlan& plan,
+                       const float* sa, int sa_step, const float* sb, int sb_step,
+                       float alpha, GemmEpi epi, float* C, int32_t* Ci,
+                       int32_t* partial, hipStream_t s) {
+  if (pitch % plan.kb != 0 || plan.stages * plan.kb != pitch) return hipErrorInvalidValue;
+  const int splits = epi == EPI_I32 ? 1 : plan.splits;
+  const int64_t sps = splits == 1 ? plan.stages : plan.sps;
+  const int64_t tiles = (int64_t)cdiv(M, plan.bm) * cdiv(N, plan.bn);
+  dim3 grid((unsigned)((tiles + 7) / 8 * 8), splits);
+  const bool use_partial = (epi == EPI_F32 && splits > 1);
+  if (use_partial && partial == nullptr) return hipErrorInvalidValue;
+  if (epi == EPI_F32 && (C == nullptr || sa == nullptr || sb == nullptr))
+    return hipErrorInvalidValue;
+  if (epi == EPI_I32 && Ci == nullptr) return hipErrorInvalidValue;
+  const int e = use_partial ? EPI_PARTIAL : epi;
+  GemmArgs a{A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C,
+             use_partial ? partial : Ci};
+  if (int4) {
+    if (e == EPI_F32) gemm_dispatch<true, EPI_F32>(plan.cfg, grid, s, a);
+    else if (e == EPI_I32) gemm_dispatch<true, EPI_I32>(plan.cfg, grid, s, a);
+    else gemm_dispatch<true, EPI_PARTIAL>(plan.cfg, grid, s, a);
+  } else {
+    if (e == EPI_F32) gemm_dispatch<false, EPI_F32>(plan.cfg, grid, s, a);
+    else if (e == EPI_I32) gemm_dispatch<false, EPI_I32>(plan.cfg, grid, s, a);
+    else gemm_dispatch<false, EPI_PARTIAL>(plan.cfg, grid, s, a);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !use_partial) return err;
+  return launch_gemm_finalize(partial, splits, M, N, sa, sa_step, sb, sb_step, alpha, C, s);
+}
+
+hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, int64_t I,
+                            int64_t kx_pitch, const GemmPlan& px, const float* s_gy,
+                            const float* s_w, int gx_step, float gx_alpha, float* g_x,
+                            const uint8_t* gwA, const uint8_t* gwB, int64_t O, int64_t kw_pitch,
+                            const GemmPlan& pw, const float* s_gyl, const float* s_xl,
+                            int gw_step, float gw_alpha, float* g_w, hipStream_t s,
+                            GemmEpi epi, int32_t* acc_x, int32_t* acc_w) {
+  if (kx_pitch % px.kb || px.stages * px.kb != kx_pitch) return hipErrorInvalidValue;
+  if (kw_pitch % pw.kb || pw.stages * pw.kb != kw_pitch) return hipErrorInvalidValue;
+  if (epi == EPI_F32 && (!g_x || !g_w || !s_gy || !s_w || !s_gyl || !s_xl))
+    return hipErrorInvalidValue;
+  if (epi == EPI_I32 && (!acc_x || !acc_w)) return hipErrorInvalidValue;
+  if (epi != EPI_F32 && epi != EPI_I32) return hipErrorInvalidValue;
+  const GemmArgs ax{gxA, gxB, T, I, kx_pitch, px.stages, px.stages, s_gy, gx_step, s_w, gx_step,
+                    gx_alpha, g_x, acc_x};
+  const GemmArgs aw{gwA, gwB, O, I, kw_pitch, pw.stages, pw.stages, s_gyl, gw_step, s_xl, gw_step,
+                    gw_alpha, g_w, acc_w};
+  // g_w tile: the plan's, except that a long-K g_w grid of fewer than 64
+  // tiles (a quarter of the CU count; its tiles are the launch's critical
+  // path) takes 64-row tiles (cfg 3: 64 x 128, KB 128, 3 stages): twice the
+  // tiles, half the K work each.  Larger grids keep 128 x 128, which reads
+  // fewer LDS bytes per MFMA (ViT-B qkv, 108 tiles: 46 -> 43 us).
+  int wcfg = pw.cfg, wbm = pw.bm;
+  if (pw.cfg == 2 && (int64_t)cdiv(O, 128) * cdiv(I, 128) < 64) { wcfg = 3; wbm = 64; }
+  const int64_t tx = (int64_t)cdiv(T, px.bm) * cdiv(I, px.bn);
+  const int64_t tw = (int64_t)cdiv(O, wbm) * cdiv(I, pw.bn);
+  const int64_t n1 = (tw + 7) / 8 * 8, n0 = (tx + 7) / 8 * 8;
+  const dim3 g((unsigned)(n1 + n0));
+#define HLQ_PAIR(W_, X_)                                                                 \
+  do {                                                                                   \
+    if (epi == EPI_F32) hipLaunchKernelGGL((k_gemm_pair<W_, X_, EPI_F32>), g, dim3(256), 0, s, aw, n1, ax); \
+    else hipLaunchKernelGGL((k_gemm_pair<W_, X_, EPI_I32>), g, dim3(256), 0, s, aw, n1, ax); \
+  } while (0)
+#define HLQ_W0 128, 128, 64, 3
+#define HLQ_W1 256, 128, 64, 3
+#define HLQ_W2 128, 128, 128, 2
+#define HLQ_W3 64, 128, 128, 3
+#define HLQ_X0 128, 128, 64, 3
+#define HLQ_X1 256, 128, 64, 3
+  const bool x1 = px.cfg == 1;
+  switch (wcfg) {
+    case 1: if (x1) HLQ_PAIR(HLQ_W1, HLQ_X1); else HLQ_PAIR(HLQ_W1, HLQ_X0); break;
+    case 2: if (x1) HLQ_PAIR(HLQ_W2, HLQ_X1); else HLQ_PAIR(HLQ_W2, HLQ_X0); break;
+    case 3: if (x1) HLQ_PAIR(HLQ_W3, HLQ_X1); else HLQ_PAIR(HLQ_W3, HLQ_X0); break;
+    default: if (x1) HLQ_PAIR(HLQ_W0, HLQ_X1); else HLQ_PAIR(HLQ_W0, HLQ_X0); break;
+  }
+#undef HLQ_PAIR
+#undef HLQ_W0
+#undef HLQ_W1
+#undef HLQ_W2
+#undef HLQ_W3
+#undef HLQ_X0
+#undef HLQ_X1
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_finalize(const int32_t* partial, int splits, int64_t M,
+                                int64_t N, const float* sa, int sa_step,
+                                const float* sb, int sb_step, float alpha, float* C,
+                                hipStream_t s) {
+  const int64_t q4 = M * N / 4;
+  hipLaunchKernelGGL(k_gemm_finalize, dim3(cdiv(q4, 256)), dim3(256), 0, s, partial, splits,
+                     M, N, sa, sa_step, sb, sb_step, alpha, C);
+  return hipGetLastError();
+}
+
+}  // namespace hlq

@@ -1,5 +1,6 @@
 // Internal launch interface between the C ABI layer (hlq_api.cpp) and the
-// gfx950 kernels (hlq_kernels.hip).  Not part of the public ABI.
+// gfx950 kernels (hlq_tr.hip, hlq_gemm.hip, hlq_lqs.hip, hlq_acbp.hip).
+// Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,7 +13,7 @@ enum GemmEpi { EPI_F32 = 0, EPI_I32 = 1, EPI_PARTIAL = 2 };
 enum TrPass { PASS_MAX = 0, PASS_QUANT = 1 };
 
 // Rows and columns of one transform tile (see the tile engine in
-// hlq_kernels.hip); the host sizes the partial-maximum arrays with them.
+// hlq_tr.hip); the host sizes the partial-maximum arrays with them.
 constexpr int TR_ROWS = 128;
 constexpr int TR_COLS = 128;
 constexpr int TR_RED_ENTRIES = 64;  // entries folded per reduce block
@@ -95,6 +96,11 @@ hipError_t launch_acbp(const void* x, int dtype, int64_t T, int64_t I, uint8_t* 
 
 // Transform pass over g_y, the ACBP codes of x and w (one grid for all three).
 hipError_t launch_tr(const TrArgs& a, int pass, int n, int r, hipStream_t s);
+// The same for one block size (one object file each; grid already sized).
+hipError_t launch_tr_n16(const TrArgs& a, int pass, int r, dim3 g, hipStream_t s);
+hipError_t launch_tr_n32(const TrArgs& a, int pass, int r, dim3 g, hipStream_t s);
+hipError_t launch_tr_n64(const TrArgs& a, int pass, int r, dim3 g, hipStream_t s);
+hipError_t launch_tr_n128(const TrArgs& a, int pass, int r, dim3 g, hipStream_t s);
 // Fold the partial maxima of the MAX pass (per-token maxima, scales, tensor maxima).
 hipError_t launch_tr_reduce(const TrArgs& a, hipStream_t s);
 
@@ -104,16 +110,20 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
                        float alpha, GemmEpi epi, float* C, int32_t* Ci,
                        int32_t* partial, hipStream_t s);
 
-// Both GEMMs of the backward in one launch, fp32 epilogues, no split-K:
-// g_x = acc(q_gy, q_w) * s_gy * s_w * gx_alpha, g_w = acc(q_gyl, q_xl) *
-// s_gyl * s_xl * gw_alpha (scale steps 1 per-token, 0 per-tensor).  The
-// plans fix the tile configurations; their splits are ignored.
+// Both GEMMs of the backward in one launch, no split-K.  EPI_F32 (the
+// backward): g_x = acc(q_gy, q_w) * s_gy * s_w * gx_alpha, g_w = acc(q_gyl,
+// q_xl) * s_gyl * s_xl * gw_alpha (scale steps 1 per-token, 0 per-tensor).
+// EPI_I32: the same launch stores the INT32 accumulators to acc_x [T][I] and
+// acc_w [O][I] instead (scales and fp32 outputs unused).  The plans fix the
+// tile configurations; their splits are ignored.
 hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, int64_t I,
                             int64_t kx_pitch, const GemmPlan& px, const float* s_gy,
                             const float* s_w, int gx_step, float gx_alpha, float* g_x,
                             const uint8_t* gwA, const uint8_t* gwB, int64_t O, int64_t kw_pitch,
                             const GemmPlan& pw, const float* s_gyl, const float* s_xl,
-                            int gw_step, float gw_alpha, float* g_w, hipStream_t s);
+                            int gw_step, float gw_alpha, float* g_w, hipStream_t s,
+                            GemmEpi epi = EPI_F32, int32_t* acc_x = nullptr,
+                            int32_t* acc_w = nullptr);
 
 hipError_t launch_gemm_finalize(const int32_t* partial, int splits, int64_t M,
                                 int64_t N, const float* sa, int sa_step,

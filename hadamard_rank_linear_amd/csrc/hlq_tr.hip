@@ -1,0 +1,979 @@
+// gfx950 (CDNA4) kernels of the HLQ/HOT linear-layer backward: operand transforms (MAX, reduce, QUANT).
+//
+// Method: "HLQ: Fast and Efficient Backpropagation via Hadamard Low-rank
+// Quantization" (TL;DR: g_x = g_y.w with 4-bit Hadamard quantization, g_w with
+// low-rank int8 processing, int4 activation compression) and "HOT:
+// Hadamard-based Optimized Training" (scime.ai summary, "Approach": INT4
+// Hadamard quantization for gx, Hadamard low-rank approximation plus INT8 for
+// gw, per-token or per-tensor scales chosen per layer).
+//
+// Numerics every kernel keeps (so codes are unique and reproducible):
+//  * Walsh-Hadamard butterflies in fp32, ascending stage distance
+//    h = 1, 2, 4, ...; pair (k, k+h) -> (a + b, a - b).  Built with
+//    -ffp-contract=off so nothing is fused into an FMA.
+//  * Quantizer: a = max|v| (exact), inv = qmax / a (IEEE division),
+//    q = clamp(rne(v * inv), -qmax, qmax), s = a / qmax; a == 0 -> q = 0, s = 0.
+//  * Cross-block maxima use atomicMax on the fp32 bit pattern of non-negative
+//    values, which orders like the values and commutes, so results do not
+//    depend on scheduling.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "hlq_device.h"
+#include "hlq_internal.h"
+
+namespace hlq {
+
+// ------------------------------------------------------------ operand transforms
+// All four GEMM operands come from one tile engine.  A tile is TT rows x CW
+// columns of a row-major source: g_y [T][O] (rows = tokens), the ACBP codes of
+// x [T][I], or w [O][I] (rows = output features).  Each tile is loaded once
+// with coalesced 16-byte loads (all of a thread's loads issued before any
+// arithmetic) and parked in LDS in its source form - bf16 or fp32 values, or
+// the packed INT4 codes plus one scale per row - with 16-byte LDS writes.
+// Every column is then transformed along the rows by one thread per (column,
+// block) task reading LDS column-wise (consecutive threads take consecutive
+// columns: no bank conflicts):
+//   * g_y and x: the low-rank rows of H_n along tokens (g_w path);
+//   * w: the full H_n along O (g_x path, operand B).
+// g_y rows are also transformed along O in registers while loading (g_x path,
+// operand A): each lane owns 8 consecutive columns, n/8 lanes form a block,
+// butterflies cross lanes with xor shuffles.
+//
+// Two launches of the same kernel:
+//   MAX:   every tile writes its partial maxima (per row chunk, per column
+//          range) to plain arrays - no atomics;
+//   QUANT: after k_tr_reduce has folded the partials, every tile recomputes
+//          its transforms and writes codes; the transposed operands are
+//          staged in LDS so each column's run of codes leaves in wide stores.
+// Workgroups of the three sources share one grid (g_y first: largest tiles).
+// Keeping the tile in its source form (35 KB for bf16) lets four workgroups
+// share a CU, which the load/transform/store phases need to overlap.
+
+constexpr int TT = TR_ROWS;     // rows per tile
+constexpr int CW = TR_COLS;     // columns per tile
+constexpr int P_F32 = CW + 4;   // LDS pitches (elements); rows stay 16-byte aligned
+constexpr int P_B16 = CW + 8;
+constexpr int P_I4 = CW / 2 + 16;  // bytes: two codes per byte
+constexpr int OUT_BYTES = 128;  // staging bytes per column (>= TT*r/n and TT/2)
+// Pitch of a staged column: 36 banks apart, so the 4-byte writes of 64
+// consecutive columns spread over 16 banks instead of 2.
+constexpr int OUT_PITCH = 144;
+
+template <bool F32>
+struct TileSmem {
+  static constexpr int bytes = F32 ? TT * P_F32 * 4 : TT * P_B16 * 2;
+};
+
+// Column readers: value of (row, c) of the tile as fp32, exactly as the
+// source holds it (bf16 widened; INT4 code times its row scale, one rounding).
+struct RdF32 {
+  const float* t;
+  __device__ __forceinline__ float operator()(int r, int c) const { return t[r * P_F32 + c]; }
+};
+struct RdB16 {
+  const uint16_t* t;
+  __device__ __forceinline__ float operator()(int r, int c) const {
+    return __uint_as_float((uint32_t)t[r * P_B16 + c] << 16);
+  }
+};
+struct RdI4 {
+  const uint8_t* q;
+  const float* s;
+  __device__ __forceinline__ float operator()(int r, int c) const {
+    const int byte = q[r * P_I4 + (c >> 1)];
+    const int code = __builtin_amdgcn_sbfe(byte, (c & 1) * 4, 4);
+    return s[r] * (float)code;
+  }
+};
+
+__device__ __forceinline__ float max_over_16_lanes(float a) {
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
+  return a;
+}
+
+// Butterflies across the lanes of one 16-lane row group (element distance
+// 8*m lives in lane ^ m; m < 16 keeps the exchange inside the group).  The
+// lower lane keeps p + v, the upper lane p - v = p + (-v) (a is the lower
+// lane's value): both exact IEEE adds.
+template <int N>
+__device__ __forceinline__ void fwht_lanes_n(float (&v)[8], int lc) {
+#pragma unroll
+  for (int m = 1; m < N / 8; m <<= 1) {
+    const bool upper = (lc & m) != 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float p = __shfl_xor(v[k], m);
+      v[k] = p + (upper ? -v[k] : v[k]);
+    }
+  }
+}
+
+// Low-rank rows of H_N for one column block: group sums of N/R consecutive
+// rows in adjacent-pair tree order (the first log2(N/R) butterfly stages on
+// the kept rows), then H_R in registers.
+template <int N, int R, class RD>
+__device__ __forceinline__ void lowrank_col(const RD& rd, int r0, int c, float (&g)[R]) {
+  constexpr int G = N / R;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    float s[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) s[k] = rd(r0 + j * G + k, c);
+#pragma unroll
+    for (int h = 1; h < G; h <<= 1)
+#pragma unroll
+      for (int k = 0; k < G; k += 2 * h) s[k] = s[k] + s[k + h];
+    g[j] = s[0];
+  }
+#pragma unroll
+  for (int h = 1; h < R; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if ((j & h) == 0) {
+        float x0 = g[j], x1 = g[j + h];
+        g[j] = x0 + x1;
+        g[j + h] = x0 - x1;
+      }
+}
+
+// Full H_N of one column block.
+template <int N, class RD>
+__device__ __forceinline__ void full_col(const RD& rd, int r0, int c, float (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = rd(r0 + k, c);
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if ((k & h) == 0) {
+        float x0 = v[k], x1 = v[k + h];
+        v[k] = x0 + x1;
+        v[k + h] = x0 - x1;
+      }
+}
+
+// 8 consecutive source elements as raw 16 bytes (bf16) or 32 bytes (fp32).
+struct Raw8 {
+  uint4 a, b;
+};
+__device__ __forceinline__ void load_raw8(const void* base, int dt, int64_t e, Raw8& r) {
+  if (dt == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + e);
+    r.a = p[0];
+    r.b = p[1];
+  } else {
+    r.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+  }
+}
+__device__ __forceinline__ void raw8_to_f32(const Raw8& r, int dt, float (&v)[8]) {
+  if (dt == 0) {
+    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+    v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+    v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+  } else {
+    v[0] = bf16_to_f32(r.a.x & 0xFFFFu); v[1] = bf16_to_f32(r.a.x >> 16);
+    v[2] = bf16_to_f32(r.a.y & 0xFFFFu); v[3] = bf16_to_f32(r.a.y >> 16);
+    v[4] = bf16_to_f32(r.a.z & 0xFFFFu); v[5] = bf16_to_f32(r.a.z >> 16);
+    v[6] = bf16_to_f32(r.a.w & 0xFFFFu); v[7] = bf16_to_f32(r.a.w >> 16);
+  }
+}
+// Park 8 source elements of (row, col..col+7) in the tile (16-byte writes).
+// A fp32 tile widens bf16 exactly; a bf16 tile only ever holds bf16 sources.
+template <bool F32>
+__device__ __forceinline__ void park8(uint8_t* smem, int row, int col, const Raw8& r, int dt) {
+  if constexpr (F32) {
+    float v[8];
+    raw8_to_f32(r, dt, v);
+    float* t = reinterpret_cast<float*>(smem) + row * P_F32 + col;
+    *reinterpret_cast<float4*>(t) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(t + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(smem) + row * P_B16 + col) = r.a;
+  }
+}
+
+// Column maxima of a tile: thread tid covers column tid % CW; the two threads
+// of a column meet in LDS.
+__device__ __forceinline__ void tile_colmax_store(float m, float* red, int tid, int cols,
+                                                  float* dst) {
+  red[tid] = m;
+  __syncthreads();
+  if (tid < CW && tid < cols) dst[tid] = fmaxf(red[tid], red[tid + CW]);
+}
+
+// Store the staged transposed codes: column c of the tile owns `len` bytes at
+// dst + c * pitch (dst already offset to the tile's first K byte).  Byte runs
+// go out in the widest unit that divides both the run and its offset.
+__device__ __forceinline__ void store_staged(const uint8_t (*outs)[OUT_PITCH], int cols,
+                                             int len, uint8_t* dst, int64_t pitch,
+                                             int64_t koff, int tid) {
+  int wdt = 16;
+  while (wdt > 1 && ((len % wdt) || (koff % wdt))) wdt >>= 1;
+  const int per_col = len / wdt;
+  const int total = cols * per_col;
+  for (int i = tid; i < total; i += 256) {
+    const int c = i / per_col, k = (i % per_col) * wdt;
+    uint8_t* d = dst + (int64_t)c * pitch + k;
+    const uint8_t* s = &outs[c][k];
+    if (wdt == 16) *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+    else if (wdt == 8) *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(s);
+    else if (wdt == 4) *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
+    else if (wdt == 2) *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
+    else *d = *s;
+  }
+}
+
+// store_staged for a full tile whose runs are LEN bytes (a multiple of 16)
+// at a 16-byte aligned offset: every column, 16-byte stores.
+template <int LEN>
+__device__ __forceinline__ void store_staged_full(const uint8_t (*outs)[OUT_PITCH], uint8_t* dst,
+                                                  int64_t pitch, int tid) {
+  static_assert(LEN % 16 == 0 && LEN <= OUT_BYTES, "16-byte runs");
+  constexpr int PER = LEN / 16;
+#pragma unroll
+  for (int i = tid; i < CW * PER; i += 256) {
+    const int c = i / PER, k = (i % PER) * 16;
+    *reinterpret_cast<uint4*>(dst + (int64_t)c * pitch + k) =
+        *reinterpret_cast<const uint4*>(&outs[c][k]);
+  }
+}
+
+// Zero bytes [from, to) of `cols` rows of a K-major operand (K padding);
+// nthr threads share the work.
+__device__ __forceinline__ void zero_tail(uint8_t* dst, int64_t pitch, int cols, int64_t from,
+                                          int64_t to, int tid, int nthr = 256) {
+  const int64_t w = to - from;
+  if (w <= 0) return;
+  for (int64_t i = tid; i < (int64_t)cols * w; i += nthr) dst[(i / w) * pitch + from + i % w] = 0;
+}
+
+// Column pass, low-rank rows of H_N (g_w operands).  Thread tid owns column
+// c = tid % CW and blocks b = tid / CW + 2t.  MAX: the tile's column maxima ->
+// part[0..cols).  QUANT: INT8 codes (reciprocal scale colinv[c], or that of tensor
+// list `list` when colinv is null) staged in LDS over the tile (after a
+// barrier) and stored K-contiguous at q[(c0 + c) * pitch + t0 / N * R ...].
+template <int PASS, int N, int R, class RD>
+__device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, uint8_t* smem,
+                                                float* red, int rows, int cols, int64_t c0,
+                                                const float* colinv, int list, float* part,
+                                                uint8_t* q, int64_t pitch, int64_t tl,
+                                                int64_t t0, bool last) {
+  constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;  // tasks per thread
+  constexpr int WPR = (R + 3) / 4;                           // code words per task
+  const int tid = threadIdx.x;
+  const int c = tid % CW;
+  const int nb = rows / N;
+  float inv_c = 0.f;
+  if constexpr (PASS == PASS_QUANT) {
+    const float tinv = colinv ? 0.f : inv_of(__uint_as_float(a.tmax[list]), list == 1 ? 7.f : 127.f);
+    inv_c = colinv ? (c < cols ? colinv[c0 + c] : 0.f) : tinv;
+  }
+  float cm = 0.f;
+  uint32_t words[TPT][WPR];
+#pragma unroll
+  for (int t = 0; t < TPT; ++t) {
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) words[t][w] = 0;
+    const int b = tid / CW + 2 * t;
+    if (b < nb && c < cols) {
+      float g[R];
+      lowrank_col<N, R>(rd, b * N, c, g);
+      if constexpr (PASS == PASS_MAX) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) cm = fmaxf(cm, fabsf(g[j]));
+      } else {
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+          words[t][j / 4] |= (quant_bits<127>(g[j], inv_c) & 0xFFu) << (8 * (j % 4));
+      }
+    }
+  }
+  if constexpr (PASS == PASS_MAX) {
+    tile_colmax_store(cm, red, tid, cols, part);
+  } else {
+    uint8_t (*outs)[OUT_PITCH] = reinterpret_cast<uint8_t (*)[OUT_PITCH]>(smem);
+    __syncthreads();  // every thread is done reading the tile
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const int b = tid / CW + 2 * t;
+      if (b < nb && c < cols) {
+        if constexpr (R >= 4) {
+#pragma unroll
+          for (int w = 0; w < WPR; ++w)
+            *reinterpret_cast<uint32_t*>(&outs[c][b * R + 4 * w]) = words[t][w];
+        } else {
+#pragma unroll
+          for (int j = 0; j < R; ++j) outs[c][b * R + j] = (uint8_t)(words[t][0] >> (8 * j));
+        }
+      }
+    }
+    __syncthreads();
+    const int64_t koff = t0 / N * R;
+    constexpr int LEN = (TT / N) * R;
+    if (LEN % 16 == 0 && rows == TT && cols == CW)
+      store_staged_full<(LEN % 16 == 0 ? LEN : 16)>(outs, q + c0 * pitch + koff, pitch, tid);
+    else
+      store_staged(outs, cols, nb * R, q + c0 * pitch + koff, pitch, koff, tid);
+    if (last) zero_tail(q + c0 * pitch, pitch, cols, tl, pitch, tid);
+  }
+}
+
+// Column pass with the full H_N along the rows (w -> INT4 codes for g_x).
+template <int PASS, int N, class RD>
+__device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint8_t* smem,
+                                             float* red, int rows, int cols, int64_t c0,
+                                             const float* colinv, int list, float* part,
+                                             uint8_t* q, int64_t pitch, int64_t o0, int64_t O,
+                                             bool last) {
+  constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;
+  constexpr int WPT = N / 8;  // code words (8 nibbles) per task
+  const int tid = threadIdx.x;
+  const int c = tid % CW;
+  const int nb = rows / N;
+  float inv_c = 0.f;
+  if constexpr (PASS == PASS_QUANT) {
+    const float tinv = colinv ? 0.f : inv_of(__uint_as_float(a.tmax[list]), list == 1 ? 7.f : 127.f);
+    inv_c = colinv ? (c < cols ? colinv[c0 + c] : 0.f) : tinv;
+  }
+  float cm = 0.f;
+  uint32_t words[TPT][WPT];
+#pragma unroll
+  for (int t = 0; t < TPT; ++t) {
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) words[t][w] = 0;
+    const int b = tid / CW + 2 * t;
+    if (b < nb && c < cols) {
+      float v[N];
+      full_col<N>(rd, b * N, c, v);
+      if constexpr (PASS == PASS_MAX) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) cm = fmaxf(cm, fabsf(v[k]));
+      } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+          words[t][k / 8] |= (quant_bits<7>(v[k], inv_c) & 0xFu) << (4 * (k % 8));
+      }
+    }
+  }
+  if constexpr (PASS == PASS_MAX) {
+    tile_colmax_store(cm, red, tid, cols, part);
+  } else {
+    uint8_t (*outs)[OUT_PITCH] = reinterpret_cast<uint8_t (*)[OUT_PITCH]>(smem);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const int b = tid / CW + 2 * t;
+      if (b < nb && c < cols) {
+#pragma unroll
+        for (int w = 0; w < WPT; ++w)
+          *reinterpret_cast<uint32_t*>(&outs[c][b * (N / 2) + 4 * w]) = words[t][w];
+      }
+    }
+    __syncthreads();
+    const int64_t koff = o0 / 2;
+    if (rows == TT && cols == CW)
+      store_staged_full<TT / 2>(outs, q + c0 * pitch + koff, pitch, tid);
+    else
+      store_staged(outs, cols, rows / 2, q + c0 * pitch + koff, pitch, koff, tid);
+    if (last) zero_tail(q + c0 * pitch, pitch, cols, O / 2, pitch, tid);
+  }
+}
+
+// Cross-lane butterfly stages h = 8, 16, .. N/2 of the row transform (lane
+// lc of a 16-lane row holds elements 8 lc .. 8 lc + 7): DPP / swizzle
+// exchanges, one fma(+-1, own, partner) per element (the exact IEEE add).
+template <int N>
+__device__ __forceinline__ void fwht_lanes_dpp(float (&v)[8], int lc) {
+  if constexpr (N >= 16) {
+    const float sg = (lc & 1) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xbfly<1>(v[k], sg);
+  }
+  if constexpr (N >= 32) {
+    const float sg = (lc & 2) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xbfly<2>(v[k], sg);
+  }
+  if constexpr (N >= 64) {
+    const float sg = (lc & 4) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xbfly<4>(v[k], sg);
+  }
+  if constexpr (N >= 128) {
+    const float sg = (lc & 8) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xbfly<8>(v[k], sg);
+  }
+}
+
+// Row phase of a full bf16 g_y tile (TT rows x CW columns inside T and O):
+// the same per-row work as the general loop of tr_job_gy, with tile-uniform
+// base pointers and 32-bit lane offsets, no bounds guards, and DPP exchanges.
+// 16 bytes of a source tile.  The QUANT pass reads g_y for the last time:
+// non-temporal loads keep it from displacing the GEMM operands the pass is
+// writing (ViT-B qkv QUANT 25.5 -> 24.5 us, GEMM -0.5 us).
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
+  if constexpr (NT) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+
+template <int PASS, int N>
+__device__ __forceinline__ void gy_rows_bf16_full(const TrArgs& a, int64_t t0, int64_t c0,
+                                                  int64_t ch, uint8_t* smem, float inv_tensor) {
+  constexpr int SW = TT / 16;
+  const int tid = threadIdx.x, lr = tid >> 4, lc = tid & 15, col = lc * 8;
+  const uint32_t O32 = (uint32_t)a.O;
+  const uint8_t* gbase = static_cast<const uint8_t*>(a.gy) + (t0 * a.O + c0) * 2;
+  const uint32_t goff = ((uint32_t)lr * O32 + (uint32_t)col) * 2u;
+  uint4 raw[SW];
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw)
+    raw[sw] = ld16<PASS == PASS_QUANT>(gbase + goff + (uint32_t)sw * 32u * O32);
+  float inv[SW];
+  if constexpr (PASS == PASS_QUANT) {
+    const float* ib = a.inv_gy + t0;
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) inv[sw] = a.gx_tok ? ib[sw * 16 + lr] : inv_tensor;
+  }
+  const uint32_t K32 = (uint32_t)a.kxb;
+  uint8_t* qbase = a.q_gy + t0 * a.kxb + c0 / 2;
+  const uint32_t qoff = (uint32_t)lr * K32 + (uint32_t)(col / 2);
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 16 + lr;
+    *reinterpret_cast<uint4*>(smem + (row * P_B16 + col) * 2) = raw[sw];
+    float v[8] = {bf16_lo(raw[sw].x), bf16_hi(raw[sw].x), bf16_lo(raw[sw].y), bf16_hi(raw[sw].y),
+                  bf16_lo(raw[sw].z), bf16_hi(raw[sw].z), bf16_lo(raw[sw].w), bf16_hi(raw[sw].w)};
+    fwht8(v);
+    fwht_lanes_dpp<N>(v, lc);
+    if constexpr (PASS == PASS_MAX) {
+      float m = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+      m = fmaxf(m, lane_xor<1>(m));
+      m = fmaxf(m, lane_xor<2>(m));
+      m = fmaxf(m, lane_xor<4>(m));
+      m = fmaxf(m, lane_xor<8>(m));
+      if (lc == 0) a.part_gy[ch * a.T + t0 + row] = m;
+    } else {
+      *reinterpret_cast<uint32_t*>(qbase + qoff + (uint32_t)sw * 16u * K32) =
+          quant_pack8_int4(v, inv[sw]);
+    }
+  }
+}
+
+// ---- job: g_y tile (rows along O for g_x, low-rank columns along T for g_w)
+template <int PASS, int N, int R, bool F32>
+__device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
+  const int tid = threadIdx.x;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
+  const int64_t t0 = tr * TT, c0 = ch * CW;
+  const int rows = (int)(a.T - t0 < TT ? a.T - t0 : TT);
+  const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
+  float inv_tensor = 0.f;
+  if constexpr (PASS == PASS_QUANT) {
+    if (!a.gx_tok) inv_tensor = inv_of(__uint_as_float(a.tmax[0]), 7.f);
+  }
+  if (!F32 && rows == TT && cols == CW) {
+    gy_rows_bf16_full<PASS, N>(a, t0, c0, ch, smem, inv_tensor);
+  } else {
+  // 16 rows per sweep, 16 lanes x 8 columns per row
+  constexpr int SW = TT / 16;
+  const int lr = tid >> 4, lc = tid & 15;
+  const int col = lc * 8;
+  Raw8 raw[SW];
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 16 + lr;
+    raw[sw].a = make_uint4(0, 0, 0, 0);
+    raw[sw].b = make_uint4(0, 0, 0, 0);
+    if (row < rows && col < cols) load_raw8(a.gy, a.gy_dt, (t0 + row) * a.O + c0 + col, raw[sw]);
+  }
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 16 + lr;
+    park8<F32>(smem, row, col, raw[sw], a.gy_dt);
+    float v[8];
+    raw8_to_f32(raw[sw], a.gy_dt, v);
+    fwht8(v);
+    fwht_lanes_n<N>(v, lc);
+    if constexpr (PASS == PASS_MAX) {
+      float m = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+      m = max_over_16_lanes(m);
+      if (lc == 0 && row < rows) a.part_gy[ch * a.T + t0 + row] = m;
+    } else if (row < rows) {
+      const float inv = a.gx_tok ? a.inv_gy[t0 + row] : inv_tensor;
+      // columns past O inside the chunk are zero -> zero codes (K padding)
+      *reinterpret_cast<uint32_t*>(a.q_gy + (t0 + row) * a.kxb + (c0 + col) / 2) =
+          col < cols ? quant_pack8_int4(v, inv) : 0u;
+    }
+  }
+  }
+  __syncthreads();
+  const bool last = t0 + rows == a.T;
+  if constexpr (F32) {
+    RdF32 rd{reinterpret_cast<const float*>(smem)};
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_gyl : nullptr,
+                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.kwb, a.tl, t0, last);
+  } else {
+    RdB16 rd{reinterpret_cast<const uint16_t*>(smem)};
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_gyl : nullptr,
+                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.kwb, a.tl, t0, last);
+  }
+}
+
+// ---- MAX pass over g_y tiles held in registers (bf16 g_y, n <= 64)
+// One wave per tile of GYR_ROWS = 64 tokens x CW = 128 channels; the four
+// waves of a workgroup take four tiles, never wait for each other and finish
+// independently.  These workgroups run in the same MAX launch as the x and w
+// tiles of the LDS engine.
+// Lane c16 = lane & 7 owns channels c0 + 16 c16 .. +15 and row group
+// rg = lane >> 3 owns tokens t0 + 8 rg .. +7, loaded once into registers
+// (8 tokens x 32 bytes).  A Hadamard block of n
+// channels spans n/16 adjacent lanes; a block of n tokens spans n/8 row
+// groups of one wave, i.e. lanes 8 apart.  Nothing goes through LDS:
+//   * along O (g_x operand A): per token, stages h = 1..8 in-lane, stages
+//     h >= 16 across lanes c16 ^ h/16 (DPP quad permutes);
+//   * along T (g_w operand): per channel, stages h = 1, 2, 4 over the lane's
+//     8 tokens, stages h = 8, 16, 32 across lanes 8, 16, 32 apart.
+// The low-rank rows are the butterfly network pruned to its surviving
+// entries: stages with h < n/r keep only a + b (the pairwise-tree group sums),
+// the later stages are full butterflies over the group sums (H_r), all in
+// ascending h as the full transform runs them.
+constexpr int GYR_ROWS = TR_GY_REG_ROWS;
+
+// max |v[i]| over 16 values with three-input maxima
+__device__ __forceinline__ float absmax16(const float (&v)[16]) {
+  float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) m = fmaxf(fmaxf(m, fabsf(v[i])), fabsf(v[i + 1]));
+  return fmaxf(m, fabsf(v[15]));
+}
+
+// Registers of one tile (zero outside T and O).
+__device__ __forceinline__ void gyr_load(const TrArgs& a, int64_t bid, uint4 (&raw)[8][2]) {
+  const int lane = threadIdx.x & 63;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
+  const int64_t t0 = tr * GYR_ROWS, c0 = ch * CW;
+  const int rows = (int)(a.T - t0 < GYR_ROWS ? a.T - t0 : GYR_ROWS);
+  const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
+  const int col = (lane & 7) * 16, r0 = (lane >> 3) * 8;
+  const bool ok = r0 < rows && col < cols;
+  const uint16_t* gy = static_cast<const uint16_t*>(a.gy);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    raw[k][0] = make_uint4(0, 0, 0, 0);
+    raw[k][1] = make_uint4(0, 0, 0, 0);
+    if (ok) {
+      const uint4* src = reinterpret_cast<const uint4*>(gy + (t0 + r0 + k) * a.O + c0 + col);
+      raw[k][0] = src[0];
+      raw[k][1] = src[1];
+    }
+  }
+}
+
+// Maxima of one tile: row maxima of H.g_y along O -> part_gy[ch][t], column
+// maxima of the low-rank g_y along T -> part_gyl[tr][o].
+template <int N, int R>
+__device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
+                                             const uint4 (&raw)[8][2]) {
+  static_assert(N >= 16 && N <= 64, "a token block spans 2..8 row groups of one wave");
+  constexpr int G = N / R;             // tokens per low-rank group
+  constexpr int GL = G < 8 ? G : 8;    // in-lane span of a group
+  constexpr int RGB = N / 8;           // row groups per token block
+  const int lane = threadIdx.x & 63;
+  const int c16 = lane & 7, rg = lane >> 3;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
+  const int64_t t0 = tr * GYR_ROWS, c0 = ch * CW;
+  const int rows = (int)(a.T - t0 < GYR_ROWS ? a.T - t0 : GYR_ROWS);
+  const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
+  const int col = c16 * 16;
+  const int r0 = rg * 8;               // first token of this lane in the tile
+  const bool act = r0 < rows;          // rows is a multiple of n >= 16
+  const bool cact = col < cols;        // cols is a multiple of n >= 16
+
+  // ---- along O: one token per iteration
+  const float sgn1 = (c16 & 1) ? -1.f : 1.f, sgn2 = (c16 & 2) ? -1.f : 1.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      v[8 * q + 0] = bf16_lo(raw[k][q].x); v[8 * q + 1] = bf16_hi(raw[k][q].x);
+      v[8 * q + 2] = bf16_lo(raw[k][q].y); v[8 * q + 3] = bf16_hi(raw[k][q].y);
+      v[8 * q + 4] = bf16_lo(raw[k][q].z); v[8 * q + 5] = bf16_hi(raw[k][q].z);
+      v[8 * q + 6] = bf16_lo(raw[k][q].w); v[8 * q + 7] = bf16_hi(raw[k][q].w);
+    }
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((e & h) == 0) {
+          const float p = v[e], q = v[e + h];
+          v[e] = p + q;
+          v[e + h] = p - q;
+        }
+    if constexpr (N >= 32) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = xbfly<1>(v[e], sgn1);
+    }
+    if constexpr (N >= 64) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = xbfly<2>(v[e], sgn2);
+    }
+    const float m = group8_max(absmax16(v));
+    if (c16 == 0 && act) a.part_gy[ch * a.T + t0 + r0 + k] = m;
+  }
+
+  // ---- along T: one channel per iteration
+  const int rib = rg % RGB;                                  // row group inside its block
+  const bool owner = (G <= 8) || (rib % (G / 8) == 0);       // holds surviving entries
+  const float sg8 = (rib & 1) ? -1.f : 1.f, sg16 = (rib & 2) ? -1.f : 1.f;
+  const float sg32 = (rib & 4) ? -1.f : 1.f;
+  float cmax[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint4& w4 = raw[k][j / 8];
+      const int jj = j % 8;
+      const uint32_t w = jj < 2 ? w4.x : jj < 4 ? w4.y : jj < 6 ? w4.z : w4.w;
+      x[k] = (jj & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+      if (h < G) {  // group sums: pairwise tree
+#pragma unroll
+        for (int k = 0; k < 8; k += 2 * h) x[k] = x[k] + x[k + h];
+      } else {      // full butterflies over the surviving group sums
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if ((k & h) == 0 && k % G == 0) {
+            const float p = x[k], q = x[k + h];
+            x[k] = p + q;
+            x[k + h] = p - q;
+          }
+      }
+    }
+    if constexpr (N >= 16) {
+#pragma unroll
+      for (int k = 0; k < 8; k += GL) x[k] = (8 < G) ? x[k] + lane_xor<8>(x[k]) : xbfly<8>(x[k], sg8);
+    }
+    if constexpr (N >= 32) {
+#pragma unroll
+      for (int k = 0; k < 8; k += GL) x[k] = (16 < G) ? x[k] + lane_xor<16>(x[k]) : xbfly<16>(x[k], sg16);
+    }
+    if constexpr (N >= 64) {
+#pragma unroll
+      for (int k = 0; k < 8; k += GL) x[k] = (32 < G) ? x[k] + lane_xor<32>(x[k]) : xbfly<32>(x[k], sg32);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k += GL) m = fmaxf(m, fabsf(x[k]));
+    cmax[j] = owner && act && cact ? m : 0.f;
+  }
+  // fold the eight row groups (lanes 8, 16, 32 apart)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float m = cmax[j];
+    m = fmaxf(m, lane_xor<8>(m));
+    m = fmaxf(m, lane_xor<16>(m));
+    m = fmaxf(m, lane_xor<32>(m));
+    cmax[j] = m;
+  }
+  if (lane < 8 && cact) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a.part_gyl[tr * a.O + c0 + col + j] = cmax[j];
+  }
+}
+
+// ---- job: x tile (ACBP codes, low-rank columns along T for g_w)
+template <int PASS, int N, int R>
+__device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
+  const int tid = threadIdx.x;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_i;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
+  const int64_t t0 = tr * TT, c0 = ch * CW;
+  const int rows = (int)(a.T - t0 < TT ? a.T - t0 : TT);
+  const int cols = (int)(a.I - c0 < CW ? a.I - c0 : CW);
+  uint8_t* codes = smem;                                          // [TT][P_I4] bytes
+  float* scales = reinterpret_cast<float*>(smem + TT * P_I4);     // [TT]
+  // 64 code bytes per tile row: 4 lanes x 16 bytes, 64 rows per sweep.  Rows
+  // are I/2 bytes (a multiple of 4, not of 16), so the loads are dwords.
+  constexpr int SW = TT / 64;
+  const int lr = tid >> 2, lq = tid & 3;
+  const int col = lq * 32;
+  uint32_t w4[SW][4];
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 64 + lr;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w4[sw][d] = 0u;
+    if (row < rows && col < cols) {
+      const uint32_t* src =
+          reinterpret_cast<const uint32_t*>(a.xc + (t0 + row) * (a.I / 2) + (c0 + col) / 2);
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        if (col + 8 * d < cols) w4[sw][d] = src[d];
+    }
+  }
+  if (tid < TT) scales[tid] = tid < rows ? a.xs[t0 + tid] : 0.f;
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw)
+    *reinterpret_cast<uint4*>(codes + (sw * 64 + lr) * P_I4 + col / 2) =
+        make_uint4(w4[sw][0], w4[sw][1], w4[sw][2], w4[sw][3]);
+  __syncthreads();
+  RdI4 rd{codes, scales};
+  colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_xl : nullptr, 3,
+                              a.part_xl + tr * a.I + c0, a.q_xl, a.kwb, a.tl, t0,
+                              t0 + rows == a.T);
+}
+
+// ---- job: w tile (full H_N along O, INT4 stored transposed for g_x)
+template <int PASS, int N, bool F32>
+__device__ void tr_job_w(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
+  const int tid = threadIdx.x;
+  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_i;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
+  const int64_t o0 = tr * TT, c0 = ch * CW;
+  const int rows = (int)(a.O - o0 < TT ? a.O - o0 : TT);
+  const int cols = (int)(a.I - c0 < CW ? a.I - c0 : CW);
+  constexpr int SW = TT / 16;
+  const int lr = tid >> 4, lc = tid & 15;
+  const int col = lc * 8;
+  Raw8 raw[SW];
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = sw * 16 + lr;
+    raw[sw].a = make_uint4(0, 0, 0, 0);
+    raw[sw].b = make_uint4(0, 0, 0, 0);
+    if (row < rows && col < cols) load_raw8(a.w, a.w_dt, (o0 + row) * a.I + c0 + col, raw[sw]);
+  }
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw) park8<F32>(smem, sw * 16 + lr, col, raw[sw], a.w_dt);
+  __syncthreads();
+  const bool last = o0 + rows == a.O;
+  if constexpr (F32) {
+    RdF32 rd{reinterpret_cast<const float*>(smem)};
+    colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.inv_w : nullptr, 1,
+                          a.part_w + tr * a.I + c0, a.q_w, a.kxb, o0, a.O, last);
+  } else {
+    RdB16 rd{reinterpret_cast<const uint16_t*>(smem)};
+    colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.inv_w : nullptr, 1,
+                          a.part_w + tr * a.I + c0, a.q_w, a.kxb, o0, a.O, last);
+  }
+}
+
+// F32: the g_y / w tiles hold fp32 (any fp32 source); otherwise bf16.
+template <int PASS, int N, int R, bool F32>
+__global__ __launch_bounds__(256) void k_tr(TrArgs a) {
+  static_assert(TT * P_I4 + TT * 4 <= TileSmem<F32>::bytes, "x tile fits the smem buffer");
+  static_assert(CW * OUT_PITCH <= TileSmem<F32>::bytes, "staging fits the smem buffer");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TileSmem<F32>::bytes];
+  __shared__ float red[4 * CW];
+  if (blockIdx.x == 0 && threadIdx.x < 4) {
+    if constexpr (PASS == PASS_MAX) {
+      a.tmax[threadIdx.x] = 0u;  // k_tr_reduce folds into it
+    } else {  // tensor scales of the per-tensor modes
+      const int l = threadIdx.x;
+      const float qmax = l < 2 ? 7.f : 127.f;
+      if (l < 2 ? !a.gx_tok : !a.gw_tok) {
+        float* sc = l == 0 ? a.s_gy : l == 1 ? a.s_w : l == 2 ? a.s_gyl : a.s_xl;
+        sc[0] = scale_of(__uint_as_float(a.tmax[l]), qmax);
+      }
+    }
+  }
+  // Workgroup -> job: consecutive ids go to the 8 XCDs in turn; slot s of an
+  // XCD walks that XCD's eighth of each job list in the order register g_y,
+  // LDS g_y, x, w (longest tiles first).  Every XCD gets the same mix of
+  // jobs, and within a job list a contiguous range of tiles.
+  const int64_t xcd = blockIdx.x % 8;
+  int64_t slot = blockIdx.x / 8;
+  const int64_t per_r = (a.gyreg_wgs + 7) / 8, per_g = (a.gy_workers + 7) / 8;
+  const int64_t per_x = (a.wg_x + 7) / 8, per_w = (a.wg_w + 7) / 8;
+  if constexpr (PASS == PASS_MAX && N <= 64) {
+    // register-resident g_y tiles: four independent waves, one tile each
+    if (slot < per_r) {
+      const int64_t bid = xcd * per_r + slot;
+      const int64_t tile = bid * 4 + (threadIdx.x >> 6);
+      if (bid < a.gyreg_wgs && tile < a.wg_gy) {
+        uint4 raw[8][2];
+        gyr_load(a, tile, raw);
+        gyr_tile_max<N, R>(a, tile, raw);
+      }
+      return;
+    }
+  }
+  slot -= per_r;
+  if (slot < per_g) {  // g_y tiles on the LDS engine
+    const int64_t bid = xcd * per_g + slot;
+    if (bid < a.gy_workers) tr_job_gy<PASS, N, R, F32>(a, bid, smem, red);
+    return;
+  }
+  slot -= per_g;
+  if (slot < per_x) {
+    const int64_t bid = xcd * per_x + slot;
+    if (bid < a.wg_x) tr_job_x<PASS, N, R>(a, bid, smem, red);
+    return;
+  }
+  slot -= per_x;
+  if (slot < per_w) {
+    const int64_t bid = xcd * per_w + slot;
+    if (bid < a.wg_w) tr_job_w<PASS, N, F32>(a, bid, smem, red);
+  }
+}
+
+// Fold the partial maxima.  Entry e of each list takes the max over its
+// partials; per-token modes store its scale and reciprocal scale (the QUANT
+// pass multiplies by the latter).  Every block folds its per-list maxima into
+// the four tensor maxima with one atomicMax each (lists: 0 H.g_y rows, 1 H.w
+// columns, 2 low-rank g_y columns, 3 low-rank x columns).  Max is exact and
+// commutes, so the result does not depend on the schedule.  A block covers 64 consecutive entries; its 16
+// waves split each entry's partials (stride 16) so every wave keeps several
+// loads in flight.
+constexpr int RED_ENTRIES = TR_RED_ENTRIES;
+constexpr int RED_WAVES = 16;
+
+#if HLQ_TR_N == 16
+__global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
+  __shared__ float wpart[RED_WAVES][RED_ENTRIES];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t e = (int64_t)blockIdx.x * RED_ENTRIES + lane;
+  const int64_t n0 = a.T, n1 = n0 + a.O, n2 = n1 + a.I, n3 = n2 + a.I;
+  const float* p = nullptr;
+  int64_t np = 0, stride = 0;
+  int list = -1;
+  if (e < n0) { list = 0; p = a.part_gy + e; np = a.nch_o; stride = a.T; }
+  else if (e < n1) { list = 2; p = a.part_gyl + (e - n0); np = a.ntr_gy; stride = a.O; }
+  else if (e < n2) { list = 3; p = a.part_xl + (e - n1); np = a.ntr_t; stride = a.I; }
+  else if (e < n3) { list = 1; p = a.part_w + (e - n2); np = a.ntr_o; stride = a.I; }
+  // wave wv folds partials wv, wv + 16, ...; four loads in flight per step
+  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+  int64_t k = wv;
+  constexpr int W = RED_WAVES;
+  for (; k + 3 * W < np; k += 4 * W) {
+    m0 = fmaxf(m0, p[k * stride]);
+    m1 = fmaxf(m1, p[(k + W) * stride]);
+    m2 = fmaxf(m2, p[(k + 2 * W) * stride]);
+    m3 = fmaxf(m3, p[(k + 3 * W) * stride]);
+  }
+  for (; k < np; k += W) m0 = fmaxf(m0, p[k * stride]);
+  wpart[wv][lane] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  __syncthreads();
+  if (wv == 0) {
+  float m = wpart[0][lane];
+#pragma unroll
+  for (int q = 1; q < RED_WAVES; ++q) m = fmaxf(m, wpart[q][lane]);
+  if (list == 0) {
+    if (a.gx_tok) { a.inv_gy[e] = inv_of(m, 7.f); a.s_gy[e] = scale_of(m, 7.f); }
+  } else if (list == 2) {
+    if (a.gw_tok) { a.inv_gyl[e - n0] = inv_of(m, 127.f); a.s_gyl[e - n0] = scale_of(m, 127.f); }
+  } else if (list == 3) {
+    if (a.gw_tok) { a.inv_xl[e - n1] = inv_of(m, 127.f); a.s_xl[e - n1] = scale_of(m, 127.f); }
+  } else if (list == 1) {
+    if (a.gx_tok) { a.inv_w[e - n2] = inv_of(m, 7.f); a.s_w[e - n2] = scale_of(m, 7.f); }
+  }
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    // tensor maxima: max over blocks by atomicMax on the bit patterns of
+    // non-negative floats (they order like the values), exact and
+    // schedule-independent; zeroed by the MAX pass
+    const float v = wave_max(list == l ? m : 0.f);
+    if (lane == 0 && v > 0.f) atomicMax(a.tmax + l, __float_as_uint(v));
+  }
+  }
+}
+#endif
+
+// One object per block size n: the build compiles this file with
+// HLQ_TR_N = 16, 32, 64 and 128 (the k_tr instantiations dominate the build
+// time).  The object of n = 16 also holds the generic launchers.
+#ifndef HLQ_TR_N
+#error "compile hlq_tr.hip with -DHLQ_TR_N=16, 32, 64 or 128"
+#endif
+#define HLQ_CAT2(a, b) a##b
+#define HLQ_CAT(a, b) HLQ_CAT2(a, b)
+
+template <int PASS, bool F32>
+static hipError_t tr_dispatch(int r, dim3 g, hipStream_t s, const TrArgs& a) {
+  constexpr int NN = HLQ_TR_N;
+#define HLQ_TR(RR) hipLaunchKernelGGL((k_tr<PASS, NN, RR, F32>), g, dim3(256), 0, s, a)
+  switch (r) {
+    case 1: HLQ_TR(1); break;
+    case 2: HLQ_TR(2); break;
+    case 4: HLQ_TR(4); break;
+    case 8: HLQ_TR(8); break;
+    case 16: HLQ_TR(16); break;
+    case 32: if constexpr (NN >= 32) { HLQ_TR((NN >= 32 ? 32 : 1)); break; } else return hipErrorInvalidValue;
+    case 64: if constexpr (NN >= 64) { HLQ_TR((NN >= 64 ? 64 : 1)); break; } else return hipErrorInvalidValue;
+    case 128: if constexpr (NN >= 128) { HLQ_TR((NN >= 128 ? 128 : 1)); break; } else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+#undef HLQ_TR
+  return hipGetLastError();
+}
+
+hipError_t HLQ_CAT(launch_tr_n, HLQ_TR_N)(const TrArgs& a, int pass, int r, dim3 g, hipStream_t s) {
+  const bool f32 = a.gy_dt == 0 || a.w_dt == 0;
+  if (pass == PASS_MAX)
+    return f32 ? tr_dispatch<PASS_MAX, true>(r, g, s, a) : tr_dispatch<PASS_MAX, false>(r, g, s, a);
+  return f32 ? tr_dispatch<PASS_QUANT, true>(r, g, s, a) : tr_dispatch<PASS_QUANT, false>(r, g, s, a);
+}
+
+#if HLQ_TR_N == 16
+hipError_t launch_tr(const TrArgs& args, int pass, int n, int r, hipStream_t s) {
+  if (r > n) return hipErrorInvalidValue;
+  TrArgs a = args;
+  // g_y tiles: the LDS engine's, except in the MAX pass of the register path,
+  // where workgroups of four register-resident waves take them
+  a.gy_workers = a.ntr_t * a.nch_o;
+  a.gyreg_wgs = 0;
+  if (pass == PASS_MAX && a.gy_reg) {
+    if (a.gy_dt != 1 || n > 64) return hipErrorInvalidValue;
+    a.gy_workers = 0;
+    a.gyreg_wgs = (a.wg_gy + 3) / 4;
+  }
+  // eight slots per XCD row: each XCD takes an eighth of every job list
+  const int64_t slots = (a.gyreg_wgs + 7) / 8 + (a.gy_workers + 7) / 8 + (a.wg_x + 7) / 8 +
+                        (a.wg_w + 7) / 8;
+  if (slots <= 0) return hipSuccess;
+  dim3 g((unsigned)(slots * 8));
+  switch (n) {
+    case 16: return launch_tr_n16(a, pass, r, g, s);
+    case 32: return launch_tr_n32(a, pass, r, g, s);
+    case 64: return launch_tr_n64(a, pass, r, g, s);
+    case 128: return launch_tr_n128(a, pass, r, g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_tr_reduce(const TrArgs& a, hipStream_t s) {
+  if (a.nred != (int64_t)cdiv(a.T + a.O + 2 * a.I, RED_ENTRIES)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tr_reduce, dim3((unsigned)a.nred), dim3(64 * RED_WAVES), 0, s, a);
+  return hipGetLastError();
+}
+#endif
+
+}  // namespace hlq

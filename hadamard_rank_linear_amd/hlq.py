@@ -25,6 +25,7 @@ EXPORTED = (
     "hlq_linear_backward",
     "hlq_linear_backward_steps",
     "hlq_workspace_layout_query",
+    "hlq_gemm_pair_acc",
     "hlq_gemm_gx_acc",
     "hlq_gemm_gw_acc",
     "hlq_lqs_workspace_size",
@@ -70,9 +71,11 @@ def _load():
     lib.hlq_workspace_layout_query.argtypes = [I64, I64, I64, I32, I32,
                                                ctypes.POINTER(WorkspaceLayout)]
     lib.hlq_workspace_layout_query.restype = I32
-    lib.hlq_gemm_gx_acc.argtypes = [P, I64, I64, I64, I32, I32, P, P]
+    lib.hlq_gemm_pair_acc.argtypes = [P, SZ, I64, I64, I64, I32, I32, P, P, P]
+    lib.hlq_gemm_pair_acc.restype = I32
+    lib.hlq_gemm_gx_acc.argtypes = [P, SZ, I64, I64, I64, I32, I32, P, P]
     lib.hlq_gemm_gx_acc.restype = I32
-    lib.hlq_gemm_gw_acc.argtypes = [P, I64, I64, I64, I32, I32, P, P]
+    lib.hlq_gemm_gw_acc.argtypes = [P, SZ, I64, I64, I64, I32, I32, P, P]
     lib.hlq_gemm_gw_acc.restype = I32
     lib.hlq_lqs_workspace_size.argtypes = [I64, I64, I64, I32, I32]
     lib.hlq_lqs_workspace_size.restype = SZ
@@ -118,12 +121,29 @@ def _dtype_code(t) -> int:
 
 
 def _require_cuda(*ts):
+    dev = None
     for t in ts:
         if t is not None:
             if not t.is_cuda:
                 raise ValueError("tensors must live on the GPU")
             if not t.is_contiguous():
                 raise ValueError("tensors must be contiguous")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+
+
+def _expect(name, t, dtype, shape):
+    """Caller-supplied buffer check: dtype and shape the kernels assume."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
 
 def version() -> int:
@@ -142,6 +162,8 @@ def hlq_compress_act(x, x_codes=None, x_scales=None, stream=None):
         x_codes = torch.empty((T, I // 2), dtype=torch.uint8, device=x.device)
     if x_scales is None:
         x_scales = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _expect("x_codes", x_codes, torch.uint8, (T, I // 2))
+    _expect("x_scales", x_scales, torch.float32, (T,))
     _require_cuda(x, x_codes, x_scales)
     _check("hlq_compress_act", _lib.hlq_compress_act(
         _ptr(x), _dtype_code(x), T, I, _ptr(x_codes), _ptr(x_scales), _stream(stream)))
@@ -183,10 +205,16 @@ def hlq_linear_backward(g_y, x_codes, x_scales, w, block, rank,
     need = hlq_linear_backward_workspace_size(T, I, O, block, rank)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _expect("x_codes", x_codes, torch.uint8, (T, I // 2))
+    _expect("x_scales", x_scales, torch.float32, (T,))
+    _expect("g_x", g_x, torch.float32, (T, I))
+    _expect("g_w", g_w, torch.float32, (O, I))
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
     _require_cuda(g_y, x_codes, x_scales, w, g_x, g_w, workspace)
     args = (_ptr(g_y), _dtype_code(g_y), _ptr(x_codes), _ptr(x_scales), _ptr(w),
             _dtype_code(w), T, I, O, block, rank, gx_mode, gw_mode, reduction, _ptr(g_x),
-            _ptr(g_w), _ptr(workspace), workspace.numel() * workspace.element_size())
+            _ptr(g_w), _ptr(workspace), _nbytes(workspace))
     if steps is None:
         _check("hlq_linear_backward", _lib.hlq_linear_backward(*args, _stream(stream)))
     else:
@@ -195,23 +223,39 @@ def hlq_linear_backward(g_y, x_codes, x_scales, w, block, rank,
     return g_x, g_w
 
 
-def hlq_gemm_gx_acc(workspace, T, I, O, block, rank, acc_x=None, stream=None):
+def _acc_out(workspace, t, shape):
     import torch
-    if acc_x is None:
-        acc_x = torch.empty((T, I), dtype=torch.int32, device=workspace.device)
+    if t is None:
+        t = torch.empty(shape, dtype=torch.int32, device=workspace.device)
+    _expect("accumulator", t, torch.int32, shape)
+    return t
+
+
+def hlq_gemm_pair_acc(workspace, T, I, O, block, rank, acc_x=None, acc_w=None, stream=None):
+    """INT32 accumulators (acc_x [T, I], acc_w [O, I]) of the one GEMM launch
+    hlq_linear_backward runs, from a workspace it has filled."""
+    acc_x = _acc_out(workspace, acc_x, (T, I))
+    acc_w = _acc_out(workspace, acc_w, (O, I))
+    _require_cuda(workspace, acc_x, acc_w)
+    _check("hlq_gemm_pair_acc", _lib.hlq_gemm_pair_acc(
+        _ptr(workspace), _nbytes(workspace), T, I, O, block, rank, _ptr(acc_x), _ptr(acc_w),
+        _stream(stream)))
+    return acc_x, acc_w
+
+
+def hlq_gemm_gx_acc(workspace, T, I, O, block, rank, acc_x=None, stream=None):
+    acc_x = _acc_out(workspace, acc_x, (T, I))
     _require_cuda(workspace, acc_x)
     _check("hlq_gemm_gx_acc", _lib.hlq_gemm_gx_acc(
-        _ptr(workspace), T, I, O, block, rank, _ptr(acc_x), _stream(stream)))
+        _ptr(workspace), _nbytes(workspace), T, I, O, block, rank, _ptr(acc_x), _stream(stream)))
     return acc_x
 
 
 def hlq_gemm_gw_acc(workspace, T, I, O, block, rank, acc_w=None, stream=None):
-    import torch
-    if acc_w is None:
-        acc_w = torch.empty((O, I), dtype=torch.int32, device=workspace.device)
+    acc_w = _acc_out(workspace, acc_w, (O, I))
     _require_cuda(workspace, acc_w)
     _check("hlq_gemm_gw_acc", _lib.hlq_gemm_gw_acc(
-        _ptr(workspace), T, I, O, block, rank, _ptr(acc_w), _stream(stream)))
+        _ptr(workspace), _nbytes(workspace), T, I, O, block, rank, _ptr(acc_w), _stream(stream)))
     return acc_w
 
 
@@ -241,11 +285,15 @@ def hlq_lqs_accumulate(g_y, x_codes, x_scales, w, block, rank, stats=None, works
     need = hlq_lqs_workspace_size(T, I, O, block, rank)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _expect("x_codes", x_codes, torch.uint8, (T, I // 2))
+    _expect("x_scales", x_scales, torch.float32, (T,))
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
     _require_cuda(g_y, x_codes, x_scales, w, stats, workspace)
     _check("hlq_lqs_accumulate", _lib.hlq_lqs_accumulate(
         _ptr(g_y), _dtype_code(g_y), _ptr(x_codes), _ptr(x_scales), _ptr(w), _dtype_code(w),
         T, I, O, block, rank, _ptr(stats), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        _nbytes(workspace), _stream(stream)))
     return stats
 
 

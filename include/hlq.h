@@ -182,17 +182,28 @@ hlq_status hlq_workspace_layout_query(int64_t T, int64_t I, int64_t O, int block
                                       int rank, hlq_workspace_layout* out);
 
 /*
- * INT32 accumulators of the two integer GEMMs, recomputed by the same GEMM
- * kernels from a workspace that hlq_linear_backward has filled (tests and
- * diagnostics).  acc_x [T][I] = sum_o q_gy[t,o] q_w[o,i];
+ * INT32 accumulators of the two integer GEMMs, recomputed from a workspace
+ * that hlq_linear_backward has filled (tests and diagnostics; HLQ TL;DR:
+ * "int8-accelerated" products).  acc_x [T][I] = sum_o q_gy[t,o] q_w[o,i];
  * acc_w [O][I] = sum_t' q_gyl[t',o] q_xl[t',i].
+ *   hlq_gemm_pair_acc: the one launch hlq_linear_backward runs for both
+ *     GEMMs (same tile grids and schedule), its epilogue storing the INT32
+ *     sums instead of the fp32 gradients.
+ *   hlq_gemm_gx_acc / hlq_gemm_gw_acc: the single-GEMM launches that
+ *     hlq_linear_backward_steps runs when only one GEMM step is selected.
+ * workspace_bytes is checked against hlq_linear_backward_workspace_size
+ * (HLQ_ERR_WORKSPACE); acc_* are device buffers of the sizes above.
  */
-hlq_status hlq_gemm_gx_acc(const void* workspace, int64_t T, int64_t I, int64_t O,
-                           int block, int rank, int32_t* acc_x, void* stream);
-hlq_status hlq_gemm_gw_acc(const void* workspace, int64_t T, int64_t I, int64_t O,
-                           int block, int rank, int32_t* acc_w, void* stream);
+hlq_status hlq_gemm_pair_acc(const void* workspace, size_t workspace_bytes, int64_t T,
+                             int64_t I, int64_t O, int block, int rank, int32_t* acc_x,
+                             int32_t* acc_w, void* stream);
+hlq_status hlq_gemm_gx_acc(const void* workspace, size_t workspace_bytes, int64_t T,
+                           int64_t I, int64_t O, int block, int rank, int32_t* acc_x,
+                           void* stream);
+hlq_status hlq_gemm_gw_acc(const void* workspace, size_t workspace_bytes, int64_t T,
+                           int64_t I, int64_t O, int block, int rank, int32_t* acc_w,
+                           void* stream);
 
-/* Static text for a status code. */
 /*
  * Layer-wise quantizer selection (LQS).  "HOT: Hadamard-based Optimized
  * Training": HF page abstract (layer-wise quantizer selection), scime.ai
@@ -240,6 +251,7 @@ hlq_status hlq_lqs_accumulate(const void* g_y, int gy_dtype, const uint8_t* x_co
 hlq_status hlq_lqs_select(const double* stats, double threshold, int* gx_mode,
                           int* gw_mode);
 
+/* Static text for a status code (never NULL). */
 const char* hlq_status_string(int status);
 
 /* Library ABI version (major*100 + minor). */

@@ -440,12 +440,25 @@ def rel_fro(a, b) -> float:
     return float(num / den)
 
 
+def max_rel_err(a, b, tiny: float) -> float:
+    """max_i |a_i - b_i| / max(|b_i|, tiny) in fp64: the element-wise relative
+    error, measured absolutely (in units of ``tiny``) where the reference is
+    below ``tiny``.  0 for empty arrays."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        raise ValueError("shapes differ")
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), float(tiny))))
+
+
 __all__ = [
     "PER_TOKEN", "PER_TENSOR", "SUM", "MEAN", "QMAX_INT4", "QMAX_INT8",
     "bf16_bits_to_f32",
     "sylvester_hadamard", "fwht_blocks", "lowrank_rows", "sequency",
     "lowrank_transform", "quantize", "pack_int4", "unpack_int4", "acbp_pack",
     "acbp_unpack", "int_matmul", "linear_backward",
-    "linear_backward_unquantized", "rel_fro", "LQS_THRESHOLD", "LQS_OPERANDS",
+    "linear_backward_unquantized", "rel_fro", "max_rel_err", "LQS_THRESHOLD", "LQS_OPERANDS",
     "lqs_operands", "quant_sq_error", "lqs_stats", "lqs_path_errors", "lqs_select",
 ]

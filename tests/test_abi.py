@@ -179,3 +179,33 @@ def test_lqs_accumulate_validates_before_launch(kw, status):
         "gy", "gy_dt", "codes", "scales", "w", "w_dt", "T", "I", "O", "block", "rank",
         "stats", "ws", "ws_bytes", "stream")))
     assert got == status
+
+
+@pytest.mark.parametrize("fn", ["hlq_gemm_pair_acc", "hlq_gemm_gx_acc", "hlq_gemm_gw_acc"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), 1), (dict(acc=None), 1), (dict(T=72), 2), (dict(block=24), 3),
+    (dict(rank=3), 4), (dict(ws_bytes=100), 9), (dict(acc=(1 << 20) + 4), 7),
+])
+def test_accumulator_exports_validate_before_launch(fn, kw, status):
+    # the INT32 exports check the caller's workspace size like the backward
+    args = dict(ws=1 << 20, ws_bytes=1 << 40, T=64, I=40, O=48, block=16, rank=8,
+                acc=1 << 20, stream=None)
+    args.update(kw)
+    lib = h.lib_handle()
+    head = [args[k] for k in ("ws", "ws_bytes", "T", "I", "O", "block", "rank")]
+    if fn == "hlq_gemm_pair_acc":
+        got = lib.hlq_gemm_pair_acc(*head, args["acc"], 1 << 21, args["stream"])
+    else:
+        got = getattr(lib, fn)(*head, args["acc"], args["stream"])
+    assert got == status
+
+
+def test_binding_checks_caller_buffers():
+    # dtype / shape of caller-supplied buffers are checked before any call
+    import torch
+    x = torch.zeros((16, 8))
+    with pytest.raises(TypeError):
+        h.hlq_compress_act(x, x_codes=torch.zeros((16, 4)), x_scales=torch.zeros(16))
+    with pytest.raises(ValueError):
+        h.hlq_compress_act(x, x_codes=torch.zeros((16, 8), dtype=torch.uint8),
+                           x_scales=torch.zeros(16))

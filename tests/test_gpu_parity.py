@@ -206,3 +206,96 @@ def test_mixed_input_dtypes(gy_dt, w_dt):
     assert o.rel_fro(g_w.cpu().numpy(), ref["g_w"]) <= 1e-5
     ost = o.lqs_stats(gy32, codes, scales, w32, cfg.block, cfg.rank)
     np.testing.assert_allclose(stats.cpu().numpy(), ost, rtol=1e-9, atol=0)
+
+
+# ----------------------------------------------- exact quantizer ties
+
+def _tie_count(v, inv):
+    """Elements whose fl32(v * inv) lies exactly halfway between integers."""
+    p = (np.asarray(v, np.float32) * np.asarray(inv, np.float32)).astype(np.float32)
+    return int(np.count_nonzero(p - np.floor(p) == np.float32(0.5)))
+
+
+def _odd_with_max(rng, shape, peak, axis):
+    """Odd integers in [-(peak-1), peak-1] with one entry +-peak (even) per
+    line along `axis`: the group maximum is peak, every other entry odd."""
+    u = 2 * rng.integers(-(peak // 2), peak // 2, shape) + 1
+    u = np.moveaxis(u, axis, -1)
+    idx = rng.integers(0, u.shape[-1], u.shape[:-1])
+    np.put_along_axis(u, idx[..., None], peak * rng.choice([-1, 1], u.shape[:-1])[..., None], -1)
+    return np.moveaxis(u, -1, axis).astype(np.float64)
+
+
+@pytest.mark.parametrize("dt,T,I,O", [(wl.F32, 64, 64, 64), (wl.BF16, 256, 128, 256)])
+@pytest.mark.parametrize("gx_mode", [0, 1])
+def test_quantizer_ties_gx_path(dt, T, I, O, gx_mode):
+    # Transformed g_y rows and w columns are odd integers with group maximum
+    # 14, so inv = fl(7 / 14) = 0.5 and every odd value lands on k + 1/2:
+    # round half to even decides most INT4 codes.  g_y = H u / 16 per block
+    # (multiples of 1/16 below 16, exact in bf16 and fp32), so the fp32
+    # butterflies give back u exactly.
+    n = 16
+    rng = np.random.default_rng(21)
+    H = o.sylvester_hadamard(n).astype(np.float64)
+    u_gy = _odd_with_max(rng, (T, O), 14, axis=1)
+    u_w = _odd_with_max(rng, (O, I), 14, axis=0)
+    gy = np.concatenate([u_gy[:, b:b + n] @ H / n for b in range(0, O, n)], axis=1)
+    w = np.concatenate([H @ u_w[b:b + n] / n for b in range(0, O, n)], axis=0)
+    cfg = dataclasses.replace(wl.BY_NAME["tiny"], T=T, I=I, O=O, block=n, rank=8, dtype=dt,
+                              gx_mode=gx_mode, gw_mode=0, index=77)
+    inp = wl.make_inputs(cfg, seed=5)
+    to_store = (lambda a: a.astype(np.float32)) if dt == wl.F32 else \
+        (lambda a: wl.f32_to_bf16_bits(a.astype(np.float32)))
+    inp = dict(inp, gy=to_store(gy), w=to_store(w))
+    _say(f"quantizer ties on the g_x path dtype={dt} T={T} I={I} O={O} gx_mode={gx_mode}")
+    ocodes, oscales, ref = run_oracle(cfg, inp)
+    gy_h = o.fwht_blocks(gy.astype(np.float32), n, 1)
+    assert np.array_equal(gy_h, u_gy.astype(np.float32))
+    ties = _tie_count(gy_h, 0.5) + _tie_count(o.fwht_blocks(w.astype(np.float32), n, 0), 0.5)
+    assert ties > (T * O + O * I) // 2, "the inputs should plant exact ties"
+    gpu = run_gpu(cfg, inp, x_codes=ocodes, x_scales=oscales)
+    compare(cfg, gpu, ocodes, oscales, ref)
+
+
+def test_quantizer_ties_gw_path():
+    # rank 1: the low-rank value of a block is its plain sum.  g_y block sums
+    # are odd with column maximum 254 (inv = fl(127 / 254) = 0.5: every odd
+    # sum is a tie); x decodes with scale 127/32 and its block code sums are
+    # +-64 (low-rank value +-254, the column maximum: inv 0.5) or +-32
+    # (low-rank value +-127, times 0.5 exactly +-63.5): ties again.
+    n, T, I, O = 16, 128, 32, 32
+    nb = T // n
+    rng = np.random.default_rng(22)
+    cfg = dataclasses.replace(wl.BY_NAME["tiny"], T=T, I=I, O=O, block=n, rank=1, dtype=wl.F32,
+                              gx_mode=0, gw_mode=0, index=78)
+    inp = wl.make_inputs(cfg, seed=6)
+    sums = _odd_with_max(rng, (nb, O), 254, axis=0)
+    gy = rng.integers(-20, 21, (T, O)).astype(np.float64)
+    for b in range(nb):
+        gy[b * n + n - 1] = sums[b] - gy[b * n:b * n + n - 1].sum(axis=0)
+    q = np.zeros((T, I), np.int64)
+    for i in range(I):
+        targets = rng.choice([-32, 32, -32, 32, 5, -11], nb)
+        targets[rng.integers(0, nb)] = 64 * rng.choice([-1, 1])
+        for b in range(nb):
+            left, k = int(targets[b]), b * n
+            sgn = 1 if left >= 0 else -1
+            while left != 0:
+                step = sgn * min(7, abs(left))
+                q[k, i] = step
+                left -= step
+                k += 1
+    codes = o.pack_int4(q)
+    scales = np.full(T, 127.0 / 32.0, np.float32)
+    inp = dict(inp, gy=gy.astype(np.float32))
+    _say(f"quantizer ties on the g_w path T={T} I={I} O={O} n={n} r=1")
+    ref = o.linear_backward(inp["gy"], codes, scales, inp["w"], n, 1, 0, 0, cfg.reduction)
+    gyl = o.lowrank_transform(inp["gy"], n, 1, 0)
+    xl = o.lowrank_transform(o.acbp_unpack(codes, scales), n, 1, 0)
+    assert np.array_equal(gyl, sums.astype(np.float32))
+    assert (np.abs(xl).max(axis=0) == 254).all()
+    ties = _tie_count(gyl, 0.5) + _tie_count(xl, 0.5)
+    assert ties >= nb * O // 2, "the inputs should plant exact ties"
+    gpu = run_gpu(cfg, inp, x_codes=codes, x_scales=scales)
+    ocodes, oscales = o.acbp_pack(inp["x"])   # run_gpu also packs inp["x"]
+    compare(cfg, gpu, ocodes, oscales, ref)

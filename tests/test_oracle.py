@@ -384,7 +384,12 @@ def test_per_tensor_equals_per_token_when_absmax_shared():
     assert a2["s_gy"].shape == (1,)
     assert np.array_equal(a1["q_gy"], a2["q_gy"])
     assert (a1["s_gy"] == a2["s_gy"][0]).all()
-    assert not np.array_equal(a1["q_w"], a2["q_w"]) or a2["s_w"].shape == (1,)
+    # the per-tensor scale of H.w is the largest per-column one (fl(a / 7) is
+    # monotone in a), and its codes are the brute-force quantizer's with it
+    assert a2["s_w"].shape == (1,) and a2["s_w"][0] == a1["s_w"].max()
+    w_h = o.fwht_blocks(w, n, 0)
+    bq, bs = _brute_quant(w_h.ravel(), 7)
+    assert np.array_equal(a2["q_w"].ravel(), np.array(bq)) and float(a2["s_w"][0]) == bs
 
 
 def test_quantized_close_to_exact_product():
@@ -423,3 +428,65 @@ def test_bf16_widening_exact():
     assert got[4] == np.float32(2.0 ** -133)
     assert wl.f32_to_bf16_bits(np.array([1.0, 1.00390625, 1.01171875], np.float32)).tolist() == [
         0x3F80, 0x3F80, 0x3F82]   # ties to even: 1+2^-8 -> 1, 1+3*2^-8 -> 1+2^-6
+
+
+def test_quantized_path_per_tensor_follows_explicit_matrix():
+    # both paths PER_TENSOR: every operand's codes from one scale (the
+    # brute-force quantizer over the whole explicit-matrix transform), integer
+    # GEMMs by brute force, the fp64 epilogue with the two tensor scales;
+    # catches a per-tensor scale taken over the wrong operand or a per-token
+    # scale left in one of the epilogues
+    rng = np.random.default_rng(5)
+    n, r, T, I, O = 16, 4, 64, 10, 32
+    gy = rng.integers(-30, 31, (T, O)).astype(np.float32)
+    w = rng.integers(-30, 31, (O, I)).astype(np.float32)
+    xq = rng.integers(-7, 8, (T, I))
+    x_codes = o.pack_int4(xq)
+    x_scales = np.ones(T, np.float32)
+    out = o.linear_backward(gy, x_codes, x_scales, w, n, r, o.PER_TENSOR, o.PER_TENSOR)
+    H = kron_hadamard(n)
+    gy_h = np.concatenate([gy[:, b:b + n] @ H.T for b in range(0, O, n)], axis=1)
+    w_h = np.concatenate([H @ w[b:b + n] for b in range(0, O, n)], axis=0)
+    Hl = H[o.lowrank_rows(n, r)]
+    gyl = np.concatenate([Hl @ gy[b:b + n] for b in range(0, T, n)], axis=0)
+    xl = np.concatenate([Hl @ xq[b:b + n] for b in range(0, T, n)], axis=0)
+    for key, v, qmax in (("gy", gy_h, 7), ("w", w_h, 7), ("gyl", gyl, 127), ("xl", xl, 127)):
+        bq, bs = _brute_quant(v.astype(np.float32).ravel(), qmax)
+        assert out["s_" + key].shape == (1,)
+        assert float(out["s_" + key][0]) == bs, key
+        assert np.array_equal(out["q_" + key].ravel(), np.array(bq)), key
+    sg, sw = float(out["s_gy"][0]), float(out["s_w"][0])
+    sgl, sxl = float(out["s_gyl"][0]), float(out["s_xl"][0])
+    Tl = T * r // n
+    for t, i in ((0, 0), (17, 9), (63, 4)):
+        acc = sum(int(out["q_gy"][t, k]) * int(out["q_w"][k, i]) for k in range(O))
+        assert out["acc_x"][t, i] == acc
+        assert out["g_x"][t, i] == np.float32(acc * sg * sw / n)
+    for c, i in ((0, 0), (31, 5), (12, 9)):
+        acc = sum(int(out["q_gyl"][k, c]) * int(out["q_xl"][k, i]) for k in range(Tl))
+        assert out["acc_w"][c, i] == acc
+        assert out["g_w"][c, i] == np.float32(acc * sgl * sxl / n)
+
+
+def test_rel_fro_golden():
+    g = GOLDEN["rel_fro_2x2"]
+    assert o.rel_fro(np.array(g["a"]), np.array(g["b"])) == pytest.approx(g["value"], rel=1e-15)
+    assert o.rel_fro(np.zeros(3), np.zeros(3)) == 0.0
+    assert o.rel_fro(np.ones(3), np.zeros(3)) == float("inf")
+
+
+def test_max_rel_err_golden():
+    g = GOLDEN["max_rel_err"]
+    assert o.max_rel_err(g["a1"], g["b1"], g["tiny1"]) == pytest.approx(g["value1"], rel=1e-15)
+    assert o.max_rel_err(g["a2"], g["b2"], g["tiny2"]) == pytest.approx(g["value2"], rel=1e-15)
+    assert o.max_rel_err(np.zeros(0), np.zeros(0), 1.0) == 0.0
+
+
+def test_acbp_unpack_rounds_once_to_fp32():
+    # a scale that is not a power of two: fl32(s * q) differs from the exact
+    # product, so an unrounded (fp64) or twice-rounded decode fails
+    g = GOLDEN["acbp_unpack_non_power_of_two"]
+    s = np.array([int(g["scale_bits"], 16)], np.uint32).view(np.float32)
+    got = o.acbp_unpack(np.array([g["bytes"]], np.uint8), s)
+    assert got.dtype == np.float32 and got.shape == (1, 2)
+    assert [hex(v) for v in got.view(np.uint32).ravel()] == [b.lower() for b in g["output_bits"]]
