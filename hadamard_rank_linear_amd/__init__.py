@@ -11,7 +11,8 @@ import importlib
 
 _BINDING_NAMES = {
     "hlq_compress_act", "hlq_linear_backward", "hlq_linear_backward_workspace_size",
-    "hlq_workspace_layout_query", "hlq_gemm_pair_acc", "hlq_gemm_gx_acc", "hlq_gemm_gw_acc", "HLQError",
+    "hlq_workspace_layout_query", "hlq_linear_backward_noalloc", "HLQ_NOALLOC_SCRATCH_BYTES",
+    "hlq_gemm_pair_acc", "hlq_gemm_gx_acc", "hlq_gemm_gw_acc", "HLQError",
     "HLQ_F32", "HLQ_BF16", "HLQ_PER_TOKEN", "HLQ_PER_TENSOR", "HLQ_SUM", "HLQ_MEAN",
     "version", "status_string", "lib_handle", "LIB_PATH", "EXPORTED", "STEP_NAMES",
     "HLQ_STEPS_ALL", "hlq_lqs_workspace_size", "hlq_lqs_accumulate", "hlq_lqs_select",

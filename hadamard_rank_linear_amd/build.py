@@ -16,7 +16,8 @@ LIB = os.path.join(HERE, "libhlq.so")
 # (source, object, extra flags): the transform kernels build once per block size
 SOURCES = [("hlq_tr.hip", f"hlq_tr{n}", [f"-DHLQ_TR_N={n}"]) for n in (16, 32, 64, 128)] + [
     ("hlq_gemm.hip", "hlq_gemm", []), ("hlq_lqs.hip", "hlq_lqs", []),
-    ("hlq_acbp.hip", "hlq_acbp", []), ("hlq_api.cpp", "hlq_api", [])]
+    ("hlq_acbp.hip", "hlq_acbp", []), ("hlq_noalloc.hip", "hlq_noalloc", []),
+    ("hlq_api.cpp", "hlq_api", [])]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -231,13 +231,12 @@ hlq_status hlq_workspace_layout_query(int64_t T, int64_t I, int64_t O, int block
   return HLQ_OK;
 }
 
-hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
-                                     const uint8_t* x_codes, const float* x_scales,
-                                     const void* w, int w_dtype, int64_t T, int64_t I,
-                                     int64_t O, int block, int rank, int gx_mode,
-                                     int gw_mode, int reduction, float* g_x, float* g_w,
-                                     void* workspace, size_t workspace_bytes,
-                                     uint32_t step_mask, void* stream) {
+// Argument checks shared by the backward's entry points (everything but the
+// workspace).
+static hlq_status check_backward(const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                                 const float* x_scales, const void* w, int w_dtype, int64_t T,
+                                 int64_t I, int64_t O, int block, int rank, int gx_mode,
+                                 int gw_mode, int reduction, const float* g_x, const float* g_w) {
   if (!g_y || !x_codes || !x_scales || !w || !g_x || !g_w) return HLQ_ERR_NULL;
   if ((gy_dtype != HLQ_F32 && gy_dtype != HLQ_BF16) ||
       (w_dtype != HLQ_F32 && w_dtype != HLQ_BF16))
@@ -248,14 +247,18 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
       (gw_mode != HLQ_PER_TOKEN && gw_mode != HLQ_PER_TENSOR) ||
       (reduction != HLQ_SUM && reduction != HLQ_MEAN))
     return HLQ_ERR_MODE;
-  const Layout L = make_layout(T, I, O, block, rank);
-  if (!workspace || workspace_bytes < L.pub.total) return HLQ_ERR_WORKSPACE;
   if (!aligned16(g_y) || !aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w) ||
-      !aligned16(g_x) || !aligned16(g_w) || !aligned16(workspace))
+      !aligned16(g_x) || !aligned16(g_w))
     return HLQ_ERR_ALIGN;
+  return HLQ_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+// The launch sequence of a validated call.
+static hlq_status run_backward(const Layout& L, const void* g_y, int gy_dtype,
+                               const uint8_t* x_codes, const float* x_scales, const void* w,
+                               int w_dtype, int64_t T, int64_t I, int64_t O, int block,
+                               int rank, int gx_mode, int gw_mode, int reduction, float* g_x,
+                               float* g_w, uint8_t* ws, uint32_t step_mask, hipStream_t s) {
   const bool gx_tok = gx_mode == HLQ_PER_TOKEN;
   const bool gw_tok = gw_mode == HLQ_PER_TOKEN;
   const hlq::TrArgs a = make_tr_args(L, g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O,
@@ -287,6 +290,24 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
   return HLQ_OK;
 }
 
+hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
+                                     const uint8_t* x_codes, const float* x_scales,
+                                     const void* w, int w_dtype, int64_t T, int64_t I,
+                                     int64_t O, int block, int rank, int gx_mode,
+                                     int gw_mode, int reduction, float* g_x, float* g_w,
+                                     void* workspace, size_t workspace_bytes,
+                                     uint32_t step_mask, void* stream) {
+  hlq_status st = check_backward(g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O, block,
+                                 rank, gx_mode, gw_mode, reduction, g_x, g_w);
+  if (st != HLQ_OK) return st;
+  const Layout L = make_layout(T, I, O, block, rank);
+  if (!workspace || workspace_bytes < L.pub.total) return HLQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return HLQ_ERR_ALIGN;
+  return run_backward(L, g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O, block, rank,
+                      gx_mode, gw_mode, reduction, g_x, g_w, static_cast<uint8_t*>(workspace),
+                      step_mask, static_cast<hipStream_t>(stream));
+}
+
 hlq_status hlq_linear_backward(const void* g_y, int gy_dtype, const uint8_t* x_codes,
                                const float* x_scales, const void* w, int w_dtype,
                                int64_t T, int64_t I, int64_t O, int block, int rank,
@@ -296,6 +317,25 @@ hlq_status hlq_linear_backward(const void* g_y, int gy_dtype, const uint8_t* x_c
   return hlq_linear_backward_steps(g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O,
                                    block, rank, gx_mode, gw_mode, reduction, g_x, g_w,
                                    workspace, workspace_bytes, HLQ_STEPS_ALL, stream);
+}
+
+hlq_status hlq_linear_backward_noalloc(const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                                       const float* x_scales, const void* w, int w_dtype,
+                                       int64_t T, int64_t I, int64_t O, int block, int rank,
+                                       int gx_mode, int gw_mode, int reduction, float* g_x,
+                                       float* g_w, void* stream) {
+  hlq_status st = check_backward(g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O, block,
+                                 rank, gx_mode, gw_mode, reduction, g_x, g_w);
+  if (st != HLQ_OK) return st;
+  // All five steps run, the GEMMs as the one paired launch, which uses no
+  // split-K partials: the intermediates end where the partial region begins.
+  const Layout L = make_layout(T, I, O, block, rank);
+  if (L.partial > (size_t)HLQ_NOALLOC_SCRATCH_BYTES) return HLQ_ERR_WORKSPACE;
+  uint8_t* scratch = static_cast<uint8_t*>(hlq::noalloc_scratch());
+  if (!scratch) return HLQ_ERR_HIP;
+  return run_backward(L, g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O, block, rank,
+                      gx_mode, gw_mode, reduction, g_x, g_w, scratch, HLQ_STEPS_ALL,
+                      static_cast<hipStream_t>(stream));
 }
 
 // Shared checks of the accumulator exports: the workspace holds the layout of

@@ -91,6 +91,10 @@ struct LqsArgs {
 // ERR pass and the final fold (after launch_tr MAX and launch_tr_reduce).
 hipError_t launch_lqs(const LqsArgs& a, int n, hipStream_t s);
 
+// Device address of the current device's static scratch array
+// (hlq_linear_backward_noalloc), nullptr on a runtime error.
+void* noalloc_scratch();
+
 hipError_t launch_acbp(const void* x, int dtype, int64_t T, int64_t I, uint8_t* codes,
                        float* scales, hipStream_t s);
 

@@ -24,6 +24,7 @@ EXPORTED = (
     "hlq_linear_backward_workspace_size",
     "hlq_linear_backward",
     "hlq_linear_backward_steps",
+    "hlq_linear_backward_noalloc",
     "hlq_workspace_layout_query",
     "hlq_gemm_pair_acc",
     "hlq_gemm_gx_acc",
@@ -68,6 +69,9 @@ def _load():
     lib.hlq_linear_backward_steps.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I32, I32,
                                               I32, I32, I32, P, P, P, SZ, ctypes.c_uint32, P]
     lib.hlq_linear_backward_steps.restype = I32
+    lib.hlq_linear_backward_noalloc.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I32, I32,
+                                                I32, I32, I32, P, P, P]
+    lib.hlq_linear_backward_noalloc.restype = I32
     lib.hlq_workspace_layout_query.argtypes = [I64, I64, I64, I32, I32,
                                                ctypes.POINTER(WorkspaceLayout)]
     lib.hlq_workspace_layout_query.restype = I32
@@ -229,6 +233,37 @@ def _acc_out(workspace, t, shape):
         t = torch.empty(shape, dtype=torch.int32, device=workspace.device)
     _expect("accumulator", t, torch.int32, shape)
     return t
+
+
+HLQ_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def hlq_linear_backward_noalloc(g_y, x_codes, x_scales, w, block, rank, gx_mode=HLQ_PER_TOKEN,
+                                gw_mode=HLQ_PER_TOKEN, reduction=HLQ_SUM, g_x=None, g_w=None,
+                                stream=None):
+    """hlq_linear_backward with the library's static scratch array in place of
+    a workspace (no device allocation inside the call; calls that overlap on
+    one GPU race).  g_x / g_w are allocated here only when omitted."""
+    import torch
+    T, O = g_y.shape
+    O2, I = w.shape
+    if O2 != O:
+        raise ValueError("w must be [O, I] with O = g_y.shape[1]")
+    dev = g_y.device
+    if g_x is None:
+        g_x = torch.empty((T, I), dtype=torch.float32, device=dev)
+    if g_w is None:
+        g_w = torch.empty((O, I), dtype=torch.float32, device=dev)
+    _expect("x_codes", x_codes, torch.uint8, (T, I // 2))
+    _expect("x_scales", x_scales, torch.float32, (T,))
+    _expect("g_x", g_x, torch.float32, (T, I))
+    _expect("g_w", g_w, torch.float32, (O, I))
+    _require_cuda(g_y, x_codes, x_scales, w, g_x, g_w)
+    _check("hlq_linear_backward_noalloc", _lib.hlq_linear_backward_noalloc(
+        _ptr(g_y), _dtype_code(g_y), _ptr(x_codes), _ptr(x_scales), _ptr(w), _dtype_code(w),
+        T, I, O, block, rank, gx_mode, gw_mode, reduction, _ptr(g_x), _ptr(g_w),
+        _stream(stream)))
+    return g_x, g_w
 
 
 def hlq_gemm_pair_acc(workspace, T, I, O, block, rank, acc_x=None, acc_w=None, stream=None):

@@ -118,6 +118,31 @@ hlq_status hlq_linear_backward(const void* g_y, int gy_dtype,
                                void* stream);
 
 /*
+ * hlq_linear_backward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, no workspace.  The intermediates go to a static
+ * device array owned by the library, HLQ_NOALLOC_SCRATCH_BYTES on each GPU the
+ * library runs on, held until the process ends; the call allocates and frees
+ * nothing.  Its first call on a device resolves that device's copy of the
+ * array (hipGetSymbolAddress, a runtime query; make one call before any graph
+ * capture).  A shape whose intermediates do not fit (the workspace of
+ * hlq_linear_backward_workspace_size less its split-K partial region, which
+ * this call never uses) returns HLQ_ERR_WORKSPACE before anything is
+ * enqueued.  All calls on one GPU share its array: calls that can overlap on
+ * one GPU (other streams, other host threads) race and must be serialised by
+ * the caller.  Each call writes every intermediate before reading it, so the
+ * array needs no clearing between calls.
+ */
+#define HLQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+hlq_status hlq_linear_backward_noalloc(const void* g_y, int gy_dtype,
+                                       const uint8_t* x_codes, const float* x_scales,
+                                       const void* w, int w_dtype,
+                                       int64_t T, int64_t I, int64_t O,
+                                       int block, int rank,
+                                       int gx_mode, int gw_mode, int reduction,
+                                       float* g_x, float* g_w, void* stream);
+
+/*
  * The launches hlq_linear_backward enqueues, in order.  Bit k of a step mask
  * selects HLQ_STEP k.
  */
