@@ -3,7 +3,8 @@
 
 One step = one full backward of the layer (hlq_linear_backward: every launch
 of the hot path) on inputs already resident in HBM.  The ACBP compression of x
-happens at forward time; it is timed separately and reported as acbp_us.
+happens at forward time; it is timed separately (as one more launch of the
+instrumented pass below) and reported as acbp_us.
 
 Timing: W untimed warm-up steps, then K steps bracketed by
 torch.cuda.synchronize(); the steps rotate over several copies of the
@@ -13,7 +14,8 @@ HIP events around each launch step (same stream, same rotation) to get
 per-kernel durations (less the interval of an empty step, the cost of the
 event itself); the longest one is reported against its roofline.
 
-The CPU baseline is the oracle (numpy) running the same layer once on the host.
+The CPU baseline is the oracle (numpy) running the same layer once on one host
+thread.
 """
 from __future__ import annotations
 
@@ -131,7 +133,8 @@ class LayerSets:
         self.sets = []
         for _ in range(nsets):
             self.sets.append(dict(
-                gy=gy0.clone(), codes=codes0.clone(), scales=scales0.clone(), w=w0.clone(),
+                gy=gy0.clone(), x=x0.clone(), codes=codes0.clone(), scales=scales0.clone(),
+                w=w0.clone(),
                 g_x=torch.empty((cfg.T, cfg.I), dtype=torch.float32, device=dev),
                 g_w=torch.empty((cfg.O, cfg.I), dtype=torch.float32, device=dev),
                 ws=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)))
@@ -139,10 +142,18 @@ class LayerSets:
         del gy0, w0
         torch.cuda.synchronize()
 
+    def acbp(self, i):
+        import hadamard_rank_linear_amd as h
+        s = self.sets[i % len(self.sets)]
+        h.hlq_compress_act(s["x"], s["codes"], s["scales"])
+
     def run(self, i, steps=None):
         import hadamard_rank_linear_amd as h
         s = self.sets[i % len(self.sets)]
         c = self.cfg
+        if steps == "acbp":
+            self.acbp(i)
+            return
         h.hlq_linear_backward(s["gy"], s["codes"], s["scales"], s["w"], c.block, c.rank,
                               c.gx_mode, c.gw_mode, c.reduction, g_x=s["g_x"], g_w=s["g_w"],
                               workspace=s["ws"], steps=steps)
@@ -171,21 +182,6 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
     wall_ms = (time.perf_counter() - t0) * 1e3
     gpu_ms = ev0.elapsed_time(ev1)
     res = dict(wall_ms_per_step=wall_ms / steps, gpu_ms_per_step=gpu_ms / steps, nsets=nsets)
-
-    # ACBP (forward time) on the same rotation scheme
-    xs = [sets.x0.clone() for _ in range(nsets)]
-    codes = [s["codes"] for s in sets.sets]
-    scales = [s["scales"] for s in sets.sets]
-    for i in range(warmup):
-        h.hlq_compress_act(xs[i % nsets], codes[i % nsets], scales[i % nsets])
-    torch.cuda.synchronize()
-    ev0.record()
-    for i in range(steps):
-        h.hlq_compress_act(xs[i % nsets], codes[i % nsets], scales[i % nsets])
-    ev1.record()
-    torch.cuda.synchronize()
-    res["acbp_us"] = ev0.elapsed_time(ev1) / steps * 1e3
-    del xs
 
     if per_kernel:
         # Distribution of single-step latencies: an event before every step of
@@ -219,8 +215,9 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
         # together are one launch
         # The "empty" unit launches nothing: its interval is the cost of one
         # event record in the queue, subtracted from the others.
+        # ACBP (forward time, hlq_compress_act) is timed the same way
         units = [("tr_max", 1 << 0), ("tr_reduce", 1 << 1), ("tr_quant", 1 << 2),
-                 ("gemm", (1 << 3) | (1 << 4)), ("empty", 0)]
+                 ("gemm", (1 << 3) | (1 << 4)), ("acbp", "acbp"), ("empty", 0)]
         active = list(range(len(units)))
         n_inst = min(steps, 20)
         cal0 = torch.cuda.Event(enable_timing=True)
@@ -248,6 +245,7 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
             acc[k] += a.elapsed_time(b)
         raw = {units[k][0]: acc[k] / n_inst * 1e3 for k in active}
         empty = raw.pop("empty")
+        res["acbp_us"] = max(raw.pop("acbp") - empty, 0.0)
         res["kernels_event_us"] = raw
         res["event_overhead_us"] = empty
         res["kernels_us"] = {k: max(v - empty, 0.0) for k, v in raw.items()}
@@ -260,6 +258,69 @@ def time_layer(cfg, inp, steps, warmup, per_kernel=True):
     del sets
     torch.cuda.empty_cache()
     return res
+
+
+def roofline_of(cfg, kernels_us):
+    """Roofline object of the dominant (longest) launch of one backward: its
+    algorithmic work per launch over its measured duration, against the bound
+    its arithmetic intensity gives (INT8 MFMA or HBM)."""
+    dt_bytes = 4 if cfg.dtype == 0 else 2
+    costs = step_costs(cfg, dt_bytes)
+    kname = max((k for k in kernels_us if k in costs), key=lambda k: kernels_us[k])
+    kus = kernels_us[kname]
+    ops, nbytes = costs[kname]
+    _, bound = ideal_us(ops, nbytes)
+    if bound == "mfma":
+        achieved = ops / (kus * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+    else:
+        achieved = nbytes / (kus * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update(kernel=kname, kernel_us=round(kus, 2), algorithmic_bytes=nbytes,
+                algorithmic_ops=ops, traffic=measured_traffic(cfg.name, kname))
+    return roof
+
+
+def layer_summary(cfg, r):
+    """µs per backward, effective TOPS, per-launch times, latency
+    percentiles and the dominant launch's roofline of one timed layer."""
+    us = r["wall_ms_per_step"] * 1e3
+    ops = 2 * cfg.T * cfg.I * cfg.O + 2 * cfg.Tl * cfg.O * cfg.I
+    out = {"us": round(us, 2), "effective_tops": round(ops / (us * 1e-6) / 1e12, 1)}
+    if "kernels_us" in r:
+        out["kernels_us"] = {k: round(v, 2) for k, v in r["kernels_us"].items()}
+        out["acbp_us"] = round(r["acbp_us"], 2)
+        out["latency_us"] = r["latency_us"]
+        out["roofline"] = roofline_of(cfg, r["kernels_us"])
+    return out
+
+
+def time_int8_library_gemm(M, N, K, reps=20):
+    """Context, not this library: torch._int_mm (hipBLASLt) INT8 x INT8 ->
+    INT32 of an M x K by K x N product, µs per call on resident operands, and
+    its fraction of the INT8 peak.  None when the build has no INT8 GEMM."""
+    import torch
+    try:
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
+        b = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda").t()
+        for _ in range(3):
+            torch._int_mm(a, b)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch._int_mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+    except Exception as ex:  # pragma: no cover - depends on the torch build
+        return {"error": str(ex)[:120]}
+    us = e0.elapsed_time(e1) / reps * 1e3
+    tops = 2 * M * N * K / (us * 1e-6) / 1e12
+    return {"M": M, "N": N, "K": K, "us": round(us, 2), "tops": round(tops, 1),
+            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
 
 
 def time_lqs(cfg, inp, reps=10):
@@ -346,50 +407,44 @@ def time_torch_backward(cfg, inp, dtype_name="bf16", steps=20, warmup=5):
 
 
 def per_config_side(steps, warmup):
-    """Every other layer config at full size: µs per backward, effective TOPS
-    and the per-launch event times (no roofline object: the bench line's
-    roofline is the headline layer's)."""
+    """Every other layer config at full size: µs per backward, effective TOPS,
+    per-launch event times and the dominant launch's roofline."""
     from hadamard_rank_linear_amd import workloads as wl
     out = {}
     for cfg in wl.LAYERS:
         if cfg.name in ("vitb_qkv", "vitb_fc2"):
             continue
         log(f"side measurement: {cfg.name}")
-        r = time_layer(cfg, wl.make_inputs(cfg), steps, warmup)
-        us = r["wall_ms_per_step"] * 1e3
-        ops = 2 * cfg.T * cfg.I * cfg.O + 2 * cfg.Tl * cfg.O * cfg.I
-        out[cfg.name] = {"us": round(us, 2), "effective_tops": round(ops / (us * 1e-6) / 1e12, 1),
-                         "kernels_us": {k: round(v, 2) for k, v in r["kernels_us"].items()}}
+        out[cfg.name] = layer_summary(cfg, time_layer(cfg, wl.make_inputs(cfg), steps, warmup))
     return out
 
 
 def cpu_baseline(cfg, inp):
-    import numpy as np
+    """The oracle (numpy, as it stands) on the same full layer, once, on one
+    host thread: BLAS is held to one thread for the integer GEMMs (fp64
+    products), and the transforms and quantizers are single-threaded numpy."""
     import oracle as o
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    from threadpoolctl import threadpool_limits
     f = (lambda a: a) if cfg.dtype == 0 else o.bf16_bits_to_f32
     gy, x, w = f(inp["gy"]), f(inp["x"]), f(inp["w"])
     codes, scales = o.acbp_pack(x)
-    t0 = time.perf_counter()
-    o.linear_backward(gy, codes, scales, w, cfg.block, cfg.rank, cfg.gx_mode, cfg.gw_mode,
-                      cfg.reduction)
-    sec = time.perf_counter() - t0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        o.linear_backward(gy, codes, scales, w, cfg.block, cfg.rank, cfg.gx_mode, cfg.gw_mode,
+                          cfg.reduction)
+        sec = time.perf_counter() - t0
     cpu = "unknown"
     try:
-        with open("/proc/cpuinfo") as f:
-            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
                        cpu)
     except OSError:
         pass
-    return {"value": round(sec * 1e6, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
+    return {"value": round(sec * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
             "cpu": cpu, "host_cpus": os.cpu_count(),
             "sample": (f"one full {cfg.name} layer backward (T={cfg.T}, I={cfg.I}, O={cfg.O}) by "
-                       f"the numpy oracle: fp32 transforms/quantizers single-threaded, exact "
-                       f"integer GEMMs as fp64 BLAS on {threads} threads; ACBP excluded"),
+                       f"the numpy oracle on one host thread (BLAS limited to 1 thread for the "
+                       f"exact fp64 integer GEMMs); ACBP excluded"),
             "seconds": round(sec, 2)}
 
 
@@ -422,44 +477,36 @@ def main():
     inp = wl.make_inputs(cfg)
     res = time_layer(cfg, inp, args.steps, args.warmup)
     lat_us = res["wall_ms_per_step"] * 1e3
-    dt_bytes = 4 if cfg.dtype == 0 else 2
-    costs = step_costs(cfg, dt_bytes)
+    costs = step_costs(cfg, 4 if cfg.dtype == 0 else 2)
     ops_total = 2 * cfg.T * cfg.I * cfg.O + 2 * cfg.Tl * cfg.O * cfg.I
     ideal_total = sum(ideal_us(*costs[k])[0] for k in res["kernels_us"] if k in costs)
 
     # dominant kernel against its roofline
-    kname = max((k for k in res["kernels_us"] if k in costs), key=lambda k: res["kernels_us"][k])
-    kus = res["kernels_us"][kname]
-    ops, nbytes = costs[kname]
-    _, bound = ideal_us(ops, nbytes)
-    if bound == "mfma":
-        achieved = ops / (kus * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
-                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-    else:
-        achieved = nbytes / (kus * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    traffic = measured_traffic(cfg.name, kname)
-    roof.update(kernel=kname, kernel_us=round(kus, 2), algorithmic_bytes=nbytes,
-                algorithmic_ops=ops, traffic=traffic)
+    roof = roofline_of(cfg, res["kernels_us"])
 
     extra = {}
     if not args.no_extra:
         log("layer-wise quantizer selection statistics")
         extra["lqs"] = time_lqs(cfg, inp)
     if not args.no_extra and cfg.name != "vitb_fc2":
+        # the other half of the metric's "qkv/fc2 shape": same measurement
         c2 = wl.BY_NAME["vitb_fc2"]
         log("side measurement: vitb_fc2")
-        r2 = time_layer(c2, wl.make_inputs(c2), max(10, args.steps // 2), args.warmup,
-                        per_kernel=False)
-        extra["vitb_fc2_us"] = round(r2["wall_ms_per_step"] * 1e3, 2)
+        extra["vitb_fc2"] = layer_summary(c2, time_layer(c2, wl.make_inputs(c2),
+                                                         max(10, args.steps // 2), args.warmup))
+        extra["vitb_fc2_us"] = extra["vitb_fc2"]["us"]
     if not args.no_extra:
         extra["per_config"] = per_config_side(max(10, args.steps // 2), args.warmup)
         log("context: torch bf16 and fp32 backward of the same layer")
         extra["context_torch_bf16_backward_us"] = time_torch_backward(cfg, inp, "bf16")
         extra["context_torch_fp32_backward_us"] = time_torch_backward(cfg, inp, "fp32", steps=10,
                                                                       warmup=3)
+        # the library INT8 GEMM on the same two products (g_w: INT8 codes,
+        # K = T'; g_x: its INT4 codes as INT8, K = O), for context
+        log("context: hipBLASLt INT8 GEMMs of the layer's shapes")
+        extra["context_hipblaslt_int8"] = {
+            "gemm_gw": time_int8_library_gemm(cfg.O, cfg.I, -(-cfg.Tl // 8) * 8),
+            "gemm_gx": time_int8_library_gemm(cfg.T, cfg.I, cfg.O)}
 
     if args.copy_calib:
         copy_calibration()
