@@ -274,6 +274,39 @@ def _bcast(s: np.ndarray, axis: int) -> np.ndarray:
 # The backward pass
 # --------------------------------------------------------------------------
 
+def _backward_core(gy, x, w, block: int, rank: int, gx_mode: int, gw_mode: int,
+                   reduction: int) -> dict:
+    """Both paths of the backward for fp32 g_y [T x O], x [T x I] (the
+    decoded activation) and w [O x I]; the epilogues are left in fp64
+    (gx64, gw64) for the caller to round once.  See linear_backward."""
+    T, O = gy.shape
+    O2, I = w.shape
+    assert O2 == O and x.shape == (T, I)
+    n, r = block, rank
+
+    # g_x path: Hadamard along O (the contracted dimension), INT4.
+    gy_h = fwht_blocks(gy, n, axis=1)
+    w_h = fwht_blocks(w, n, axis=0)
+    q_gy, s_gy = quantize(gy_h, QMAX_INT4, _group_axis(gx_mode, 1))
+    q_w, s_w = quantize(w_h, QMAX_INT4, _group_axis(gx_mode, 0))
+    acc_x = int_matmul(q_gy, q_w)
+    gx64 = acc_x.astype(np.float64) * _bcast(s_gy, 0) * _bcast(s_w, 1) / n
+
+    # g_w path: low-rank Hadamard along T (the contracted dimension), INT8.
+    gy_l = lowrank_transform(gy, n, r, axis=0)
+    x_l = lowrank_transform(x, n, r, axis=0)
+    q_gyl, s_gyl = quantize(gy_l, QMAX_INT8, _group_axis(gw_mode, 0))
+    q_xl, s_xl = quantize(x_l, QMAX_INT8, _group_axis(gw_mode, 0))
+    acc_w = int_matmul(q_gyl.T, q_xl)
+    gw64 = acc_w.astype(np.float64) * _bcast(s_gyl, 0) * _bcast(s_xl, 1) / n
+    if reduction == MEAN:
+        gw64 = gw64 / T
+    elif reduction != SUM:
+        raise ValueError("reduction must be SUM or MEAN")
+    return dict(q_gy=q_gy, s_gy=s_gy, q_w=q_w, s_w=s_w, acc_x=acc_x, gx64=gx64,
+                q_gyl=q_gyl, s_gyl=s_gyl, q_xl=q_xl, s_xl=s_xl, acc_w=acc_w, gw64=gw64)
+
+
 def linear_backward(gy, x_codes, x_scales, w, block: int, rank: int,
                     gx_mode: int = PER_TOKEN, gw_mode: int = PER_TOKEN,
                     reduction: int = SUM) -> dict:
@@ -298,38 +331,12 @@ def linear_backward(gy, x_codes, x_scales, w, block: int, rank: int,
     """
     gy = np.asarray(gy, dtype=np.float32)
     w = np.asarray(w, dtype=np.float32)
-    T, O = gy.shape
-    O2, I = w.shape
-    assert O2 == O
-    n, r = block, rank
-
-    # g_x path: Hadamard along O (the contracted dimension), INT4.
-    gy_h = fwht_blocks(gy, n, axis=1)
-    w_h = fwht_blocks(w, n, axis=0)
-    q_gy, s_gy = quantize(gy_h, QMAX_INT4, _group_axis(gx_mode, 1))
-    q_w, s_w = quantize(w_h, QMAX_INT4, _group_axis(gx_mode, 0))
-    acc_x = int_matmul(q_gy, q_w)
-    g_x = (acc_x.astype(np.float64) * _bcast(s_gy, 0) * _bcast(s_w, 1)
-           / n).astype(np.float32)
-
-    # g_w path: low-rank Hadamard along T (the contracted dimension), INT8.
     x = acbp_unpack(x_codes, x_scales)
-    assert x.shape == (T, I)
-    gy_l = lowrank_transform(gy, n, r, axis=0)
-    x_l = lowrank_transform(x, n, r, axis=0)
-    q_gyl, s_gyl = quantize(gy_l, QMAX_INT8, _group_axis(gw_mode, 0))
-    q_xl, s_xl = quantize(x_l, QMAX_INT8, _group_axis(gw_mode, 0))
-    acc_w = int_matmul(q_gyl.T, q_xl)
-    gw64 = acc_w.astype(np.float64) * _bcast(s_gyl, 0) * _bcast(s_xl, 1) / n
-    if reduction == MEAN:
-        gw64 = gw64 / T
-    elif reduction != SUM:
-        raise ValueError("reduction must be SUM or MEAN")
-    g_w = gw64.astype(np.float32)
-
-    return dict(q_gy=q_gy, s_gy=s_gy, q_w=q_w, s_w=s_w, acc_x=acc_x, g_x=g_x,
-                x_deq=x, q_gyl=q_gyl, s_gyl=s_gyl, q_xl=q_xl, s_xl=s_xl,
-                acc_w=acc_w, g_w=g_w)
+    out = _backward_core(gy, x, w, block, rank, gx_mode, gw_mode, reduction)
+    out["g_x"] = out.pop("gx64").astype(np.float32)
+    out["g_w"] = out.pop("gw64").astype(np.float32)
+    out["x_deq"] = x
+    return out
 
 
 def linear_backward_unquantized(gy, x, w, block: int, rank: int,
@@ -350,6 +357,106 @@ def linear_backward_unquantized(gy, x, w, block: int, rank: int,
     if reduction == MEAN:
         g_w = g_w / T
     return dict(g_x=g_x, g_w=g_w)
+
+
+# --------------------------------------------------------------------------
+# Convolution layers ([HLQ] abstract: backpropagation of convolutional and
+# linear layers; [HOT-sum] "Key results": ResNet-50 at batch size 256)
+# --------------------------------------------------------------------------
+#
+# R11 A convolution y[n,p,q,o] = sum_{r,s,c} x[n, p*st - pad + r, q*st - pad + s, c]
+#     * w[o,r,s,c] (NHWC activations, OHWI weights, zero padding) is the
+#     linear layer y = im2col(x) . w^T with tokens t = (n, p, q) and input
+#     features i = (r, s, c) (column (r*S + s)*C + c).  Its HLQ/HOT backward is
+#     the linear backward on (g_y, im2col(x), w): ACBP stores the convolution
+#     input x itself (per pixel (n, h, w), over its C channels) and im2col
+#     gathers the decoded values; g_w [O][R][S][C] is the linear g_w; g_x is
+#     col2im of the linear g_x, the sum over the taps (r, s) that read each
+#     input pixel, in fp64, rounded once to fp32 (as R9).
+
+
+def conv_out_size(H: int, R: int, stride: int, pad: int) -> int:
+    """Output rows of a convolution along one spatial axis."""
+    return (H + 2 * pad - R) // stride + 1
+
+
+def im2col(x, R: int, S: int, stride: int, pad: int) -> np.ndarray:
+    """x [N, H, W, C] -> [N*P*Q, R*S*C]: row (n, p, q), column (r*S + s)*C + c
+    holds x[n, p*stride - pad + r, q*stride - pad + s, c], 0 outside the image."""
+    x = np.asarray(x)
+    N, H, W, C = x.shape
+    P, Q = conv_out_size(H, R, stride, pad), conv_out_size(W, S, stride, pad)
+    cols = np.zeros((N, P, Q, R, S, C), dtype=x.dtype)
+    for r in range(R):
+        for s in range(S):
+            for p in range(P):
+                h = p * stride - pad + r
+                if not 0 <= h < H:
+                    continue
+                for q in range(Q):
+                    w_ = q * stride - pad + s
+                    if 0 <= w_ < W:
+                        cols[:, p, q, r, s, :] = x[:, h, w_, :]
+    return cols.reshape(N * P * Q, R * S * C)
+
+
+def col2im(cols, N: int, H: int, W: int, C: int, R: int, S: int, stride: int,
+           pad: int) -> np.ndarray:
+    """Adjoint of im2col: [N*P*Q, R*S*C] -> [N, H, W, C], each input pixel the
+    sum of the entries im2col copied it to (in the dtype of ``cols``: fp64 for
+    gradients, int64 for integer accumulators)."""
+    P, Q = conv_out_size(H, R, stride, pad), conv_out_size(W, S, stride, pad)
+    c6 = np.asarray(cols).reshape(N, P, Q, R, S, C)
+    g = np.zeros((N, H, W, C), dtype=c6.dtype)
+    for r in range(R):
+        for s in range(S):
+            for p in range(P):
+                h = p * stride - pad + r
+                if not 0 <= h < H:
+                    continue
+                for q in range(Q):
+                    w_ = q * stride - pad + s
+                    if 0 <= w_ < W:
+                        g[:, h, w_, :] += c6[:, p, q, r, s, :]
+    return g
+
+
+def conv_backward(gy, x_codes, x_scales, w, N: int, H: int, W: int, C: int, R: int, S: int,
+                  stride: int, pad: int, block: int, rank: int, gx_mode: int = PER_TOKEN,
+                  gw_mode: int = PER_TOKEN, reduction: int = SUM) -> dict:
+    """HLQ/HOT backward of one convolution (reading R11).
+
+    gy [N*P*Q x O] (rows (n, p, q)), x_codes [N*H*W][C/2] and x_scales [N*H*W]
+    (ACBP of the input, per pixel), w [O x R*S*C] (OHWI).  Returns the linear
+    backward's intermediates on (gy, im2col(x), w) (q_gy, s_gy, q_w, s_w,
+    q_gyl, s_gyl, q_xl, s_xl, acc_w, g_w, with acc_x_col the linear g_x
+    accumulators) and g_x [N*H*W x C] = col2im of the fp64 linear g_x, rounded
+    once; acc_x [N*H*W x C] = col2im of acc_x_col (int64), the integer sums a
+    per-tensor g_x epilogue scales.
+    """
+    gy = np.asarray(gy, dtype=np.float32)
+    w = np.asarray(w, dtype=np.float32)
+    xd = acbp_unpack(x_codes, x_scales).reshape(N, H, W, C)
+    cols = im2col(xd, R, S, stride, pad)
+    out = _backward_core(gy, cols, w, block, rank, gx_mode, gw_mode, reduction)
+    out["acc_x_col"] = out.pop("acc_x")
+    out["acc_x"] = col2im(out["acc_x_col"], N, H, W, C, R, S, stride, pad).reshape(N * H * W, C)
+    gx = col2im(out.pop("gx64"), N, H, W, C, R, S, stride, pad)
+    out["g_x"] = gx.reshape(N * H * W, C).astype(np.float32)
+    out["g_w"] = out.pop("gw64").astype(np.float32)
+    out["x_col"] = cols
+    return out
+
+
+def conv_backward_unquantized(gy, x, w, N: int, H: int, W: int, C: int, R: int, S: int,
+                              stride: int, pad: int, block: int, rank: int,
+                              reduction: int = SUM) -> dict:
+    """Quantization-off form of :func:`conv_backward` (self-checks): fp64
+    transforms and products, x given directly as [N, H, W, C]."""
+    cols = im2col(np.asarray(x, dtype=np.float64), R, S, stride, pad)
+    lin = linear_backward_unquantized(gy, cols, w, block, rank, reduction)
+    gx = col2im(lin["g_x"], N, H, W, C, R, S, stride, pad)
+    return dict(g_x=gx.reshape(N * H * W, C), g_w=lin["g_w"])
 
 
 # --------------------------------------------------------------------------
@@ -459,6 +566,7 @@ __all__ = [
     "sylvester_hadamard", "fwht_blocks", "lowrank_rows", "sequency",
     "lowrank_transform", "quantize", "pack_int4", "unpack_int4", "acbp_pack",
     "acbp_unpack", "int_matmul", "linear_backward",
-    "linear_backward_unquantized", "rel_fro", "max_rel_err", "LQS_THRESHOLD", "LQS_OPERANDS",
+    "linear_backward_unquantized", "rel_fro", "max_rel_err", "conv_out_size", "im2col",
+    "col2im", "conv_backward", "conv_backward_unquantized", "LQS_THRESHOLD", "LQS_OPERANDS",
     "lqs_operands", "quant_sq_error", "lqs_stats", "lqs_path_errors", "lqs_select",
 ]
