@@ -101,7 +101,8 @@ def test_conv_golden():
     x = np.array(g["x"], np.float64).reshape(1, 3, 3, 1)
     gy = np.array(g["gy"], np.float64).reshape(4, 1)
     w = np.array(g["w"], np.float64).reshape(1, 4)
-    out = o.conv_backward_unquantized(gy, x, w, 1, 3, 3, 1, 2, 2, 1, 0, 4, 4)
+    # block 1 (H_1 = [1]): O = 1 admits no larger block; the geometry is under test
+    out = o.conv_backward_unquantized(gy, x, w, 1, 3, 3, 1, 2, 2, 1, 0, 1, 1)
     assert out["g_w"].reshape(2, 2).tolist() == g["g_w"]
     assert out["g_x"].reshape(3, 3).tolist() == g["g_x"]
 
