@@ -111,7 +111,7 @@ def test_conv_backward_is_linear_backward_on_im2col():
     # the quantized conv backward: every code, scale and g_w of the linear
     # backward on the gathered decoded input, and g_x its col2im (integer
     # accumulators summed exactly, fp64 gradient rounded once)
-    N, H, W, C, R, S, st, pad, O, n, r = 2, 6, 6, 8, 3, 3, 1, 1, 32, 16, 4
+    N, H, W, C, R, S, st, pad, O, n, r = 2, 8, 8, 8, 3, 3, 1, 1, 32, 16, 4
     rng = np.random.default_rng(4)
     P, Q = o.conv_out_size(H, R, st, pad), o.conv_out_size(W, S, st, pad)
     gy = rng.standard_normal((N * P * Q, O)).astype(np.float32)
