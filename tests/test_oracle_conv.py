@@ -121,7 +121,8 @@ def test_conv_backward_is_linear_backward_on_im2col():
     out = o.conv_backward(gy, codes, sc, w, N, H, W, C, R, S, st, pad, n, r,
                           o.PER_TENSOR, o.PER_TOKEN)
     cols = o.im2col(o.acbp_unpack(codes, sc).reshape(N, H, W, C), R, S, st, pad)
-    lin = o._backward_core(gy, cols, w, n, r, o.PER_TENSOR, o.PER_TOKEN, o.SUM)
+    from oracle import hlq_oracle as ho
+    lin = ho._backward_core(gy, cols, w, n, r, o.PER_TENSOR, o.PER_TOKEN, o.SUM)
     for k in ("q_gy", "s_gy", "q_w", "s_w", "q_gyl", "s_gyl", "q_xl", "s_xl", "acc_w"):
         assert np.array_equal(out[k], lin[k]), k
     assert np.array_equal(out["g_w"], lin["gw64"].astype(np.float32))
