@@ -372,7 +372,10 @@ def linear_backward_unquantized(gy, x, w, block: int, rank: int,
 #     input x itself (per pixel (n, h, w), over its C channels) and im2col
 #     gathers the decoded values; g_w [O][R][S][C] is the linear g_w; g_x is
 #     col2im of the linear g_x, the sum over the taps (r, s) that read each
-#     input pixel, in fp64, rounded once to fp32 (as R9).
+#     input pixel, rounded once to fp32 (as R9).  With per-tensor g_x scales
+#     every term shares the scale pair, and the sum is taken exactly as the
+#     integer col2im of the accumulators times the scales / n; with
+#     per-token scales the terms are summed in fp64.
 
 
 def conv_out_size(H: int, R: int, stride: int, pad: int) -> int:
@@ -441,8 +444,14 @@ def conv_backward(gy, x_codes, x_scales, w, N: int, H: int, W: int, C: int, R: i
     out = _backward_core(gy, cols, w, block, rank, gx_mode, gw_mode, reduction)
     out["acc_x_col"] = out.pop("acc_x")
     out["acc_x"] = col2im(out["acc_x_col"], N, H, W, C, R, S, stride, pad).reshape(N * H * W, C)
-    gx = col2im(out.pop("gx64"), N, H, W, C, R, S, stride, pad)
-    out["g_x"] = gx.reshape(N * H * W, C).astype(np.float32)
+    gx64 = out.pop("gx64")
+    if gx_mode == PER_TENSOR:
+        # one scale pair for every term: the exact sum over the taps is the
+        # integer sum times the scales (so exact cancellations give exact 0)
+        gx = out["acc_x"].astype(np.float64) * _bcast(out["s_gy"], 0) * _bcast(out["s_w"], 1) / block
+    else:
+        gx = col2im(gx64, N, H, W, C, R, S, stride, pad).reshape(N * H * W, C)
+    out["g_x"] = gx.astype(np.float32)
     out["g_w"] = out.pop("gw64").astype(np.float32)
     out["x_col"] = cols
     return out
