@@ -16,7 +16,8 @@ _BINDING_NAMES = {
     "HLQ_F32", "HLQ_BF16", "HLQ_PER_TOKEN", "HLQ_PER_TENSOR", "HLQ_SUM", "HLQ_MEAN",
     "version", "status_string", "lib_handle", "LIB_PATH", "EXPORTED", "STEP_NAMES",
     "HLQ_STEPS_ALL", "hlq_lqs_workspace_size", "hlq_lqs_accumulate", "hlq_lqs_select",
-    "HLQ_LQS_STATS", "HLQ_LQS_THRESHOLD",
+    "HLQ_LQS_STATS", "HLQ_LQS_THRESHOLD", "hlq_conv_backward",
+    "hlq_conv_backward_workspace_size", "hlq_conv_gemm_acc",
 }
 
 

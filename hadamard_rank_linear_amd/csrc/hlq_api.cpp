@@ -174,6 +174,9 @@ hlq::TrArgs make_tr_args(const Layout& L, const void* g_y, int gy_dtype, const u
   a.gyreg_wgs = 0;
   a.wg_x = L.ntr_t * L.nch_i;
   a.wg_w = L.ntr_o * L.nch_i;
+  a.conv = 0;
+  a.Hc = a.Wc = a.Cc = a.P = a.Q = a.S = a.cstride = a.cpad = 0;
+  a.zero_row = nullptr;
   return a;
 }
 
@@ -395,6 +398,151 @@ hlq_status hlq_gemm_pair_acc(const void* workspace, size_t workspace_bytes, int6
                                 ws + L.pub.q_xl, O, L.pub.kw_pitch, L.plan_gw, nullptr, nullptr,
                                 0, 1.f, nullptr, static_cast<hipStream_t>(stream),
                                 hlq::EPI_I32, acc_x, acc_w));
+  return HLQ_OK;
+}
+
+// ---------------------------------------------------------------- convolution
+
+namespace {
+
+struct ConvShape {
+  int64_t N, H, W, C, O, R, S, P, Q, T, I;
+  int stride, pad;
+};
+
+hlq_status check_conv(int64_t N, int64_t H, int64_t W, int64_t C, int64_t O, int R, int S,
+                      int stride, int pad, int block, int rank, ConvShape* cs) {
+  if (N <= 0 || H <= 0 || W <= 0 || C <= 0 || O <= 0 || R <= 0 || S <= 0 || stride <= 0 ||
+      pad < 0)
+    return HLQ_ERR_SHAPE;
+  if (H + 2 * pad < R || W + 2 * pad < S) return HLQ_ERR_SHAPE;
+  ConvShape c;
+  c.N = N; c.H = H; c.W = W; c.C = C; c.O = O; c.R = R; c.S = S;
+  c.stride = stride; c.pad = pad;
+  c.P = (H + 2 * pad - R) / stride + 1;
+  c.Q = (W + 2 * pad - S) / stride + 1;
+  c.T = N * c.P * c.Q;
+  c.I = (int64_t)R * S * C;
+  if (C % 8) return HLQ_ERR_SHAPE;
+  // the kernels index pixels, output positions and channels in 32 bits
+  const int64_t lim = (int64_t)1 << 31;
+  if (N * H * W >= lim || c.T >= lim || c.I >= lim) return HLQ_ERR_OVERFLOW;
+  hlq_status st = check_shape(c.T, c.I, O, block, rank);
+  if (st != HLQ_OK) return st;
+  // the input gradient's INT32 sums run over every (tap, O) pair
+  if (O * R * S > kMaxO) return HLQ_ERR_OVERFLOW;
+  *cs = c;
+  return HLQ_OK;
+}
+
+// Workspace of the convolution backward: the linear backward's for
+// (T = N*P*Q, I = R*S*C, O), then the zero row of the input-gradient GEMM.
+struct ConvLayout {
+  Layout L;
+  size_t zero, total;
+};
+
+ConvLayout make_conv_layout(const ConvShape& c, int block, int rank) {
+  ConvLayout cl;
+  cl.L = make_layout(c.T, c.I, c.O, block, rank);
+  cl.zero = cl.L.pub.total;
+  cl.total = align256(cl.zero + (size_t)cl.L.pub.kx_pitch);
+  return cl;
+}
+
+hlq::ConvGemm conv_gemm(const ConvShape& c, const ConvLayout& cl, const uint8_t* ws) {
+  hlq::ConvGemm g;
+  memset(&g, 0, sizeof(g));
+  g.q_gy = ws + cl.L.pub.q_gy;
+  g.q_w = ws + cl.L.pub.q_w;
+  g.zero = ws + cl.zero;
+  g.kx_pitch = cl.L.pub.kx_pitch;
+  g.N = c.N; g.H = c.H; g.W = c.W; g.C = c.C; g.P = c.P; g.Q = c.Q; g.S = c.S;
+  g.taps = c.R * c.S;
+  g.stride = c.stride; g.pad = c.pad;
+  return g;
+}
+
+}  // namespace
+
+size_t hlq_conv_backward_workspace_size(int64_t N, int64_t H, int64_t W, int64_t C, int64_t O,
+                                        int R, int S, int stride, int pad, int block,
+                                        int rank) {
+  ConvShape c;
+  if (check_conv(N, H, W, C, O, R, S, stride, pad, block, rank, &c) != HLQ_OK) return 0;
+  return make_conv_layout(c, block, rank).total;
+}
+
+hlq_status hlq_conv_backward(const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                             const float* x_scales, const void* w, int w_dtype, int64_t N,
+                             int64_t H, int64_t W, int64_t C, int64_t O, int R, int S,
+                             int stride, int pad, int block, int rank, int gx_mode,
+                             int gw_mode, int reduction, float* g_x, float* g_w,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!g_y || !x_codes || !x_scales || !w || !g_x || !g_w) return HLQ_ERR_NULL;
+  if ((gy_dtype != HLQ_F32 && gy_dtype != HLQ_BF16) ||
+      (w_dtype != HLQ_F32 && w_dtype != HLQ_BF16))
+    return HLQ_ERR_DTYPE;
+  ConvShape c;
+  hlq_status st = check_conv(N, H, W, C, O, R, S, stride, pad, block, rank, &c);
+  if (st != HLQ_OK) return st;
+  // g_x: per-tensor scales only (per-token scales of H.g_y and H.w would not
+  // factor out of the sum over the taps)
+  if (gx_mode != HLQ_PER_TENSOR || (gw_mode != HLQ_PER_TOKEN && gw_mode != HLQ_PER_TENSOR) ||
+      (reduction != HLQ_SUM && reduction != HLQ_MEAN))
+    return HLQ_ERR_MODE;
+  const ConvLayout cl = make_conv_layout(c, block, rank);
+  if (!workspace || workspace_bytes < cl.total) return HLQ_ERR_WORKSPACE;
+  if (!aligned16(g_y) || !aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w) ||
+      !aligned16(g_x) || !aligned16(g_w) || !aligned16(workspace))
+    return HLQ_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const bool gw_tok = gw_mode == HLQ_PER_TOKEN;
+  hlq::TrArgs a = make_tr_args(cl.L, g_y, gy_dtype, x_codes, x_scales, w, w_dtype, c.T, c.I,
+                               c.O, block, false, gw_tok, ws);
+  a.conv = 1;
+  a.Hc = c.H; a.Wc = c.W; a.Cc = c.C; a.P = c.P; a.Q = c.Q; a.S = c.S;
+  a.cstride = c.stride; a.cpad = c.pad;
+  a.zero_row = ws + cl.zero;
+  HLQ_TRY(hlq::launch_tr(a, hlq::PASS_MAX, block, rank, s));
+  HLQ_TRY(hlq::launch_tr_reduce(a, s));
+  HLQ_TRY(hlq::launch_tr(a, hlq::PASS_QUANT, block, rank, s));
+  const float gw_alpha =
+      reduction == HLQ_MEAN ? (float)(1.0 / ((double)block * (double)c.T)) : 1.0f / (float)block;
+  HLQ_TRY(hlq::launch_gemm(false, a.q_gyl, a.q_xl, c.O, c.I, a.kwb, cl.L.plan_gw, a.s_gyl,
+                           gw_tok ? 1 : 0, a.s_xl, gw_tok ? 1 : 0, gw_alpha, hlq::EPI_F32, g_w,
+                           nullptr, reinterpret_cast<int32_t*>(ws + cl.L.partial), s));
+  hlq::ConvGemm g = conv_gemm(c, cl, ws);
+  g.s_gy = a.s_gy;
+  g.s_w = a.s_w;
+  g.alpha = 1.0f / (float)block;
+  g.epi = hlq::EPI_F32;
+  g.g_x = g_x;
+  HLQ_TRY(hlq::launch_dgrad(g, s));
+  return HLQ_OK;
+}
+
+hlq_status hlq_conv_gemm_acc(const void* workspace, size_t workspace_bytes, int64_t N,
+                             int64_t H, int64_t W, int64_t C, int64_t O, int R, int S,
+                             int stride, int pad, int block, int rank, int32_t* acc_x,
+                             int32_t* acc_w, void* stream) {
+  if (!workspace || !acc_x || !acc_w) return HLQ_ERR_NULL;
+  ConvShape c;
+  hlq_status st = check_conv(N, H, W, C, O, R, S, stride, pad, block, rank, &c);
+  if (st != HLQ_OK) return st;
+  const ConvLayout cl = make_conv_layout(c, block, rank);
+  if (workspace_bytes < cl.total) return HLQ_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(acc_x) || !aligned16(acc_w)) return HLQ_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  HLQ_TRY(hlq::launch_gemm(false, ws + cl.L.pub.q_gyl, ws + cl.L.pub.q_xl, c.O, c.I,
+                           cl.L.pub.kw_pitch, cl.L.plan_gw, nullptr, 0, nullptr, 0, 1.f,
+                           hlq::EPI_I32, nullptr, acc_w, nullptr, s));
+  hlq::ConvGemm g = conv_gemm(c, cl, ws);
+  g.epi = hlq::EPI_I32;
+  g.acc_x = acc_x;
+  HLQ_TRY(hlq::launch_dgrad(g, s));
   return HLQ_OK;
 }
 

@@ -133,11 +133,20 @@ struct GemmArgs {
   float alpha;
   float* C;
   int32_t* Ci;
+  // Implicit-GEMM input gradient of a convolution (gemm_tile CONV): output
+  // rows m = input pixels (n, h, w) of an [N][cH][cW] image, columns the cC
+  // channels; K stage st belongs to tap (st / cSO) = r * cS + s.  A (the
+  // H.g_y codes, pitch bytes per output pixel of the cP x cQ grid) is read at
+  // the output pixel (n, (h + pad - r) / stride, (w + pad - s) / stride)
+  // when that is a whole in-range position, else at `zero` (pitch zero
+  // bytes); B (the H.w codes) at row tap * cC + channel.
+  int32_t cH, cW, cP, cQ, cS, cC, cstride, cpad, cSO;
+  const uint8_t* zero;
 };
 
 // One output tile (workgroup w of the tile grid, K split `split`) of one GEMM.
 // Every thread of the workgroup calls it; `lds` holds NS * STAGE bytes.
-template <bool INT4, int BM, int BN, int KB, int NS, int EPI>
+template <bool INT4, int BM, int BN, int KB, int NS, int EPI, bool CONV = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t split,
                                           uint8_t* lds, float* sc) {
   using G = GemmShape<INT4, BM, BN, KB, NS>;
@@ -163,27 +172,71 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 
   // DMA sources of this lane for stage 0 (rows past M / N re-read the last row)
   const uint8_t* src[IPW];
+  // CONV: input pixel (n, h, w) of each A slot's row, channel of each B
+  // slot's row, byte offset of each slot's 16-byte chunk
+  int32_t cv_n[CONV ? IA : 1], cv_h[CONV ? IA : 1], cv_w[CONV ? IA : 1];
+  int32_t cv_c[CONV ? IB : 1], cv_off[CONV ? IPW : 1];
 #pragma unroll
   for (int j = 0; j < IA; ++j) {
     const int slot = (wave * IA + j) * 64 + lane;
     const int row = slot / CPR, c = (slot % CPR) ^ chunk_swz<KB>(row);
     const int64_t r = m0 + row < M ? m0 + row : M - 1;
-    src[j] = A + r * pitch + kbase + c * 16;
+    if constexpr (CONV) {
+      const int32_t hw = g.cH * g.cW, m = (int32_t)r;
+      cv_n[j] = m / hw;
+      cv_h[j] = (m - cv_n[j] * hw) / g.cW;
+      cv_w[j] = m - cv_n[j] * hw - cv_h[j] * g.cW;
+      cv_off[j] = c * 16;
+      src[j] = nullptr;
+    } else {
+      src[j] = A + r * pitch + kbase + c * 16;
+    }
   }
 #pragma unroll
   for (int j = 0; j < IB; ++j) {
     const int slot = (wave * IB + j) * 64 + lane;
     const int row = slot / CPR, c = (slot % CPR) ^ chunk_swz<KB>(row);
     const int64_t r = n0 + row < N ? n0 + row : N - 1;
-    src[IA + j] = B + r * pitch + kbase + c * 16;
+    if constexpr (CONV) {
+      cv_c[j] = (int32_t)r;
+      cv_off[IA + j] = c * 16;
+      src[IA + j] = nullptr;
+    } else {
+      src[IA + j] = B + r * pitch + kbase + c * 16;
+    }
   }
-#define HLQ_GEMM_ISSUE(st, bf)                                                           \
-  do {                                                                                   \
-    uint8_t* base_ = lds + (bf) * G::STAGE;                                              \
-    for (int j = 0; j < IA; ++j) lds_dma16(src[j] + (st) * KB, base_ + (wave * IA + j) * 1024); \
-    for (int j = 0; j < IB; ++j)                                                         \
-      lds_dma16(src[IA + j] + (st) * KB, base_ + BM * KB + (wave * IB + j) * 1024);      \
-  } while (0)
+  // Issue the LDS DMA of K stage st into ring buffer bf.
+  auto issue = [&](int64_t st, int bf) {
+    uint8_t* base_ = lds + bf * G::STAGE;
+    if constexpr (CONV) {
+      const int32_t tap = (int32_t)st / g.cSO, ko = (int32_t)st - tap * g.cSO;
+      const int32_t tr = tap / g.cS, ts = tap - tr * g.cS;
+#pragma unroll
+      for (int j = 0; j < IA; ++j) {
+        int32_t p = cv_h[j] + g.cpad - tr, q = cv_w[j] + g.cpad - ts;
+        bool ok = p >= 0 && q >= 0;
+        if (g.cstride != 1) {
+          ok = ok && p % g.cstride == 0 && q % g.cstride == 0;
+          p /= g.cstride;
+          q /= g.cstride;
+        }
+        ok = ok && p < g.cP && q < g.cQ;
+        const uint8_t* row = ok ? A + ((int64_t)(cv_n[j] * g.cP + p) * g.cQ + q) * pitch : g.zero;
+        lds_dma16(row + ko * KB + cv_off[j], base_ + (wave * IA + j) * 1024);
+      }
+#pragma unroll
+      for (int j = 0; j < IB; ++j)
+        lds_dma16(B + (int64_t)(tap * g.cC + cv_c[j]) * pitch + ko * KB + cv_off[IA + j],
+                  base_ + BM * KB + (wave * IB + j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < IA; ++j) lds_dma16(src[j] + st * KB, base_ + (wave * IA + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < IB; ++j)
+        lds_dma16(src[IA + j] + st * KB, base_ + BM * KB + (wave * IB + j) * 1024);
+    }
+  };
+#define HLQ_GEMM_ISSUE(st, bf) issue((st), (bf))
   // wait until at most k stages of this wave's DMA are still in flight
 #define HLQ_GEMM_WAIT(k)                                        \
   do {                                                          \
@@ -396,6 +449,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
   gemm_tile<INT4, BM, BN, KB, NS, EPI>(g, blockIdx.x, blockIdx.y, lds, sc);
 }
 
+// Input gradient of a convolution as an implicit GEMM over the taps (CONV
+// addressing in gemm_tile): no im2col / col2im buffer; the INT32 sum runs over
+// every (tap, O) pair of an input pixel, so one per-tensor epilogue finishes it.
+template <int BM, int BN, int KB, int NS, int EPI>
+__global__ __launch_bounds__(256, 2) void k_dgrad(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * GemmShape<true, BM, BN, KB, NS>::STAGE];
+  __shared__ float sc[BM + BN];
+  gemm_tile<true, BM, BN, KB, NS, EPI, true>(g, blockIdx.x, 0, lds, sc);
+}
+
 // Both GEMMs of the backward in one launch (fp32 epilogues, no split-K): the
 // first n1 workgroups take the g_w tiles (longer K, so they start first), the
 // rest the g_x tiles, which fill the CUs around them.  One launch instead of
@@ -564,6 +627,25 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
 #undef HLQ_W3
 #undef HLQ_X0
 #undef HLQ_X1
+  return hipGetLastError();
+}
+
+hipError_t launch_dgrad(const ConvGemm& c, hipStream_t s) {
+  if (c.kx_pitch % 64 || c.taps <= 0 || c.C % 8) return hipErrorInvalidValue;
+  if ((c.epi == EPI_F32 && (!c.g_x || !c.s_gy || !c.s_w)) || (c.epi == EPI_I32 && !c.acc_x))
+    return hipErrorInvalidValue;
+  const int64_t M = c.N * c.H * c.W;
+  const int64_t so = c.kx_pitch / 64;  // 64-byte stages per tap
+  GemmArgs a{c.q_gy, c.q_w, M, c.C, c.kx_pitch, so * c.taps, so * c.taps, c.s_gy, 0, c.s_w, 0,
+             c.alpha, c.g_x, c.acc_x};
+  a.cH = (int32_t)c.H; a.cW = (int32_t)c.W; a.cP = (int32_t)c.P; a.cQ = (int32_t)c.Q;
+  a.cS = (int32_t)c.S; a.cC = (int32_t)c.C; a.cstride = c.stride; a.cpad = c.pad;
+  a.cSO = (int32_t)so;
+  a.zero = c.zero;
+  const int64_t tiles = (int64_t)cdiv(M, 128) * cdiv(c.C, 128);
+  const dim3 g((unsigned)((tiles + 7) / 8 * 8));
+  if (c.epi == EPI_F32) hipLaunchKernelGGL((k_dgrad<128, 128, 64, 3, EPI_F32>), g, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_dgrad<128, 128, 64, 3, EPI_I32>), g, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

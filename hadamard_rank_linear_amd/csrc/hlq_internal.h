@@ -47,6 +47,12 @@ struct TrArgs {
   int64_t wg_gy, wg_x, wg_w;  // tiles of each job
   int64_t gy_workers;         // LDS-engine g_y tiles of the transform launch (set per launch)
   int64_t gyreg_wgs;          // register-path g_y workgroups of that launch (4 tiles each)
+  // Convolution (conv = 1): the x job gathers im2col of the ACBP-coded input
+  // [N][Hc][Wc][Cc] (one scale per pixel) for the output grid P x Q, taps
+  // R x S (feature (r*S + s)*Cc + c, so I = R*S*Cc), stride, zero padding.
+  int conv;
+  int64_t Hc, Wc, Cc, P, Q, S, cstride, cpad;
+  uint8_t* zero_row;          // kxb zero bytes written by QUANT (conv), else null
 };
 
 // Launch configuration of one integer GEMM C[m][n] = sum_k A[m][k] B[n][k],
@@ -128,6 +134,25 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
                             int gw_step, float gw_alpha, float* g_w, hipStream_t s,
                             GemmEpi epi = EPI_F32, int32_t* acc_x = nullptr,
                             int32_t* acc_w = nullptr);
+
+// Input gradient of a convolution, implicit GEMM over the taps:
+// g_x[(n,h,w)][c] = alpha * s_gy * s_w * sum_{tap, o} q_gy[(n,p,q)][o] *
+// q_w[tap * C + c][o] over the taps whose (p, q) is a whole in-range output
+// position (per-tensor scales only).  EPI_I32 stores the INT32 sums instead.
+struct ConvGemm {
+  const uint8_t* q_gy;  // [N*P*Q][kx_pitch] INT4 codes of H.g_y
+  const uint8_t* q_w;   // [R*S*C][kx_pitch] INT4 codes of H.w (K-major)
+  const uint8_t* zero;  // kx_pitch zero bytes
+  int64_t kx_pitch, N, H, W, C, P, Q, S, taps;
+  int stride, pad;
+  const float* s_gy;    // [1]
+  const float* s_w;     // [1]
+  float alpha;          // 1 / n
+  GemmEpi epi;
+  float* g_x;           // [N*H*W][C]
+  int32_t* acc_x;       // [N*H*W][C]
+};
+hipError_t launch_dgrad(const ConvGemm& c, hipStream_t s);
 
 hipError_t launch_gemm_finalize(const int32_t* partial, int splits, int64_t M,
                                 int64_t N, const float* sa, int sa_step,

@@ -79,13 +79,17 @@ struct RdB16 {
     return __uint_as_float((uint32_t)t[r * P_B16 + c] << 16);
   }
 };
+// ACBP codes: one scale per (row, 8-column chunk) of the tile, s[r][c / 8]
+// (a linear layer's x tile repeats its token's scale; a convolution's im2col
+// tile can change input pixel, hence scale, at every tap boundary).
+constexpr int X_CHUNKS = CW / 8;
 struct RdI4 {
   const uint8_t* q;
   const float* s;
   __device__ __forceinline__ float operator()(int r, int c) const {
     const int byte = q[r * P_I4 + (c >> 1)];
     const int code = __builtin_amdgcn_sbfe(byte, (c & 1) * 4, 4);
-    return s[r] * (float)code;
+    return s[r * X_CHUNKS + (c >> 3)] * (float)code;
   }
 };
 
@@ -708,6 +712,12 @@ __device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
 }
 
 // ---- job: x tile (ACBP codes, low-rank columns along T for g_w)
+// Linear layer: rows are tokens of the code matrix [T][I/2].  Convolution
+// (a.conv): rows are output pixels t = (n, p, q) and columns the im2col
+// features (r*S + s)*C + c; each 8-column chunk (C is a multiple of 8, so a
+// chunk stays inside one tap) gathers 4 code bytes of input pixel
+// (n, p*stride - pad + r, q*stride - pad + s) with that pixel's scale, or
+// zeros outside the image.
 template <int PASS, int N, int R>
 __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red) {
   const int tid = threadIdx.x;
@@ -718,27 +728,71 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
   const int rows = (int)(a.T - t0 < TT ? a.T - t0 : TT);
   const int cols = (int)(a.I - c0 < CW ? a.I - c0 : CW);
   uint8_t* codes = smem;                                          // [TT][P_I4] bytes
-  float* scales = reinterpret_cast<float*>(smem + TT * P_I4);     // [TT]
+  float* scales = reinterpret_cast<float*>(smem + TT * P_I4);     // [TT][X_CHUNKS]
   // 64 code bytes per tile row: 4 lanes x 16 bytes, 64 rows per sweep.  Rows
   // are I/2 bytes (a multiple of 4, not of 16), so the loads are dwords.
   constexpr int SW = TT / 64;
   const int lr = tid >> 2, lq = tid & 3;
   const int col = lq * 32;
   uint32_t w4[SW][4];
+  if (!a.conv) {
 #pragma unroll
-  for (int sw = 0; sw < SW; ++sw) {
-    const int row = sw * 64 + lr;
+    for (int sw = 0; sw < SW; ++sw) {
+      const int row = sw * 64 + lr;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) w4[sw][d] = 0u;
-    if (row < rows && col < cols) {
-      const uint32_t* src =
-          reinterpret_cast<const uint32_t*>(a.xc + (t0 + row) * (a.I / 2) + (c0 + col) / 2);
+      for (int d = 0; d < 4; ++d) w4[sw][d] = 0u;
+      if (row < rows && col < cols) {
+        const uint32_t* src =
+            reinterpret_cast<const uint32_t*>(a.xc + (t0 + row) * (a.I / 2) + (c0 + col) / 2);
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        if (col + 8 * d < cols) w4[sw][d] = src[d];
+        for (int d = 0; d < 4; ++d)
+          if (col + 8 * d < cols) w4[sw][d] = src[d];
+      }
     }
+    if (tid < TT) {
+      const float sv = tid < rows ? a.xs[t0 + tid] : 0.f;
+#pragma unroll
+      for (int k = 0; k < X_CHUNKS; k += 4)
+        *reinterpret_cast<float4*>(scales + tid * X_CHUNKS + k) = make_float4(sv, sv, sv, sv);
+    }
+  } else {
+    // taps and channels of this thread's four chunks
+    int tap_r[4], tap_s[4];
+    int64_t chan[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int64_t cc = c0 + col + 8 * d;
+      const int64_t rs = cc / a.Cc;
+      chan[d] = cc - rs * a.Cc;
+      tap_r[d] = (int)(rs / a.S);
+      tap_s[d] = (int)(rs - (int64_t)tap_r[d] * a.S);
+    }
+    float sv[SW][4];
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) {
+      const int row = sw * 64 + lr;
+      const int64_t t = t0 + row;
+      const int64_t pq = a.P * a.Q;
+      const int64_t nn = t / pq, rem = t - nn * pq;
+      const int64_t p = rem / a.Q, q = rem - p * a.Q;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        w4[sw][d] = 0u;
+        sv[sw][d] = 0.f;
+        const int64_t hh = p * a.cstride - a.cpad + tap_r[d];
+        const int64_t ww = q * a.cstride - a.cpad + tap_s[d];
+        if (row < rows && col + 8 * d < cols && hh >= 0 && hh < a.Hc && ww >= 0 && ww < a.Wc) {
+          const int64_t pix = (nn * a.Hc + hh) * a.Wc + ww;
+          w4[sw][d] = *reinterpret_cast<const uint32_t*>(a.xc + pix * (a.Cc / 2) + chan[d] / 2);
+          sv[sw][d] = a.xs[pix];
+        }
+      }
+    }
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw)
+      *reinterpret_cast<float4*>(scales + (sw * 64 + lr) * X_CHUNKS + lq * 4) =
+          make_float4(sv[sw][0], sv[sw][1], sv[sw][2], sv[sw][3]);
   }
-  if (tid < TT) scales[tid] = tid < rows ? a.xs[t0 + tid] : 0.f;
 #pragma unroll
   for (int sw = 0; sw < SW; ++sw)
     *reinterpret_cast<uint4*>(codes + (sw * 64 + lr) * P_I4 + col / 2) =
@@ -789,10 +843,17 @@ __device__ void tr_job_w(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
 // F32: the g_y / w tiles hold fp32 (any fp32 source); otherwise bf16.
 template <int PASS, int N, int R, bool F32>
 __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
-  static_assert(TT * P_I4 + TT * 4 <= TileSmem<F32>::bytes, "x tile fits the smem buffer");
+  static_assert(TT * P_I4 + TT * X_CHUNKS * 4 <= TileSmem<F32>::bytes, "x tile fits the smem buffer");
   static_assert(CW * OUT_PITCH <= TileSmem<F32>::bytes, "staging fits the smem buffer");
   __shared__ __attribute__((aligned(16))) uint8_t smem[TileSmem<F32>::bytes];
   __shared__ float red[4 * CW];
+  if constexpr (PASS == PASS_QUANT) {
+    // the zero row the convolution's input-gradient GEMM reads for taps
+    // outside the image
+    if (a.zero_row && blockIdx.x == 0)
+      for (int64_t i = threadIdx.x; i < a.kxb / 16; i += 256)
+        reinterpret_cast<uint4*>(a.zero_row)[i] = make_uint4(0, 0, 0, 0);
+  }
   if (blockIdx.x == 0 && threadIdx.x < 4) {
     if constexpr (PASS == PASS_MAX) {
       a.tmax[threadIdx.x] = 0u;  // k_tr_reduce folds into it

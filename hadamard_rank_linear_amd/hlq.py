@@ -29,6 +29,9 @@ EXPORTED = (
     "hlq_gemm_pair_acc",
     "hlq_gemm_gx_acc",
     "hlq_gemm_gw_acc",
+    "hlq_conv_backward_workspace_size",
+    "hlq_conv_backward",
+    "hlq_conv_gemm_acc",
     "hlq_lqs_workspace_size",
     "hlq_lqs_accumulate",
     "hlq_lqs_select",
@@ -81,6 +84,15 @@ def _load():
     lib.hlq_gemm_gx_acc.restype = I32
     lib.hlq_gemm_gw_acc.argtypes = [P, SZ, I64, I64, I64, I32, I32, P, P]
     lib.hlq_gemm_gw_acc.restype = I32
+    lib.hlq_conv_backward_workspace_size.argtypes = [I64, I64, I64, I64, I64, I32, I32, I32, I32,
+                                                     I32, I32]
+    lib.hlq_conv_backward_workspace_size.restype = SZ
+    lib.hlq_conv_backward.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I64, I64, I32, I32,
+                                      I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    lib.hlq_conv_backward.restype = I32
+    lib.hlq_conv_gemm_acc.argtypes = [P, SZ, I64, I64, I64, I64, I64, I32, I32, I32, I32, I32,
+                                      I32, P, P, P]
+    lib.hlq_conv_gemm_acc.restype = I32
     lib.hlq_lqs_workspace_size.argtypes = [I64, I64, I64, I32, I32]
     lib.hlq_lqs_workspace_size.restype = SZ
     lib.hlq_lqs_accumulate.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I32, I32, P, P,
@@ -292,6 +304,60 @@ def hlq_gemm_gw_acc(workspace, T, I, O, block, rank, acc_w=None, stream=None):
     _check("hlq_gemm_gw_acc", _lib.hlq_gemm_gw_acc(
         _ptr(workspace), _nbytes(workspace), T, I, O, block, rank, _ptr(acc_w), _stream(stream)))
     return acc_w
+
+
+def hlq_conv_backward_workspace_size(N, H, W, C, O, R, S, stride, pad, block, rank) -> int:
+    return int(_lib.hlq_conv_backward_workspace_size(N, H, W, C, O, R, S, stride, pad, block,
+                                                     rank))
+
+
+def _conv_out(H, R, stride, pad):
+    return (H + 2 * pad - R) // stride + 1
+
+
+def hlq_conv_backward(g_y, x_codes, x_scales, w, N, H, W, C, R, S, stride, pad, block, rank,
+                      gx_mode=HLQ_PER_TENSOR, gw_mode=HLQ_PER_TOKEN, reduction=HLQ_SUM,
+                      g_x=None, g_w=None, workspace=None, stream=None):
+    """HLQ/HOT backward of a 2-D convolution: returns (g_x [N*H*W, C],
+    g_w [O, R*S*C]) fp32.  g_y [N*P*Q, O] (rows (n, p, q)); (x_codes,
+    x_scales) = hlq_compress_act of x as [N*H*W, C]; w [O, R*S*C] (OHWI)."""
+    import torch
+    P, Q = _conv_out(H, R, stride, pad), _conv_out(W, S, stride, pad)
+    T, O = g_y.shape
+    if T != N * P * Q or tuple(w.shape) != (O, R * S * C):
+        raise ValueError("g_y must be [N*P*Q, O] and w [O, R*S*C]")
+    dev = g_y.device
+    if g_x is None:
+        g_x = torch.empty((N * H * W, C), dtype=torch.float32, device=dev)
+    if g_w is None:
+        g_w = torch.empty((O, R * S * C), dtype=torch.float32, device=dev)
+    need = hlq_conv_backward_workspace_size(N, H, W, C, O, R, S, stride, pad, block, rank)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _expect("x_codes", x_codes, torch.uint8, (N * H * W, C // 2))
+    _expect("x_scales", x_scales, torch.float32, (N * H * W,))
+    _expect("g_x", g_x, torch.float32, (N * H * W, C))
+    _expect("g_w", g_w, torch.float32, (O, R * S * C))
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
+    _require_cuda(g_y, x_codes, x_scales, w, g_x, g_w, workspace)
+    _check("hlq_conv_backward", _lib.hlq_conv_backward(
+        _ptr(g_y), _dtype_code(g_y), _ptr(x_codes), _ptr(x_scales), _ptr(w), _dtype_code(w),
+        N, H, W, C, O, R, S, stride, pad, block, rank, gx_mode, gw_mode, reduction, _ptr(g_x),
+        _ptr(g_w), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+    return g_x, g_w
+
+
+def hlq_conv_gemm_acc(workspace, N, H, W, C, O, R, S, stride, pad, block, rank, stream=None):
+    """INT32 accumulators (acc_x [N*H*W, C], acc_w [O, R*S*C]) of the
+    convolution backward's GEMMs, from a workspace it has filled."""
+    acc_x = _acc_out(workspace, None, (N * H * W, C))
+    acc_w = _acc_out(workspace, None, (O, R * S * C))
+    _require_cuda(workspace, acc_x, acc_w)
+    _check("hlq_conv_gemm_acc", _lib.hlq_conv_gemm_acc(
+        _ptr(workspace), _nbytes(workspace), N, H, W, C, O, R, S, stride, pad, block, rank,
+        _ptr(acc_x), _ptr(acc_w), _stream(stream)))
+    return acc_x, acc_w
 
 
 HLQ_LQS_STATS = 16

@@ -112,6 +112,8 @@ def _draw(dist: str, shape, rng: np.random.Generator, cfg: LayerConfig) -> np.nd
         return rng.standard_normal(shape) * c[None, :]
     if dist == "he_normal(2304)":
         return math.sqrt(2.0 / 2304.0) * rng.standard_normal(shape)
+    if dist == "he_normal(fan_in)":   # fan-in = the feature count shape[1]
+        return math.sqrt(2.0 / shape[1]) * rng.standard_normal(shape)
     raise ValueError(f"unknown distribution {dist!r}")
 
 
@@ -141,5 +143,76 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, plant_zero_rows: bool = False) 
         gy[0, :] = 0.0
         x[0, :] = 0.0
         w[0, :] = 0.0
+    return dict(gy=_store(gy, cfg.dtype), x=_store(x, cfg.dtype),
+                w=_store(w, cfg.dtype), dtype=cfg.dtype)
+
+
+# ---------------------------------------------------------------- convolutions
+
+@dataclasses.dataclass(frozen=True)
+class ConvConfig:
+    """A 2-D convolution layer: NHWC input [N, H, W, C], OHWI weight
+    [O, R, S, C], zero padding.  Tokens of its linear form are the output
+    pixels (n, p, q); features are (r, s, c)."""
+    index: int
+    name: str
+    N: int
+    H: int
+    W: int
+    C: int
+    O: int
+    R: int
+    S: int
+    stride: int
+    pad: int
+    dtype: int
+    block: int
+    rank: int
+    gx_mode: int
+    gw_mode: int
+    reduction: int
+    gy_dist: str
+    x_dist: str
+    w_dist: str
+
+    @property
+    def P(self) -> int:
+        return (self.H + 2 * self.pad - self.R) // self.stride + 1
+
+    @property
+    def Q(self) -> int:
+        return (self.W + 2 * self.pad - self.S) // self.stride + 1
+
+    @property
+    def T(self) -> int:
+        return self.N * self.P * self.Q
+
+    @property
+    def I(self) -> int:
+        return self.R * self.S * self.C
+
+    @property
+    def Tl(self) -> int:
+        return self.T * self.rank // self.block
+
+
+CONV_LAYERS = [
+    # ResNet-50 stage 3, 3x3 convolution at batch 256 (the im2col layer config
+    # above, run as a convolution)
+    ConvConfig(20, "resnet50_s3_conv3x3", 256, 14, 14, 256, 256, 3, 3, 1, 1, BF16, 16, 4,
+               PER_TENSOR, PER_TENSOR, SUM, "normal(1e-3)", "relu(normal(1))", "he_normal(fan_in)"),
+    # small strided, padded convolution
+    ConvConfig(21, "small_stride2_pad1", 2, 15, 15, 16, 32, 3, 3, 2, 1, F32, 16, 8,
+               PER_TENSOR, PER_TOKEN, SUM, "normal(1)", "relu(normal(1))", "he_normal(fan_in)"),
+]
+CONV_BY_NAME = {c.name: c for c in CONV_LAYERS}
+
+
+def make_conv_inputs(cfg: ConvConfig, seed: int = 0) -> dict:
+    """g_y [N*P*Q x O] (rows (n, p, q)), x [N*H*W x C] (rows (n, h, w)) and
+    w [O x R*S*C] (OHWI) for ``cfg``, in the storage dtype."""
+    gy = _draw(cfg.gy_dist, (cfg.T, cfg.O), _rng(seed, cfg.index, 0), cfg)
+    x = _draw(cfg.x_dist, (cfg.N * cfg.H * cfg.W, cfg.C), _rng(seed, cfg.index, 1), cfg)
+    w = _draw(cfg.w_dist, (cfg.O, cfg.I), _rng(seed, cfg.index, 2), cfg)
     return dict(gy=_store(gy, cfg.dtype), x=_store(x, cfg.dtype),
                 w=_store(w, cfg.dtype), dtype=cfg.dtype)

@@ -230,6 +230,52 @@ hlq_status hlq_gemm_gw_acc(const void* workspace, size_t workspace_bytes, int64_
                            void* stream);
 
 /*
+ * The HLQ/HOT backward of one 2-D convolution (HLQ abstract: backpropagation
+ * of convolutional and linear layers; HOT summary, "Key results": ResNet-50
+ * at batch 256), as implicit GEMMs: no im2col or col2im buffer.
+ *   y[n,p,q,o] = sum_{r,s,c} x[n, p*stride - pad + r, q*stride - pad + s, c]
+ *                * w[o,r,s,c]   (zero padding; P = (H + 2 pad - R)/stride + 1,
+ *                                Q = (W + 2 pad - S)/stride + 1)
+ * is the linear layer y = im2col(x) . w^T with tokens t = (n, p, q) and
+ * features i = (r*S + s)*C + c; the backward is that layer's (same
+ * transforms, quantizers, codes and g_w), with the g_w path's low-rank x
+ * gathered from the ACBP codes of x itself and g_x the sum over the taps
+ * that read each input pixel (col2im).
+ *   g_y      [N][P][Q][O] f32 or bf16.
+ *   x_codes, x_scales: hlq_compress_act of x viewed as [N*H*W][C] (one scale
+ *            per pixel).
+ *   w        [O][R][S][C] f32 or bf16.
+ *   g_x      [N][H][W][C] f32 out = s_gy * s_w / n * sum over taps and O of
+ *            the INT4 code products (an implicit GEMM over the taps).
+ *   g_w      [O][R][S][C] f32 out, as hlq_linear_backward's g_w.
+ * Requires C % 8 == 0, N*P*Q and O multiples of block, gx_mode ==
+ * HLQ_PER_TENSOR (HLQ_ERR_MODE otherwise: per-token scales of H.g_y and H.w
+ * do not factor out of the sum over the taps), O*R*S <= 171196 and
+ * T' = N*P*Q*rank/block <= 133143 (HLQ_ERR_OVERFLOW), pixel and position
+ * counts below 2^31.  workspace: hlq_conv_backward_workspace_size bytes.
+ * Launches: the transform MAX, reduce and QUANT passes, the INT8 g_w GEMM
+ * (with split-K partials when its grid is small), the INT4 input-gradient GEMM.
+ */
+size_t hlq_conv_backward_workspace_size(int64_t N, int64_t H, int64_t W, int64_t C, int64_t O,
+                                        int R, int S, int stride, int pad, int block,
+                                        int rank);
+hlq_status hlq_conv_backward(const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                             const float* x_scales, const void* w, int w_dtype, int64_t N,
+                             int64_t H, int64_t W, int64_t C, int64_t O, int R, int S,
+                             int stride, int pad, int block, int rank, int gx_mode,
+                             int gw_mode, int reduction, float* g_x, float* g_w,
+                             void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * INT32 accumulators of the convolution backward's two GEMMs from a workspace
+ * hlq_conv_backward has filled (tests): acc_x [N*H*W][C] (sums over taps and
+ * O, before the per-tensor scales), acc_w [O][R*S*C].
+ */
+hlq_status hlq_conv_gemm_acc(const void* workspace, size_t workspace_bytes, int64_t N,
+                             int64_t H, int64_t W, int64_t C, int64_t O, int R, int S,
+                             int stride, int pad, int block, int rank, int32_t* acc_x,
+                             int32_t* acc_w, void* stream);
+
+/*
  * Layer-wise quantizer selection (LQS).  "HOT: Hadamard-based Optimized
  * Training": HF page abstract (layer-wise quantizer selection), scime.ai
  * summary "Approach" (per-token vs per-tensor chosen per layer) and

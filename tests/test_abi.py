@@ -209,3 +209,33 @@ def test_binding_checks_caller_buffers():
     with pytest.raises(ValueError):
         h.hlq_compress_act(x, x_codes=torch.zeros((16, 8), dtype=torch.uint8),
                            x_scales=torch.zeros(16))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gy=None), 1), (dict(C=12), 2), (dict(H=9, W=9), 2),  # C % 8; N*P*Q = 162
+    (dict(stride=0), 2), (dict(R=40), 2), (dict(block=24), 3), (dict(rank=3), 4),
+    (dict(gx=0), 5),                                         # per-token g_x: not supported
+    (dict(red=3), 5), (dict(gy_dt=4), 6), (dict(w=(1 << 20) + 8), 7),
+    (dict(O=16, R=120, S=120, H=200, W=200, pad=0), 8),      # O*R*S beyond the INT32 bound
+    (dict(ws_bytes=64), 9),
+])
+def test_conv_backward_validates_before_launch(kw, status):
+    args = dict(gy=1 << 20, gy_dt=1, codes=1 << 20, scales=1 << 20, w=1 << 20, w_dt=1,
+                N=2, H=8, W=8, C=16, O=32, R=3, S=3, stride=1, pad=1, block=16, rank=8,
+                gx=1, gw=0, red=0, g_x=1 << 20, g_w=1 << 20, ws=1 << 20, ws_bytes=1 << 40,
+                stream=None)
+    args.update(kw)
+    lib = h.lib_handle()
+    got = lib.hlq_conv_backward(*(args[k] for k in (
+        "gy", "gy_dt", "codes", "scales", "w", "w_dt", "N", "H", "W", "C", "O", "R", "S",
+        "stride", "pad", "block", "rank", "gx", "gw", "red", "g_x", "g_w", "ws", "ws_bytes",
+        "stream")))
+    assert got == status
+
+
+def test_conv_workspace_covers_the_linear_layout():
+    c = wl.CONV_BY_NAME["resnet50_s3_conv3x3"]
+    conv = h.hlq_conv_backward_workspace_size(c.N, c.H, c.W, c.C, c.O, c.R, c.S, c.stride, c.pad,
+                                              c.block, c.rank)
+    lin = h.hlq_linear_backward_workspace_size(c.T, c.I, c.O, c.block, c.rank)
+    assert conv > lin > 0
