@@ -216,7 +216,7 @@ def test_binding_checks_caller_buffers():
     (dict(stride=0), 2), (dict(R=40), 2), (dict(block=24), 3), (dict(rank=3), 4),
     (dict(gx=0), 5),                                         # per-token g_x: not supported
     (dict(red=3), 5), (dict(gy_dt=4), 6), (dict(w=(1 << 20) + 8), 7),
-    (dict(O=16, R=120, S=120, H=200, W=200, pad=0), 8),      # O*R*S beyond the INT32 bound
+    (dict(O=16, R=120, S=120, H=135, W=135, pad=0), 8),      # O*R*S beyond the INT32 bound
     (dict(ws_bytes=64), 9),
 ])
 def test_conv_backward_validates_before_launch(kw, status):
