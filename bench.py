@@ -323,6 +323,59 @@ def time_int8_library_gemm(M, N, K, reps=20):
             "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
 
 
+def time_conv(cfg, steps, warmup):
+    """The convolution backward (hlq_conv_backward: implicit GEMMs, no
+    im2col / col2im buffer) on rotating device copies: µs per backward and
+    effective TOPS (the same integer work as its im2col linear form)."""
+    import numpy as np
+    import torch
+    import hadamard_rank_linear_amd as h
+    from hadamard_rank_linear_amd import workloads as wl
+    inp = wl.make_conv_inputs(cfg)
+    dev = torch.device("cuda:0")
+
+    def dev_t(a):
+        if cfg.dtype == wl.BF16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    geo = (cfg.N, cfg.H, cfg.W, cfg.C, cfg.O, cfg.R, cfg.S, cfg.stride, cfg.pad, cfg.block,
+           cfg.rank)
+    ws_bytes = h.hlq_conv_backward_workspace_size(*geo)
+    gy0, x0, w0 = dev_t(inp["gy"]), dev_t(inp["x"]), dev_t(inp["w"])
+    codes0, scales0 = h.hlq_compress_act(x0)
+    per_set = (gy0.numel() * gy0.element_size() + codes0.numel() + 4 * scales0.numel()
+               + w0.numel() * w0.element_size() + 4 * (x0.numel() + w0.numel()) + ws_bytes)
+    n = max(2, -(-2 * LLC_BYTES // per_set))
+    sets = [dict(gy=gy0.clone(), codes=codes0.clone(), scales=scales0.clone(), w=w0.clone(),
+                 g_x=torch.empty((cfg.N * cfg.H * cfg.W, cfg.C), dtype=torch.float32, device=dev),
+                 g_w=torch.empty((cfg.O, cfg.I), dtype=torch.float32, device=dev),
+                 ws=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)) for _ in range(n)]
+    del x0
+
+    def run(i):
+        st = sets[i % n]
+        h.hlq_conv_backward(st["gy"], st["codes"], st["scales"], st["w"], cfg.N, cfg.H, cfg.W,
+                            cfg.C, cfg.R, cfg.S, cfg.stride, cfg.pad, cfg.block, cfg.rank,
+                            cfg.gx_mode, cfg.gw_mode, cfg.reduction, g_x=st["g_x"],
+                            g_w=st["g_w"], workspace=st["ws"])
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    ops = 2 * cfg.T * cfg.I * cfg.O + 2 * cfg.Tl * cfg.O * cfg.I
+    del sets
+    torch.cuda.empty_cache()
+    return {"us": round(us, 2), "effective_tops": round(ops / (us * 1e-6) / 1e12, 1),
+            "shape": f"N={cfg.N} H={cfg.H} W={cfg.W} C={cfg.C} O={cfg.O} R={cfg.R} S={cfg.S} "
+                     f"stride={cfg.stride} pad={cfg.pad}", "rotating_sets": n}
+
+
 def time_lqs(cfg, inp, reps=10):
     """Layer-wise quantizer selection statistics of one calibration batch
     (hlq_lqs_accumulate: the backward's MAX and reduce launches, an error
@@ -497,6 +550,9 @@ def main():
         extra["vitb_fc2_us"] = extra["vitb_fc2"]["us"]
     if not args.no_extra:
         extra["per_config"] = per_config_side(max(10, args.steps // 2), args.warmup)
+        log("side measurement: ResNet-50 stage-3 convolution (implicit GEMM)")
+        extra["conv"] = {"resnet50_s3_conv3x3": time_conv(
+            wl.CONV_BY_NAME["resnet50_s3_conv3x3"], max(10, args.steps // 2), args.warmup)}
         log("context: torch bf16 and fp32 backward of the same layer")
         extra["context_torch_bf16_backward_us"] = time_torch_backward(cfg, inp, "bf16")
         extra["context_torch_fp32_backward_us"] = time_torch_backward(cfg, inp, "fp32", steps=10,
