@@ -17,7 +17,9 @@ _BINDING_NAMES = {
     "version", "status_string", "lib_handle", "LIB_PATH", "EXPORTED", "STEP_NAMES",
     "HLQ_STEPS_ALL", "hlq_lqs_workspace_size", "hlq_lqs_accumulate", "hlq_lqs_select",
     "HLQ_LQS_STATS", "HLQ_LQS_THRESHOLD", "hlq_conv_backward",
-    "hlq_conv_backward_workspace_size", "hlq_conv_gemm_acc",
+    "hlq_conv_backward_workspace_size", "hlq_conv_gemm_acc", "hlq_linear_backward_ablation",
+    "hlq_ablation_workspace_size", "VARIANT_NAMES", "HLQ_VAR_HQ4", "HLQ_VAR_Q4", "HLQ_VAR_HLA8_INT",
+    "HLQ_VAR_HLA8_EXT",
 }
 
 

@@ -17,6 +17,7 @@ LIB = os.path.join(HERE, "libhlq.so")
 SOURCES = [("hlq_tr.hip", f"hlq_tr{n}", [f"-DHLQ_TR_N={n}"]) for n in (16, 32, 64, 128)] + [
     ("hlq_gemm.hip", "hlq_gemm", []), ("hlq_lqs.hip", "hlq_lqs", []),
     ("hlq_acbp.hip", "hlq_acbp", []), ("hlq_noalloc.hip", "hlq_noalloc", []),
+    ("hlq_ablation.hip", "hlq_ablation", []),
     ("hlq_api.cpp", "hlq_api", [])]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -546,6 +546,160 @@ hlq_status hlq_conv_gemm_acc(const void* workspace, size_t workspace_bytes, int6
   return HLQ_OK;
 }
 
+// ---------------------------------------------------------------- ablation variants
+
+namespace {
+
+// One path's operands and GEMM under a variant (HLQ_VAR_*).  K = the
+// contracted dimension, Ma / Nb = the two output dimensions.
+struct AblPath {
+  int variant;
+  int64_t K, Ma, Nb;       // source sizes
+  int64_t MoA, Ko, Kpad;   // operand A rows (Ma or its low rank), K' (K or low rank)
+  float alpha;             // Hadamard along K: 1/n
+  size_t qA, qB, sA, sB, mA, mB, G, part, end;
+  hlq::GemmPlan plan;
+};
+
+bool var_ok(int v) { return v >= HLQ_VAR_HQ4 && v <= HLQ_VAR_HLA8_EXT; }
+
+AblPath abl_path(int variant, int64_t K, int64_t Ma, int64_t Nb, int n, int r, size_t off) {
+  AblPath p;
+  memset(&p, 0, sizeof(p));
+  p.variant = variant; p.K = K; p.Ma = Ma; p.Nb = Nb;
+  p.MoA = variant == HLQ_VAR_HLA8_EXT ? Ma / n * r : Ma;
+  p.Ko = variant == HLQ_VAR_HLA8_INT ? K / n * r : K;
+  p.Kpad = (p.Ko + 127) / 128 * 128;
+  p.alpha = (variant == HLQ_VAR_HQ4 || variant == HLQ_VAR_HLA8_INT) ? 1.0f / (float)n : 1.0f;
+  p.plan = hlq::plan_gemm(false, p.MoA, Nb, p.Kpad);
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  p.qA = take((size_t)p.MoA * p.Kpad);
+  p.qB = take((size_t)Nb * p.Kpad);
+  p.sA = take((size_t)p.MoA * 4);
+  p.sB = take((size_t)Nb * 4);
+  p.mA = take((size_t)p.MoA * 4);
+  p.mB = take((size_t)Nb * 4);
+  p.G = take(variant == HLQ_VAR_HLA8_EXT ? (size_t)p.MoA * Nb * 4 : 0);
+  p.part = take(p.plan.splits > 1 ? (size_t)p.plan.splits * p.MoA * Nb * 4 : 0);
+  p.end = off;
+  return p;
+}
+
+// Operand A (left, rows MoA) or B of one path.  src_a_rows: the source holds
+// the K axis along its columns (g_y for the g_x path) rather than its rows.
+hlq::AblOperand abl_operand(const AblPath& p, bool left, const void* src, int dt,
+                            const uint8_t* codes, const float* cscales, int64_t rows,
+                            int64_t cols, bool m_is_row, int n, int r, bool per_token,
+                            uint8_t* ws) {
+  hlq::AblOperand o;
+  memset(&o, 0, sizeof(o));
+  o.src = src; o.dt = dt; o.codes = codes; o.cscales = cscales;
+  o.rows = rows; o.cols = cols; o.m_is_row = m_is_row ? 1 : 0;
+  o.r = r;
+  o.qmax = (p.variant == HLQ_VAR_HQ4 || p.variant == HLQ_VAR_Q4) ? 7 : 127;
+  o.per_token = per_token ? 1 : 0;
+  const int64_t M = left ? p.Ma : p.Nb;
+  if (p.variant == HLQ_VAR_HLA8_EXT) {
+    o.along_m = left ? 1 : 0;
+    o.kind = left ? 2 : 0;
+  } else {
+    o.along_m = 0;
+    o.kind = p.variant == HLQ_VAR_Q4 ? 0 : p.variant == HLQ_VAR_HQ4 ? 1 : 2;
+  }
+  o.lines = o.along_m ? p.K : M;
+  o.blocks = (o.along_m ? M : p.K) / n;
+  o.Mo = left ? p.MoA : p.Nb;
+  o.Ko = p.Ko;
+  o.Kpad = p.Kpad;
+  o.q = reinterpret_cast<int8_t*>(ws + (left ? p.qA : p.qB));
+  o.s = reinterpret_cast<float*>(ws + (left ? p.sA : p.sB));
+  o.maxbits = reinterpret_cast<unsigned*>(ws + (left ? p.mA : p.mB));
+  return o;
+}
+
+struct AblLayout {
+  AblPath x, w;
+  size_t total;
+};
+
+AblLayout abl_layout(int64_t T, int64_t I, int64_t O, int n, int r, int gxv, int gwv) {
+  AblLayout L;
+  L.x = abl_path(gxv, O, T, I, n, r, 0);
+  L.w = abl_path(gwv, T, O, I, n, r, L.x.end);
+  L.total = L.w.end;
+  return L;
+}
+
+// GEMM of one path; fp32 result (or the external variant's expansion), and
+// the INT32 sums when acc is given.
+hlq_status abl_gemm(const AblPath& p, uint8_t* ws, bool tok, float out_alpha, float* out,
+                    int32_t* acc, int n, int r, hipStream_t s) {
+  const uint8_t* A = ws + p.qA;
+  const uint8_t* B = ws + p.qB;
+  const float* sa = reinterpret_cast<const float*>(ws + p.sA);
+  const float* sb = reinterpret_cast<const float*>(ws + p.sB);
+  int32_t* part = reinterpret_cast<int32_t*>(ws + p.part);
+  const bool ext = p.variant == HLQ_VAR_HLA8_EXT;
+  float* C = ext ? reinterpret_cast<float*>(ws + p.G) : out;
+  const float alpha = ext ? 1.0f : p.alpha * out_alpha;
+  HLQ_TRY(hlq::launch_gemm(false, A, B, p.MoA, p.Nb, p.Kpad, p.plan, sa, tok ? 1 : 0, sb,
+                           tok ? 1 : 0, alpha, hlq::EPI_F32, C, nullptr, part, s));
+  if (ext)
+    HLQ_TRY(hlq::launch_abl_expand(C, p.Ma, p.Nb, n, r, out_alpha / (float)n, out, s));
+  if (acc)
+    HLQ_TRY(hlq::launch_gemm(false, A, B, p.MoA, p.Nb, p.Kpad, p.plan, nullptr, 0, nullptr, 0,
+                             1.f, hlq::EPI_I32, nullptr, acc, nullptr, s));
+  return HLQ_OK;
+}
+
+}  // namespace
+
+size_t hlq_ablation_workspace_size(int64_t T, int64_t I, int64_t O, int block, int rank,
+                                   int gx_variant, int gw_variant) {
+  if (check_shape(T, I, O, block, rank) != HLQ_OK || !var_ok(gx_variant) || !var_ok(gw_variant))
+    return 0;
+  return abl_layout(T, I, O, block, rank, gx_variant, gw_variant).total;
+}
+
+hlq_status hlq_linear_backward_ablation(const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                                        const float* x_scales, const void* w, int w_dtype,
+                                        int64_t T, int64_t I, int64_t O, int block, int rank,
+                                        int gx_variant, int gw_variant, int gx_mode,
+                                        int gw_mode, int reduction, float* g_x, float* g_w,
+                                        int32_t* acc_x, int32_t* acc_w, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  hlq_status st = check_backward(g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O, block,
+                                 rank, gx_mode, gw_mode, reduction, g_x, g_w);
+  if (st != HLQ_OK) return st;
+  if (!var_ok(gx_variant) || !var_ok(gw_variant)) return HLQ_ERR_MODE;
+  const AblLayout L = abl_layout(T, I, O, block, rank, gx_variant, gw_variant);
+  if (!workspace || workspace_bytes < L.total) return HLQ_ERR_WORKSPACE;
+  if (!aligned16(workspace) || (acc_x && !aligned16(acc_x)) || (acc_w && !aligned16(acc_w)))
+    return HLQ_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const bool gx_tok = gx_mode == HLQ_PER_TOKEN, gw_tok = gw_mode == HLQ_PER_TOKEN;
+  // g_x = g_y . w over O: A from g_y [T][O] (m = row t), B from w [O][I] (m = column i)
+  HLQ_TRY(hlq::launch_abl_operand(abl_operand(L.x, true, g_y, gy_dtype, nullptr, nullptr, T, O,
+                                              true, block, rank, gx_tok, ws), block, s));
+  HLQ_TRY(hlq::launch_abl_operand(abl_operand(L.x, false, w, w_dtype, nullptr, nullptr, O, I,
+                                              false, block, rank, gx_tok, ws), block, s));
+  st = abl_gemm(L.x, ws, gx_tok, 1.0f, g_x, acc_x, block, rank, s);
+  if (st != HLQ_OK) return st;
+  // g_w = g_y^T . x over T: A from g_y [T][O] (m = column o), B from the
+  // ACBP codes of x [T][I] (m = column i)
+  HLQ_TRY(hlq::launch_abl_operand(abl_operand(L.w, true, g_y, gy_dtype, nullptr, nullptr, T, O,
+                                              false, block, rank, gw_tok, ws), block, s));
+  HLQ_TRY(hlq::launch_abl_operand(abl_operand(L.w, false, nullptr, 2, x_codes, x_scales, T, I,
+                                              false, block, rank, gw_tok, ws), block, s));
+  const float mean = reduction == HLQ_MEAN ? (float)(1.0 / (double)T) : 1.0f;
+  return abl_gemm(L.w, ws, gw_tok, mean, g_w, acc_w, block, rank, s);
+}
+
 size_t hlq_lqs_workspace_size(int64_t T, int64_t I, int64_t O, int block, int rank) {
   if (check_shape(T, I, O, block, rank) != HLQ_OK) return 0;
   return make_lqs_layout(T, I, O, block, rank).total;

@@ -154,6 +154,25 @@ struct ConvGemm {
 };
 hipError_t launch_dgrad(const ConvGemm& c, hipStream_t s);
 
+// One GEMM operand of an ablation variant (hlq_ablation.hip): V[k][m] read
+// from src (dt 0 fp32 / 1 bf16 matrix [rows][cols], dt 2 ACBP codes with
+// per-row scales), V = S^T (m_is_row) or S; transform along M (along_m) or
+// K over blocks of n: kind 0 none, 1 full Hadamard, 2 low rank (rows j*n/r).
+// Threads: lines x blocks (lines = the other axis' length, blocks = the
+// transformed axis / n).  Output codes q [Mo][Kpad] (K' = Ko valid), scales
+// s [Mo] or [1], maxima maxbits (float bits) of the same size.
+struct AblOperand {
+  const void* src; int dt;
+  const uint8_t* codes; const float* cscales;
+  int64_t rows, cols;
+  int m_is_row, along_m, kind, r, qmax, per_token;
+  int64_t lines, blocks, Mo, Ko, Kpad;
+  int8_t* q; float* s; unsigned* maxbits;
+};
+hipError_t launch_abl_operand(const AblOperand& o, int n, hipStream_t s);
+hipError_t launch_abl_expand(const float* G, int64_t rows, int64_t cols, int n, int r,
+                             float alpha, float* out, hipStream_t s);
+
 hipError_t launch_gemm_finalize(const int32_t* partial, int splits, int64_t M,
                                 int64_t N, const float* sa, int sa_step,
                                 const float* sb, int sb_step, float alpha, float* C,

@@ -32,6 +32,8 @@ EXPORTED = (
     "hlq_conv_backward_workspace_size",
     "hlq_conv_backward",
     "hlq_conv_gemm_acc",
+    "hlq_ablation_workspace_size",
+    "hlq_linear_backward_ablation",
     "hlq_lqs_workspace_size",
     "hlq_lqs_accumulate",
     "hlq_lqs_select",
@@ -93,6 +95,11 @@ def _load():
     lib.hlq_conv_gemm_acc.argtypes = [P, SZ, I64, I64, I64, I64, I64, I32, I32, I32, I32, I32,
                                       I32, P, P, P]
     lib.hlq_conv_gemm_acc.restype = I32
+    lib.hlq_ablation_workspace_size.argtypes = [I64, I64, I64, I32, I32, I32, I32]
+    lib.hlq_ablation_workspace_size.restype = SZ
+    lib.hlq_linear_backward_ablation.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I32, I32,
+                                                 I32, I32, I32, I32, I32, P, P, P, P, P, SZ, P]
+    lib.hlq_linear_backward_ablation.restype = I32
     lib.hlq_lqs_workspace_size.argtypes = [I64, I64, I64, I32, I32]
     lib.hlq_lqs_workspace_size.restype = SZ
     lib.hlq_lqs_accumulate.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I32, I32, P, P,
@@ -358,6 +365,47 @@ def hlq_conv_gemm_acc(workspace, N, H, W, C, O, R, S, stride, pad, block, rank, 
         _ptr(workspace), _nbytes(workspace), N, H, W, C, O, R, S, stride, pad, block, rank,
         _ptr(acc_x), _ptr(acc_w), _stream(stream)))
     return acc_x, acc_w
+
+
+HLQ_VAR_HQ4, HLQ_VAR_Q4, HLQ_VAR_HLA8_INT, HLQ_VAR_HLA8_EXT = 0, 1, 2, 3
+VARIANT_NAMES = ("hq4", "q4", "hla8_int", "hla8_ext")
+
+
+def hlq_ablation_workspace_size(T, I, O, block, rank, gx_variant, gw_variant) -> int:
+    return int(_lib.hlq_ablation_workspace_size(T, I, O, block, rank, gx_variant, gw_variant))
+
+
+def hlq_linear_backward_ablation(g_y, x_codes, x_scales, w, block, rank, gx_variant, gw_variant,
+                                 gx_mode=HLQ_PER_TOKEN, gw_mode=HLQ_PER_TOKEN,
+                                 reduction=HLQ_SUM, want_acc=False, stream=None):
+    """The backward under an ablation variant per path (HLQ_VAR_*; names in
+    VARIANT_NAMES).  Returns (g_x, g_w) fp32, plus (acc_x, acc_w) INT32 when
+    want_acc."""
+    import torch
+    T, O = g_y.shape
+    O2, I = w.shape
+    if O2 != O:
+        raise ValueError("w must be [O, I] with O = g_y.shape[1]")
+    dev = g_y.device
+    _expect("x_codes", x_codes, torch.uint8, (T, I // 2))
+    _expect("x_scales", x_scales, torch.float32, (T,))
+    g_x = torch.empty((T, I), dtype=torch.float32, device=dev)
+    g_w = torch.empty((O, I), dtype=torch.float32, device=dev)
+    ext = HLQ_VAR_HLA8_EXT
+    acc_x = acc_w = None
+    if want_acc:
+        acc_x = torch.empty((T // block * rank if gx_variant == ext else T, I),
+                            dtype=torch.int32, device=dev)
+        acc_w = torch.empty((O // block * rank if gw_variant == ext else O, I),
+                            dtype=torch.int32, device=dev)
+    need = hlq_ablation_workspace_size(T, I, O, block, rank, gx_variant, gw_variant)
+    ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _require_cuda(g_y, x_codes, x_scales, w, g_x, g_w, ws, acc_x, acc_w)
+    _check("hlq_linear_backward_ablation", _lib.hlq_linear_backward_ablation(
+        _ptr(g_y), _dtype_code(g_y), _ptr(x_codes), _ptr(x_scales), _ptr(w), _dtype_code(w),
+        T, I, O, block, rank, gx_variant, gw_variant, gx_mode, gw_mode, reduction, _ptr(g_x),
+        _ptr(g_w), _ptr(acc_x), _ptr(acc_w), _ptr(ws), _nbytes(ws), _stream(stream)))
+    return (g_x, g_w, acc_x, acc_w) if want_acc else (g_x, g_w)
 
 
 HLQ_LQS_STATS = 16

@@ -276,6 +276,41 @@ hlq_status hlq_conv_gemm_acc(const void* workspace, size_t workspace_bytes, int6
                              int32_t* acc_w, void* stream);
 
 /*
+ * Ablation variants: the backward with another transform / quantizer on
+ * either path, for synthetic error studies (HOT summary, "Measured effects":
+ * the ResNet50 ablation rows; "Surprising findings": internal and external
+ * Hadamard low-rank approximation on the activation-gradient path,
+ * quantization sensitivity of the weight-gradient path).  Each path is one
+ * integer GEMM over its contracted dimension K (O for g_x, T for g_w):
+ *   HLQ_VAR_HQ4       block Hadamard along K on both operands, INT4 (the
+ *                     method's g_x path);
+ *   HLQ_VAR_Q4        no transform, INT4;
+ *   HLQ_VAR_HLA8_INT  low-rank rows j*n/r of the block Hadamard along K on
+ *                     both operands ("internal" HLA), INT8 (the method's g_w
+ *                     path);
+ *   HLQ_VAR_HLA8_EXT  low-rank Hadamard along the left operand's output
+ *                     dimension (T for g_x, O for g_w: "external" HLA), none
+ *                     on the right operand, INT8; the r rows per block of the
+ *                     product are expanded back to n by H_low^T / n.
+ * The pages list HLA without a quantizer; HOT pairs it with INT8, as here.
+ * Scale groups and modes as hlq_linear_backward.  Plain kernels, one thread
+ * per block of n source values, then the library's INT8 GEMM (INT4 codes are
+ * stored one per byte): not the hot path.  acc_x [T or T*r/n][I] and acc_w
+ * [O or O*r/n][I] (device, may be NULL) receive the GEMMs' INT32 sums.
+ * Errors as hlq_linear_backward; HLQ_ERR_MODE for an unknown variant.
+ */
+enum { HLQ_VAR_HQ4 = 0, HLQ_VAR_Q4 = 1, HLQ_VAR_HLA8_INT = 2, HLQ_VAR_HLA8_EXT = 3 };
+size_t hlq_ablation_workspace_size(int64_t T, int64_t I, int64_t O, int block, int rank,
+                                   int gx_variant, int gw_variant);
+hlq_status hlq_linear_backward_ablation(const void* g_y, int gy_dtype, const uint8_t* x_codes,
+                                        const float* x_scales, const void* w, int w_dtype,
+                                        int64_t T, int64_t I, int64_t O, int block, int rank,
+                                        int gx_variant, int gw_variant, int gx_mode,
+                                        int gw_mode, int reduction, float* g_x, float* g_w,
+                                        int32_t* acc_x, int32_t* acc_w, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * Layer-wise quantizer selection (LQS).  "HOT: Hadamard-based Optimized
  * Training": HF page abstract (layer-wise quantizer selection), scime.ai
  * summary "Approach" (per-token vs per-tensor chosen per layer) and

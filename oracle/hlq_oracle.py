@@ -360,6 +360,109 @@ def linear_backward_unquantized(gy, x, w, block: int, rank: int,
 
 
 # --------------------------------------------------------------------------
+# Ablation variants ([HOT-sum] "Measured effects": the ResNet50 / CIFAR100
+# ablation rows, and "Surprising findings": internal and external HLA on the
+# activation-gradient path, quantization sensitivity of the weight-gradient
+# path)
+# --------------------------------------------------------------------------
+#
+# R12 Each backward path is one GEMM C = A^T-contracted product of two
+#     operands over a contracted dimension K (O for g_x, T for g_w).  A
+#     variant fixes the operands' transform and quantizer:
+#       "hq4"      block Hadamard along K on both operands, INT4 (the method's
+#                  g_x path);
+#       "q4"       no transform, INT4;
+#       "hla8_int" low-rank Hadamard along K on both operands ("internal"
+#                  HLA, along the contracted dimension), INT8 (the method's
+#                  g_w path);
+#       "hla8_ext" low-rank Hadamard along the output dimension of the left
+#                  operand (T for g_x, O for g_w: "external" HLA), none on the
+#                  right operand, INT8; the GEMM result of r rows per block is
+#                  expanded back to n rows by H_low^T / n.
+#     The pages' ablation rows list HLA without a quantizer; HOT applies HLA
+#     with INT8, so the variants here pair HLA with INT8 and keep integer
+#     GEMMs.  A Hadamard along K (hq4, hla8_int) brings the 1/n of R1; q4 none;
+#     hla8_ext has its 1/n in the expansion.  Scale groups as R6 (one scale per
+#     GEMM output index of each operand, or one per operand).
+
+VARIANTS = ("hq4", "q4", "hla8_int", "hla8_ext")
+
+
+def expand_lowrank_rows(g, n: int, r: int) -> np.ndarray:
+    """(1/n) H_low^T along rows: [B*r x N] -> [B*n x N] in fp64; row k of
+    block b is sum_j H[j*n/r][k] * g[b*r + j] / n."""
+    h = sylvester_hadamard(n)[lowrank_rows(n, r)].astype(np.float64)   # [r x n]
+    g = np.asarray(g, dtype=np.float64)
+    B = g.shape[0] // r
+    out = np.einsum("jk,bjc->bkc", h, g.reshape(B, r, -1)) / n
+    return out.reshape(B * n, -1)
+
+
+def _variant_operands(a, b, variant: str, n: int, r: int, quant: bool, a_mode: int, b_mode: int):
+    """Operands of one path.  a [K x Ma] and b [K x Nb] with K (the
+    contracted dimension) along axis 0.  Returns (qa, sa, qb, sb, alpha):
+    quantized codes (or the fp64 values when quant is False) along with their
+    scales (1 when unquantized), and the factor of the product."""
+    def tr(v, kind):
+        if kind == "h":
+            return fwht_blocks(v, n, 0)
+        if kind == "low_k":
+            return lowrank_transform(v, n, r, 0)
+        if kind == "low_m":
+            return lowrank_transform(v, n, r, 1)
+        return v
+    kinds = {"hq4": ("h", "h", QMAX_INT4, 1.0 / n), "q4": ("none", "none", QMAX_INT4, 1.0),
+             "hla8_int": ("low_k", "low_k", QMAX_INT8, 1.0 / n),
+             "hla8_ext": ("low_m", "none", QMAX_INT8, 1.0)}
+    if variant not in kinds:
+        raise ValueError(f"unknown variant {variant!r}")
+    ka, kb, qmax, alpha = kinds[variant]
+    va, vb = tr(a, ka), tr(b, kb)
+    if not quant:
+        return va, np.ones(1), vb, np.ones(1), alpha
+    qa, sa = quantize(va, qmax, _group_axis(a_mode, 0))
+    qb, sb = quantize(vb, qmax, _group_axis(b_mode, 0))
+    return qa, sa, qb, sb, alpha
+
+
+def linear_backward_variant(gy, x_codes, x_scales, w, block: int, rank: int, gx_variant: str,
+                            gw_variant: str, gx_mode: int = PER_TOKEN, gw_mode: int = PER_TOKEN,
+                            reduction: int = SUM, quant: bool = True) -> dict:
+    """The backward with one variant per path (reading R12).  Inputs as
+    :func:`linear_backward`; ``quant=False`` skips the quantizers (fp64
+    throughout, self-checks).  Returns the codes / scales of each operand
+    (qa_x, sa_x, qb_x, sb_x; qa_w, sa_w, qb_w, sb_w, each K-contracted along
+    axis 0), the INT32 sums acc_x [T' or T x I] and acc_w [O' or O x I], and
+    g_x [T x I], g_w [O x I] (fp64 epilogue and expansion, rounded once)."""
+    dt = np.float32 if quant else np.float64
+    gy = np.asarray(gy, dtype=dt)
+    w = np.asarray(w, dtype=dt)
+    x = acbp_unpack(x_codes, x_scales).astype(dt)
+    n, r = block, rank
+    T = gy.shape[0]
+    out = {}
+    # g_x = gy . w: K = O; a = gy^T [O x T], b = w [O x I]
+    qa, sa, qb, sb, alpha = _variant_operands(gy.T, w, gx_variant, n, r, quant, gx_mode, gx_mode)
+    acc = int_matmul(qa.T, qb) if quant else qa.T @ qb
+    g = acc.astype(np.float64) * _bcast(sa, 0) * _bcast(sb, 1) * alpha
+    if gx_variant == "hla8_ext":
+        g = expand_lowrank_rows(g, n, r)
+    out.update(qa_x=qa, sa_x=sa, qb_x=qb, sb_x=sb, acc_x=acc, g_x=g.astype(dt))
+    # g_w = gy^T . x: K = T; a = gy [T x O], b = x [T x I]
+    qa, sa, qb, sb, alpha = _variant_operands(gy, x, gw_variant, n, r, quant, gw_mode, gw_mode)
+    acc = int_matmul(qa.T, qb) if quant else qa.T @ qb
+    g = acc.astype(np.float64) * _bcast(sa, 0) * _bcast(sb, 1) * alpha
+    if gw_variant == "hla8_ext":
+        g = expand_lowrank_rows(g, n, r)
+    if reduction == MEAN:
+        g = g / T
+    elif reduction != SUM:
+        raise ValueError("reduction must be SUM or MEAN")
+    out.update(qa_w=qa, sa_w=sa, qb_w=qb, sb_w=sb, acc_w=acc, g_w=g.astype(dt))
+    return out
+
+
+# --------------------------------------------------------------------------
 # Convolution layers ([HLQ] abstract: backpropagation of convolutional and
 # linear layers; [HOT-sum] "Key results": ResNet-50 at batch size 256)
 # --------------------------------------------------------------------------
@@ -576,6 +679,7 @@ __all__ = [
     "lowrank_transform", "quantize", "pack_int4", "unpack_int4", "acbp_pack",
     "acbp_unpack", "int_matmul", "linear_backward",
     "linear_backward_unquantized", "rel_fro", "max_rel_err", "conv_out_size", "im2col",
-    "col2im", "conv_backward", "conv_backward_unquantized", "LQS_THRESHOLD", "LQS_OPERANDS",
+    "col2im", "conv_backward", "conv_backward_unquantized", "VARIANTS",
+    "expand_lowrank_rows", "linear_backward_variant", "LQS_THRESHOLD", "LQS_OPERANDS",
     "lqs_operands", "quant_sq_error", "lqs_stats", "lqs_path_errors", "lqs_select",
 ]
