@@ -10,7 +10,7 @@ from __future__ import annotations
 import importlib
 
 _BINDING_NAMES = {
-    "hlq_compress_act", "hlq_linear_backward", "hlq_linear_backward_workspace_size",
+    "hlq_compress_act", "hlq_linear_forward", "hlq_linear_backward", "hlq_linear_backward_workspace_size",
     "hlq_workspace_layout_query", "hlq_linear_backward_noalloc", "HLQ_NOALLOC_SCRATCH_BYTES",
     "hlq_gemm_pair_acc", "hlq_gemm_gx_acc", "hlq_gemm_gw_acc", "HLQError",
     "HLQ_F32", "HLQ_BF16", "HLQ_PER_TOKEN", "HLQ_PER_TENSOR", "HLQ_SUM", "HLQ_MEAN",

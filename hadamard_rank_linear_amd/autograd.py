@@ -5,11 +5,13 @@ HLQ/HOT backward of libhlq.so.
 stored activation is compressed at forward time (activation buffer
 compression), and the backward runs Hadamard quantization on g_x and Hadamard
 low-rank approximation plus INT8 on g_w.  The forward product itself is
-unchanged by the method, so it stays torch's matmul; what this wrapper keeps
-for the backward is the ACBP form of x (INT4 codes + one fp32 scale per
-token, from ``hlq_compress_act``) instead of x, and its backward is one
-``hlq_linear_backward`` call.  Leading dimensions of x are flattened into
-tokens.  No bias (its gradient is not part of the method).
+unchanged by the method; what this wrapper keeps for the backward is the ACBP
+form of x (INT4 codes + one fp32 scale per token) instead of x, and its
+backward is one ``hlq_linear_backward`` call.  For bf16 x and w with I a
+multiple of 32 the forward is one ``hlq_linear_forward`` launch (the bf16
+MFMA product with the codes of x emitted by the same launch); otherwise
+torch's matmul and ``hlq_compress_act``.  Leading dimensions of x are
+flattened into tokens.  No bias (its gradient is not part of the method).
 """
 from __future__ import annotations
 
@@ -26,8 +28,11 @@ class HLQLinearFunction(torch.autograd.Function):
         if x.shape[-1] != w.shape[1]:
             raise ValueError("x [..., I] and w [O, I] disagree on I")
         x2 = x.reshape(-1, x.shape[-1]).contiguous()
-        y = x2 @ w.t()
-        codes, scales = hlq.hlq_compress_act(x2)
+        if x2.dtype == torch.bfloat16 and w.dtype == torch.bfloat16 and x2.shape[1] % 32 == 0:
+            y, codes, scales = hlq.hlq_linear_forward(x2, w.contiguous())
+        else:
+            y = x2 @ w.t()
+            codes, scales = hlq.hlq_compress_act(x2)
         ctx.save_for_backward(codes, scales, w)
         ctx.cfg = (block, rank, gx_mode, gw_mode, reduction)
         ctx.x_shape, ctx.x_dtype = x.shape, x.dtype

@@ -219,6 +219,23 @@ hlq_status hlq_compress_act(const void* x, int x_dtype, int64_t T, int64_t I,
   return HLQ_OK;
 }
 
+hlq_status hlq_linear_forward(const void* x, const void* w, int64_t T, int64_t I, int64_t O,
+                              void* y, int y_dtype, uint8_t* x_codes, float* x_scales,
+                              void* stream) {
+  if (!x || !w || !y) return HLQ_ERR_NULL;
+  if ((x_codes == nullptr) != (x_scales == nullptr)) return HLQ_ERR_NULL;
+  if (y_dtype != HLQ_F32 && y_dtype != HLQ_BF16) return HLQ_ERR_DTYPE;
+  if (T <= 0 || O <= 0 || I < 32 || I % 32) return HLQ_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (x_codes && !aligned16(x_codes)) ||
+      (x_scales && !aligned16(x_scales)))
+    return HLQ_ERR_ALIGN;
+  HLQ_TRY(hlq::launch_forward(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                              T, I, O, y_dtype == HLQ_F32 ? static_cast<float*>(y) : nullptr,
+                              y_dtype == HLQ_BF16 ? static_cast<uint16_t*>(y) : nullptr, x_codes,
+                              x_scales, static_cast<hipStream_t>(stream)));
+  return HLQ_OK;
+}
+
 size_t hlq_linear_backward_workspace_size(int64_t T, int64_t I, int64_t O, int block,
                                           int rank) {
   if (check_shape(T, I, O, block, rank) != HLQ_OK) return 0;

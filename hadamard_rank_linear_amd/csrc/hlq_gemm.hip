@@ -63,6 +63,15 @@ namespace hlq {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even (finite values)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
 
 __device__ __forceinline__ void widen_int4x2(u32x4 p, v4i& a, v4i& b) {
   a[0] = (int)((p[0] << 4) & 0xF0F0F0F0u); a[1] = (int)(p[0] & 0xF0F0F0F0u);
@@ -142,13 +151,29 @@ struct GemmArgs {
   // bytes); B (the H.w codes) at row tap * cC + channel.
   int32_t cH, cW, cP, cQ, cS, cC, cstride, cpad, cSO;
   const uint8_t* zero;
+  // bf16 forward (gemm_tile BF16): y [M][N] as bf16 bits (EPI_BF16) and, when
+  // acbp_codes is set, the ACBP codes [M][K/2] and scales [M] of A (= x),
+  // emitted by the workgroups of the first column of tiles.
+  uint16_t* Cb;
+  uint8_t* acbp_codes;
+  float* acbp_scales;
 };
 
 // One output tile (workgroup w of the tile grid, K split `split`) of one GEMM.
 // Every thread of the workgroup calls it; `lds` holds NS * STAGE bytes.
-template <bool INT4, int BM, int BN, int KB, int NS, int EPI, bool CONV = false>
+//
+// BF16: bf16 operands (8 per 16-byte fragment, v_mfma_f32_32x32x16_bf16, fp32
+// sums), the forward product y = x . w^T; EPI_F32 stores y in fp32 (no
+// scales), EPI_BF16 rounds it to bf16.  With g.acbp_codes set, the waves of
+// the first column of tiles keep the running maximum of |x| of their A rows
+// (packed 16-bit maxima of the magnitude bits of the fragments they feed to
+// the MFMAs, no extra load); after the K loop the tile's 256 threads re-read
+// its rows (from cache) and write their INT4 codes and scales.
+template <bool INT4, int BM, int BN, int KB, int NS, int EPI, bool CONV = false,
+          bool BF16 = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t split,
                                           uint8_t* lds, float* sc) {
+  static_assert(!(INT4 && BF16), "one operand type");
   using G = GemmShape<INT4, BM, BN, KB, NS>;
   constexpr int FM = G::FM, FN = G::FN, IA = G::IA, IB = G::IB, IPW = G::IPW;
   constexpr int CPR = G::CPR, KK = G::KK;
@@ -261,7 +286,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   // global load while its stores are in flight.
   constexpr int NSC = (BM + BN + 255) / 256;
   float scv[NSC];
-  if constexpr (EPI == EPI_F32) {
+  if constexpr (EPI == EPI_F32 && !BF16) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q) {
       // one unconditional load per slot (a select of the address, so the
@@ -281,17 +306,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   // the scale loads before the stage loads are in flight)
   asm volatile("" ::: "memory");
 
-  v16i acc[FM][FN];
+  using AccT = std::conditional_t<BF16, v16f, v16i>;
+  AccT acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+  // ACBP row maxima (BF16 forward): packed 16-bit maxima of |x| bits
+  const bool acbp = BF16 && g.acbp_codes != nullptr && tn == 0;
+  const bool track = acbp && wn == 0;
+  // (a plain array: bit casts of ext-vector elements read element 0 here)
+  unsigned amax[FM][4];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) amax[i][d] = 0u;
 
   u32x4 fa[2][FM], fb[2][FN];
   HLQ_GEMM_WAIT((S - 1 < NS - 1 ? S - 1 : NS - 1));
-  if constexpr (EPI == EPI_F32) {
+  if constexpr (EPI == EPI_F32 && !BF16) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q)
       if (tid + 256 * q < BM + BN) sc[tid + 256 * q] = tid + 256 * q < BM ? scv[q] * alpha : scv[q];
@@ -362,6 +397,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa1[i], yb1[j], acc[i][j], 0, 0, 0);
         // INT4: the compiler's own interleaving of reads, widening and MFMAs
         // (explicit groups measured no better: fc2 pair 52.5 vs 51 us)
+      } else if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(v8bf, fa[cur][i]), __builtin_bit_cast(v8bf, fb[cur][j]),
+                acc[i][j], 0, 0, 0);
+        if (track) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const unsigned run = amax[i][d], mag = fa[cur][i][d] & 0x7FFF7FFFu;
+              amax[i][d] = __builtin_bit_cast(
+                  unsigned, __builtin_elementwise_max(__builtin_bit_cast(us2, run),
+                                                      __builtin_bit_cast(us2, mag)));
+            }
+        }
+        if (reads) {
+          HLQ_SGB(0x100, FM + FN);
+          HLQ_SGB(0x008, FM * FN);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -390,11 +448,53 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 #undef HLQ_GEMM_ISSUE
 #undef HLQ_GEMM_WAIT
 
+  if constexpr (BF16) {
+    if (acbp) {
+      // row maxima: the 8 packed maxima of a fragment, then the other K half
+      // (lane ^ 32); rows wm*WTM + i*32 + lane % 32 -> sc[row] (|x| max),
+      // sc[BM + row] (reciprocal scale)
+      static_assert(BN >= BM, "row maxima and reciprocal scales fit sc");
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (wn == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          unsigned m = 0u;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const unsigned v = amax[i][d];
+            m = max(m, max(v & 0xFFFFu, v >> 16));
+          }
+          m = max(m, (unsigned)__shfl_xor((int)m, 32));
+          if (lane < 32) {
+            const int row = wm * G::WTM + i * 32 + lane;
+            const float a = bf16_to_f32(m);
+            sc[row] = a;
+            sc[BM + row] = inv_of(a, 7.f);
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // codes of the tile's rows, 8 elements (16 bytes of x) per item, read
+      // again from cache
+      const int64_t c8 = pitch / 16;  // 8-element chunks per row
+      const int64_t rows = M - m0 < BM ? M - m0 : BM;
+      for (int64_t it = tid; it < rows * c8; it += 256) {
+        const int64_t row = it / c8, c = it - row * c8;
+        const uint4 raw = *reinterpret_cast<const uint4*>(A + (m0 + row) * pitch + c * 16);
+        float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                      bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+        *reinterpret_cast<uint32_t*>(g.acbp_codes + (m0 + row) * (pitch / 4) + c * 4) =
+            quant_pack8_int4(v, sc[BM + row]);
+      }
+      if (tid < rows) g.acbp_scales[m0 + tid] = scale_of(sc[tid], 7.f);
+    }
+  }
+
   constexpr int SH = INT4 ? 8 : 0;
   int32_t* Cp = Ci + (EPI == EPI_PARTIAL ? split * M * N : 0);
   // Scales from LDS (written before the K loop; its barriers published them).
   float s_n[FN], s_m[FM][16];
-  if constexpr (EPI == EPI_F32) {
+  if constexpr (EPI == EPI_F32 && !BF16) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) s_n[j] = sc[BM + wn * G::WTN + j * 32 + fr];
 #pragma unroll
@@ -418,9 +518,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
-          const int32_t v = acc[i][j][r] >> SH;
-          if constexpr (EPI == EPI_F32) __builtin_nontemporal_store((float)v * s_m[i][r] * s_n[j], &C[m * N + n]);
-          else Cp[m * N + n] = v;
+          if constexpr (BF16) {
+            if constexpr (EPI == EPI_BF16) g.Cb[m * N + n] = f32_to_bf16_rne(acc[i][j][r]);
+            else C[m * N + n] = acc[i][j][r];
+          } else {
+            const int32_t v = acc[i][j][r] >> SH;
+            if constexpr (EPI == EPI_F32) __builtin_nontemporal_store((float)v * s_m[i][r] * s_n[j], &C[m * N + n]);
+            else Cp[m * N + n] = v;
+          }
         }
       }
     return;
@@ -435,9 +540,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
       for (int j = 0; j < FN; ++j) {
         const int64_t n = n0 + wn * G::WTN + j * 32 + fr;
         if (n >= N) continue;
-        const int32_t v = acc[i][j][r] >> SH;
-        if constexpr (EPI == EPI_F32) __builtin_nontemporal_store((float)v * s_m[i][r] * s_n[j], &C[m * N + n]);
-        else Cp[m * N + n] = v;
+        if constexpr (BF16) {
+          if constexpr (EPI == EPI_BF16) g.Cb[m * N + n] = f32_to_bf16_rne(acc[i][j][r]);
+          else C[m * N + n] = acc[i][j][r];
+        } else {
+          const int32_t v = acc[i][j][r] >> SH;
+          if constexpr (EPI == EPI_F32) __builtin_nontemporal_store((float)v * s_m[i][r] * s_n[j], &C[m * N + n]);
+          else Cp[m * N + n] = v;
+        }
       }
   }
 }
@@ -447,6 +557,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * GemmShape<INT4, BM, BN, KB, NS>::STAGE];
   __shared__ float sc[BM + BN];
   gemm_tile<INT4, BM, BN, KB, NS, EPI>(g, blockIdx.x, blockIdx.y, lds, sc);
+}
+
+// Forward product y = x . w^T of a bf16 linear layer, with the ACBP codes of
+// x emitted by the first column of tiles (gemm_tile BF16).
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void k_forward(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * GemmShape<false, 128, 128, 64, 3>::STAGE];
+  __shared__ float sc[256];
+  gemm_tile<false, 128, 128, 64, 3, EPI, false, true>(g, blockIdx.x, 0, lds, sc);
 }
 
 // Input gradient of a convolution as an implicit GEMM over the taps (CONV
@@ -646,6 +765,23 @@ hipError_t launch_dgrad(const ConvGemm& c, hipStream_t s) {
   const dim3 g((unsigned)((tiles + 7) / 8 * 8));
   if (c.epi == EPI_F32) hipLaunchKernelGGL((k_dgrad<128, 128, 64, 3, EPI_F32>), g, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_dgrad<128, 128, 64, 3, EPI_I32>), g, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const uint16_t* x, const uint16_t* w, int64_t T, int64_t I, int64_t O,
+                          float* y32, uint16_t* y16, uint8_t* codes, float* scales,
+                          hipStream_t s) {
+  if (I % 32 || (!y32 && !y16) || (codes && !scales)) return hipErrorInvalidValue;
+  const int64_t pitch = 2 * I, stages = pitch / 64;
+  GemmArgs a{reinterpret_cast<const uint8_t*>(x), reinterpret_cast<const uint8_t*>(w), T, O, pitch,
+             stages, stages, nullptr, 0, nullptr, 0, 1.f, y32, nullptr};
+  a.Cb = y16;
+  a.acbp_codes = codes;
+  a.acbp_scales = scales;
+  const int64_t tiles = (int64_t)cdiv(T, 128) * cdiv(O, 128);
+  const dim3 g((unsigned)((tiles + 7) / 8 * 8));
+  if (y16) hipLaunchKernelGGL((k_forward<EPI_BF16>), g, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_forward<EPI_F32>), g, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

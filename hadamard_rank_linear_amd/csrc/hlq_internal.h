@@ -9,7 +9,7 @@
 
 namespace hlq {
 
-enum GemmEpi { EPI_F32 = 0, EPI_I32 = 1, EPI_PARTIAL = 2 };
+enum GemmEpi { EPI_F32 = 0, EPI_I32 = 1, EPI_PARTIAL = 2, EPI_BF16 = 3 };
 enum TrPass { PASS_MAX = 0, PASS_QUANT = 1 };
 
 // Rows and columns of one transform tile (see the tile engine in
@@ -172,6 +172,13 @@ struct AblOperand {
 hipError_t launch_abl_operand(const AblOperand& o, int n, hipStream_t s);
 hipError_t launch_abl_expand(const float* G, int64_t rows, int64_t cols, int n, int r,
                              float alpha, float* out, hipStream_t s);
+
+// Forward product y = x . w^T (bf16 x [T][I], w [O][I]; I % 32 == 0) into
+// y32 (fp32) or y16 (bf16, round to nearest even), and the ACBP codes
+// [T][I/2] and scales [T] of x when codes is set.
+hipError_t launch_forward(const uint16_t* x, const uint16_t* w, int64_t T, int64_t I, int64_t O,
+                          float* y32, uint16_t* y16, uint8_t* codes, float* scales,
+                          hipStream_t s);
 
 hipError_t launch_gemm_finalize(const int32_t* partial, int splits, int64_t M,
                                 int64_t N, const float* sa, int sa_step,

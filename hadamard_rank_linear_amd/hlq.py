@@ -21,6 +21,7 @@ HLQ_STEPS_ALL = (1 << len(STEP_NAMES)) - 1
 
 EXPORTED = (
     "hlq_compress_act",
+    "hlq_linear_forward",
     "hlq_linear_backward_workspace_size",
     "hlq_linear_backward",
     "hlq_linear_backward_steps",
@@ -66,6 +67,8 @@ def _load():
     P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.hlq_compress_act.argtypes = [P, I32, I64, I64, P, P, P]
     lib.hlq_compress_act.restype = I32
+    lib.hlq_linear_forward.argtypes = [P, P, I64, I64, I64, P, I32, P, P, P]
+    lib.hlq_linear_forward.restype = I32
     lib.hlq_linear_backward_workspace_size.argtypes = [I64, I64, I64, I32, I32]
     lib.hlq_linear_backward_workspace_size.restype = SZ
     lib.hlq_linear_backward.argtypes = [P, I32, P, P, P, I32, I64, I64, I64, I32, I32,
@@ -191,6 +194,38 @@ def hlq_compress_act(x, x_codes=None, x_scales=None, stream=None):
     _check("hlq_compress_act", _lib.hlq_compress_act(
         _ptr(x), _dtype_code(x), T, I, _ptr(x_codes), _ptr(x_scales), _stream(stream)))
     return x_codes, x_scales
+
+
+def hlq_linear_forward(x, w, y=None, y_dtype=None, compress=True, x_codes=None,
+                       x_scales=None, stream=None):
+    """y = x . w^T for bf16 x [T, I] and w [O, I] (I % 32 == 0) on the bf16
+    matrix cores; with ``compress`` the same launch also returns the ACBP
+    codes / scales of x.  Returns y, or (y, x_codes, x_scales)."""
+    import torch
+    T, I = x.shape
+    O, I2 = w.shape
+    if I2 != I:
+        raise ValueError("w must be [O, I] with I = x.shape[1]")
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("hlq_linear_forward takes bf16 x and w")
+    if y is None:
+        y = torch.empty((T, O), dtype=y_dtype or torch.bfloat16, device=x.device)
+    if y.dtype not in (torch.float32, torch.bfloat16) or tuple(y.shape) != (T, O):
+        raise ValueError("y must be a float32 or bfloat16 [T, O] tensor")
+    if compress:
+        if x_codes is None:
+            x_codes = torch.empty((T, I // 2), dtype=torch.uint8, device=x.device)
+        if x_scales is None:
+            x_scales = torch.empty((T,), dtype=torch.float32, device=x.device)
+        _expect("x_codes", x_codes, torch.uint8, (T, I // 2))
+        _expect("x_scales", x_scales, torch.float32, (T,))
+    else:
+        x_codes = x_scales = None
+    _require_cuda(x, w, y, x_codes, x_scales)
+    _check("hlq_linear_forward", _lib.hlq_linear_forward(
+        _ptr(x), _ptr(w), T, I, O, _ptr(y), _dtype_code(y), _ptr(x_codes), _ptr(x_scales),
+        _stream(stream)))
+    return (y, x_codes, x_scales) if compress else y
 
 
 def hlq_linear_backward_workspace_size(T, I, O, block, rank) -> int:

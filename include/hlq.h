@@ -79,6 +79,24 @@ hlq_status hlq_compress_act(const void* x, int x_dtype, int64_t T, int64_t I,
                             uint8_t* x_codes, float* x_scales, void* stream);
 
 /*
+ * Forward product of a bf16 linear layer, y = x . w^T, with ACBP fused in
+ * (HOT summary, "Approach": stored activations compressed at forward time;
+ * HOT abstract: activation buffer compression): the same launch writes the
+ * INT4 codes and per-token scales of x that hlq_compress_act would, without a
+ * separate read of x from HBM (the first column of output tiles tracks each
+ * token row's maximum |x| from the operand fragments of its MFMAs, then
+ * re-reads its rows from cache for the codes).
+ *   x        [T][I] bf16;  w [O][I] bf16;  I % 32 == 0.
+ *   y        [T][O] out, y_dtype HLQ_F32 (fp32 sums) or HLQ_BF16 (rounded to
+ *            nearest even).
+ *   x_codes  [T][I/2], x_scales [T] out (both NULL: the product only);
+ *            bit-identical to hlq_compress_act of x.
+ */
+hlq_status hlq_linear_forward(const void* x, const void* w, int64_t T, int64_t I, int64_t O,
+                              void* y, int y_dtype, uint8_t* x_codes, float* x_scales,
+                              void* stream);
+
+/*
  * Bytes of device workspace hlq_linear_backward needs for this shape
  * (0 if the shape or block/rank is invalid).  Independent of modes/dtypes.
  */

@@ -339,6 +339,12 @@ def linear_backward(gy, x_codes, x_scales, w, block: int, rank: int,
     return out
 
 
+def linear_forward(x, w) -> np.ndarray:
+    """y = x . w^T in fp64 (the layer's forward product; ACBP of x is
+    :func:`acbp_pack`)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
 def linear_backward_unquantized(gy, x, w, block: int, rank: int,
                                 reduction: int = SUM) -> dict:
     """Quantization-off form of :func:`linear_backward` (self-checks only).
@@ -677,7 +683,7 @@ __all__ = [
     "bf16_bits_to_f32",
     "sylvester_hadamard", "fwht_blocks", "lowrank_rows", "sequency",
     "lowrank_transform", "quantize", "pack_int4", "unpack_int4", "acbp_pack",
-    "acbp_unpack", "int_matmul", "linear_backward",
+    "acbp_unpack", "int_matmul", "linear_backward", "linear_forward",
     "linear_backward_unquantized", "rel_fro", "max_rel_err", "conv_out_size", "im2col",
     "col2im", "conv_backward", "conv_backward_unquantized", "VARIANTS",
     "expand_lowrank_rows", "linear_backward_variant", "LQS_THRESHOLD", "LQS_OPERANDS",

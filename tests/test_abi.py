@@ -239,3 +239,15 @@ def test_conv_workspace_covers_the_linear_layout():
                                               c.block, c.rank)
     lin = h.hlq_linear_backward_workspace_size(c.T, c.I, c.O, c.block, c.rank)
     assert conv > lin > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(ydt=5), 6), (dict(I=48), 2), (dict(T=0), 2),
+    (dict(y=(1 << 20) + 4), 7)])
+def test_forward_validates_before_launch(kw, status):
+    args = dict(x=1 << 20, w=1 << 20, T=64, I=64, O=32, y=1 << 20, ydt=1, codes=1 << 20,
+                scales=1 << 20, stream=None)
+    args.update(kw)
+    lib = h.lib_handle()
+    assert lib.hlq_linear_forward(*(args[k] for k in (
+        "x", "w", "T", "I", "O", "y", "ydt", "codes", "scales", "stream"))) == status

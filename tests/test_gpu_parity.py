@@ -299,3 +299,33 @@ def test_quantizer_ties_gw_path():
     gpu = run_gpu(cfg, inp, x_codes=codes, x_scales=scales)
     ocodes, oscales = o.acbp_pack(inp["x"])   # run_gpu also packs inp["x"]
     compare(cfg, gpu, ocodes, oscales, ref)
+
+
+# ----------------------------------------------- forward with fused ACBP
+
+@pytest.mark.parametrize("T,I,O", [(12608, 768, 2304), (1040, 3072, 768), (200, 96, 72),
+                                   (64, 32, 16)])
+def test_forward_with_fused_acbp(T, I, O):
+    # y = x . w^T on the bf16 matrix cores against the fp64 product (fp32
+    # output: within 1e-5 relative Frobenius error; bf16 output: within one
+    # bf16 rounding of it), and the codes / scales the same launch emits
+    # bit-identical to the oracle's ACBP of x
+    import torch
+    import hadamard_rank_linear_amd as h
+    from parity_util import to_device
+    _say(f"forward T={T} I={I} O={O}")
+    cfg = dataclasses.replace(wl.BY_NAME["vitb_qkv"], T=T, I=I, O=O, index=95 + T % 5)
+    inp = wl.make_inputs(cfg, plant_zero_rows=True)
+    x32, w32 = o.bf16_bits_to_f32(inp["x"]), o.bf16_bits_to_f32(inp["w"])
+    ref = o.linear_forward(x32, w32)
+    oc, os_ = o.acbp_pack(x32)
+    x, w = to_device(inp["x"], wl.BF16), to_device(inp["w"], wl.BF16)
+    y, codes, scales = h.hlq_linear_forward(x, w, y_dtype=torch.float32)
+    y16 = h.hlq_linear_forward(x, w, compress=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), oc), "ACBP codes of the forward differ"
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    e = o.rel_fro(y.cpu().numpy(), ref)
+    assert e <= 1e-5, f"forward relative Frobenius error {e:.3e}"
+    y16f = y16.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(y16f - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30 + np.abs(y.cpu().numpy() - ref) * 2)
