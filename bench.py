@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20
 METRIC = "per-layer BP latency (us) + effective TOPS & % roofline, ViT-B qkv/fc2 shape"
 
@@ -376,6 +377,58 @@ def time_conv(cfg, steps, warmup):
                      f"stride={cfg.stride} pad={cfg.pad}", "rotating_sets": n}
 
 
+def time_forward(cfg, inp, steps=20, warmup=5):
+    """Forward of the layer (bf16): hlq_linear_forward (the bf16 MFMA product
+    with the ACBP codes of x from the same launch) against torch's matmul
+    followed by hlq_compress_act, on rotating operand copies.  µs per forward,
+    TFLOP/s of the product against the bf16 dense peak."""
+    import numpy as np
+    import torch
+    import hadamard_rank_linear_amd as h
+    if cfg.dtype != 1 or cfg.I % 32:
+        return None
+    dev = torch.device("cuda:0")
+
+    def dev_t(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x0, w0 = dev_t(inp["x"]), dev_t(inp["w"])
+    per_set = 2 * (x0.numel() + w0.numel() + cfg.T * cfg.O) + cfg.T * cfg.I // 2 + 4 * cfg.T
+    n = max(2, -(-2 * LLC_BYTES // per_set))
+    sets = [(x0.clone(), w0.clone(), torch.empty((cfg.T, cfg.O), dtype=torch.bfloat16, device=dev),
+             torch.empty((cfg.T, cfg.I // 2), dtype=torch.uint8, device=dev),
+             torch.empty((cfg.T,), dtype=torch.float32, device=dev)) for _ in range(n)]
+
+    def fused(i):
+        x, w, y, c, sc = sets[i % n]
+        h.hlq_linear_forward(x, w, y=y, x_codes=c, x_scales=sc)
+
+    def unfused(i):
+        x, w, y, c, sc = sets[i % n]
+        torch.mm(x, w.t(), out=y)
+        h.hlq_compress_act(x, c, sc)
+
+    out = {}
+    for name, fn in (("fused_us", fused), ("torch_matmul_plus_acbp_us", unfused)):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+    flops = 2 * cfg.T * cfg.I * cfg.O
+    out["fused_tflops"] = round(flops / (out["fused_us"] * 1e-6) / 1e12, 1)
+    out["fused_frac_of_bf16_peak"] = round(out["fused_tflops"] / BF16_PEAK_TFLOPS, 4)
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_lqs(cfg, inp, reps=10):
     """Layer-wise quantizer selection statistics of one calibration batch
     (hlq_lqs_accumulate: the backward's MAX and reduce launches, an error
@@ -550,6 +603,8 @@ def main():
         extra["vitb_fc2_us"] = extra["vitb_fc2"]["us"]
     if not args.no_extra:
         extra["per_config"] = per_config_side(max(10, args.steps // 2), args.warmup)
+        log("side measurement: forward with fused ACBP")
+        extra["forward"] = time_forward(cfg, inp)
         log("side measurement: ResNet-50 stage-3 convolution (implicit GEMM)")
         extra["conv"] = {"resnet50_s3_conv3x3": time_conv(
             wl.CONV_BY_NAME["resnet50_s3_conv3x3"], max(10, args.steps // 2), args.warmup)}
