@@ -79,11 +79,21 @@ struct RdB16 {
     return __uint_as_float((uint32_t)t[r * P_B16 + c] << 16);
   }
 };
-// ACBP codes: one scale per (row, 8-column chunk) of the tile, s[r][c / 8]
-// (a linear layer's x tile repeats its token's scale; a convolution's im2col
-// tile can change input pixel, hence scale, at every tap boundary).
-constexpr int X_CHUNKS = CW / 8;
+// ACBP codes of a linear layer's x tile: one scale per row (token).
 struct RdI4 {
+  const uint8_t* q;
+  const float* s;
+  __device__ __forceinline__ float operator()(int r, int c) const {
+    const int byte = q[r * P_I4 + (c >> 1)];
+    const int code = __builtin_amdgcn_sbfe(byte, (c & 1) * 4, 4);
+    return s[r] * (float)code;
+  }
+};
+// ACBP codes of a convolution's im2col tile: one scale per (row, 8-column
+// chunk), s[r][c / 8] (the input pixel, hence the scale, can change at every
+// tap boundary).
+constexpr int X_CHUNKS = CW / 8;
+struct RdI4c {
   const uint8_t* q;
   const float* s;
   __device__ __forceinline__ float operator()(int r, int c) const {
@@ -728,7 +738,7 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
   const int rows = (int)(a.T - t0 < TT ? a.T - t0 : TT);
   const int cols = (int)(a.I - c0 < CW ? a.I - c0 : CW);
   uint8_t* codes = smem;                                          // [TT][P_I4] bytes
-  float* scales = reinterpret_cast<float*>(smem + TT * P_I4);     // [TT][X_CHUNKS]
+  float* scales = reinterpret_cast<float*>(smem + TT * P_I4);     // [TT] or [TT][X_CHUNKS]
   // 64 code bytes per tile row: 4 lanes x 16 bytes, 64 rows per sweep.  Rows
   // are I/2 bytes (a multiple of 4, not of 16), so the loads are dwords.
   constexpr int SW = TT / 64;
@@ -749,12 +759,7 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
           if (col + 8 * d < cols) w4[sw][d] = src[d];
       }
     }
-    if (tid < TT) {
-      const float sv = tid < rows ? a.xs[t0 + tid] : 0.f;
-#pragma unroll
-      for (int k = 0; k < X_CHUNKS; k += 4)
-        *reinterpret_cast<float4*>(scales + tid * X_CHUNKS + k) = make_float4(sv, sv, sv, sv);
-    }
+    if (tid < TT) scales[tid] = tid < rows ? a.xs[t0 + tid] : 0.f;
   } else {
     // taps and channels of this thread's four chunks
     int tap_r[4], tap_s[4];
@@ -798,10 +803,17 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
     *reinterpret_cast<uint4*>(codes + (sw * 64 + lr) * P_I4 + col / 2) =
         make_uint4(w4[sw][0], w4[sw][1], w4[sw][2], w4[sw][3]);
   __syncthreads();
-  RdI4 rd{codes, scales};
-  colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_xl : nullptr, 3,
-                              a.part_xl + tr * a.I + c0, a.q_xl, a.kwb, a.tl, t0,
-                              t0 + rows == a.T);
+  if (!a.conv) {
+    RdI4 rd{codes, scales};
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_xl : nullptr,
+                                3, a.part_xl + tr * a.I + c0, a.q_xl, a.kwb, a.tl, t0,
+                                t0 + rows == a.T);
+  } else {
+    RdI4c rd{codes, scales};
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_xl : nullptr,
+                                3, a.part_xl + tr * a.I + c0, a.q_xl, a.kwb, a.tl, t0,
+                                t0 + rows == a.T);
+  }
 }
 
 // ---- job: w tile (full H_N along O, INT4 stored transposed for g_x)

@@ -11,7 +11,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libhlq.so")
+# the in-tree build; HLQ_LIBRARY names another build of the same library
+# (for side-by-side timing of two builds)
+LIB_PATH = os.environ.get("HLQ_LIBRARY") or os.path.join(HERE, "libhlq.so")
 
 HLQ_F32, HLQ_BF16 = 0, 1
 HLQ_PER_TOKEN, HLQ_PER_TENSOR = 0, 1
