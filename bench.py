@@ -403,13 +403,18 @@ def time_forward(cfg, inp, steps=20, warmup=5):
         x, w, y, c, sc = sets[i % n]
         h.hlq_linear_forward(x, w, y=y, x_codes=c, x_scales=sc)
 
+    def product(i):
+        x, w, y, c, sc = sets[i % n]
+        h.hlq_linear_forward(x, w, y=y, compress=False)
+
     def unfused(i):
         x, w, y, c, sc = sets[i % n]
         torch.mm(x, w.t(), out=y)
         h.hlq_compress_act(x, c, sc)
 
     out = {}
-    for name, fn in (("fused_us", fused), ("torch_matmul_plus_acbp_us", unfused)):
+    for name, fn in (("fused_us", fused), ("product_only_us", product),
+                     ("torch_matmul_plus_acbp_us", unfused)):
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()

@@ -164,11 +164,13 @@ struct GemmArgs {
 //
 // BF16: bf16 operands (8 per 16-byte fragment, v_mfma_f32_32x32x16_bf16, fp32
 // sums), the forward product y = x . w^T; EPI_F32 stores y in fp32 (no
-// scales), EPI_BF16 rounds it to bf16.  With g.acbp_codes set, the waves of
-// the first column of tiles keep the running maximum of |x| of their A rows
-// (packed 16-bit maxima of the magnitude bits of the fragments they feed to
-// the MFMAs, no extra load); after the K loop the tile's 256 threads re-read
-// its rows (from cache) and write their INT4 codes and scales.
+// scales), EPI_BF16 rounds it to bf16.  With g.acbp_codes set, every tile's
+// waves of the first column keep the running maximum of |x| of the tile's A
+// rows (packed 16-bit maxima of the magnitude bits of the fragments they
+// feed to the MFMAs, no extra load: every tile streams the whole K of its
+// rows); after the K loop each tile re-reads (from cache) an equal slice of
+// its rows' columns and writes their INT4 codes, the first column of tiles
+// also the scales.
 template <bool INT4, int BM, int BN, int KB, int NS, int EPI, bool CONV = false,
           bool BF16 = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t split,
@@ -315,7 +317,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
   // ACBP row maxima (BF16 forward): packed 16-bit maxima of |x| bits
-  const bool acbp = BF16 && g.acbp_codes != nullptr && tn == 0;
+  const bool acbp = BF16 && g.acbp_codes != nullptr;
   const bool track = acbp && wn == 0;
   // (a plain array: bit casts of ext-vector elements read element 0 here)
   unsigned amax[FM][4];
@@ -453,7 +455,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
       // row maxima: the 8 packed maxima of a fragment, then the other K half
       // (lane ^ 32); rows wm*WTM + i*32 + lane % 32 -> sc[row] (|x| max),
       // sc[BM + row] (reciprocal scale)
-      static_assert(BN >= BM, "row maxima and reciprocal scales fit sc");
+      // sc: the row maxima and reciprocal scales of the tile's BM rows (2 BM floats)
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (wn == 0) {
 #pragma unroll
@@ -474,19 +476,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // codes of the tile's rows, 8 elements (16 bytes of x) per item, read
-      // again from cache
+      // codes of this tile's slice of its rows' 8-element chunks (16 bytes
+      // of x each, read again from cache): eight loads in flight per thread
       const int64_t c8 = pitch / 16;  // 8-element chunks per row
+      const int64_t nt_n = (N + BN - 1) / BN;
+      const int64_t per = (c8 + nt_n - 1) / nt_n;
+      const int64_t cb = tn * per, cw = (c8 - cb < per ? c8 - cb : per);
       const int64_t rows = M - m0 < BM ? M - m0 : BM;
-      for (int64_t it = tid; it < rows * c8; it += 256) {
-        const int64_t row = it / c8, c = it - row * c8;
-        const uint4 raw = *reinterpret_cast<const uint4*>(A + (m0 + row) * pitch + c * 16);
-        float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                      bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
-        *reinterpret_cast<uint32_t*>(g.acbp_codes + (m0 + row) * (pitch / 4) + c * 4) =
-            quant_pack8_int4(v, sc[BM + row]);
+      const int64_t items = cw > 0 ? rows * cw : 0;
+      for (int64_t base = tid; base < items; base += 256 * 8) {
+        uint4 raw[8];
+        int64_t off[8];
+        int rw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t it = base + u * 256;
+          rw[u] = -1;
+          if (it < items) {
+            const int64_t row = it / cw, c = cb + (it - row * cw);
+            rw[u] = (int)row;
+            off[u] = (m0 + row) * pitch + c * 16;
+            raw[u] = *reinterpret_cast<const uint4*>(A + off[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (rw[u] < 0) continue;
+          float v[8] = {bf16_lo(raw[u].x), bf16_hi(raw[u].x), bf16_lo(raw[u].y), bf16_hi(raw[u].y),
+                        bf16_lo(raw[u].z), bf16_hi(raw[u].z), bf16_lo(raw[u].w), bf16_hi(raw[u].w)};
+          *reinterpret_cast<uint32_t*>(g.acbp_codes + off[u] / 4) = quant_pack8_int4(v, sc[BM + rw[u]]);
+        }
       }
-      if (tid < rows) g.acbp_scales[m0 + tid] = scale_of(sc[tid], 7.f);
+      if (tn == 0 && tid < rows) g.acbp_scales[m0 + tid] = scale_of(sc[tid], 7.f);
     }
   }
 
@@ -561,11 +582,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
 
 // Forward product y = x . w^T of a bf16 linear layer, with the ACBP codes of
 // x emitted by the first column of tiles (gemm_tile BF16).
-template <int EPI>
+// BM = 256 where the grid still fills every workgroup slot of the chip (two
+// per CU), else BM = 128 (more, shorter tiles).
+template <int BM, int EPI>
 __global__ __launch_bounds__(256, 2) void k_forward(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * GemmShape<false, 128, 128, 64, 3>::STAGE];
-  __shared__ float sc[256];
-  gemm_tile<false, 128, 128, 64, 3, EPI, false, true>(g, blockIdx.x, 0, lds, sc);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * GemmShape<false, BM, 128, 64, 3>::STAGE];
+  __shared__ float sc[BM + (BM > 128 ? BM : 128)];
+  gemm_tile<false, BM, 128, 64, 3, EPI, false, true>(g, blockIdx.x, 0, lds, sc);
 }
 
 // Input gradient of a convolution as an implicit GEMM over the taps (CONV
@@ -778,10 +801,17 @@ hipError_t launch_forward(const uint16_t* x, const uint16_t* w, int64_t T, int64
   a.Cb = y16;
   a.acbp_codes = codes;
   a.acbp_scales = scales;
-  const int64_t tiles = (int64_t)cdiv(T, 128) * cdiv(O, 128);
+  const int64_t tiles256 = (int64_t)cdiv(T, 256) * cdiv(O, 128);
+  const bool big = tiles256 >= 2 * 256;  // two workgroups per CU, 256 CUs
+  const int64_t tiles = big ? tiles256 : (int64_t)cdiv(T, 128) * cdiv(O, 128);
   const dim3 g((unsigned)((tiles + 7) / 8 * 8));
-  if (y16) hipLaunchKernelGGL((k_forward<EPI_BF16>), g, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_forward<EPI_F32>), g, dim3(256), 0, s, a);
+  if (big) {
+    if (y16) hipLaunchKernelGGL((k_forward<256, EPI_BF16>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_forward<256, EPI_F32>), g, dim3(256), 0, s, a);
+  } else {
+    if (y16) hipLaunchKernelGGL((k_forward<128, EPI_BF16>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_forward<128, EPI_F32>), g, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
