@@ -43,6 +43,8 @@ struct Layout {
   size_t partial;                             // int32 split-K partials
   int64_t nch_o, nch_i, ntr_t, ntr_o;         // transform tile grid
   hlq::GemmPlan plan_gx, plan_gw;
+  hlq::PairPlan pair;                         // tiles and g_w K splits of the pair launch
+  size_t pair_part, pair_ctr;                 // its INT32 partial sums, arrival counters
 };
 
 hlq_status check_shape(int64_t T, int64_t I, int64_t O, int block, int rank) {
@@ -105,6 +107,9 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   L.pub.gw_splits = L.plan_gw.splits;
   L.partial = take(part);
   L.pub.partial = L.partial;
+  L.pair = hlq::plan_pair(T, I, O, L.plan_gx, L.plan_gw);
+  L.pair_part = take(L.pair.part_bytes);
+  L.pair_ctr = take((size_t)L.pair.nctr * 4);
   L.pub.total = off;
   return L;
 }
@@ -177,6 +182,8 @@ hlq::TrArgs make_tr_args(const Layout& L, const void* g_y, int gy_dtype, const u
   a.conv = 0;
   a.Hc = a.Wc = a.Cc = a.P = a.Q = a.S = a.cstride = a.cpad = 0;
   a.zero_row = nullptr;
+  a.pair_ctr = reinterpret_cast<unsigned*>(ws + L.pair_ctr);
+  a.pair_nctr = L.pair.nctr;
   return a;
 }
 
@@ -293,10 +300,13 @@ static hlq_status run_backward(const Layout& L, const void* g_y, int gy_dtype,
   const float gw_alpha =
       reduction == HLQ_MEAN ? (float)(1.0 / ((double)block * (double)T)) : inv_n;
   if (on(HLQ_STEP_GEMM_GX) && on(HLQ_STEP_GEMM_GW)) {  // both GEMMs, one launch
+    // the QUANT pass (this call's or, for a GEMM-only step call, the one that
+    // wrote the codes) cleared the g_w split counters; every launch leaves them zero
     HLQ_TRY(hlq::launch_gemm_pair(a.q_gy, a.q_w, T, I, a.kxb, L.plan_gx, a.s_gy, a.s_w,
                                   gx_tok ? 1 : 0, inv_n, g_x, a.q_gyl, a.q_xl, O, a.kwb,
                                   L.plan_gw, a.s_gyl, a.s_xl, gw_tok ? 1 : 0, gw_alpha, g_w,
-                                  s));
+                                  L.pair, reinterpret_cast<int32_t*>(ws + L.pair_part),
+                                  a.pair_ctr, false, s));
     return HLQ_OK;
   }
   if (on(HLQ_STEP_GEMM_GX))  // g_x = acc * s_gy[t] * s_w[i] / n
@@ -401,20 +411,22 @@ hlq_status hlq_gemm_gw_acc(const void* workspace, size_t workspace_bytes, int64_
   return HLQ_OK;
 }
 
-hlq_status hlq_gemm_pair_acc(const void* workspace, size_t workspace_bytes, int64_t T,
-                             int64_t I, int64_t O, int block, int rank, int32_t* acc_x,
-                             int32_t* acc_w, void* stream) {
+hlq_status hlq_gemm_pair_acc(void* workspace, size_t workspace_bytes, int64_t T, int64_t I,
+                             int64_t O, int block, int rank, int32_t* acc_x, int32_t* acc_w,
+                             void* stream) {
   if (!acc_x || !acc_w) return HLQ_ERR_NULL;
   Layout L;
   hlq_status st = acc_checks(workspace, workspace_bytes, T, I, O, block, rank, &L);
   if (st != HLQ_OK) return st;
   if (!aligned16(acc_x) || !aligned16(acc_w)) return HLQ_ERR_ALIGN;
-  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   HLQ_TRY(hlq::launch_gemm_pair(ws + L.pub.q_gy, ws + L.pub.q_w, T, I, L.pub.kx_pitch,
                                 L.plan_gx, nullptr, nullptr, 0, 1.f, nullptr, ws + L.pub.q_gyl,
                                 ws + L.pub.q_xl, O, L.pub.kw_pitch, L.plan_gw, nullptr, nullptr,
-                                0, 1.f, nullptr, static_cast<hipStream_t>(stream),
-                                hlq::EPI_I32, acc_x, acc_w));
+                                0, 1.f, nullptr, L.pair,
+                                reinterpret_cast<int32_t*>(ws + L.pair_part),
+                                reinterpret_cast<unsigned*>(ws + L.pair_ctr), true,
+                                static_cast<hipStream_t>(stream), hlq::EPI_I32, acc_x, acc_w));
   return HLQ_OK;
 }
 

@@ -17,6 +17,8 @@
 //    values, which orders like the values and commutes, so results do not
 //    depend on scheduling.
 #include <hip/hip_runtime.h>
+#include <algorithm>
+#include <cmath>
 #include <stdint.h>
 
 #include <type_traits>
@@ -157,6 +159,15 @@ struct GemmArgs {
   uint16_t* Cb;
   uint8_t* acbp_codes;
   float* acbp_scales;
+  // K split across workgroups (INT8 tiles of the pair launch): with nsplit > 1,
+  // split s of tile t stores its INT32 sums to part + (t * nsplit + s) * BM * BN
+  // (thread-major, device-coherent write-through), then counts itself into
+  // ctr[t]; the workgroup that arrives last adds the other splits' sums (loads
+  // that bypass the XCD's own L2) and alone runs the epilogue, resetting ctr[t]
+  // to zero.  No workgroup waits on another.
+  int32_t nsplit;
+  int32_t* part;
+  unsigned* ctr;
 };
 
 // One output tile (workgroup w of the tile grid, K split `split`) of one GEMM.
@@ -450,6 +461,54 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 #undef HLQ_GEMM_ISSUE
 #undef HLQ_GEMM_WAIT
 
+  if constexpr (!BF16 && !CONV && EPI != EPI_PARTIAL) {
+    if (g.nsplit > 1) {
+      typedef int v4i __attribute__((ext_vector_type(4)));
+      constexpr int NQ = FM * FN * 4;  // 16-byte groups of this thread's sums
+      const int64_t tile = tm * ((N + BN - 1) / BN) + tn;
+      const int ns = g.nsplit, sp = (int)split;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          g.part + tile * ns * (int64_t)(BM * BN), 0, ns * BM * BN * 4, 0x00020000);
+      constexpr int SC1 = 16;  // cache policy: device scope (write-through / coherent load)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const v4i v = {acc[i][j][4 * k], acc[i][j][4 * k + 1], acc[i][j][4 * k + 2],
+                           acc[i][j][4 * k + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v, rs, ((sp * NQ + (i * FN + j) * 4 + k) * 256 + tid) * 16, 0, SC1);
+          }
+      wait_vmcnt<0>();  // this thread's sums have reached device scope
+      __shared__ unsigned arrived;
+      __syncthreads();
+      if (tid == 0)
+        arrived = __hip_atomic_fetch_add(g.ctr + tile, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (arrived != (unsigned)(ns - 1)) return;
+      if (tid == 0) __hip_atomic_store(g.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int o = 0; o < ns; ++o) {
+        if (o == sp) continue;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
+                  rs, ((o * NQ + (i * FN + j) * 4 + k) * 256 + tid) * 16, 0, SC1);
+              acc[i][j][4 * k] += v[0];
+              acc[i][j][4 * k + 1] += v[1];
+              acc[i][j][4 * k + 2] += v[2];
+              acc[i][j][4 * k + 3] += v[3];
+            }
+      }
+    }
+  }
+
   if constexpr (BF16) {
     if (acbp) {
       // row maxima: the 8 packed maxima of a fragment, then the other K half
@@ -607,16 +666,25 @@ __global__ __launch_bounds__(256, 2) void k_dgrad(GemmArgs g) {
 // two plus a split-K pass, and neither GEMM's tail leaves the GPU idle.
 // EPI_I32 stores the INT32 accumulators instead of the fp32 gradients (tests
 // compare them bit for bit); everything else is the same launch.
+// With gw.nsplit > 1 the first n1 = nsplit * n1w workgroups are split s =
+// b / n1w of g_w workgroup b % n1w (n1w a multiple of 8, so every split of a
+// tile runs on the XCD the tile mapping gives it).
 template <int BM1, int BN1, int KB1, int NS1, int BM0, int BN0, int KB0, int NS0, int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm_pair(GemmArgs gw, int64_t n1, GemmArgs gx) {
+__global__ __launch_bounds__(256, 2) void k_gemm_pair(GemmArgs gw, int64_t n1, int64_t n1w,
+                                                      GemmArgs gx) {
   constexpr int L1 = NS1 * GemmShape<false, BM1, BN1, KB1, NS1>::STAGE;
   constexpr int L0 = NS0 * GemmShape<true, BM0, BN0, KB0, NS0>::STAGE;
   constexpr int SC = BM1 + BN1 > BM0 + BN0 ? BM1 + BN1 : BM0 + BN0;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L1 > L0 ? L1 : L0];
   __shared__ float sc[SC];
   const int64_t b = blockIdx.x;
-  if (b < n1) gemm_tile<false, BM1, BN1, KB1, NS1, EPI>(gw, b, 0, lds, sc);
+  if (b < n1) gemm_tile<false, BM1, BN1, KB1, NS1, EPI>(gw, b % n1w, b / n1w, lds, sc);
   else gemm_tile<true, BM0, BN0, KB0, NS0, EPI>(gx, b - n1, 0, lds, sc);
+}
+
+__global__ void k_zero_u32(unsigned* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
 }
 
 // Sum of split-K INT32 partials (exact) followed by the dequantizing epilogue.
@@ -716,12 +784,39 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
   return launch_gemm_finalize(partial, splits, M, N, sa, sa_step, sb, sb_step, alpha, C, s);
 }
 
+// g_w tile of the pair launch: the plan's, except that a long-K grid of fewer
+// than 64 tiles takes 64-row tiles (cfg 3: 64 x 128, KB 128, 3 stages): twice
+// the tiles, half the K work each.  Then K splits: the g_w tiles start first,
+// so a g_w tile longer than the launch's mean work per workgroup slot (two per
+// CU) sets its length; nsplit cuts it to about that mean (at most 4 splits of
+// at least 4 stages each).  Work is counted in MACs, an INT4 MAC (widened onto
+// the INT8 matrix cores) at 1.3 INT8 MACs.
+PairPlan plan_pair(int64_t T, int64_t I, int64_t O, const GemmPlan& px, const GemmPlan& pw) {
+  PairPlan pp;
+  pp.wcfg = pw.cfg; pp.wbm = pw.bm; pp.wbn = pw.bn;
+  if (pw.cfg == 2 && (int64_t)cdiv(O, 128) * cdiv(I, 128) < 64) { pp.wcfg = 3; pp.wbm = 64; }
+  pp.tx = (int64_t)cdiv(T, px.bm) * cdiv(I, px.bn);
+  pp.tw = (int64_t)cdiv(O, pp.wbm) * cdiv(I, pp.wbn);
+  const double dw = (double)pp.wbm * pp.wbn * pw.stages * pw.kb;
+  const double dx = 1.3 * px.bm * px.bn * px.stages * px.kb * 2;
+  const double mean = (pp.tw * dw + pp.tx * dx) / 512.0;
+  int ns = (int)std::ceil(dw / mean - 0.25);
+  ns = std::max(1, std::min(ns, 4));
+  while (ns > 1 && pw.stages / ns < 4) --ns;
+  pp.sps = (pw.stages + ns - 1) / ns;
+  pp.nsplit = (int)((pw.stages + pp.sps - 1) / pp.sps);  // every split non-empty
+  pp.part_bytes = pp.nsplit > 1 ? (size_t)pp.tw * pp.nsplit * pp.wbm * pp.wbn * 4 : 0;
+  pp.nctr = pp.nsplit > 1 ? pp.tw : 0;
+  return pp;
+}
+
 hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, int64_t I,
                             int64_t kx_pitch, const GemmPlan& px, const float* s_gy,
                             const float* s_w, int gx_step, float gx_alpha, float* g_x,
                             const uint8_t* gwA, const uint8_t* gwB, int64_t O, int64_t kw_pitch,
                             const GemmPlan& pw, const float* s_gyl, const float* s_xl,
-                            int gw_step, float gw_alpha, float* g_w, hipStream_t s,
+                            int gw_step, float gw_alpha, float* g_w, const PairPlan& pp,
+                            int32_t* part, unsigned* ctr, bool zero_ctr, hipStream_t s,
                             GemmEpi epi, int32_t* acc_x, int32_t* acc_w) {
   if (kx_pitch % px.kb || px.stages * px.kb != kx_pitch) return hipErrorInvalidValue;
   if (kw_pitch % pw.kb || pw.stages * pw.kb != kw_pitch) return hipErrorInvalidValue;
@@ -729,25 +824,28 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
     return hipErrorInvalidValue;
   if (epi == EPI_I32 && (!acc_x || !acc_w)) return hipErrorInvalidValue;
   if (epi != EPI_F32 && epi != EPI_I32) return hipErrorInvalidValue;
+  if (pp.nsplit < 1 || pp.nsplit > 4 || (pp.nsplit > 1 && (!part || !ctr))) return hipErrorInvalidValue;
+  if ((pp.nsplit - 1) * pp.sps >= pw.stages) return hipErrorInvalidValue;  // an empty split
   const GemmArgs ax{gxA, gxB, T, I, kx_pitch, px.stages, px.stages, s_gy, gx_step, s_w, gx_step,
                     gx_alpha, g_x, acc_x};
-  const GemmArgs aw{gwA, gwB, O, I, kw_pitch, pw.stages, pw.stages, s_gyl, gw_step, s_xl, gw_step,
-                    gw_alpha, g_w, acc_w};
-  // g_w tile: the plan's, except that a long-K g_w grid of fewer than 64
-  // tiles (a quarter of the CU count; its tiles are the launch's critical
-  // path) takes 64-row tiles (cfg 3: 64 x 128, KB 128, 3 stages): twice the
-  // tiles, half the K work each.  Larger grids keep 128 x 128, which reads
-  // fewer LDS bytes per MFMA (ViT-B qkv, 108 tiles: 46 -> 43 us).
-  int wcfg = pw.cfg, wbm = pw.bm;
-  if (pw.cfg == 2 && (int64_t)cdiv(O, 128) * cdiv(I, 128) < 64) { wcfg = 3; wbm = 64; }
-  const int64_t tx = (int64_t)cdiv(T, px.bm) * cdiv(I, px.bn);
-  const int64_t tw = (int64_t)cdiv(O, wbm) * cdiv(I, pw.bn);
-  const int64_t n1 = (tw + 7) / 8 * 8, n0 = (tx + 7) / 8 * 8;
+  GemmArgs aw{gwA, gwB, O, I, kw_pitch, pw.stages, pp.sps, s_gyl, gw_step, s_xl, gw_step,
+              gw_alpha, g_w, acc_w};
+  aw.nsplit = pp.nsplit;
+  aw.part = part;
+  aw.ctr = ctr;
+  if (pp.nsplit > 1 && zero_ctr) {
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)std::min<int64_t>(cdiv(pp.nctr, 256), 64)),
+                       dim3(256), 0, s, ctr, pp.nctr);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n1w = (pp.tw + 7) / 8 * 8, n0 = (pp.tx + 7) / 8 * 8;
+  const int64_t n1 = n1w * pp.nsplit;
   const dim3 g((unsigned)(n1 + n0));
 #define HLQ_PAIR(W_, X_)                                                                 \
   do {                                                                                   \
-    if (epi == EPI_F32) hipLaunchKernelGGL((k_gemm_pair<W_, X_, EPI_F32>), g, dim3(256), 0, s, aw, n1, ax); \
-    else hipLaunchKernelGGL((k_gemm_pair<W_, X_, EPI_I32>), g, dim3(256), 0, s, aw, n1, ax); \
+    if (epi == EPI_F32) hipLaunchKernelGGL((k_gemm_pair<W_, X_, EPI_F32>), g, dim3(256), 0, s, aw, n1, n1w, ax); \
+    else hipLaunchKernelGGL((k_gemm_pair<W_, X_, EPI_I32>), g, dim3(256), 0, s, aw, n1, n1w, ax); \
   } while (0)
 #define HLQ_W0 128, 128, 64, 3
 #define HLQ_W1 256, 128, 64, 3
@@ -756,7 +854,7 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
 #define HLQ_X0 128, 128, 64, 3
 #define HLQ_X1 256, 128, 64, 3
   const bool x1 = px.cfg == 1;
-  switch (wcfg) {
+  switch (pp.wcfg) {
     case 1: if (x1) HLQ_PAIR(HLQ_W1, HLQ_X1); else HLQ_PAIR(HLQ_W1, HLQ_X0); break;
     case 2: if (x1) HLQ_PAIR(HLQ_W2, HLQ_X1); else HLQ_PAIR(HLQ_W2, HLQ_X0); break;
     case 3: if (x1) HLQ_PAIR(HLQ_W3, HLQ_X1); else HLQ_PAIR(HLQ_W3, HLQ_X0); break;

@@ -53,6 +53,8 @@ struct TrArgs {
   int conv;
   int64_t Hc, Wc, Cc, P, Q, S, cstride, cpad;
   uint8_t* zero_row;          // kxb zero bytes written by QUANT (conv), else null
+  unsigned* pair_ctr;         // arrival counters of the pair GEMM, cleared by QUANT
+  int64_t pair_nctr;
 };
 
 // Launch configuration of one integer GEMM C[m][n] = sum_k A[m][k] B[n][k],
@@ -120,18 +122,35 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
                        float alpha, GemmEpi epi, float* C, int32_t* Ci,
                        int32_t* partial, hipStream_t s);
 
-// Both GEMMs of the backward in one launch, no split-K.  EPI_F32 (the
-// backward): g_x = acc(q_gy, q_w) * s_gy * s_w * gx_alpha, g_w = acc(q_gyl,
-// q_xl) * s_gyl * s_xl * gw_alpha (scale steps 1 per-token, 0 per-tensor).
-// EPI_I32: the same launch stores the INT32 accumulators to acc_x [T][I] and
-// acc_w [O][I] instead (scales and fp32 outputs unused).  The plans fix the
-// tile configurations; their splits are ignored.
+// Tiles of the pair launch (both GEMMs of the backward in one grid).  The g_w
+// tiles (long K = T') may split K over nsplit workgroups: each stores its INT32
+// sums to `part` (device-coherent), counts itself into its tile's counter, and
+// the last to arrive adds the others' sums and runs the epilogue.
+struct PairPlan {
+  int wcfg, wbm, wbn;   // g_w tile configuration (rows of O x rows of I)
+  int64_t tw, tx;       // g_w and g_x tiles
+  int nsplit;           // K splits of each g_w tile (1: none)
+  int64_t sps;          // K stages per split (the last takes the remainder)
+  size_t part_bytes;    // INT32 partial sums, tw * nsplit * wbm * wbn * 4 (0 without split)
+  int64_t nctr;         // arrival counters, one per g_w tile (0 without split)
+};
+PairPlan plan_pair(int64_t T, int64_t I, int64_t O, const GemmPlan& px, const GemmPlan& pw);
+
+// Both GEMMs of the backward in one launch.  EPI_F32 (the backward): g_x =
+// acc(q_gy, q_w) * s_gy * s_w * gx_alpha, g_w = acc(q_gyl, q_xl) * s_gyl *
+// s_xl * gw_alpha (scale steps 1 per-token, 0 per-tensor).  EPI_I32: the
+// same launch stores the INT32 accumulators to acc_x [T][I] and acc_w [O][I]
+// instead (scales and fp32 outputs unused).  With pp.nsplit > 1, part holds
+// pp.part_bytes and ctr pp.nctr counters that must read zero at launch (the
+// QUANT transform pass clears them; every launch leaves them zero);
+// zero_ctr clears them first with a small kernel.
 hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, int64_t I,
                             int64_t kx_pitch, const GemmPlan& px, const float* s_gy,
                             const float* s_w, int gx_step, float gx_alpha, float* g_x,
                             const uint8_t* gwA, const uint8_t* gwB, int64_t O, int64_t kw_pitch,
                             const GemmPlan& pw, const float* s_gyl, const float* s_xl,
-                            int gw_step, float gw_alpha, float* g_w, hipStream_t s,
+                            int gw_step, float gw_alpha, float* g_w, const PairPlan& pp,
+                            int32_t* part, unsigned* ctr, bool zero_ctr, hipStream_t s,
                             GemmEpi epi = EPI_F32, int32_t* acc_x = nullptr,
                             int32_t* acc_w = nullptr);
 

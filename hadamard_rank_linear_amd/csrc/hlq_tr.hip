@@ -865,6 +865,9 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
     if (a.zero_row && blockIdx.x == 0)
       for (int64_t i = threadIdx.x; i < a.kxb / 16; i += 256)
         reinterpret_cast<uint4*>(a.zero_row)[i] = make_uint4(0, 0, 0, 0);
+    // arrival counters of the GEMM launch that follows (K-split g_w tiles)
+    if (blockIdx.x == 1 % gridDim.x)
+      for (int64_t i = threadIdx.x; i < a.pair_nctr; i += 256) a.pair_ctr[i] = 0u;
   }
   if (blockIdx.x == 0 && threadIdx.x < 4) {
     if constexpr (PASS == PASS_MAX) {

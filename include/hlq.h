@@ -182,6 +182,8 @@ enum {
  * hlq_linear_backward.  A subset re-runs those launches on a workspace that
  * the earlier steps have filled (every step is idempotent given its inputs),
  * which lets a caller time or inspect one kernel of the sequence in place.
+ * The GEMM steps read what the QUANT step last wrote to the workspace,
+ * including the arrival counters of the K-split g_w tiles it clears.
  */
 hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
                                      const uint8_t* x_codes, const float* x_scales,
@@ -230,16 +232,18 @@ hlq_status hlq_workspace_layout_query(int64_t T, int64_t I, int64_t O, int block
  * "int8-accelerated" products).  acc_x [T][I] = sum_o q_gy[t,o] q_w[o,i];
  * acc_w [O][I] = sum_t' q_gyl[t',o] q_xl[t',i].
  *   hlq_gemm_pair_acc: the one launch hlq_linear_backward runs for both
- *     GEMMs (same tile grids and schedule), its epilogue storing the INT32
- *     sums instead of the fp32 gradients.
+ *     GEMMs (same tile grids, K splits and schedule), its epilogue storing
+ *     the INT32 sums instead of the fp32 gradients.  It writes the
+ *     workspace's split-K partial sums and arrival counters (the codes and
+ *     scales are only read), hence the non-const workspace.
  *   hlq_gemm_gx_acc / hlq_gemm_gw_acc: the single-GEMM launches that
  *     hlq_linear_backward_steps runs when only one GEMM step is selected.
  * workspace_bytes is checked against hlq_linear_backward_workspace_size
  * (HLQ_ERR_WORKSPACE); acc_* are device buffers of the sizes above.
  */
-hlq_status hlq_gemm_pair_acc(const void* workspace, size_t workspace_bytes, int64_t T,
-                             int64_t I, int64_t O, int block, int rank, int32_t* acc_x,
-                             int32_t* acc_w, void* stream);
+hlq_status hlq_gemm_pair_acc(void* workspace, size_t workspace_bytes, int64_t T, int64_t I,
+                             int64_t O, int block, int rank, int32_t* acc_x, int32_t* acc_w,
+                             void* stream);
 hlq_status hlq_gemm_gx_acc(const void* workspace, size_t workspace_bytes, int64_t T,
                            int64_t I, int64_t O, int block, int rank, int32_t* acc_x,
                            void* stream);

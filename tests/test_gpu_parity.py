@@ -93,6 +93,26 @@ def test_shapes(T, I, O, n, r, dt, gx_mode, gw_mode):
     _case(cfg)
 
 
+# The g_w tiles of the pair launch split K over 2, 3 and 4 workgroups when
+# T' is long against the rest of the launch (the last to arrive adds the
+# others' INT32 sums): the accumulators stay bit-exact for every split count.
+SPLIT_SHAPES = [
+    # (T, I, O, n, r, dtype): g_w tiles x K splits
+    (2048, 128, 64, 16, 8, wl.F32),     # 1 tile x 2 splits of 4 stages
+    (3072, 520, 336, 16, 8, wl.BF16),   # 30 tiles (ragged O and I) x 3 splits
+    (2048, 384, 256, 16, 16, wl.BF16),  # 12 tiles x 4 splits
+]
+
+
+@pytest.mark.parametrize("T,I,O,n,r,dt", SPLIT_SHAPES)
+@pytest.mark.parametrize("gx_mode,gw_mode", [(0, 0), (1, 1)])
+def test_split_k_shapes(T, I, O, n, r, dt, gx_mode, gw_mode):
+    base = wl.BY_NAME["vitb_qkv"] if dt == wl.BF16 else wl.BY_NAME["tiny"]
+    cfg = dataclasses.replace(base, T=T, I=I, O=O, block=n, rank=r, dtype=dt,
+                              gx_mode=gx_mode, gw_mode=gw_mode, index=200 + T % 89)
+    _case(cfg)
+
+
 # ----------------------------------------------- layer configs, reduced tokens
 
 REDUCED_T = {"vitb_qkv": 1040, "vitb_fc2": 1056, "llama3_8b_down": 1024,
