@@ -25,7 +25,7 @@
 
 namespace {
 
-constexpr int64_t kMaxO = 171196;       // 256 * 49 * O < 2^31 (INT4 lanes hold 16*code)
+constexpr int64_t kMaxO = 342391;       // 49 * O < 2^24: the FP6 product's fp32 sums stay exact
 constexpr int64_t kMaxTLow = 133143;    // 127^2 * T' < 2^31
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -60,8 +60,8 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   Layout L;
   memset(&L, 0, sizeof(L));
   const int64_t t_low = T / block * rank;
-  const int64_t kx = (O + 127) / 128 * 128;  // INT4 codes per row, 64-byte stages
-  const int64_t kxb = kx / 2;
+  const int64_t kx = (O + 127) / 128 * 128;  // codes per row: FP6 groups of 128 in 96 bytes
+  const int64_t kxb = kx / 128 * 96;
   const int64_t kwb = (t_low + 127) / 128 * 128;  // INT8 codes, 128-byte stages
   L.pub.kx_pitch = kxb;
   L.pub.kw_pitch = kwb;

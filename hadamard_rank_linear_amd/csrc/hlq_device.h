@@ -1,6 +1,6 @@
 // Device helpers shared by the gfx950 kernels of the HLQ/HOT backward:
 // bf16 widening, in-register and cross-lane Walsh-Hadamard butterflies, the
-// quantizer's rounding and nibble packing.  Header-only, internal.
+// quantizer's rounding, nibble and FP6 packing.  Header-only, internal.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -102,6 +102,43 @@ __device__ __forceinline__ uint32_t pack8_nibbles(const uint32_t (&q)[8]) {
   const uint32_t ev = pack_lo_bytes(q[0], q[2], q[4], q[6]);
   const uint32_t od = pack_lo_bytes(q[1], q[3], q[5], q[7]);
   return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+}
+
+// ---- g_x GEMM operands: INT4 codes stored as FP6 E2M3
+// Every code q in [-7, 7] is exact in FP6 E2M3 (sign, 2 exponent bits with
+// bias 1, 3 mantissa bits), so are the products (|q q'| <= 49) and every fp32
+// partial sum below 2^24: the g_x product runs on the FP6 matrix cores with
+// exact integer results.  A row of codes is stored in groups of 128 K values
+// (96 bytes): quarter Q of a group (its values 32 Q .. 32 Q + 31) is a 24-byte
+// stream of 6-bit fields (value j at bits 6 j .. 6 j + 5), and the quarters
+// sit in the order 0, 2, 1, 3.  Lane half h of the matrix instruction then
+// finds its K values of both K steps of a group (quarters h and 2 + h) in
+// the 48 contiguous bytes 48 h .. 48 h + 47.
+__device__ __forceinline__ constexpr int fp6_quarter_pos(int q) { return ((q & 1) << 1) | (q >> 1); }
+
+// The code rne(fl(v * inv)) as an integer-valued float (the magic add of
+// quant_bits, then an exact subtraction; never -0).
+__device__ __forceinline__ float quant_code_f32(float v, float inv) {
+  const float p = v * inv;
+  return (p + 12582912.0f) - 12582912.0f;
+}
+
+typedef float v16f_cvt __attribute__((ext_vector_type(16)));
+typedef int v6i_cvt __attribute__((ext_vector_type(6)));
+
+// 32 integer-valued floats in [-7, 7] -> 6 dwords of FP6 E2M3 fields, value j
+// at bits 6 j (exact conversion; the instruction interleaves its two 16-value
+// operands, the first at the even positions).
+__device__ __forceinline__ void fp6_pack32(const float (&v)[32], uint32_t (&d)[6]) {
+  v16f_cvt ev, od;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    ev[k] = v[2 * k];
+    od[k] = v[2 * k + 1];
+  }
+  const v6i_cvt r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+#pragma unroll
+  for (int k = 0; k < 6; ++k) d[k] = (uint32_t)r[k];
 }
 
 __device__ __forceinline__ uint32_t quant_pack8_int4(const float (&v)[8], float inv) {

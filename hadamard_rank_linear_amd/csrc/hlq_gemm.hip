@@ -30,18 +30,21 @@ namespace hlq {
 
 // ------------------------------------------------------------ integer GEMM
 // C[m][n] = sum_k A[m][k] * B[n][k]; A [M][pitch], B [N][pitch] bytes, K
-// contiguous and zero-padded to a multiple of the stage depth KB.  INT4
-// operands hold two codes per byte and stay packed in HBM, L2 and LDS; each
-// 16-byte fragment is widened on the LDS->register path into two int8
-// fragments holding 16*code (low nibble shifted up, high nibble masked in
-// place), so the INT32 sum is 256 times the code product sum and is shifted
-// back exactly.  Both operands are widened the same way, so the nibble order
-// inside a lane leaves the dot product unchanged.
+// contiguous and zero-padded to a multiple of the stage depth KB.
 //
-// Matrix core: v_mfma_i32_32x32x32_i8 (32 cycles of the matrix pipe for a
-// 32x32x32 product; the 16x16x64 form needs more independent accumulators
-// than a wave has to stay busy).  Operand X holds 32 rows of A, operand Y 32
-// rows of B; lane l feeds row l%32 with 16 consecutive K bytes of half l/32.
+// Matrix cores: INT8 operands (the g_w product) on v_mfma_i32_32x32x32_i8
+// (32 cycles of the matrix pipe for a 32x32x32 product; the 16x16x64 form
+// needs more independent accumulators than a wave has to stay busy); lane l
+// feeds row l%32 with 16 consecutive K bytes of half l/32.  The INT4 codes of
+// the g_x product arrive as FP6 E2M3 fields (exact for [-7, 7]; see
+// hlq_device.h) and run on v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales):
+// twice the K of the INT8 instruction in the same 32 cycles, no unpacking,
+// and fp32 sums that are exact integers below 2^24.  Lane l feeds row l%32
+// with the 32 K values 32*(l/32) .. of the K step (6 dwords); a 96-byte
+// stage row (128 K values, two K steps) holds those of half h at bytes
+// 48 h .. 48 h + 47, read as three 16-byte chunks whose first and last six
+// dwords are the operands of the two steps.
+// Operand X holds 32 rows of A, operand Y 32 rows of B.
 // Lane l then holds D[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator r: one
 // column n of C per lane, so a store of register r writes 128 contiguous
 // bytes of a C row per half-wave.
@@ -75,11 +78,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-__device__ __forceinline__ void widen_int4x2(u32x4 p, v4i& a, v4i& b) {
-  a[0] = (int)((p[0] << 4) & 0xF0F0F0F0u); a[1] = (int)(p[0] & 0xF0F0F0F0u);
-  a[2] = (int)((p[1] << 4) & 0xF0F0F0F0u); a[3] = (int)(p[1] & 0xF0F0F0F0u);
-  b[0] = (int)((p[2] << 4) & 0xF0F0F0F0u); b[1] = (int)(p[2] & 0xF0F0F0F0u);
-  b[2] = (int)((p[3] << 4) & 0xF0F0F0F0u); b[3] = (int)(p[3] & 0xF0F0F0F0u);
+
+typedef unsigned int v12u __attribute__((ext_vector_type(12)));
+typedef unsigned int v8u __attribute__((ext_vector_type(8)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// The three 16-byte chunks of a lane's FP6 stage row as one 12-dword value.
+__device__ __forceinline__ v12u join12(u32x4 a, u32x4 b, u32x4 c) {
+  const v8u ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  const v8u cc = __builtin_shufflevector(c, c, 0, 1, 2, 3, -1, -1, -1, -1);
+  return __builtin_shufflevector(ab, cc, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11);
+}
+// Operand of K step K (0, 1): six dwords of FP6 fields (the instruction reads six).
+template <int K>
+__device__ __forceinline__ v8i step_op(v12u r) {
+  return __builtin_bit_cast(
+      v8i, __builtin_shufflevector(r, r, 6 * K, 6 * K + 1, 6 * K + 2, 6 * K + 3, 6 * K + 4,
+                                   6 * K + 5, -1, -1));
+}
+// One 32x32x64 product of FP6 E2M3 operands, unit block scales (E8M0 127).
+__device__ __forceinline__ v16f mfma_fp6(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ bool xcd_tile(int64_t w, int64_t nt_m, int64_t nt_n, int64_t& tm,
@@ -107,24 +126,32 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* l) {
 
 // Physical 16-byte chunk slot of logical chunk 0 in row r (XOR with it).
 // Depends on r & 15 only, so fragment bases (multiples of 32 rows) keep it.
+// The LDS serves a 16-byte read 16 lanes (16 rows) at a time from 64 banks
+// (16 groups of 16 bytes).  KB 96 (six chunks per row): rows 8..15 of every
+// 16 swap chunk pairs, so those 16 rows at one chunk fall in 16 distinct
+// groups (rows 0..7 at 6 r cover the even groups, the swap the odd ones;
+// measured 132 against 94 B/clk per CU for a swap on row bit 2).
 template <int KB>
 __device__ __forceinline__ int chunk_swz(int r) {
   if constexpr (KB == 128) return (r & 7) ^ ((r >> 3) & 1);
+  else if constexpr (KB == 96) return (r >> 3) & 1;
   else return (r >> 2) & 3;
 }
 
-template <bool INT4, int BM, int BN, int KB, int NS>
+// WNW waves along N (2 x WNW waves, NT = 128 * WNW threads per workgroup).
+template <bool FP6, int BM, int BN, int KB, int NS, int WNW = 2>
 struct GemmShape {
-  static constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
+  static constexpr int NT = 128 * WNW;
+  static constexpr int WTM = BM / 2, WTN = BN / WNW, FM = WTM / 32, FN = WTN / 32;
   static constexpr int CPR = KB / 16;                              // chunks per row
-  static constexpr int IA = BM * CPR / 256, IB = BN * CPR / 256;   // DMA ops per wave
+  static constexpr int IA = BM * CPR / NT, IB = BN * CPR / NT;     // DMA ops per wave
   static constexpr int IPW = IA + IB;
   static constexpr int STAGE = (BM + BN) * KB;
-  static constexpr int KK = KB / 32;                               // k-steps per stage
+  static constexpr int KK = FP6 ? KB / 48 : KB / 32;               // k-steps per stage
   static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA tile");
-  static_assert(IA * 256 == BM * CPR && IB * 256 == BN * CPR, "stage load split");
+  static_assert(IA * NT == BM * CPR && IB * NT == BN * CPR, "stage load split");
   static_assert(KK % 2 == 0, "fragment slots alternate per k-step");
-  static_assert(KB == 64 || KB == 128, "swizzle covers 4 or 8 chunks per row");
+  static_assert(FP6 ? KB == 96 : (KB == 64 || KB == 128), "swizzle covers 4, 6 or 8 chunks per row");
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   static_assert(NS * STAGE <= 160 * 1024, "LDS ring fits the CU");
 };
@@ -182,12 +209,13 @@ struct GemmArgs {
 // rows); after the K loop each tile re-reads (from cache) an equal slice of
 // its rows' columns and writes their INT4 codes, the first column of tiles
 // also the scales.
-template <bool INT4, int BM, int BN, int KB, int NS, int EPI, bool CONV = false,
-          bool BF16 = false>
+template <bool FP6, int BM, int BN, int KB, int NS, int EPI, bool CONV = false,
+          bool BF16 = false, int WNW = 2>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t split,
                                           uint8_t* lds, float* sc) {
-  static_assert(!(INT4 && BF16), "one operand type");
-  using G = GemmShape<INT4, BM, BN, KB, NS>;
+  static_assert(!(FP6 && BF16), "one operand type");
+  using G = GemmShape<FP6, BM, BN, KB, NS, WNW>;
+  constexpr int NT = G::NT;
   constexpr int FM = G::FM, FN = G::FN, IA = G::IA, IB = G::IB, IPW = G::IPW;
   constexpr int CPR = G::CPR, KK = G::KK;
   const uint8_t* __restrict__ A = g.A;
@@ -200,7 +228,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   float* __restrict__ C = g.C;
   int32_t* __restrict__ Ci = g.Ci;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   int64_t tm, tn;
   if (!xcd_tile(w, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn)) return;
   const int64_t m0 = tm * BM, n0 = tn * BN;
@@ -292,19 +320,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   int coff[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) coff[kk] = ((kk * 2 + fh) ^ sw) * 16;
+  // FP6: chunks 3 fh .. 3 fh + 2 of a stage row
+  int c6[3];
+#pragma unroll
+  for (int m = 0; m < 3; ++m) c6[m] = ((3 * fh + m) ^ sw) * 16;
 
   // Dequantization scales of the tile's rows (times alpha) and columns, read
   // before the K loop and parked in LDS (sc, an array of its own, so the
   // ring's DMA does not order its accesses): the epilogue then waits on no
   // global load while its stores are in flight.
-  constexpr int NSC = (BM + BN + 255) / 256;
+  constexpr int NSC = (BM + BN + NT - 1) / NT;
   float scv[NSC];
   if constexpr (EPI == EPI_F32 && !BF16) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q) {
       // one unconditional load per slot (a select of the address, so the
       // loaded value is not merged across branches, which would wait on it)
-      const int i = tid + 256 * q;
+      const int i = tid + NT * q;
       const int64_t m = m0 + i, n = n0 + (i - BM);
       const float* src = i < BM ? sa + (m < M ? m : M - 1) * sa_step
                                 : sb + (n < N ? (n >= 0 ? n : 0) : N - 1) * sb_step;
@@ -319,7 +351,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   // the scale loads before the stage loads are in flight)
   asm volatile("" ::: "memory");
 
-  using AccT = std::conditional_t<BF16, v16f, v16i>;
+  using AccT = std::conditional_t<BF16 || FP6, v16f, v16i>;
   AccT acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -342,15 +374,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   if constexpr (EPI == EPI_F32 && !BF16) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q)
-      if (tid + 256 * q < BM + BN) sc[tid + 256 * q] = tid + 256 * q < BM ? scv[q] * alpha : scv[q];
+      if (tid + NT * q < BM + BN) sc[tid + NT * q] = tid + NT * q < BM ? scv[q] * alpha : scv[q];
   }
   asm volatile("s_barrier" ::: "memory");
+  // FP6: chunks 0 and 1 of each fragment row (K step 0 and the first half of
+  // step 1), chunk 2 (the rest of step 1) loads under step 0's MFMAs
+  u32x4 p0a[FM], p1a[FM], p2a[FM], p0b[FN], p1b[FN], p2b[FN];
+  if constexpr (FP6) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-    fa[0][i] = *reinterpret_cast<const u32x4*>(lds + a_off + i * 32 * KB + coff[0]);
+    for (int i = 0; i < FM; ++i) {
+      p0a[i] = *reinterpret_cast<const u32x4*>(lds + a_off + i * 32 * KB + c6[0]);
+      p1a[i] = *reinterpret_cast<const u32x4*>(lds + a_off + i * 32 * KB + c6[1]);
+    }
 #pragma unroll
-  for (int j = 0; j < FN; ++j)
-    fb[0][j] = *reinterpret_cast<const u32x4*>(lds + b_off + j * 32 * KB + coff[0]);
+    for (int j = 0; j < FN; ++j) {
+      p0b[j] = *reinterpret_cast<const u32x4*>(lds + b_off + j * 32 * KB + c6[0]);
+      p1b[j] = *reinterpret_cast<const u32x4*>(lds + b_off + j * 32 * KB + c6[1]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[0][i] = *reinterpret_cast<const u32x4*>(lds + a_off + i * 32 * KB + coff[0]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[0][j] = *reinterpret_cast<const u32x4*>(lds + b_off + j * 32 * KB + coff[0]);
+  }
 
   // One K stage.  MODE 0: steady state (refill a buffer, prefetch the next
   // stage's first fragments); 1: the last NS-1 stages but one (prefetch, no
@@ -360,6 +408,52 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   auto stage = [&](int64_t st, auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
     const uint8_t* base = lds + buf * G::STAGE;
+    if constexpr (FP6) {
+      // K step 0: chunk 2 of every fragment row loads under its MFMAs
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        p2a[i] = *reinterpret_cast<const u32x4*>(base + a_off + i * 32 * KB + c6[2]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        p2b[j] = *reinterpret_cast<const u32x4*>(base + b_off + j * 32 * KB + c6[2]);
+      v12u ra[FM], rb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) ra[i] = join12(p0a[i], p1a[i], p2a[i]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) rb[j] = join12(p0b[j], p1b[j], p2b[j]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = mfma_fp6(step_op<0>(ra[i]), step_op<0>(rb[j]), acc[i][j]);
+      if constexpr (MODE != 2) {
+        // stage st+1 landed in every wave and no wave reads stage st any
+        // more: its chunks 0 and 1 load under step 1's MFMAs, and stage st's
+        // buffer is refilled (after those reads are issued)
+        if constexpr (MODE == 0) wait_vmcnt<(NS - 2) * IPW>();
+        else HLQ_GEMM_WAIT((S - st - 2 < NS - 2 ? S - st - 2 : NS - 2));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int ob = buf;
+        buf = buf + 1 == NS ? 0 : buf + 1;
+        const uint8_t* nb = lds + buf * G::STAGE;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          p0a[i] = *reinterpret_cast<const u32x4*>(nb + a_off + i * 32 * KB + c6[0]);
+          p1a[i] = *reinterpret_cast<const u32x4*>(nb + a_off + i * 32 * KB + c6[1]);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          p0b[j] = *reinterpret_cast<const u32x4*>(nb + b_off + j * 32 * KB + c6[0]);
+          p1b[j] = *reinterpret_cast<const u32x4*>(nb + b_off + j * 32 * KB + c6[1]);
+        }
+        if constexpr (MODE == 0) HLQ_GEMM_ISSUE(st + NS, ob);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = mfma_fp6(step_op<1>(ra[i]), step_op<1>(rb[j]), acc[i][j]);
+    } else {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1, nxt = cur ^ 1;
@@ -392,25 +486,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
           fb[nxt][j] = *reinterpret_cast<const u32x4*>(nb + b_off + j * 32 * KB + coff[0]);
         if constexpr (MODE == 0) HLQ_GEMM_ISSUE(st + NS, ob);
       }
-      if constexpr (INT4) {
-        v4i xa0[FM], xa1[FM], yb0[FN], yb1[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) widen_int4x2(fa[cur][i], xa0[i], xa1[i]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) widen_int4x2(fb[cur][j], yb0[j], yb1[j]);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa0[i], yb0[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa1[i], yb1[j], acc[i][j], 0, 0, 0);
-        // INT4: the compiler's own interleaving of reads, widening and MFMAs
-        // (explicit groups measured no better: fc2 pair 52.5 vs 51 us)
-      } else if constexpr (BF16) {
+      if constexpr (BF16) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -453,6 +529,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
         }
       }
     }
+    }
   };
   int64_t st = 0;
   for (; st + NS < S; ++st) stage(st, std::integral_constant<int, 0>());
@@ -461,7 +538,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 #undef HLQ_GEMM_ISSUE
 #undef HLQ_GEMM_WAIT
 
-  if constexpr (!BF16 && !CONV && EPI != EPI_PARTIAL) {
+  if constexpr (!BF16 && !FP6 && !CONV && EPI != EPI_PARTIAL) {
     if (g.nsplit > 1) {
       typedef int v4i __attribute__((ext_vector_type(4)));
       constexpr int NQ = FM * FN * 4;  // 16-byte groups of this thread's sums
@@ -479,7 +556,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
             const v4i v = {acc[i][j][4 * k], acc[i][j][4 * k + 1], acc[i][j][4 * k + 2],
                            acc[i][j][4 * k + 3]};
             __builtin_amdgcn_raw_buffer_store_b128(
-                v, rs, ((sp * NQ + (i * FN + j) * 4 + k) * 256 + tid) * 16, 0, SC1);
+                v, rs, ((sp * NQ + (i * FN + j) * 4 + k) * NT + tid) * 16, 0, SC1);
           }
       wait_vmcnt<0>();  // this thread's sums have reached device scope
       __shared__ unsigned arrived;
@@ -499,7 +576,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
-                  rs, ((o * NQ + (i * FN + j) * 4 + k) * 256 + tid) * 16, 0, SC1);
+                  rs, ((o * NQ + (i * FN + j) * 4 + k) * NT + tid) * 16, 0, SC1);
               acc[i][j][4 * k] += v[0];
               acc[i][j][4 * k + 1] += v[1];
               acc[i][j][4 * k + 2] += v[2];
@@ -543,13 +620,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
       const int64_t cb = tn * per, cw = (c8 - cb < per ? c8 - cb : per);
       const int64_t rows = M - m0 < BM ? M - m0 : BM;
       const int64_t items = cw > 0 ? rows * cw : 0;
-      for (int64_t base = tid; base < items; base += 256 * 8) {
+      for (int64_t base = tid; base < items; base += NT * 8) {
         uint4 raw[8];
         int64_t off[8];
         int rw[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int64_t it = base + u * 256;
+          const int64_t it = base + u * NT;
           rw[u] = -1;
           if (it < items) {
             const int64_t row = it / cw, c = cb + (it - row * cw);
@@ -570,7 +647,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
     }
   }
 
-  constexpr int SH = INT4 ? 8 : 0;
   int32_t* Cp = Ci + (EPI == EPI_PARTIAL ? split * M * N : 0);
   // Scales from LDS (written before the K loop; its barriers published them).
   float s_n[FN], s_m[FM][16];
@@ -602,7 +678,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
             if constexpr (EPI == EPI_BF16) g.Cb[m * N + n] = f32_to_bf16_rne(acc[i][j][r]);
             else C[m * N + n] = acc[i][j][r];
           } else {
-            const int32_t v = acc[i][j][r] >> SH;
+            const int32_t v = (int32_t)acc[i][j][r];  // exact (FP6: an integer-valued float)
             if constexpr (EPI == EPI_F32) __builtin_nontemporal_store((float)v * s_m[i][r] * s_n[j], &C[m * N + n]);
             else Cp[m * N + n] = v;
           }
@@ -624,7 +700,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
           if constexpr (EPI == EPI_BF16) g.Cb[m * N + n] = f32_to_bf16_rne(acc[i][j][r]);
           else C[m * N + n] = acc[i][j][r];
         } else {
-          const int32_t v = acc[i][j][r] >> SH;
+          const int32_t v = (int32_t)acc[i][j][r];
           if constexpr (EPI == EPI_F32) __builtin_nontemporal_store((float)v * s_m[i][r] * s_n[j], &C[m * N + n]);
           else Cp[m * N + n] = v;
         }
@@ -632,11 +708,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   }
 }
 
-template <bool INT4, int BM, int BN, int KB, int NS, int EPI>
+template <bool FP6, int BM, int BN, int KB, int NS, int EPI>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * GemmShape<INT4, BM, BN, KB, NS>::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * GemmShape<FP6, BM, BN, KB, NS>::STAGE];
   __shared__ float sc[BM + BN];
-  gemm_tile<INT4, BM, BN, KB, NS, EPI>(g, blockIdx.x, blockIdx.y, lds, sc);
+  gemm_tile<FP6, BM, BN, KB, NS, EPI>(g, blockIdx.x, blockIdx.y, lds, sc);
 }
 
 // Forward product y = x . w^T of a bf16 linear layer, with the ACBP codes of
@@ -669,17 +745,18 @@ __global__ __launch_bounds__(256, 2) void k_dgrad(GemmArgs g) {
 // With gw.nsplit > 1 the first n1 = nsplit * n1w workgroups are split s =
 // b / n1w of g_w workgroup b % n1w (n1w a multiple of 8, so every split of a
 // tile runs on the XCD the tile mapping gives it).
-template <int BM1, int BN1, int KB1, int NS1, int BM0, int BN0, int KB0, int NS0, int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm_pair(GemmArgs gw, int64_t n1, int64_t n1w,
-                                                      GemmArgs gx) {
-  constexpr int L1 = NS1 * GemmShape<false, BM1, BN1, KB1, NS1>::STAGE;
-  constexpr int L0 = NS0 * GemmShape<true, BM0, BN0, KB0, NS0>::STAGE;
+// WNW = 4: 512 threads (2 x 4 waves), one workgroup per CU.
+template <int WNW, int BM1, int BN1, int KB1, int NS1, int BM0, int BN0, int KB0, int NS0, int EPI>
+__global__ __launch_bounds__(128 * WNW, WNW == 2 ? 2 : 1) void k_gemm_pair(GemmArgs gw, int64_t n1,
+                                                                           int64_t n1w, GemmArgs gx) {
+  constexpr int L1 = NS1 * GemmShape<false, BM1, BN1, KB1, NS1, WNW>::STAGE;
+  constexpr int L0 = NS0 * GemmShape<true, BM0, BN0, KB0, NS0, WNW>::STAGE;
   constexpr int SC = BM1 + BN1 > BM0 + BN0 ? BM1 + BN1 : BM0 + BN0;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L1 > L0 ? L1 : L0];
   __shared__ float sc[SC];
   const int64_t b = blockIdx.x;
-  if (b < n1) gemm_tile<false, BM1, BN1, KB1, NS1, EPI>(gw, b % n1w, b / n1w, lds, sc);
-  else gemm_tile<true, BM0, BN0, KB0, NS0, EPI>(gx, b - n1, 0, lds, sc);
+  if (b < n1) gemm_tile<false, BM1, BN1, KB1, NS1, EPI, false, false, WNW>(gw, b % n1w, b / n1w, lds, sc);
+  else gemm_tile<true, BM0, BN0, KB0, NS0, EPI, false, false, WNW>(gx, b - n1, 0, lds, sc);
 }
 
 __global__ void k_zero_u32(unsigned* p, int64_t n) {
@@ -715,22 +792,25 @@ __global__ __launch_bounds__(256) void k_gemm_finalize(const int32_t* __restrict
 }
 
 // Tile configurations (rows of A x rows of B, stage depth, ring depth):
-//   0: 128 x 128, KB  64, 3 stages  (48 KB LDS, two workgroups per CU)
-//   1: 256 x 128, KB  64, 3 stages  (72 KB LDS, two workgroups per CU)
-//   2: 128 x 128, KB 128, 2 stages  (64 KB LDS, two workgroups per CU)
-// Large grids take the 256 x 128 tile; INT8 operands with K a multiple of 128
-// bytes take the deeper stage; grids below the CU count split K.
-GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes) {
+//   INT8: 0: 128 x 128, KB  64, 3 stages  (48 KB LDS, two workgroups per CU)
+//         1: 256 x 128, KB  64, 3 stages  (72 KB LDS, two workgroups per CU)
+//         2: 128 x 128, KB 128, 2 stages  (64 KB LDS, two workgroups per CU)
+//   FP6:  0: 128 x 128, KB  96, 3 stages  (72 KB LDS, two workgroups per CU)
+//         (a 256 x 128 FP6 tile needs more than the 256 VGPRs of two
+//         workgroups per CU)
+// Large INT8 grids take the 256 x 128 tile; INT8 operands with K a multiple
+// of 128 bytes take the deeper stage; grids below the CU count split K.
+GemmPlan plan_gemm(bool fp6, int64_t M, int64_t N, int64_t kbytes) {
   static const int cfg_bm[3] = {128, 256, 128}, cfg_bn[3] = {128, 128, 128};
   static const int cfg_kb[3] = {64, 64, 128};
   GemmPlan p;
   auto tiles = [&](int c) { return (int64_t)cdiv(M, cfg_bm[c]) * cdiv(N, cfg_bn[c]); };
-  if (tiles(1) >= 1024) p.cfg = 1;
-  else if (!int4 && kbytes % 128 == 0) p.cfg = 2;
+  if (!fp6 && tiles(1) >= 1024) p.cfg = 1;
+  else if (!fp6 && kbytes % 128 == 0) p.cfg = 2;
   else p.cfg = 0;
   p.bm = cfg_bm[p.cfg];
   p.bn = cfg_bn[p.cfg];
-  p.kb = cfg_kb[p.cfg];
+  p.kb = fp6 ? 96 : cfg_kb[p.cfg];
   p.stages = kbytes / p.kb;
   const int64_t t = tiles(p.cfg);
   int64_t sp = 1;
@@ -740,19 +820,23 @@ GemmPlan plan_gemm(bool int4, int64_t M, int64_t N, int64_t kbytes) {
   return p;
 }
 
-template <bool I4, int EPI>
+template <bool F6, int EPI>
 static void gemm_dispatch(int cfg, dim3 g, hipStream_t s, const GemmArgs& a) {
 #define HLQ_GEMM(BM_, BN_, KB_, NS_) \
-  hipLaunchKernelGGL((k_gemm<I4, BM_, BN_, KB_, NS_, EPI>), g, dim3(256), 0, s, a)
-  switch (cfg) {
-    case 1: HLQ_GEMM(256, 128, 64, 3); break;
-    case 2: HLQ_GEMM(128, 128, 128, 2); break;
-    default: HLQ_GEMM(128, 128, 64, 3); break;
+  hipLaunchKernelGGL((k_gemm<F6, BM_, BN_, KB_, NS_, EPI>), g, dim3(256), 0, s, a)
+  if constexpr (F6) {
+    HLQ_GEMM(128, 128, 96, 3);
+  } else {
+    switch (cfg) {
+      case 1: HLQ_GEMM(256, 128, 64, 3); break;
+      case 2: HLQ_GEMM(128, 128, 128, 2); break;
+      default: HLQ_GEMM(128, 128, 64, 3); break;
+    }
   }
 #undef HLQ_GEMM
 }
 
-hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
+hipError_t launch_gemm(bool fp6, const uint8_t* A, const uint8_t* B, int64_t M,
                        int64_t N, int64_t pitch, const GemmPlan& plan,
                        const float* sa, int sa_step, const float* sb, int sb_step,
                        float alpha, GemmEpi epi, float* C, int32_t* Ci,
@@ -770,7 +854,7 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
   const int e = use_partial ? EPI_PARTIAL : epi;
   GemmArgs a{A, B, M, N, pitch, plan.stages, sps, sa, sa_step, sb, sb_step, alpha, C,
              use_partial ? partial : Ci};
-  if (int4) {
+  if (fp6) {
     if (e == EPI_F32) gemm_dispatch<true, EPI_F32>(plan.cfg, grid, s, a);
     else if (e == EPI_I32) gemm_dispatch<true, EPI_I32>(plan.cfg, grid, s, a);
     else gemm_dispatch<true, EPI_PARTIAL>(plan.cfg, grid, s, a);
@@ -789,22 +873,49 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
 // the tiles, half the K work each.  Then K splits: the g_w tiles start first,
 // so a g_w tile longer than the launch's mean work per workgroup slot (two per
 // CU) sets its length; nsplit cuts it to about that mean (at most 4 splits of
-// at least 4 stages each).  Work is counted in MACs, an INT4 MAC (widened onto
-// the INT8 matrix cores) at 1.3 INT8 MACs.
-PairPlan plan_pair(int64_t T, int64_t I, int64_t O, const GemmPlan& px, const GemmPlan& pw) {
-  PairPlan pp;
-  pp.wcfg = pw.cfg; pp.wbm = pw.bm; pp.wbn = pw.bn;
-  if (pw.cfg == 2 && (int64_t)cdiv(O, 128) * cdiv(I, 128) < 64) { pp.wcfg = 3; pp.wbm = 64; }
-  pp.tx = (int64_t)cdiv(T, px.bm) * cdiv(I, px.bn);
-  pp.tw = (int64_t)cdiv(O, pp.wbm) * cdiv(I, pp.wbn);
-  const double dw = (double)pp.wbm * pp.wbn * pw.stages * pw.kb;
-  const double dx = 1.3 * px.bm * px.bn * px.stages * px.kb * 2;
-  const double mean = (pp.tw * dw + pp.tx * dx) / 512.0;
+// at least 4 stages each).  Work is counted in MACs, an FP6 MAC (twice the
+// INT8 rate on the matrix cores, more LDS bytes per MAC) at 0.7 INT8 MACs.
+static int pair_splits(double dw, double dx, int64_t tw, int64_t tx, int64_t slots,
+                       int64_t wstages) {
+  const double mean = (tw * dw + tx * dx) / (double)slots;
   int ns = (int)std::ceil(dw / mean - 0.25);
   ns = std::max(1, std::min(ns, 4));
-  while (ns > 1 && pw.stages / ns < 4) --ns;
-  pp.sps = (pw.stages + ns - 1) / ns;
-  pp.nsplit = (int)((pw.stages + pp.sps - 1) / pp.sps);  // every split non-empty
+  while (ns > 1 && wstages / ns < 4) --ns;
+  return ns;
+}
+
+PairPlan plan_pair(int64_t T, int64_t I, int64_t O, const GemmPlan& px, const GemmPlan& pw) {
+  PairPlan pp;
+  // 256 x 256 tiles (8 waves, one workgroup per CU) for long-K grids that
+  // 128-tiles would run in many rounds: each 128 x 128 tile re-reads its
+  // operand rows from L2 twice as often (Llama-3 down-proj pair 336 -> 264
+  // us).  Grids of one or two rounds keep 128-tiles (ViT-B qkv: 42.6 us
+  // against 59.6 for 256-tiles in one round, whose K-split g_w tiles run
+  // longest); so do short-K grids, bound by their fp32 output.
+  {
+    const int64_t sx = (int64_t)cdiv(T, 128) * cdiv(I, 128), sw = (int64_t)cdiv(O, 128) * cdiv(I, 128);
+    pp.big = px.kb == 96 && pw.kb % 64 == 0 && sx + sw >= 8 * 512 && px.stages >= 8;
+  }
+  int64_t wstages = pw.stages, xbm = px.bm, xbn = px.bn, slots = 512;
+  if (pp.big) {
+    // 256 x 256 tiles, 8 waves, one workgroup per CU: half the L2 -> LDS
+    // bytes per product of 128 x 128 tiles, the LDS rings 4 x 32 KB (INT8,
+    // KB 64) and 3 x 48 KB (FP6)
+    pp.wcfg = 4; pp.wbm = 256; pp.wbn = 256;
+    wstages = pw.stages * pw.kb / 64;
+    xbm = 256; xbn = 256; slots = 256;
+  } else {
+    pp.wcfg = pw.cfg; pp.wbm = pw.bm; pp.wbn = pw.bn;
+    if (pw.cfg == 2 && (int64_t)cdiv(O, 128) * cdiv(I, 128) < 64) { pp.wcfg = 3; pp.wbm = 64; }
+  }
+  pp.wstages = wstages;
+  pp.tx = (int64_t)cdiv(T, xbm) * cdiv(I, xbn);
+  pp.tw = (int64_t)cdiv(O, pp.wbm) * cdiv(I, pp.wbn);
+  const double dw = (double)pp.wbm * pp.wbn * pw.stages * pw.kb;
+  const double dx = 0.7 * xbm * xbn * px.stages * (px.kb * 4 / 3);
+  int ns = pair_splits(dw, dx, pp.tw, pp.tx, slots, wstages);
+  pp.sps = (wstages + ns - 1) / ns;
+  pp.nsplit = (int)((wstages + pp.sps - 1) / pp.sps);  // every split non-empty
   pp.part_bytes = pp.nsplit > 1 ? (size_t)pp.tw * pp.nsplit * pp.wbm * pp.wbn * 4 : 0;
   pp.nctr = pp.nsplit > 1 ? pp.tw : 0;
   return pp;
@@ -825,10 +936,11 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
   if (epi == EPI_I32 && (!acc_x || !acc_w)) return hipErrorInvalidValue;
   if (epi != EPI_F32 && epi != EPI_I32) return hipErrorInvalidValue;
   if (pp.nsplit < 1 || pp.nsplit > 4 || (pp.nsplit > 1 && (!part || !ctr))) return hipErrorInvalidValue;
-  if ((pp.nsplit - 1) * pp.sps >= pw.stages) return hipErrorInvalidValue;  // an empty split
+  if ((pp.nsplit - 1) * pp.sps >= pp.wstages) return hipErrorInvalidValue;  // an empty split
+  if (pp.wstages * (pp.big ? 64 : pw.kb) != kw_pitch) return hipErrorInvalidValue;
   const GemmArgs ax{gxA, gxB, T, I, kx_pitch, px.stages, px.stages, s_gy, gx_step, s_w, gx_step,
                     gx_alpha, g_x, acc_x};
-  GemmArgs aw{gwA, gwB, O, I, kw_pitch, pw.stages, pp.sps, s_gyl, gw_step, s_xl, gw_step,
+  GemmArgs aw{gwA, gwB, O, I, kw_pitch, pp.wstages, pp.sps, s_gyl, gw_step, s_xl, gw_step,
               gw_alpha, g_w, acc_w};
   aw.nsplit = pp.nsplit;
   aw.part = part;
@@ -844,21 +956,27 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
   const dim3 g((unsigned)(n1 + n0));
 #define HLQ_PAIR(W_, X_)                                                                 \
   do {                                                                                   \
-    if (epi == EPI_F32) hipLaunchKernelGGL((k_gemm_pair<W_, X_, EPI_F32>), g, dim3(256), 0, s, aw, n1, n1w, ax); \
-    else hipLaunchKernelGGL((k_gemm_pair<W_, X_, EPI_I32>), g, dim3(256), 0, s, aw, n1, n1w, ax); \
+    if (epi == EPI_F32) hipLaunchKernelGGL((k_gemm_pair<2, W_, X_, EPI_F32>), g, dim3(256), 0, s, aw, n1, n1w, ax); \
+    else hipLaunchKernelGGL((k_gemm_pair<2, W_, X_, EPI_I32>), g, dim3(256), 0, s, aw, n1, n1w, ax); \
   } while (0)
+  if (pp.big) {
+    if (epi == EPI_F32)
+      hipLaunchKernelGGL((k_gemm_pair<4, 256, 256, 64, 4, 256, 256, 96, 3, EPI_F32>), g, dim3(512), 0, s, aw, n1, n1w, ax);
+    else
+      hipLaunchKernelGGL((k_gemm_pair<4, 256, 256, 64, 4, 256, 256, 96, 3, EPI_I32>), g, dim3(512), 0, s, aw, n1, n1w, ax);
+    return hipGetLastError();
+  }
 #define HLQ_W0 128, 128, 64, 3
 #define HLQ_W1 256, 128, 64, 3
 #define HLQ_W2 128, 128, 128, 2
 #define HLQ_W3 64, 128, 128, 3
-#define HLQ_X0 128, 128, 64, 3
-#define HLQ_X1 256, 128, 64, 3
-  const bool x1 = px.cfg == 1;
+#define HLQ_X0 128, 128, 96, 3
+  if (px.cfg != 0 || px.kb != 96) return hipErrorInvalidValue;
   switch (pp.wcfg) {
-    case 1: if (x1) HLQ_PAIR(HLQ_W1, HLQ_X1); else HLQ_PAIR(HLQ_W1, HLQ_X0); break;
-    case 2: if (x1) HLQ_PAIR(HLQ_W2, HLQ_X1); else HLQ_PAIR(HLQ_W2, HLQ_X0); break;
-    case 3: if (x1) HLQ_PAIR(HLQ_W3, HLQ_X1); else HLQ_PAIR(HLQ_W3, HLQ_X0); break;
-    default: if (x1) HLQ_PAIR(HLQ_W0, HLQ_X1); else HLQ_PAIR(HLQ_W0, HLQ_X0); break;
+    case 1: HLQ_PAIR(HLQ_W1, HLQ_X0); break;
+    case 2: HLQ_PAIR(HLQ_W2, HLQ_X0); break;
+    case 3: HLQ_PAIR(HLQ_W3, HLQ_X0); break;
+    default: HLQ_PAIR(HLQ_W0, HLQ_X0); break;
   }
 #undef HLQ_PAIR
 #undef HLQ_W0
@@ -866,16 +984,15 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
 #undef HLQ_W2
 #undef HLQ_W3
 #undef HLQ_X0
-#undef HLQ_X1
   return hipGetLastError();
 }
 
 hipError_t launch_dgrad(const ConvGemm& c, hipStream_t s) {
-  if (c.kx_pitch % 64 || c.taps <= 0 || c.C % 8) return hipErrorInvalidValue;
+  if (c.kx_pitch % 96 || c.taps <= 0 || c.C % 8) return hipErrorInvalidValue;
   if ((c.epi == EPI_F32 && (!c.g_x || !c.s_gy || !c.s_w)) || (c.epi == EPI_I32 && !c.acc_x))
     return hipErrorInvalidValue;
   const int64_t M = c.N * c.H * c.W;
-  const int64_t so = c.kx_pitch / 64;  // 64-byte stages per tap
+  const int64_t so = c.kx_pitch / 96;  // 96-byte (128-value) stages per tap
   GemmArgs a{c.q_gy, c.q_w, M, c.C, c.kx_pitch, so * c.taps, so * c.taps, c.s_gy, 0, c.s_w, 0,
              c.alpha, c.g_x, c.acc_x};
   a.cH = (int32_t)c.H; a.cW = (int32_t)c.W; a.cP = (int32_t)c.P; a.cQ = (int32_t)c.Q;
@@ -884,8 +1001,8 @@ hipError_t launch_dgrad(const ConvGemm& c, hipStream_t s) {
   a.zero = c.zero;
   const int64_t tiles = (int64_t)cdiv(M, 128) * cdiv(c.C, 128);
   const dim3 g((unsigned)((tiles + 7) / 8 * 8));
-  if (c.epi == EPI_F32) hipLaunchKernelGGL((k_dgrad<128, 128, 64, 3, EPI_F32>), g, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_dgrad<128, 128, 64, 3, EPI_I32>), g, dim3(256), 0, s, a);
+  if (c.epi == EPI_F32) hipLaunchKernelGGL((k_dgrad<128, 128, 96, 3, EPI_F32>), g, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_dgrad<128, 128, 96, 3, EPI_I32>), g, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -127,7 +127,9 @@ hipError_t launch_gemm(bool int4, const uint8_t* A, const uint8_t* B, int64_t M,
 // sums to `part` (device-coherent), counts itself into its tile's counter, and
 // the last to arrive adds the others' sums and runs the epilogue.
 struct PairPlan {
+  bool big;             // 256 x 256 tiles, 512-thread workgroups (one per CU)
   int wcfg, wbm, wbn;   // g_w tile configuration (rows of O x rows of I)
+  int64_t wstages;      // K stages of a g_w tile (its KB may differ from the plan's)
   int64_t tw, tx;       // g_w and g_x tiles
   int nsplit;           // K splits of each g_w tile (1: none)
   int64_t sps;          // K stages per split (the last takes the remainder)

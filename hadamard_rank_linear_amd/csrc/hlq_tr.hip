@@ -337,7 +337,8 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
   }
 }
 
-// Column pass with the full H_N along the rows (w -> INT4 codes for g_x).
+// Column pass with the full H_N along the rows (w -> INT4 codes for g_x, stored
+// as FP6 E2M3 groups of 128 K values).
 template <int PASS, int N, class RD>
 __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint8_t* smem,
                                              float* red, int rows, int cols, int64_t c0,
@@ -345,7 +346,8 @@ __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint
                                              uint8_t* q, int64_t pitch, int64_t o0, int64_t O,
                                              bool last) {
   constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;
-  constexpr int WPT = N / 8;  // code words (8 nibbles) per task
+  constexpr int NB = TT / N;  // blocks of the tile's group
+  static_assert(TT == 128, "one tile of rows is one 128-value FP6 group");
   const int tid = threadIdx.x;
   const int c = tid % CW;
   const int nb = rows / N;
@@ -354,48 +356,89 @@ __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint
     const float tinv = colinv ? 0.f : inv_of(__uint_as_float(a.tmax[list]), list == 1 ? 7.f : 127.f);
     inv_c = colinv ? (c < cols ? colinv[c0 + c] : 0.f) : tinv;
   }
-  float cm = 0.f;
-  uint32_t words[TPT][WPT];
-#pragma unroll
-  for (int t = 0; t < TPT; ++t) {
-#pragma unroll
-    for (int w = 0; w < WPT; ++w) words[t][w] = 0;
-    const int b = tid / CW + 2 * t;
-    if (b < nb && c < cols) {
-      float v[N];
-      full_col<N>(rd, b * N, c, v);
-      if constexpr (PASS == PASS_MAX) {
-#pragma unroll
-        for (int k = 0; k < N; ++k) cm = fmaxf(cm, fabsf(v[k]));
-      } else {
-#pragma unroll
-        for (int k = 0; k < N; ++k)
-          words[t][k / 8] |= (quant_bits<7>(v[k], inv_c) & 0xFu) << (4 * (k % 8));
-      }
-    }
-  }
   if constexpr (PASS == PASS_MAX) {
-    tile_colmax_store(cm, red, tid, cols, part);
-  } else {
-    uint8_t (*outs)[OUT_PITCH] = reinterpret_cast<uint8_t (*)[OUT_PITCH]>(smem);
-    __syncthreads();
+    float cm = 0.f;
 #pragma unroll
     for (int t = 0; t < TPT; ++t) {
       const int b = tid / CW + 2 * t;
       if (b < nb && c < cols) {
+        float v[N];
+        full_col<N>(rd, b * N, c, v);
 #pragma unroll
-        for (int w = 0; w < WPT; ++w)
-          *reinterpret_cast<uint32_t*>(&outs[c][b * (N / 2) + 4 * w]) = words[t][w];
+        for (int k = 0; k < N; ++k) cm = fmaxf(cm, fabsf(v[k]));
+      }
+    }
+    tile_colmax_store(cm, red, tid, cols, part);
+  } else {
+    // FP6 codes of the thread's blocks (zero codes for blocks past O or
+    // columns past I), 32 values per conversion: a block of 16 is paired
+    // with the thread's next (16 rows on, the same half of the next quarter)
+    uint8_t (*outs)[OUT_PITCH] = reinterpret_cast<uint8_t (*)[OUT_PITCH]>(smem);
+    float r[TPT][N];
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const int b = tid / CW + 2 * t;
+#pragma unroll
+      for (int k = 0; k < N; ++k) r[t][k] = 0.f;
+      if (b < nb && c < cols) {
+        float v[N];
+        full_col<N>(rd, b * N, c, v);
+#pragma unroll
+        for (int k = 0; k < N; ++k) r[t][k] = quant_code_f32(v[k], inv_c);
+      }
+    }
+    __syncthreads();  // the column reads of the tile are done: smem is staging now
+    if constexpr (N == 16) {
+#pragma unroll
+      for (int t = 0; t < TPT; t += 2) {
+        const int b = tid / CW + 2 * t;  // blocks b and b + 2: quarters b/2 and b/2 + 1
+        float f[32];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          f[k] = r[t][k];
+          f[16 + k] = r[t + 1][k];
+        }
+        uint32_t d[6];
+        fp6_pack32(f, d);
+        const int e = b & 1, qa = b >> 1;
+        uint8_t* pa = &outs[c][fp6_quarter_pos(qa) * 24 + 12 * e];
+        uint8_t* pb = &outs[c][fp6_quarter_pos(qa + 1) * 24 + 12 * e];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          reinterpret_cast<uint32_t*>(pa)[k] = d[k];
+          reinterpret_cast<uint32_t*>(pb)[k] = d[3 + k];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < TPT; ++t) {
+        const int b = tid / CW + 2 * t;
+        if (b < NB) {
+#pragma unroll
+          for (int p = 0; p < N / 32; ++p) {
+            float f[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k) f[k] = r[t][32 * p + k];
+            uint32_t d[6];
+            fp6_pack32(f, d);
+            uint32_t* dst = reinterpret_cast<uint32_t*>(
+                &outs[c][fp6_quarter_pos(b * (N / 32) + p) * 24]);
+#pragma unroll
+            for (int k = 0; k < 6; ++k) dst[k] = d[k];
+          }
+        }
       }
     }
     __syncthreads();
-    const int64_t koff = o0 / 2;
-    if (rows == TT && cols == CW)
-      store_staged_full<TT / 2>(outs, q + c0 * pitch + koff, pitch, tid);
+    // the whole 96-byte group of each column, K padding (zero codes) included
+    const int64_t koff = (o0 / TT) * 96;
+    if (cols == CW)
+      store_staged_full<96>(outs, q + c0 * pitch + koff, pitch, tid);
     else
-      store_staged(outs, cols, rows / 2, q + c0 * pitch + koff, pitch, koff, tid);
-    if (last) zero_tail(q + c0 * pitch, pitch, cols, O / 2, pitch, tid);
+      store_staged(outs, cols, 96, q + c0 * pitch + koff, pitch, koff, tid);
   }
+  (void)last;
+  (void)O;
 }
 
 // Cross-lane butterfly stages h = 8, 16, .. N/2 of the row transform (lane
@@ -442,6 +485,43 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) {
   }
 }
 
+// FP6 codes of H.g_y: lane lc (0..15) of a row's 16 lanes holds the 48-bit
+// fields (lo: bits 0-31, hi: bits 32-47) of the codes of columns 8 lc ..
+// 8 lc + 7 of one 128-value group, i.e. bits 48 (lc & 3) .. of quarter lc >> 2.
+// The four lanes of a quarter swap a half word with lane ^ 1, then write whole
+// dwords of its 24-byte stream: lane 0 bytes 0-7, 1 bytes 8-11, 2 bytes 12-15,
+// 3 bytes 16-23.  Every lane of the quad calls it (the swap reads lane ^ 1);
+// `store` masks the write.
+__device__ __forceinline__ void store_fp6_lane8(uint8_t* group, int lc, uint32_t lo, uint32_t hi,
+                                                bool store) {
+  const int k4 = lc & 3;
+  const uint32_t send = k4 == 1 ? (lo & 0xFFFFu) : hi;
+  const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);
+  if (!store) return;
+  uint8_t* q = group + fp6_quarter_pos(lc >> 2) * 24;
+  if (k4 == 0) *reinterpret_cast<uint2*>(q) = make_uint2(lo, hi | (recv << 16));
+  else if (k4 == 1) *reinterpret_cast<uint32_t*>(q + 8) = (lo >> 16) | (hi << 16);
+  else if (k4 == 2) *reinterpret_cast<uint32_t*>(q + 12) = lo;
+  else *reinterpret_cast<uint2*>(q + 16) = make_uint2(recv | (lo << 16), (lo >> 16) | (hi << 16));
+}
+
+// FP6 codes of four rows' 8-value lane slices (rc[k][0..7], integer-valued
+// floats) in one conversion; row k's 48-bit field is bits 48 k .. 48 k + 47.
+__device__ __forceinline__ void fp6_rows4(const float (&rc)[4][8], uint32_t (&lo)[4],
+                                          uint32_t (&hi)[4]) {
+  float f[32];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[8 * k + e] = rc[k][e];
+  uint32_t d[6];
+  fp6_pack32(f, d);
+  lo[0] = d[0];                                 hi[0] = d[1] & 0xFFFFu;
+  lo[1] = __builtin_amdgcn_alignbit(d[2], d[1], 16); hi[1] = d[2] >> 16;
+  lo[2] = d[3];                                 hi[2] = d[4] & 0xFFFFu;
+  lo[3] = __builtin_amdgcn_alignbit(d[5], d[4], 16); hi[3] = d[5] >> 16;
+}
+
 template <int PASS, int N>
 __device__ __forceinline__ void gy_rows_bf16_full(const TrArgs& a, int64_t t0, int64_t c0,
                                                   int64_t ch, uint8_t* smem, float inv_tensor) {
@@ -460,9 +540,11 @@ __device__ __forceinline__ void gy_rows_bf16_full(const TrArgs& a, int64_t t0, i
 #pragma unroll
     for (int sw = 0; sw < SW; ++sw) inv[sw] = a.gx_tok ? ib[sw * 16 + lr] : inv_tensor;
   }
+  static_assert(SW % 4 == 0 && CW == 128, "four rows per FP6 conversion, one group per tile");
   const uint32_t K32 = (uint32_t)a.kxb;
-  uint8_t* qbase = a.q_gy + t0 * a.kxb + c0 / 2;
-  const uint32_t qoff = (uint32_t)lr * K32 + (uint32_t)(col / 2);
+  // the tile's 128 columns are one FP6 group of each row (96 bytes)
+  uint8_t* qbase = a.q_gy + t0 * a.kxb + (c0 / CW) * 96;
+  float rc[4][8];
 #pragma unroll
   for (int sw = 0; sw < SW; ++sw) {
     const int row = sw * 16 + lr;
@@ -481,8 +563,15 @@ __device__ __forceinline__ void gy_rows_bf16_full(const TrArgs& a, int64_t t0, i
       m = fmaxf(m, lane_xor<8>(m));
       if (lc == 0) a.part_gy[ch * a.T + t0 + row] = m;
     } else {
-      *reinterpret_cast<uint32_t*>(qbase + qoff + (uint32_t)sw * 16u * K32) =
-          quant_pack8_int4(v, inv[sw]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rc[sw & 3][k] = quant_code_f32(v[k], inv[sw]);
+      if ((sw & 3) == 3) {
+        uint32_t lo[4], hi[4];
+        fp6_rows4(rc, lo, hi);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          store_fp6_lane8(qbase + (uint32_t)((sw - 3 + k) * 16 + lr) * K32, lc, lo[k], hi[k], true);
+      }
     }
   }
 }
@@ -516,6 +605,8 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
     raw[sw].b = make_uint4(0, 0, 0, 0);
     if (row < rows && col < cols) load_raw8(a.gy, a.gy_dt, (t0 + row) * a.O + c0 + col, raw[sw]);
   }
+  float rc[4][8];
+  uint8_t* qbase = a.q_gy + t0 * a.kxb + (c0 / CW) * 96;
 #pragma unroll
   for (int sw = 0; sw < SW; ++sw) {
     const int row = sw * 16 + lr;
@@ -530,11 +621,21 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
       for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
       m = max_over_16_lanes(m);
       if (lc == 0 && row < rows) a.part_gy[ch * a.T + t0 + row] = m;
-    } else if (row < rows) {
-      const float inv = a.gx_tok ? a.inv_gy[t0 + row] : inv_tensor;
-      // columns past O inside the chunk are zero -> zero codes (K padding)
-      *reinterpret_cast<uint32_t*>(a.q_gy + (t0 + row) * a.kxb + (c0 + col) / 2) =
-          col < cols ? quant_pack8_int4(v, inv) : 0u;
+    } else {
+      // rows past T quantize nothing; columns past O inside the group are
+      // zero codes (K padding)
+      const float inv = row < rows ? (a.gx_tok ? a.inv_gy[t0 + row] : inv_tensor) : 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rc[sw & 3][k] = col < cols ? quant_code_f32(v[k], inv) : 0.f;
+      if ((sw & 3) == 3) {
+        uint32_t lo[4], hi[4];
+        fp6_rows4(rc, lo, hi);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int rk = (sw - 3 + k) * 16 + lr;
+          store_fp6_lane8(qbase + (int64_t)rk * a.kxb, lc, lo[k], hi[k], rk < rows);
+        }
+      }
     }
   }
   }

@@ -122,8 +122,11 @@ size_t hlq_linear_backward_workspace_size(int64_t T, int64_t I, int64_t O,
  *   workspace device buffer of at least hlq_linear_backward_workspace_size()
  *            bytes; holds the quantized operands and scales afterwards (layout
  *            from hlq_workspace_layout).
- * Also requires I % 8 == 0 and that no INT32 accumulator can overflow:
- * O <= 171196 and T*rank/block <= 133143.
+ * Also requires I % 8 == 0 (stricter than the even I that nibble packing
+ * alone needs: every kernel moves a row's codes in whole 32-bit words of 8
+ * codes, so rows never split a word; HLQ_ERR_SHAPE otherwise) and that no
+ * accumulator can lose exactness: O <= 342391 (49 * O < 2^24, the fp32 sums of
+ * the FP6 g_x product) and T*rank/block <= 133143 (127^2 * T' < 2^31, INT32).
  */
 hlq_status hlq_linear_backward(const void* g_y, int gy_dtype,
                                const uint8_t* x_codes, const float* x_scales,
@@ -198,11 +201,15 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
 /*
  * Where hlq_linear_backward leaves its intermediates inside the workspace
  * (byte offsets), for tests and diagnostics.
- *   q_gy   [T][kx_pitch]  INT4 codes of H.g_y (along O), packed as in ACBP;
- *          bytes past O/2 in each row are zero.
+ *   q_gy   [T][kx_pitch]  INT4 codes of H.g_y (along O), stored as FP6 E2M3
+ *          fields (exact for -7..7: sign bit 5, exponent bits 4-3 with bias
+ *          1, mantissa bits 2-0) in groups of 128 codes (96 bytes): quarter Q
+ *          of a group (codes 32Q .. 32Q+31) is a 24-byte stream, code j at
+ *          bits 6j .. 6j+5, and the quarters are stored in the order 0, 2, 1,
+ *          3.  Codes past O are zero fields (kx_pitch = 96 * ceil(O / 128)).
  *   s_gy   [T] (PER_TOKEN) or [1] f32.
  *   q_w    [I][kx_pitch]  INT4 codes of H.w, stored transposed (K = O
- *          contiguous), packed as above, zero-padded.
+ *          contiguous), in the same FP6 groups.
  *   s_w    [I] or [1] f32.
  *   q_gyl  [O][kw_pitch]  INT8 codes of the low-rank g_y, transposed (K = T'
  *          contiguous), zero past T' = T*rank/block.
@@ -210,6 +217,8 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
  *   q_xl   [I][kw_pitch]  INT8 codes of the low-rank x, transposed.
  *   s_xl   [I] or [1] f32.
  *   partial  scratch of the split-K GEMMs (contents unspecified).
+ * The workspace also holds, after these, the INT32 partial sums and arrival
+ * counters of the K-split g_w tiles of the pair launch (contents unspecified).
  */
 typedef struct hlq_workspace_layout {
   size_t q_gy, s_gy, q_w, s_w, q_gyl, s_gyl, q_xl, s_xl;
@@ -272,7 +281,7 @@ hlq_status hlq_gemm_gw_acc(const void* workspace, size_t workspace_bytes, int64_
  *   g_w      [O][R][S][C] f32 out, as hlq_linear_backward's g_w.
  * Requires C % 8 == 0, N*P*Q and O multiples of block, gx_mode ==
  * HLQ_PER_TENSOR (HLQ_ERR_MODE otherwise: per-token scales of H.g_y and H.w
- * do not factor out of the sum over the taps), O*R*S <= 171196 and
+ * do not factor out of the sum over the taps), O*R*S <= 342391 and
  * T' = N*P*Q*rank/block <= 133143 (HLQ_ERR_OVERFLOW), pixel and position
  * counts below 2^31.  workspace: hlq_conv_backward_workspace_size bytes.
  * Launches: the transform MAX, reduce and QUANT passes, the INT8 g_w GEMM

@@ -39,6 +39,49 @@ def to_device(arr, dtype):
     return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def _fp6_e2m3_table() -> np.ndarray:
+    """Value of each 6-bit FP6 E2M3 field (bit 5 sign, bits 4-3 exponent with
+    bias 1, bits 2-0 mantissa; exponent 0 is subnormal, mantissa / 8)."""
+    t = np.empty(64, np.float64)
+    for f in range(64):
+        s, e, m = f >> 5, (f >> 3) & 3, f & 7
+        mag = m / 8.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 8.0)
+        t[f] = -mag if s else mag
+    return t
+
+
+FP6_E2M3 = _fp6_e2m3_table()
+
+
+def decode_fp6_groups(b: np.ndarray) -> np.ndarray:
+    """uint8 [.., 96 * G] -> int8 [.., 128 * G]: INT4 codes stored as FP6 E2M3
+    in groups of 128 (96 bytes).  Quarter Q of a group (codes 32Q .. 32Q+31)
+    is a 24-byte little-endian stream, code j at bits 6j .. 6j+5; the
+    quarters are stored in the order 0, 2, 1, 3.  Every field must be an
+    integer in [-7, 7] and never a negative zero."""
+    assert b.shape[-1] % 96 == 0
+    lead = b.shape[:-1]
+    g = b.reshape(lead + (b.shape[-1] // 96, 4, 24))
+    out = np.empty(lead + (b.shape[-1] // 96, 4, 32), np.int8)
+    for pos, q in enumerate((0, 2, 1, 3)):
+        chunk = g[..., pos, :].astype(np.uint64)
+        # 24 bytes = three little-endian 64-bit words
+        words = [sum(chunk[..., 8 * w + k] << np.uint64(8 * k) for k in range(8)) for w in range(3)]
+        for j in range(32):
+            bit = 6 * j
+            w, o = bit // 64, bit % 64
+            f = (words[w] >> np.uint64(o)) & np.uint64(63)
+            if o > 58:
+                f |= (words[w + 1] << np.uint64(64 - o)) & np.uint64(63)
+            f = f.astype(np.int64)
+            assert not (f == 32).any(), "negative-zero FP6 field"
+            v = FP6_E2M3[f]
+            assert np.array_equal(v, np.round(v)) and np.abs(v).max(initial=0) <= 7, \
+                "FP6 field is not an INT4 code"
+            out[..., q, j] = v.astype(np.int8)
+    return out.reshape(lead + (b.shape[-1] // 96 * 128,))
+
+
 def unpack_nibbles(b: np.ndarray) -> np.ndarray:
     """uint8 [.., K/2] -> int8 [.., K]: element 2k = low nibble, 2k+1 = high."""
     b = b.astype(np.int16)
@@ -139,11 +182,11 @@ def compare(cfg, gpu: GpuRun, ocodes, oscales, ref: dict, check_acc=True):
     assert np.array_equal(gpu.codes, ocodes), "ACBP codes differ"
     assert np.array_equal(bits(gpu.scales), bits(oscales)), "ACBP scales differ"
     # g_x operands
-    q_gy = unpack_nibbles(it["q_gy_packed"])
+    q_gy = decode_fp6_groups(it["q_gy_packed"])
     assert np.array_equal(q_gy[:, :O], ref["q_gy"]), "INT4 codes of H.g_y differ"
     assert not q_gy[:, O:].any(), "K padding of q_gy is not zero"
     assert np.array_equal(bits(it["s_gy"]), bits(ref["s_gy"])), "scales of H.g_y differ"
-    q_w = unpack_nibbles(it["q_w_packed"])
+    q_w = decode_fp6_groups(it["q_w_packed"])
     assert np.array_equal(q_w[:, :O].T, ref["q_w"]), "INT4 codes of H.w differ"
     assert not q_w[:, O:].any(), "K padding of q_w is not zero"
     assert np.array_equal(bits(it["s_w"]), bits(ref["s_w"])), "scales of H.w differ"

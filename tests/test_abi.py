@@ -7,6 +7,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import hadamard_rank_linear_amd as h
@@ -66,7 +68,7 @@ def _raw_backward(**kw):
     (dict(red=7), 5),
     (dict(gy_dt=3), 6),
     (dict(w=(1 << 20) + 4), 7),      # misaligned
-    (dict(O=171200, block=16), 8),   # INT4 accumulator could overflow
+    (dict(O=342400, block=16), 8),   # 49 * O >= 2^24: FP6 sums not exact
     (dict(T=16 * 133144, rank=16), 8),
     (dict(ws=None), 9),
     (dict(ws_bytes=100), 9),
@@ -93,7 +95,8 @@ def test_workspace_layout_consistent(cfg):
     size = h.hlq_linear_backward_workspace_size(T, I, O, n, r)
     assert lay["total"] == size > 0
     assert lay["t_low"] == T * r // n
-    assert lay["kx_pitch"] % 64 == 0 and lay["kx_pitch"] * 2 >= O
+    # FP6 groups: 128 codes in 96 bytes
+    assert lay["kx_pitch"] % 96 == 0 and lay["kx_pitch"] // 96 * 128 >= O > lay["kx_pitch"] // 96 * 128 - 128
     assert lay["kw_pitch"] % 64 == 0 and lay["kw_pitch"] >= lay["t_low"]
     regions = sorted([
         (lay["q_gy"], T * lay["kx_pitch"]), (lay["s_gy"], 4 * T),
@@ -216,7 +219,7 @@ def test_binding_checks_caller_buffers():
     (dict(stride=0), 2), (dict(R=40), 2), (dict(block=24), 3), (dict(rank=3), 4),
     (dict(gx=0), 5),                                         # per-token g_x: not supported
     (dict(red=3), 5), (dict(gy_dt=4), 6), (dict(w=(1 << 20) + 8), 7),
-    (dict(O=16, R=120, S=120, H=135, W=135, pad=0), 8),      # O*R*S beyond the INT32 bound
+    (dict(O=16, R=150, S=150, H=165, W=165, pad=0), 8),      # 49*O*R*S >= 2^24 (FP6 sums)
     (dict(ws_bytes=64), 9),
 ])
 def test_conv_backward_validates_before_launch(kw, status):
@@ -251,3 +254,52 @@ def test_forward_validates_before_launch(kw, status):
     lib = h.lib_handle()
     assert lib.hlq_linear_forward(*(args[k] for k in (
         "x", "w", "T", "I", "O", "y", "ydt", "codes", "scales", "stream"))) == status
+
+
+# ------------------------------------------------ FP6 storage of the g_x codes
+
+def test_fp6_field_values_follow_e2m3():
+    # E2M3: sign bit 5, exponent bits 4-3 (bias 1), mantissa bits 2-0
+    from parity_util import FP6_E2M3
+    fields = {0: 0b000000, 1: 0b001000, 2: 0b010000, 3: 0b010100, 4: 0b011000,
+              5: 0b011010, 6: 0b011100, 7: 0b011110}
+    for q, f in fields.items():
+        assert FP6_E2M3[f] == q
+        assert FP6_E2M3[f | 0b100000] == -q
+    assert FP6_E2M3[0b000001] == 0.125 and FP6_E2M3[0b011111] == 7.5
+
+
+def _encode_fp6_groups(codes):
+    # plain bit-stream writer: quarter Q of each group of 128 at byte
+    # 24 * pos(Q), pos = (0, 2, 1, 3)[Q], code j of a quarter at bits 6j
+    enc = {q: (0b100000 if q < 0 else 0) | {0: 0, 1: 8, 2: 16, 3: 20, 4: 24, 5: 26, 6: 28, 7: 30}[abs(q)]
+           for q in range(-7, 8)}
+    rows, k = codes.shape
+    out = np.zeros((rows, k // 128 * 96), np.uint8)
+    for r in range(rows):
+        for g in range(k // 128):
+            for q in range(4):
+                pos = (0, 2, 1, 3)[q]
+                acc = 0
+                for j in range(32):
+                    acc |= enc[int(codes[r, 128 * g + 32 * q + j])] << (6 * j)
+                out[r, 96 * g + 24 * pos: 96 * g + 24 * pos + 24] = np.frombuffer(
+                    acc.to_bytes(24, "little"), np.uint8)
+    return out
+
+
+def test_fp6_group_decoder_round_trip_and_hand_bytes():
+    from parity_util import decode_fp6_groups
+    rng = np.random.default_rng(5)
+    codes = rng.integers(-7, 8, size=(3, 256)).astype(np.int8)
+    assert np.array_equal(decode_fp6_groups(_encode_fp6_groups(codes)), codes)
+    # hand bytes: code 1 at K 0 -> field 8 in byte 0; code -7 at K 32
+    # (quarter 1, stored second-to-... third: position 2) -> field 62 at byte 48;
+    # code 3 at K 64 + 1 (quarter 2, position 1, bits 6-11) -> byte 24 bits 6-7
+    # hold 20 & 3 = 0, byte 25 bits 0-3 hold 20 >> 2 = 5
+    c = np.zeros((1, 128), np.int8)
+    c[0, 0], c[0, 32], c[0, 65] = 1, -7, 3
+    b = _encode_fp6_groups(c)
+    assert b[0, 0] == 8 and b[0, 48] == 62 and b[0, 24] == 0 and b[0, 25] == 5
+    assert int(b.sum()) == 8 + 62 + 5
+    assert np.array_equal(decode_fp6_groups(b), c)

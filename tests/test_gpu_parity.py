@@ -113,6 +113,16 @@ def test_split_k_shapes(T, I, O, n, r, dt, gx_mode, gw_mode):
     _case(cfg)
 
 
+# Long-K grids that 128 x 128 tiles would run in many rounds take 256 x 256
+# tiles (512-thread workgroups); this one is ragged along every dimension
+# (T, I past the last tile, O past the last 128-value FP6 group).
+def test_large_tile_pair_ragged():
+    base = wl.BY_NAME["vitb_qkv"]
+    cfg = dataclasses.replace(base, T=1040, I=13000, O=4112, block=16, rank=8, dtype=wl.BF16,
+                              gx_mode=0, gw_mode=0, index=311)
+    _case(cfg)
+
+
 # ----------------------------------------------- layer configs, reduced tokens
 
 REDUCED_T = {"vitb_qkv": 1040, "vitb_fc2": 1056, "llama3_8b_down": 1024,
