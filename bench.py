@@ -569,6 +569,10 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements (fc2 layer, LQS statistics)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run 256 MiB device copies (scale of the HBM byte counters)")
+    ap.add_argument("--side", choices=("conv", "forward"),
+                    help="run only this side measurement (the ResNet-50 stage-3 convolution "
+                         "backward, or the forward with fused ACBP on --workload) and print "
+                         "its JSON; for profiling")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -582,6 +586,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.side == "conv":
+        c = wl.CONV_BY_NAME["resnet50_s3_conv3x3"]
+        print(json.dumps({"side": "conv", "workload": c.name,
+                          "result": time_conv(c, args.steps, args.warmup)}), flush=True)
+        return
+    if args.side == "forward":
+        c = wl.BY_NAME[args.workload]
+        print(json.dumps({"side": "forward", "workload": c.name,
+                          "result": time_forward(c, wl.make_inputs(c), args.steps, args.warmup)}),
+              flush=True)
+        return
 
     cfg = wl.BY_NAME[args.workload]
     log(f"generating {cfg.name} inputs")
