@@ -488,21 +488,18 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) {
 // FP6 codes of H.g_y: lane lc (0..15) of a row's 16 lanes holds the 48-bit
 // fields (lo: bits 0-31, hi: bits 32-47) of the codes of columns 8 lc ..
 // 8 lc + 7 of one 128-value group, i.e. bits 48 (lc & 3) .. of quarter lc >> 2.
-// The four lanes of a quarter swap a half word with lane ^ 1, then write whole
-// dwords of its 24-byte stream: lane 0 bytes 0-7, 1 bytes 8-11, 2 bytes 12-15,
-// 3 bytes 16-23.  Every lane of the quad calls it (the swap reads lane ^ 1);
-// `store` masks the write.
+// An even lane takes its odd neighbour's field (DPP quad permute) and writes
+// the pair's 96 bits, bytes 12 (lc & 3) / 2 .. + 11 of the quarter's 24-byte
+// stream, with one 12-byte store.  Every lane of the quad calls it (the
+// exchange reads lane ^ 1); `store` masks the write.
 __device__ __forceinline__ void store_fp6_lane8(uint8_t* group, int lc, uint32_t lo, uint32_t hi,
                                                 bool store) {
-  const int k4 = lc & 3;
-  const uint32_t send = k4 == 1 ? (lo & 0xFFFFu) : hi;
-  const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);
-  if (!store) return;
-  uint8_t* q = group + fp6_quarter_pos(lc >> 2) * 24;
-  if (k4 == 0) *reinterpret_cast<uint2*>(q) = make_uint2(lo, hi | (recv << 16));
-  else if (k4 == 1) *reinterpret_cast<uint32_t*>(q + 8) = (lo >> 16) | (hi << 16);
-  else if (k4 == 2) *reinterpret_cast<uint32_t*>(q + 12) = lo;
-  else *reinterpret_cast<uint2*>(q + 16) = make_uint2(recv | (lo << 16), (lo >> 16) | (hi << 16));
+  const uint32_t nlo = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, 0xB1, 0xF, 0xF, true);
+  const uint32_t nhi = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, 0xB1, 0xF, 0xF, true);
+  if (!store || (lc & 1)) return;
+  uint32_t* q = reinterpret_cast<uint32_t*>(group + fp6_quarter_pos(lc >> 2) * 24 + 6 * (lc & 2));
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  *reinterpret_cast<u32x3*>(q) = u32x3{lo, hi | (nlo << 16), (nlo >> 16) | (nhi << 16)};
 }
 
 // FP6 codes of four rows' 8-value lane slices (rc[k][0..7], integer-valued
