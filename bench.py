@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
+FP6_PEAK_TOPS = 10100.0        # MI355X dense FP6 / FP4 MFMA (the g_x product's unit)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20
 METRIC = "per-layer BP latency (us) + effective TOPS & % roofline, ViT-B qkv/fc2 shape"
@@ -105,8 +106,19 @@ def copy_calibration(nbytes=256 << 20, reps=5):
     log(f"copy calibration: {reps} copies of {nbytes} bytes")
 
 
-def ideal_us(ops, nbytes):
-    t_mfma = ops / (INT8_PEAK_TOPS * 1e12) * 1e6
+def mfma_peak_tops(cfg, kname):
+    """Matrix-core peak of a launch step: the g_x product runs on the FP6
+    matrix cores (its INT4 codes stored as FP6, 10.1 POP/s), the g_w product
+    on the INT8 ones (5.0 POP/s); the pair's peak is their time-weighted mean
+    (total ops over the sum of each product's ideal time)."""
+    if kname != "gemm":
+        return INT8_PEAK_TOPS
+    ox, ow = 2 * cfg.T * cfg.I * cfg.O, 2 * cfg.O * cfg.I * cfg.Tl
+    return (ox + ow) / (ox / FP6_PEAK_TOPS + ow / INT8_PEAK_TOPS)
+
+
+def ideal_us(ops, nbytes, peak_tops=INT8_PEAK_TOPS):
+    t_mfma = ops / (peak_tops * 1e12) * 1e6
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
     return max(t_mfma, t_hbm), ("mfma" if t_mfma > t_hbm else "hbm")
 
@@ -270,15 +282,22 @@ def roofline_of(cfg, kernels_us):
     kname = max((k for k in kernels_us if k in costs), key=lambda k: kernels_us[k])
     kus = kernels_us[kname]
     ops, nbytes = costs[kname]
-    _, bound = ideal_us(ops, nbytes)
+    peak = mfma_peak_tops(cfg, kname)
+    _, bound = ideal_us(ops, nbytes, peak)
     if bound == "mfma":
         achieved = ops / (kus * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
-                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": round(peak, 1),
+                "unit": "TOP/s", "frac": round(achieved / peak, 4),
+                "peak_parts": {"g_x FP6 (INT4 codes)": FP6_PEAK_TOPS, "g_w INT8": INT8_PEAK_TOPS},
+                "frac_of_int8_peak": round(achieved / INT8_PEAK_TOPS, 4)}
     else:
         achieved = nbytes / (kus * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        if ops:  # a product whose ideal HBM time exceeds its ideal matrix-core time
+            roof.update(achieved_tops=round(ops / (kus * 1e-6) / 1e12, 1),
+                        mfma_peak_tops=round(peak, 1),
+                        mfma_frac=round(ops / (kus * 1e-6) / 1e12 / peak, 4))
     roof.update(kernel=kname, kernel_us=round(kus, 2), algorithmic_bytes=nbytes,
                 algorithmic_ops=ops, traffic=measured_traffic(cfg.name, kname))
     return roof
@@ -606,7 +625,8 @@ def main():
     lat_us = res["wall_ms_per_step"] * 1e3
     costs = step_costs(cfg, 4 if cfg.dtype == 0 else 2)
     ops_total = 2 * cfg.T * cfg.I * cfg.O + 2 * cfg.Tl * cfg.O * cfg.I
-    ideal_total = sum(ideal_us(*costs[k])[0] for k in res["kernels_us"] if k in costs)
+    ideal_total = sum(ideal_us(*costs[k], mfma_peak_tops(cfg, k))[0]
+                      for k in res["kernels_us"] if k in costs)
 
     # dominant kernel against its roofline
     roof = roofline_of(cfg, res["kernels_us"])
