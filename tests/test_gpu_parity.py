@@ -123,6 +123,49 @@ def test_large_tile_pair_ragged():
     _case(cfg)
 
 
+# Accumulators at their exactness limits.  Inputs planted so that every
+# transformed value of an operand has the same magnitude (a one-hot first
+# element per Hadamard block transforms to a block of ones), hence every
+# code is qmax and every accumulator the largest the API admits.
+def _limit_case(T, I, O, n, r, gy, x, w, expect_x=None, expect_w=None):
+    base = wl.BY_NAME["tiny"]
+    cfg = dataclasses.replace(base, T=T, I=I, O=O, block=n, rank=r, dtype=wl.F32,
+                              gx_mode=0, gw_mode=0, index=401)
+    _say(f"limit case T={T} I={I} O={O} n={n} r={r}")
+    inp = {"gy": gy, "x": x, "w": w}
+    ocodes, oscales, ref = run_oracle(cfg, inp)
+    gpu = run_gpu(cfg, inp, x_codes=ocodes, x_scales=oscales)
+    compare(cfg, gpu, ocodes, oscales, ref)
+    if expect_x is not None:
+        assert (gpu.inter["acc_x"] == expect_x).all()
+    if expect_w is not None:
+        assert (gpu.inter["acc_w"] == expect_w).all()
+
+
+def test_gx_accumulator_at_the_fp6_exactness_limit():
+    # O = 342384 (<= 342391): acc_x = 49 * O = 16776816 < 2^24, every fp32
+    # partial sum of the FP6 product an exact integer up to the last one
+    T, I, O, n = 16, 8, 342384, 16
+    gy = np.zeros((T, O), np.float32)
+    gy[:, ::n] = 1.0
+    w = np.zeros((O, I), np.float32)
+    w[::n, :] = 1.0
+    x = np.random.default_rng(7).standard_normal((T, I)).astype(np.float32)
+    _limit_case(T, I, O, n, 8, gy, x, w, expect_x=49 * O)
+
+
+def test_gw_accumulator_at_the_int32_limit():
+    # T' = T = 133136 (<= 133143, full rank): acc_w = 127^2 * T' = 2147350544
+    # < 2^31; the g_w tile's K also splits over workgroups here
+    T, I, O, n = 133136, 8, 16, 16
+    gy = np.zeros((T, O), np.float32)
+    gy[::n, :] = 1.0
+    x = np.zeros((T, I), np.float32)
+    x[::n, :] = 1.0
+    w = np.random.default_rng(8).standard_normal((O, I)).astype(np.float32) * 0.02
+    _limit_case(T, I, O, n, 16, gy, x, w, expect_w=127 * 127 * T)
+
+
 # ----------------------------------------------- layer configs, reduced tokens
 
 REDUCED_T = {"vitb_qkv": 1040, "vitb_fc2": 1056, "llama3_8b_down": 1024,
