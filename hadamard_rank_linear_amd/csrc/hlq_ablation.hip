@@ -13,8 +13,8 @@
 // Hadamard, or its low-rank rows j*n/r (the full butterfly network in fp32,
 // ascending stages, then the kept outputs).  Codes: symmetric absmax with
 // round-half-even, one scale per output index m' (PER_TOKEN) or per operand;
-// stored one signed byte per code (INT4 values fit), K-major [M'][Kpad],
-// zero past K'.
+// stored one signed byte per code (INT4 values fit), M' rows of Kpad K bytes
+// in the INT8 K planes the library's GEMM reads (hlq_device.h), zero past K'.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_abl_init(AblOperand o) {
   const int64_t groups = o.per_token ? o.Mo : 1;
   if (i < groups) o.maxbits[i] = 0u;
   const int64_t pad = o.Kpad - o.Ko;
-  if (pad > 0 && i < o.Mo * pad) o.q[(i / pad) * o.Kpad + o.Ko + i % pad] = 0;
+  if (pad > 0 && i < o.Mo * pad) o.q[i8_plane_off(o.Mo, i / pad, o.Ko + i % pad)] = 0;
 }
 
 template <int N, int PASS>
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void k_abl_operand(AblOperand o) {
       const float a = __uint_as_float(o.maxbits[g]);
       const float inv = inv_of(a, qmax);
       const float q = fminf(fmaxf(rintf(v[j] * inv), -qmax), qmax);
-      o.q[mo * o.Kpad + ko] = (int8_t)(int)q;
+      o.q[i8_plane_off(o.Mo, mo, ko)] = (int8_t)(int)q;
       if (ko == 0 && (o.per_token || mo == 0)) o.s[g] = scale_of(a, qmax);
     }
   }

@@ -116,6 +116,20 @@ __device__ __forceinline__ uint32_t pack8_nibbles(const uint32_t (&q)[8]) {
 // the 48 contiguous bytes 48 h .. 48 h + 47.
 __device__ __forceinline__ constexpr int fp6_quarter_pos(int q) { return ((q & 1) << 1) | (q >> 1); }
 
+// K-plane storage of the integer GEMM operands.  An operand of `rows` rows
+// and a K run of kpitch bytes per row is stored as kpitch / U planes of
+// rows * U bytes: plane p holds bytes [p U, (p + 1) U) of every row's run,
+// row after row.  U = 96 for the FP6 codes (one 128-value group per plane)
+// and 64 for the INT8 codes.  A GEMM stage then reads one contiguous block
+// per operand (tile rows x U bytes) instead of rows x U bytes scattered at
+// the row pitch, which leaves most of each cache line it touches unused.
+constexpr int FP6_PLANE = 96;
+constexpr int I8_PLANE = 64;
+// Byte offset of byte k of row m of an INT8 operand with `rows` rows.
+__device__ __forceinline__ int64_t i8_plane_off(int64_t rows, int64_t m, int64_t k) {
+  return (k >> 6) * rows * I8_PLANE + m * I8_PLANE + (k & (I8_PLANE - 1));
+}
+
 // The code rne(fl(v * inv)) as an integer-valued float (the magic add of
 // quant_bits, then an exact subtraction; never -0).
 __device__ __forceinline__ float quant_code_f32(float v, float inv) {

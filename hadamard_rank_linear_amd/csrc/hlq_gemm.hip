@@ -29,8 +29,12 @@
 namespace hlq {
 
 // ------------------------------------------------------------ integer GEMM
-// C[m][n] = sum_k A[m][k] * B[n][k]; A [M][pitch], B [N][pitch] bytes, K
-// contiguous and zero-padded to a multiple of the stage depth KB.
+// C[m][n] = sum_k A[m][k] * B[n][k]; the K run of every row is pitch bytes,
+// zero-padded to a multiple of the stage depth KB, and the integer operands
+// are stored in K planes (hlq_device.h: plane p = bytes [p U, (p + 1) U) of
+// every row, rows consecutive; U = 96 for FP6, 64 for INT8), so one stage of
+// a tile is one contiguous block per operand.  The bf16 operands of the
+// forward are plain row-major [M][pitch] / [N][pitch].
 //
 // Matrix cores: INT8 operands (the g_w product) on v_mfma_i32_32x32x32_i8
 // (32 cycles of the matrix pipe for a 32x32x32 product; the 16x16x64 form
@@ -119,6 +123,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait for this wave's LDS reads, then a workgroup barrier.  Written with
+// the builtins so the compiler knows the reads are complete and adds no wait
+// of its own before their first use (an asm wait is opaque to it, and the one
+// it would add also covers the next stage's reads issued after the barrier);
+// the empty asm statements keep every memory access on its side.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // 16 bytes per lane from global memory into LDS run l (lane i -> l + 16 i).
 __device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
@@ -173,12 +189,14 @@ struct GemmArgs {
   int32_t* Ci;
   // Implicit-GEMM input gradient of a convolution (gemm_tile CONV): output
   // rows m = input pixels (n, h, w) of an [N][cH][cW] image, columns the cC
-  // channels; K stage st belongs to tap (st / cSO) = r * cS + s.  A (the
-  // H.g_y codes, pitch bytes per output pixel of the cP x cQ grid) is read at
-  // the output pixel (n, (h + pad - r) / stride, (w + pad - s) / stride)
-  // when that is a whole in-range position, else at `zero` (pitch zero
-  // bytes); B (the H.w codes) at row tap * cC + channel.
+  // channels; K stage st belongs to tap (st / cSO) = r * cS + s and is plane
+  // st % cSO of the operands.  A (the H.g_y codes, one row per output pixel
+  // of the cP x cQ grid) is read at the output pixel (n, (h + pad - r) /
+  // stride, (w + pad - s) / stride) when that is a whole in-range position,
+  // else at `zero` (96 zero bytes); B (the H.w codes) at row tap * cC +
+  // channel.
   int32_t cH, cW, cP, cQ, cS, cC, cstride, cpad, cSO;
+  int64_t cArows, cBrows;  // rows of A (output pixels) and B (taps x channels): plane heights
   const uint8_t* zero;
   // bf16 forward (gemm_tile BF16): y [M][N] as bf16 bits (EPI_BF16) and, when
   // acbp_codes is set, the ACBP codes [M][K/2] and scales [M] of A (= x),
@@ -236,7 +254,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
   const int64_t S = (S_total - s_first < sps ? S_total - s_first : sps);  // >= 1 by plan
   const int64_t kbase = s_first * KB;
 
-  // DMA sources of this lane for stage 0 (rows past M / N re-read the last row)
+  // DMA sources of this lane for stage 0 (rows past M / N re-read the last row).
+  // The integer operands are in K planes of U bytes (FP6: 96, one plane per
+  // stage; INT8: 64, one or two per stage): chunk c of row r of a stage sits
+  // in plane c * 16 / U of it at r * U + c * 16 % U, and a stage is M * KB
+  // (N * KB) bytes on.  The bf16 operands of the forward are plain row-major.
+  constexpr int U = FP6 ? FP6_PLANE : I8_PLANE;
+  const int64_t sta = BF16 ? KB : M * KB, stb = BF16 ? KB : N * KB;
   const uint8_t* src[IPW];
   // CONV: input pixel (n, h, w) of each A slot's row, channel of each B
   // slot's row, byte offset of each slot's 16-byte chunk
@@ -255,7 +279,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
       cv_off[j] = c * 16;
       src[j] = nullptr;
     } else {
-      src[j] = A + r * pitch + kbase + c * 16;
+      src[j] = BF16 ? A + r * pitch + kbase + c * 16
+                    : A + s_first * sta + ((c * 16 / U) * M + r) * U + c * 16 % U;
     }
   }
 #pragma unroll
@@ -268,7 +293,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
       cv_off[IA + j] = c * 16;
       src[IA + j] = nullptr;
     } else {
-      src[IA + j] = B + r * pitch + kbase + c * 16;
+      src[IA + j] = BF16 ? B + r * pitch + kbase + c * 16
+                         : B + s_first * stb + ((c * 16 / U) * N + r) * U + c * 16 % U;
     }
   }
   // Issue the LDS DMA of K stage st into ring buffer bf.
@@ -287,19 +313,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
           q /= g.cstride;
         }
         ok = ok && p < g.cP && q < g.cQ;
-        const uint8_t* row = ok ? A + ((int64_t)(cv_n[j] * g.cP + p) * g.cQ + q) * pitch : g.zero;
-        lds_dma16(row + ko * KB + cv_off[j], base_ + (wave * IA + j) * 1024);
+        // plane ko of the output pixel's row (FP6 planes of KB bytes)
+        const uint8_t* row =
+            ok ? A + ((int64_t)ko * g.cArows + (int64_t)(cv_n[j] * g.cP + p) * g.cQ + q) * KB
+               : g.zero;
+        lds_dma16(row + cv_off[j], base_ + (wave * IA + j) * 1024);
       }
 #pragma unroll
       for (int j = 0; j < IB; ++j)
-        lds_dma16(B + (int64_t)(tap * g.cC + cv_c[j]) * pitch + ko * KB + cv_off[IA + j],
+        lds_dma16(B + ((int64_t)ko * g.cBrows + tap * g.cC + cv_c[j]) * KB + cv_off[IA + j],
                   base_ + BM * KB + (wave * IB + j) * 1024);
     } else {
 #pragma unroll
-      for (int j = 0; j < IA; ++j) lds_dma16(src[j] + st * KB, base_ + (wave * IA + j) * 1024);
+      for (int j = 0; j < IA; ++j) lds_dma16(src[j] + st * sta, base_ + (wave * IA + j) * 1024);
 #pragma unroll
       for (int j = 0; j < IB; ++j)
-        lds_dma16(src[IA + j] + st * KB, base_ + BM * KB + (wave * IB + j) * 1024);
+        lds_dma16(src[IA + j] + st * stb, base_ + BM * KB + (wave * IB + j) * 1024);
     }
   };
 #define HLQ_GEMM_ISSUE(st, bf) issue((st), (bf))
@@ -432,7 +461,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
         // buffer is refilled (after those reads are issued)
         if constexpr (MODE == 0) wait_vmcnt<(NS - 2) * IPW>();
         else HLQ_GEMM_WAIT((S - st - 2 < NS - 2 ? S - st - 2 : NS - 2));
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        lds_barrier();
         const int ob = buf;
         buf = buf + 1 == NS ? 0 : buf + 1;
         const uint8_t* nb = lds + buf * G::STAGE;
@@ -471,7 +500,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int64_t w, int64_t 
         // still fly) and no wave reads stage st any more ...
         if constexpr (MODE == 0) wait_vmcnt<(NS - 2) * IPW>();
         else HLQ_GEMM_WAIT((S - st - 2 < NS - 2 ? S - st - 2 : NS - 2));
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        lds_barrier();
         // ... so the first fragments of stage st+1 load under this step's
         // MFMAs, and stage st's buffer is refilled (after those reads are
         // issued: an LDS read behind a DMA into LDS would wait for the DMA).
@@ -998,6 +1027,8 @@ hipError_t launch_dgrad(const ConvGemm& c, hipStream_t s) {
   a.cH = (int32_t)c.H; a.cW = (int32_t)c.W; a.cP = (int32_t)c.P; a.cQ = (int32_t)c.Q;
   a.cS = (int32_t)c.S; a.cC = (int32_t)c.C; a.cstride = c.stride; a.cpad = c.pad;
   a.cSO = (int32_t)so;
+  a.cArows = c.N * c.P * c.Q;
+  a.cBrows = c.taps * c.C;
   a.zero = c.zero;
   const int64_t tiles = (int64_t)cdiv(M, 128) * cdiv(c.C, 128);
   const dim3 g((unsigned)((tiles + 7) / 8 * 8));

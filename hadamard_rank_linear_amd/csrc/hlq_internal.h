@@ -161,9 +161,9 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
 // q_w[tap * C + c][o] over the taps whose (p, q) is a whole in-range output
 // position (per-tensor scales only).  EPI_I32 stores the INT32 sums instead.
 struct ConvGemm {
-  const uint8_t* q_gy;  // [N*P*Q][kx_pitch] INT4 codes of H.g_y
-  const uint8_t* q_w;   // [R*S*C][kx_pitch] INT4 codes of H.w (K-major)
-  const uint8_t* zero;  // kx_pitch zero bytes
+  const uint8_t* q_gy;  // N*P*Q rows x kx_pitch: FP6 codes of H.g_y (96-byte K planes)
+  const uint8_t* q_w;   // R*S*C rows x kx_pitch: FP6 codes of H.w (96-byte K planes)
+  const uint8_t* zero;  // kx_pitch (>= 96) zero bytes
   int64_t kx_pitch, N, H, W, C, P, Q, S, taps;
   int stride, pad;
   const float* s_gy;    // [1]

@@ -257,26 +257,69 @@ __device__ __forceinline__ void store_staged_full(const uint8_t (*outs)[OUT_PITC
   }
 }
 
-// Zero bytes [from, to) of `cols` rows of a K-major operand (K padding);
-// nthr threads share the work.
-__device__ __forceinline__ void zero_tail(uint8_t* dst, int64_t pitch, int cols, int64_t from,
-                                          int64_t to, int tid, int nthr = 256) {
+// Store the staged INT8 codes of a tile into the K planes of an operand with
+// `nrows` rows: column c of the tile (operand row c0 + c) owns `len` bytes at
+// K offset koff.  Units of the widest width dividing len and koff (at most
+// 16, so no unit crosses a 64-byte plane).
+__device__ __forceinline__ void store_staged_i8(const uint8_t (*outs)[OUT_PITCH], int cols,
+                                                int len, uint8_t* q, int64_t nrows, int64_t c0,
+                                                int64_t koff, int tid) {
+  int wdt = 16;
+  while (wdt > 1 && ((len % wdt) || (koff % wdt))) wdt >>= 1;
+  const int per_col = len / wdt;
+  const int total = cols * per_col;
+  for (int i = tid; i < total; i += 256) {
+    const int c = i / per_col, k = (i % per_col) * wdt;
+    uint8_t* d = q + i8_plane_off(nrows, c0 + c, koff + k);
+    const uint8_t* s = &outs[c][k];
+    if (wdt == 16) *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+    else if (wdt == 8) *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(s);
+    else if (wdt == 4) *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
+    else if (wdt == 2) *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
+    else *d = *s;
+  }
+}
+
+// store_staged_i8 for a full tile whose runs are LEN bytes, LEN a multiple of
+// 16 that divides 64 (koff a multiple of LEN: every run inside one plane):
+// the tile's runs are CW consecutive 64-byte rows of that plane.
+template <int LEN>
+__device__ __forceinline__ void store_staged_i8_full(const uint8_t (*outs)[OUT_PITCH],
+                                                     uint8_t* q, int64_t nrows, int64_t c0,
+                                                     int64_t koff, int tid) {
+  static_assert(LEN % 16 == 0 && I8_PLANE % LEN == 0, "16-byte runs inside one plane");
+  constexpr int PER = LEN / 16;
+  uint8_t* dst = q + i8_plane_off(nrows, c0, koff);
+#pragma unroll
+  for (int i = tid; i < CW * PER; i += 256) {
+    const int c = i / PER, k = (i % PER) * 16;
+    *reinterpret_cast<uint4*>(dst + (int64_t)c * I8_PLANE + k) =
+        *reinterpret_cast<const uint4*>(&outs[c][k]);
+  }
+}
+
+// Zero K bytes [from, to) of operand rows c0 .. c0 + cols - 1 (INT8 K planes,
+// `nrows` rows; K padding); nthr threads share the work.
+__device__ __forceinline__ void zero_tail_i8(uint8_t* q, int64_t nrows, int64_t c0, int cols,
+                                             int64_t from, int64_t to, int tid, int nthr = 256) {
   const int64_t w = to - from;
   if (w <= 0) return;
-  for (int64_t i = tid; i < (int64_t)cols * w; i += nthr) dst[(i / w) * pitch + from + i % w] = 0;
+  for (int64_t i = tid; i < (int64_t)cols * w; i += nthr)
+    q[i8_plane_off(nrows, c0 + i / w, from + i % w)] = 0;
 }
 
 // Column pass, low-rank rows of H_N (g_w operands).  Thread tid owns column
 // c = tid % CW and blocks b = tid / CW + 2t.  MAX: the tile's column maxima ->
 // part[0..cols).  QUANT: INT8 codes (reciprocal scale colinv[c], or that of tensor
 // list `list` when colinv is null) staged in LDS over the tile (after a
-// barrier) and stored K-contiguous at q[(c0 + c) * pitch + t0 / N * R ...].
+// barrier) and stored as operand row c0 + c, K bytes t0 / N * R ..., of the
+// INT8 K planes of q (nrows rows, kpitch bytes of K per row).
 template <int PASS, int N, int R, class RD>
 __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, uint8_t* smem,
                                                 float* red, int rows, int cols, int64_t c0,
                                                 const float* colinv, int list, float* part,
-                                                uint8_t* q, int64_t pitch, int64_t tl,
-                                                int64_t t0, bool last) {
+                                                uint8_t* q, int64_t nrows, int64_t kpitch,
+                                                int64_t tl, int64_t t0, bool last) {
   constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;  // tasks per thread
   constexpr int WPR = (R + 3) / 4;                           // code words per task
   const int tid = threadIdx.x;
@@ -329,11 +372,12 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
     __syncthreads();
     const int64_t koff = t0 / N * R;
     constexpr int LEN = (TT / N) * R;
-    if (LEN % 16 == 0 && rows == TT && cols == CW)
-      store_staged_full<(LEN % 16 == 0 ? LEN : 16)>(outs, q + c0 * pitch + koff, pitch, tid);
+    constexpr bool FULL_OK = LEN % 16 == 0 && I8_PLANE % LEN == 0;
+    if (FULL_OK && rows == TT && cols == CW)
+      store_staged_i8_full<(FULL_OK ? LEN : 16)>(outs, q, nrows, c0, koff, tid);
     else
-      store_staged(outs, cols, nb * R, q + c0 * pitch + koff, pitch, koff, tid);
-    if (last) zero_tail(q + c0 * pitch, pitch, cols, tl, pitch, tid);
+      store_staged_i8(outs, cols, nb * R, q, nrows, c0, koff, tid);
+    if (last) zero_tail_i8(q, nrows, c0, cols, tl, kpitch, tid);
   }
 }
 
@@ -343,7 +387,7 @@ template <int PASS, int N, class RD>
 __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint8_t* smem,
                                              float* red, int rows, int cols, int64_t c0,
                                              const float* colinv, int list, float* part,
-                                             uint8_t* q, int64_t pitch, int64_t o0, int64_t O,
+                                             uint8_t* q, int64_t nrows, int64_t o0, int64_t O,
                                              bool last) {
   constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;
   constexpr int NB = TT / N;  // blocks of the tile's group
@@ -430,12 +474,13 @@ __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint
       }
     }
     __syncthreads();
-    // the whole 96-byte group of each column, K padding (zero codes) included
-    const int64_t koff = (o0 / TT) * 96;
+    // the whole 96-byte group of each column, K padding (zero codes)
+    // included: rows c0 .. of FP6 plane o0 / TT (nrows rows of 96 bytes)
+    uint8_t* dst = q + ((o0 / TT) * nrows + c0) * FP6_PLANE;
     if (cols == CW)
-      store_staged_full<96>(outs, q + c0 * pitch + koff, pitch, tid);
+      store_staged_full<96>(outs, dst, FP6_PLANE, tid);
     else
-      store_staged(outs, cols, 96, q + c0 * pitch + koff, pitch, koff, tid);
+      store_staged(outs, cols, 96, dst, FP6_PLANE, 0, tid);
   }
   (void)last;
   (void)O;
@@ -538,9 +583,9 @@ __device__ __forceinline__ void gy_rows_bf16_full(const TrArgs& a, int64_t t0, i
     for (int sw = 0; sw < SW; ++sw) inv[sw] = a.gx_tok ? ib[sw * 16 + lr] : inv_tensor;
   }
   static_assert(SW % 4 == 0 && CW == 128, "four rows per FP6 conversion, one group per tile");
-  const uint32_t K32 = (uint32_t)a.kxb;
-  // the tile's 128 columns are one FP6 group of each row (96 bytes)
-  uint8_t* qbase = a.q_gy + t0 * a.kxb + (c0 / CW) * 96;
+  // the tile's 128 columns are one FP6 group of each row: rows t0 .. of FP6
+  // plane c0 / CW (T rows of 96 bytes)
+  uint8_t* qbase = a.q_gy + ((c0 / CW) * a.T + t0) * FP6_PLANE;
   float rc[4][8];
 #pragma unroll
   for (int sw = 0; sw < SW; ++sw) {
@@ -567,7 +612,8 @@ __device__ __forceinline__ void gy_rows_bf16_full(const TrArgs& a, int64_t t0, i
         fp6_rows4(rc, lo, hi);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          store_fp6_lane8(qbase + (uint32_t)((sw - 3 + k) * 16 + lr) * K32, lc, lo[k], hi[k], true);
+          store_fp6_lane8(qbase + (uint32_t)((sw - 3 + k) * 16 + lr) * FP6_PLANE, lc, lo[k], hi[k],
+                          true);
       }
     }
   }
@@ -603,7 +649,7 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
     if (row < rows && col < cols) load_raw8(a.gy, a.gy_dt, (t0 + row) * a.O + c0 + col, raw[sw]);
   }
   float rc[4][8];
-  uint8_t* qbase = a.q_gy + t0 * a.kxb + (c0 / CW) * 96;
+  uint8_t* qbase = a.q_gy + ((c0 / CW) * a.T + t0) * FP6_PLANE;
 #pragma unroll
   for (int sw = 0; sw < SW; ++sw) {
     const int row = sw * 16 + lr;
@@ -630,7 +676,7 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int rk = (sw - 3 + k) * 16 + lr;
-          store_fp6_lane8(qbase + (int64_t)rk * a.kxb, lc, lo[k], hi[k], rk < rows);
+          store_fp6_lane8(qbase + (int64_t)rk * FP6_PLANE, lc, lo[k], hi[k], rk < rows);
         }
       }
     }
@@ -641,11 +687,13 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
   if constexpr (F32) {
     RdF32 rd{reinterpret_cast<const float*>(smem)};
     colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_gyl : nullptr,
-                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.kwb, a.tl, t0, last);
+                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.O, a.kwb, a.tl, t0,
+                                last);
   } else {
     RdB16 rd{reinterpret_cast<const uint16_t*>(smem)};
     colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_gyl : nullptr,
-                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.kwb, a.tl, t0, last);
+                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.O, a.kwb, a.tl, t0,
+                                last);
   }
 }
 
@@ -904,12 +952,12 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
   if (!a.conv) {
     RdI4 rd{codes, scales};
     colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_xl : nullptr,
-                                3, a.part_xl + tr * a.I + c0, a.q_xl, a.kwb, a.tl, t0,
+                                3, a.part_xl + tr * a.I + c0, a.q_xl, a.I, a.kwb, a.tl, t0,
                                 t0 + rows == a.T);
   } else {
     RdI4c rd{codes, scales};
     colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_xl : nullptr,
-                                3, a.part_xl + tr * a.I + c0, a.q_xl, a.kwb, a.tl, t0,
+                                3, a.part_xl + tr * a.I + c0, a.q_xl, a.I, a.kwb, a.tl, t0,
                                 t0 + rows == a.T);
   }
 }
@@ -942,11 +990,11 @@ __device__ void tr_job_w(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
   if constexpr (F32) {
     RdF32 rd{reinterpret_cast<const float*>(smem)};
     colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.inv_w : nullptr, 1,
-                          a.part_w + tr * a.I + c0, a.q_w, a.kxb, o0, a.O, last);
+                          a.part_w + tr * a.I + c0, a.q_w, a.I, o0, a.O, last);
   } else {
     RdB16 rd{reinterpret_cast<const uint16_t*>(smem)};
     colpass_full<PASS, N>(a, rd, smem, red, rows, cols, c0, a.gx_tok ? a.inv_w : nullptr, 1,
-                          a.part_w + tr * a.I + c0, a.q_w, a.kxb, o0, a.O, last);
+                          a.part_w + tr * a.I + c0, a.q_w, a.I, o0, a.O, last);
   }
 }
 

@@ -201,20 +201,26 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
 /*
  * Where hlq_linear_backward leaves its intermediates inside the workspace
  * (byte offsets), for tests and diagnostics.
- *   q_gy   [T][kx_pitch]  INT4 codes of H.g_y (along O), stored as FP6 E2M3
- *          fields (exact for -7..7: sign bit 5, exponent bits 4-3 with bias
- *          1, mantissa bits 2-0) in groups of 128 codes (96 bytes): quarter Q
- *          of a group (codes 32Q .. 32Q+31) is a 24-byte stream, code j at
- *          bits 6j .. 6j+5, and the quarters are stored in the order 0, 2, 1,
- *          3.  Codes past O are zero fields (kx_pitch = 96 * ceil(O / 128)).
+ * The four code operands are matrices of `rows` rows whose K run is pitch
+ * bytes per row, stored in K planes of U bytes: plane p (p = 0 ..
+ * pitch/U - 1) holds bytes [p*U, (p+1)*U) of every row's run, row after row,
+ * so byte k of row m is at (k / U) * rows * U + m * U + k % U.  U = 96 for
+ * q_gy and q_w, 64 for q_gyl and q_xl.
+ *   q_gy   T rows, kx_pitch bytes: INT4 codes of H.g_y (along O), stored as
+ *          FP6 E2M3 fields (exact for -7..7: sign bit 5, exponent bits 4-3
+ *          with bias 1, mantissa bits 2-0) in groups of 128 codes (96 bytes,
+ *          one plane): quarter Q of a group (codes 32Q .. 32Q+31) is a
+ *          24-byte stream, code j at bits 6j .. 6j+5, and the quarters are
+ *          stored in the order 0, 2, 1, 3.  Codes past O are zero fields
+ *          (kx_pitch = 96 * ceil(O / 128)).
  *   s_gy   [T] (PER_TOKEN) or [1] f32.
- *   q_w    [I][kx_pitch]  INT4 codes of H.w, stored transposed (K = O
- *          contiguous), in the same FP6 groups.
+ *   q_w    I rows, kx_pitch bytes: INT4 codes of H.w, transposed (K = O), in
+ *          the same FP6 groups.
  *   s_w    [I] or [1] f32.
- *   q_gyl  [O][kw_pitch]  INT8 codes of the low-rank g_y, transposed (K = T'
- *          contiguous), zero past T' = T*rank/block.
+ *   q_gyl  O rows, kw_pitch bytes: INT8 codes of the low-rank g_y, transposed
+ *          (K = T'), zero past T' = T*rank/block.
  *   s_gyl  [O] or [1] f32.
- *   q_xl   [I][kw_pitch]  INT8 codes of the low-rank x, transposed.
+ *   q_xl   I rows, kw_pitch bytes: INT8 codes of the low-rank x, transposed.
  *   s_xl   [I] or [1] f32.
  *   partial  scratch of the split-K GEMMs (contents unspecified).
  * The workspace also holds, after these, the INT32 partial sums and arrival
@@ -222,8 +228,8 @@ hlq_status hlq_linear_backward_steps(const void* g_y, int gy_dtype,
  */
 typedef struct hlq_workspace_layout {
   size_t q_gy, s_gy, q_w, s_w, q_gyl, s_gyl, q_xl, s_xl;
-  int64_t kx_pitch;  /* bytes per row of q_gy and q_w  */
-  int64_t kw_pitch;  /* bytes per row of q_gyl and q_xl */
+  int64_t kx_pitch;  /* K bytes per row of q_gy and q_w (96-byte planes)  */
+  int64_t kw_pitch;  /* K bytes per row of q_gyl and q_xl (64-byte planes) */
   int64_t t_low;     /* T' = T * rank / block           */
   size_t total;      /* == hlq_linear_backward_workspace_size() */
   size_t partial;    /* INT32 split-K partial sums shared by both GEMMs */

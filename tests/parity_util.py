@@ -53,6 +53,15 @@ def _fp6_e2m3_table() -> np.ndarray:
 FP6_E2M3 = _fp6_e2m3_table()
 
 
+def unplane(flat: np.ndarray, rows: int, pitch: int, unit: int) -> np.ndarray:
+    """Row-major [rows][pitch] copy of an operand stored in K planes of
+    `unit` bytes (include/hlq.h: byte k of row m at (k // unit) * rows * unit
+    + m * unit + k % unit; 96 for the FP6 codes, 64 for the INT8 codes)."""
+    assert pitch % unit == 0 and flat.size >= rows * pitch
+    planes = flat[: rows * pitch].reshape(pitch // unit, rows, unit)
+    return np.ascontiguousarray(planes.transpose(1, 0, 2)).reshape(rows, pitch)
+
+
 def decode_fp6_groups(b: np.ndarray) -> np.ndarray:
     """uint8 [.., 96 * G] -> int8 [.., 128 * G]: INT4 codes stored as FP6 E2M3
     in groups of 128 (96 bytes).  Quarter Q of a group (codes 32Q .. 32Q+31)
@@ -143,13 +152,13 @@ def run_gpu(cfg, inp, x_codes=None, x_scales=None, want_acc=True, reduction=None
     n_gyl = O if cfg.gw_mode == wl.PER_TOKEN else 1
     n_xl = I if cfg.gw_mode == wl.PER_TOKEN else 1
     inter.update(
-        q_gy_packed=region(lay["q_gy"], T * kxb, np.uint8).reshape(T, kxb),
+        q_gy_packed=unplane(region(lay["q_gy"], T * kxb, np.uint8), T, kxb, 96),
         s_gy=region(lay["s_gy"], n_gx, np.float32).copy(),
-        q_w_packed=region(lay["q_w"], I * kxb, np.uint8).reshape(I, kxb),
+        q_w_packed=unplane(region(lay["q_w"], I * kxb, np.uint8), I, kxb, 96),
         s_w=region(lay["s_w"], n_w, np.float32).copy(),
-        q_gyl_stored=region(lay["q_gyl"], O * kwb, np.int8).reshape(O, kwb),
+        q_gyl_stored=unplane(region(lay["q_gyl"], O * kwb, np.int8), O, kwb, 64),
         s_gyl=region(lay["s_gyl"], n_gyl, np.float32).copy(),
-        q_xl_stored=region(lay["q_xl"], I * kwb, np.int8).reshape(I, kwb),
+        q_xl_stored=unplane(region(lay["q_xl"], I * kwb, np.int8), I, kwb, 64),
         s_xl=region(lay["s_xl"], n_xl, np.float32).copy(),
         kxb=kxb, kwb=kwb, t_low=tl,
     )

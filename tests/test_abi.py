@@ -303,3 +303,17 @@ def test_fp6_group_decoder_round_trip_and_hand_bytes():
     assert b[0, 0] == 8 and b[0, 48] == 62 and b[0, 24] == 0 and b[0, 25] == 5
     assert int(b.sum()) == 8 + 62 + 5
     assert np.array_equal(decode_fp6_groups(b), c)
+
+
+def test_k_plane_decoder_follows_the_header_formula():
+    """unplane inverts the K-plane storage of include/hlq.h (byte k of row m
+    at (k // U) * rows * U + m * U + k % U), checked byte by byte."""
+    from parity_util import unplane
+    for rows, pitch, unit in ((5, 192, 96), (3, 128, 64), (7, 64, 64)):
+        flat = np.zeros(rows * pitch, np.int64)
+        for m in range(rows):
+            for k in range(pitch):
+                flat[(k // unit) * rows * unit + m * unit + k % unit] = 1000 * m + k
+        got = unplane(flat, rows, pitch, unit)
+        assert got.shape == (rows, pitch)
+        assert np.array_equal(got, 1000 * np.arange(rows)[:, None] + np.arange(pitch)[None, :])

@@ -12,7 +12,7 @@ import pytest
 
 import oracle as o
 from hadamard_rank_linear_amd import workloads as wl
-from parity_util import GpuRun, compare, host_f32, to_device
+from parity_util import GpuRun, compare, host_f32, to_device, unplane
 
 pytestmark = pytest.mark.gpu
 
@@ -58,13 +58,13 @@ def _run(cfg, seed=0):
     n_gw = O if cfg.gw_mode == wl.PER_TOKEN else 1
     n_xw = I if cfg.gw_mode == wl.PER_TOKEN else 1
     inter = dict(
-        q_gy_packed=region(lay["q_gy"], T * kxb, np.uint8).reshape(T, kxb),
+        q_gy_packed=unplane(region(lay["q_gy"], T * kxb, np.uint8), T, kxb, 96),
         s_gy=region(lay["s_gy"], 1, np.float32).copy(),
-        q_w_packed=region(lay["q_w"], I * kxb, np.uint8).reshape(I, kxb),
+        q_w_packed=unplane(region(lay["q_w"], I * kxb, np.uint8), I, kxb, 96),
         s_w=region(lay["s_w"], 1, np.float32).copy(),
-        q_gyl_stored=region(lay["q_gyl"], O * kwb, np.int8).reshape(O, kwb),
+        q_gyl_stored=unplane(region(lay["q_gyl"], O * kwb, np.int8), O, kwb, 64),
         s_gyl=region(lay["s_gyl"], n_gw, np.float32).copy(),
-        q_xl_stored=region(lay["q_xl"], I * kwb, np.int8).reshape(I, kwb),
+        q_xl_stored=unplane(region(lay["q_xl"], I * kwb, np.int8), I, kwb, 64),
         s_xl=region(lay["s_xl"], n_xw, np.float32).copy(),
         kxb=kxb, kwb=kwb, t_low=lay["t_low"])
     # the input-gradient GEMM and the g_w GEMM are the only GEMM launches here
