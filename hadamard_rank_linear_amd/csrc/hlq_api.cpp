@@ -38,7 +38,7 @@ struct Layout {
   hlq_workspace_layout pub;
   size_t part_gy, part_gyl, part_xl, part_w;  // partial maxima of the MAX pass
   size_t inv_gy, inv_gyl, inv_xl, inv_w;      // reciprocal scales of per-token maxima
-  size_t tmax;                                // tensor maxima (float bits) [4]
+  size_t tmax;                                // tensor maxima (float bits) [4][TMAX_SLOTS]
   int64_t nred;
   size_t partial;                             // int32 split-K partials
   int64_t nch_o, nch_i, ntr_t, ntr_o;         // transform tile grid
@@ -95,7 +95,7 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   L.inv_xl = take((size_t)I * 4);
   L.inv_w = take((size_t)I * 4);
   L.nred = (T + O + 2 * I + hlq::TR_RED_ENTRIES - 1) / hlq::TR_RED_ENTRIES;
-  L.tmax = take(4 * 4);
+  L.tmax = take(4 * hlq::TMAX_SLOTS * 4);
   // split-K partials: the two GEMMs run one after the other on one stream and
   // share this buffer
   size_t part = 0;

@@ -47,6 +47,13 @@ __device__ __forceinline__ float wave_max(float a) {
   return a;
 }
 
+// Maximum of one list's 64 slots of non-negative float bit patterns (the
+// tensor maxima of the transform passes).  Every lane of the wave must call
+// it (one load per lane, then a wave maximum); every lane gets the result.
+__device__ __forceinline__ float tensor_max_slots(const unsigned* slots64) {
+  return wave_max(__uint_as_float(slots64[threadIdx.x & 63]));
+}
+
 // In-lane butterflies over 8 consecutive elements (stages h = 1, 2, 4).
 __device__ __forceinline__ void fwht8(float (&v)[8]) {
 #pragma unroll

@@ -897,17 +897,19 @@ hipError_t launch_gemm(bool fp6, const uint8_t* A, const uint8_t* B, int64_t M,
   return launch_gemm_finalize(partial, splits, M, N, sa, sa_step, sb, sb_step, alpha, C, s);
 }
 
-// g_w tile of the pair launch: the plan's, except that a long-K grid of fewer
-// than 64 tiles takes 64-row tiles (cfg 3: 64 x 128, KB 128, 3 stages): twice
-// the tiles, half the K work each.  Then K splits: the g_w tiles start first,
-// so a g_w tile longer than the launch's mean work per workgroup slot (two per
-// CU) sets its length; nsplit cuts it to about that mean (at most 4 splits of
-// at least 4 stages each).  Work is counted in MACs, an FP6 MAC (twice the
-// INT8 rate on the matrix cores, more LDS bytes per MAC) at 0.7 INT8 MACs.
+// g_w tile of the pair launch: the plan's, except that a grid of at most 128
+// tiles of 128 x 128 takes the deep-ring configuration (wcfg 5: 128 x 128, KB
+// 64, 4 stages).  Then K splits: the g_w tiles start first, so a g_w tile
+// longer than the launch's mean work per workgroup slot (two per CU) sets its
+// length; nsplit cuts it (at most 4 splits of at least 4 stages each) when it
+// is more than twice that mean.  Work is counted in MACs, an FP6 MAC (twice
+// the INT8 rate on the matrix cores, more LDS bytes per MAC) at 0.7 INT8 MACs.
 static int pair_splits(double dw, double dx, int64_t tw, int64_t tx, int64_t slots,
                        int64_t wstages) {
   const double mean = (tw * dw + tx * dx) / (double)slots;
-  int ns = (int)std::ceil(dw / mean - 0.25);
+  // a split costs a merge (the partial sums written and read back once): split
+  // only tiles that cost more than twice a slot's mean load
+  int ns = (int)std::ceil(dw / mean - 1.0);
   ns = std::max(1, std::min(ns, 4));
   while (ns > 1 && wstages / ns < 4) --ns;
   return ns;
@@ -935,13 +937,27 @@ PairPlan plan_pair(int64_t T, int64_t I, int64_t O, const GemmPlan& px, const Ge
     xbm = 256; xbn = 256; slots = 256;
   } else {
     pp.wcfg = pw.cfg; pp.wbm = pw.bm; pp.wbn = pw.bn;
-    if (pw.cfg == 2 && (int64_t)cdiv(O, 128) * cdiv(I, 128) < 64) { pp.wcfg = 3; pp.wbm = 64; }
+    if (pw.kb % 64 == 0 && (int64_t)cdiv(O, 128) * cdiv(I, 128) <= 128) {
+      // a small g_w grid (its tiles run beside the g_x tiles, K long): 64-byte
+      // stages in a four-deep ring, three stages (48 KB) in flight per
+      // workgroup instead of one 32 KB stage of the two-deep 128-byte ring
+      // (64 KB of LDS, inside the FP6 ring's 72 KB; ViT-B qkv pair 41.5 ->
+      // 39.4 us, ResNet-50 stage-3 shape 89.5 -> 80.7; fc2's 144-tile grid
+      // is faster with the 128-byte stages)
+      pp.wcfg = 5; pp.wbm = 128; pp.wbn = 128;
+      wstages = pw.stages * pw.kb / 64;
+    }
   }
   pp.wstages = wstages;
   pp.tx = (int64_t)cdiv(T, xbm) * cdiv(I, xbn);
   pp.tw = (int64_t)cdiv(O, pp.wbm) * cdiv(I, pp.wbn);
-  const double dw = (double)pp.wbm * pp.wbn * pw.stages * pw.kb;
-  const double dx = 0.7 * xbm * xbn * px.stages * (px.kb * 4 / 3);
+  // tile costs in K values: the K loop, plus the fp32 epilogue, which costs
+  // about as much as six 128-value stages (it sets the time of short-K
+  // tiles: ResNet-50 stage-3 shape pair 94.8 -> 88.5 us without the K split
+  // this term removes)
+  constexpr double kEpi = 768;
+  const double dw = (double)pp.wbm * pp.wbn * (pw.stages * pw.kb + kEpi);
+  const double dx = 0.7 * xbm * xbn * (px.stages * (px.kb * 4 / 3) + kEpi);
   int ns = pair_splits(dw, dx, pp.tw, pp.tx, slots, wstages);
   pp.sps = (wstages + ns - 1) / ns;
   pp.nsplit = (int)((wstages + pp.sps - 1) / pp.sps);  // every split non-empty
@@ -966,7 +982,7 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
   if (epi != EPI_F32 && epi != EPI_I32) return hipErrorInvalidValue;
   if (pp.nsplit < 1 || pp.nsplit > 4 || (pp.nsplit > 1 && (!part || !ctr))) return hipErrorInvalidValue;
   if ((pp.nsplit - 1) * pp.sps >= pp.wstages) return hipErrorInvalidValue;  // an empty split
-  if (pp.wstages * (pp.big ? 64 : pw.kb) != kw_pitch) return hipErrorInvalidValue;
+  if (pp.wstages * (pp.big || pp.wcfg == 5 ? 64 : pw.kb) != kw_pitch) return hipErrorInvalidValue;
   const GemmArgs ax{gxA, gxB, T, I, kx_pitch, px.stages, px.stages, s_gy, gx_step, s_w, gx_step,
                     gx_alpha, g_x, acc_x};
   GemmArgs aw{gwA, gwB, O, I, kw_pitch, pp.wstages, pp.sps, s_gyl, gw_step, s_xl, gw_step,
@@ -998,20 +1014,20 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
 #define HLQ_W0 128, 128, 64, 3
 #define HLQ_W1 256, 128, 64, 3
 #define HLQ_W2 128, 128, 128, 2
-#define HLQ_W3 64, 128, 128, 3
+#define HLQ_W5 128, 128, 64, 4
 #define HLQ_X0 128, 128, 96, 3
   if (px.cfg != 0 || px.kb != 96) return hipErrorInvalidValue;
   switch (pp.wcfg) {
     case 1: HLQ_PAIR(HLQ_W1, HLQ_X0); break;
     case 2: HLQ_PAIR(HLQ_W2, HLQ_X0); break;
-    case 3: HLQ_PAIR(HLQ_W3, HLQ_X0); break;
+    case 5: HLQ_PAIR(HLQ_W5, HLQ_X0); break;
     default: HLQ_PAIR(HLQ_W0, HLQ_X0); break;
   }
 #undef HLQ_PAIR
 #undef HLQ_W0
 #undef HLQ_W1
 #undef HLQ_W2
-#undef HLQ_W3
+#undef HLQ_W5
 #undef HLQ_X0
   return hipGetLastError();
 }

@@ -17,6 +17,10 @@ enum TrPass { PASS_MAX = 0, PASS_QUANT = 1 };
 constexpr int TR_ROWS = 128;
 constexpr int TR_COLS = 128;
 constexpr int TR_RED_ENTRIES = 64;  // entries folded per reduce block
+// Atomic slots per tensor maximum: reduce block b folds into slot b % 64, so
+// same-address atomics queue 64 times less; readers fold the 64 slots (one
+// load per lane and a wave maximum).
+constexpr int TMAX_SLOTS = 64;
 constexpr int TR_GY_REG_ROWS = 64;   // token rows of a register-resident g_y tile (one wave)
 
 // Everything the three transform launches (MAX, reduce, QUANT) read and write.
@@ -34,8 +38,9 @@ struct TrArgs {
   float *part_gy, *part_gyl, *part_xl, *part_w;
   // reciprocal scales qmax / max of the folded maxima (per-token modes)
   float *inv_gy, *inv_gyl, *inv_xl, *inv_w;
-  // tensor maxima as float bit patterns, [4]: list 0 H.g_y, 1 H.w,
-  // 2 low-rank g_y, 3 low-rank x (zeroed by the MAX pass, folded by reduce)
+  // tensor maxima as float bit patterns, [4][TMAX_SLOTS] (the maximum of
+  // list l is the maximum of its slots): list 0 H.g_y, 1 H.w, 2 low-rank
+  // g_y, 3 low-rank x (zeroed by the MAX pass, folded into by reduce)
   unsigned* tmax;
   int64_t nred;  // reduce blocks = ceil((T + O + 2 I) / TR_RED_ENTRIES)
   int64_t nch_o, nch_i, ntr_t, ntr_o;
@@ -86,7 +91,7 @@ struct LqsArgs {
   // reciprocal scales and scales, [T], [I], [O], [I]
   const float* tok_inv[4];
   const float* tok_s[4];
-  const unsigned* tmax;  // [4] tensor maxima (float bits)
+  const unsigned* tmax;  // [4][TMAX_SLOTS] slots of the tensor maxima (float bits)
   double* part;          // [wg0[4]][3] per-workgroup sums of v^2, e_tok^2, e_ten^2
   double* stats;         // [16] the caller's accumulated statistics
   int64_t items[4];      // op 0: threads (one row block each); ops 1-3: tiles of

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void k_lqs_rows(LqsArgs a) {
       }
     }
   }
-  const float at = __uint_as_float(a.tmax[0]);
+  const float at = tensor_max_slots(a.tmax);  // every lane of every wave
   const LqsQuant zT{inv_of(at, 7.f), scale_of(at, 7.f), 7.f};
 #pragma unroll
   for (int q = 0; q < RPT; ++q) {
@@ -172,10 +172,10 @@ __global__ __launch_bounds__(64) void k_lqs_cols(LqsArgs a) {
   const int dt = op == 1 ? a.w_dt : a.gy_dt;
   const char* src = static_cast<const char*>(op == 1 ? a.w : a.gy);
   LqsQuant zt{0.f, 0.f, qmax}, zT{0.f, 0.f, qmax};
+  const float at = tensor_max_slots(a.tmax + op * TMAX_SLOTS);  // the whole wave
   if (valid) {
     zt.inv = a.tok_inv[op][col];
     zt.s = a.tok_s[op][col];
-    const float at = __uint_as_float(a.tmax[op]);
     zT.inv = inv_of(at, qmax);
     zT.s = scale_of(at, qmax);
   }

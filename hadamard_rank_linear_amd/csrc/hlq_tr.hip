@@ -308,28 +308,33 @@ __device__ __forceinline__ void zero_tail_i8(uint8_t* q, int64_t nrows, int64_t 
     q[i8_plane_off(nrows, c0 + i / w, from + i % w)] = 0;
 }
 
+// Reciprocal scale of column c0 + tid % CW of a low-rank column pass (QUANT):
+// colinv[column] in per-token mode, else that of tensor list `list` (INT8).
+// Every thread of the workgroup calls it (the tensor maximum is a wave fold).
+__device__ __forceinline__ float lowrank_col_inv(const TrArgs& a, const float* colinv, int list,
+                                                 int64_t c0, int cols) {
+  const int c = threadIdx.x % CW;
+  if (colinv) return c < cols ? colinv[c0 + c] : 0.f;
+  return inv_of(tensor_max_slots(a.tmax + list * TMAX_SLOTS), 127.f);
+}
+
 // Column pass, low-rank rows of H_N (g_w operands).  Thread tid owns column
 // c = tid % CW and blocks b = tid / CW + 2t.  MAX: the tile's column maxima ->
-// part[0..cols).  QUANT: INT8 codes (reciprocal scale colinv[c], or that of tensor
-// list `list` when colinv is null) staged in LDS over the tile (after a
-// barrier) and stored as operand row c0 + c, K bytes t0 / N * R ..., of the
-// INT8 K planes of q (nrows rows, kpitch bytes of K per row).
+// part[0..cols).  QUANT: INT8 codes (reciprocal scale inv_c of the thread's
+// column, lowrank_col_inv) staged in LDS over the tile (after a barrier) and
+// stored as operand row c0 + c, K bytes t0 / N * R ..., of the INT8 K planes
+// of q (nrows rows, kpitch bytes of K per row).
 template <int PASS, int N, int R, class RD>
 __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, uint8_t* smem,
                                                 float* red, int rows, int cols, int64_t c0,
-                                                const float* colinv, int list, float* part,
-                                                uint8_t* q, int64_t nrows, int64_t kpitch,
-                                                int64_t tl, int64_t t0, bool last) {
+                                                float inv_c, float* part, uint8_t* q,
+                                                int64_t nrows, int64_t kpitch, int64_t tl,
+                                                int64_t t0, bool last) {
   constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;  // tasks per thread
   constexpr int WPR = (R + 3) / 4;                           // code words per task
   const int tid = threadIdx.x;
   const int c = tid % CW;
   const int nb = rows / N;
-  float inv_c = 0.f;
-  if constexpr (PASS == PASS_QUANT) {
-    const float tinv = colinv ? 0.f : inv_of(__uint_as_float(a.tmax[list]), list == 1 ? 7.f : 127.f);
-    inv_c = colinv ? (c < cols ? colinv[c0 + c] : 0.f) : tinv;
-  }
   float cm = 0.f;
   uint32_t words[TPT][WPR];
 #pragma unroll
@@ -397,7 +402,8 @@ __device__ __forceinline__ void colpass_full(const TrArgs& a, const RD& rd, uint
   const int nb = rows / N;
   float inv_c = 0.f;
   if constexpr (PASS == PASS_QUANT) {
-    const float tinv = colinv ? 0.f : inv_of(__uint_as_float(a.tmax[list]), list == 1 ? 7.f : 127.f);
+    const float tinv =
+        colinv ? 0.f : inv_of(tensor_max_slots(a.tmax + list * TMAX_SLOTS), list == 1 ? 7.f : 127.f);
     inv_c = colinv ? (c < cols ? colinv[c0 + c] : 0.f) : tinv;
   }
   if constexpr (PASS == PASS_MAX) {
@@ -631,7 +637,7 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
   const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
   float inv_tensor = 0.f;
   if constexpr (PASS == PASS_QUANT) {
-    if (!a.gx_tok) inv_tensor = inv_of(__uint_as_float(a.tmax[0]), 7.f);
+    if (!a.gx_tok) inv_tensor = inv_of(tensor_max_slots(a.tmax), 7.f);
   }
   if (!F32 && rows == TT && cols == CW) {
     gy_rows_bf16_full<PASS, N>(a, t0, c0, ch, smem, inv_tensor);
@@ -684,16 +690,16 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
   }
   __syncthreads();
   const bool last = t0 + rows == a.T;
+  const float inv_c =
+      PASS == PASS_QUANT ? lowrank_col_inv(a, a.gw_tok ? a.inv_gyl : nullptr, 2, c0, cols) : 0.f;
   if constexpr (F32) {
     RdF32 rd{reinterpret_cast<const float*>(smem)};
-    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_gyl : nullptr,
-                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.O, a.kwb, a.tl, t0,
-                                last);
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, inv_c,
+                                a.part_gyl + tr * a.O + c0, a.q_gyl, a.O, a.kwb, a.tl, t0, last);
   } else {
     RdB16 rd{reinterpret_cast<const uint16_t*>(smem)};
-    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_gyl : nullptr,
-                                2, a.part_gyl + tr * a.O + c0, a.q_gyl, a.O, a.kwb, a.tl, t0,
-                                last);
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, inv_c,
+                                a.part_gyl + tr * a.O + c0, a.q_gyl, a.O, a.kwb, a.tl, t0, last);
   }
 }
 
@@ -949,15 +955,17 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
     *reinterpret_cast<uint4*>(codes + (sw * 64 + lr) * P_I4 + col / 2) =
         make_uint4(w4[sw][0], w4[sw][1], w4[sw][2], w4[sw][3]);
   __syncthreads();
+  const float inv_c =
+      PASS == PASS_QUANT ? lowrank_col_inv(a, a.gw_tok ? a.inv_xl : nullptr, 3, c0, cols) : 0.f;
   if (!a.conv) {
     RdI4 rd{codes, scales};
-    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_xl : nullptr,
-                                3, a.part_xl + tr * a.I + c0, a.q_xl, a.I, a.kwb, a.tl, t0,
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, inv_c,
+                                a.part_xl + tr * a.I + c0, a.q_xl, a.I, a.kwb, a.tl, t0,
                                 t0 + rows == a.T);
   } else {
     RdI4c rd{codes, scales};
-    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, a.gw_tok ? a.inv_xl : nullptr,
-                                3, a.part_xl + tr * a.I + c0, a.q_xl, a.I, a.kwb, a.tl, t0,
+    colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, inv_c,
+                                a.part_xl + tr * a.I + c0, a.q_xl, a.I, a.kwb, a.tl, t0,
                                 t0 + rows == a.T);
   }
 }
@@ -1015,15 +1023,19 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
     if (blockIdx.x == 1 % gridDim.x)
       for (int64_t i = threadIdx.x; i < a.pair_nctr; i += 256) a.pair_ctr[i] = 0u;
   }
-  if (blockIdx.x == 0 && threadIdx.x < 4) {
+  if (blockIdx.x == 0) {
     if constexpr (PASS == PASS_MAX) {
-      a.tmax[threadIdx.x] = 0u;  // k_tr_reduce folds into it
-    } else {  // tensor scales of the per-tensor modes
-      const int l = threadIdx.x;
-      const float qmax = l < 2 ? 7.f : 127.f;
-      if (l < 2 ? !a.gx_tok : !a.gw_tok) {
-        float* sc = l == 0 ? a.s_gy : l == 1 ? a.s_w : l == 2 ? a.s_gyl : a.s_xl;
-        sc[0] = scale_of(__uint_as_float(a.tmax[l]), qmax);
+      static_assert(4 * TMAX_SLOTS <= 256, "one slot per thread");
+      if (threadIdx.x < 4 * TMAX_SLOTS) a.tmax[threadIdx.x] = 0u;  // k_tr_reduce folds into them
+    } else if (threadIdx.x < 64) {  // tensor scales of the per-tensor modes (wave 0)
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        const float m = tensor_max_slots(a.tmax + l * TMAX_SLOTS);
+        const float qmax = l < 2 ? 7.f : 127.f;
+        if (threadIdx.x == 0 && (l < 2 ? !a.gx_tok : !a.gw_tok)) {
+          float* sc = l == 0 ? a.s_gy : l == 1 ? a.s_w : l == 2 ? a.s_gyl : a.s_xl;
+          sc[0] = scale_of(m, qmax);
+        }
       }
     }
   }
@@ -1070,8 +1082,10 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
 // Fold the partial maxima.  Entry e of each list takes the max over its
 // partials; per-token modes store its scale and reciprocal scale (the QUANT
 // pass multiplies by the latter).  Every block folds its per-list maxima into
-// the four tensor maxima with one atomicMax each (lists: 0 H.g_y rows, 1 H.w
-// columns, 2 low-rank g_y columns, 3 low-rank x columns).  Max is exact and
+// the four tensor maxima with one atomicMax each, on slot blockIdx % 64 of
+// the list (lists: 0 H.g_y rows, 1 H.w columns, 2 low-rank g_y columns, 3
+// low-rank x columns; 64 slots: same-address atomics serialize, ResNet-50
+// stage-3 shape reduce 13.6 -> 6.4 us without them).  Max is exact and
 // commutes, so the result does not depend on the schedule.  A block covers 64 consecutive entries; its 16
 // waves split each entry's partials (stride 16) so every wave keeps several
 // loads in flight.
@@ -1091,18 +1105,25 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
   else if (e < n1) { list = 2; p = a.part_gyl + (e - n0); np = a.ntr_gy; stride = a.O; }
   else if (e < n2) { list = 3; p = a.part_xl + (e - n1); np = a.ntr_t; stride = a.I; }
   else if (e < n3) { list = 1; p = a.part_w + (e - n2); np = a.ntr_o; stride = a.I; }
-  // wave wv folds partials wv, wv + 16, ...; four loads in flight per step
-  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+  // wave wv folds partials wv, wv + 16, ...; eight loads in flight per step
+  // (the low-rank column lists have up to T / 64 partials: ResNet-50 stage-3
+  // shape, 784)
+  constexpr int W = RED_WAVES, U = 8;
+  float mx[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) mx[u] = 0.f;
   int64_t k = wv;
-  constexpr int W = RED_WAVES;
-  for (; k + 3 * W < np; k += 4 * W) {
-    m0 = fmaxf(m0, p[k * stride]);
-    m1 = fmaxf(m1, p[(k + W) * stride]);
-    m2 = fmaxf(m2, p[(k + 2 * W) * stride]);
-    m3 = fmaxf(m3, p[(k + 3 * W) * stride]);
+  for (; k + (U - 1) * W < np; k += U * W) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p[(k + u * W) * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx[u] = fmaxf(mx[u], v[u]);
   }
-  for (; k < np; k += W) m0 = fmaxf(m0, p[k * stride]);
-  wpart[wv][lane] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  for (; k < np; k += W) mx[0] = fmaxf(mx[0], p[k * stride]);
+#pragma unroll
+  for (int u = 1; u < U; ++u) mx[0] = fmaxf(mx[0], mx[u]);
+  wpart[wv][lane] = mx[0];
   __syncthreads();
   if (wv == 0) {
   float m = wpart[0][lane];
@@ -1123,7 +1144,8 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
     // non-negative floats (they order like the values), exact and
     // schedule-independent; zeroed by the MAX pass
     const float v = wave_max(list == l ? m : 0.f);
-    if (lane == 0 && v > 0.f) atomicMax(a.tmax + l, __float_as_uint(v));
+    if (lane == 0 && v > 0.f)
+      atomicMax(a.tmax + l * TMAX_SLOTS + blockIdx.x % TMAX_SLOTS, __float_as_uint(v));
   }
   }
 }
