@@ -69,14 +69,46 @@ struct TileSmem {
 
 // Column readers: value of (row, c) of the tile as fp32, exactly as the
 // source holds it (bf16 widened; INT4 code times its row scale, one rounding).
+// Readers of a parked tile.  operator()(r, c): element (r, c) as fp32;
+// row<K>(r, c, v): the K adjacent elements c .. c + K - 1 of row r (c a
+// multiple of K, K = 1, 2 or 4) with one LDS read.  (The bit-field extract
+// builtin returns an unsigned int: the INT4 codes go through int before the
+// conversion to float.)
 struct RdF32 {
   const float* t;
   __device__ __forceinline__ float operator()(int r, int c) const { return t[r * P_F32 + c]; }
+  template <int K>
+  __device__ __forceinline__ void row(int r, int c, float (&v)[K]) const {
+    const float* p = t + r * P_F32 + c;
+    if constexpr (K == 4) {
+      const float4 u = *reinterpret_cast<const float4*>(p);
+      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    } else if constexpr (K == 2) {
+      const float2 u = *reinterpret_cast<const float2*>(p);
+      v[0] = u.x; v[1] = u.y;
+    } else {
+      v[0] = p[0];
+    }
+  }
 };
 struct RdB16 {
   const uint16_t* t;
   __device__ __forceinline__ float operator()(int r, int c) const {
     return __uint_as_float((uint32_t)t[r * P_B16 + c] << 16);
+  }
+  template <int K>
+  __device__ __forceinline__ void row(int r, int c, float (&v)[K]) const {
+    const uint16_t* p = t + r * P_B16 + c;
+    if constexpr (K == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    } else if constexpr (K == 2) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+      v[0] = __uint_as_float(u << 16); v[1] = __uint_as_float(u & 0xFFFF0000u);
+    } else {
+      v[0] = __uint_as_float((uint32_t)p[0] << 16);
+    }
   }
 };
 // ACBP codes of a linear layer's x tile: one scale per row (token).
@@ -87,6 +119,16 @@ struct RdI4 {
     const int byte = q[r * P_I4 + (c >> 1)];
     const int code = __builtin_amdgcn_sbfe(byte, (c & 1) * 4, 4);
     return s[r] * (float)code;
+  }
+  template <int K>
+  __device__ __forceinline__ void row(int r, int c, float (&v)[K]) const {
+    const float sr = s[r];
+    int bits;
+    if constexpr (K == 4) bits = *reinterpret_cast<const uint16_t*>(q + r * P_I4 + (c >> 1));
+    else bits = q[r * P_I4 + (c >> 1)];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      v[k] = sr * (float)(int)__builtin_amdgcn_sbfe(bits, ((K == 1 ? c & 1 : 0) + k) * 4, 4);
   }
 };
 // ACBP codes of a convolution's im2col tile: one scale per (row, 8-column
@@ -100,6 +142,17 @@ struct RdI4c {
     const int byte = q[r * P_I4 + (c >> 1)];
     const int code = __builtin_amdgcn_sbfe(byte, (c & 1) * 4, 4);
     return s[r * X_CHUNKS + (c >> 3)] * (float)code;
+  }
+  // the K columns share one 8-column chunk, hence one scale
+  template <int K>
+  __device__ __forceinline__ void row(int r, int c, float (&v)[K]) const {
+    const float sr = s[r * X_CHUNKS + (c >> 3)];
+    int bits;
+    if constexpr (K == 4) bits = *reinterpret_cast<const uint16_t*>(q + r * P_I4 + (c >> 1));
+    else bits = q[r * P_I4 + (c >> 1)];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      v[k] = sr * (float)(int)__builtin_amdgcn_sbfe(bits, ((K == 1 ? c & 1 : 0) + k) * 4, 4);
   }
 };
 
@@ -152,6 +205,38 @@ __device__ __forceinline__ void lowrank_col(const RD& rd, int r0, int c, float (
         g[j] = x0 + x1;
         g[j + h] = x0 - x1;
       }
+}
+
+// lowrank_col for the K adjacent columns c .. c + K - 1 (one LDS read per
+// row for all of them); per column the same additions in the same order.
+template <int N, int R, int K, class RD>
+__device__ __forceinline__ void lowrank_cols(const RD& rd, int r0, int c, float (&g)[K][R]) {
+  constexpr int G = N / R;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    float s[G][K];
+#pragma unroll
+    for (int k = 0; k < G; ++k) rd.template row<K>(r0 + j * G + k, c, s[k]);
+#pragma unroll
+    for (int h = 1; h < G; h <<= 1)
+#pragma unroll
+      for (int k = 0; k < G; k += 2 * h)
+#pragma unroll
+        for (int q = 0; q < K; ++q) s[k][q] = s[k][q] + s[k + h][q];
+#pragma unroll
+    for (int q = 0; q < K; ++q) g[q][j] = s[0][q];
+  }
+#pragma unroll
+  for (int q = 0; q < K; ++q)
+#pragma unroll
+    for (int h = 1; h < R; h <<= 1)
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        if ((j & h) == 0) {
+          float x0 = g[q][j], x1 = g[q][j + h];
+          g[q][j] = x0 + x1;
+          g[q][j + h] = x0 - x1;
+        }
 }
 
 // Full H_N of one column block.
@@ -308,69 +393,113 @@ __device__ __forceinline__ void zero_tail_i8(uint8_t* q, int64_t nrows, int64_t 
     q[i8_plane_off(nrows, c0 + i / w, from + i % w)] = 0;
 }
 
-// Reciprocal scale of column c0 + tid % CW of a low-rank column pass (QUANT):
-// colinv[column] in per-token mode, else that of tensor list `list` (INT8).
-// Every thread of the workgroup calls it (the tensor maximum is a wave fold).
-__device__ __forceinline__ float lowrank_col_inv(const TrArgs& a, const float* colinv, int list,
-                                                 int64_t c0, int cols) {
-  const int c = threadIdx.x % CW;
-  if (colinv) return c < cols ? colinv[c0 + c] : 0.f;
-  return inv_of(tensor_max_slots(a.tmax + list * TMAX_SLOTS), 127.f);
+// Adjacent columns per thread of a low-rank column pass: 64 / n (4, 2, 1), so
+// that the tile's (CW / CPT) column groups x (TT / n) blocks are the 256
+// threads' tasks (n = 128: 128 tasks).
+template <int N>
+constexpr int lowrank_cpt() { return N <= 16 ? 4 : N == 32 ? 2 : 1; }
+
+// Reciprocal scales of a thread's CPT columns c0 + (tid % (CW / CPT)) * CPT ..
+// of a low-rank column pass (QUANT): colinv[column] in per-token mode (0 past
+// cols), else that of tensor list `list` (INT8).  Every thread of the
+// workgroup calls it (the tensor maximum is a wave fold).
+template <int N>
+__device__ __forceinline__ void lowrank_col_inv(const TrArgs& a, const float* colinv, int list,
+                                                int64_t c0, int cols,
+                                                float (&inv)[lowrank_cpt<N>()]) {
+  constexpr int CPT = lowrank_cpt<N>();
+  const int c = (threadIdx.x % (CW / CPT)) * CPT;
+  if (colinv) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) inv[k] = c + k < cols ? colinv[c0 + c + k] : 0.f;
+  } else {
+    const float t = inv_of(tensor_max_slots(a.tmax + list * TMAX_SLOTS), 127.f);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) inv[k] = t;
+  }
 }
 
-// Column pass, low-rank rows of H_N (g_w operands).  Thread tid owns column
-// c = tid % CW and blocks b = tid / CW + 2t.  MAX: the tile's column maxima ->
-// part[0..cols).  QUANT: INT8 codes (reciprocal scale inv_c of the thread's
-// column, lowrank_col_inv) staged in LDS over the tile (after a barrier) and
-// stored as operand row c0 + c, K bytes t0 / N * R ..., of the INT8 K planes
-// of q (nrows rows, kpitch bytes of K per row).
+// Column pass, low-rank rows of H_N (g_w operands).  Thread tid owns the CPT
+// adjacent columns c = (tid % NCG) * CPT .. and block b = tid / NCG (NCG =
+// CW / CPT column groups), reading a row of its columns with one LDS read.
+// MAX: the tile's column maxima -> part[0..cols).  QUANT: INT8 codes
+// (reciprocal scales inv of the thread's columns, lowrank_col_inv) staged in
+// LDS over the tile (after a barrier) and stored as operand rows c0 + c, K
+// bytes t0 / N * R ..., of the INT8 K planes of q (nrows rows, kpitch bytes
+// of K per row).
 template <int PASS, int N, int R, class RD>
 __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, uint8_t* smem,
                                                 float* red, int rows, int cols, int64_t c0,
-                                                float inv_c, float* part, uint8_t* q,
-                                                int64_t nrows, int64_t kpitch, int64_t tl,
-                                                int64_t t0, bool last) {
-  constexpr int TPT = (TT / N) / 2 > 0 ? (TT / N) / 2 : 1;  // tasks per thread
-  constexpr int WPR = (R + 3) / 4;                           // code words per task
+                                                const float (&inv)[lowrank_cpt<N>()], float* part,
+                                                uint8_t* q, int64_t nrows, int64_t kpitch,
+                                                int64_t tl, int64_t t0, bool last) {
+  constexpr int CPT = lowrank_cpt<N>(), NCG = CW / CPT;
+  constexpr int WPR = (R + 3) / 4;  // code words per column
+  static_assert(NCG * (TT / N) <= 256, "one task per thread");
   const int tid = threadIdx.x;
-  const int c = tid % CW;
+  const int c = (tid % NCG) * CPT, b = tid / NCG;
   const int nb = rows / N;
-  float cm = 0.f;
-  uint32_t words[TPT][WPR];
+  const bool act = b < nb && c < cols;
+  float cm[CPT];
+  uint32_t words[CPT][WPR];
 #pragma unroll
-  for (int t = 0; t < TPT; ++t) {
+  for (int k = 0; k < CPT; ++k) {
+    cm[k] = 0.f;
 #pragma unroll
-    for (int w = 0; w < WPR; ++w) words[t][w] = 0;
-    const int b = tid / CW + 2 * t;
-    if (b < nb && c < cols) {
-      float g[R];
-      lowrank_col<N, R>(rd, b * N, c, g);
+    for (int w = 0; w < WPR; ++w) words[k][w] = 0;
+  }
+  if (act) {
+    float g[CPT][R];
+    lowrank_cols<N, R, CPT>(rd, b * N, c, g);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
       if constexpr (PASS == PASS_MAX) {
 #pragma unroll
-        for (int j = 0; j < R; ++j) cm = fmaxf(cm, fabsf(g[j]));
+        for (int j = 0; j < R; ++j) cm[k] = fmaxf(cm[k], fabsf(g[k][j]));
       } else {
 #pragma unroll
         for (int j = 0; j < R; ++j)
-          words[t][j / 4] |= (quant_bits<127>(g[j], inv_c) & 0xFFu) << (8 * (j % 4));
+          words[k][j / 4] |= (quant_bits<127>(g[k][j], inv[k]) & 0xFFu) << (8 * (j % 4));
       }
     }
   }
   if constexpr (PASS == PASS_MAX) {
-    tile_colmax_store(cm, red, tid, cols, part);
+    // maxima over the column's blocks: with NCG = 32 the two blocks of a
+    // wave meet by a lane exchange, then at most four slots per column in LDS
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      if constexpr (NCG == 32) cm[k] = fmaxf(cm[k], __shfl_xor(cm[k], 32));
+    }
+    constexpr int SLOTS = (TT / N) / (NCG == 32 ? 2 : 1);  // <= 4
+    static_assert(SLOTS >= 1 && SLOTS <= 4, "red holds four slots per column");
+    const int slot = NCG == 32 ? b / 2 : b;
+    if (NCG != 32 || (tid & 32) == 0) {
+      if (slot < SLOTS) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) red[slot * CW + c + k] = cm[k];
+      }
+    }
+    __syncthreads();
+    if (tid < CW && tid < cols) {
+      float m = red[tid];
+#pragma unroll
+      for (int sl = 1; sl < SLOTS; ++sl) m = fmaxf(m, red[sl * CW + tid]);
+      part[tid] = m;
+    }
   } else {
     uint8_t (*outs)[OUT_PITCH] = reinterpret_cast<uint8_t (*)[OUT_PITCH]>(smem);
     __syncthreads();  // every thread is done reading the tile
+    if (act) {
 #pragma unroll
-    for (int t = 0; t < TPT; ++t) {
-      const int b = tid / CW + 2 * t;
-      if (b < nb && c < cols) {
+      for (int k = 0; k < CPT; ++k) {
+        if (c + k >= cols) continue;
         if constexpr (R >= 4) {
 #pragma unroll
           for (int w = 0; w < WPR; ++w)
-            *reinterpret_cast<uint32_t*>(&outs[c][b * R + 4 * w]) = words[t][w];
+            *reinterpret_cast<uint32_t*>(&outs[c + k][b * R + 4 * w]) = words[k][w];
         } else {
 #pragma unroll
-          for (int j = 0; j < R; ++j) outs[c][b * R + j] = (uint8_t)(words[t][0] >> (8 * j));
+          for (int j = 0; j < R; ++j) outs[c + k][b * R + j] = (uint8_t)(words[k][0] >> (8 * j));
         }
       }
     }
@@ -690,8 +819,9 @@ __device__ void tr_job_gy(const TrArgs& a, int64_t bid, uint8_t* smem, float* re
   }
   __syncthreads();
   const bool last = t0 + rows == a.T;
-  const float inv_c =
-      PASS == PASS_QUANT ? lowrank_col_inv(a, a.gw_tok ? a.inv_gyl : nullptr, 2, c0, cols) : 0.f;
+  float inv_c[lowrank_cpt<N>()] = {};
+  if constexpr (PASS == PASS_QUANT)
+    lowrank_col_inv<N>(a, a.gw_tok ? a.inv_gyl : nullptr, 2, c0, cols, inv_c);
   if constexpr (F32) {
     RdF32 rd{reinterpret_cast<const float*>(smem)};
     colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, inv_c,
@@ -955,8 +1085,9 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
     *reinterpret_cast<uint4*>(codes + (sw * 64 + lr) * P_I4 + col / 2) =
         make_uint4(w4[sw][0], w4[sw][1], w4[sw][2], w4[sw][3]);
   __syncthreads();
-  const float inv_c =
-      PASS == PASS_QUANT ? lowrank_col_inv(a, a.gw_tok ? a.inv_xl : nullptr, 3, c0, cols) : 0.f;
+  float inv_c[lowrank_cpt<N>()] = {};
+  if constexpr (PASS == PASS_QUANT)
+    lowrank_col_inv<N>(a, a.gw_tok ? a.inv_xl : nullptr, 3, c0, cols, inv_c);
   if (!a.conv) {
     RdI4 rd{codes, scales};
     colpass_lowrank<PASS, N, R>(a, rd, smem, red, rows, cols, c0, inv_c,
