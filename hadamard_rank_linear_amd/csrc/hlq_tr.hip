@@ -887,9 +887,9 @@ __device__ __forceinline__ void gyr_load(const TrArgs& a, int64_t bid, uint4 (&r
 
 // Maxima of one tile: row maxima of H.g_y along O -> part_gy[ch][t], column
 // maxima of the low-rank g_y along T -> part_gyl[tr][o].
-template <int N, int R>
+template <int N, int R, bool LEAN>
 __device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
-                                             const uint4 (&raw)[8][2]) {
+                                             uint4 (&raw)[8][2]) {
   static_assert(N >= 16 && N <= 64, "a token block spans 2..8 row groups of one wave");
   constexpr int G = N / R;             // tokens per low-rank group
   constexpr int GL = G < 8 ? G : 8;    // in-lane span of a group
@@ -940,6 +940,21 @@ __device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
     if (c16 == 0 && act) a.part_gy[ch * a.T + t0 + r0 + k] = m;
   }
 
+  // LEAN: the tile's words pass through an empty asm statement, so the fp32
+  // values unpacked along O are not kept for the pass along T (which unpacks
+  // the same words again, two VALU operations per element).  Kept, they
+  // double the live registers of the whole launch (154 VGPRs against 90:
+  // three waves per SIMD instead of four), which the LDS-engine jobs of the
+  // same launch feel; the host takes LEAN when those jobs outnumber the
+  // register tiles' workgroups (ResNet-50 stage-3 shape MAX 49 -> 39 us,
+  // ViT-B qkv, mostly register tiles, 18.1 -> 19.2 with it).
+  if constexpr (LEAN) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        asm volatile("" : "+v"(raw[k][q].x), "+v"(raw[k][q].y), "+v"(raw[k][q].z), "+v"(raw[k][q].w));
+  }
   // ---- along T: one channel per iteration
   const int rib = rg % RGB;                                  // row group inside its block
   const bool owner = (G <= 8) || (rib % (G / 8) == 0);       // holds surviving entries
@@ -1138,7 +1153,8 @@ __device__ void tr_job_w(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
 }
 
 // F32: the g_y / w tiles hold fp32 (any fp32 source); otherwise bf16.
-template <int PASS, int N, int R, bool F32>
+// LEAN (MAX pass): the register-resident g_y tiles in the register-lean form.
+template <int PASS, int N, int R, bool F32, bool LEAN = false>
 __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
   static_assert(TT * P_I4 + TT * X_CHUNKS * 4 <= TileSmem<F32>::bytes, "x tile fits the smem buffer");
   static_assert(CW * OUT_PITCH <= TileSmem<F32>::bytes, "staging fits the smem buffer");
@@ -1186,7 +1202,7 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
       if (bid < a.gyreg_wgs && tile < a.wg_gy) {
         uint4 raw[8][2];
         gyr_load(a, tile, raw);
-        gyr_tile_max<N, R>(a, tile, raw);
+        gyr_tile_max<N, R, LEAN>(a, tile, raw);
       }
       return;
     }
@@ -1291,10 +1307,10 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
 #define HLQ_CAT2(a, b) a##b
 #define HLQ_CAT(a, b) HLQ_CAT2(a, b)
 
-template <int PASS, bool F32>
+template <int PASS, bool F32, bool LEAN = false>
 static hipError_t tr_dispatch(int r, dim3 g, hipStream_t s, const TrArgs& a) {
   constexpr int NN = HLQ_TR_N;
-#define HLQ_TR(RR) hipLaunchKernelGGL((k_tr<PASS, NN, RR, F32>), g, dim3(256), 0, s, a)
+#define HLQ_TR(RR) hipLaunchKernelGGL((k_tr<PASS, NN, RR, F32, LEAN>), g, dim3(256), 0, s, a)
   switch (r) {
     case 1: HLQ_TR(1); break;
     case 2: HLQ_TR(2); break;
@@ -1312,6 +1328,11 @@ static hipError_t tr_dispatch(int r, dim3 g, hipStream_t s, const TrArgs& a) {
 
 hipError_t HLQ_CAT(launch_tr_n, HLQ_TR_N)(const TrArgs& a, int pass, int r, dim3 g, hipStream_t s) {
   const bool f32 = a.gy_dt == 0 || a.w_dt == 0;
+  // register-lean g_y tiles when the LDS-engine workgroups outnumber theirs
+  const bool lean = a.gyreg_wgs > 0 && a.gyreg_wgs < a.gy_workers + a.wg_x + a.wg_w;
+  if (pass == PASS_MAX && lean)
+    return f32 ? tr_dispatch<PASS_MAX, true, true>(r, g, s, a)
+               : tr_dispatch<PASS_MAX, false, true>(r, g, s, a);
   if (pass == PASS_MAX)
     return f32 ? tr_dispatch<PASS_MAX, true>(r, g, s, a) : tr_dispatch<PASS_MAX, false>(r, g, s, a);
   return f32 ? tr_dispatch<PASS_QUANT, true>(r, g, s, a) : tr_dispatch<PASS_QUANT, false>(r, g, s, a);
