@@ -490,16 +490,30 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
     uint8_t (*outs)[OUT_PITCH] = reinterpret_cast<uint8_t (*)[OUT_PITCH]>(smem);
     __syncthreads();  // every thread is done reading the tile
     if (act) {
+      // column groups of CPT columns are CPT * OUT_PITCH bytes apart, which
+      // maps 16 lanes onto 4 banks; each lane writes its columns starting
+      // at a rotation (cg / 4 or cg / 8 mod CPT), so that the 16 lanes of
+      // one write cover 16 columns mod 16 (16 distinct banks)
+      const int cg = tid % NCG;
+      const int rot = CPT == 1 ? 0 : (cg >> (CPT == 4 ? 2 : 3)) & (CPT - 1);
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) {
+      for (int kk = 0; kk < CPT; ++kk) {
+        const int k = (kk + rot) & (CPT - 1);
+        uint32_t wv[WPR];
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) {
+          wv[w] = words[0][w];
+#pragma unroll
+          for (int q = 1; q < CPT; ++q) wv[w] = k == q ? words[q][w] : wv[w];
+        }
         if (c + k >= cols) continue;
         if constexpr (R >= 4) {
 #pragma unroll
           for (int w = 0; w < WPR; ++w)
-            *reinterpret_cast<uint32_t*>(&outs[c + k][b * R + 4 * w]) = words[k][w];
+            *reinterpret_cast<uint32_t*>(&outs[c + k][b * R + 4 * w]) = wv[w];
         } else {
 #pragma unroll
-          for (int j = 0; j < R; ++j) outs[c + k][b * R + j] = (uint8_t)(words[k][0] >> (8 * j));
+          for (int j = 0; j < R; ++j) outs[c + k][b * R + j] = (uint8_t)(wv[0] >> (8 * j));
         }
       }
     }
