@@ -775,8 +775,11 @@ __global__ __launch_bounds__(256, 2) void k_dgrad(GemmArgs g) {
 // b / n1w of g_w workgroup b % n1w (n1w a multiple of 8, so every split of a
 // tile runs on the XCD the tile mapping gives it).
 // WNW = 4: 512 threads (2 x 4 waves), one workgroup per CU.
-template <int WNW, int BM1, int BN1, int KB1, int NS1, int BM0, int BN0, int KB0, int NS0, int EPI>
-__global__ __launch_bounds__(128 * WNW, WNW == 2 ? 2 : 1) void k_gemm_pair(GemmArgs gw, int64_t n1,
+// MINW: waves per SIMD the registers must allow (three workgroups of 256
+// threads per CU take 3: at most 168 VGPRs).
+template <int WNW, int BM1, int BN1, int KB1, int NS1, int BM0, int BN0, int KB0, int NS0, int EPI,
+          int MINW = (WNW == 2 ? 2 : 1)>
+__global__ __launch_bounds__(128 * WNW, MINW) void k_gemm_pair(GemmArgs gw, int64_t n1,
                                                                            int64_t n1w, GemmArgs gx) {
   constexpr int L1 = NS1 * GemmShape<false, BM1, BN1, KB1, NS1, WNW>::STAGE;
   constexpr int L0 = NS0 * GemmShape<true, BM0, BN0, KB0, NS0, WNW>::STAGE;
@@ -899,7 +902,9 @@ hipError_t launch_gemm(bool fp6, const uint8_t* A, const uint8_t* B, int64_t M,
 
 // g_w tile of the pair launch: the plan's, except that a grid of at most 128
 // tiles of 128 x 128 takes the deep-ring configuration (wcfg 5: 128 x 128, KB
-// 64, 4 stages).  Then K splits: the g_w tiles start first, so a g_w tile
+// 64, 4 stages), and a larger one beside g_x tiles of at most 8 stages the
+// three-workgroup configuration (wcfg 6: KB 64 in 3 stages, the g_x ring 2
+// deep).  Then K splits: the g_w tiles start first, so a g_w tile
 // longer than the launch's mean work per workgroup slot (two per CU) sets its
 // length; nsplit cuts it (at most 4 splits of at least 4 stages each) when it
 // is more than twice that mean.  Work is counted in MACs, an FP6 MAC (twice
@@ -946,6 +951,16 @@ PairPlan plan_pair(int64_t T, int64_t I, int64_t O, const GemmPlan& px, const Ge
       // is faster with the 128-byte stages)
       pp.wcfg = 5; pp.wbm = 128; pp.wbn = 128;
       wstages = pw.stages * pw.kb / 64;
+    } else if (pw.kb % 64 == 0 && px.kb == 96 && px.stages <= 8) {
+      // a larger g_w grid beside short-K g_x tiles (their fixed per-tile
+      // costs, prologue loads and fp32 epilogue, dominate): three workgroups
+      // per CU, a two-deep FP6 ring and a three-deep ring of 64-byte INT8
+      // stages (48 KB each; ViT-B fc2 pair 54.7 -> 50.6 us median of 21
+      // interleaved rounds, T = 25216 95.6 -> 86.3; qkv and the ResNet-50
+      // shape are slower this way)
+      pp.wcfg = 6; pp.wbm = 128; pp.wbn = 128;
+      wstages = pw.stages * pw.kb / 64;
+      slots = 768;
     }
   }
   pp.wstages = wstages;
@@ -982,7 +997,7 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
   if (epi != EPI_F32 && epi != EPI_I32) return hipErrorInvalidValue;
   if (pp.nsplit < 1 || pp.nsplit > 4 || (pp.nsplit > 1 && (!part || !ctr))) return hipErrorInvalidValue;
   if ((pp.nsplit - 1) * pp.sps >= pp.wstages) return hipErrorInvalidValue;  // an empty split
-  if (pp.wstages * (pp.big || pp.wcfg == 5 ? 64 : pw.kb) != kw_pitch) return hipErrorInvalidValue;
+  if (pp.wstages * (pp.big || pp.wcfg >= 5 ? 64 : pw.kb) != kw_pitch) return hipErrorInvalidValue;
   const GemmArgs ax{gxA, gxB, T, I, kx_pitch, px.stages, px.stages, s_gy, gx_step, s_w, gx_step,
                     gx_alpha, g_x, acc_x};
   GemmArgs aw{gwA, gwB, O, I, kw_pitch, pp.wstages, pp.sps, s_gyl, gw_step, s_xl, gw_step,
@@ -1015,12 +1030,18 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
 #define HLQ_W1 256, 128, 64, 3
 #define HLQ_W2 128, 128, 128, 2
 #define HLQ_W5 128, 128, 64, 4
+#define HLQ_W6 128, 128, 64, 3
 #define HLQ_X0 128, 128, 96, 3
+#define HLQ_X6 128, 128, 96, 2
   if (px.cfg != 0 || px.kb != 96) return hipErrorInvalidValue;
   switch (pp.wcfg) {
     case 1: HLQ_PAIR(HLQ_W1, HLQ_X0); break;
     case 2: HLQ_PAIR(HLQ_W2, HLQ_X0); break;
     case 5: HLQ_PAIR(HLQ_W5, HLQ_X0); break;
+    case 6:
+      if (epi == EPI_F32) hipLaunchKernelGGL((k_gemm_pair<2, HLQ_W6, HLQ_X6, EPI_F32, 3>), g, dim3(256), 0, s, aw, n1, n1w, ax);
+      else hipLaunchKernelGGL((k_gemm_pair<2, HLQ_W6, HLQ_X6, EPI_I32, 3>), g, dim3(256), 0, s, aw, n1, n1w, ax);
+      break;
     default: HLQ_PAIR(HLQ_W0, HLQ_X0); break;
   }
 #undef HLQ_PAIR
@@ -1028,6 +1049,8 @@ hipError_t launch_gemm_pair(const uint8_t* gxA, const uint8_t* gxB, int64_t T, i
 #undef HLQ_W1
 #undef HLQ_W2
 #undef HLQ_W5
+#undef HLQ_W6
+#undef HLQ_X6
 #undef HLQ_X0
   return hipGetLastError();
 }
