@@ -39,7 +39,6 @@ struct Layout {
   size_t part_gy, part_gyl, part_xl, part_w;  // partial maxima of the MAX pass
   size_t inv_gy, inv_gyl, inv_xl, inv_w;      // reciprocal scales of per-token maxima
   size_t tmax;                                // tensor maxima (float bits) [4][TMAX_SLOTS]
-  int64_t nred;
   size_t partial;                             // int32 split-K partials
   int64_t nch_o, nch_i, ntr_t, ntr_o;         // transform tile grid
   hlq::GemmPlan plan_gx, plan_gw;
@@ -94,7 +93,6 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   L.inv_gyl = take((size_t)O * 4);
   L.inv_xl = take((size_t)I * 4);
   L.inv_w = take((size_t)I * 4);
-  L.nred = (T + O + 2 * I + hlq::TR_RED_ENTRIES - 1) / hlq::TR_RED_ENTRIES;
   L.tmax = take(4 * hlq::TMAX_SLOTS * 4);
   // split-K partials: the two GEMMs run one after the other on one stream and
   // share this buffer
@@ -168,7 +166,6 @@ hlq::TrArgs make_tr_args(const Layout& L, const void* g_y, int gy_dtype, const u
   a.inv_gy = f32(L.inv_gy); a.inv_gyl = f32(L.inv_gyl);
   a.inv_xl = f32(L.inv_xl); a.inv_w = f32(L.inv_w);
   a.tmax = reinterpret_cast<unsigned*>(ws + L.tmax);
-  a.nred = L.nred;
   a.nch_o = L.nch_o; a.nch_i = L.nch_i; a.ntr_t = L.ntr_t; a.ntr_o = L.ntr_o;
   // bf16 g_y with n <= 64 runs the register-resident kernel (64-token tiles;
   // part_gyl is sized for them)

@@ -42,7 +42,6 @@ struct TrArgs {
   // list l is the maximum of its slots): list 0 H.g_y, 1 H.w, 2 low-rank
   // g_y, 3 low-rank x (zeroed by the MAX pass, folded into by reduce)
   unsigned* tmax;
-  int64_t nred;  // reduce blocks = ceil((T + O + 2 I) / TR_RED_ENTRIES)
   int64_t nch_o, nch_i, ntr_t, ntr_o;
   // gy_reg: the MAX pass runs g_y on the register-resident kernel (bf16 g_y,
   // n <= 64, TR_GY_REG_ROWS-token tiles, wg_gy of them); ntr_gy = its token

@@ -1240,35 +1240,126 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
   }
 }
 
-// Fold the partial maxima.  Entry e of each list takes the max over its
-// partials; per-token modes store its scale and reciprocal scale (the QUANT
-// pass multiplies by the latter).  Every block folds its per-list maxima into
-// the four tensor maxima with one atomicMax each, on slot blockIdx % 64 of
-// the list (lists: 0 H.g_y rows, 1 H.w columns, 2 low-rank g_y columns, 3
-// low-rank x columns; 64 slots: same-address atomics serialize, ResNet-50
-// stage-3 shape reduce 13.6 -> 6.4 us without them).  Max is exact and
-// commutes, so the result does not depend on the schedule.  A block covers 64 consecutive entries; its 16
-// waves split each entry's partials (stride 16) so every wave keeps several
-// loads in flight.
+// Fold the partial maxima.  Lists: 0 H.g_y rows, 1 H.w columns, 2 low-rank
+// g_y columns, 3 low-rank x columns.
+//  * A list in per-token mode is folded entry by entry: entry e takes the max
+//    over its partials and stores its scale s = a/qmax and qmax/a (the QUANT
+//    pass multiplies by the latter).  A block covers 64 consecutive entries
+//    of the per-token lists (order 0, 2, 3, 1); its 16 waves split each
+//    entry's partials (stride 16), eight loads in flight per wave.
+//  * A list in per-tensor mode needs only its maximum: its partial array is
+//    folded flat, RED_FLAT floats per block with 16-byte loads (a low-rank
+//    column list has up to T / 64 partials per entry, which entry by entry
+//    made a few blocks long: ResNet-50 stage-3 shape, 784).
+// Every block folds its per-list maxima into the tensor maxima with one
+// atomicMax each, on slot blockIdx % 64 of the list (same-address atomics
+// serialize: the ResNet shape's reduce 13.6 -> 6.4 us without them).  Max of
+// non-negative float bit patterns is exact and commutes, so the result does
+// not depend on the schedule.
 constexpr int RED_ENTRIES = TR_RED_ENTRIES;
 constexpr int RED_WAVES = 16;
+constexpr int RED_FLAT = 64 * RED_WAVES * 16;  // floats per flat block
+
+// List l of the reduce: its partial array (np rows of `stride` entries) and
+// whether it is folded per entry.
+struct RedList {
+  const float* p;
+  int64_t np, stride;
+  bool tok;
+};
+__device__ __forceinline__ RedList red_list(const TrArgs& a, int l) {
+  if (l == 0) return {a.part_gy, a.nch_o, a.T, a.gx_tok != 0};
+  if (l == 1) return {a.part_w, a.ntr_o, a.I, a.gx_tok != 0};
+  if (l == 2) return {a.part_gyl, a.ntr_gy, a.O, a.gw_tok != 0};
+  return {a.part_xl, a.ntr_t, a.I, a.gw_tok != 0};
+}
+
+// Blocks of the reduce: per-entry blocks first, then each per-tensor list's
+// flat blocks (order 0, 2, 3, 1).  Host and device use the same count.
+__host__ __device__ __forceinline__ int64_t red_tok_entries(const TrArgs& a) {
+  return (a.gx_tok ? a.T + a.I : 0) + (a.gw_tok ? a.O + a.I : 0);
+}
+__host__ __device__ __forceinline__ int64_t red_flat_blocks(const TrArgs& a, int l) {
+  const bool tok = l < 2 ? a.gx_tok != 0 : a.gw_tok != 0;
+  if (tok) return 0;
+  const int64_t n = l == 0 ? a.nch_o * a.T : l == 1 ? a.ntr_o * a.I : l == 2 ? a.ntr_gy * a.O
+                                                                      : a.ntr_t * a.I;
+  return (n + RED_FLAT - 1) / RED_FLAT;
+}
+__host__ __device__ __forceinline__ int64_t red_blocks(const TrArgs& a) {
+  return (red_tok_entries(a) + RED_ENTRIES - 1) / RED_ENTRIES + red_flat_blocks(a, 0) +
+         red_flat_blocks(a, 2) + red_flat_blocks(a, 3) + red_flat_blocks(a, 1);
+}
 
 #if HLQ_TR_N == 16
 __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
   __shared__ float wpart[RED_WAVES][RED_ENTRIES];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t e = (int64_t)blockIdx.x * RED_ENTRIES + lane;
-  const int64_t n0 = a.T, n1 = n0 + a.O, n2 = n1 + a.I, n3 = n2 + a.I;
+  const int64_t ntok = red_tok_entries(a);
+  const int64_t nbt = (ntok + RED_ENTRIES - 1) / RED_ENTRIES;
+  const int slot = (int)(blockIdx.x % TMAX_SLOTS);
+  if ((int64_t)blockIdx.x >= nbt) {
+    // flat block of a per-tensor list
+    int64_t fb = (int64_t)blockIdx.x - nbt;
+    int l = -1;
+    const int order[4] = {0, 2, 3, 1};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t nb = red_flat_blocks(a, order[q]);
+      if (l < 0 && fb < nb) l = order[q];
+      else if (l < 0) fb -= nb;
+    }
+    if (l < 0) return;  // uniform: the grid holds no more blocks than counted
+    const RedList L = red_list(a, l);
+    const int64_t n = L.np * L.stride, c0 = fb * RED_FLAT;
+    float m = 0.f;
+    if ((n & 3) == 0) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t i = c0 + 4 * ((int64_t)u * 64 * RED_WAVES + threadIdx.x);
+        v[u] = i < n ? *reinterpret_cast<const float4*>(L.p + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m = fmaxf(m, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+    } else {
+      for (int64_t i = c0 + threadIdx.x; i < c0 + RED_FLAT && i < n; i += 64 * RED_WAVES)
+        m = fmaxf(m, L.p[i]);
+    }
+    m = wave_max(m);
+    if (lane == 0) wpart[wv][0] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float b = wpart[0][0];
+#pragma unroll
+      for (int q = 1; q < RED_WAVES; ++q) b = fmaxf(b, wpart[q][0]);
+      if (b > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(b));
+    }
+    return;
+  }
+  // per-entry block: entry e of the per-token lists in the order 0, 2, 3, 1
+  int64_t e = (int64_t)blockIdx.x * RED_ENTRIES + lane;
+  int list = -1;
+  int64_t idx = 0;
+  {
+    const int order[4] = {0, 2, 3, 1};
+    const int64_t len[4] = {a.T, a.O, a.I, a.I};
+    int64_t rest = e;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool tok = order[q] < 2 ? a.gx_tok != 0 : a.gw_tok != 0;
+      if (!tok || list >= 0) continue;
+      if (rest < len[q]) { list = order[q]; idx = rest; }
+      else rest -= len[q];
+    }
+  }
   const float* p = nullptr;
   int64_t np = 0, stride = 0;
-  int list = -1;
-  if (e < n0) { list = 0; p = a.part_gy + e; np = a.nch_o; stride = a.T; }
-  else if (e < n1) { list = 2; p = a.part_gyl + (e - n0); np = a.ntr_gy; stride = a.O; }
-  else if (e < n2) { list = 3; p = a.part_xl + (e - n1); np = a.ntr_t; stride = a.I; }
-  else if (e < n3) { list = 1; p = a.part_w + (e - n2); np = a.ntr_o; stride = a.I; }
+  if (list >= 0) {
+    const RedList L = red_list(a, list);
+    p = L.p + idx; np = L.np; stride = L.stride;
+  }
   // wave wv folds partials wv, wv + 16, ...; eight loads in flight per step
-  // (the low-rank column lists have up to T / 64 partials: ResNet-50 stage-3
-  // shape, 784)
   constexpr int W = RED_WAVES, U = 8;
   float mx[U];
 #pragma unroll
@@ -1287,27 +1378,24 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
   wpart[wv][lane] = mx[0];
   __syncthreads();
   if (wv == 0) {
-  float m = wpart[0][lane];
+    float m = wpart[0][lane];
 #pragma unroll
-  for (int q = 1; q < RED_WAVES; ++q) m = fmaxf(m, wpart[q][lane]);
-  if (list == 0) {
-    if (a.gx_tok) { a.inv_gy[e] = inv_of(m, 7.f); a.s_gy[e] = scale_of(m, 7.f); }
-  } else if (list == 2) {
-    if (a.gw_tok) { a.inv_gyl[e - n0] = inv_of(m, 127.f); a.s_gyl[e - n0] = scale_of(m, 127.f); }
-  } else if (list == 3) {
-    if (a.gw_tok) { a.inv_xl[e - n1] = inv_of(m, 127.f); a.s_xl[e - n1] = scale_of(m, 127.f); }
-  } else if (list == 1) {
-    if (a.gx_tok) { a.inv_w[e - n2] = inv_of(m, 7.f); a.s_w[e - n2] = scale_of(m, 7.f); }
-  }
+    for (int q = 1; q < RED_WAVES; ++q) m = fmaxf(m, wpart[q][lane]);
+    if (list == 0) {
+      a.inv_gy[idx] = inv_of(m, 7.f); a.s_gy[idx] = scale_of(m, 7.f);
+    } else if (list == 2) {
+      a.inv_gyl[idx] = inv_of(m, 127.f); a.s_gyl[idx] = scale_of(m, 127.f);
+    } else if (list == 3) {
+      a.inv_xl[idx] = inv_of(m, 127.f); a.s_xl[idx] = scale_of(m, 127.f);
+    } else if (list == 1) {
+      a.inv_w[idx] = inv_of(m, 7.f); a.s_w[idx] = scale_of(m, 7.f);
+    }
 #pragma unroll
-  for (int l = 0; l < 4; ++l) {
-    // tensor maxima: max over blocks by atomicMax on the bit patterns of
-    // non-negative floats (they order like the values), exact and
-    // schedule-independent; zeroed by the MAX pass
-    const float v = wave_max(list == l ? m : 0.f);
-    if (lane == 0 && v > 0.f)
-      atomicMax(a.tmax + l * TMAX_SLOTS + blockIdx.x % TMAX_SLOTS, __float_as_uint(v));
-  }
+    for (int l = 0; l < 4; ++l) {
+      // the per-token lists' tensor maxima too (the LQS statistics read them)
+      const float v = wave_max(list == l ? m : 0.f);
+      if (lane == 0 && v > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(v));
+    }
   }
 }
 #endif
@@ -1380,8 +1468,9 @@ hipError_t launch_tr(const TrArgs& args, int pass, int n, int r, hipStream_t s) 
 }
 
 hipError_t launch_tr_reduce(const TrArgs& a, hipStream_t s) {
-  if (a.nred != (int64_t)cdiv(a.T + a.O + 2 * a.I, RED_ENTRIES)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_tr_reduce, dim3((unsigned)a.nred), dim3(64 * RED_WAVES), 0, s, a);
+  const int64_t nb = red_blocks(a);
+  if (nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tr_reduce, dim3((unsigned)nb), dim3(64 * RED_WAVES), 0, s, a);
   return hipGetLastError();
 }
 #endif
