@@ -582,7 +582,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 300 untimed steps (about 30 ms of ViT-B qkv work): the GPU's clocks
+    # settle under load only after some tens of milliseconds; ten warmup
+    # steps timed the same 50 steps 10 % slower
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="vitb_qkv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements (fc2 layer, LQS statistics)")
@@ -645,14 +648,15 @@ def main():
     if not args.no_extra:
         extra["per_config"] = per_config_side(max(10, args.steps // 2), args.warmup)
         log("side measurement: forward with fused ACBP")
-        extra["forward"] = time_forward(cfg, inp)
+        extra["forward"] = time_forward(cfg, inp, warmup=args.warmup)
         log("side measurement: ResNet-50 stage-3 convolution (implicit GEMM)")
         extra["conv"] = {"resnet50_s3_conv3x3": time_conv(
             wl.CONV_BY_NAME["resnet50_s3_conv3x3"], max(10, args.steps // 2), args.warmup)}
         log("context: torch bf16 and fp32 backward of the same layer")
-        extra["context_torch_bf16_backward_us"] = time_torch_backward(cfg, inp, "bf16")
+        extra["context_torch_bf16_backward_us"] = time_torch_backward(cfg, inp, "bf16",
+                                                                      warmup=args.warmup)
         extra["context_torch_fp32_backward_us"] = time_torch_backward(cfg, inp, "fp32", steps=10,
-                                                                      warmup=3)
+                                                                      warmup=args.warmup // 4)
         # the library INT8 GEMM on the same two products (g_w: INT8 codes,
         # K = T'; g_x: its INT4 codes as INT8, K = O), for context
         log("context: hipBLASLt INT8 GEMMs of the layer's shapes")

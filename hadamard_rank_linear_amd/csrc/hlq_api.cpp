@@ -166,6 +166,7 @@ hlq::TrArgs make_tr_args(const Layout& L, const void* g_y, int gy_dtype, const u
   a.inv_gy = f32(L.inv_gy); a.inv_gyl = f32(L.inv_gyl);
   a.inv_xl = f32(L.inv_xl); a.inv_w = f32(L.inv_w);
   a.tmax = reinterpret_cast<unsigned*>(ws + L.tmax);
+  a.tok_tmax = 0;
   a.nch_o = L.nch_o; a.nch_i = L.nch_i; a.ntr_t = L.ntr_t; a.ntr_o = L.ntr_o;
   // bf16 g_y with n <= 64 runs the register-resident kernel (64-token tiles;
   // part_gyl is sized for them)
@@ -756,8 +757,9 @@ hlq_status hlq_lqs_accumulate(const void* g_y, int gy_dtype, const uint8_t* x_co
   // group maxima, per-token scales and tensor maxima: the backward's MAX and
   // reduce launches with both paths per token
   const Layout B = make_layout(T, I, O, block, rank);
-  const hlq::TrArgs t = make_tr_args(B, g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O,
-                                     block, true, true, ws);
+  hlq::TrArgs t = make_tr_args(B, g_y, gy_dtype, x_codes, x_scales, w, w_dtype, T, I, O,
+                               block, true, true, ws);
+  t.tok_tmax = 1;  // the statistics compare against the tensor maxima too
   HLQ_TRY(hlq::launch_tr(t, hlq::PASS_MAX, block, rank, s));
   HLQ_TRY(hlq::launch_tr_reduce(t, s));
   hlq::LqsArgs a;

@@ -41,9 +41,18 @@ __device__ __forceinline__ float load1(const void* base, int64_t e) {
   else return bf16_to_f32(static_cast<const uint16_t*>(base)[e]);
 }
 
+// Maximum of two values that are >= +0 and not NaN (maxima of magnitudes):
+// their bit patterns order like the values, so one integer maximum does it.
+// Unlike fmaxf it needs no NaN canonicalization of operands that come from
+// lane exchanges or memory, and a DPP lane exchange folds into it.
+__device__ __forceinline__ float nnmax(float a, float b) {
+  return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
+}
+
+// Maximum over the wave of values >= +0 (every lane gets it).
 __device__ __forceinline__ float wave_max(float a) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
+  for (int m = 32; m >= 1; m >>= 1) a = nnmax(a, __shfl_xor(a, m));
   return a;
 }
 
@@ -191,11 +200,11 @@ __device__ __forceinline__ float lane_xor(float v) {
 }
 
 // Max over the 8 lanes c16 = 0..7 of a row group (quad swaps, then the
-// half-row mirror pairs each lane with one of the other quad).
+// half-row mirror pairs each lane with one of the other quad); m >= +0.
 __device__ __forceinline__ float group8_max(float m) {
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, true)));
+  m = nnmax(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+  m = nnmax(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+  m = nnmax(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, true)));
   return m;
 }
 

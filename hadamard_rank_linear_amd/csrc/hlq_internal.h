@@ -42,6 +42,9 @@ struct TrArgs {
   // list l is the maximum of its slots): list 0 H.g_y, 1 H.w, 2 low-rank
   // g_y, 3 low-rank x (zeroed by the MAX pass, folded into by reduce)
   unsigned* tmax;
+  // tok_tmax: reduce also folds the per-token lists' tensor maxima (the LQS
+  // statistics read them; the backward reads only the per-tensor lists')
+  int tok_tmax;
   int64_t nch_o, nch_i, ntr_t, ntr_o;
   // gy_reg: the MAX pass runs g_y on the register-resident kernel (bf16 g_y,
   // n <= 64, TR_GY_REG_ROWS-token tiles, wg_gy of them); ntr_gy = its token

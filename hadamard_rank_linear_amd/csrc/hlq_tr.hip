@@ -158,7 +158,7 @@ struct RdI4c {
 
 __device__ __forceinline__ float max_over_16_lanes(float a) {
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
+  for (int m = 8; m >= 1; m >>= 1) a = nnmax(a, __shfl_xor(a, m));
   return a;
 }
 
@@ -302,7 +302,7 @@ __device__ __forceinline__ void tile_colmax_store(float m, float* red, int tid, 
                                                   float* dst) {
   red[tid] = m;
   __syncthreads();
-  if (tid < CW && tid < cols) dst[tid] = fmaxf(red[tid], red[tid + CW]);
+  if (tid < CW && tid < cols) dst[tid] = nnmax(red[tid], red[tid + CW]);
 }
 
 // Store the staged transposed codes: column c of the tile owns `len` bytes at
@@ -468,7 +468,7 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
     // wave meet by a lane exchange, then at most four slots per column in LDS
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      if constexpr (NCG == 32) cm[k] = fmaxf(cm[k], __shfl_xor(cm[k], 32));
+      if constexpr (NCG == 32) cm[k] = nnmax(cm[k], __shfl_xor(cm[k], 32));
     }
     constexpr int SLOTS = (TT / N) / (NCG == 32 ? 2 : 1);  // <= 4
     static_assert(SLOTS >= 1 && SLOTS <= 4, "red holds four slots per column");
@@ -483,7 +483,7 @@ __device__ __forceinline__ void colpass_lowrank(const TrArgs& a, const RD& rd, u
     if (tid < CW && tid < cols) {
       float m = red[tid];
 #pragma unroll
-      for (int sl = 1; sl < SLOTS; ++sl) m = fmaxf(m, red[sl * CW + tid]);
+      for (int sl = 1; sl < SLOTS; ++sl) m = nnmax(m, red[sl * CW + tid]);
       part[tid] = m;
     }
   } else {
@@ -721,16 +721,26 @@ __device__ __forceinline__ void gy_rows_bf16_full(const TrArgs& a, int64_t t0, i
   const uint32_t O32 = (uint32_t)a.O;
   const uint8_t* gbase = static_cast<const uint8_t*>(a.gy) + (t0 * a.O + c0) * 2;
   const uint32_t goff = ((uint32_t)lr * O32 + (uint32_t)col) * 2u;
+  // The row scales are loaded before the tile and in either mode (the array
+  // holds T floats): each sweep then waits only for its own tile rows.
+  // Loaded after the tile, or under a per-mode branch (the compiler moves
+  // loads used on one side into it), they made the first sweep wait for the
+  // whole tile.  Per-tensor mode masks the loaded bits to +0 and takes the
+  // tensor scale (scales are >= +0, never NaN).
+  float inv[SW];
+  if constexpr (PASS == PASS_QUANT) {
+    const float* ib = a.inv_gy + t0;
+    const uint32_t keep = a.gx_tok ? 0xFFFFFFFFu : 0u;
+    const float base = a.gx_tok ? 0.f : inv_tensor;
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) inv[sw] = ib[sw * 16 + lr];
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) inv[sw] = nnmax(__uint_as_float(__float_as_uint(inv[sw]) & keep), base);
+  }
   uint4 raw[SW];
 #pragma unroll
   for (int sw = 0; sw < SW; ++sw)
     raw[sw] = ld16<PASS == PASS_QUANT>(gbase + goff + (uint32_t)sw * 32u * O32);
-  float inv[SW];
-  if constexpr (PASS == PASS_QUANT) {
-    const float* ib = a.inv_gy + t0;
-#pragma unroll
-    for (int sw = 0; sw < SW; ++sw) inv[sw] = a.gx_tok ? ib[sw * 16 + lr] : inv_tensor;
-  }
   static_assert(SW % 4 == 0 && CW == 128, "four rows per FP6 conversion, one group per tile");
   // the tile's 128 columns are one FP6 group of each row: rows t0 .. of FP6
   // plane c0 / CW (T rows of 96 bytes)
@@ -748,10 +758,10 @@ __device__ __forceinline__ void gy_rows_bf16_full(const TrArgs& a, int64_t t0, i
       float m = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
-      m = fmaxf(m, lane_xor<1>(m));
-      m = fmaxf(m, lane_xor<2>(m));
-      m = fmaxf(m, lane_xor<4>(m));
-      m = fmaxf(m, lane_xor<8>(m));
+      m = nnmax(m, lane_xor<1>(m));
+      m = nnmax(m, lane_xor<2>(m));
+      m = nnmax(m, lane_xor<4>(m));
+      m = nnmax(m, lane_xor<8>(m));
       if (lc == 0) a.part_gy[ch * a.T + t0 + row] = m;
     } else {
 #pragma unroll
@@ -899,6 +909,30 @@ __device__ __forceinline__ void gyr_load(const TrArgs& a, int64_t bid, uint4 (&r
   }
 }
 
+// Whether tile `bid` lies wholly inside T and O (uniform over the wave).
+__device__ __forceinline__ bool gyr_full(const TrArgs& a, int64_t bid) {
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
+  return (tr + 1) * GYR_ROWS <= a.T && (ch + 1) * CW <= a.O;
+}
+
+// gyr_load for a whole tile: the sixteen loads back to back with no per-lane
+// guards.  (Guarded, the compiler placed register moves between the loads
+// that waited for the first ones to arrive, a memory latency per tile.)
+__device__ __forceinline__ void gyr_load_full(const TrArgs& a, int64_t bid, uint4 (&raw)[8][2]) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
+  const int64_t tr = b32 / n32, ch = b32 % n32;
+  const int64_t t0 = tr * GYR_ROWS + (lane >> 3) * 8, c0 = ch * CW + (lane & 7) * 16;
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.gy) + t0 * a.O + c0);
+  const int64_t pitch = a.O / 8;  // uint4 per row (O is a multiple of 16)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    raw[k][0] = src[k * pitch];
+    raw[k][1] = src[k * pitch + 1];
+  }
+}
+
 // Maxima of one tile: row maxima of H.g_y along O -> part_gy[ch][t], column
 // maxima of the low-rank g_y along T -> part_gyl[tr][o].
 template <int N, int R, bool LEAN>
@@ -1021,9 +1055,9 @@ __device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     float m = cmax[j];
-    m = fmaxf(m, lane_xor<8>(m));
-    m = fmaxf(m, lane_xor<16>(m));
-    m = fmaxf(m, lane_xor<32>(m));
+    m = nnmax(m, lane_xor<8>(m));
+    m = nnmax(m, lane_xor<16>(m));
+    m = nnmax(m, lane_xor<32>(m));
     cmax[j] = m;
   }
   if (lane < 8 && cact) {
@@ -1215,8 +1249,13 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
       const int64_t tile = bid * 4 + (threadIdx.x >> 6);
       if (bid < a.gyreg_wgs && tile < a.wg_gy) {
         uint4 raw[8][2];
-        gyr_load(a, tile, raw);
-        gyr_tile_max<N, R, LEAN>(a, tile, raw);
+        if (gyr_full(a, tile)) {  // separate copies: no register moves between the loads
+          gyr_load_full(a, tile, raw);
+          gyr_tile_max<N, R, LEAN>(a, tile, raw);
+        } else {
+          gyr_load(a, tile, raw);
+          gyr_tile_max<N, R, LEAN>(a, tile, raw);
+        }
       }
       return;
     }
@@ -1246,16 +1285,19 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
 //    over its partials and stores its scale s = a/qmax and qmax/a (the QUANT
 //    pass multiplies by the latter).  A block covers 64 consecutive entries
 //    of the per-token lists (order 0, 2, 3, 1); its 16 waves split each
-//    entry's partials (stride 16), eight loads in flight per wave.
+//    entry's partials (stride 16), all of a wave's loads (up to eight) in
+//    flight at once.
 //  * A list in per-tensor mode needs only its maximum: its partial array is
 //    folded flat, RED_FLAT floats per block with 16-byte loads (a low-rank
 //    column list has up to T / 64 partials per entry, which entry by entry
 //    made a few blocks long: ResNet-50 stage-3 shape, 784).
-// Every block folds its per-list maxima into the tensor maxima with one
-// atomicMax each, on slot blockIdx % 64 of the list (same-address atomics
-// serialize: the ResNet shape's reduce 13.6 -> 6.4 us without them).  Max of
-// non-negative float bit patterns is exact and commutes, so the result does
-// not depend on the schedule.
+// A flat block folds its list's maximum into the tensor maximum with one
+// atomicMax, on slot blockIdx % 64 of the list (same-address atomics
+// serialize: the ResNet shape's reduce 13.6 -> 6.4 us without the slots).
+// Per-entry blocks do the same for their lists only when the tensor maxima of
+// per-token lists are asked for (tok_tmax: the LQS statistics); the backward
+// reads only the per-tensor lists'.  Max of non-negative float bit patterns
+// is exact and commutes, so the result does not depend on the schedule.
 constexpr int RED_ENTRIES = TR_RED_ENTRIES;
 constexpr int RED_WAVES = 16;
 constexpr int RED_FLAT = 64 * RED_WAVES * 16;  // floats per flat block
@@ -1321,10 +1363,10 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
         v[u] = i < n ? *reinterpret_cast<const float4*>(L.p + i) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) m = fmaxf(m, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+      for (int u = 0; u < 4; ++u) m = nnmax(m, nnmax(nnmax(v[u].x, v[u].y), nnmax(v[u].z, v[u].w)));
     } else {
       for (int64_t i = c0 + threadIdx.x; i < c0 + RED_FLAT && i < n; i += 64 * RED_WAVES)
-        m = fmaxf(m, L.p[i]);
+        m = nnmax(m, L.p[i]);
     }
     m = wave_max(m);
     if (lane == 0) wpart[wv][0] = m;
@@ -1332,7 +1374,7 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
     if (threadIdx.x == 0) {
       float b = wpart[0][0];
 #pragma unroll
-      for (int q = 1; q < RED_WAVES; ++q) b = fmaxf(b, wpart[q][0]);
+      for (int q = 1; q < RED_WAVES; ++q) b = nnmax(b, wpart[q][0]);
       if (b > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(b));
     }
     return;
@@ -1359,28 +1401,27 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
     const RedList L = red_list(a, list);
     p = L.p + idx; np = L.np; stride = L.stride;
   }
-  // wave wv folds partials wv, wv + 16, ...; eight loads in flight per step
+  // wave wv folds partials wv, wv + 16, ...: rounds of eight loads, all of a
+  // round issued before its maxima (one round up to 128 partials)
   constexpr int W = RED_WAVES, U = 8;
   float mx[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) mx[u] = 0.f;
-  int64_t k = wv;
-  for (; k + (U - 1) * W < np; k += U * W) {
+  for (int64_t k = wv; k < np; k += U * W) {
     float v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = p[(k + u * W) * stride];
+    for (int u = 0; u < U; ++u) v[u] = k + u * W < np ? p[(k + u * W) * stride] : 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) mx[u] = fmaxf(mx[u], v[u]);
+    for (int u = 0; u < U; ++u) mx[u] = nnmax(mx[u], v[u]);
   }
-  for (; k < np; k += W) mx[0] = fmaxf(mx[0], p[k * stride]);
 #pragma unroll
-  for (int u = 1; u < U; ++u) mx[0] = fmaxf(mx[0], mx[u]);
+  for (int u = 1; u < U; ++u) mx[0] = nnmax(mx[0], mx[u]);
   wpart[wv][lane] = mx[0];
   __syncthreads();
   if (wv == 0) {
     float m = wpart[0][lane];
 #pragma unroll
-    for (int q = 1; q < RED_WAVES; ++q) m = fmaxf(m, wpart[q][lane]);
+    for (int q = 1; q < RED_WAVES; ++q) m = nnmax(m, wpart[q][lane]);
     if (list == 0) {
       a.inv_gy[idx] = inv_of(m, 7.f); a.s_gy[idx] = scale_of(m, 7.f);
     } else if (list == 2) {
@@ -1390,11 +1431,12 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
     } else if (list == 1) {
       a.inv_w[idx] = inv_of(m, 7.f); a.s_w[idx] = scale_of(m, 7.f);
     }
+    if (a.tok_tmax) {  // uniform
 #pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      // the per-token lists' tensor maxima too (the LQS statistics read them)
-      const float v = wave_max(list == l ? m : 0.f);
-      if (lane == 0 && v > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(v));
+      for (int l = 0; l < 4; ++l) {
+        const float v = wave_max(list == l ? m : 0.f);
+        if (lane == 0 && v > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(v));
+      }
     }
   }
 }
