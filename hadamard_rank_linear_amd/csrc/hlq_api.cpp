@@ -167,6 +167,7 @@ hlq::TrArgs make_tr_args(const Layout& L, const void* g_y, int gy_dtype, const u
   a.inv_xl = f32(L.inv_xl); a.inv_w = f32(L.inv_w);
   a.tmax = reinterpret_cast<unsigned*>(ws + L.tmax);
   a.tok_tmax = 0;
+  a.red_waves = 4;  // set per launch by launch_tr_reduce
   a.nch_o = L.nch_o; a.nch_i = L.nch_i; a.ntr_t = L.ntr_t; a.ntr_o = L.ntr_o;
   // bf16 g_y with n <= 64 runs the register-resident kernel (64-token tiles;
   // part_gyl is sized for them)

@@ -16,7 +16,6 @@ enum TrPass { PASS_MAX = 0, PASS_QUANT = 1 };
 // hlq_tr.hip); the host sizes the partial-maximum arrays with them.
 constexpr int TR_ROWS = 128;
 constexpr int TR_COLS = 128;
-constexpr int TR_RED_ENTRIES = 64;  // entries folded per reduce block
 // Atomic slots per tensor maximum: reduce block b folds into slot b % 64, so
 // same-address atomics queue 64 times less; readers fold the 64 slots (one
 // load per lane and a wave maximum).
@@ -45,6 +44,9 @@ struct TrArgs {
   // tok_tmax: reduce also folds the per-token lists' tensor maxima (the LQS
   // statistics read them; the backward reads only the per-tensor lists')
   int tok_tmax;
+  // waves per fold block (4, or 16 when a per-token list has over 32
+  // partials per entry; set by launch_tr_reduce)
+  int red_waves;
   int64_t nch_o, nch_i, ntr_t, ntr_o;
   // gy_reg: the MAX pass runs g_y on the register-resident kernel (bf16 g_y,
   // n <= 64, TR_GY_REG_ROWS-token tiles, wg_gy of them); ntr_gy = its token

@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "hlq_device.h"
@@ -1283,12 +1284,15 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
 // g_y columns, 3 low-rank x columns.
 //  * A list in per-token mode is folded entry by entry: entry e takes the max
 //    over its partials and stores its scale s = a/qmax and qmax/a (the QUANT
-//    pass multiplies by the latter).  A block covers 64 consecutive entries
-//    of the per-token lists (order 0, 2, 3, 1); its 16 waves split each
-//    entry's partials (stride 16), all of a wave's loads (up to eight) in
-//    flight at once.
+//    pass multiplies by the latter).  A block of W waves covers 64
+//    consecutive entries of the per-token lists (order 0, 2, 3, 1), its
+//    threads splitting each entry's partials W ways, up to eight loads in
+//    flight per thread: W = 4 when every such list has at most 32 partials
+//    per entry (one round of loads; sixteen waves had one or two partials
+//    each on the ViT-B qkv shape, reduce 3.9 -> 3.0 us), else 16 (a
+//    197-partial column list folds in two rounds).
 //  * A list in per-tensor mode needs only its maximum: its partial array is
-//    folded flat, RED_FLAT floats per block with 16-byte loads (a low-rank
+//    folded flat, 1024 W floats per block with 16-byte loads (a low-rank
 //    column list has up to T / 64 partials per entry, which entry by entry
 //    made a few blocks long: ResNet-50 stage-3 shape, 784).
 // A flat block folds its list's maximum into the tensor maximum with one
@@ -1298,9 +1302,9 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
 // per-token lists are asked for (tok_tmax: the LQS statistics); the backward
 // reads only the per-tensor lists'.  Max of non-negative float bit patterns
 // is exact and commutes, so the result does not depend on the schedule.
-constexpr int RED_ENTRIES = TR_RED_ENTRIES;
-constexpr int RED_WAVES = 16;
-constexpr int RED_FLAT = 64 * RED_WAVES * 16;  // floats per flat block
+constexpr int RED_ENTRIES = 64;  // per-token entries per fold block
+// floats per flat fold block of W waves (16 per thread)
+__host__ __device__ constexpr int64_t red_flat(int w) { return 64 * 16 * (int64_t)w; }
 
 // List l of the reduce: its partial array (np rows of `stride` entries) and
 // whether it is folded per entry.
@@ -1326,7 +1330,7 @@ __host__ __device__ __forceinline__ int64_t red_flat_blocks(const TrArgs& a, int
   if (tok) return 0;
   const int64_t n = l == 0 ? a.nch_o * a.T : l == 1 ? a.ntr_o * a.I : l == 2 ? a.ntr_gy * a.O
                                                                       : a.ntr_t * a.I;
-  return (n + RED_FLAT - 1) / RED_FLAT;
+  return (n + red_flat(a.red_waves) - 1) / red_flat(a.red_waves);
 }
 __host__ __device__ __forceinline__ int64_t red_blocks(const TrArgs& a) {
   return (red_tok_entries(a) + RED_ENTRIES - 1) / RED_ENTRIES + red_flat_blocks(a, 0) +
@@ -1334,11 +1338,13 @@ __host__ __device__ __forceinline__ int64_t red_blocks(const TrArgs& a) {
 }
 
 #if HLQ_TR_N == 16
-__global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
-  __shared__ float wpart[RED_WAVES][RED_ENTRIES];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t ntok = red_tok_entries(a);
-  const int64_t nbt = (ntok + RED_ENTRIES - 1) / RED_ENTRIES;
+template <int W>
+__global__ __launch_bounds__(64 * W) void k_tr_reduce(TrArgs a) {
+  constexpr int NT = 64 * W;
+  constexpr int64_t FLAT = red_flat(W);
+  __shared__ float wpart[NT];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t nbt = (red_tok_entries(a) + RED_ENTRIES - 1) / RED_ENTRIES;
   const int slot = (int)(blockIdx.x % TMAX_SLOTS);
   if ((int64_t)blockIdx.x >= nbt) {
     // flat block of a per-tensor list
@@ -1353,34 +1359,36 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
     }
     if (l < 0) return;  // uniform: the grid holds no more blocks than counted
     const RedList L = red_list(a, l);
-    const int64_t n = L.np * L.stride, c0 = fb * RED_FLAT;
+    const int64_t n = L.np * L.stride, c0 = fb * FLAT;
     float m = 0.f;
     if ((n & 3) == 0) {
       float4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int64_t i = c0 + 4 * ((int64_t)u * 64 * RED_WAVES + threadIdx.x);
+        const int64_t i = c0 + 4 * ((int64_t)u * NT + tid);
         v[u] = i < n ? *reinterpret_cast<const float4*>(L.p + i) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) m = nnmax(m, nnmax(nnmax(v[u].x, v[u].y), nnmax(v[u].z, v[u].w)));
     } else {
-      for (int64_t i = c0 + threadIdx.x; i < c0 + RED_FLAT && i < n; i += 64 * RED_WAVES)
-        m = nnmax(m, L.p[i]);
+      for (int64_t i = c0 + tid; i < c0 + FLAT && i < n; i += NT) m = nnmax(m, L.p[i]);
     }
     m = wave_max(m);
-    if (lane == 0) wpart[wv][0] = m;
+    if (lane == 0) wpart[wv] = m;
     __syncthreads();
-    if (threadIdx.x == 0) {
-      float b = wpart[0][0];
+    if (tid == 0) {
+      float b = wpart[0];
 #pragma unroll
-      for (int q = 1; q < RED_WAVES; ++q) b = nnmax(b, wpart[q][0]);
+      for (int q = 1; q < W; ++q) b = nnmax(b, wpart[q]);
       if (b > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(b));
     }
     return;
   }
-  // per-entry block: entry e of the per-token lists in the order 0, 2, 3, 1
-  int64_t e = (int64_t)blockIdx.x * RED_ENTRIES + lane;
+  // entries blockIdx * 64 .. of the per-token lists in the order 0, 2, 3, 1:
+  // thread (s, e) folds partials s, s + W, ... of entry e
+  constexpr int E = RED_ENTRIES, S = W;
+  const int e_loc = tid % E, sub = tid / E;
+  const int64_t e = (int64_t)blockIdx.x * E + e_loc;
   int list = -1;
   int64_t idx = 0;
   {
@@ -1401,27 +1409,26 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
     const RedList L = red_list(a, list);
     p = L.p + idx; np = L.np; stride = L.stride;
   }
-  // wave wv folds partials wv, wv + 16, ...: rounds of eight loads, all of a
-  // round issued before its maxima (one round up to 128 partials)
-  constexpr int W = RED_WAVES, U = 8;
+  // rounds of eight loads, all of a round issued before its maxima
+  constexpr int U = 8;
   float mx[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) mx[u] = 0.f;
-  for (int64_t k = wv; k < np; k += U * W) {
+  for (int64_t k = sub; k < np; k += (int64_t)U * S) {
     float v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = k + u * W < np ? p[(k + u * W) * stride] : 0.f;
+    for (int u = 0; u < U; ++u) v[u] = k + (int64_t)u * S < np ? p[(k + (int64_t)u * S) * stride] : 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) mx[u] = nnmax(mx[u], v[u]);
   }
 #pragma unroll
   for (int u = 1; u < U; ++u) mx[0] = nnmax(mx[0], mx[u]);
-  wpart[wv][lane] = mx[0];
+  wpart[sub * E + e_loc] = mx[0];
   __syncthreads();
-  if (wv == 0) {
-    float m = wpart[0][lane];
-#pragma unroll
-    for (int q = 1; q < RED_WAVES; ++q) m = nnmax(m, wpart[q][lane]);
+  float m = 0.f;
+  if (tid < E) {
+    m = wpart[tid];
+    for (int q = 1; q < S; ++q) m = nnmax(m, wpart[q * E + tid]);
     if (list == 0) {
       a.inv_gy[idx] = inv_of(m, 7.f); a.s_gy[idx] = scale_of(m, 7.f);
     } else if (list == 2) {
@@ -1431,12 +1438,12 @@ __global__ __launch_bounds__(64 * RED_WAVES) void k_tr_reduce(TrArgs a) {
     } else if (list == 1) {
       a.inv_w[idx] = inv_of(m, 7.f); a.s_w[idx] = scale_of(m, 7.f);
     }
-    if (a.tok_tmax) {  // uniform
+  }
+  if (a.tok_tmax && wv == 0) {  // uniform; the 64 entries are wave 0's threads
 #pragma unroll
-      for (int l = 0; l < 4; ++l) {
-        const float v = wave_max(list == l ? m : 0.f);
-        if (lane == 0 && v > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(v));
-      }
+    for (int l = 0; l < 4; ++l) {
+      const float v = wave_max(list == l && tid < E ? m : 0.f);
+      if (lane == 0 && v > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(v));
     }
   }
 }
@@ -1509,10 +1516,19 @@ hipError_t launch_tr(const TrArgs& args, int pass, int n, int r, hipStream_t s) 
   }
 }
 
-hipError_t launch_tr_reduce(const TrArgs& a, hipStream_t s) {
+hipError_t launch_tr_reduce(const TrArgs& args, hipStream_t s) {
+  TrArgs a = args;
+  // 4 waves per block when every per-token list has at most 32 partials per
+  // entry (one round of loads), else 16 (a 197-partial column list folds in
+  // two rounds)
+  int64_t np = 0;
+  if (a.gx_tok) np = std::max(a.nch_o, a.ntr_o);
+  if (a.gw_tok) np = std::max(np, std::max(a.ntr_gy, a.ntr_t));
+  a.red_waves = np <= 32 ? 4 : 16;
   const int64_t nb = red_blocks(a);
   if (nb <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tr_reduce, dim3((unsigned)nb), dim3(64 * RED_WAVES), 0, s, a);
+  if (a.red_waves == 4) hipLaunchKernelGGL(k_tr_reduce<4>, dim3((unsigned)nb), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_tr_reduce<16>, dim3((unsigned)nb), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 #endif
