@@ -48,9 +48,9 @@ def step_costs(cfg, dt_bytes):
     w = O * I * dt_bytes
     xc = T * I // 2 + 4 * T
     # partial maxima: H.g_y rows per 128-channel chunk, low-rank g_y columns per
-    # token tile (64 tokens on the register path: bf16 g_y with n <= 64, else
+    # token span (256 tokens on the register path: bf16 g_y with n <= 64, else
     # 128), low-rank x columns per 128 tokens, H.w columns per 128 channels
-    gy_rows = 64 if (dt_bytes == 2 and cfg.block <= 64) else 128
+    gy_rows = 256 if (dt_bytes == 2 and cfg.block <= 64) else 128
     parts = 4 * (T * -(-O // 128) + O * -(-T // gy_rows) + I * -(-T // 128) + I * -(-O // 128))
     return {
         "tr_max": (0, gy + xc + w + parts),

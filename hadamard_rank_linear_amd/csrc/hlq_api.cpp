@@ -86,7 +86,7 @@ Layout make_layout(int64_t T, int64_t I, int64_t O, int block, int rank) {
   L.ntr_t = (T + hlq::TR_ROWS - 1) / hlq::TR_ROWS;
   L.ntr_o = (O + hlq::TR_ROWS - 1) / hlq::TR_ROWS;
   L.part_gy = take((size_t)L.nch_o * T * 4);
-  L.part_gyl = take((size_t)((T + hlq::TR_GY_REG_ROWS - 1) / hlq::TR_GY_REG_ROWS) * O * 4);
+  L.part_gyl = take((size_t)L.ntr_t * O * 4);  // 128-token tiles or 256-token register spans
   L.part_xl = take((size_t)L.ntr_t * I * 4);
   L.part_w = take((size_t)L.ntr_o * I * 4);
   L.inv_gy = take((size_t)T * 4);
@@ -167,12 +167,11 @@ hlq::TrArgs make_tr_args(const Layout& L, const void* g_y, int gy_dtype, const u
   a.inv_xl = f32(L.inv_xl); a.inv_w = f32(L.inv_w);
   a.tmax = reinterpret_cast<unsigned*>(ws + L.tmax);
   a.tok_tmax = 0;
-  a.red_waves = 4;  // set per launch by launch_tr_reduce
   a.nch_o = L.nch_o; a.nch_i = L.nch_i; a.ntr_t = L.ntr_t; a.ntr_o = L.ntr_o;
-  // bf16 g_y with n <= 64 runs the register-resident kernel (64-token tiles;
-  // part_gyl is sized for them)
+  // bf16 g_y with n <= 64 runs the register-resident kernel (64-token tiles,
+  // one partial of the low-rank column maxima per 256 tokens)
   a.gy_reg = (gy_dtype == HLQ_BF16 && block <= 64) ? 1 : 0;
-  a.ntr_gy = a.gy_reg ? (T + hlq::TR_GY_REG_ROWS - 1) / hlq::TR_GY_REG_ROWS : L.ntr_t;
+  a.ntr_gy = a.gy_reg ? (T + hlq::TR_GY_REG_SPAN - 1) / hlq::TR_GY_REG_SPAN : L.ntr_t;
   a.wg_gy = a.ntr_gy * L.nch_o;
   a.gy_workers = 0;  // both chosen per pass by launch_tr
   a.gyreg_wgs = 0;

@@ -21,6 +21,7 @@ constexpr int TR_COLS = 128;
 // load per lane and a wave maximum).
 constexpr int TMAX_SLOTS = 64;
 constexpr int TR_GY_REG_ROWS = 64;   // token rows of a register-resident g_y tile (one wave)
+constexpr int TR_GY_REG_SPAN = 256;  // token rows of a register workgroup (four tiles)
 
 // Everything the three transform launches (MAX, reduce, QUANT) read and write.
 struct TrArgs {
@@ -32,7 +33,7 @@ struct TrArgs {
   uint8_t *q_gy, *q_w, *q_gyl, *q_xl;
   float *s_gy, *s_w, *s_gyl, *s_xl;
   // partial maxima: rows of H.g_y per column chunk [nch_o][T]; low-rank g_y
-  // columns per token range [ntr_gy][O] (ntr_gy <= ceil(T / TR_GY_REG_ROWS));
+  // columns per token range [ntr_gy][O] (ntr_gy <= ceil(T / TR_ROWS));
   // low-rank x [ntr_t][I]; H.w [ntr_o][I]
   float *part_gy, *part_gyl, *part_xl, *part_w;
   // reciprocal scales qmax / max of the folded maxima (per-token modes)
@@ -44,16 +45,14 @@ struct TrArgs {
   // tok_tmax: reduce also folds the per-token lists' tensor maxima (the LQS
   // statistics read them; the backward reads only the per-tensor lists')
   int tok_tmax;
-  // waves per fold block (4, or 16 when a per-token list has over 32
-  // partials per entry; set by launch_tr_reduce)
-  int red_waves;
   int64_t nch_o, nch_i, ntr_t, ntr_o;
   // gy_reg: the MAX pass runs g_y on the register-resident kernel (bf16 g_y,
-  // n <= 64, TR_GY_REG_ROWS-token tiles, wg_gy of them); ntr_gy = its token
-  // tiles (rows of part_gyl).  The LDS engine uses TR_ROWS-token tiles.
+  // n <= 64, TR_GY_REG_ROWS-token tiles, four per workgroup: wg_gy
+  // workgroups of TR_GY_REG_SPAN tokens x TR_COLS channels); ntr_gy = its
+  // token spans (rows of part_gyl).  The LDS engine uses TR_ROWS-token tiles.
   int gy_reg;
   int64_t ntr_gy;
-  int64_t wg_gy, wg_x, wg_w;  // tiles of each job
+  int64_t wg_gy, wg_x, wg_w;  // tiles (register g_y: workgroups) of each job
   int64_t gy_workers;         // LDS-engine g_y tiles of the transform launch (set per launch)
   int64_t gyreg_wgs;          // register-path g_y workgroups of that launch (4 tiles each)
   // Convolution (conv = 1): the x job gathers im2col of the ACBP-coded input

@@ -886,12 +886,11 @@ __device__ __forceinline__ float absmax16(const float (&v)[16]) {
   return fmaxf(m, fabsf(v[15]));
 }
 
-// Registers of one tile (zero outside T and O).
-__device__ __forceinline__ void gyr_load(const TrArgs& a, int64_t bid, uint4 (&raw)[8][2]) {
+// Registers of tile (tr, ch): tokens tr * 64 .., channels ch * 128 .. (zero
+// outside T and O).
+__device__ __forceinline__ void gyr_load(const TrArgs& a, int64_t tr, int64_t ch,
+                                         uint4 (&raw)[8][2]) {
   const int lane = threadIdx.x & 63;
-  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
-  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
-  const int64_t tr = b32 / n32, ch = b32 % n32;
   const int64_t t0 = tr * GYR_ROWS, c0 = ch * CW;
   const int rows = (int)(a.T - t0 < GYR_ROWS ? a.T - t0 : GYR_ROWS);
   const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
@@ -910,20 +909,17 @@ __device__ __forceinline__ void gyr_load(const TrArgs& a, int64_t bid, uint4 (&r
   }
 }
 
-// Whether tile `bid` lies wholly inside T and O (uniform over the wave).
-__device__ __forceinline__ bool gyr_full(const TrArgs& a, int64_t bid) {
-  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
-  const int64_t tr = b32 / n32, ch = b32 % n32;
+// Whether tile (tr, ch) lies wholly inside T and O (uniform over the wave).
+__device__ __forceinline__ bool gyr_full(const TrArgs& a, int64_t tr, int64_t ch) {
   return (tr + 1) * GYR_ROWS <= a.T && (ch + 1) * CW <= a.O;
 }
 
 // gyr_load for a whole tile: the sixteen loads back to back with no per-lane
 // guards.  (Guarded, the compiler placed register moves between the loads
 // that waited for the first ones to arrive, a memory latency per tile.)
-__device__ __forceinline__ void gyr_load_full(const TrArgs& a, int64_t bid, uint4 (&raw)[8][2]) {
+__device__ __forceinline__ void gyr_load_full(const TrArgs& a, int64_t tr, int64_t ch,
+                                              uint4 (&raw)[8][2]) {
   const int lane = threadIdx.x & 63;
-  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
-  const int64_t tr = b32 / n32, ch = b32 % n32;
   const int64_t t0 = tr * GYR_ROWS + (lane >> 3) * 8, c0 = ch * CW + (lane & 7) * 16;
   const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.gy) + t0 * a.O + c0);
   const int64_t pitch = a.O / 8;  // uint4 per row (O is a multiple of 16)
@@ -934,20 +930,18 @@ __device__ __forceinline__ void gyr_load_full(const TrArgs& a, int64_t bid, uint
   }
 }
 
-// Maxima of one tile: row maxima of H.g_y along O -> part_gy[ch][t], column
-// maxima of the low-rank g_y along T -> part_gyl[tr][o].
+// Maxima of tile (tr, ch): row maxima of H.g_y along O -> part_gy[ch][t];
+// column maxima of the low-rank g_y along T -> cm[0 .. 128) (the workgroup
+// folds its four tiles' into part_gyl).
 template <int N, int R, bool LEAN>
-__device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
-                                             uint4 (&raw)[8][2]) {
+__device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t tr, int64_t ch,
+                                             uint4 (&raw)[8][2], float* cm) {
   static_assert(N >= 16 && N <= 64, "a token block spans 2..8 row groups of one wave");
   constexpr int G = N / R;             // tokens per low-rank group
   constexpr int GL = G < 8 ? G : 8;    // in-lane span of a group
   constexpr int RGB = N / 8;           // row groups per token block
   const int lane = threadIdx.x & 63;
   const int c16 = lane & 7, rg = lane >> 3;
-  // tile ids and chunk counts fit 32 bits (grids are 32-bit)
-  const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
-  const int64_t tr = b32 / n32, ch = b32 % n32;
   const int64_t t0 = tr * GYR_ROWS, c0 = ch * CW;
   const int rows = (int)(a.T - t0 < GYR_ROWS ? a.T - t0 : GYR_ROWS);
   const int cols = (int)(a.O - c0 < CW ? a.O - c0 : CW);
@@ -1061,9 +1055,9 @@ __device__ __forceinline__ void gyr_tile_max(const TrArgs& a, int64_t bid,
     m = nnmax(m, lane_xor<32>(m));
     cmax[j] = m;
   }
-  if (lane < 8 && cact) {
+  if (lane < 8) {  // lane c16 < 8 holds columns 16 c16 .. + 15 (zero past O)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) a.part_gyl[tr * a.O + c0 + col + j] = cmax[j];
+    for (int j = 0; j < 16; ++j) cm[col + j] = cact ? cmax[j] : 0.f;
   }
 }
 
@@ -1244,19 +1238,38 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
   const int64_t per_r = (a.gyreg_wgs + 7) / 8, per_g = (a.gy_workers + 7) / 8;
   const int64_t per_x = (a.wg_x + 7) / 8, per_w = (a.wg_w + 7) / 8;
   if constexpr (PASS == PASS_MAX && N <= 64) {
-    // register-resident g_y tiles: four independent waves, one tile each
+    // register-resident g_y tiles: a workgroup takes four consecutive
+    // 64-token tiles of one 128-channel chunk, one per wave; the waves run
+    // independently and meet once, to fold their low-rank column maxima into
+    // one partial per 256 tokens (a quarter of the partials to fold)
     if (slot < per_r) {
       const int64_t bid = xcd * per_r + slot;
-      const int64_t tile = bid * 4 + (threadIdx.x >> 6);
-      if (bid < a.gyreg_wgs && tile < a.wg_gy) {
-        uint4 raw[8][2];
-        if (gyr_full(a, tile)) {  // separate copies: no register moves between the loads
-          gyr_load_full(a, tile, raw);
-          gyr_tile_max<N, R, LEAN>(a, tile, raw);
+      if (bid < a.gyreg_wgs) {  // uniform over the workgroup
+        // workgroup ids and chunk counts fit 32 bits (grids are 32-bit)
+        const uint32_t b32 = (uint32_t)bid, n32 = (uint32_t)a.nch_o;
+        const int64_t trg = b32 / n32, ch = b32 % n32;
+        const int w = threadIdx.x >> 6;
+        const int64_t tr = trg * 4 + w;
+        float* cm = red + w * CW;
+        if (tr * GYR_ROWS < a.T) {
+          uint4 raw[8][2];
+          if (gyr_full(a, tr, ch)) {  // separate copies: no register moves between the loads
+            gyr_load_full(a, tr, ch, raw);
+            gyr_tile_max<N, R, LEAN>(a, tr, ch, raw, cm);
+          } else {
+            gyr_load(a, tr, ch, raw);
+            gyr_tile_max<N, R, LEAN>(a, tr, ch, raw, cm);
+          }
         } else {
-          gyr_load(a, tile, raw);
-          gyr_tile_max<N, R, LEAN>(a, tile, raw);
+          cm[threadIdx.x & 63] = 0.f;
+          cm[64 + (threadIdx.x & 63)] = 0.f;
         }
+        __syncthreads();
+        const int c = threadIdx.x;
+        const int64_t c0 = ch * CW;
+        if (c < CW && c0 + c < a.O)
+          a.part_gyl[trg * a.O + c0 + c] =
+              nnmax(nnmax(red[c], red[CW + c]), nnmax(red[2 * CW + c], red[3 * CW + c]));
       }
       return;
     }
@@ -1284,132 +1297,110 @@ __global__ __launch_bounds__(256) void k_tr(TrArgs a) {
 // g_y columns, 3 low-rank x columns.
 //  * A list in per-token mode is folded entry by entry: entry e takes the max
 //    over its partials and stores its scale s = a/qmax and qmax/a (the QUANT
-//    pass multiplies by the latter).  A block of W waves covers 64
-//    consecutive entries of the per-token lists (order 0, 2, 3, 1), its
-//    threads splitting each entry's partials W ways, up to eight loads in
-//    flight per thread: W = 4 when every such list has at most 32 partials
-//    per entry (one round of loads; sixteen waves had one or two partials
-//    each on the ViT-B qkv shape, reduce 3.9 -> 3.0 us), else 16 (a
-//    197-partial column list folds in two rounds).
+//    pass multiplies by the latter).  A 256-thread block folds E consecutive
+//    entries of one list, its threads splitting each entry's partials
+//    256 / E ways with up to eight loads in flight per thread: E = 64 for
+//    lists of at most 32 partials per entry, 32 up to 64, else 16 (one round
+//    of loads up to 128 partials).  Blocks of 16 waves for 64 entries of any
+//    list left most waves idle on the short lists (ViT-B qkv fold 3.9 ->
+//    3.0 us).
 //  * A list in per-tensor mode needs only its maximum: its partial array is
-//    folded flat, 1024 W floats per block with 16-byte loads (a low-rank
-//    column list has up to T / 64 partials per entry, which entry by entry
-//    made a few blocks long: ResNet-50 stage-3 shape, 784).
+//    folded flat, RED_FLAT floats per block with 16-byte loads (entry by
+//    entry, a long low-rank column list made a few blocks long).
 // A flat block folds its list's maximum into the tensor maximum with one
 // atomicMax, on slot blockIdx % 64 of the list (same-address atomics
 // serialize: the ResNet shape's reduce 13.6 -> 6.4 us without the slots).
-// Per-entry blocks do the same for their lists only when the tensor maxima of
+// Per-entry blocks do the same for their list only when the tensor maxima of
 // per-token lists are asked for (tok_tmax: the LQS statistics); the backward
 // reads only the per-tensor lists'.  Max of non-negative float bit patterns
 // is exact and commutes, so the result does not depend on the schedule.
-constexpr int RED_ENTRIES = 64;  // per-token entries per fold block
-// floats per flat fold block of W waves (16 per thread)
-__host__ __device__ constexpr int64_t red_flat(int w) { return 64 * 16 * (int64_t)w; }
+constexpr int64_t RED_FLAT = 256 * 16;
 
-// List l of the reduce: its partial array (np rows of `stride` entries) and
-// whether it is folded per entry.
-struct RedList {
-  const float* p;
-  int64_t np, stride;
-  bool tok;
-};
-__device__ __forceinline__ RedList red_list(const TrArgs& a, int l) {
-  if (l == 0) return {a.part_gy, a.nch_o, a.T, a.gx_tok != 0};
-  if (l == 1) return {a.part_w, a.ntr_o, a.I, a.gx_tok != 0};
-  if (l == 2) return {a.part_gyl, a.ntr_gy, a.O, a.gw_tok != 0};
-  return {a.part_xl, a.ntr_t, a.I, a.gw_tok != 0};
+// partials per entry, entries, per-token mode of list l
+__host__ __device__ __forceinline__ int64_t red_np(const TrArgs& a, int l) {
+  return l == 0 ? a.nch_o : l == 1 ? a.ntr_o : l == 2 ? a.ntr_gy : a.ntr_t;
+}
+__host__ __device__ __forceinline__ int64_t red_len(const TrArgs& a, int l) {
+  return l == 0 ? a.T : l == 2 ? a.O : a.I;
+}
+__host__ __device__ __forceinline__ bool red_tok(const TrArgs& a, int l) {
+  return l < 2 ? a.gx_tok != 0 : a.gw_tok != 0;
+}
+__host__ __device__ __forceinline__ int red_ent(int64_t np) {
+  return np <= 32 ? 64 : np <= 64 ? 32 : 16;
 }
 
-// Blocks of the reduce: per-entry blocks first, then each per-tensor list's
-// flat blocks (order 0, 2, 3, 1).  Host and device use the same count.
-__host__ __device__ __forceinline__ int64_t red_tok_entries(const TrArgs& a) {
-  return (a.gx_tok ? a.T + a.I : 0) + (a.gw_tok ? a.O + a.I : 0);
+// Blocks of the reduce: the per-entry blocks of the per-token lists (order
+// 0, 2, 3, 1), then the flat blocks of the per-tensor lists (same order).
+// Host and device use the same counts.
+__host__ __device__ __forceinline__ int64_t red_tok_blocks(const TrArgs& a, int l) {
+  if (!red_tok(a, l)) return 0;
+  const int e = red_ent(red_np(a, l));
+  return (red_len(a, l) + e - 1) / e;
 }
 __host__ __device__ __forceinline__ int64_t red_flat_blocks(const TrArgs& a, int l) {
-  const bool tok = l < 2 ? a.gx_tok != 0 : a.gw_tok != 0;
-  if (tok) return 0;
-  const int64_t n = l == 0 ? a.nch_o * a.T : l == 1 ? a.ntr_o * a.I : l == 2 ? a.ntr_gy * a.O
-                                                                      : a.ntr_t * a.I;
-  return (n + red_flat(a.red_waves) - 1) / red_flat(a.red_waves);
+  if (red_tok(a, l)) return 0;
+  return (red_np(a, l) * red_len(a, l) + RED_FLAT - 1) / RED_FLAT;
 }
 __host__ __device__ __forceinline__ int64_t red_blocks(const TrArgs& a) {
-  return (red_tok_entries(a) + RED_ENTRIES - 1) / RED_ENTRIES + red_flat_blocks(a, 0) +
-         red_flat_blocks(a, 2) + red_flat_blocks(a, 3) + red_flat_blocks(a, 1);
+  return red_tok_blocks(a, 0) + red_tok_blocks(a, 2) + red_tok_blocks(a, 3) +
+         red_tok_blocks(a, 1) + red_flat_blocks(a, 0) + red_flat_blocks(a, 2) +
+         red_flat_blocks(a, 3) + red_flat_blocks(a, 1);
 }
 
 #if HLQ_TR_N == 16
-template <int W>
-__global__ __launch_bounds__(64 * W) void k_tr_reduce(TrArgs a) {
-  constexpr int NT = 64 * W;
-  constexpr int64_t FLAT = red_flat(W);
-  __shared__ float wpart[NT];
+// The fields of list L (chosen at compile time: selected at run time, the
+// argument block was copied to scratch memory).
+template <int L>
+__device__ __forceinline__ const float* red_part(const TrArgs& a) {
+  if constexpr (L == 0) return a.part_gy;
+  else if constexpr (L == 1) return a.part_w;
+  else if constexpr (L == 2) return a.part_gyl;
+  else return a.part_xl;
+}
+
+// Flat block b of per-tensor list L: its maximum into slot blockIdx % 64.
+template <int L>
+__device__ void red_flat_block(const TrArgs& a, int64_t b, float* wpart) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t nbt = (red_tok_entries(a) + RED_ENTRIES - 1) / RED_ENTRIES;
-  const int slot = (int)(blockIdx.x % TMAX_SLOTS);
-  if ((int64_t)blockIdx.x >= nbt) {
-    // flat block of a per-tensor list
-    int64_t fb = (int64_t)blockIdx.x - nbt;
-    int l = -1;
-    const int order[4] = {0, 2, 3, 1};
+  const float* lp = red_part<L>(a);
+  const int64_t n = red_np(a, L) * red_len(a, L), c0 = b * RED_FLAT;
+  float m = 0.f;
+  if ((n & 3) == 0) {
+    float4 v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t nb = red_flat_blocks(a, order[q]);
-      if (l < 0 && fb < nb) l = order[q];
-      else if (l < 0) fb -= nb;
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = c0 + 4 * ((int64_t)u * 256 + tid);
+      v[u] = i < n ? *reinterpret_cast<const float4*>(lp + i) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (l < 0) return;  // uniform: the grid holds no more blocks than counted
-    const RedList L = red_list(a, l);
-    const int64_t n = L.np * L.stride, c0 = fb * FLAT;
-    float m = 0.f;
-    if ((n & 3) == 0) {
-      float4 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t i = c0 + 4 * ((int64_t)u * NT + tid);
-        v[u] = i < n ? *reinterpret_cast<const float4*>(L.p + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) m = nnmax(m, nnmax(nnmax(v[u].x, v[u].y), nnmax(v[u].z, v[u].w)));
-    } else {
-      for (int64_t i = c0 + tid; i < c0 + FLAT && i < n; i += NT) m = nnmax(m, L.p[i]);
-    }
-    m = wave_max(m);
-    if (lane == 0) wpart[wv] = m;
-    __syncthreads();
-    if (tid == 0) {
-      float b = wpart[0];
-#pragma unroll
-      for (int q = 1; q < W; ++q) b = nnmax(b, wpart[q]);
-      if (b > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(b));
-    }
-    return;
+    for (int u = 0; u < 4; ++u) m = nnmax(m, nnmax(nnmax(v[u].x, v[u].y), nnmax(v[u].z, v[u].w)));
+  } else {
+    for (int64_t i = c0 + tid; i < c0 + RED_FLAT && i < n; i += 256) m = nnmax(m, lp[i]);
   }
-  // entries blockIdx * 64 .. of the per-token lists in the order 0, 2, 3, 1:
-  // thread (s, e) folds partials s, s + W, ... of entry e
-  constexpr int E = RED_ENTRIES, S = W;
+  m = wave_max(m);
+  if (lane == 0) wpart[wv] = m;
+  __syncthreads();
+  if (tid == 0) {
+    const float r = nnmax(nnmax(wpart[0], wpart[1]), nnmax(wpart[2], wpart[3]));
+    if (r > 0.f) atomicMax(a.tmax + L * TMAX_SLOTS + (int)(blockIdx.x % TMAX_SLOTS), __float_as_uint(r));
+  }
+}
+
+// Entries b * E .. of per-token list L: thread (s, e) folds partials
+// s, s + S, ... of entry e, rounds of eight loads issued before their maxima
+// (every load issued, past the list's end from partial 0, then dropped:
+// predicated loads became one branch each).
+template <int L>
+__device__ void red_entry_block(const TrArgs& a, int64_t b, float* wpart) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t lnp = red_np(a, L), len = red_len(a, L);
+  const int E = red_ent(lnp), S = 256 / E;
   const int e_loc = tid % E, sub = tid / E;
-  const int64_t e = (int64_t)blockIdx.x * E + e_loc;
-  int list = -1;
-  int64_t idx = 0;
-  {
-    const int order[4] = {0, 2, 3, 1};
-    const int64_t len[4] = {a.T, a.O, a.I, a.I};
-    int64_t rest = e;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool tok = order[q] < 2 ? a.gx_tok != 0 : a.gw_tok != 0;
-      if (!tok || list >= 0) continue;
-      if (rest < len[q]) { list = order[q]; idx = rest; }
-      else rest -= len[q];
-    }
-  }
-  const float* p = nullptr;
-  int64_t np = 0, stride = 0;
-  if (list >= 0) {
-    const RedList L = red_list(a, list);
-    p = L.p + idx; np = L.np; stride = L.stride;
-  }
-  // rounds of eight loads, all of a round issued before its maxima
+  const int64_t idx = b * E + e_loc;
+  const bool valid = idx < len;
+  const float* p = red_part<L>(a) + idx;
+  const int64_t np = valid ? lnp : 0;
   constexpr int U = 8;
   float mx[U];
 #pragma unroll
@@ -1417,9 +1408,12 @@ __global__ __launch_bounds__(64 * W) void k_tr_reduce(TrArgs a) {
   for (int64_t k = sub; k < np; k += (int64_t)U * S) {
     float v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = k + (int64_t)u * S < np ? p[(k + (int64_t)u * S) * stride] : 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int64_t kk = k + (int64_t)u * S;
+      v[u] = p[(kk < np ? kk : 0) * len];
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) mx[u] = nnmax(mx[u], v[u]);
+    for (int u = 0; u < U; ++u) mx[u] = nnmax(mx[u], k + (int64_t)u * S < np ? v[u] : 0.f);
   }
 #pragma unroll
   for (int u = 1; u < U; ++u) mx[0] = nnmax(mx[0], mx[u]);
@@ -1429,23 +1423,44 @@ __global__ __launch_bounds__(64 * W) void k_tr_reduce(TrArgs a) {
   if (tid < E) {
     m = wpart[tid];
     for (int q = 1; q < S; ++q) m = nnmax(m, wpart[q * E + tid]);
-    if (list == 0) {
-      a.inv_gy[idx] = inv_of(m, 7.f); a.s_gy[idx] = scale_of(m, 7.f);
-    } else if (list == 2) {
-      a.inv_gyl[idx] = inv_of(m, 127.f); a.s_gyl[idx] = scale_of(m, 127.f);
-    } else if (list == 3) {
-      a.inv_xl[idx] = inv_of(m, 127.f); a.s_xl[idx] = scale_of(m, 127.f);
-    } else if (list == 1) {
-      a.inv_w[idx] = inv_of(m, 7.f); a.s_w[idx] = scale_of(m, 7.f);
+    if (valid) {
+      if constexpr (L == 0) {
+        a.inv_gy[idx] = inv_of(m, 7.f); a.s_gy[idx] = scale_of(m, 7.f);
+      } else if constexpr (L == 2) {
+        a.inv_gyl[idx] = inv_of(m, 127.f); a.s_gyl[idx] = scale_of(m, 127.f);
+      } else if constexpr (L == 3) {
+        a.inv_xl[idx] = inv_of(m, 127.f); a.s_xl[idx] = scale_of(m, 127.f);
+      } else {
+        a.inv_w[idx] = inv_of(m, 7.f); a.s_w[idx] = scale_of(m, 7.f);
+      }
     }
   }
-  if (a.tok_tmax && wv == 0) {  // uniform; the 64 entries are wave 0's threads
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      const float v = wave_max(list == l && tid < E ? m : 0.f);
-      if (lane == 0 && v > 0.f) atomicMax(a.tmax + l * TMAX_SLOTS + slot, __float_as_uint(v));
-    }
+  if (a.tok_tmax && wv == 0) {  // uniform; the E <= 64 entries are wave 0's threads
+    const float v = wave_max(m);
+    if (lane == 0 && v > 0.f)
+      atomicMax(a.tmax + L * TMAX_SLOTS + (int)(blockIdx.x % TMAX_SLOTS), __float_as_uint(v));
   }
+}
+
+__global__ __launch_bounds__(256) void k_tr_reduce(TrArgs a) {
+  __shared__ float wpart[256];
+  int64_t b = blockIdx.x;
+  int64_t nb = red_tok_blocks(a, 0);
+  if (b < nb) { red_entry_block<0>(a, b, wpart); return; }
+  b -= nb; nb = red_tok_blocks(a, 2);
+  if (b < nb) { red_entry_block<2>(a, b, wpart); return; }
+  b -= nb; nb = red_tok_blocks(a, 3);
+  if (b < nb) { red_entry_block<3>(a, b, wpart); return; }
+  b -= nb; nb = red_tok_blocks(a, 1);
+  if (b < nb) { red_entry_block<1>(a, b, wpart); return; }
+  b -= nb; nb = red_flat_blocks(a, 0);
+  if (b < nb) { red_flat_block<0>(a, b, wpart); return; }
+  b -= nb; nb = red_flat_blocks(a, 2);
+  if (b < nb) { red_flat_block<2>(a, b, wpart); return; }
+  b -= nb; nb = red_flat_blocks(a, 3);
+  if (b < nb) { red_flat_block<3>(a, b, wpart); return; }
+  b -= nb; nb = red_flat_blocks(a, 1);
+  if (b < nb) red_flat_block<1>(a, b, wpart);
 }
 #endif
 
@@ -1500,7 +1515,7 @@ hipError_t launch_tr(const TrArgs& args, int pass, int n, int r, hipStream_t s) 
   if (pass == PASS_MAX && a.gy_reg) {
     if (a.gy_dt != 1 || n > 64) return hipErrorInvalidValue;
     a.gy_workers = 0;
-    a.gyreg_wgs = (a.wg_gy + 3) / 4;
+    a.gyreg_wgs = a.wg_gy;
   }
   // eight slots per XCD row: each XCD takes an eighth of every job list
   const int64_t slots = (a.gyreg_wgs + 7) / 8 + (a.gy_workers + 7) / 8 + (a.wg_x + 7) / 8 +
@@ -1516,19 +1531,10 @@ hipError_t launch_tr(const TrArgs& args, int pass, int n, int r, hipStream_t s) 
   }
 }
 
-hipError_t launch_tr_reduce(const TrArgs& args, hipStream_t s) {
-  TrArgs a = args;
-  // 4 waves per block when every per-token list has at most 32 partials per
-  // entry (one round of loads), else 16 (a 197-partial column list folds in
-  // two rounds)
-  int64_t np = 0;
-  if (a.gx_tok) np = std::max(a.nch_o, a.ntr_o);
-  if (a.gw_tok) np = std::max(np, std::max(a.ntr_gy, a.ntr_t));
-  a.red_waves = np <= 32 ? 4 : 16;
+hipError_t launch_tr_reduce(const TrArgs& a, hipStream_t s) {
   const int64_t nb = red_blocks(a);
   if (nb <= 0) return hipSuccess;
-  if (a.red_waves == 4) hipLaunchKernelGGL(k_tr_reduce<4>, dim3((unsigned)nb), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_tr_reduce<16>, dim3((unsigned)nb), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(k_tr_reduce, dim3((unsigned)nb), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 #endif
