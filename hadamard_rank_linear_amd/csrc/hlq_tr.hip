@@ -1080,12 +1080,24 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
   uint8_t* codes = smem;                                          // [TT][P_I4] bytes
   float* scales = reinterpret_cast<float*>(smem + TT * P_I4);     // [TT] or [TT][X_CHUNKS]
   // 64 code bytes per tile row: 4 lanes x 16 bytes, 64 rows per sweep.  Rows
-  // are I/2 bytes (a multiple of 4, not of 16), so the loads are dwords.
+  // are I/2 bytes, a multiple of 4: whole tiles of rows that are a multiple
+  // of 16 bytes take one 16-byte load per lane and sweep, the rest dwords
+  // (four dword loads per lane touched every 64-byte run four times).
   constexpr int SW = TT / 64;
   const int lr = tid >> 2, lq = tid & 3;
   const int col = lq * 32;
   uint32_t w4[SW][4];
-  if (!a.conv) {
+  if (!a.conv && rows == TT && cols == CW && a.I % 32 == 0) {
+    // whole tile with 16-byte aligned rows (uniform): one 16-byte load per
+    // sweep, no guards
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) {
+      const uint4 u = *reinterpret_cast<const uint4*>(a.xc + (t0 + sw * 64 + lr) * (a.I / 2) +
+                                                      (c0 + col) / 2);
+      w4[sw][0] = u.x; w4[sw][1] = u.y; w4[sw][2] = u.z; w4[sw][3] = u.w;
+    }
+    if (tid < TT) scales[tid] = a.xs[t0 + tid];
+  } else if (!a.conv) {
 #pragma unroll
     for (int sw = 0; sw < SW; ++sw) {
       const int row = sw * 64 + lr;
