@@ -1112,6 +1112,36 @@ __device__ void tr_job_x(const TrArgs& a, int64_t bid, uint8_t* smem, float* red
       }
     }
     if (tid < TT) scales[tid] = tid < rows ? a.xs[t0 + tid] : 0.f;
+  } else if (a.Cc % 32 == 0 && cols == CW) {
+    // the thread's four chunks are 32 consecutive channels of one tap (the
+    // channel count a multiple of 32): one 16-byte load of one pixel's codes
+    // and one scale per row
+    const int64_t cc = c0 + col, rs = cc / a.Cc, chan = cc - rs * a.Cc;
+    const int tap_r = (int)(rs / a.S), tap_s = (int)(rs - (int64_t)tap_r * a.S);
+    float sv[SW];
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) {
+      const int row = sw * 64 + lr;
+      const int64_t t = t0 + row;
+      const int64_t pq = a.P * a.Q;
+      const int64_t nn = t / pq, rem = t - nn * pq;
+      const int64_t p = rem / a.Q, q = rem - p * a.Q;
+      const int64_t hh = p * a.cstride - a.cpad + tap_r;
+      const int64_t ww = q * a.cstride - a.cpad + tap_s;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) w4[sw][d] = 0u;
+      sv[sw] = 0.f;
+      if (row < rows && hh >= 0 && hh < a.Hc && ww >= 0 && ww < a.Wc) {
+        const int64_t pix = (nn * a.Hc + hh) * a.Wc + ww;
+        const uint4 u = *reinterpret_cast<const uint4*>(a.xc + pix * (a.Cc / 2) + chan / 2);
+        w4[sw][0] = u.x; w4[sw][1] = u.y; w4[sw][2] = u.z; w4[sw][3] = u.w;
+        sv[sw] = a.xs[pix];
+      }
+    }
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw)
+      *reinterpret_cast<float4*>(scales + (sw * 64 + lr) * X_CHUNKS + lq * 4) =
+          make_float4(sv[sw], sv[sw], sv[sw], sv[sw]);
   } else {
     // taps and channels of this thread's four chunks
     int tap_r[4], tap_s[4];
